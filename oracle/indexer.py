@@ -1,0 +1,95 @@
+"""Indexer scoring and top-k selection over the compressed cache.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__``).
+
+[FP4] section "Les ingrédients": the 128-channel indexer key is what scores
+cached positions. [CS] section "L'architecture : trois leviers contre le
+cache": a Full layer computes new top-512 indices with its own indexer; a
+hierarchical sparse indexer caps the candidates at 16384 positions. [F24]
+section "Tre meccanismi al posto di un solo trucco": deeper indexing layers
+only look at the candidate pool that the first Full layer built.
+
+Readings taken (the pages give no score formula):
+
+* RELU_W score: S_i = sum_h w_h * max(0, q_h . k_i) over the indexer heads;
+  DOT score (one head): S_i = q . k_i. k_i is the exact dequantized key,
+  q_h the bf16 query. Computed in float64 and rounded once to float32; the
+  selection then works on those float32 values, the precision the hot path
+  keeps its scores in.
+* Order: score descending, ties broken by the lower position. The selected
+  positions are returned in ascending order, padded with -1 when fewer than
+  k positions exist.
+* Pool: the top-16384 positions by the same order (all positions when there
+  are at most 16384). The Full layer's top-512 is taken from that pool.
+* Reindex: the shared indexer key rows of the pool positions are rescored
+  with the layer's own query and weights; its top-512 is taken from the pool.
+"""
+import numpy as np
+
+from .cache import dequant_indexer
+from .formats import bf16_bits_to_float
+
+SCORE_DOT = 0
+SCORE_RELU_W = 1
+
+
+def scores(ik_rows, iks_rows, q_idx_bits, w=None, mode=SCORE_RELU_W):
+    """Scores of the given indexer rows. q_idx_bits: uint16 [Hi, 128]; w: float32 [Hi] or None (= 1).
+
+    Returns float32 [n].
+    """
+    k = dequant_indexer(ik_rows, iks_rows)                       # float64 [n, 128]
+    q = bf16_bits_to_float(q_idx_bits).astype(np.float64)        # [Hi, 128]
+    d = k @ q.T                                                  # [n, Hi]
+    if mode == SCORE_DOT:
+        if q.shape[0] != 1:
+            raise ValueError("DOT score takes exactly one indexer head")
+        s = d[:, 0]
+    elif mode == SCORE_RELU_W:
+        wh = np.ones(q.shape[0]) if w is None else np.asarray(w, np.float32).astype(np.float64)
+        s = np.maximum(d, 0.0) @ wh
+    else:
+        raise ValueError("unknown score mode")
+    return s.astype(np.float32)
+
+
+def order(score_values, positions):
+    """Positions sorted by (score descending, position ascending)."""
+    score_values = np.asarray(score_values, dtype=np.float32)
+    positions = np.asarray(positions, dtype=np.int64)
+    return positions[np.lexsort((positions, -score_values.astype(np.float64)))]
+
+
+def topk(score_values, positions, k):
+    """Top-k of (score, position) pairs; returns int32 [k] ascending, -1 padded."""
+    best = order(score_values, positions)[:k]
+    out = np.full(k, -1, dtype=np.int32)
+    out[: best.size] = np.sort(best)
+    return out
+
+
+def full_layer(ik_rows, iks_rows, q_idx_bits, w, mode, k=512, pool_k=0):
+    """Full layer of one sequence: score every entry, build the pool, take top-k.
+
+    Returns (topk int32 [k], pool int32 [pool_k] or None, scores float32 [n]).
+    """
+    n = ik_rows.shape[0]
+    s = scores(ik_rows, iks_rows, q_idx_bits, w, mode)
+    pos = np.arange(n)
+    if pool_k:
+        pool = topk(s, pos, pool_k)
+        members = pool[pool >= 0]
+        top = topk(s[members], members, k)
+        return top, pool, s
+    return topk(s, pos, k), None, s
+
+
+def reindex_layer(ik_rows, iks_rows, pool, q_idx_bits, w, mode, k=512):
+    """Reindex layer of one sequence: rescore the pool rows of the shared key, take top-k.
+
+    Returns (topk int32 [k], pool scores float32 [len(members)]).
+    """
+    members = np.asarray(pool)
+    members = members[members >= 0].astype(np.int64)
+    s = scores(ik_rows[members], iks_rows[members], q_idx_bits, w, mode)
+    return topk(s, members, k), s
