@@ -1,0 +1,201 @@
+"""Decode benchmark of the FP4 compressed-KV sparse decode path on one MI355X.
+
+One step = one Full CSA2 layer for every sequence of the batch: the indexer
+scores all cached entries (packed MXFP4 keys), the top-512 is selected, and all
+query heads attend over the dequantized FP4 latent at those positions. The
+workload is 32 sequences of 131072 tokens (65536 ratio-2 entries each), 64
+query heads, 16 indexer heads; every step is one query token per sequence.
+
+The cache is written once, from seeded synthetic hidden states, by the
+library's own cache-write kernel, then copied so that consecutive steps read
+different copies (4 copies of the 142.6 MB indexer stream exceed the 256 MB
+last-level cache, so the timed passes read HBM). The scoring kernel is timed
+by itself with HIP events that the library records around its launch on the
+step's stream; the whole step is timed with events around K steps.
+
+Prints one JSON line. `--gpus N` with N > 1 exits: this path runs on one GPU.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+COPIES = 4
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle timing budget")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def build_cache(L, synth, torch, w, p):
+    E = w.T // w.m
+    kv = torch.empty((w.B * E, 288), dtype=torch.uint8, device="cuda")
+    ik = torch.empty((w.B * E, 64), dtype=torch.uint8, device="cuda")
+    iks = torch.empty((w.B * E, 4), dtype=torch.uint8, device="cuda")
+    d = lambda a: torch.from_numpy(a).cuda()
+    for b in range(w.B):
+        x_lat, x_idx = synth.hidden_states_device(w, p, b)
+        L.cache_write(x_lat[None], x_idx[None], d(p["w_lat"]), d(p["w_idx"]), w.m,
+                      kv=kv[b * E:(b + 1) * E], ik=ik[b * E:(b + 1) * E], iks=iks[b * E:(b + 1) * E])
+    torch.cuda.synchronize()
+    return kv, ik, iks
+
+
+def cpu_baseline(w, p, budget_s):
+    """The oracle's decode step (scores, top-512, attention) on a sample of the same workload."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    from long_context_fp4_amd import synth
+    from oracle import cache as OC
+    from oracle import indexer as OI
+    from oracle import attention as OA
+    import torch
+
+    Lr = p["layers"][0]
+    seqs = [0, 1]
+    caches = []
+    for b in seqs:
+        x_lat, x_idx = synth.hidden_states_device(w, p, b)
+        xl = x_lat.cpu().numpy().view(np.uint16)
+        xi = x_idx.cpu().numpy().view(np.uint16)
+        caches.append(OC.cache_write(xl, xi, p["w_lat"], p["w_idx"], w.m))
+    del x_lat, x_idx
+    torch.cuda.empty_cache()
+    done = 0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1):
+        while True:
+            for b, (kv, ik, iks) in zip(seqs, caches):
+                n = ik.shape[0]
+                s = OI.scores(ik, iks, Lr["q_idx"][b], Lr["w"][b], OI.SCORE_RELU_W)
+                top = OI.topk(s, np.arange(n), w.k)
+                OA.sparse_attention(kv, top, Lr["q"][b], 1.0)
+                done += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s:
+                break
+    return {"value": done / el, "unit": "query-tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} decode steps (one query token each) of the decode128k workload on "
+                      f"sequences {seqs} (65536 entries, 64 heads, 16 indexer heads, top-512), "
+                      f"numpy oracle with BLAS limited to 1 thread, {el:.1f} s"}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported "
+              f"(the path shards by whole sequences, with no exchange between GPUs)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    import long_context_fp4_amd as L
+    from long_context_fp4_amd import synth
+
+    w = synth.workload("decode128k")
+    p = synth.params(w)
+    E = w.T // w.m
+    log("writing the cache")
+    kv, ik, iks = build_cache(L, synth, torch, w, p)
+    copies = [(kv, ik, iks)] + [(kv.clone(), ik.clone(), iks.clone()) for _ in range(COPIES - 1)]
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    Lr = p["layers"][0]
+    q = d(Lr["q"].view(np.int16))
+    q_idx = d(Lr["q_idx"].view(np.int16))
+    wh = d(Lr["w"])
+    off = d(np.arange(w.B, dtype=np.int64) * E)
+    nb = d(np.full(w.B, E, np.int32))
+    ws = L.Workspace()
+    topk = torch.empty((w.B, w.k), dtype=torch.int32, device="cuda")
+    out = torch.empty((w.B, w.H, 512), dtype=torch.float32, device="cuda")
+    lse = torch.empty((w.B, w.H), dtype=torch.float32, device="cuda")
+
+    def step(i, evs=None):
+        c = copies[i % COPIES]
+        if evs is not None:
+            L.set_profile_events(*evs)
+        L.decode_layer(L.CSA2_FULL, c[0], c[1], c[2], off, nb, E, q, q_idx=q_idx, w=wh, k=w.k,
+                       topk=topk, out=out, lse=lse, workspace=ws)
+
+    log(f"warmup {a.warmup}")
+    for i in range(a.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # whole-step timing: events around K steps
+    ev_s = torch.cuda.Event(enable_timing=True)
+    ev_e = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev_s.record()
+    for i in range(a.steps):
+        step(i)
+    ev_e.record()
+    torch.cuda.synchronize()
+    total_ms = ev_s.elapsed_time(ev_e)
+
+    # scoring kernel alone: events recorded by the library around its launch
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
+    for e0, e1 in pairs:
+        e0.record()
+        e1.record()
+    torch.cuda.synchronize()
+    for i in range(a.steps):
+        step(i, pairs[i])
+    torch.cuda.synchronize()
+    score_ms = [e0.elapsed_time(e1) for e0, e1 in pairs]
+    score_avg_us = 1e3 * float(np.mean(score_ms))
+
+    steps_per_s = a.steps / (total_ms / 1e3)
+    qtok_s = w.B * steps_per_s
+    idx_bytes = w.B * E * 68                      # packed indexer keys read by one scoring launch
+    gather_bytes = w.B * w.k * 288                # latent rows read by the attention
+    achieved = idx_bytes / (score_avg_us * 1e-6) / 1e9
+    step_gbs = (idx_bytes + gather_bytes) / (total_ms / a.steps * 1e-3) / 1e9
+    res = {
+        "metric": "decode query-tokens/sec at 128K ctx; cache-read HBM GB/s vs peak (1 GPU)",
+        "value": qtok_s,
+        "unit": "query-tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": total_ms / a.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) bf16 hidden states packed to FP4 by the library; seeded queries",
+        "config": {"workload": "decode128k: 32 sequences x 131072 tokens (65536 ratio-2 entries), one Full "
+                               "layer: indexer over all entries (16 heads), top-512, attention with 64 heads "
+                               "over the 512-d FP4 latent",
+                   "batch": w.B, "context_tokens": w.T, "entries_per_seq": E, "heads": w.H,
+                   "indexer_heads": w.Hi, "k": w.k, "cache_copies": COPIES},
+        "roofline": {"bound": "hbm", "kernel": "score_kernel (indexer scoring pass)",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "bytes_per_launch": idx_bytes, "avg_launch_us": score_avg_us},
+        "step_cache_read_gbs": step_gbs,
+    }
+    log(f"step {total_ms / a.steps * 1e3:.1f} us, scoring kernel {score_avg_us:.1f} us "
+        f"({achieved:.0f} GB/s), {qtok_s:.0f} query-tokens/s")
+    if not a.no_cpu_baseline:
+        log("timing the oracle on the host")
+        res["cpu_baseline"] = cpu_baseline(w, p, a.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

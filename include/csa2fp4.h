@@ -1,0 +1,222 @@
+/*
+ * csa2fp4.h — C ABI of the FP4 compressed global KV cache and its sparse
+ * decode path (CSA2-style attention), for AMD MI355X (gfx950).
+ *
+ * Pages this interface follows (web pages on DeepSeek-V4.1-Flash's cache):
+ *   [FP4] "Le cache KV en FP4 — les 890 octets, vérifiés" (mkdocs.reaper.mx)
+ *   [CS]  "DeepSeek V4.1 Flash : 890 octets de cache KV par token" (contextstudios.ai)
+ *   [TF]  "DeepSeek-V4.1 Flash compresse le KV-Cache de 4 fois" (techfi24.com)
+ *   [F24] "KV cache da 890 byte per token" (flash24.org)
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Every tensor pointer is a DEVICE pointer owned by the caller. The library
+ *   never allocates, frees or retains them; it only enqueues kernels on
+ *   `stream` (a hipStream_t passed as void*; NULL = the null stream). Calls
+ *   return as soon as the work is enqueued and are ordered on that stream.
+ * - bf16 tensors are passed as uint16_t bit patterns, row-major, contiguous.
+ * - Return value: CSA2_OK (0) or a negative CSA2_ERR_* code. On an argument
+ *   error nothing is enqueued and no HIP call is made; csa2_last_error()
+ *   then returns a message for the calling thread. Device-side faults surface
+ *   at the caller's next synchronisation of the stream.
+ * - Alignment: every data pointer must be 16-byte aligned (CSA2_ERR_ALIGN).
+ * - Workspaces: a workspace must be zero-filled by the caller before its
+ *   first use (e.g. allocated with zeros). In every call's layout its first
+ *   CSA2_MAX_BATCH * 16640 bytes hold one control block per sequence index
+ *   (selection state and a score histogram), which every successful call
+ *   leaves zero again; the rest is scratch. One workspace can therefore be
+ *   reused by later calls of any kind and size without clearing. Calls that
+ *   share a workspace must not overlap (use one stream or separate
+ *   workspaces).
+ * - Thread safety: the library holds no global mutable state apart from the
+ *   thread-local last-error message.
+ */
+#ifndef CSA2FP4_H
+#define CSA2FP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define CSA2_OK               0
+#define CSA2_ERR_NULL        -1  /* a required pointer is NULL */
+#define CSA2_ERR_SHAPE       -2  /* a size or count is out of range */
+#define CSA2_ERR_ALIGN       -3  /* a data pointer is not 16-byte aligned */
+#define CSA2_ERR_WORKSPACE   -4  /* workspace missing or smaller than required */
+#define CSA2_ERR_UNSUPPORTED -5  /* a mode or option this build does not implement */
+#define CSA2_ERR_HIP         -6  /* the HIP runtime reported an error at launch */
+
+/* indexer score definitions */
+#define CSA2_SCORE_DOT     0   /* S_i = q . k_i, exactly one indexer head */
+#define CSA2_SCORE_RELU_W  1   /* S_i = sum_h w_h * max(0, q_h . k_i) */
+
+/* CSA2 layer modes ([CS] section "L'architecture : trois leviers contre le cache") */
+#define CSA2_FULL     0   /* own indexer pass over every entry, new top-k */
+#define CSA2_REINDEX  1   /* rescore the Full layer's candidate pool, new top-k */
+#define CSA2_REUSE    2   /* reuse the previous layer's indices */
+
+/* layout constants ([FP4] section "Le coût d'une entrée") */
+#define CSA2_LATENT_CH           512
+#define CSA2_LATENT_BLOCK        16
+#define CSA2_MAIN_ROW_BYTES      288   /* 256 B of E2M1 codes + 32 B of E4M3 scales */
+#define CSA2_INDEXER_CH          128
+#define CSA2_INDEXER_BLOCK       32
+#define CSA2_INDEXER_CODE_BYTES  64    /* E2M1 codes */
+#define CSA2_INDEXER_SCALE_BYTES 4     /* E8M0 scales, kept in a separate array */
+
+/* limits of this build */
+#define CSA2_MAX_K               2048   /* top-k of a Full/Reindex layer (512 in the pages) */
+#define CSA2_MAX_POOL            16384  /* hierarchical candidate pool ([CS], same section) */
+#define CSA2_MAX_INDEXER_HEADS   16
+#define CSA2_MAX_HEADS           128    /* query heads of the attention */
+#define CSA2_MAX_RATIO           16
+#define CSA2_MAX_BATCH           1024   /* sequences per indexer / decode call */
+
+/*
+ * Cache write: ratio-m merge, then FP4 packing of the latent and the indexer key.
+ *
+ * Follows [TF] section "Mécanismes de compression du KV-Cache" (m consecutive
+ * positions fused with learned per-channel weights), [FP4] section "Le compte
+ * par couche" (one entry per m tokens) and [FP4] section "Le coût d'une entrée"
+ * (latent: E2M1 + one E4M3 scale per 16 channels; key: E2M1 + one E8M0 scale
+ * per 32 channels).
+ *
+ *   x_lat  bf16 [B][T][512]   hidden latent rows of B sequences
+ *   x_idx  bf16 [B][T][128]   hidden indexer-key rows
+ *   w_lat  f32  [m][512]      merge weights, already normalised over the m positions
+ *   w_idx  f32  [m][128]
+ *   kv     u8   [B*E][288]    out: row b*E+i = 256 code bytes (channel 2j in the low
+ *                             nibble of byte j) then 32 E4M3FN scale bytes (block b
+ *                             covers channels 16b..16b+15)
+ *   ik     u8   [B*E][64]     out: indexer-key codes, same nibble order
+ *   iks    u8   [B*E][4]      out: E8M0 scale bytes of the 4 blocks of 32 channels
+ * with E = floor(T/m); a trailing partial group of a sequence is not written.
+ *
+ * Merge, per channel c: acc = w[0][c]*x[m*i][c], then acc = acc + w[j][c]*x[m*i+j][c]
+ * for j = 1..m-1, each product and sum rounded to float32 (no fused multiply-add).
+ * Latent block: s = E4M3FN(amax/6) (correctly rounded float32 division, nearest-even,
+ * saturating at 448); codes = E2M1 nearest-even of the float32 quotient x/s, sign bit
+ * from x; s == 0 gives all codes 0. Key block: X = floor(log2 amax) - 2, byte X+127
+ * clamped to [0,254]; codes = E2M1 of x*2^-X; amax == 0 gives byte 0 and codes 0.
+ * Errors: NULL pointer, B < 1, T < 0, m outside [1, CSA2_MAX_RATIO], misalignment.
+ */
+int csa2_cache_write(const uint16_t* x_lat, const uint16_t* x_idx,
+                     const float* w_lat, const float* w_idx,
+                     int B, int64_t T, int m,
+                     uint8_t* kv, uint8_t* ik, uint8_t* iks, void* stream);
+
+/*
+ * Indexer pass and top-k ([FP4] section "Les ingrédients": the indexer key scores
+ * positions; [CS] section "L'architecture : trois leviers contre le cache": new
+ * top-512 per Full layer, hierarchical pool of at most 16384 candidates; [F24]
+ * section "Tre meccanismi al posto di un solo trucco": deeper layers rescore only
+ * the pool).
+ *
+ *   ik, iks        the cache's indexer rows (see csa2_cache_write)
+ *   entry_offset   i64 [B]  first cache row of sequence b
+ *   n_entries      i32 [B]  entries of sequence b; positions are 0..n_entries[b]-1
+ *   B, max_n       host ints; 1 <= B <= CSA2_MAX_BATCH; max_n >= every n_entries[b]
+ *                  (rows at positions >= max_n are not scored)
+ *   q_idx          bf16 [B][Hi][128] indexer queries; w f32 [B][Hi] head weights
+ *                  (NULL = all 1; ignored by CSA2_SCORE_DOT)
+ *   Hi, score_mode 1 <= Hi <= 16; CSA2_SCORE_DOT needs Hi == 1
+ *   cand           i32 [B][cand_stride] or NULL. NULL: score every entry (Full).
+ *                  Otherwise score only the listed positions (Reindex); entries
+ *                  < 0 are skipped. cand_stride <= CSA2_MAX_POOL.
+ *   k              1 <= k <= CSA2_MAX_K
+ *   topk           out i32 [B][k]: the k best positions by (score descending,
+ *                  position ascending), written in ascending position order,
+ *                  -1 padded when fewer than k candidates exist
+ *   pool_k, pool   0/NULL, or 1 <= pool_k <= CSA2_MAX_POOL with pool out i32
+ *                  [B][pool_k]: the best pool_k positions (same order rule, ascending,
+ *                  -1 padded); topk is then chosen from the pool. Full only.
+ *   scores_out     NULL, or out f32 [B][max_n] (Full) / [B][cand_stride] (Reindex):
+ *                  the float32 scores, for inspection
+ *   workspace      csa2_indexer_workspace_bytes(B, max_n, cand_stride) bytes
+ */
+size_t csa2_indexer_workspace_bytes(int B, int64_t max_n, int cand_stride);
+int csa2_indexer_topk(const uint8_t* ik, const uint8_t* iks,
+                      const int64_t* entry_offset, const int32_t* n_entries,
+                      int B, int64_t max_n,
+                      const uint16_t* q_idx, const float* w, int Hi, int score_mode,
+                      const int32_t* cand, int cand_stride,
+                      int k, int32_t* topk, int pool_k, int32_t* pool,
+                      float* scores_out, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Sparse attention of all query heads over the dequantized latent at the selected
+ * positions ([TF] section "Mécanismes de compression du KV-Cache", item 1: one
+ * 512-d latent shared by keys and values across heads; [FP4] section "Les
+ * ingrédients": the main-cache latent serves attention).
+ *
+ *   kv             the cache's main rows (see csa2_cache_write)
+ *   entry_offset   i64 [B]; n_entries i32 [B] (indices >= n_entries[b] are skipped)
+ *   idx            i32 [B][k] positions, -1 = skip; 1 <= k <= CSA2_MAX_K
+ *   q              bf16 [B][H][512]; 1 <= H <= CSA2_MAX_HEADS
+ *   softmax_scale  tau: logit = tau * (q_h . c_i)
+ *   out            out f32 [B][H][512]: o_h = sum_i softmax_i * c_i (0 if no valid index)
+ *   lse            out f32 [B][H] or NULL: log sum_i exp(logit_i) (-inf if none)
+ *   workspace      csa2_attention_workspace_bytes(B, H, k) bytes
+ */
+size_t csa2_attention_workspace_bytes(int B, int H, int k);
+int csa2_sparse_attention(const uint8_t* kv, const int64_t* entry_offset, const int32_t* n_entries,
+                          const int32_t* idx, int k, const uint16_t* q, int B, int H,
+                          float softmax_scale, float* out, float* lse,
+                          void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * One CSA2 layer of a decode step ([CS] section "L'architecture : trois leviers
+ * contre le cache": Full = own indexer and new top-k; Reindex = rescoring of the
+ * pool against the shared cache; Reuse = indices taken over).
+ *
+ *   mode CSA2_FULL:    indexer over every entry -> pool (if pool_k > 0) -> topk (out),
+ *                      pool (out) -> attention
+ *   mode CSA2_REINDEX: pool (in, [B][pool_k]) rescored with q_idx/w -> topk (out)
+ *                      -> attention
+ *   mode CSA2_REUSE:   topk (in) -> attention; q_idx, w, pool unused
+ * Arguments mean what they mean in csa2_indexer_topk and csa2_sparse_attention.
+ * workspace: csa2_decode_workspace_bytes(B, max_n, H, k, pool_k) bytes.
+ */
+size_t csa2_decode_workspace_bytes(int B, int64_t max_n, int H, int k, int pool_k);
+int csa2_decode_layer(int mode,
+                      const uint8_t* kv, const uint8_t* ik, const uint8_t* iks,
+                      const int64_t* entry_offset, const int32_t* n_entries,
+                      int B, int64_t max_n,
+                      const uint16_t* q_idx, const float* w, int Hi, int score_mode,
+                      const uint16_t* q, int H, float softmax_scale,
+                      int k, int pool_k, int32_t* pool, int32_t* topk,
+                      float* out, float* lse,
+                      void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Host-only byte accounting ([FP4] sections "Le coût d'une entrée" and "Le
+ * compte par couche"): sum over layers of (entry bytes of the latent + entry
+ * bytes of the key) / ratio, where an entry of ch channels with block blk and
+ * sbytes scale bytes per block costs ch/2 + (ch/blk)*sbytes (blk == 0: no
+ * scales). Returns a negative value on bad arguments.
+ */
+double csa2_bytes_per_token(const int* ratios, int n_layers,
+                            int lat_ch, int lat_blk, int lat_sbytes,
+                            int idx_ch, int idx_blk, int idx_sbytes);
+
+/*
+ * Measurement hook (not part of the method): two hipEvent_t handles (as void*)
+ * that the next Full-pass call of this thread (csa2_indexer_topk without cand,
+ * or csa2_decode_layer in CSA2_FULL mode) records on its stream immediately
+ * before and after the launch of its indexer scoring kernel, so a caller can
+ * time that kernel alone. One-shot: the handles are dropped by that call. Both
+ * NULL clears them. The events must be created by the caller (hipEventCreate).
+ */
+int csa2_set_profile_events(void* before_score, void* after_score);
+
+/* Message of the calling thread's last non-zero status ("" if none). */
+const char* csa2_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CSA2FP4_H */

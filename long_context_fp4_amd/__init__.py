@@ -1,0 +1,12 @@
+"""FP4 compressed global KV cache and sparse decode attention for AMD MI355X.
+
+The compute path is the HIP library ``libcsa2fp4.so`` (gfx950 kernels behind a
+C ABI, declared in ``include/csa2fp4.h``). This package holds its thin ctypes
+binding (argument marshalling only; PyTorch supplies device memory and the
+stream) and the seeded synthetic inputs used by the tests and the benchmark.
+"""
+from .binding import (  # noqa: F401
+    CSA2_FULL, CSA2_REINDEX, CSA2_REUSE, CSA2_SCORE_DOT, CSA2_SCORE_RELU_W,
+    Csa2Error, Workspace, bytes_per_token, cache_write, decode_layer, indexer_topk,
+    lib, library_path, set_profile_events, sparse_attention,
+)

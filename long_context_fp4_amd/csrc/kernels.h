@@ -1,0 +1,53 @@
+// Host-visible launchers of the gfx950 kernels (internal to libcsa2fp4).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace csa2 {
+
+// Per-sequence selection state kept in the indexer workspace (zero between calls).
+struct SelState {
+  uint32_t done_score;    // score workgroups of the sequence that finished
+  uint32_t done_select;   // select workgroups of the sequence that finished
+  int32_t thr_bin;        // histogram bin holding the K-th best key (-1: all selected)
+  uint32_t above;         // keys in bins above thr_bin
+  uint32_t ncand;         // candidates appended from thr_bin
+  uint32_t pad[3];
+};
+
+constexpr int kNumBins = 4096;
+constexpr int kSmallMax = 16384;
+// Per-sequence control block of the indexer workspace: SelState, then the
+// histogram. The control region at the start of the workspace always holds
+// CSA2_MAX_BATCH blocks, so a block's place never depends on B or max_n.
+constexpr int64_t kCtrlStride = 256 + 4 * kNumBins;   // 16640 bytes
+__host__ __device__ inline SelState* ctrl_state(uint8_t* ctrl, int b) { return (SelState*)(ctrl + b * kCtrlStride); }
+__host__ __device__ inline uint32_t* ctrl_hist(uint8_t* ctrl, int b) { return (uint32_t*)(ctrl + b * kCtrlStride + 256); }
+
+hipError_t launch_cache_write(const uint16_t* x_lat, const uint16_t* x_idx, const float* w_lat,
+                              const float* w_idx, int B, int64_t T, int m, uint8_t* kv, uint8_t* ik,
+                              uint8_t* iks, hipStream_t stream);
+
+hipError_t launch_score(const uint8_t* ik, const uint8_t* iks, const int64_t* entry_offset,
+                        const int32_t* n_entries, int B, int64_t max_n, const uint16_t* q_idx,
+                        const float* w, int Hi, int mode, const int32_t* cand, int cand_stride,
+                        float* scores, int64_t sstride, uint8_t* ctrl, uint32_t* bitmap,
+                        int64_t bm_stride, int K, hipStream_t stream);
+
+hipError_t launch_select(const float* scores, int64_t sstride, const int32_t* n_entries, int B,
+                         int64_t max_n, uint8_t* ctrl, uint32_t* bitmap, int64_t bm_stride,
+                         uint64_t* cbuf, int64_t cb_stride, int K, int32_t* out, int out_stride,
+                         hipStream_t stream);
+
+hipError_t launch_select_small(const float* scores, int64_t sstride, const int32_t* slot_pos,
+                               int pstride, int score_by_pos, const int32_t* n_entries, int B,
+                               int64_t max_n, int K, int32_t* out, int out_stride, hipStream_t stream);
+
+// Attention: number of entry splits used for B sequences, H heads, k indices.
+int attention_splits(int B, int H, int k);
+size_t attention_lds_bytes();
+hipError_t launch_attention(const uint8_t* kv, const int64_t* entry_offset, const int32_t* n_entries,
+                            const int32_t* idx, int k, const uint16_t* q, int B, int H, float tau,
+                            int S, float* out, float* lse, float* part, hipStream_t stream);
+
+}  // namespace csa2

@@ -1,0 +1,106 @@
+"""GPU parity of whole decode layers (Full / Reindex / Reuse) against the oracle."""
+import numpy as np
+import pytest
+
+from oracle import attention as OA
+from oracle import cache as OC
+from oracle import indexer as OI
+from long_context_fp4_amd import synth
+from tests.gpu_util import ATTN_REL_TOL, attn_rel_err, check_topk, dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+def oracle_cache(rng, n_list, m):
+    w_lat = synth.merge_weights(rng, m, 512)
+    w_idx = synth.merge_weights(rng, m, 128)
+    parts = [OC.cache_write(synth.hidden_host(rng, (n * m, 512)), synth.hidden_host(rng, (n * m, 128)),
+                            w_lat, w_idx, m) for n in n_list]
+    kv, ik, iks = (np.concatenate([p[i] for p in parts]) for i in range(3))
+    off = np.concatenate([[0], np.cumsum(n_list)[:-1]]).astype(np.int64)
+    return kv, ik, iks, off
+
+
+def check_attention(kv_rows, sel, q, out, lse, what):
+    ro, rl = OA.sparse_attention(kv_rows, sel, q)
+    err = attn_rel_err(out, ro)
+    assert np.all(err <= ATTN_REL_TOL), f"{what}: max rel err {err.max():.3g}"
+    assert np.all(np.abs(lse - rl) <= 2e-3), f"{what}: lse"
+
+
+@pytest.mark.parametrize("n_list,pool_k", [([40000, 23000, 70000], 16384), ([9000, 30000], 4096)])
+def test_layer_group_full_reindex_reuse(n_list, pool_k):
+    import torch
+    import long_context_fp4_amd as L
+    rng = np.random.default_rng(sum(n_list))
+    kv, ik, iks, off = oracle_cache(rng, n_list, 1)
+    B, H = len(n_list), 64
+    nb = np.asarray(n_list, np.int32)
+    ws = L.Workspace()
+    d = dict(kv=dev(kv), ik=dev(ik), iks=dev(iks), entry_offset=dev(off), n_entries=dev(nb), max_n=max(n_list),
+             workspace=ws)
+    qF, qiF, wF = (np.stack([f(rng, h) for _ in range(B)]) for f, h in
+                   ((synth.latent_query, H), (synth.indexer_query, 16), (synth.head_weights, 16)))
+    qR, qiR, wR = (np.stack([f(rng, h) for _ in range(B)]) for f, h in
+                   ((synth.latent_query, H), (synth.indexer_query, 16), (synth.head_weights, 16)))
+    qU = np.stack([synth.perturb(rng, qR[b], 0.01) for b in range(B)])
+    topF, pool, outF, lseF = L.decode_layer(L.CSA2_FULL, q=dev(qF), q_idx=dev(qiF), w=dev(wF), pool_k=pool_k, **d)
+    topR, _, outR, lseR = L.decode_layer(L.CSA2_REINDEX, q=dev(qR), q_idx=dev(qiR), w=dev(wR), pool=pool, **d)
+    _, _, outU, lseU = L.decode_layer(L.CSA2_REUSE, q=dev(qU), topk=topR, **d)
+    torch.cuda.synchronize()
+    assert int(ws.buf[: 1024 * 16640].count_nonzero()) == 0      # control region clean after the calls
+    # a standalone attention call on the same workspace leaves it clean too
+    L.sparse_attention(d["kv"], d["entry_offset"], d["n_entries"], topR, dev(qU), workspace=ws)
+    torch.cuda.synchronize()
+    assert int(ws.buf[: 1024 * 16640].count_nonzero()) == 0
+    topF, pool, topR = host(topF), host(pool), host(topR)
+    outF, outR, outU, lseF, lseR, lseU = map(host, (outF, outR, outU, lseF, lseR, lseU))
+    for b, n in enumerate(n_list):
+        rows = slice(off[b], off[b] + n)
+        s = OI.scores(ik[rows], iks[rows], qiF[b], wF[b], 1)
+        check_topk(pool[b], OI.topk(s, np.arange(n), pool_k), lambda p: s[p], pool_k, f"pool{b}")
+        gp = pool[b][pool[b] >= 0]
+        check_topk(topF[b], OI.topk(s[gp], gp, 512), lambda p: s[p], 512, f"full{b}")
+        check_attention(kv[rows], topF[b], qF[b], outF[b], lseF[b], f"full attention {b}")
+        s2 = np.zeros(n, np.float32)
+        s2[gp] = OI.scores(ik[rows][gp], iks[rows][gp], qiR[b], wR[b], 1)
+        check_topk(topR[b], OI.topk(s2[gp], gp, 512), lambda p: s2[p], 512, f"reindex{b}")
+        check_attention(kv[rows], topR[b], qR[b], outR[b], lseR[b], f"reindex attention {b}")
+        check_attention(kv[rows], topR[b], qU[b], outU[b], lseU[b], f"reuse attention {b}")
+
+
+def test_decode128k_full_size_sampled():
+    """32 sequences x 131072 tokens (65536 ratio-2 entries), one Full layer, as the benchmark runs it.
+
+    Sequences 0 and 31: cache bytes bit-exact, scores, top-512 and attention against the oracle.
+    """
+    import torch
+    import long_context_fp4_amd as L
+    w = synth.workload("decode128k")
+    p = synth.params(w)
+    E = w.T // w.m
+    kv = torch.empty((w.B * E, 288), dtype=torch.uint8, device="cuda")
+    ik = torch.empty((w.B * E, 64), dtype=torch.uint8, device="cuda")
+    iks = torch.empty((w.B * E, 4), dtype=torch.uint8, device="cuda")
+    hidden = {}
+    for b in range(w.B):
+        x_lat, x_idx = synth.hidden_states_device(w, p, b)
+        L.cache_write(x_lat[None], x_idx[None], dev(p["w_lat"]), dev(p["w_idx"]), w.m,
+                      kv=kv[b * E:(b + 1) * E], ik=ik[b * E:(b + 1) * E], iks=iks[b * E:(b + 1) * E])
+        if b in (0, w.B - 1):
+            hidden[b] = (host(x_lat), host(x_idx))
+    Lr = p["layers"][0]
+    off = np.arange(w.B, dtype=np.int64) * E
+    nb = np.full(w.B, E, np.int32)
+    top, _, out, lse = L.decode_layer(L.CSA2_FULL, kv, ik, iks, dev(off), dev(nb), E, dev(Lr["q"]),
+                                      q_idx=dev(Lr["q_idx"]), w=dev(Lr["w"]), k=w.k)
+    torch.cuda.synchronize()
+    top, out, lse = host(top), host(out), host(lse)
+    for b, (xl, xi) in hidden.items():
+        okv, oik, oiks = OC.cache_write(xl, xi, p["w_lat"], p["w_idx"], w.m)
+        assert np.array_equal(host(kv[b * E:(b + 1) * E]), okv)
+        assert np.array_equal(host(ik[b * E:(b + 1) * E]), oik)
+        assert np.array_equal(host(iks[b * E:(b + 1) * E]), oiks)
+        s = OI.scores(oik, oiks, Lr["q_idx"][b], Lr["w"][b], 1)
+        check_topk(top[b], OI.topk(s, np.arange(E), w.k), lambda q: s[q], w.k, f"seq{b}")
+        check_attention(okv, top[b], Lr["q"][b], out[b], lse[b], f"attention seq{b}")
