@@ -40,8 +40,8 @@ size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // the place of any block depends on B or max_n: the scratch regions behind it
 // can never overlap a control block of a later call with other sizes.
 struct IndexerWs {
-  size_t ctrl, bitmap, cand, scores, total;
-  int64_t slots, bm_words;
+  size_t ctrl, bitmap, cand, scores, summ, wgc, gscr, total;
+  int64_t slots, bm_words, nblk, gscr_stride;
 };
 
 size_t ctrl_bytes();
@@ -56,6 +56,11 @@ IndexerWs indexer_layout(int B, int64_t max_n, int cand_stride) {
   L.bitmap = off; off = round_up(off + (size_t)B * L.bm_words * 4, 256);
   L.cand = off;   off = round_up(off + (size_t)B * L.slots * 8, 256);
   L.scores = off; off = round_up(off + (size_t)B * L.slots * 4, 256);
+  L.nblk = (L.slots + csa2::kScoreChunk - 1) / csa2::kScoreChunk;
+  L.summ = off;   off = round_up(off + (size_t)B * L.nblk * csa2::kSumWords * 4, 256);
+  L.wgc = off;    off = round_up(off + (size_t)B * L.nblk * csa2::kCandCap * 8, 256);
+  L.gscr_stride = L.slots > L.nblk * csa2::kCandCap ? L.slots : L.nblk * csa2::kCandCap;
+  L.gscr = off;   off = round_up(off + (size_t)B * L.gscr_stride * 8, 256);
   L.total = off;
   return L;
 }
@@ -123,36 +128,58 @@ int run_indexer(const uint8_t* ik, const uint8_t* iks, const int64_t* entry_offs
                 int Hi, int score_mode, const int32_t* cand, int cand_stride, int k, int32_t* topk,
                 int pool_k, int32_t* pool, float* scores_out, uint8_t* ws, hipStream_t stream) {
   const IndexerWs L = indexer_layout(B, max_n, cand ? cand_stride : 0);
-  uint8_t* ctrl = ws + L.ctrl;
-  uint32_t* bitmap = (uint32_t*)(ws + L.bitmap);
+  csa2::SelBufs sb;
+  sb.ctrl = ws + L.ctrl;
+  sb.bitmap = (uint32_t*)(ws + L.bitmap);
+  sb.bm_stride = L.bm_words;
+  sb.summ = (uint32_t*)(ws + L.summ);
+  sb.summ_stride = L.nblk * csa2::kSumWords;
+  sb.wgc = (uint64_t*)(ws + L.wgc);
+  sb.wgc_stride = L.nblk * csa2::kCandCap;
+  sb.gscr = (uint64_t*)(ws + L.gscr);
+  sb.gscr_stride = L.gscr_stride;
   uint64_t* cbuf = (uint64_t*)(ws + L.cand);
   float* scores = scores_out ? scores_out : (float*)(ws + L.scores);
   const int64_t sstride = scores_out ? (cand ? cand_stride : max_n) : L.slots;
   hipError_t e;
+  hipEvent_t ev0 = g_ev_before, ev1 = g_ev_after;
+  if (!cand) g_ev_before = g_ev_after = nullptr;
+  auto score = [&](int sel, int K) -> hipError_t {
+    hipError_t r;
+    if (!cand && ev0 && (r = hipEventRecord(ev0, stream)) != hipSuccess) return r;
+    r = csa2::launch_score(ik, iks, entry_offset, n_entries, B, max_n, q_idx, w, Hi, score_mode, cand,
+                           cand_stride, scores, sstride, sb, sel, K, stream);
+    if (r != hipSuccess) return r;
+    if (!cand && ev1 && (r = hipEventRecord(ev1, stream)) != hipSuccess) return r;
+    return hipSuccess;
+  };
   if (cand) {
     // Reindex: score the listed positions, select k among them
-    e = csa2::launch_score(ik, iks, entry_offset, n_entries, B, max_n, q_idx, w, Hi, score_mode, cand,
-                           cand_stride, scores, sstride, nullptr, nullptr, 0, 0, stream);
+    e = score(csa2::SEL_NONE, 0);
     if (e != hipSuccess) return hip_status(e, "indexer score");
     e = csa2::launch_select_small(scores, sstride, cand, cand_stride, 0, n_entries, B, max_n, k, topk, k, stream);
     return hip_status(e, "indexer select");
   }
-  const bool small = max_n <= csa2::kSmallMax && pool_k == 0;
-  const int K1 = pool_k > 0 ? pool_k : k;
-  hipEvent_t ev0 = g_ev_before, ev1 = g_ev_after;
-  g_ev_before = g_ev_after = nullptr;
-  if (ev0 && (e = hipEventRecord(ev0, stream)) != hipSuccess) return hip_status(e, "profile event");
-  e = csa2::launch_score(ik, iks, entry_offset, n_entries, B, max_n, q_idx, w, Hi, score_mode, nullptr, 0,
-                         scores, sstride, small ? nullptr : ctrl, bitmap, L.bm_words, K1, stream);
-  if (e != hipSuccess) return hip_status(e, "indexer score");
-  if (ev1 && (e = hipEventRecord(ev1, stream)) != hipSuccess) return hip_status(e, "profile event");
-  if (small) {
+  if (max_n <= csa2::kSmallMax && pool_k == 0) {
+    e = score(csa2::SEL_NONE, 0);
+    if (e != hipSuccess) return hip_status(e, "indexer score");
     e = csa2::launch_select_small(scores, sstride, nullptr, 0, 0, n_entries, B, max_n, k, topk, k, stream);
     return hip_status(e, "indexer select");
   }
+  if (pool_k == 0 && k <= csa2::kDirectMaxK) {
+    e = score(csa2::SEL_DIRECT, k);
+    if (e != hipSuccess) return hip_status(e, "indexer score");
+    e = csa2::launch_finish(csa2::SEL_DIRECT, n_entries, B, max_n, scores, sstride, sb, k, topk, k, stream);
+    return hip_status(e, "indexer select");
+  }
+  const int K1 = pool_k > 0 ? pool_k : k;
   int32_t* first_out = pool_k > 0 ? pool : topk;
-  e = csa2::launch_select(scores, sstride, n_entries, B, max_n, ctrl, bitmap, L.bm_words, cbuf, L.slots, K1,
-                          first_out, K1, stream);
+  e = score(csa2::SEL_THRESHOLD, K1);
+  if (e != hipSuccess) return hip_status(e, "indexer score");
+  e = csa2::launch_finish(csa2::SEL_THRESHOLD, n_entries, B, max_n, scores, sstride, sb, K1, nullptr, 0, stream);
+  if (e != hipSuccess) return hip_status(e, "indexer threshold");
+  e = csa2::launch_select(scores, sstride, n_entries, B, max_n, sb.ctrl, sb.bitmap, L.bm_words, cbuf, L.slots,
+                          K1, first_out, K1, stream);
   if (e != hipSuccess) return hip_status(e, "indexer select");
   if (pool_k > 0) {
     e = csa2::launch_select_small(scores, sstride, pool, pool_k, 1, n_entries, B, max_n, k, topk, k, stream);

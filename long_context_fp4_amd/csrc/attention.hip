@@ -119,42 +119,57 @@ __global__ __launch_bounds__(AT_THREADS) void attention_kernel(
   const int64_t row_base = entry_offset[b];
   const int32_t* ib = idx + (int64_t)b * k;
   uint8_t* wlds = smem + wave * AT_WAVE_LDS;
-
   f32x4_t O[32];
 #pragma unroll
   for (int t = 0; t < 32; ++t) O[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   float m_ref = -INFINITY, l_run = 0.0f;
 
-  for (int tile = wave; tile < ntiles; tile += 4) {
-    const int ent = e_lo + 16 * tile + r;        // this lane gathers entry r of the tile
-    int64_t pos = -1;
-    if (ent < e_hi) pos = ib[ent];
-    const bool valid = pos >= 0 && pos < nb;
-    u32x4_t cw[4] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};
-    u32x2_t sw = {0, 0};
-    if (valid) {
-      const uint8_t* row = kv + (row_base + pos) * 288;
+  // Tiles of this wave: wave, wave + 4, ... Software pipeline: the index of the
+  // tile two steps ahead and the rows of the next tile are in flight while the
+  // current tile is computed. Loads are unconditional (an invalid entry reads
+  // row 0 of the sequence and is masked), so they never wait on a branch.
+  const bool any_rows = nb > 0;
+  auto idx_of = [&](int tile) -> int {
+    const int ent = e_lo + 16 * tile + r;
+    return (tile < ntiles && ent < e_hi) ? ib[ent] : -1;
+  };
+  auto rowp = [&](int p) -> const uint8_t* {
+    const int64_t pc = (p >= 0 && p < nb) ? p : 0;
+    return kv + (row_base + pc) * 288;
+  };
+  int pA = idx_of(wave), pB = idx_of(wave + 4);
+  u32x4_t cw[4] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};
+  u32x2_t sw = {0, 0};
+  if (any_rows && wave < ntiles) {
+    const uint8_t* row = rowp(pA);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) cw[c] = *(const u32x4_t*)(row + 64 * kg + 16 * c);
-      sw = *(const u32x2_t*)(row + 256 + 8 * kg);
+    for (int c = 0; c < 4; ++c) cw[c] = *(const u32x4_t*)(row + 64 * kg + 16 * c);
+    sw = *(const u32x2_t*)(row + 256 + 8 * kg);
+  }
+
+  for (int tile = wave; tile < ntiles; tile += 4) {
+    const int pC = idx_of(tile + 8);
+    u32x4_t cwn[4] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};
+    u32x2_t swn = {0, 0};
+    if (any_rows && tile + 4 < ntiles) {
+      const uint8_t* row = rowp(pB);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) cwn[c] = *(const u32x4_t*)(row + 64 * kg + 16 * c);
+      swn = *(const u32x2_t*)(row + 256 + 8 * kg);
     }
+    const bool valid = pA >= 0 && pA < nb;
     const uint64_t vmask = __ballot(valid);
 
-    // dequantize 128 dims (128kg .. 128kg+127) to fp16: A operands of QK
-    f16x8_t ca[16];
+    // dequantize 128 dims (128kg .. 128kg+127) to fp16, feed QK and copy the tile
+    // to the wave's LDS area (row = entry r); logits^T: rows = entries, columns = heads
+    f32x4_t lg = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const uint32_t sbyte = (sw[j >> 3] >> (8 * ((j >> 1) & 3))) & 0xFFu;
-      ca[j] = dequant_latent8(cw[j >> 2][j & 3], scale_pair(sbyte));
+      const f16x8_t ca = dequant_latent8(cw[j >> 2][j & 3], scale_pair(sbyte));
+      lg = __builtin_amdgcn_mfma_f32_16x16x32_f16(ca, qb[j], lg, 0, 0, 0);
+      *(f16x8_t*)(wlds + r * AT_PITCH + 256 * kg + 16 * j) = ca;
     }
-    // logits^T: rows = entries (A), columns = heads (B)
-    f32x4_t lg = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int j = 0; j < 16; ++j) lg = __builtin_amdgcn_mfma_f32_16x16x32_f16(ca[j], qb[j], lg, 0, 0, 0);
-
-    // copy the tile to the wave's LDS area (row = entry r)
-#pragma unroll
-    for (int j = 0; j < 16; ++j) *(f16x8_t*)(wlds + r * AT_PITCH + 256 * kg + 16 * j) = ca[j];
 
     // online softmax for head r; this lane holds entries 4kg + i of the tile
     float x[4];
@@ -205,6 +220,11 @@ __global__ __launch_bounds__(AT_THREADS) void attention_kernel(
       O[2 * u + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(a1, pb, O[2 * u + 1], 0, 0, 0);
     }
     __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int c = 0; c < 4; ++c) cw[c] = cwn[c];
+    sw = swn;
+    pA = pB;
+    pB = pC;
   }
 
   // --- merge the 4 waves: per head max, weights, then pairwise sums of O in LDS

@@ -13,39 +13,56 @@
 // Kernels
 // -------
 // score_kernel   streams the packed MXFP4 keys (one 16-byte load of codes and
-//                one scale byte per lane), dequantizes them in registers with
-//                the gfx950 scaled FP4->bf16 conversion (exact: an E2M1 value
-//                times a power of two fits bf16), and contracts 16 entries x 16
-//                heads x 32 channels per v_mfma_f32_16x16x32_bf16. The head sum
-//                is a 4-term in-lane sum plus two cross-lane steps. Each
-//                workgroup also builds a 4096-bin LDS histogram of its score
-//                keys and adds it into a per-sequence histogram; the last
-//                workgroup of a sequence to finish finds the bin that holds the
-//                K-th best key.
-// select_kernel  (long sequences) marks every position whose key lies above
-//                that bin in a per-sequence bitmap and appends the ones inside
-//                it as (key, position) candidates; the last workgroup of the
-//                sequence radix-selects the missing ones among the candidates,
-//                then compacts the bitmap into ascending positions.
+//                one scale byte per lane, several tiles in flight), dequantizes
+//                them in registers with the gfx950 scaled FP4->bf16 conversion
+//                (exact: an E2M1 value times a power of two fits bf16), and
+//                contracts 16 entries x 16 heads x 32 channels per
+//                v_mfma_f32_16x16x32_bf16; the head sum is a 4-term in-lane sum
+//                plus two VALU lane swaps. Scores are staged in LDS and written
+//                with coalesced 16-byte stores.
+//                Selection without contended atomics: each workgroup builds an
+//                LDS histogram of its 1024 score keys, picks a local cutoff bin
+//                that keeps about four times its expected share of the top-k,
+//                and writes to its own slot the (bin, count) pairs above that
+//                cutoff (and, for k <= 512, the candidates themselves). The last
+//                workgroup of a sequence merges the slots: bins at or above the
+//                highest cutoff are complete, so the bin holding the k-th best
+//                key follows exactly whenever it lies there (otherwise it falls
+//                back to a full histogram of the sequence's scores). For
+//                k <= 512 it then radix-selects the k best among the gathered
+//                candidates and writes them in ascending order; larger k (the
+//                hierarchical pool) go on to select_kernel.
+// select_kernel  (large k) marks every position whose key lies above that bin
+//                in a per-sequence bitmap and appends the ones inside it as
+//                (key, position) candidates; the last workgroup of the sequence
+//                radix-selects the missing ones among the candidates, then
+//                compacts the bitmap into ascending positions.
 // select_small_kernel  one workgroup per sequence for at most 16384 slots
 //                (the pool, a Reindex candidate list or a short sequence):
 //                keys in LDS, 8-bit radix select on (key, slot), bitmap
 //                compaction in slot order.
-// The per-sequence control block (state + histogram, at a fixed place in the
+// The per-sequence control block (counters, at a fixed place in the
 // workspace) is left zero by the last workgroups; bitmap words are cleared by
-// the score pass before use.
+// the score pass before use; every other workspace region is rewritten before
+// it is read.
 #include "device.h"
 #include "kernels.h"
 
 namespace csa2 {
 
 constexpr int SC_THREADS = 256;
-constexpr int SC_CHUNK = 1024;      // slots per score workgroup
+constexpr int SC_CHUNK = kScoreChunk;   // slots per score workgroup
+
 constexpr int SC_UNROLL = 4;        // tiles in flight per wave
 constexpr int NBINS = 4096;         // histogram over the top 12 bits of the key
 constexpr int BIN_SHIFT = 20;
+constexpr int SUM_PAIRS = kSumWords;   // (bin, count) pairs a workgroup reports above its cutoff
+constexpr int CAND_CAP = kCandCap;     // candidates a workgroup reports in direct top-k mode
+
+constexpr int LAST_LDS_CANDS = (NBINS + SC_CHUNK) / 2;   // u64 candidates the last workgroup keeps in LDS
 constexpr int SEL_THREADS = 256;
 constexpr int SEL_CHUNK = 4096;     // slots per select workgroup
+constexpr int SEL_LDS_CAP = 4096;   // candidates staged in LDS by the last select workgroup
 constexpr int SMALL_THREADS = 1024;
 constexpr int SMALL_MAX = 16384;
 
@@ -79,7 +96,7 @@ __device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* tmp, uint32_t* to
   return r;
 }
 
-// ---------------------------------------------------------------- score kernel
+// ---------------------------------------------------------------- scoring helpers
 __device__ __forceinline__ bf16x8_t dequant_mx_block8(uint32_t dw, float scale) {
   bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, scale, 0);
   bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, scale, 1);
@@ -88,159 +105,29 @@ __device__ __forceinline__ bf16x8_t dequant_mx_block8(uint32_t dw, float scale) 
   return bf16x8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
-__global__ __launch_bounds__(SC_THREADS) void score_kernel(
-    const uint8_t* __restrict__ ik, const uint8_t* __restrict__ iks,
-    const int64_t* __restrict__ entry_offset, const int32_t* __restrict__ n_entries, int64_t max_n,
-    const uint16_t* __restrict__ q_idx, const float* __restrict__ w, int Hi, int mode,
-    const int32_t* __restrict__ cand, int cand_stride,
-    float* __restrict__ scores, int64_t sstride,
-    uint8_t* __restrict__ ctrl, uint32_t* __restrict__ bitmap, int64_t bm_stride, int K) {
-  __shared__ uint32_t lhist[NBINS];
-  __shared__ uint32_t scan_tmp[SC_THREADS / 64 + 1];
-  __shared__ int s_last;
-
-  const int b = blockIdx.y;
-  const int64_t n_pos = min((int64_t)n_entries[b], max_n);
-  const int64_t nslots = cand ? (int64_t)cand_stride : n_pos;
-  const int64_t start = (int64_t)blockIdx.x * SC_CHUNK;
-  if (start >= nslots) return;
-  const int64_t end = min(start + (int64_t)SC_CHUNK, nslots);
-  const bool do_hist = ctrl != nullptr;
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n = lane & 15, g = lane >> 4;
-  if (do_hist) {
-    for (int i = tid; i < NBINS; i += SC_THREADS) lhist[i] = 0;
-    // the select pass ORs into the bitmap words of this chunk: clear them here
-    uint32_t* bm = bitmap + (int64_t)b * bm_stride;
-    for (int64_t wd = start / 32 + tid; wd < (end + 31) / 32; wd += SC_THREADS) bm[wd] = 0;
-  }
-
-  // A operand: q[head = n][channels 32g + 8j .. +7] for MFMA j
-  bf16x8_t qa[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    u32x4_t v = {0, 0, 0, 0};
-    if (n < Hi) v = *(const u32x4_t*)(q_idx + ((int64_t)b * Hi + n) * 128 + 32 * g + 8 * j);
-    __builtin_memcpy(&qa[j], &v, 16);
-  }
-  // head weights of this lane's output rows (heads 4g + i)
-  float wr[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int hh = 4 * g + i;
-    wr[i] = hh < Hi ? (w ? w[(int64_t)b * Hi + hh] : 1.0f) : 0.0f;
-  }
-  const int64_t row_base = entry_offset[b];
-  float* srow = scores + (int64_t)b * sstride;
-  if (do_hist) __syncthreads();
-
-  for (int64_t t0 = start + 16 * wave; t0 < end; t0 += 16 * 4 * SC_UNROLL) {
-    u32x4_t codes[SC_UNROLL];
-    float scl[SC_UNROLL];
-    bool ok[SC_UNROLL];
-    int64_t slot[SC_UNROLL];
-#pragma unroll
-    for (int u = 0; u < SC_UNROLL; ++u) {
-      slot[u] = t0 + 64 * u + n;
-      const bool in = slot[u] < end;
-      int64_t pos = slot[u];
-      if (cand) pos = in ? (int64_t)cand[(int64_t)b * cand_stride + slot[u]] : -1;
-      ok[u] = in && pos >= 0 && pos < n_pos;
-      codes[u] = u32x4_t{0, 0, 0, 0};
-      scl[u] = 0.0f;
-      if (ok[u]) {
-        const int64_t row = row_base + pos;
-        codes[u] = __builtin_nontemporal_load((const u32x4_t*)(ik + row * 64 + 16 * g));
-        scl[u] = __uint_as_float((uint32_t)iks[row * 4 + g] << 23);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < SC_UNROLL; ++u) {
-      f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        bf16x8_t kb = dequant_mx_block8(codes[u][j], scl[u]);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[j], kb, acc, 0, 0, 0);
-      }
-      float s;
-      if (mode == 0) {
-        s = acc[0];                       // head 0 is row 0, held by lanes 0..15
-      } else {
-        s = wr[0] * fmaxf(acc[0], 0.0f) + wr[1] * fmaxf(acc[1], 0.0f) +
-            wr[2] * fmaxf(acc[2], 0.0f) + wr[3] * fmaxf(acc[3], 0.0f);
-        s += shfl_xor_f(s, 16);
-        s += shfl_xor_f(s, 32);
-      }
-      if (g == 0 && ok[u]) {
-        srow[slot[u]] = s;
-        if (do_hist) atomicAdd(&lhist[score_key(s) >> BIN_SHIFT], 1u);
-      }
-    }
-  }
-  if (!do_hist) return;
-
-  __syncthreads();
-  SelState* st = ctrl_state(ctrl, b);
-  uint32_t* gh = ctrl_hist(ctrl, b);
-  for (int i = tid; i < NBINS; i += SC_THREADS) {
-    const uint32_t v = lhist[i];
-    if (v) atomicAdd(&gh[i], v);
-  }
-  __syncthreads();
-  if (tid == 0) {
-    __threadfence();
-    const uint32_t nblk = (uint32_t)((nslots + SC_CHUNK - 1) / SC_CHUNK);
-    s_last = atomicAdd(&st->done_score, 1u) == nblk - 1;
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-
-  // last workgroup of sequence b: find the bin holding the K-th best key.
-  // Thread t owns bins NBINS-1-16t down to NBINS-16-16t (best bins first).
-  uint32_t hv[16], local = 0;
-#pragma unroll
-  for (int q = 0; q < 16; ++q) {
-    const int bin = NBINS - 1 - (16 * tid + q);
-    hv[q] = __hip_atomic_load(&gh[bin], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    local += hv[q];
-    gh[bin] = 0;
-  }
-  uint32_t total;
-  const uint32_t prefix = block_exclusive_scan(local, scan_tmp, &total);
-  if (total <= (uint32_t)K) {
-    if (tid == 0) { st->thr_bin = -1; st->above = 0; }
-  } else if (prefix < (uint32_t)K && prefix + local >= (uint32_t)K) {
-    uint32_t cum = prefix;
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      if (cum + hv[q] >= (uint32_t)K) {
-        st->thr_bin = NBINS - 1 - (16 * tid + q);
-        st->above = cum;
-        break;
-      }
-      cum += hv[q];
-    }
-  }
-  if (tid == 0) st->done_score = 0;
+// Sum of v over the four lanes l, l^16, l^32, l^48 (VALU lane swaps, no LDS).
+__device__ __forceinline__ float sum_lane_groups(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const float t = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  const auto r2 = __builtin_amdgcn_permlane16_swap(__float_as_uint(t), __float_as_uint(t), false, false);
+  return __uint_as_float(r2[0]) + __uint_as_float(r2[1]);
 }
 
 // ---------------------------------------------------------------- radix select
-// Among n distinct 64-bit composites at `v` (global memory written by other
-// workgroups of the same launch, read through agent-scope atomic loads),
-// find the `need` largest (0 < need < n). On return every composite c with
-// (c >> *shift_out) >= (*prefix_out >> *shift_out) is selected, and exactly
-// `need` composites qualify. All threads of the workgroup must call it.
+// Among n distinct 64-bit composites at `v` (LDS, or global memory read after
+// an acquire fence), find the `need` largest (0 < need < n); all composites
+// agree on the bits above top_shift + 7. On return the composites c with
+// (c & *mask_out) >= *prefix_out are exactly the `need` largest. All threads of
+// the workgroup must call it.
 __device__ void radix_select_u64(const uint64_t* v, uint32_t n, uint32_t need, int top_shift,
-                                 uint32_t* h, uint32_t* ctl, uint64_t* prefix_out, int* shift_out) {
+                                 uint32_t* h, uint32_t* ctl, uint64_t* prefix_out, uint64_t* mask_out) {
   uint64_t prefix = 0, pmask = 0;
   int shift = top_shift;
   for (;;) {
     for (int i = threadIdx.x; i < 256; i += blockDim.x) h[i] = 0;
     __syncthreads();
     for (uint32_t i = threadIdx.x; i < n; i += blockDim.x) {
-      const uint64_t c = __hip_atomic_load(v + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint64_t c = v[i];
       if ((c & pmask) == prefix) atomicAdd(&h[(uint32_t)(c >> shift) & 255u], 1u);
     }
     __syncthreads();
@@ -277,61 +164,426 @@ __device__ void radix_select_u64(const uint64_t* v, uint32_t n, uint32_t need, i
     pmask |= (uint64_t)255 << shift;
     need -= above;
     if (cnt == need || shift == 0) break;
-    shift -= 8;
+    shift = shift >= 8 ? shift - 8 : 0;     // the last digit may overlap resolved bits
   }
   *prefix_out = prefix;
-  *shift_out = shift;
+  *mask_out = pmask;
 }
 
-// Ascending compaction of a bitmap of nbits bits into out[0..cnt), -1 padding up to K.
-// kGlobal: the bitmap lives in global memory and was filled by other workgroups
-// of the same launch; it is read through agent-scope atomic loads.
-template <bool kGlobal>
-__device__ void compact_bitmap(uint32_t* bm, int64_t nbits, const int32_t* slot_pos, int K,
-                               int32_t* out, uint32_t* scan_tmp) {
+// Ascending compaction of a bitmap of nbits bits into out[0..cnt), -1 padding up
+// to K. The bitmap is read in chunks of `stage_words` words into the LDS buffer
+// `stage` with independent coalesced loads; a global bitmap filled by other
+// workgroups of the launch is read after the caller's acquire fence.
+__device__ void compact_bitmap(const uint32_t* bm, int64_t nbits, const int32_t* slot_pos, int K,
+                               int32_t* out, uint32_t* scan_tmp, uint32_t* stage, int stage_words) {
   const int64_t nwords = (nbits + 31) / 32;
   const int nt = blockDim.x;
-  const int64_t per = (nwords + nt - 1) / nt;
-  const int64_t w0 = min((int64_t)threadIdx.x * per, nwords), w1 = min(w0 + per, nwords);
-  uint32_t cnt = 0;
-  auto rd = [&](int64_t i) -> uint32_t {
-    if (kGlobal) return __hip_atomic_load(bm + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return bm[i];
-  };
-  for (int64_t i = w0; i < w1; ++i) cnt += __popc(rd(i));
+  uint32_t base = 0;                     // positions written by the previous chunks
+  for (int64_t c0 = 0; c0 < nwords; c0 += stage_words) {
+    const int cw = (int)min((int64_t)stage_words, nwords - c0);
+#pragma unroll 8
+    for (int i = threadIdx.x; i < cw; i += nt) stage[i] = bm[c0 + i];
+    __syncthreads();
+    const int per = (cw + nt - 1) / nt;
+    const int w0 = min((int)threadIdx.x * per, cw), w1 = min(w0 + per, cw);
+    uint32_t cnt = 0;
+    for (int i = w0; i < w1; ++i) cnt += __popc(stage[i]);
+    uint32_t total;
+    uint32_t off = base + block_exclusive_scan(cnt, scan_tmp, &total);
+    for (int i = w0; i < w1; ++i) {
+      uint32_t word = stage[i];
+      while (word) {
+        const int bit = __ffs(word) - 1;
+        word &= word - 1;
+        const int64_t slot = (c0 + i) * 32 + bit;
+        if (off < (uint32_t)K) out[off] = slot_pos ? slot_pos[slot] : (int32_t)slot;
+        ++off;
+      }
+    }
+    base += total;
+    __syncthreads();
+  }
+  for (int64_t j = (int64_t)base + threadIdx.x; j < K; j += nt) out[j] = -1;
+}
+
+// ---------------------------------------------------------------- score kernel
+
+
+__device__ __forceinline__ uint64_t composite(uint32_t key, uint32_t pos) {
+  return ((uint64_t)key << 32) | (uint64_t)(0xFFFFFFFFu - pos);
+}
+
+// Block-wide max / or of one value per thread (blockDim.x == SC_THREADS).
+__device__ uint32_t block_max_u32(uint32_t v, uint32_t* tmp) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, d, 64));
+  if ((threadIdx.x & 63) == 0) tmp[threadIdx.x >> 6] = v;
+  __syncthreads();
+  uint32_t r = tmp[0];
+  for (int i = 1; i < SC_THREADS / 64; ++i) r = max(r, tmp[i]);
+  __syncthreads();
+  return r;
+}
+__device__ uint32_t block_or_u32(uint32_t v, uint32_t* tmp) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v |= (uint32_t)__shfl_xor((int)v, d, 64);
+  if ((threadIdx.x & 63) == 0) tmp[threadIdx.x >> 6] = v;
+  __syncthreads();
+  uint32_t r = 0;
+  for (int i = 0; i < SC_THREADS / 64; ++i) r |= tmp[i];
+  __syncthreads();
+  return r;
+}
+
+// Bin holding the `need`-th best key of an LDS histogram (thread t owns bins
+// NBINS-1-16t .. NBINS-16-16t). Returns the number of keys counted in *total,
+// the bin in ctl[0] and the count strictly above it in ctl[1] (ctl[0] = -1
+// when total < need). All threads must call it.
+__device__ void hist_kth_bin(const uint32_t* lhist, uint32_t need, uint32_t* scan_tmp, uint32_t* ctl,
+                             uint32_t* total_out) {
+  uint32_t hv[16], local = 0;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    hv[q] = lhist[NBINS - 1 - (16 * threadIdx.x + q)];
+    local += hv[q];
+  }
+  if (threadIdx.x == 0) { ctl[0] = 0xFFFFFFFFu; ctl[1] = 0; }
   uint32_t total;
-  uint32_t off = block_exclusive_scan(cnt, scan_tmp, &total);
-  for (int64_t i = w0; i < w1; ++i) {
-    uint32_t word = rd(i);
-    while (word) {
-      const int bit = __ffs(word) - 1;
-      word &= word - 1;
-      const int64_t slot = i * 32 + bit;
-      if (off < (uint32_t)K) out[off] = slot_pos ? slot_pos[slot] : (int32_t)slot;
-      ++off;
+  const uint32_t prefix = block_exclusive_scan(local, scan_tmp, &total);
+  if (prefix < need && prefix + local >= need) {
+    uint32_t cum = prefix;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      if (cum + hv[q] >= need) {
+        ctl[0] = NBINS - 1 - (16 * threadIdx.x + q);
+        ctl[1] = cum;
+        break;
+      }
+      cum += hv[q];
     }
   }
-  for (int64_t j = (int64_t)total + threadIdx.x; j < K; j += nt) out[j] = -1;
+  __syncthreads();
+  *total_out = total;
+}
+
+// CAND: score the listed positions (Reindex) instead of every entry.
+// SEL: SEL_NONE (scores only); SEL_THRESHOLD / SEL_DIRECT (also report the
+//      local cutoff summary, and for SEL_DIRECT the candidates, that
+//      finish_kernel turns into the threshold bin or the final top-K).
+// MODE: 0 = dot product of head 0, 1 = sum_h w_h * ReLU(q_h . k).
+template <bool CAND, int SEL, int MODE>
+__global__ __launch_bounds__(SC_THREADS) void score_kernel(
+    const uint8_t* __restrict__ ik, const uint8_t* __restrict__ iks,
+    const int64_t* __restrict__ entry_offset, const int32_t* __restrict__ n_entries, int64_t max_n,
+    const uint16_t* __restrict__ q_idx, const float* __restrict__ w, int Hi,
+    const int32_t* __restrict__ cand, int cand_stride,
+    float* __restrict__ scores, int64_t sstride, SelBufs sb, int K) {
+  __shared__ uint32_t lbuf[NBINS + SC_CHUNK];     // histogram + staged scores
+  __shared__ uint32_t scan_tmp[SC_THREADS / 64 + 1];
+  __shared__ uint32_t ctl[8];
+  uint32_t* lhist = lbuf;
+  float* lsc = (float*)(lbuf + NBINS);
+
+  const int b = blockIdx.y;
+  const int64_t n_pos = min((int64_t)n_entries[b], max_n);
+  const int64_t nslots = CAND ? (int64_t)cand_stride : n_pos;
+  const int64_t start = (int64_t)blockIdx.x * SC_CHUNK;
+  if (start >= nslots) return;
+  if (CAND && n_pos <= 0) return;                  // no listed position can be valid
+  const int end = (int)min((int64_t)SC_CHUNK, nslots - start);   // slots of this workgroup
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  if (SEL != SEL_NONE) {
+    for (int i = tid; i < NBINS; i += SC_THREADS) lhist[i] = 0;
+    // the selection ORs into the bitmap words of this chunk: clear them here
+    uint32_t* bm = sb.bitmap + (int64_t)b * sb.bm_stride;
+    for (int64_t wd = start / 32 + tid; wd < (start + end + 31) / 32; wd += SC_THREADS) bm[wd] = 0;
+  }
+
+  // A operand: q[head = n][channels 32g + 8j .. +7] for MFMA j
+  bf16x8_t qa[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    u32x4_t v = {0, 0, 0, 0};
+    if (n < Hi) v = *(const u32x4_t*)(q_idx + ((int64_t)b * Hi + n) * 128 + 32 * g + 8 * j);
+    __builtin_memcpy(&qa[j], &v, 16);
+  }
+  // head weights of this lane's output rows (heads 4g + i)
+  float wr[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int hh = 4 * g + i;
+    wr[i] = hh < Hi ? (w ? w[(int64_t)b * Hi + hh] : 1.0f) : 0.0f;
+  }
+  const int64_t row_base = entry_offset[b];
+  const uint8_t* ikb = ik + row_base * 64 + 16 * g;     // this lane's 16-byte block of row 0
+  const uint8_t* iksb = iks + row_base * 4 + g;
+  const int32_t* crow = CAND ? cand + (int64_t)b * cand_stride + start : nullptr;
+
+  // each wave takes tiles of 16 slots; SC_UNROLL tiles are loaded before any is used.
+  // Loads are unconditional (invalid slots read row 0 of the sequence) so that the
+  // compiler issues them all ahead of the first wait.
+  for (int t0 = 16 * wave; t0 < end; t0 += 64 * SC_UNROLL) {
+    int pos[SC_UNROLL];
+    bool ok[SC_UNROLL];
+    if (CAND) {
+      int cv[SC_UNROLL];
+#pragma unroll
+      for (int u = 0; u < SC_UNROLL; ++u) cv[u] = crow[min(t0 + 64 * u + n, end - 1)];
+#pragma unroll
+      for (int u = 0; u < SC_UNROLL; ++u) {
+        ok[u] = (t0 + 64 * u + n < end) && cv[u] >= 0 && cv[u] < n_pos;
+        pos[u] = ok[u] ? cv[u] : 0;
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < SC_UNROLL; ++u) {
+        const int ls = t0 + 64 * u + n;
+        ok[u] = ls < end;
+        pos[u] = ok[u] ? (int)(start + ls) : 0;
+      }
+    }
+    u32x4_t codes[SC_UNROLL];
+    uint32_t sbyte[SC_UNROLL];
+#pragma unroll
+    for (int u = 0; u < SC_UNROLL; ++u) {
+      codes[u] = __builtin_nontemporal_load((const u32x4_t*)(ikb + (int64_t)pos[u] * 64));
+      sbyte[u] = iksb[(int64_t)pos[u] * 4];
+    }
+#pragma unroll
+    for (int u = 0; u < SC_UNROLL; ++u) {
+      const float scl = __uint_as_float(sbyte[u] << 23);
+      f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        bf16x8_t kb = dequant_mx_block8(codes[u][j], scl);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[j], kb, acc, 0, 0, 0);
+      }
+      float sc;
+      if (MODE == 0) {
+        sc = acc[0];                       // head 0 is row 0, held by lanes 0..15
+      } else {
+        sc = wr[0] * fmaxf(acc[0], 0.0f) + wr[1] * fmaxf(acc[1], 0.0f) +
+             wr[2] * fmaxf(acc[2], 0.0f) + wr[3] * fmaxf(acc[3], 0.0f);
+        sc = sum_lane_groups(sc);
+      }
+      const int ls = t0 + 64 * u + n;
+      if (g == 0 && ls < end) lsc[ls] = ok[u] ? sc : 0.0f;
+    }
+  }
+  __syncthreads();
+  // coalesced store of the chunk's scores (slots of invalid candidates hold 0)
+  {
+    float* srow = scores + (int64_t)b * sstride + start;
+    const int i4 = 4 * tid;
+    if (i4 + 3 < end && (((uintptr_t)(srow + i4)) & 15) == 0) {
+      *(float4*)(srow + i4) = *(const float4*)(lsc + i4);
+    } else {
+      for (int i = i4; i < min(i4 + 4, end); ++i) srow[i] = lsc[i];
+    }
+  }
+  if (SEL == SEL_NONE) return;
+
+  // ---- local histogram and cutoff (every slot of a Full pass is a valid position)
+  for (int i = tid; i < end; i += SC_THREADS) atomicAdd(&lhist[score_key(lsc[i]) >> BIN_SHIFT], 1u);
+  __syncthreads();
+  const int64_t budget64 = 4 * (((int64_t)K * SC_CHUNK + n_pos - 1) / n_pos) + 32;
+  const uint32_t budget = (uint32_t)min(budget64, (int64_t)end);
+  uint32_t cnt_all;
+  hist_kth_bin(lhist, budget, scan_tmp, ctl, &cnt_all);
+  const uint32_t cut = (ctl[0] == 0xFFFFFFFFu) ? 0u : ctl[0];   // fewer keys than the budget: keep all
+  SelState* st = ctrl_state(sb.ctrl, b);
+  // (bin, count) pairs for bins >= cut, appended to the sequence's pair list
+  {
+    uint32_t np = 0;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const uint32_t bin = NBINS - 1 - (16 * tid + q);
+      np += (bin >= cut && lhist[bin] != 0) ? 1u : 0u;
+    }
+    uint32_t tot;
+    uint32_t off = block_exclusive_scan(np, scan_tmp, &tot);
+    const uint32_t keep = min(tot, (uint32_t)SUM_PAIRS);
+    if (tid == 0) {
+      ctl[2] = atomicAdd(&st->npairs, keep);
+      atomicMax(&st->cut_max, cut);
+      if (tot > SUM_PAIRS) atomicOr(&st->flags, 1u);
+    }
+    __syncthreads();
+    uint32_t* pl = sb.summ + (int64_t)b * sb.summ_stride + ctl[2];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const uint32_t bin = NBINS - 1 - (16 * tid + q);
+      const uint32_t c = lhist[bin];
+      if (bin >= cut && c != 0) {
+        if (off < keep) pl[off] = (bin << 16) | c;
+        ++off;
+      }
+    }
+  }
+  if (SEL == SEL_DIRECT) {
+    // this chunk's candidates (every slot whose key bin is >= cut), appended to the sequence's list
+    uint32_t nc = 0;
+    for (int i = tid; i < end; i += SC_THREADS) nc += (score_key(lsc[i]) >> BIN_SHIFT) >= cut ? 1u : 0u;
+    uint32_t tot;
+    uint32_t off = block_exclusive_scan(nc, scan_tmp, &tot);
+    const uint32_t keep = min(tot, (uint32_t)CAND_CAP);
+    if (tid == 0) {
+      ctl[3] = atomicAdd(&st->nsc, keep);
+      if (tot > CAND_CAP) atomicOr(&st->flags, 2u);
+    }
+    __syncthreads();
+    uint64_t* wc = sb.wgc + (int64_t)b * sb.wgc_stride + ctl[3];
+    for (int i = tid; i < end; i += SC_THREADS) {
+      const uint32_t key = score_key(lsc[i]);
+      if ((key >> BIN_SHIFT) >= cut) {
+        if (off < keep) wc[off] = composite(key, (uint32_t)(start + i));
+        ++off;
+      }
+    }
+  }
+
+}
+
+// ---------------------------------------------------------------- finish (one workgroup per sequence)
+// Runs after the score pass: merges the sequence's (bin, count) pairs, finds
+// the bin of the K-th best key (exactly, or from a full histogram of the
+// sequence's scores when the reported bins do not reach it), then either hands
+// the bin to select_kernel (SEL_THRESHOLD) or selects the K best among the
+// gathered candidates and writes them in ascending order (SEL_DIRECT).
+template <int SEL>
+__global__ __launch_bounds__(SC_THREADS) void finish_kernel(
+    const int32_t* __restrict__ n_entries, int64_t max_n, const float* __restrict__ scores, int64_t sstride,
+    SelBufs sb, int K, int32_t* __restrict__ out, int out_stride) {
+  __shared__ uint32_t lbuf[NBINS + SC_CHUNK];     // histogram; candidates and bitmap staging later
+  __shared__ uint32_t hsel[256];
+  __shared__ uint32_t scan_tmp[SC_THREADS / 64 + 1];
+  __shared__ uint32_t ctl[8];
+  uint32_t* lhist = lbuf;
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int64_t n_pos = min((int64_t)n_entries[b], max_n);
+  SelState* st = ctrl_state(sb.ctrl, b);
+  const float* sall = scores + (int64_t)b * sstride;
+  int32_t* ob = out ? out + (int64_t)b * out_stride : nullptr;
+  uint32_t* bm = sb.bitmap + (int64_t)b * sb.bm_stride;
+  const uint32_t bmax = st->cut_max, flags = st->flags, npairs = st->npairs, nsc = st->nsc;
+  __syncthreads();
+  if (tid == 0) { st->cut_max = 0; st->flags = 0; st->npairs = 0; st->nsc = 0; }
+
+  if (n_pos <= K) {                       // every position is selected (or none exists)
+    if (SEL == SEL_THRESHOLD) {
+      if (tid == 0) { st->thr_bin = -1; st->above = 0; }
+    } else {
+      for (int j = tid; j < K; j += SC_THREADS) ob[j] = j < n_pos ? j : -1;
+    }
+    return;
+  }
+  // merge the complete bins (>= bmax) of the pair list
+  for (int i = tid; i < NBINS; i += SC_THREADS) lhist[i] = 0;
+  __syncthreads();
+  {
+    const uint32_t* pl = sb.summ + (int64_t)b * sb.summ_stride;
+    for (uint32_t i = tid; i < npairs; i += SC_THREADS) {
+      const uint32_t v = pl[i];
+      if ((v >> 16) >= bmax) atomicAdd(&lhist[v >> 16], v & 0xFFFFu);
+    }
+  }
+  __syncthreads();
+  uint32_t tot_hi;
+  hist_kth_bin(lhist, (uint32_t)K, scan_tmp, ctl, &tot_hi);
+  const bool exact = (flags & 1u) == 0 && ctl[0] != 0xFFFFFFFFu;
+  uint32_t T = ctl[0], above = ctl[1];
+  if (!exact) {
+    // fallback: histogram of every score of the sequence
+    __syncthreads();
+    for (int i = tid; i < NBINS; i += SC_THREADS) lhist[i] = 0;
+    __syncthreads();
+    for (int64_t i = tid; i < n_pos; i += SC_THREADS) atomicAdd(&lhist[score_key(sall[i]) >> BIN_SHIFT], 1u);
+    __syncthreads();
+    hist_kth_bin(lhist, (uint32_t)K, scan_tmp, ctl, &tot_hi);
+    T = ctl[0];
+    above = ctl[1];
+  }
+  if (SEL == SEL_THRESHOLD) {
+    if (tid == 0) { st->thr_bin = (int32_t)T; st->above = above; }
+    return;
+  }
+
+  // SEL_DIRECT: gather every key with bin >= T (the K best are among them)
+  __syncthreads();
+  uint64_t* lc = (uint64_t*)lbuf;
+  uint64_t* gs = sb.gscr + (int64_t)b * sb.gscr_stride;
+  if (tid == 0) ctl[4] = 0;
+  __syncthreads();
+  const bool from_list = exact && (flags & 2u) == 0;
+  if (from_list) {
+    // eight independent loads per thread in flight, then the filter
+    const uint64_t* wc = sb.wgc + (int64_t)b * sb.wgc_stride;
+    for (uint32_t base = 0; base < nsc; base += 8 * SC_THREADS) {
+      uint64_t cv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t i = base + j * SC_THREADS + tid;
+        cv[j] = i < nsc ? wc[i] : 0ull;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t i = base + j * SC_THREADS + tid;
+        if (i < nsc && (uint32_t)(cv[j] >> (32 + BIN_SHIFT)) >= T) {
+          const uint32_t at = atomicAdd(&ctl[4], 1u);
+          if (at < LAST_LDS_CANDS) lc[at] = cv[j];
+          gs[at] = cv[j];
+        }
+      }
+    }
+  } else {
+    for (int64_t i = tid; i < n_pos; i += SC_THREADS) {
+      const uint32_t key = score_key(sall[i]);
+      if ((key >> BIN_SHIFT) >= T) {
+        const uint32_t at = atomicAdd(&ctl[4], 1u);
+        const uint64_t c = composite(key, (uint32_t)i);
+        if (at < LAST_LDS_CANDS) lc[at] = c;
+        gs[at] = c;
+      }
+    }
+  }
+  __syncthreads();
+  const uint32_t ncand = ctl[4];
+  const uint64_t* src = ncand <= LAST_LDS_CANDS ? (const uint64_t*)lc : (const uint64_t*)gs;
+  if (ncand > LAST_LDS_CANDS) __threadfence_block();   // this workgroup reads its global copy back
+  __syncthreads();
+  if (ncand <= (uint32_t)K) {
+    for (uint32_t i = tid; i < ncand; i += SC_THREADS) {
+      const uint32_t pos = 0xFFFFFFFFu - (uint32_t)src[i];
+      atomicOr(&bm[pos >> 5], 1u << (pos & 31));
+    }
+  } else {
+    uint64_t prefix, mask;
+    radix_select_u64(src, ncand, (uint32_t)K, 56, hsel, ctl, &prefix, &mask);
+    for (uint32_t i = tid; i < ncand; i += SC_THREADS) {
+      const uint64_t c = src[i];
+      if ((c & mask) >= prefix) {
+        const uint32_t pos = 0xFFFFFFFFu - (uint32_t)c;
+        atomicOr(&bm[pos >> 5], 1u << (pos & 31));
+      }
+    }
+  }
+  __threadfence_block();
+  __syncthreads();
+  compact_bitmap(bm, n_pos, nullptr, K, ob, scan_tmp, lbuf, NBINS + SC_CHUNK);
 }
 
 // ---------------------------------------------------------------- select (long)
+// Marking pass: every key above the threshold bin sets its bit in the
+// sequence's bitmap; keys inside the bin are appended as (key, position)
+// candidates. select_finish_kernel completes the selection.
 __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
     const float* __restrict__ scores, int64_t sstride, const int32_t* __restrict__ n_entries,
     int64_t max_n, uint8_t* __restrict__ ctrl, uint32_t* __restrict__ bitmap, int64_t bm_stride,
-    uint64_t* __restrict__ cbuf, int64_t cb_stride, int K, int32_t* __restrict__ out, int out_stride) {
-  __shared__ uint32_t h[256];
-  __shared__ uint32_t ctl[4];
-  __shared__ uint32_t scan_tmp[SEL_THREADS / 64 + 1];
-  __shared__ int s_last;
-
+    uint64_t* __restrict__ cbuf, int64_t cb_stride) {
   const int b = blockIdx.y;
   const int64_t nb = min((int64_t)n_entries[b], max_n);
-  int32_t* ob = out + (int64_t)b * out_stride;
-  if (nb <= 0) {
-    if (blockIdx.x == 0)
-      for (int j = threadIdx.x; j < K; j += SEL_THREADS) ob[j] = -1;
-    return;
-  }
   const int64_t start = (int64_t)blockIdx.x * SEL_CHUNK;
   if (start >= nb) return;
   const int64_t end = min(start + (int64_t)SEL_CHUNK, nb);
@@ -364,54 +616,67 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
       basei = __shfl(basei, 0, 64);
       if (cnd) {
         const uint32_t rank = (uint32_t)__popcll(bc & ((1ull << lane) - 1ull));
-        cb[basei + rank] = ((uint64_t)key << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i);
+        cb[basei + rank] = composite(key, (uint32_t)i);
       }
     }
   }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    __threadfence();
-    const uint32_t nblk = (uint32_t)((nb + SEL_CHUNK - 1) / SEL_CHUNK);
-    s_last = atomicAdd(&st->done_select, 1u) == nblk - 1;
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
+}
 
-  // the candidates are a subset of the sequence's nb slots: clamp defensively
-  const uint32_t ncand = min(__hip_atomic_load(&st->ncand, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
-                             (uint32_t)nb);
+// One workgroup per sequence: picks the missing keys among the threshold-bin
+// candidates, then compacts the bitmap into ascending positions.
+__global__ __launch_bounds__(SEL_THREADS) void select_finish_kernel(
+    const int32_t* __restrict__ n_entries, int64_t max_n, uint8_t* __restrict__ ctrl,
+    uint32_t* __restrict__ bitmap, int64_t bm_stride, const uint64_t* __restrict__ cbuf, int64_t cb_stride,
+    int K, int32_t* __restrict__ out, int out_stride) {
+  __shared__ uint32_t h[256];
+  __shared__ uint32_t ctl[8];
+  __shared__ uint32_t scan_tmp[SEL_THREADS / 64 + 1];
+  __shared__ uint64_t lcand[SEL_LDS_CAP];
+  const int b = blockIdx.x;
+  const int64_t nb = min((int64_t)n_entries[b], max_n);
+  int32_t* ob = out + (int64_t)b * out_stride;
+  SelState* st = ctrl_state(ctrl, b);
+  const int thr = st->thr_bin;
   const uint32_t above = st->above;
+  // the candidates are a subset of the sequence's nb slots: clamp defensively
+  const uint32_t ncand = min(st->ncand, (uint32_t)max(nb, (int64_t)0));
+  __syncthreads();
+  if (threadIdx.x == 0) { st->ncand = 0; st->thr_bin = 0; st->above = 0; }
+  if (nb <= 0) {
+    for (int j = threadIdx.x; j < K; j += SEL_THREADS) ob[j] = -1;
+    return;
+  }
+  uint32_t* bm = bitmap + (int64_t)b * bm_stride;
+  const uint64_t* cb = cbuf + (int64_t)b * cb_stride;
   const uint32_t need = (thr >= 0 && (uint32_t)K > above) ? (uint32_t)K - above : 0u;
   if (need > 0) {
     if (need >= ncand) {
       for (uint32_t i = threadIdx.x; i < ncand; i += SEL_THREADS) {
-        const uint64_t c = __hip_atomic_load(cb + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const uint32_t pos = 0xFFFFFFFFu - (uint32_t)c;
+        const uint32_t pos = 0xFFFFFFFFu - (uint32_t)cb[i];
         atomicOr(&bm[pos >> 5], 1u << (pos & 31));
       }
     } else {
-      uint64_t prefix;
-      int shift;
-      radix_select_u64(cb, ncand, need, 56, h, ctl, &prefix, &shift);
+      // candidates share the 12 bin bits (composite bits 63..52): radix from bit 51
+      const bool in_lds = ncand <= SEL_LDS_CAP;
+      if (in_lds) {
+        for (uint32_t i = threadIdx.x; i < ncand; i += SEL_THREADS) lcand[i] = cb[i];
+        __syncthreads();
+      }
+      const uint64_t* src = in_lds ? (const uint64_t*)lcand : cb;
+      uint64_t prefix, mask;
+      radix_select_u64(src, ncand, need, 44, h, ctl, &prefix, &mask);
       for (uint32_t i = threadIdx.x; i < ncand; i += SEL_THREADS) {
-        const uint64_t c = __hip_atomic_load(cb + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if ((c >> shift) >= (prefix >> shift)) {
+        const uint64_t c = src[i];
+        if ((c & mask) >= prefix) {
           const uint32_t pos = 0xFFFFFFFFu - (uint32_t)c;
           atomicOr(&bm[pos >> 5], 1u << (pos & 31));
         }
       }
     }
   }
-  __threadfence();
+  __threadfence_block();
   __syncthreads();
-  compact_bitmap<true>(bm, nb, nullptr, K, ob, scan_tmp);
-  if (threadIdx.x == 0) {
-    st->done_select = 0;
-    st->ncand = 0;
-    st->thr_bin = 0;
-    st->above = 0;
-  }
+  compact_bitmap(bm, nb, nullptr, K, ob, scan_tmp, (uint32_t*)lcand, 2 * SEL_LDS_CAP);
 }
 
 // ---------------------------------------------------------------- select (small)
@@ -501,7 +766,7 @@ __global__ __launch_bounds__(SMALL_THREADS) void select_small_kernel(
       pmask |= (uint64_t)255 << shift;
       need -= above;
       if (cnt == need || shift == 0) break;
-      shift -= 8;
+      shift = shift >= 8 ? shift - 8 : 0;
     }
     for (int i = threadIdx.x; i < nslots; i += SMALL_THREADS) {
       if (!((valid[i >> 5] >> (i & 31)) & 1u)) continue;
@@ -510,20 +775,45 @@ __global__ __launch_bounds__(SMALL_THREADS) void select_small_kernel(
     }
   }
   __syncthreads();
-  compact_bitmap<false>(selbm, nslots, sp, K, ob, scan_tmp);
+  compact_bitmap(selbm, nslots, sp, K, ob, scan_tmp, keys, SMALL_MAX);
 }
 
 // ---------------------------------------------------------------- launchers
 hipError_t launch_score(const uint8_t* ik, const uint8_t* iks, const int64_t* entry_offset,
                         const int32_t* n_entries, int B, int64_t max_n, const uint16_t* q_idx,
                         const float* w, int Hi, int mode, const int32_t* cand, int cand_stride,
-                        float* scores, int64_t sstride, uint8_t* ctrl, uint32_t* bitmap,
-                        int64_t bm_stride, int K, hipStream_t stream) {
+                        float* scores, int64_t sstride, const SelBufs& sb, int sel, int K,
+                        hipStream_t stream) {
   const int64_t nslots = cand ? cand_stride : max_n;
   if (nslots <= 0) return hipSuccess;
-  dim3 grid((unsigned)((nslots + SC_CHUNK - 1) / SC_CHUNK), (unsigned)B), block(SC_THREADS);
-  hipLaunchKernelGGL(score_kernel, grid, block, 0, stream, ik, iks, entry_offset, n_entries, max_n,
-                     q_idx, w, Hi, mode, cand, cand_stride, scores, sstride, ctrl, bitmap, bm_stride, K);
+  const int64_t nx = (nslots + SC_CHUNK - 1) / SC_CHUNK;
+  dim3 grid((unsigned)nx, (unsigned)B), block(SC_THREADS);
+#define CSA2_SCORE_LAUNCH(C, S, Mo)                                                              \
+  hipLaunchKernelGGL((score_kernel<C, S, Mo>), grid, block, 0, stream, ik, iks, entry_offset,   \
+                     n_entries, max_n, q_idx, w, Hi, cand, cand_stride, scores, sstride, sb, K)
+  if (cand) {
+    if (mode == 0) CSA2_SCORE_LAUNCH(true, SEL_NONE, 0); else CSA2_SCORE_LAUNCH(true, SEL_NONE, 1);
+  } else if (sel == SEL_THRESHOLD) {
+    if (mode == 0) CSA2_SCORE_LAUNCH(false, SEL_THRESHOLD, 0); else CSA2_SCORE_LAUNCH(false, SEL_THRESHOLD, 1);
+  } else if (sel == SEL_DIRECT) {
+    if (mode == 0) CSA2_SCORE_LAUNCH(false, SEL_DIRECT, 0); else CSA2_SCORE_LAUNCH(false, SEL_DIRECT, 1);
+  } else {
+    if (mode == 0) CSA2_SCORE_LAUNCH(false, SEL_NONE, 0); else CSA2_SCORE_LAUNCH(false, SEL_NONE, 1);
+  }
+#undef CSA2_SCORE_LAUNCH
+  return hipGetLastError();
+}
+
+hipError_t launch_finish(int sel, const int32_t* n_entries, int B, int64_t max_n, const float* scores,
+                         int64_t sstride, const SelBufs& sb, int K, int32_t* out, int out_stride,
+                         hipStream_t stream) {
+  dim3 grid((unsigned)B), block(SC_THREADS);
+  if (sel == SEL_DIRECT)
+    hipLaunchKernelGGL(finish_kernel<SEL_DIRECT>, grid, block, 0, stream, n_entries, max_n, scores, sstride, sb,
+                       K, out, out_stride);
+  else
+    hipLaunchKernelGGL(finish_kernel<SEL_THRESHOLD>, grid, block, 0, stream, n_entries, max_n, scores, sstride,
+                       sb, K, out, out_stride);
   return hipGetLastError();
 }
 
@@ -531,10 +821,15 @@ hipError_t launch_select(const float* scores, int64_t sstride, const int32_t* n_
                          int64_t max_n, uint8_t* ctrl, uint32_t* bitmap, int64_t bm_stride,
                          uint64_t* cbuf, int64_t cb_stride, int K, int32_t* out, int out_stride,
                          hipStream_t stream) {
-  const int64_t nx = max_n > 0 ? (max_n + SEL_CHUNK - 1) / SEL_CHUNK : 1;
-  dim3 grid((unsigned)nx, (unsigned)B), block(SEL_THREADS);
-  hipLaunchKernelGGL(select_kernel, grid, block, 0, stream, scores, sstride, n_entries, max_n, ctrl,
-                     bitmap, bm_stride, cbuf, cb_stride, K, out, out_stride);
+  if (max_n > 0) {
+    dim3 grid((unsigned)((max_n + SEL_CHUNK - 1) / SEL_CHUNK), (unsigned)B), block(SEL_THREADS);
+    hipLaunchKernelGGL(select_kernel, grid, block, 0, stream, scores, sstride, n_entries, max_n, ctrl, bitmap,
+                       bm_stride, cbuf, cb_stride);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(select_finish_kernel, dim3((unsigned)B), dim3(SEL_THREADS), 0, stream, n_entries, max_n,
+                     ctrl, bitmap, bm_stride, cbuf, cb_stride, K, out, out_stride);
   return hipGetLastError();
 }
 

@@ -7,13 +7,18 @@ namespace csa2 {
 
 // Per-sequence selection state kept in the indexer workspace (zero between calls).
 struct SelState {
-  uint32_t done_score;    // score workgroups of the sequence that finished
-  uint32_t done_select;   // select workgroups of the sequence that finished
+  uint32_t unused0;
+  uint32_t unused1;
   int32_t thr_bin;        // histogram bin holding the K-th best key (-1: all selected)
   uint32_t above;         // keys in bins above thr_bin
-  uint32_t ncand;         // candidates appended from thr_bin
-  uint32_t pad[3];
+  uint32_t ncand;         // select pass: candidates appended from thr_bin
+  uint32_t cut_max;       // score pass: highest local cutoff bin over the workgroups
+  uint32_t flags;         // score pass: 1 = a pair list overflowed, 2 = a candidate list overflowed
+  uint32_t npairs;        // score pass: (bin, count) pairs appended to the sequence's list
+  uint32_t nsc;           // score pass: candidates appended to the sequence's list
+  uint32_t pad[7];
 };
+static_assert(sizeof(SelState) == 64, "control block header");
 
 constexpr int kNumBins = 4096;
 constexpr int kSmallMax = 16384;
@@ -28,11 +33,35 @@ hipError_t launch_cache_write(const uint16_t* x_lat, const uint16_t* x_idx, cons
                               const float* w_idx, int B, int64_t T, int m, uint8_t* kv, uint8_t* ik,
                               uint8_t* iks, hipStream_t stream);
 
+// Selection modes of the score pass.
+enum { SEL_NONE = 0, SEL_THRESHOLD = 1, SEL_DIRECT = 2 };
+constexpr int kScoreChunk = 1024;     // slots per score workgroup
+constexpr int kSumWords = 32;         // (bin, count) pairs a workgroup may report
+constexpr int kCandCap = 256;         // candidates a workgroup reports in direct mode
+constexpr int kDirectMaxK = 512;      // largest k the score pass selects by itself
+
+// Workspace views used by the score pass's selection (per-sequence strides).
+struct SelBufs {
+  uint8_t* ctrl;        // control blocks (SelState + histogram), fixed places
+  uint32_t* bitmap;     // [B][bm_stride] words; the score pass clears its chunk's words
+  int64_t bm_stride;
+  uint32_t* summ;       // [B][summ_stride] words: the sequence's (bin, count) pair list
+  int64_t summ_stride;
+  uint64_t* wgc;        // [B][wgc_stride]: the sequence's candidate list (direct mode)
+  int64_t wgc_stride;
+  uint64_t* gscr;       // [B][gscr_stride]: gathered candidates that do not fit LDS
+  int64_t gscr_stride;
+};
+
 hipError_t launch_score(const uint8_t* ik, const uint8_t* iks, const int64_t* entry_offset,
                         const int32_t* n_entries, int B, int64_t max_n, const uint16_t* q_idx,
                         const float* w, int Hi, int mode, const int32_t* cand, int cand_stride,
-                        float* scores, int64_t sstride, uint8_t* ctrl, uint32_t* bitmap,
-                        int64_t bm_stride, int K, hipStream_t stream);
+                        float* scores, int64_t sstride, const SelBufs& sb, int sel, int K,
+                        hipStream_t stream);
+
+hipError_t launch_finish(int sel, const int32_t* n_entries, int B, int64_t max_n, const float* scores,
+                         int64_t sstride, const SelBufs& sb, int K, int32_t* out, int out_stride,
+                         hipStream_t stream);
 
 hipError_t launch_select(const float* scores, int64_t sstride, const int32_t* n_entries, int B,
                          int64_t max_n, uint8_t* ctrl, uint32_t* bitmap, int64_t bm_stride,
