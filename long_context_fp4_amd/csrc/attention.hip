@@ -30,7 +30,9 @@
 //   the 128 accumulators are rescaled rarely).
 //   PV: O^T += C^T P^T with v_mfma_f32_16x16x16_f16; P^T comes straight from
 //   the QK output registers, C^T is read back from the wave's LDS copy of the
-//   tile (pitch 1040 B: conflict-free reads) and repacked with v_perm.
+//   tile with gfx950's transposing LDS read (ds_read_b64_tr_b16), which hands
+//   every lane 4 entries of one dimension; rows are 1056 B apart so the 16 rows
+//   of a read fall on distinct banks.
 // The 4 waves' partial states are merged through LDS; with several splits the
 // workgroup writes an unnormalised partial that a small kernel combines.
 #include "device.h"
@@ -40,10 +42,12 @@
 namespace csa2 {
 
 constexpr int AT_THREADS = 256;
-constexpr int AT_PITCH = 1040;                 // bytes per entry row of the fp16 tile
-constexpr int AT_WAVE_LDS = 16 * AT_PITCH;     // 16640
-constexpr int AT_LDS = 4 * AT_WAVE_LDS;        // 66560 (>= 2 x 32 KiB for the merge)
+constexpr int AT_PITCH = 1056;                 // bytes per entry row of the fp16 tile (rows 8 banks apart)
+constexpr int AT_WAVE_LDS = 16 * AT_PITCH;     // 16896
+constexpr int AT_LDS = 4 * AT_WAVE_LDS;        // 67584 (>= 2 x 32 KiB for the merge)
 constexpr float AT_RESCALE = 8.0f;
+constexpr int AT_QPITCH = 1040;                // bytes per head row of the fp16 queries
+constexpr int AT_MAX_CHUNK = 2048;             // positions of one split (k <= CSA2_MAX_K)
 
 __device__ __forceinline__ f16x8_t dequant_latent8(uint32_t dw, uint32_t spair) {
   const f16x2_t sp = bitcast_u32<f16x2_t>(spair);
@@ -60,6 +64,20 @@ __device__ __forceinline__ uint32_t scale_pair(uint32_t sbyte) {
   return h | (h << 16);
 }
 
+// max / sum over the four lanes l, l^16, l^32, l^48 (VALU lane swaps)
+__device__ __forceinline__ float max_lane_groups(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const float t = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  const auto r2 = __builtin_amdgcn_permlane16_swap(__float_as_uint(t), __float_as_uint(t), false, false);
+  return fmaxf(__uint_as_float(r2[0]), __uint_as_float(r2[1]));
+}
+__device__ __forceinline__ float sum_lane_groups_a(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const float t = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  const auto r2 = __builtin_amdgcn_permlane16_swap(__float_as_uint(t), __float_as_uint(t), false, false);
+  return __uint_as_float(r2[0]) + __uint_as_float(r2[1]);
+}
+
 __global__ __launch_bounds__(AT_THREADS) void attention_kernel(
     const uint8_t* __restrict__ kv, const int64_t* __restrict__ entry_offset,
     const int32_t* __restrict__ n_entries, const int32_t* __restrict__ idx, int k,
@@ -67,6 +85,9 @@ __global__ __launch_bounds__(AT_THREADS) void attention_kernel(
     float* __restrict__ out, float* __restrict__ lse, float* __restrict__ part) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ float sm_m[4][16], sm_l[4][16];
+  __shared__ float sm_lscale[16];
+  __shared__ __attribute__((aligned(16))) uint8_t qlds[16 * AT_QPITCH];   // fp16 queries, row = head
+  __shared__ int32_t sidx[AT_MAX_CHUNK];                                   // the split's positions (-1 = skip)
 
   const int HG = (H + 15) / 16;
   const int wg = blockIdx.x;
@@ -78,158 +99,181 @@ __global__ __launch_bounds__(AT_THREADS) void attention_kernel(
   const int head = 16 * hg + r;
   const bool head_ok = head < H;
 
-  // --- queries: B operand of QK (column = head r, K-slice = dims 128kg + 8j .. +7)
-  const uint16_t* qh = q + ((int64_t)b * H + (head_ok ? head : 0)) * 512 + 128 * kg;
-  u32x4_t qraw[16];
-  float qmax = 0.0f;
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    qraw[j] = head_ok ? *(const u32x4_t*)(qh + 8 * j) : u32x4_t{0, 0, 0, 0};
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      qmax = fmaxf(qmax, fabsf(bf16_to_f32(qraw[j][t] & 0xFFFFu)));
-      qmax = fmaxf(qmax, fabsf(bf16_to_f32(qraw[j][t] >> 16)));
-    }
-  }
-  qmax = fmaxf(qmax, shfl_xor_f(qmax, 16));
-  qmax = fmaxf(qmax, shfl_xor_f(qmax, 32));
-  int sigma = 0;
-  if (qmax > 0.0f) {
-    int e;
-    frexpf(qmax, &e);          // qmax in [2^(e-1), 2^e)
-    sigma = 15 - e;            // qmax * 2^sigma in [2^14, 2^15)
-  }
-  f16x8_t qb[16];
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      qb[j][2 * t] = (_Float16)ldexpf(bf16_to_f32(qraw[j][t] & 0xFFFFu), sigma);
-      qb[j][2 * t + 1] = (_Float16)ldexpf(bf16_to_f32(qraw[j][t] >> 16), sigma);
-    }
-  }
-  const float lscale = ldexpf(tau, -sigma);
-
-  // --- entry range of this split, in tiles of 16
+  // --- entry range of this split, in tiles of 16; its positions go to LDS
   const int chunk = ((k + S - 1) / S + 15) & ~15;
   const int e_lo = s * chunk;
   const int e_hi = min(k, e_lo + chunk);
-  const int ntiles = e_hi > e_lo ? (e_hi - e_lo + 15) / 16 : 0;
+  const int nent = max(e_hi - e_lo, 0);
+  const int ntiles = (nent + 15) / 16;
   const int64_t nb = n_entries[b];
   const int64_t row_base = entry_offset[b];
-  const int32_t* ib = idx + (int64_t)b * k;
+  {
+    const int32_t* ib = idx + (int64_t)b * k + e_lo;
+    for (int i = tid; i < ntiles * 16; i += AT_THREADS) {
+      int p = i < nent ? ib[i] : -1;
+      sidx[i] = (p >= 0 && p < nb) ? p : -1;
+    }
+  }
+
+  // --- queries: thread (qh = tid/16, c = tid%16) converts dims 32c .. 32c+31 of head 16hg + qh.
+  // Each head is scaled by a power of two that puts its largest magnitude in
+  // [2^14, 2^15) before rounding to fp16; the logit divides it out again.
+  {
+    const int qh = tid >> 4, c = tid & 15;
+    const int hq = 16 * hg + qh;
+    u32x4_t raw[4] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};
+    if (hq < H) {
+      const uint16_t* src = q + ((int64_t)b * H + hq) * 512 + 32 * c;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) raw[j] = *(const u32x4_t*)(src + 8 * j);
+    }
+    float qmax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        qmax = fmaxf(qmax, fabsf(bf16_to_f32(raw[j][t] & 0xFFFFu)));
+        qmax = fmaxf(qmax, fabsf(bf16_to_f32(raw[j][t] >> 16)));
+      }
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) qmax = fmaxf(qmax, shfl_xor_f(qmax, d));
+    int sigma = 0;
+    if (qmax > 0.0f) {
+      int e;
+      frexpf(qmax, &e);          // qmax in [2^(e-1), 2^e)
+      sigma = 15 - e;            // qmax * 2^sigma in [2^14, 2^15)
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f16x8_t v;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        v[2 * t] = (_Float16)ldexpf(bf16_to_f32(raw[j][t] & 0xFFFFu), sigma);
+        v[2 * t + 1] = (_Float16)ldexpf(bf16_to_f32(raw[j][t] >> 16), sigma);
+      }
+      *(f16x8_t*)(qlds + qh * AT_QPITCH + 64 * c + 16 * j) = v;
+    }
+    if (c == 0) sm_lscale[qh] = ldexpf(tau, -sigma);
+  }
+  __syncthreads();
+  // B operand of QK: column = head r, K-slice = dims 128kg + 8j .. +7
+  f16x8_t qb[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) qb[j] = *(const f16x8_t*)(qlds + r * AT_QPITCH + 256 * kg + 16 * j);
+  const float lscale = sm_lscale[r];
   uint8_t* wlds = smem + wave * AT_WAVE_LDS;
+
   f32x4_t O[32];
 #pragma unroll
   for (int t = 0; t < 32; ++t) O[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   float m_ref = -INFINITY, l_run = 0.0f;
 
-  // Tiles of this wave: wave, wave + 4, ... Software pipeline: the index of the
-  // tile two steps ahead and the rows of the next tile are in flight while the
-  // current tile is computed. Loads are unconditional (an invalid entry reads
-  // row 0 of the sequence and is masked), so they never wait on a branch.
+  // Tiles of this wave: wave, wave + 4, ... The rows of the next tile are in
+  // flight while the current tile is computed. Loads are unconditional (a
+  // skipped entry reads row 0 of the sequence and is masked).
   const bool any_rows = nb > 0;
-  auto idx_of = [&](int tile) -> int {
-    const int ent = e_lo + 16 * tile + r;
-    return (tile < ntiles && ent < e_hi) ? ib[ent] : -1;
-  };
-  auto rowp = [&](int p) -> const uint8_t* {
-    const int64_t pc = (p >= 0 && p < nb) ? p : 0;
-    return kv + (row_base + pc) * 288;
-  };
-  int pA = idx_of(wave), pB = idx_of(wave + 4);
-  u32x4_t cw[4] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};
-  u32x2_t sw = {0, 0};
-  if (any_rows && wave < ntiles) {
-    const uint8_t* row = rowp(pA);
+  auto load_rows = [&](int tile, u32x4_t* cw, u32x2_t& sw) {
+    const int p = sidx[16 * tile + r];
+    const uint8_t* row = kv + (row_base + (p >= 0 ? p : 0)) * 288;
 #pragma unroll
     for (int c = 0; c < 4; ++c) cw[c] = *(const u32x4_t*)(row + 64 * kg + 16 * c);
     sw = *(const u32x2_t*)(row + 256 + 8 * kg);
-  }
+  };
+  // ping-pong row buffers (no register copies of loads in flight)
+  u32x4_t cwA[4] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};
+  u32x4_t cwB[4] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};
+  u32x2_t swA = {0, 0}, swB = {0, 0};
+  auto compute_tile = [&](int tile, const u32x4_t* cw, const u32x2_t sw) {
+      const uint64_t vmask = __ballot(sidx[16 * tile + r] >= 0);
 
-  for (int tile = wave; tile < ntiles; tile += 4) {
-    const int pC = idx_of(tile + 8);
-    u32x4_t cwn[4] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};
-    u32x2_t swn = {0, 0};
-    if (any_rows && tile + 4 < ntiles) {
-      const uint8_t* row = rowp(pB);
+      // dequantize 128 dims (128kg .. 128kg+127) to fp16, feed QK and copy the tile
+      // to the wave's LDS area (row = entry r); logits^T: rows = entries, columns = heads
+      f32x4_t lg0 = {0.0f, 0.0f, 0.0f, 0.0f}, lg1 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int c = 0; c < 4; ++c) cwn[c] = *(const u32x4_t*)(row + 64 * kg + 16 * c);
-      swn = *(const u32x2_t*)(row + 256 + 8 * kg);
-    }
-    const bool valid = pA >= 0 && pA < nb;
-    const uint64_t vmask = __ballot(valid);
+      for (int j = 0; j < 16; ++j) {
+        const uint32_t sbyte = (sw[j >> 3] >> (8 * ((j >> 1) & 3))) & 0xFFu;
+        const f16x8_t ca = dequant_latent8(cw[j >> 2][j & 3], scale_pair(sbyte));
+        if (j & 1) lg1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ca, qb[j], lg1, 0, 0, 0);
+        else lg0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ca, qb[j], lg0, 0, 0, 0);
+        *(f16x8_t*)(wlds + r * AT_PITCH + 256 * kg + 16 * j) = ca;
+      }
+      const f32x4_t lg = lg0 + lg1;
 
-    // dequantize 128 dims (128kg .. 128kg+127) to fp16, feed QK and copy the tile
-    // to the wave's LDS area (row = entry r); logits^T: rows = entries, columns = heads
-    f32x4_t lg = {0.0f, 0.0f, 0.0f, 0.0f};
+      // online softmax for head r; this lane holds entries 4kg + i of the tile
+      float x[4];
+      float tmax = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const uint32_t sbyte = (sw[j >> 3] >> (8 * ((j >> 1) & 3))) & 0xFFu;
-      const f16x8_t ca = dequant_latent8(cw[j >> 2][j & 3], scale_pair(sbyte));
-      lg = __builtin_amdgcn_mfma_f32_16x16x32_f16(ca, qb[j], lg, 0, 0, 0);
-      *(f16x8_t*)(wlds + r * AT_PITCH + 256 * kg + 16 * j) = ca;
-    }
+      for (int i = 0; i < 4; ++i) {
+        const bool v = (vmask >> (4 * kg + i)) & 1ull;
+        x[i] = v ? lg[i] * lscale : -INFINITY;
+        tmax = fmaxf(tmax, x[i]);
+      }
+      tmax = max_lane_groups(tmax);
+      const bool raise = tmax > m_ref + AT_RESCALE || (m_ref == -INFINITY && tmax > -INFINITY);
+      if (__any(raise)) {
+        const float m_new = raise ? fmaxf(m_ref, tmax) : m_ref;
+        const float alpha = (m_ref == -INFINITY) ? 0.0f : __expf(m_ref - m_new);
+        if (raise) {
+          l_run *= alpha;
+#pragma unroll
+          for (int t = 0; t < 32; ++t) O[t] *= alpha;
+          m_ref = m_new;
+        }
+      }
+      float p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[i] = (m_ref == -INFINITY) ? 0.0f : expf(x[i] - m_ref);
+        l_run += p[i];
+      }
+      const f16x4_t pb = {(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
 
-    // online softmax for head r; this lane holds entries 4kg + i of the tile
-    float x[4];
-    float tmax = -INFINITY;
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      // O^T[dims x heads] += C^T[dims x entries] P^T[entries x heads], one M-tile per 16 dims.
+      // A operand by transposing LDS reads: lane 4m + a of lane group kg points at entry
+      // 4kg + m, dims 16u + 4a .. +3; lane i of the group then holds dim 16u + i of
+      // entries 4kg .. 4kg+3.
+      {
+        typedef short i16x4_t __attribute__((ext_vector_type(4)));
+        typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
+        const int j = lane & 15;
+        __attribute__((address_space(3))) uint8_t* tb =
+            (__attribute__((address_space(3))) uint8_t*)wlds + (4 * kg + (j >> 2)) * AT_PITCH + 8 * (j & 3);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bool v = (vmask >> (4 * kg + i)) & 1ull;
-      x[i] = v ? lg[i] * lscale : -INFINITY;
-      tmax = fmaxf(tmax, x[i]);
-    }
-    tmax = fmaxf(tmax, shfl_xor_f(tmax, 16));
-    tmax = fmaxf(tmax, shfl_xor_f(tmax, 32));
-    const bool raise = tmax > m_ref + AT_RESCALE || (m_ref == -INFINITY && tmax > -INFINITY);
-    if (__any(raise)) {
-      const float m_new = raise ? fmaxf(m_ref, tmax) : m_ref;
-      const float alpha = (m_ref == -INFINITY) ? 0.0f : __expf(m_ref - m_new);
-      if (raise) {
-        l_run *= alpha;
+        for (int u = 0; u < 32; ++u) {
+          const i16x4_t raw = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tb + 32 * u));
+          f16x4_t a;
+          __builtin_memcpy(&a, &raw, 8);
+          O[u] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, pb, O[u], 0, 0, 0);
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+  };
+  // rounds of up to 8 tiles per wave, unrolled so the load/compute pipeline is
+  // straight-line code (one full wait per round at most)
+  // (loads are unconditional inside a round: the prefetch past the wave's last
+  // tile re-reads its last tile, so the wait analysis sees one path)
+  const int last = ntiles - 1 - ((ntiles - 1 - wave) & 3);   // this wave's last tile
+  for (int base = wave; any_rows && base < ntiles; base += 32) {
+    load_rows(base, cwA, swA);
 #pragma unroll
-        for (int t = 0; t < 32; ++t) O[t] *= alpha;
-        m_ref = m_new;
+    for (int i = 0; i < 8; ++i) {
+      const int tile = base + 4 * i;
+      if (tile >= ntiles) break;
+      if (i & 1) {
+        if (i < 7) load_rows(min(tile + 4, last), cwA, swA);
+        compute_tile(tile, cwB, swB);
+      } else {
+        load_rows(min(tile + 4, last), cwB, swB);
+        compute_tile(tile, cwA, swA);
       }
     }
-    float p[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      p[i] = (m_ref == -INFINITY) ? 0.0f : expf(x[i] - m_ref);
-      l_run += p[i];
-    }
-    const f16x4_t pb = {(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
-
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    // O^T[dims x heads] += C^T[dims x entries] P^T[entries x heads].
-    // M-tile (u, v): lane row r <-> dim 32u + 2r + v; K = entries 4kg .. 4kg+3.
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      uint32_t d[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) d[i] = *(const uint32_t*)(wlds + (4 * kg + i) * AT_PITCH + 64 * u + 4 * r);
-      const u32x2_t lo = {__builtin_amdgcn_perm(d[1], d[0], 0x05040100u), __builtin_amdgcn_perm(d[3], d[2], 0x05040100u)};
-      const u32x2_t hi = {__builtin_amdgcn_perm(d[1], d[0], 0x07060302u), __builtin_amdgcn_perm(d[3], d[2], 0x07060302u)};
-      f16x4_t a0, a1;
-      __builtin_memcpy(&a0, &lo, 8);
-      __builtin_memcpy(&a1, &hi, 8);
-      O[2 * u] = __builtin_amdgcn_mfma_f32_16x16x16f16(a0, pb, O[2 * u], 0, 0, 0);
-      O[2 * u + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(a1, pb, O[2 * u + 1], 0, 0, 0);
-    }
-    __builtin_amdgcn_wave_barrier();
-#pragma unroll
-    for (int c = 0; c < 4; ++c) cw[c] = cwn[c];
-    sw = swn;
-    pA = pB;
-    pB = pC;
   }
 
   // --- merge the 4 waves: per head max, weights, then pairwise sums of O in LDS
-  l_run += shfl_xor_f(l_run, 16);
-  l_run += shfl_xor_f(l_run, 32);
+  l_run = sum_lane_groups_a(l_run);
   if (lane < 16) { sm_m[wave][lane] = m_ref; sm_l[wave][lane] = l_run; }
   __syncthreads();
   float M = -INFINITY;
@@ -270,28 +314,24 @@ __global__ __launch_bounds__(AT_THREADS) void attention_kernel(
   for (int t = 0; t < 32; ++t) O[t] += bufA[t * 64 + lane];
   if (!head_ok) return;
 
-  // lane (r, kg) holds dims 32u + 8kg + 2i + v of head r in O[2u + v][i]
+  // lane (r, kg) holds dims 16u + 4kg + i of head r in O[u][i]
   if (S == 1) {
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
     float* ob = out + ((int64_t)b * H + head) * 512;
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const f32x4_t x0 = O[2 * u], x1 = O[2 * u + 1];
-      float4 lo4 = {x0[0] * inv, x1[0] * inv, x0[1] * inv, x1[1] * inv};
-      float4 hi4 = {x0[2] * inv, x1[2] * inv, x0[3] * inv, x1[3] * inv};
-      *(float4*)(ob + 32 * u + 8 * kg) = lo4;
-      *(float4*)(ob + 32 * u + 8 * kg + 4) = hi4;
+    for (int u = 0; u < 32; ++u) {
+      const f32x4_t x = O[u];
+      *(float4*)(ob + 16 * u + 4 * kg) = float4{x[0] * inv, x[1] * inv, x[2] * inv, x[3] * inv};
     }
     if (lse && kg == 0) lse[(int64_t)b * H + head] = L > 0.0f ? M + logf(L) : -INFINITY;
   } else {
     // partial: [B][H][S][512 + 2] -> unnormalised O, then (M, L)
     float* pb = part + (((int64_t)b * H + head) * S + s) * 514;
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const f32x4_t x0 = O[2 * u], x1 = O[2 * u + 1];
-      float* o = pb + 32 * u + 8 * kg;
-      o[0] = x0[0]; o[1] = x1[0]; o[2] = x0[1]; o[3] = x1[1];
-      o[4] = x0[2]; o[5] = x1[2]; o[6] = x0[3]; o[7] = x1[3];
+    for (int u = 0; u < 32; ++u) {
+      const f32x4_t x = O[u];
+      float* o = pb + 16 * u + 4 * kg;
+      o[0] = x[0]; o[1] = x[1]; o[2] = x[2]; o[3] = x[3];
     }
     if (kg == 0) { pb[512] = M; pb[513] = L; }
   }
@@ -324,8 +364,8 @@ __global__ __launch_bounds__(128) void attention_combine_kernel(const float* __r
 int attention_splits(int B, int H, int k) {
   const int base = B * ((H + 15) / 16);
   int S = 1;
-  // enough workgroups to cover the 256 compute units, at least 4 tiles per split
-  while (base * S < 256 && (k + 2 * S - 1) / (2 * S) >= 64) S *= 2;
+  // at least 128 workgroups (one per compute unit pair), each split keeping >= 64 entries
+  while (base * S < 128 && (k + 2 * S - 1) / (2 * S) >= 64) S *= 2;
   return S;
 }
 

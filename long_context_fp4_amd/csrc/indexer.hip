@@ -170,6 +170,42 @@ __device__ void radix_select_u64(const uint64_t* v, uint32_t n, uint32_t need, i
   *mask_out = pmask;
 }
 
+// Index in an LDS list for the lanes whose `take` is set: one LDS atomic per wave.
+__device__ __forceinline__ uint32_t wave_append(bool take, uint32_t* counter) {
+  const uint64_t m = __ballot(take);
+  const int lane = threadIdx.x & 63;
+  uint32_t base = 0;
+  if (m) {
+    const int leader = __ffsll((long long)m) - 1;
+    if (lane == leader) base = atomicAdd(counter, (uint32_t)__popcll(m));
+    base = __shfl(base, leader, 64);
+  }
+  return base + (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
+}
+
+// Top shift for radix_select_u64 over n composites at v: the 8-bit digit that
+// holds the highest bit in which any two composites differ (bits above it are
+// common to all of them). All threads of the workgroup must call it.
+__device__ int radix_top_shift(const uint64_t* v, uint32_t n, uint64_t* red) {
+  uint64_t o = 0, a = ~0ull;
+  for (uint32_t i = threadIdx.x; i < n; i += blockDim.x) { o |= v[i]; a &= v[i]; }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) {
+    o |= __shfl_xor(o, d, 64);
+    a &= __shfl_xor(a, d, 64);
+  }
+  const int nw = blockDim.x >> 6;
+  if ((threadIdx.x & 63) == 0) { red[threadIdx.x >> 6] = o; red[8 + (threadIdx.x >> 6)] = a; }
+  __syncthreads();
+  o = 0; a = ~0ull;
+  for (int i = 0; i < nw; ++i) { o |= red[i]; a &= red[8 + i]; }
+  __syncthreads();
+  const uint64_t diff = o ^ a;
+  if (diff == 0) return 0;
+  const int hb = 63 - __clzll(diff);
+  return hb >= 7 ? hb - 7 : 0;
+}
+
 // Ascending compaction of a bitmap of nbits bits into out[0..cnt), -1 padding up
 // to K. The bitmap is read in chunks of `stage_words` words into the LDS buffer
 // `stage` with independent coalesced loads; a global bitmap filled by other
@@ -296,7 +332,9 @@ __global__ __launch_bounds__(SC_THREADS) void score_kernel(
   const int n = lane & 15, g = lane >> 4;
   if (SEL != SEL_NONE) {
     for (int i = tid; i < NBINS; i += SC_THREADS) lhist[i] = 0;
-    // the selection ORs into the bitmap words of this chunk: clear them here
+  }
+  if (SEL == SEL_THRESHOLD) {
+    // select_kernel ORs into the bitmap words of this chunk: clear them here
     uint32_t* bm = sb.bitmap + (int64_t)b * sb.bm_stride;
     for (int64_t wd = start / 32 + tid; wd < (start + end + 31) / 32; wd += SC_THREADS) bm[wd] = 0;
   }
@@ -456,8 +494,9 @@ template <int SEL>
 __global__ __launch_bounds__(SC_THREADS) void finish_kernel(
     const int32_t* __restrict__ n_entries, int64_t max_n, const float* __restrict__ scores, int64_t sstride,
     SelBufs sb, int K, int32_t* __restrict__ out, int out_stride) {
-  __shared__ uint32_t lbuf[NBINS + SC_CHUNK];     // histogram; candidates and bitmap staging later
-  __shared__ uint32_t hsel[256];
+  __shared__ uint32_t lbuf[NBINS + SC_CHUNK];     // histogram; candidates later
+  __shared__ uint32_t hsel[256 + kDirectMaxK];     // radix histogram, then the selected positions
+  __shared__ uint64_t scan_red[16];
   __shared__ uint32_t scan_tmp[SC_THREADS / 64 + 1];
   __shared__ uint32_t ctl[8];
   uint32_t* lhist = lbuf;
@@ -466,7 +505,6 @@ __global__ __launch_bounds__(SC_THREADS) void finish_kernel(
   SelState* st = ctrl_state(sb.ctrl, b);
   const float* sall = scores + (int64_t)b * sstride;
   int32_t* ob = out ? out + (int64_t)b * out_stride : nullptr;
-  uint32_t* bm = sb.bitmap + (int64_t)b * sb.bm_stride;
   const uint32_t bmax = st->cut_max, flags = st->flags, npairs = st->npairs, nsc = st->nsc;
   __syncthreads();
   if (tid == 0) { st->cut_max = 0; st->flags = 0; st->npairs = 0; st->nsc = 0; }
@@ -530,18 +568,21 @@ __global__ __launch_bounds__(SC_THREADS) void finish_kernel(
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const uint32_t i = base + j * SC_THREADS + tid;
-        if (i < nsc && (uint32_t)(cv[j] >> (32 + BIN_SHIFT)) >= T) {
-          const uint32_t at = atomicAdd(&ctl[4], 1u);
+        const bool take = i < nsc && (uint32_t)(cv[j] >> (32 + BIN_SHIFT)) >= T;
+        const uint32_t at = wave_append(take, &ctl[4]);
+        if (take) {
           if (at < LAST_LDS_CANDS) lc[at] = cv[j];
           gs[at] = cv[j];
         }
       }
     }
   } else {
-    for (int64_t i = tid; i < n_pos; i += SC_THREADS) {
-      const uint32_t key = score_key(sall[i]);
-      if ((key >> BIN_SHIFT) >= T) {
-        const uint32_t at = atomicAdd(&ctl[4], 1u);
+    for (int64_t i0 = 0; i0 < n_pos; i0 += SC_THREADS) {
+      const int64_t i = i0 + tid;
+      const uint32_t key = i < n_pos ? score_key(sall[i]) : 0u;
+      const bool take = i < n_pos && (key >> BIN_SHIFT) >= T;
+      const uint32_t at = wave_append(take, &ctl[4]);
+      if (take) {
         const uint64_t c = composite(key, (uint32_t)i);
         if (at < LAST_LDS_CANDS) lc[at] = c;
         gs[at] = c;
@@ -553,25 +594,44 @@ __global__ __launch_bounds__(SC_THREADS) void finish_kernel(
   const uint64_t* src = ncand <= LAST_LDS_CANDS ? (const uint64_t*)lc : (const uint64_t*)gs;
   if (ncand > LAST_LDS_CANDS) __threadfence_block();   // this workgroup reads its global copy back
   __syncthreads();
+  // the K best composites -> positions in selp[] (any order)
+  uint32_t* selp = hsel + 256;
+  if (tid == 0) ctl[5] = 0;
+  __syncthreads();
   if (ncand <= (uint32_t)K) {
-    for (uint32_t i = tid; i < ncand; i += SC_THREADS) {
-      const uint32_t pos = 0xFFFFFFFFu - (uint32_t)src[i];
-      atomicOr(&bm[pos >> 5], 1u << (pos & 31));
-    }
+    for (uint32_t i = tid; i < ncand; i += SC_THREADS) selp[i] = 0xFFFFFFFFu - (uint32_t)src[i];
+    if (tid == 0) ctl[5] = ncand;
   } else {
     uint64_t prefix, mask;
-    radix_select_u64(src, ncand, (uint32_t)K, 56, hsel, ctl, &prefix, &mask);
-    for (uint32_t i = tid; i < ncand; i += SC_THREADS) {
-      const uint64_t c = src[i];
-      if ((c & mask) >= prefix) {
-        const uint32_t pos = 0xFFFFFFFFu - (uint32_t)c;
-        atomicOr(&bm[pos >> 5], 1u << (pos & 31));
-      }
+    const int top = radix_top_shift(src, ncand, (uint64_t*)scan_red);
+    radix_select_u64(src, ncand, (uint32_t)K, top, hsel, ctl, &prefix, &mask);
+    for (uint32_t i0 = 0; i0 < ncand; i0 += SC_THREADS) {
+      const uint32_t i = i0 + tid;
+      const uint64_t c = i < ncand ? src[i] : 0ull;
+      const bool take = i < ncand && (c & mask) >= prefix;
+      const uint32_t at = wave_append(take, &ctl[5]);
+      if (take) selp[at] = 0xFFFFFFFFu - (uint32_t)c;
     }
   }
-  __threadfence_block();
   __syncthreads();
-  compact_bitmap(bm, n_pos, nullptr, K, ob, scan_tmp, lbuf, NBINS + SC_CHUNK);
+  // ascending output: bitonic sort of the (at most kDirectMaxK) positions in LDS,
+  // padded with 0xFFFFFFFF
+  const uint32_t nsel = ctl[5];
+  for (uint32_t i = nsel + tid; i < (uint32_t)kDirectMaxK; i += SC_THREADS) selp[i] = 0xFFFFFFFFu;
+  __syncthreads();
+  for (int size = 2; size <= kDirectMaxK; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int t = tid; t < kDirectMaxK / 2; t += SC_THREADS) {
+        const int lo = 2 * t - (t & (stride - 1));
+        const int hi = lo + stride;
+        const bool asc = (lo & size) == 0;
+        const uint32_t x = selp[lo], y = selp[hi];
+        if ((x > y) == asc) { selp[lo] = y; selp[hi] = x; }
+      }
+      __syncthreads();
+    }
+  }
+  for (int j = tid; j < K; j += SC_THREADS) ob[j] = j < (int)nsel ? (int32_t)selp[j] : -1;
 }
 
 // ---------------------------------------------------------------- select (long)
@@ -632,6 +692,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_finish_kernel(
   __shared__ uint32_t ctl[8];
   __shared__ uint32_t scan_tmp[SEL_THREADS / 64 + 1];
   __shared__ uint64_t lcand[SEL_LDS_CAP];
+  __shared__ uint64_t red[16];
   const int b = blockIdx.x;
   const int64_t nb = min((int64_t)n_entries[b], max_n);
   int32_t* ob = out + (int64_t)b * out_stride;
@@ -656,7 +717,6 @@ __global__ __launch_bounds__(SEL_THREADS) void select_finish_kernel(
         atomicOr(&bm[pos >> 5], 1u << (pos & 31));
       }
     } else {
-      // candidates share the 12 bin bits (composite bits 63..52): radix from bit 51
       const bool in_lds = ncand <= SEL_LDS_CAP;
       if (in_lds) {
         for (uint32_t i = threadIdx.x; i < ncand; i += SEL_THREADS) lcand[i] = cb[i];
@@ -664,7 +724,8 @@ __global__ __launch_bounds__(SEL_THREADS) void select_finish_kernel(
       }
       const uint64_t* src = in_lds ? (const uint64_t*)lcand : cb;
       uint64_t prefix, mask;
-      radix_select_u64(src, ncand, need, 44, h, ctl, &prefix, &mask);
+      const int top = radix_top_shift(src, ncand, red);
+      radix_select_u64(src, ncand, need, top, h, ctl, &prefix, &mask);
       for (uint32_t i = threadIdx.x; i < ncand; i += SEL_THREADS) {
         const uint64_t c = src[i];
         if ((c & mask) >= prefix) {
