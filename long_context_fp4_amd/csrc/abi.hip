@@ -40,7 +40,7 @@ size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // the place of any block depends on B or max_n: the scratch regions behind it
 // can never overlap a control block of a later call with other sizes.
 struct IndexerWs {
-  size_t ctrl, bitmap, cand, scores, summ, wgc, gscr, total;
+  size_t ctrl, bitmap, cand, scores, hdr, summ, wgc, gscr, total;
   int64_t slots, bm_words, nblk, gscr_stride;
 };
 
@@ -57,6 +57,7 @@ IndexerWs indexer_layout(int B, int64_t max_n, int cand_stride) {
   L.cand = off;   off = round_up(off + (size_t)B * L.slots * 8, 256);
   L.scores = off; off = round_up(off + (size_t)B * L.slots * 4, 256);
   L.nblk = (L.slots + csa2::kScoreChunk - 1) / csa2::kScoreChunk;
+  L.hdr = off;    off = round_up(off + (size_t)B * L.nblk * 8, 256);
   L.summ = off;   off = round_up(off + (size_t)B * L.nblk * csa2::kSumWords * 4, 256);
   L.wgc = off;    off = round_up(off + (size_t)B * L.nblk * csa2::kCandCap * 8, 256);
   L.gscr_stride = L.slots > L.nblk * csa2::kCandCap ? L.slots : L.nblk * csa2::kCandCap;
@@ -132,6 +133,8 @@ int run_indexer(const uint8_t* ik, const uint8_t* iks, const int64_t* entry_offs
   sb.ctrl = ws + L.ctrl;
   sb.bitmap = (uint32_t*)(ws + L.bitmap);
   sb.bm_stride = L.bm_words;
+  sb.hdr = (uint64_t*)(ws + L.hdr);
+  sb.hdr_stride = L.nblk;
   sb.summ = (uint32_t*)(ws + L.summ);
   sb.summ_stride = L.nblk * csa2::kSumWords;
   sb.wgc = (uint64_t*)(ws + L.wgc);

@@ -59,7 +59,9 @@ constexpr int BIN_SHIFT = 20;
 constexpr int SUM_PAIRS = kSumWords;   // (bin, count) pairs a workgroup reports above its cutoff
 constexpr int CAND_CAP = kCandCap;     // candidates a workgroup reports in direct top-k mode
 
-constexpr int LAST_LDS_CANDS = (NBINS + SC_CHUNK) / 2;   // u64 candidates the last workgroup keeps in LDS
+constexpr int FIN_THREADS = 1024;  // finish workgroup of the direct top-k
+constexpr int FIN_MAX_WG = kFinMaxWg;        // score workgroups per sequence the finish reads
+constexpr int FIN_LDS_CANDS = kFinLdsCands;  // candidates the direct finish keeps in LDS
 constexpr int SEL_THREADS = 256;
 constexpr int SEL_CHUNK = 4096;     // slots per select workgroup
 constexpr int SEL_LDS_CAP = 4096;   // candidates staged in LDS by the last select workgroup
@@ -114,6 +116,36 @@ __device__ __forceinline__ float sum_lane_groups(float v) {
 }
 
 // ---------------------------------------------------------------- radix select
+// Run by the 64 lanes of wave 0: among the 256 digit counts h (digit 255 is the
+// best), finds the digit that holds the need-th best element (1 <= need <= the
+// sum of h): ctl[0] = digit, ctl[1] = count strictly above it, ctl[2] = count
+// with it. Lane l scans digits 255-4l .. 252-4l.
+__device__ __forceinline__ void digit_kth(const uint32_t* h, uint32_t need, uint32_t* ctl) {
+  const int l = threadIdx.x & 63;
+  uint32_t c4[4], loc = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) { c4[q] = h[255 - 4 * l - q]; loc += c4[q]; }
+  uint32_t inc = loc;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    uint32_t y = __shfl_up(inc, d, 64);
+    if (l >= d) inc += y;
+  }
+  const uint32_t pre = inc - loc;
+  if (pre < need && pre + loc >= need) {
+    uint32_t cum = pre;
+    for (int q = 0; q < 4; ++q) {
+      if (cum + c4[q] >= need) {
+        ctl[0] = 255 - 4 * l - q;
+        ctl[1] = cum;
+        ctl[2] = c4[q];
+        break;
+      }
+      cum += c4[q];
+    }
+  }
+}
+
 // Among n distinct 64-bit composites at `v` (LDS, or global memory read after
 // an acquire fence), find the `need` largest (0 < need < n); all composites
 // agree on the bits above top_shift + 7. On return the composites c with
@@ -131,32 +163,7 @@ __device__ void radix_select_u64(const uint64_t* v, uint32_t n, uint32_t need, i
       if ((c & pmask) == prefix) atomicAdd(&h[(uint32_t)(c >> shift) & 255u], 1u);
     }
     __syncthreads();
-    if (threadIdx.x < 64) {
-      // lane l owns digits 255-4l .. 252-4l (best digits first)
-      const int l = threadIdx.x;
-      uint32_t c4[4], loc = 0;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) { c4[q] = h[255 - 4 * l - q]; loc += c4[q]; }
-      uint32_t inc = loc;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        uint32_t y = __shfl_up(inc, d, 64);
-        if (l >= d) inc += y;
-      }
-      const uint32_t pre = inc - loc;
-      if (pre < need && pre + loc >= need) {
-        uint32_t cum = pre;
-        for (int q = 0; q < 4; ++q) {
-          if (cum + c4[q] >= need) {
-            ctl[0] = 255 - 4 * l - q;   // digit
-            ctl[1] = cum;               // count strictly above this digit
-            ctl[2] = c4[q];             // count with this digit
-            break;
-          }
-          cum += c4[q];
-        }
-      }
-    }
+    if (threadIdx.x < 64) digit_kth(h, need, ctl);
     __syncthreads();
     const uint32_t d = ctl[0], above = ctl[1], cnt = ctl[2];
     __syncthreads();
@@ -194,11 +201,11 @@ __device__ int radix_top_shift(const uint64_t* v, uint32_t n, uint64_t* red) {
     o |= __shfl_xor(o, d, 64);
     a &= __shfl_xor(a, d, 64);
   }
-  const int nw = blockDim.x >> 6;
-  if ((threadIdx.x & 63) == 0) { red[threadIdx.x >> 6] = o; red[8 + (threadIdx.x >> 6)] = a; }
+  const int nw = blockDim.x >> 6;          // at most 16 waves; red holds 32 words
+  if ((threadIdx.x & 63) == 0) { red[threadIdx.x >> 6] = o; red[16 + (threadIdx.x >> 6)] = a; }
   __syncthreads();
   o = 0; a = ~0ull;
-  for (int i = 0; i < nw; ++i) { o |= red[i]; a &= red[8 + i]; }
+  for (int i = 0; i < nw; ++i) { o |= red[i]; a &= red[16 + i]; }
   __syncthreads();
   const uint64_t diff = o ^ a;
   if (diff == 0) return 0;
@@ -249,14 +256,14 @@ __device__ __forceinline__ uint64_t composite(uint32_t key, uint32_t pos) {
   return ((uint64_t)key << 32) | (uint64_t)(0xFFFFFFFFu - pos);
 }
 
-// Block-wide max / or of one value per thread (blockDim.x == SC_THREADS).
+// Block-wide max / or of one value per thread; tmp holds blockDim.x/64 words of LDS.
 __device__ uint32_t block_max_u32(uint32_t v, uint32_t* tmp) {
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, d, 64));
   if ((threadIdx.x & 63) == 0) tmp[threadIdx.x >> 6] = v;
   __syncthreads();
   uint32_t r = tmp[0];
-  for (int i = 1; i < SC_THREADS / 64; ++i) r = max(r, tmp[i]);
+  for (int i = 1; i < (int)(blockDim.x >> 6); ++i) r = max(r, tmp[i]);
   __syncthreads();
   return r;
 }
@@ -266,21 +273,23 @@ __device__ uint32_t block_or_u32(uint32_t v, uint32_t* tmp) {
   if ((threadIdx.x & 63) == 0) tmp[threadIdx.x >> 6] = v;
   __syncthreads();
   uint32_t r = 0;
-  for (int i = 0; i < SC_THREADS / 64; ++i) r |= tmp[i];
+  for (int i = 0; i < (int)(blockDim.x >> 6); ++i) r |= tmp[i];
   __syncthreads();
   return r;
 }
 
-// Bin holding the `need`-th best key of an LDS histogram (thread t owns bins
-// NBINS-1-16t .. NBINS-16-16t). Returns the number of keys counted in *total,
+// Bin holding the `need`-th best key of an LDS histogram (with BPT = NBINS /
+// THREADS, thread t owns bins NBINS-1-BPT*t .. NBINS-BPT-BPT*t). Returns the number of keys counted in *total,
 // the bin in ctl[0] and the count strictly above it in ctl[1] (ctl[0] = -1
 // when total < need). All threads must call it.
+template <int THREADS>
 __device__ void hist_kth_bin(const uint32_t* lhist, uint32_t need, uint32_t* scan_tmp, uint32_t* ctl,
                              uint32_t* total_out) {
-  uint32_t hv[16], local = 0;
+  constexpr int BPT = NBINS / THREADS;
+  uint32_t hv[BPT], local = 0;
 #pragma unroll
-  for (int q = 0; q < 16; ++q) {
-    hv[q] = lhist[NBINS - 1 - (16 * threadIdx.x + q)];
+  for (int q = 0; q < BPT; ++q) {
+    hv[q] = lhist[NBINS - 1 - (BPT * threadIdx.x + q)];
     local += hv[q];
   }
   if (threadIdx.x == 0) { ctl[0] = 0xFFFFFFFFu; ctl[1] = 0; }
@@ -289,9 +298,9 @@ __device__ void hist_kth_bin(const uint32_t* lhist, uint32_t need, uint32_t* sca
   if (prefix < need && prefix + local >= need) {
     uint32_t cum = prefix;
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
+    for (int q = 0; q < BPT; ++q) {
       if (cum + hv[q] >= need) {
-        ctl[0] = NBINS - 1 - (16 * threadIdx.x + q);
+        ctl[0] = NBINS - 1 - (BPT * threadIdx.x + q);
         ctl[1] = cum;
         break;
       }
@@ -423,17 +432,22 @@ __global__ __launch_bounds__(SC_THREADS) void score_kernel(
   }
   if (SEL == SEL_NONE) return;
 
-  // ---- local histogram and cutoff (every slot of a Full pass is a valid position)
+  // ---- local histogram and cutoff (every slot of a Full pass is a valid position).
+  // The workgroup reports into its own slot of the workspace (a header word and
+  // a list), so no global atomics are needed.
   for (int i = tid; i < end; i += SC_THREADS) atomicAdd(&lhist[score_key(lsc[i]) >> BIN_SHIFT], 1u);
   __syncthreads();
-  const int64_t budget64 = 4 * (((int64_t)K * SC_CHUNK + n_pos - 1) / n_pos) + 32;
+  const int64_t nwg = (n_pos + SC_CHUNK - 1) / SC_CHUNK;
+  int64_t budget64 = 4 * (((int64_t)K * SC_CHUNK + n_pos - 1) / n_pos) + 32;
+  if (SEL == SEL_DIRECT) budget64 = min(budget64, max((int64_t)8, (int64_t)FIN_LDS_CANDS / nwg));
   const uint32_t budget = (uint32_t)min(budget64, (int64_t)end);
   uint32_t cnt_all;
-  hist_kth_bin(lhist, budget, scan_tmp, ctl, &cnt_all);
-  const uint32_t cut = (ctl[0] == 0xFFFFFFFFu) ? 0u : ctl[0];   // fewer keys than the budget: keep all
-  SelState* st = ctrl_state(sb.ctrl, b);
-  // (bin, count) pairs for bins >= cut, appended to the sequence's pair list
-  {
+  hist_kth_bin<SC_THREADS>(lhist, budget, scan_tmp, ctl, &cnt_all);
+  const uint32_t cbin = ctl[0], cabove = ctl[1];
+  uint64_t* hdr = sb.hdr + (int64_t)b * sb.hdr_stride + blockIdx.x;
+  if (SEL == SEL_THRESHOLD) {
+    // (bin, count) pairs for the non-empty bins >= cut
+    const uint32_t cut = (cbin == 0xFFFFFFFFu) ? 0u : cbin;   // fewer keys than the budget: keep all
     uint32_t np = 0;
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
@@ -442,196 +456,287 @@ __global__ __launch_bounds__(SC_THREADS) void score_kernel(
     }
     uint32_t tot;
     uint32_t off = block_exclusive_scan(np, scan_tmp, &tot);
-    const uint32_t keep = min(tot, (uint32_t)SUM_PAIRS);
-    if (tid == 0) {
-      ctl[2] = atomicAdd(&st->npairs, keep);
-      atomicMax(&st->cut_max, cut);
-      if (tot > SUM_PAIRS) atomicOr(&st->flags, 1u);
-    }
-    __syncthreads();
-    uint32_t* pl = sb.summ + (int64_t)b * sb.summ_stride + ctl[2];
+    uint32_t* pl = sb.summ + (int64_t)b * sb.summ_stride + (int64_t)blockIdx.x * SUM_PAIRS;
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
       const uint32_t bin = NBINS - 1 - (16 * tid + q);
       const uint32_t c = lhist[bin];
       if (bin >= cut && c != 0) {
-        if (off < keep) pl[off] = (bin << 16) | c;
+        if (off < SUM_PAIRS) pl[off] = (bin << 16) | c;
         ++off;
       }
     }
+    if (tid == 0) *hdr = ((uint64_t)cut << 32) | (tot > SUM_PAIRS ? 0x80000000u : tot);
   }
   if (SEL == SEL_DIRECT) {
-    // this chunk's candidates (every slot whose key bin is >= cut), appended to the sequence's list
-    uint32_t nc = 0;
-    for (int i = tid; i < end; i += SC_THREADS) nc += (score_key(lsc[i]) >> BIN_SHIFT) >= cut ? 1u : 0u;
-    uint32_t tot;
-    uint32_t off = block_exclusive_scan(nc, scan_tmp, &tot);
-    const uint32_t keep = min(tot, (uint32_t)CAND_CAP);
-    if (tid == 0) {
-      ctl[3] = atomicAdd(&st->nsc, keep);
-      if (tot > CAND_CAP) atomicOr(&st->flags, 2u);
+    // refine the cutoff to the top 20 key bits: 256 sub-bins of the cutoff bin
+    uint32_t fine = 0;                                       // fewer keys than the budget: keep all
+    if (cbin != 0xFFFFFFFFu) {
+      uint32_t* h2 = lhist;                                  // every read of the 4096 bins is done
+      h2[tid] = 0;
+      __syncthreads();
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int i = 4 * tid + q;
+        if (i < end) {
+          const uint32_t key = score_key(lsc[i]);
+          if ((key >> BIN_SHIFT) == cbin) atomicAdd(&h2[(key >> 12) & 255u], 1u);
+        }
+      }
+      __syncthreads();
+      if (tid < 64) digit_kth(h2, budget - cabove, ctl + 4);
+      __syncthreads();
+      fine = (cbin << 8) | ctl[4];
     }
-    __syncthreads();
-    uint64_t* wc = sb.wgc + (int64_t)b * sb.wgc_stride + ctl[3];
-    for (int i = tid; i < end; i += SC_THREADS) {
-      const uint32_t key = score_key(lsc[i]);
-      if ((key >> BIN_SHIFT) >= cut) {
-        if (off < keep) wc[off] = composite(key, (uint32_t)(start + i));
+    // candidates: every slot whose top 20 key bits are >= fine, in slot order
+    // (thread t owns slots 4t .. 4t+3)
+    uint32_t keys[4], m = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int i = 4 * tid + q;
+      keys[q] = i < end ? score_key(lsc[i]) : 0u;
+      m |= ((i < end && (keys[q] >> 12) >= fine) ? 1u : 0u) << q;
+    }
+    uint32_t tot;
+    uint32_t off = block_exclusive_scan((uint32_t)__popc(m), scan_tmp, &tot);
+    uint64_t* wc = sb.wgc + (int64_t)b * sb.wgc_stride + (int64_t)blockIdx.x * CAND_CAP;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if ((m >> q) & 1u) {
+        if (off < CAND_CAP) wc[off] = composite(keys[q], (uint32_t)(start + 4 * tid + q));
         ++off;
       }
     }
+    if (tid == 0) *hdr = ((uint64_t)fine << 32) | (tot > CAND_CAP ? 0x80000000u : tot);
   }
-
 }
 
 // ---------------------------------------------------------------- finish (one workgroup per sequence)
-// Runs after the score pass: merges the sequence's (bin, count) pairs, finds
-// the bin of the K-th best key (exactly, or from a full histogram of the
-// sequence's scores when the reported bins do not reach it), then either hands
-// the bin to select_kernel (SEL_THRESHOLD) or selects the K best among the
-// gathered candidates and writes them in ascending order (SEL_DIRECT).
-template <int SEL>
-__global__ __launch_bounds__(SC_THREADS) void finish_kernel(
+// Runs after the score pass. Every score workgroup w of the sequence left a
+// header word (count | overflow bit 31, cutoff << 32) and a list in its own
+// slot. The cutoffs differ per workgroup; at or above the highest of them
+// every workgroup's list is complete.
+
+// Threshold bin of the K-th best key from the (bin, count) pair lists, exact
+// when the merged bins at or above the highest cutoff hold at least K keys;
+// otherwise from a histogram of every score of the sequence. The bin and the
+// count above it go to the control block for select_kernel.
+__global__ __launch_bounds__(SC_THREADS) void finish_threshold_kernel(
     const int32_t* __restrict__ n_entries, int64_t max_n, const float* __restrict__ scores, int64_t sstride,
-    SelBufs sb, int K, int32_t* __restrict__ out, int out_stride) {
-  __shared__ uint32_t lbuf[NBINS + SC_CHUNK];     // histogram; candidates later
-  __shared__ uint32_t hsel[256 + kDirectMaxK];     // radix histogram, then the selected positions
-  __shared__ uint64_t scan_red[16];
+    SelBufs sb, int K) {
+  __shared__ uint32_t lhist[NBINS];
+  __shared__ uint32_t lcnt[FIN_MAX_WG];
   __shared__ uint32_t scan_tmp[SC_THREADS / 64 + 1];
   __shared__ uint32_t ctl[8];
-  uint32_t* lhist = lbuf;
   const int b = blockIdx.x, tid = threadIdx.x;
   const int64_t n_pos = min((int64_t)n_entries[b], max_n);
   SelState* st = ctrl_state(sb.ctrl, b);
-  const float* sall = scores + (int64_t)b * sstride;
-  int32_t* ob = out ? out + (int64_t)b * out_stride : nullptr;
-  const uint32_t bmax = st->cut_max, flags = st->flags, npairs = st->npairs, nsc = st->nsc;
-  __syncthreads();
-  if (tid == 0) { st->cut_max = 0; st->flags = 0; st->npairs = 0; st->nsc = 0; }
-
   if (n_pos <= K) {                       // every position is selected (or none exists)
-    if (SEL == SEL_THRESHOLD) {
-      if (tid == 0) { st->thr_bin = -1; st->above = 0; }
-    } else {
-      for (int j = tid; j < K; j += SC_THREADS) ob[j] = j < n_pos ? j : -1;
-    }
+    if (tid == 0) { st->thr_bin = -1; st->above = 0; }
     return;
   }
-  // merge the complete bins (>= bmax) of the pair list
+  const float* sall = scores + (int64_t)b * sstride;
+  const int64_t nw = (n_pos + SC_CHUNK - 1) / SC_CHUNK;
   for (int i = tid; i < NBINS; i += SC_THREADS) lhist[i] = 0;
-  __syncthreads();
-  {
-    const uint32_t* pl = sb.summ + (int64_t)b * sb.summ_stride;
-    for (uint32_t i = tid; i < npairs; i += SC_THREADS) {
-      const uint32_t v = pl[i];
-      if ((v >> 16) >= bmax) atomicAdd(&lhist[v >> 16], v & 0xFFFFu);
+  bool exact = false;
+  uint32_t T = 0, above = 0, tot = 0;
+  if (nw <= FIN_MAX_WG) {
+    const uint64_t* hd = sb.hdr + (int64_t)b * sb.hdr_stride;
+    uint32_t cmax = 0, ovf = 0;
+    for (int w = tid; w < nw; w += SC_THREADS) {
+      const uint64_t h = hd[w];
+      lcnt[w] = min((uint32_t)h & 0x7FFFFFFFu, (uint32_t)SUM_PAIRS);
+      ovf |= (uint32_t)h >> 31;
+      cmax = max(cmax, (uint32_t)(h >> 32));
+    }
+    cmax = block_max_u32(cmax, scan_tmp);
+    ovf = block_or_u32(ovf, scan_tmp);
+    if (ovf == 0) {
+      const uint32_t* pl = sb.summ + (int64_t)b * sb.summ_stride;
+      for (int64_t i = tid; i < nw * SUM_PAIRS; i += SC_THREADS) {
+        if ((uint32_t)(i % SUM_PAIRS) < lcnt[i / SUM_PAIRS]) {
+          const uint32_t v = pl[i];
+          if ((v >> 16) >= cmax) atomicAdd(&lhist[v >> 16], v & 0xFFFFu);
+        }
+      }
+      __syncthreads();
+      hist_kth_bin<SC_THREADS>(lhist, (uint32_t)K, scan_tmp, ctl, &tot);
+      exact = ctl[0] != 0xFFFFFFFFu;
+      T = ctl[0];
+      above = ctl[1];
     }
   }
-  __syncthreads();
-  uint32_t tot_hi;
-  hist_kth_bin(lhist, (uint32_t)K, scan_tmp, ctl, &tot_hi);
-  const bool exact = (flags & 1u) == 0 && ctl[0] != 0xFFFFFFFFu;
-  uint32_t T = ctl[0], above = ctl[1];
   if (!exact) {
-    // fallback: histogram of every score of the sequence
     __syncthreads();
     for (int i = tid; i < NBINS; i += SC_THREADS) lhist[i] = 0;
     __syncthreads();
     for (int64_t i = tid; i < n_pos; i += SC_THREADS) atomicAdd(&lhist[score_key(sall[i]) >> BIN_SHIFT], 1u);
     __syncthreads();
-    hist_kth_bin(lhist, (uint32_t)K, scan_tmp, ctl, &tot_hi);
+    hist_kth_bin<SC_THREADS>(lhist, (uint32_t)K, scan_tmp, ctl, &tot);
     T = ctl[0];
     above = ctl[1];
   }
-  if (SEL == SEL_THRESHOLD) {
-    if (tid == 0) { st->thr_bin = (int32_t)T; st->above = above; }
+  if (tid == 0) { st->thr_bin = (int32_t)T; st->above = above; }
+}
+
+// Direct top-K (K <= kDirectMaxK). The candidate lists hold, per workgroup,
+// every key whose top 20 bits reach its refined cutoff, in position order, so
+// their concatenation in workgroup order is in position order too. Keeping the
+// ones at or above the highest cutoff gives every key of the sequence there;
+// when they are at least K, the K best among them are the answer, and an
+// ordered compaction writes them ascending. Otherwise (a list overflowed, or
+// too few keys reach the highest cutoff, or the lists exceed LDS) every score
+// of the sequence is histogrammed and the keys in or above the K-th best bin
+// are gathered in position order instead.
+__global__ __launch_bounds__(FIN_THREADS) void finish_direct_kernel(
+    const int32_t* __restrict__ n_entries, int64_t max_n, const float* __restrict__ scores, int64_t sstride,
+    SelBufs sb, int K, int32_t* __restrict__ out, int out_stride) {
+  __shared__ uint64_t lc[FIN_LDS_CANDS];          // candidates; the fallback's histogram first
+  __shared__ uint32_t loff[FIN_MAX_WG + 1];       // list offsets of the workgroups
+  __shared__ uint32_t h[256];
+  __shared__ uint64_t red[32];
+  __shared__ uint32_t scan_tmp[FIN_THREADS / 64 + 1];
+  __shared__ uint32_t ctl[8];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int64_t n_pos = min((int64_t)n_entries[b], max_n);
+  int32_t* ob = out + (int64_t)b * out_stride;
+  if (n_pos <= K) {                       // every position is selected (or none exists)
+    for (int j = tid; j < K; j += FIN_THREADS) ob[j] = j < n_pos ? j : -1;
     return;
   }
-
-  // SEL_DIRECT: gather every key with bin >= T (the K best are among them)
-  __syncthreads();
-  uint64_t* lc = (uint64_t*)lbuf;
-  uint64_t* gs = sb.gscr + (int64_t)b * sb.gscr_stride;
-  if (tid == 0) ctl[4] = 0;
-  __syncthreads();
-  const bool from_list = exact && (flags & 2u) == 0;
-  if (from_list) {
-    // eight independent loads per thread in flight, then the filter
-    const uint64_t* wc = sb.wgc + (int64_t)b * sb.wgc_stride;
-    for (uint32_t base = 0; base < nsc; base += 8 * SC_THREADS) {
-      uint64_t cv[8];
+  const int64_t nw = (n_pos + SC_CHUNK - 1) / SC_CHUNK;
+  uint32_t nk = 0;
+  bool fast = false;
+  const uint64_t* src = lc;
+  if (nw <= FIN_MAX_WG) {
+    // list lengths -> offsets; thread t owns workgroups [w0, w1)
+    const uint64_t* hd = sb.hdr + (int64_t)b * sb.hdr_stride;
+    const int per = (int)((nw + FIN_THREADS - 1) / FIN_THREADS);
+    const int w0 = (int)min((int64_t)tid * per, nw), w1 = (int)min((int64_t)w0 + per, nw);
+    uint32_t cnt = 0, cmax = 0, ovf = 0;
+    for (int w = w0; w < w1; ++w) {
+      const uint64_t hv = hd[w];
+      const uint32_t c = (uint32_t)hv & 0x7FFFFFFFu;
+      ovf |= (uint32_t)hv >> 31;
+      cmax = max(cmax, (uint32_t)(hv >> 32));
+      loff[w] = c;
+      cnt += c;
+    }
+    uint32_t total;
+    uint32_t run = block_exclusive_scan(cnt, scan_tmp, &total);
+    for (int w = w0; w < w1; ++w) {
+      const uint32_t c = loff[w];
+      loff[w] = run;
+      run += c;
+    }
+    if (tid == 0) loff[nw] = total;
+    cmax = block_max_u32(cmax, scan_tmp);
+    ovf = block_or_u32(ovf, scan_tmp);
+    if (ovf == 0 && total <= (uint32_t)FIN_LDS_CANDS) {
+      // gather the lists in workgroup order (four independent loads per thread in flight)
+      const uint64_t* wc = sb.wgc + (int64_t)b * sb.wgc_stride;
+      for (uint32_t f0 = 0; f0 < total; f0 += 4 * FIN_THREADS) {
+        uint64_t v[4];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint32_t i = base + j * SC_THREADS + tid;
-        cv[j] = i < nsc ? wc[i] : 0ull;
-      }
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t f = min(f0 + q * FIN_THREADS + tid, total - 1);
+          int lo = 0, hi = (int)nw;                 // last workgroup with loff <= f
+          while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (loff[mid] <= f) lo = mid; else hi = mid;
+          }
+          v[q] = wc[(int64_t)lo * CAND_CAP + (f - loff[lo])];
+        }
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint32_t i = base + j * SC_THREADS + tid;
-        const bool take = i < nsc && (uint32_t)(cv[j] >> (32 + BIN_SHIFT)) >= T;
-        const uint32_t at = wave_append(take, &ctl[4]);
-        if (take) {
-          if (at < LAST_LDS_CANDS) lc[at] = cv[j];
-          gs[at] = cv[j];
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t f = f0 + q * FIN_THREADS + tid;
+          if (f < total) lc[f] = v[q];
         }
       }
+      __syncthreads();
+      // keep the keys at or above the highest cutoff, in order (in place: every
+      // thread holds its elements in registers before any is written)
+      {
+        const uint32_t per2 = (total + FIN_THREADS - 1) / FIN_THREADS;   // <= 16
+        const uint32_t i0 = min(tid * per2, total), i1 = min(i0 + per2, total);
+        uint64_t v[16];
+        uint32_t m = 0;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const uint32_t i = i0 + q;
+          v[q] = i < i1 ? lc[i] : 0ull;
+          m |= ((i < i1 && (uint32_t)(v[q] >> 44) >= cmax) ? 1u : 0u) << q;
+        }
+        uint32_t off = block_exclusive_scan((uint32_t)__popc(m), scan_tmp, &nk);
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+          if ((m >> q) & 1u) lc[off++] = v[q];
+        __syncthreads();
+      }
+      fast = nk >= (uint32_t)K;
     }
-  } else {
-    for (int64_t i0 = 0; i0 < n_pos; i0 += SC_THREADS) {
-      const int64_t i = i0 + tid;
+  }
+  if (!fast) {
+    const float* sall = scores + (int64_t)b * sstride;
+    uint32_t* hist = (uint32_t*)lc;
+    __syncthreads();
+    for (int i = tid; i < NBINS; i += FIN_THREADS) hist[i] = 0;
+    __syncthreads();
+    for (int64_t i = tid; i < n_pos; i += FIN_THREADS) atomicAdd(&hist[score_key(sall[i]) >> BIN_SHIFT], 1u);
+    __syncthreads();
+    uint32_t tot;
+    hist_kth_bin<FIN_THREADS>(hist, (uint32_t)K, scan_tmp, ctl, &tot);
+    const uint32_t T = ctl[0];             // defined: n_pos > K
+    const uint32_t ng = ctl[1] + hist[T];
+    __syncthreads();
+    uint64_t* gs = sb.gscr + (int64_t)b * sb.gscr_stride;
+    uint64_t* dst = ng <= (uint32_t)FIN_LDS_CANDS ? lc : gs;
+    uint32_t base = 0;
+    for (int64_t c0 = 0; c0 < n_pos; c0 += FIN_THREADS) {
+      const int64_t i = c0 + tid;
       const uint32_t key = i < n_pos ? score_key(sall[i]) : 0u;
       const bool take = i < n_pos && (key >> BIN_SHIFT) >= T;
-      const uint32_t at = wave_append(take, &ctl[4]);
-      if (take) {
-        const uint64_t c = composite(key, (uint32_t)i);
-        if (at < LAST_LDS_CANDS) lc[at] = c;
-        gs[at] = c;
+      uint32_t t2;
+      const uint32_t off = block_exclusive_scan(take ? 1u : 0u, scan_tmp, &t2);
+      if (take) dst[base + off] = composite(key, (uint32_t)i);
+      base += t2;
+    }
+    nk = base;
+    src = dst;
+    if (dst == gs) __threadfence_block();   // this workgroup reads its global copy back
+    __syncthreads();
+  }
+  // the K best of src[0, nk) (nk >= K), written in position order
+  uint64_t prefix = 0, mask = 0;
+  if (nk > (uint32_t)K) {
+    const int top = radix_top_shift(src, nk, red);
+    radix_select_u64(src, nk, (uint32_t)K, top, h, ctl, &prefix, &mask);
+  }
+  uint32_t base = 0;
+  for (uint32_t c0 = 0; c0 < nk; c0 += 16 * FIN_THREADS) {
+    const uint32_t cn = min(nk - c0, 16u * FIN_THREADS);
+    const uint32_t per = (cn + FIN_THREADS - 1) / FIN_THREADS;
+    const uint32_t i0 = c0 + min(tid * per, cn), i1 = c0 + min(tid * per + per, cn);
+    uint64_t v[16];
+    uint32_t m = 0;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const uint32_t i = i0 + q;
+      v[q] = i < i1 ? src[i] : 0ull;
+      m |= ((i < i1 && (v[q] & mask) >= prefix) ? 1u : 0u) << q;
+    }
+    uint32_t t3;
+    uint32_t off = base + block_exclusive_scan((uint32_t)__popc(m), scan_tmp, &t3);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      if ((m >> q) & 1u) {
+        if (off < (uint32_t)K) ob[off] = (int32_t)(0xFFFFFFFFu - (uint32_t)v[q]);
+        ++off;
       }
     }
+    base += t3;
   }
-  __syncthreads();
-  const uint32_t ncand = ctl[4];
-  const uint64_t* src = ncand <= LAST_LDS_CANDS ? (const uint64_t*)lc : (const uint64_t*)gs;
-  if (ncand > LAST_LDS_CANDS) __threadfence_block();   // this workgroup reads its global copy back
-  __syncthreads();
-  // the K best composites -> positions in selp[] (any order)
-  uint32_t* selp = hsel + 256;
-  if (tid == 0) ctl[5] = 0;
-  __syncthreads();
-  if (ncand <= (uint32_t)K) {
-    for (uint32_t i = tid; i < ncand; i += SC_THREADS) selp[i] = 0xFFFFFFFFu - (uint32_t)src[i];
-    if (tid == 0) ctl[5] = ncand;
-  } else {
-    uint64_t prefix, mask;
-    const int top = radix_top_shift(src, ncand, (uint64_t*)scan_red);
-    radix_select_u64(src, ncand, (uint32_t)K, top, hsel, ctl, &prefix, &mask);
-    for (uint32_t i0 = 0; i0 < ncand; i0 += SC_THREADS) {
-      const uint32_t i = i0 + tid;
-      const uint64_t c = i < ncand ? src[i] : 0ull;
-      const bool take = i < ncand && (c & mask) >= prefix;
-      const uint32_t at = wave_append(take, &ctl[5]);
-      if (take) selp[at] = 0xFFFFFFFFu - (uint32_t)c;
-    }
-  }
-  __syncthreads();
-  // ascending output: bitonic sort of the (at most kDirectMaxK) positions in LDS,
-  // padded with 0xFFFFFFFF
-  const uint32_t nsel = ctl[5];
-  for (uint32_t i = nsel + tid; i < (uint32_t)kDirectMaxK; i += SC_THREADS) selp[i] = 0xFFFFFFFFu;
-  __syncthreads();
-  for (int size = 2; size <= kDirectMaxK; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int t = tid; t < kDirectMaxK / 2; t += SC_THREADS) {
-        const int lo = 2 * t - (t & (stride - 1));
-        const int hi = lo + stride;
-        const bool asc = (lo & size) == 0;
-        const uint32_t x = selp[lo], y = selp[hi];
-        if ((x > y) == asc) { selp[lo] = y; selp[hi] = x; }
-      }
-      __syncthreads();
-    }
-  }
-  for (int j = tid; j < K; j += SC_THREADS) ob[j] = j < (int)nsel ? (int32_t)selp[j] : -1;
+  for (uint32_t j = base + tid; j < (uint32_t)K; j += FIN_THREADS) ob[j] = -1;
 }
 
 // ---------------------------------------------------------------- select (long)
@@ -692,7 +797,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_finish_kernel(
   __shared__ uint32_t ctl[8];
   __shared__ uint32_t scan_tmp[SEL_THREADS / 64 + 1];
   __shared__ uint64_t lcand[SEL_LDS_CAP];
-  __shared__ uint64_t red[16];
+  __shared__ uint64_t red[32];
   const int b = blockIdx.x;
   const int64_t nb = min((int64_t)n_entries[b], max_n);
   int32_t* ob = out + (int64_t)b * out_stride;
@@ -868,13 +973,12 @@ hipError_t launch_score(const uint8_t* ik, const uint8_t* iks, const int64_t* en
 hipError_t launch_finish(int sel, const int32_t* n_entries, int B, int64_t max_n, const float* scores,
                          int64_t sstride, const SelBufs& sb, int K, int32_t* out, int out_stride,
                          hipStream_t stream) {
-  dim3 grid((unsigned)B), block(SC_THREADS);
   if (sel == SEL_DIRECT)
-    hipLaunchKernelGGL(finish_kernel<SEL_DIRECT>, grid, block, 0, stream, n_entries, max_n, scores, sstride, sb,
-                       K, out, out_stride);
+    hipLaunchKernelGGL(finish_direct_kernel, dim3((unsigned)B), dim3(FIN_THREADS), 0, stream, n_entries, max_n,
+                       scores, sstride, sb, K, out, out_stride);
   else
-    hipLaunchKernelGGL(finish_kernel<SEL_THRESHOLD>, grid, block, 0, stream, n_entries, max_n, scores, sstride,
-                       sb, K, out, out_stride);
+    hipLaunchKernelGGL(finish_threshold_kernel, dim3((unsigned)B), dim3(SC_THREADS), 0, stream, n_entries,
+                       max_n, scores, sstride, sb, K);
   return hipGetLastError();
 }
 

@@ -12,11 +12,7 @@ struct SelState {
   int32_t thr_bin;        // histogram bin holding the K-th best key (-1: all selected)
   uint32_t above;         // keys in bins above thr_bin
   uint32_t ncand;         // select pass: candidates appended from thr_bin
-  uint32_t cut_max;       // score pass: highest local cutoff bin over the workgroups
-  uint32_t flags;         // score pass: 1 = a pair list overflowed, 2 = a candidate list overflowed
-  uint32_t npairs;        // score pass: (bin, count) pairs appended to the sequence's list
-  uint32_t nsc;           // score pass: candidates appended to the sequence's list
-  uint32_t pad[7];
+  uint32_t pad[11];
 };
 static_assert(sizeof(SelState) == 64, "control block header");
 
@@ -39,15 +35,19 @@ constexpr int kScoreChunk = 1024;     // slots per score workgroup
 constexpr int kSumWords = 32;         // (bin, count) pairs a workgroup may report
 constexpr int kCandCap = 256;         // candidates a workgroup reports in direct mode
 constexpr int kDirectMaxK = 512;      // largest k the score pass selects by itself
+constexpr int kFinMaxWg = 2048;       // score workgroups per sequence whose slots the finish reads
+constexpr int kFinLdsCands = 16384;   // candidates the direct finish holds in LDS
 
 // Workspace views used by the score pass's selection (per-sequence strides).
 struct SelBufs {
   uint8_t* ctrl;        // control blocks (SelState + histogram), fixed places
   uint32_t* bitmap;     // [B][bm_stride] words; the score pass clears its chunk's words
   int64_t bm_stride;
-  uint32_t* summ;       // [B][summ_stride] words: the sequence's (bin, count) pair list
+  uint64_t* hdr;        // [B][hdr_stride]: one header word per score workgroup
+  int64_t hdr_stride;
+  uint32_t* summ;       // [B][summ_stride] words: kSumWords (bin, count) pairs per workgroup
   int64_t summ_stride;
-  uint64_t* wgc;        // [B][wgc_stride]: the sequence's candidate list (direct mode)
+  uint64_t* wgc;        // [B][wgc_stride]: kCandCap candidates per workgroup (direct mode)
   int64_t wgc_stride;
   uint64_t* gscr;       // [B][gscr_stride]: gathered candidates that do not fit LDS
   int64_t gscr_stride;
