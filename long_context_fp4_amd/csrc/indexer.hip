@@ -62,6 +62,7 @@ constexpr int CAND_CAP = kCandCap;     // candidates a workgroup reports in dire
 constexpr int FIN_THREADS = 1024;  // finish workgroup of the direct top-k
 constexpr int FIN_MAX_WG = kFinMaxWg;        // score workgroups per sequence the finish reads
 constexpr int FIN_LDS_CANDS = kFinLdsCands;  // candidates the direct finish keeps in LDS
+constexpr int FIN_SUB_CAP = 4096;   // keys of the threshold bin the direct finish keeps in LDS
 constexpr int SEL_THREADS = 256;
 constexpr int SEL_CHUNK = 4096;     // slots per select workgroup
 constexpr int SEL_LDS_CAP = 4096;   // candidates staged in LDS by the last select workgroup
@@ -73,29 +74,16 @@ constexpr int SMALL_MAX = 16384;
 // the total in *total. `tmp` holds at least blockDim.x/64 + 1 words of LDS.
 __device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* tmp, uint32_t* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    uint32_t y = __shfl_up(x, d, 64);
-    if (lane >= d) x += y;
-  }
+  const uint32_t x = wave_incl_sum(v);
   if (lane == 63) tmp[wave] = x;
   __syncthreads();
-  if (wave == 0) {
-    uint32_t t = lane < nw ? tmp[lane] : 0u, s = t;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      uint32_t y = __shfl_up(s, d, 64);
-      if (lane >= d) s += y;
-    }
-    if (lane < nw) tmp[lane] = s - t;
-    if (lane == nw - 1) tmp[nw] = s;
-  }
+  // the wave totals, scanned across lanes 0 .. nw-1 of every wave
+  const uint32_t t = lane < nw ? tmp[lane] : 0u;
+  const uint32_t ti = wave_incl_sum(t);
+  const uint32_t pre = readlane_u32(ti - t, wave);
+  *total = readlane_u32(ti, nw - 1);
   __syncthreads();
-  uint32_t r = tmp[wave] + x - v;
-  *total = tmp[nw];
-  __syncthreads();
-  return r;
+  return pre + x - v;
 }
 
 // ---------------------------------------------------------------- scoring helpers
@@ -125,13 +113,7 @@ __device__ __forceinline__ void digit_kth(const uint32_t* h, uint32_t need, uint
   uint32_t c4[4], loc = 0;
 #pragma unroll
   for (int q = 0; q < 4; ++q) { c4[q] = h[255 - 4 * l - q]; loc += c4[q]; }
-  uint32_t inc = loc;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    uint32_t y = __shfl_up(inc, d, 64);
-    if (l >= d) inc += y;
-  }
-  const uint32_t pre = inc - loc;
+  const uint32_t pre = wave_incl_sum(loc) - loc;
   if (pre < need && pre + loc >= need) {
     uint32_t cum = pre;
     for (int q = 0; q < 4; ++q) {
@@ -149,24 +131,27 @@ __device__ __forceinline__ void digit_kth(const uint32_t* h, uint32_t need, uint
 // Among n distinct 64-bit composites at `v` (LDS, or global memory read after
 // an acquire fence), find the `need` largest (0 < need < n); all composites
 // agree on the bits above top_shift + 7. On return the composites c with
-// (c & *mask_out) >= *prefix_out are exactly the `need` largest. All threads of
-// the workgroup must call it.
+// (c & *mask_out) >= *prefix_out are exactly the `need` largest. h holds 512
+// words and ctl 8 words of LDS. All threads of the workgroup must call it.
 __device__ void radix_select_u64(const uint64_t* v, uint32_t n, uint32_t need, int top_shift,
                                  uint32_t* h, uint32_t* ctl, uint64_t* prefix_out, uint64_t* mask_out) {
+  // h: two 256-bin histograms and ctl: two 4-word results, alternating by pass,
+  // so each pass needs two barriers
   uint64_t prefix = 0, pmask = 0;
   int shift = top_shift;
-  for (;;) {
-    for (int i = threadIdx.x; i < 256; i += blockDim.x) h[i] = 0;
-    __syncthreads();
+  for (int i = threadIdx.x; i < 256; i += blockDim.x) h[i] = 0;
+  __syncthreads();
+  for (int p = 0;; p ^= 1) {
+    uint32_t* hp = h + 256 * p;
     for (uint32_t i = threadIdx.x; i < n; i += blockDim.x) {
       const uint64_t c = v[i];
-      if ((c & pmask) == prefix) atomicAdd(&h[(uint32_t)(c >> shift) & 255u], 1u);
+      if ((c & pmask) == prefix) atomicAdd(&hp[(uint32_t)(c >> shift) & 255u], 1u);
     }
     __syncthreads();
-    if (threadIdx.x < 64) digit_kth(h, need, ctl);
+    if (threadIdx.x < 64) digit_kth(hp, need, ctl + 4 * p);
+    for (int i = threadIdx.x; i < 256; i += blockDim.x) h[256 * (p ^ 1) + i] = 0;
     __syncthreads();
-    const uint32_t d = ctl[0], above = ctl[1], cnt = ctl[2];
-    __syncthreads();
+    const uint32_t d = ctl[4 * p], above = ctl[4 * p + 1], cnt = ctl[4 * p + 2];
     prefix |= (uint64_t)d << shift;
     pmask |= (uint64_t)255 << shift;
     need -= above;
@@ -185,7 +170,7 @@ __device__ __forceinline__ uint32_t wave_append(bool take, uint32_t* counter) {
   if (m) {
     const int leader = __ffsll((long long)m) - 1;
     if (lane == leader) base = atomicAdd(counter, (uint32_t)__popcll(m));
-    base = __shfl(base, leader, 64);
+    base = readlane_u32(base, leader);
   }
   return base + (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
 }
@@ -196,17 +181,16 @@ __device__ __forceinline__ uint32_t wave_append(bool take, uint32_t* counter) {
 __device__ int radix_top_shift(const uint64_t* v, uint32_t n, uint64_t* red) {
   uint64_t o = 0, a = ~0ull;
   for (uint32_t i = threadIdx.x; i < n; i += blockDim.x) { o |= v[i]; a &= v[i]; }
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) {
-    o |= __shfl_xor(o, d, 64);
-    a &= __shfl_xor(a, d, 64);
-  }
-  const int nw = blockDim.x >> 6;          // at most 16 waves; red holds 32 words
-  if ((threadIdx.x & 63) == 0) { red[threadIdx.x >> 6] = o; red[16 + (threadIdx.x >> 6)] = a; }
+  o = ((uint64_t)wave_or_u32((uint32_t)(o >> 32)) << 32) | wave_or_u32((uint32_t)o);
+  a = ((uint64_t)wave_and_u32((uint32_t)(a >> 32)) << 32) | wave_and_u32((uint32_t)a);
+  const int nw = blockDim.x >> 6, lane = threadIdx.x & 63;   // at most 16 waves; red holds 32 words
+  if (lane == 0) { red[threadIdx.x >> 6] = o; red[16 + (threadIdx.x >> 6)] = a; }
   __syncthreads();
-  o = 0; a = ~0ull;
-  for (int i = 0; i < nw; ++i) { o |= red[i]; a &= red[16 + i]; }
+  o = lane < nw ? red[lane] : 0ull;
+  a = lane < nw ? red[16 + lane] : ~0ull;
   __syncthreads();
+  o = ((uint64_t)wave_or_u32((uint32_t)(o >> 32)) << 32) | wave_or_u32((uint32_t)o);
+  a = ((uint64_t)wave_and_u32((uint32_t)(a >> 32)) << 32) | wave_and_u32((uint32_t)a);
   const uint64_t diff = o ^ a;
   if (diff == 0) return 0;
   const int hb = 63 - __clzll(diff);
@@ -258,22 +242,30 @@ __device__ __forceinline__ uint64_t composite(uint32_t key, uint32_t pos) {
 
 // Block-wide max / or of one value per thread; tmp holds blockDim.x/64 words of LDS.
 __device__ uint32_t block_max_u32(uint32_t v, uint32_t* tmp) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, d, 64));
-  if ((threadIdx.x & 63) == 0) tmp[threadIdx.x >> 6] = v;
+  const int lane = threadIdx.x & 63;
+  v = wave_max_u32(v);
+  if (lane == 0) tmp[threadIdx.x >> 6] = v;
   __syncthreads();
-  uint32_t r = tmp[0];
-  for (int i = 1; i < (int)(blockDim.x >> 6); ++i) r = max(r, tmp[i]);
+  const uint32_t r = wave_max_u32(lane < (int)(blockDim.x >> 6) ? tmp[lane] : 0u);
   __syncthreads();
   return r;
 }
-__device__ uint32_t block_or_u32(uint32_t v, uint32_t* tmp) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v |= (uint32_t)__shfl_xor((int)v, d, 64);
-  if ((threadIdx.x & 63) == 0) tmp[threadIdx.x >> 6] = v;
+// Both at once (one barrier pair); tmp holds 32 words.
+__device__ void block_max_or_u32(uint32_t* mx, uint32_t* ov, uint32_t* tmp) {
+  const int lane = threadIdx.x & 63, nw = blockDim.x >> 6;
+  const uint32_t m = wave_max_u32(*mx), o = wave_or_u32(*ov);
+  if (lane == 0) { tmp[threadIdx.x >> 6] = m; tmp[16 + (threadIdx.x >> 6)] = o; }
   __syncthreads();
-  uint32_t r = 0;
-  for (int i = 0; i < (int)(blockDim.x >> 6); ++i) r |= tmp[i];
+  *mx = wave_max_u32(lane < nw ? tmp[lane] : 0u);
+  *ov = wave_or_u32(lane < nw ? tmp[16 + lane] : 0u);
+  __syncthreads();
+}
+__device__ uint32_t block_or_u32(uint32_t v, uint32_t* tmp) {
+  const int lane = threadIdx.x & 63;
+  v = wave_or_u32(v);
+  if (lane == 0) tmp[threadIdx.x >> 6] = v;
+  __syncthreads();
+  const uint32_t r = wave_or_u32(lane < (int)(blockDim.x >> 6) ? tmp[lane] : 0u);
   __syncthreads();
   return r;
 }
@@ -438,7 +430,11 @@ __global__ __launch_bounds__(SC_THREADS) void score_kernel(
   for (int i = tid; i < end; i += SC_THREADS) atomicAdd(&lhist[score_key(lsc[i]) >> BIN_SHIFT], 1u);
   __syncthreads();
   const int64_t nwg = (n_pos + SC_CHUNK - 1) / SC_CHUNK;
-  int64_t budget64 = 4 * (((int64_t)K * SC_CHUNK + n_pos - 1) / n_pos) + 32;
+  // local budget: a multiple of the chunk's expected share of the top-K plus a
+  // margin, so that the highest cutoff over the workgroups still leaves at
+  // least K keys of the sequence above it (the finish checks this)
+  const int64_t share = ((int64_t)K * SC_CHUNK + n_pos - 1) / n_pos;
+  int64_t budget64 = SEL == SEL_DIRECT ? 2 * share + 16 : 4 * share + 32;
   if (SEL == SEL_DIRECT) budget64 = min(budget64, max((int64_t)8, (int64_t)FIN_LDS_CANDS / nwg));
   const uint32_t budget = (uint32_t)min(budget64, (int64_t)end);
   uint32_t cnt_all;
@@ -526,7 +522,7 @@ __global__ __launch_bounds__(SC_THREADS) void finish_threshold_kernel(
     SelBufs sb, int K) {
   __shared__ uint32_t lhist[NBINS];
   __shared__ uint32_t lcnt[FIN_MAX_WG];
-  __shared__ uint32_t scan_tmp[SC_THREADS / 64 + 1];
+  __shared__ uint32_t scan_tmp[32];
   __shared__ uint32_t ctl[8];
   const int b = blockIdx.x, tid = threadIdx.x;
   const int64_t n_pos = min((int64_t)n_entries[b], max_n);
@@ -549,8 +545,7 @@ __global__ __launch_bounds__(SC_THREADS) void finish_threshold_kernel(
       ovf |= (uint32_t)h >> 31;
       cmax = max(cmax, (uint32_t)(h >> 32));
     }
-    cmax = block_max_u32(cmax, scan_tmp);
-    ovf = block_or_u32(ovf, scan_tmp);
+    block_max_or_u32(&cmax, &ovf, scan_tmp);
     if (ovf == 0) {
       const uint32_t* pl = sb.summ + (int64_t)b * sb.summ_stride;
       for (int64_t i = tid; i < nw * SUM_PAIRS; i += SC_THREADS) {
@@ -579,50 +574,89 @@ __global__ __launch_bounds__(SC_THREADS) void finish_threshold_kernel(
   if (tid == 0) { st->thr_bin = (int32_t)T; st->above = above; }
 }
 
+// Ordered compaction over elements [0, n): pred(i) selects, emit(i, slot)
+// receives the element's place among the selected ones. Every wave owns a
+// contiguous range (a multiple of 64 elements) and ranks inside it with
+// ballots, so only one exchange of wave totals is needed. Returns the number
+// selected. All threads of the workgroup must call it.
+template <typename Pred, typename Emit>
+__device__ uint32_t ordered_compact(uint32_t n, Pred pred, Emit emit, uint32_t* tmp) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const uint32_t span = (n + 64 * nw - 1) / (64 * nw) * 64;
+  const uint32_t lo = min((uint32_t)wave * span, n), hi = min(lo + span, n);
+  uint32_t cnt = 0;
+  for (uint32_t i0 = lo; i0 < hi; i0 += 64) {
+    const uint32_t i = i0 + lane;
+    cnt += (uint32_t)__popcll(__ballot(i < hi && pred(i)));
+  }
+  if (lane == 0) tmp[wave] = cnt;
+  __syncthreads();
+  const uint32_t t = lane < nw ? tmp[lane] : 0u;
+  const uint32_t ti = wave_incl_sum(t);
+  uint32_t base = readlane_u32(ti - t, wave);
+  const uint32_t total = readlane_u32(ti, nw - 1);
+  __syncthreads();
+  for (uint32_t i0 = lo; i0 < hi; i0 += 64) {
+    const uint32_t i = i0 + lane;
+    const bool p = i < hi && pred(i);
+    const uint64_t m = __ballot(p);
+    if (p) emit(i, base + (uint32_t)__popcll(m & ((1ull << lane) - 1ull)));
+    base += (uint32_t)__popcll(m);
+  }
+  return total;
+}
+
 // Direct top-K (K <= kDirectMaxK). The candidate lists hold, per workgroup,
 // every key whose top 20 bits reach its refined cutoff, in position order, so
-// their concatenation in workgroup order is in position order too. Keeping the
-// ones at or above the highest cutoff gives every key of the sequence there;
-// when they are at least K, the K best among them are the answer, and an
-// ordered compaction writes them ascending. Otherwise (a list overflowed, or
-// too few keys reach the highest cutoff, or the lists exceed LDS) every score
-// of the sequence is histogrammed and the keys in or above the K-th best bin
-// are gathered in position order instead.
+// their concatenation in workgroup order is in position order too; the ones
+// at or above the highest cutoff are every key of the sequence there. While
+// the lists are copied to LDS, their 20-bit prefixes (relative to that cutoff,
+// the last bin holding everything 4095 or more above it) are histogrammed; the
+// bin of the K-th best prefix follows, all keys above it are selected, and the
+// few inside it are radix-selected on the full (key, position) composite. An
+// ordered compaction then writes the K positions ascending. When a list
+// overflowed, the lists exceed LDS or fewer than K keys reach the highest
+// cutoff, the same steps run on a histogram of every score of the sequence.
 __global__ __launch_bounds__(FIN_THREADS) void finish_direct_kernel(
     const int32_t* __restrict__ n_entries, int64_t max_n, const float* __restrict__ scores, int64_t sstride,
     SelBufs sb, int K, int32_t* __restrict__ out, int out_stride) {
-  __shared__ uint64_t lc[FIN_LDS_CANDS];          // candidates; the fallback's histogram first
+  __shared__ uint64_t lc[FIN_LDS_CANDS];          // the candidate lists, concatenated
+  __shared__ uint64_t sub[FIN_SUB_CAP];           // histogram, then the keys inside the threshold bin
   __shared__ uint32_t loff[FIN_MAX_WG + 1];       // list offsets of the workgroups
-  __shared__ uint32_t h[256];
+  __shared__ uint32_t h[512];
   __shared__ uint64_t red[32];
-  __shared__ uint32_t scan_tmp[FIN_THREADS / 64 + 1];
+  __shared__ uint32_t scan_tmp[32];
   __shared__ uint32_t ctl[8];
+  uint32_t* hist = (uint32_t*)sub;
   const int b = blockIdx.x, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  // the first header words are read before the sequence length is known
+  const int64_t nw_max = (max_n + SC_CHUNK - 1) / SC_CHUNK;
+  const uint64_t* hd = sb.hdr + (int64_t)b * sb.hdr_stride;
+  const uint64_t h0 = tid < nw_max ? hd[tid] : 0ull;
   const int64_t n_pos = min((int64_t)n_entries[b], max_n);
   int32_t* ob = out + (int64_t)b * out_stride;
   if (n_pos <= K) {                       // every position is selected (or none exists)
     for (int j = tid; j < K; j += FIN_THREADS) ob[j] = j < n_pos ? j : -1;
     return;
   }
+  for (int i = tid; i < NBINS; i += FIN_THREADS) hist[i] = 0;
   const int64_t nw = (n_pos + SC_CHUNK - 1) / SC_CHUNK;
-  uint32_t nk = 0;
   bool fast = false;
-  const uint64_t* src = lc;
+  uint32_t total = 0, cmax = 0;
   if (nw <= FIN_MAX_WG) {
     // list lengths -> offsets; thread t owns workgroups [w0, w1)
-    const uint64_t* hd = sb.hdr + (int64_t)b * sb.hdr_stride;
     const int per = (int)((nw + FIN_THREADS - 1) / FIN_THREADS);
     const int w0 = (int)min((int64_t)tid * per, nw), w1 = (int)min((int64_t)w0 + per, nw);
-    uint32_t cnt = 0, cmax = 0, ovf = 0;
+    uint32_t cnt = 0, ovf = 0;
     for (int w = w0; w < w1; ++w) {
-      const uint64_t hv = hd[w];
+      const uint64_t hv = (per == 1) ? h0 : hd[w];
       const uint32_t c = (uint32_t)hv & 0x7FFFFFFFu;
       ovf |= (uint32_t)hv >> 31;
       cmax = max(cmax, (uint32_t)(hv >> 32));
       loff[w] = c;
       cnt += c;
     }
-    uint32_t total;
     uint32_t run = block_exclusive_scan(cnt, scan_tmp, &total);
     for (int w = w0; w < w1; ++w) {
       const uint32_t c = loff[w];
@@ -630,113 +664,99 @@ __global__ __launch_bounds__(FIN_THREADS) void finish_direct_kernel(
       run += c;
     }
     if (tid == 0) loff[nw] = total;
-    cmax = block_max_u32(cmax, scan_tmp);
-    ovf = block_or_u32(ovf, scan_tmp);
+    block_max_or_u32(&cmax, &ovf, scan_tmp);
     if (ovf == 0 && total <= (uint32_t)FIN_LDS_CANDS) {
-      // gather the lists in workgroup order (four independent loads per thread in flight)
+      // copy the lists in workgroup order (wave v takes workgroups v, v + 16, ...,
+      // eight independent loads per lane in flight) and histogram the prefixes
       const uint64_t* wc = sb.wgc + (int64_t)b * sb.wgc_stride;
-      for (uint32_t f0 = 0; f0 < total; f0 += 4 * FIN_THREADS) {
-        uint64_t v[4];
+      constexpr int NWAVE = FIN_THREADS / 64;
+      auto take = [&](uint64_t c, uint32_t at) {
+        lc[at] = c;
+        const uint32_t p20 = (uint32_t)(c >> 44);
+        if (p20 >= cmax) atomicAdd(&hist[min(p20 - cmax, (uint32_t)NBINS - 1)], 1u);
+      };
+      for (int w0 = wave; w0 < nw; w0 += 4 * NWAVE) {
+        uint64_t v[4][2];
+        uint32_t cn[4], of[4];
+        int ws[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint32_t f = min(f0 + q * FIN_THREADS + tid, total - 1);
-          int lo = 0, hi = (int)nw;                 // last workgroup with loff <= f
-          while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (loff[mid] <= f) lo = mid; else hi = mid;
-          }
-          v[q] = wc[(int64_t)lo * CAND_CAP + (f - loff[lo])];
+        for (int s = 0; s < 4; ++s) {
+          ws[s] = min(w0 + s * NWAVE, (int)nw - 1);
+          cn[s] = (w0 + s * NWAVE < nw) ? loff[ws[s] + 1] - loff[ws[s]] : 0u;
+          of[s] = loff[ws[s]];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) v[s][u] = wc[(int64_t)ws[s] * CAND_CAP + lane + 64 * u];
         }
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint32_t f = f0 + q * FIN_THREADS + tid;
-          if (f < total) lc[f] = v[q];
+        for (int s = 0; s < 4; ++s) {
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+            if ((uint32_t)(lane + 64 * u) < cn[s]) take(v[s][u], of[s] + lane + 64 * u);
+          for (uint32_t j = 128 + lane; j < cn[s]; j += 64) take(wc[(int64_t)ws[s] * CAND_CAP + j], of[s] + j);
         }
       }
       __syncthreads();
-      // keep the keys at or above the highest cutoff, in order (in place: every
-      // thread holds its elements in registers before any is written)
-      {
-        const uint32_t per2 = (total + FIN_THREADS - 1) / FIN_THREADS;   // <= 16
-        const uint32_t i0 = min(tid * per2, total), i1 = min(i0 + per2, total);
-        uint64_t v[16];
-        uint32_t m = 0;
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const uint32_t i = i0 + q;
-          v[q] = i < i1 ? lc[i] : 0ull;
-          m |= ((i < i1 && (uint32_t)(v[q] >> 44) >= cmax) ? 1u : 0u) << q;
-        }
-        uint32_t off = block_exclusive_scan((uint32_t)__popc(m), scan_tmp, &nk);
-#pragma unroll
-        for (int q = 0; q < 16; ++q)
-          if ((m >> q) & 1u) lc[off++] = v[q];
-        __syncthreads();
-      }
-      fast = nk >= (uint32_t)K;
+      uint32_t tot;
+      hist_kth_bin<FIN_THREADS>(hist, (uint32_t)K, scan_tmp, ctl, &tot);
+      fast = ctl[0] != 0xFFFFFFFFu;       // at least K keys reach the highest cutoff
     }
   }
+  const float* sall = scores + (int64_t)b * sstride;
   if (!fast) {
-    const float* sall = scores + (int64_t)b * sstride;
-    uint32_t* hist = (uint32_t*)lc;
+    // histogram of every score of the sequence (12-bit key bins)
     __syncthreads();
     for (int i = tid; i < NBINS; i += FIN_THREADS) hist[i] = 0;
     __syncthreads();
     for (int64_t i = tid; i < n_pos; i += FIN_THREADS) atomicAdd(&hist[score_key(sall[i]) >> BIN_SHIFT], 1u);
     __syncthreads();
     uint32_t tot;
-    hist_kth_bin<FIN_THREADS>(hist, (uint32_t)K, scan_tmp, ctl, &tot);
-    const uint32_t T = ctl[0];             // defined: n_pos > K
-    const uint32_t ng = ctl[1] + hist[T];
-    __syncthreads();
-    uint64_t* gs = sb.gscr + (int64_t)b * sb.gscr_stride;
-    uint64_t* dst = ng <= (uint32_t)FIN_LDS_CANDS ? lc : gs;
-    uint32_t base = 0;
-    for (int64_t c0 = 0; c0 < n_pos; c0 += FIN_THREADS) {
-      const int64_t i = c0 + tid;
-      const uint32_t key = i < n_pos ? score_key(sall[i]) : 0u;
-      const bool take = i < n_pos && (key >> BIN_SHIFT) >= T;
-      uint32_t t2;
-      const uint32_t off = block_exclusive_scan(take ? 1u : 0u, scan_tmp, &t2);
-      if (take) dst[base + off] = composite(key, (uint32_t)i);
-      base += t2;
-    }
-    nk = base;
-    src = dst;
-    if (dst == gs) __threadfence_block();   // this workgroup reads its global copy back
-    __syncthreads();
+    hist_kth_bin<FIN_THREADS>(hist, (uint32_t)K, scan_tmp, ctl, &tot);   // defined: n_pos > K
   }
-  // the K best of src[0, nk) (nk >= K), written in position order
+  const uint32_t T = ctl[0], above = ctl[1], in_bin = hist[T];
+  const uint32_t need = (uint32_t)K - above;      // 1 .. in_bin
+  // The threshold bin as a range [lo20, hi20] of 20-bit key prefixes: fast
+  // path, prefix cmax + T (the last bin: everything from cmax + 4095 up);
+  // fallback, the 256 prefixes under the 12-bit bin T.
+  const uint32_t lo20 = fast ? cmax + T : T << 8;
+  const uint32_t hi20 = fast ? (T == NBINS - 1 ? 0xFFFFFu : cmax + T) : (T << 8) | 255u;
+  auto elem = [&](uint32_t i) -> uint64_t {
+    return fast ? lc[i] : composite(score_key(sall[i]), i);
+  };
+  const uint32_t n_src = fast ? total : (uint32_t)n_pos;
   uint64_t prefix = 0, mask = 0;
-  if (nk > (uint32_t)K) {
-    const int top = radix_top_shift(src, nk, red);
-    radix_select_u64(src, nk, (uint32_t)K, top, h, ctl, &prefix, &mask);
-  }
-  uint32_t base = 0;
-  for (uint32_t c0 = 0; c0 < nk; c0 += 16 * FIN_THREADS) {
-    const uint32_t cn = min(nk - c0, 16u * FIN_THREADS);
-    const uint32_t per = (cn + FIN_THREADS - 1) / FIN_THREADS;
-    const uint32_t i0 = c0 + min(tid * per, cn), i1 = c0 + min(tid * per + per, cn);
-    uint64_t v[16];
-    uint32_t m = 0;
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const uint32_t i = i0 + q;
-      v[q] = i < i1 ? src[i] : 0ull;
-      m |= ((i < i1 && (v[q] & mask) >= prefix) ? 1u : 0u) << q;
+  if (need < in_bin) {
+    // the threshold bin is split: its keys (unordered) -> radix select
+    __syncthreads();                               // hist reads done before sub is reused
+    uint64_t* dst = in_bin <= (uint32_t)FIN_SUB_CAP ? sub : sb.gscr + (int64_t)b * sb.gscr_stride;
+    if (tid == 0) ctl[6] = 0;
+    __syncthreads();
+    for (uint32_t i0 = 0; i0 < n_src; i0 += FIN_THREADS) {
+      const uint32_t i = i0 + tid;
+      const uint64_t c = i < n_src ? elem(i) : 0ull;
+      const uint32_t p20 = (uint32_t)(c >> 44);
+      const bool t = i < n_src && p20 >= lo20 && p20 <= hi20;
+      const uint32_t at = wave_append(t, &ctl[6]);
+      if (t && at < in_bin) dst[at] = c;
     }
-    uint32_t t3;
-    uint32_t off = base + block_exclusive_scan((uint32_t)__popc(m), scan_tmp, &t3);
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      if ((m >> q) & 1u) {
-        if (off < (uint32_t)K) ob[off] = (int32_t)(0xFFFFFFFFu - (uint32_t)v[q]);
-        ++off;
-      }
-    }
-    base += t3;
+    if (dst != sub) __threadfence_block();         // this workgroup reads its global copy back
+    __syncthreads();
+    const int top = radix_top_shift(dst, in_bin, red);
+    radix_select_u64(dst, in_bin, need, top, h, ctl, &prefix, &mask);
   }
-  for (uint32_t j = base + tid; j < (uint32_t)K; j += FIN_THREADS) ob[j] = -1;
+  // the K best in position order: above the threshold bin, or inside it and
+  // radix-selected
+  const uint32_t nsel = ordered_compact(
+      n_src,
+      [&](uint32_t i) {
+        const uint64_t c = elem(i);
+        const uint32_t p20 = (uint32_t)(c >> 44);
+        return p20 > hi20 || (p20 >= lo20 && p20 <= hi20 && (c & mask) >= prefix);
+      },
+      [&](uint32_t i, uint32_t at) {
+        if (at < (uint32_t)K) ob[at] = fast ? (int32_t)(0xFFFFFFFFu - (uint32_t)lc[i]) : (int32_t)i;
+      },
+      scan_tmp);
+  for (uint32_t j = nsel + tid; j < (uint32_t)K; j += FIN_THREADS) ob[j] = -1;
 }
 
 // ---------------------------------------------------------------- select (long)
@@ -778,7 +798,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
     if (bc) {
       uint32_t basei = 0;
       if (lane == 0) basei = atomicAdd(&st->ncand, (uint32_t)__popcll(bc));
-      basei = __shfl(basei, 0, 64);
+      basei = readlane_u32(basei, 0);
       if (cnd) {
         const uint32_t rank = (uint32_t)__popcll(bc & ((1ull << lane) - 1ull));
         cb[basei + rank] = composite(key, (uint32_t)i);
@@ -793,7 +813,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_finish_kernel(
     const int32_t* __restrict__ n_entries, int64_t max_n, uint8_t* __restrict__ ctrl,
     uint32_t* __restrict__ bitmap, int64_t bm_stride, const uint64_t* __restrict__ cbuf, int64_t cb_stride,
     int K, int32_t* __restrict__ out, int out_stride) {
-  __shared__ uint32_t h[256];
+  __shared__ uint32_t h[512];
   __shared__ uint32_t ctl[8];
   __shared__ uint32_t scan_tmp[SEL_THREADS / 64 + 1];
   __shared__ uint64_t lcand[SEL_LDS_CAP];
@@ -905,26 +925,7 @@ __global__ __launch_bounds__(SMALL_THREADS) void select_small_kernel(
         if ((c & pmask) == prefix) atomicAdd(&h[(uint32_t)(c >> shift) & 255u], 1u);
       }
       __syncthreads();
-      if (threadIdx.x < 64) {
-        const int l = threadIdx.x;
-        uint32_t c4[4], loc = 0;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) { c4[q] = h[255 - 4 * l - q]; loc += c4[q]; }
-        uint32_t inc = loc;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-          uint32_t y = __shfl_up(inc, d, 64);
-          if (l >= d) inc += y;
-        }
-        const uint32_t pre = inc - loc;
-        if (pre < need && pre + loc >= need) {
-          uint32_t cum = pre;
-          for (int q = 0; q < 4; ++q) {
-            if (cum + c4[q] >= need) { ctl[0] = 255 - 4 * l - q; ctl[1] = cum; ctl[2] = c4[q]; break; }
-            cum += c4[q];
-          }
-        }
-      }
+      if (threadIdx.x < 64) digit_kth(h, need, ctl);
       __syncthreads();
       const uint32_t d = ctl[0], above = ctl[1], cnt = ctl[2];
       __syncthreads();

@@ -36,7 +36,7 @@ constexpr int kSumWords = 32;         // (bin, count) pairs a workgroup may repo
 constexpr int kCandCap = 256;         // candidates a workgroup reports in direct mode
 constexpr int kDirectMaxK = 512;      // largest k the score pass selects by itself
 constexpr int kFinMaxWg = 2048;       // score workgroups per sequence whose slots the finish reads
-constexpr int kFinLdsCands = 16384;   // candidates the direct finish holds in LDS
+constexpr int kFinLdsCands = 12288;   // candidates the direct finish holds in LDS
 
 // Workspace views used by the score pass's selection (per-sequence strides).
 struct SelBufs {
