@@ -41,12 +41,14 @@
 
 namespace csa2 {
 
-constexpr int AT_THREADS = 256;
+constexpr int AT_WAVES = 8;                    // two waves per SIMD
+constexpr int AT_THREADS = 64 * AT_WAVES;
 constexpr int AT_PITCH = 1056;                 // bytes per entry row of the fp16 tile (rows 8 banks apart)
 constexpr int AT_WAVE_LDS = 16 * AT_PITCH;     // 16896
-constexpr int AT_LDS = 4 * AT_WAVE_LDS;        // 67584 (>= 2 x 32 KiB for the merge)
+constexpr int AT_LDS = AT_WAVES * AT_WAVE_LDS; // 135168 (>= 4 x 32 KiB for the merge; the queries first)
 constexpr float AT_RESCALE = 8.0f;
 constexpr int AT_QPITCH = 1040;                // bytes per head row of the fp16 queries
+constexpr int AT_QLDS_K = 2;                   // query K-slices read from LDS at every tile
 constexpr int AT_MAX_CHUNK = 2048;             // positions of one split (k <= CSA2_MAX_K)
 
 __device__ __forceinline__ f16x8_t dequant_latent8(uint32_t dw, uint32_t spair) {
@@ -84,10 +86,11 @@ __global__ __launch_bounds__(AT_THREADS) void attention_kernel(
     const uint16_t* __restrict__ q, int B, int H, float tau, int S,
     float* __restrict__ out, float* __restrict__ lse, float* __restrict__ part) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  __shared__ float sm_m[4][16], sm_l[4][16];
+  __shared__ float sm_m[AT_WAVES][16], sm_l[AT_WAVES][16];
   __shared__ float sm_lscale[16];
-  __shared__ __attribute__((aligned(16))) uint8_t qlds[16 * AT_QPITCH];   // fp16 queries, row = head
   __shared__ int32_t sidx[AT_MAX_CHUNK];                                   // the split's positions (-1 = skip)
+  __shared__ f16x8_t qtail[AT_QLDS_K][64];                                 // last query slices, per lane
+  uint8_t* qlds = smem;                    // fp16 queries (row = head) until the tiles start
 
   const int HG = (H + 15) / 16;
   const int wg = blockIdx.x;
@@ -107,6 +110,17 @@ __global__ __launch_bounds__(AT_THREADS) void attention_kernel(
   const int ntiles = (nent + 15) / 16;
   const int64_t nb = n_entries[b];
   const int64_t row_base = entry_offset[b];
+  // --- queries: thread (qh = tid/32, c = tid%32) takes dims 16c .. 16c+15 of head 16hg + qh;
+  // their loads are issued before the split's positions are read
+  const int qh = tid >> 5, qc = tid & 31;
+  const int hq = 16 * hg + qh;
+  u32x4_t raw[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
+  if (hq < H) {
+    const uint16_t* src = q + ((int64_t)b * H + hq) * 512 + 16 * qc;
+    raw[0] = *(const u32x4_t*)src;
+    raw[1] = *(const u32x4_t*)(src + 8);
+  }
+  // --- entry range of this split, in tiles of 16; its positions go to LDS
   {
     const int32_t* ib = idx + (int64_t)b * k + e_lo;
     for (int i = tid; i < ntiles * 16; i += AT_THREADS) {
@@ -114,90 +128,95 @@ __global__ __launch_bounds__(AT_THREADS) void attention_kernel(
       sidx[i] = (p >= 0 && p < nb) ? p : -1;
     }
   }
-
-  // --- queries: thread (qh = tid/16, c = tid%16) converts dims 32c .. 32c+31 of head 16hg + qh.
   // Each head is scaled by a power of two that puts its largest magnitude in
   // [2^14, 2^15) before rounding to fp16; the logit divides it out again.
   {
-    const int qh = tid >> 4, c = tid & 15;
-    const int hq = 16 * hg + qh;
-    u32x4_t raw[4] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};
-    if (hq < H) {
-      const uint16_t* src = q + ((int64_t)b * H + hq) * 512 + 32 * c;
+    uint32_t qmax = 0;                       // |bf16| bit patterns order like their values
 #pragma unroll
-      for (int j = 0; j < 4; ++j) raw[j] = *(const u32x4_t*)(src + 8 * j);
-    }
-    float qmax = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        qmax = fmaxf(qmax, fabsf(bf16_to_f32(raw[j][t] & 0xFFFFu)));
-        qmax = fmaxf(qmax, fabsf(bf16_to_f32(raw[j][t] >> 16)));
+        qmax = max(qmax, raw[j][t] & 0x7FFFu);
+        qmax = max(qmax, (raw[j][t] >> 16) & 0x7FFFu);
       }
-#pragma unroll
-    for (int d = 1; d < 16; d <<= 1) qmax = fmaxf(qmax, shfl_xor_f(qmax, d));
+    qmax = row_max_u32(qmax);                // 16 lanes, then the other half of the head's 32
+    {
+      const auto r = __builtin_amdgcn_permlane16_swap(qmax, qmax, false, false);
+      qmax = max((uint32_t)r[0], (uint32_t)r[1]);
+    }
+    const float qmaxf = bf16_to_f32(qmax);
     int sigma = 0;
-    if (qmax > 0.0f) {
+    if (qmaxf > 0.0f) {
       int e;
-      frexpf(qmax, &e);          // qmax in [2^(e-1), 2^e)
+      frexpf(qmaxf, &e);         // qmax in [2^(e-1), 2^e)
       sigma = 15 - e;            // qmax * 2^sigma in [2^14, 2^15)
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < 2; ++j) {
       f16x8_t v;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         v[2 * t] = (_Float16)ldexpf(bf16_to_f32(raw[j][t] & 0xFFFFu), sigma);
         v[2 * t + 1] = (_Float16)ldexpf(bf16_to_f32(raw[j][t] >> 16), sigma);
       }
-      *(f16x8_t*)(qlds + qh * AT_QPITCH + 64 * c + 16 * j) = v;
+      *(f16x8_t*)(qlds + qh * AT_QPITCH + 32 * qc + 16 * j) = v;
     }
-    if (c == 0) sm_lscale[qh] = ldexpf(tau, -sigma);
+    if (qc == 0) sm_lscale[qh] = ldexpf(tau, -sigma);
   }
   __syncthreads();
   // B operand of QK: column = head r, K-slice = dims 128kg + 8j .. +7
-  f16x8_t qb[16];
+  // (the last AT_QLDS_K slices stay in a small LDS copy, read per tile, to keep
+  // the wave within 256 registers)
+  f16x8_t qb[16 - AT_QLDS_K];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) qb[j] = *(const f16x8_t*)(qlds + r * AT_QPITCH + 256 * kg + 16 * j);
+  for (int j = 0; j < 16 - AT_QLDS_K; ++j) qb[j] = *(const f16x8_t*)(qlds + r * AT_QPITCH + 256 * kg + 16 * j);
+  if (wave == 0) {
+#pragma unroll
+    for (int j = 0; j < AT_QLDS_K; ++j)
+      qtail[j][lane] = *(const f16x8_t*)(qlds + r * AT_QPITCH + 256 * kg + 16 * (16 - AT_QLDS_K + j));
+  }
   const float lscale = sm_lscale[r];
   uint8_t* wlds = smem + wave * AT_WAVE_LDS;
+  __syncthreads();                           // the queries' LDS becomes tile space
 
   f32x4_t O[32];
 #pragma unroll
   for (int t = 0; t < 32; ++t) O[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   float m_ref = -INFINITY, l_run = 0.0f;
 
-  // Tiles of this wave: wave, wave + 4, ... The rows of the next tile are in
-  // flight while the current tile is computed. Loads are unconditional (a
-  // skipped entry reads row 0 of the sequence and is masked).
+  // Tiles of this wave: wave, wave + 8, ... A lane holds a quarter row (64
+  // code bytes, 8 scale bytes) of one entry; each 16-byte part is reloaded
+  // with the next tile's row as soon as the current tile has consumed it, so
+  // the next rows are in flight during the rest of the tile. Loads are
+  // unconditional (a skipped entry reads row 0 of the sequence and is masked).
   const bool any_rows = nb > 0;
-  auto load_rows = [&](int tile, u32x4_t* cw, u32x2_t& sw) {
-    const int p = sidx[16 * tile + r];
+  u32x4_t cw[4] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};
+  u32x2_t sw = {0, 0};
+  if (any_rows && wave < ntiles) {
+    const int p = sidx[16 * wave + r];
     const uint8_t* row = kv + (row_base + (p >= 0 ? p : 0)) * 288;
 #pragma unroll
     for (int c = 0; c < 4; ++c) cw[c] = *(const u32x4_t*)(row + 64 * kg + 16 * c);
     sw = *(const u32x2_t*)(row + 256 + 8 * kg);
-  };
-  // ping-pong row buffers (no register copies of loads in flight)
-  u32x4_t cwA[4] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};
-  u32x4_t cwB[4] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};
-  u32x2_t swA = {0, 0}, swB = {0, 0};
-  auto compute_tile = [&](int tile, const u32x4_t* cw, const u32x2_t sw) {
+  }
+  auto compute_tile = [&](int tile, int next) {
       const uint64_t vmask = __ballot(sidx[16 * tile + r] >= 0);
+      const int pn = sidx[16 * next + r];
+      const uint8_t* rown = kv + (row_base + (pn >= 0 ? pn : 0)) * 288;
 
       // dequantize 128 dims (128kg .. 128kg+127) to fp16, feed QK and copy the tile
       // to the wave's LDS area (row = entry r); logits^T: rows = entries, columns = heads
-      f32x4_t lg0 = {0.0f, 0.0f, 0.0f, 0.0f}, lg1 = {0.0f, 0.0f, 0.0f, 0.0f};
+      f32x4_t lg = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const uint32_t sbyte = (sw[j >> 3] >> (8 * ((j >> 1) & 3))) & 0xFFu;
         const f16x8_t ca = dequant_latent8(cw[j >> 2][j & 3], scale_pair(sbyte));
-        if (j & 1) lg1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ca, qb[j], lg1, 0, 0, 0);
-        else lg0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ca, qb[j], lg0, 0, 0, 0);
+        const f16x8_t qj = j < 16 - AT_QLDS_K ? qb[j < 16 - AT_QLDS_K ? j : 0] : qtail[j - (16 - AT_QLDS_K)][lane];
+        lg = __builtin_amdgcn_mfma_f32_16x16x32_f16(ca, qj, lg, 0, 0, 0);
         *(f16x8_t*)(wlds + r * AT_PITCH + 256 * kg + 16 * j) = ca;
+        if ((j & 3) == 3) cw[j >> 2] = *(const u32x4_t*)(rown + 64 * kg + 16 * (j >> 2));
       }
-      const f32x4_t lg = lg0 + lg1;
+      sw = *(const u32x2_t*)(rown + 256 + 8 * kg);
 
       // online softmax for head r; this lane holds entries 4kg + i of the tile
       float x[4];
@@ -252,36 +271,20 @@ __global__ __launch_bounds__(AT_THREADS) void attention_kernel(
       __builtin_amdgcn_wave_barrier();
   };
   // rounds of up to 8 tiles per wave, unrolled so the load/compute pipeline is
-  // straight-line code (one full wait per round at most)
-  // (loads are unconditional inside a round: the prefetch past the wave's last
-  // tile re-reads its last tile, so the wait analysis sees one path)
-  const int last = ntiles - 1 - ((ntiles - 1 - wave) & 3);   // this wave's last tile
-  for (int base = wave; any_rows && base < ntiles; base += 32) {
-    load_rows(base, cwA, swA);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int tile = base + 4 * i;
-      if (tile >= ntiles) break;
-      if (i & 1) {
-        if (i < 7) load_rows(min(tile + 4, last), cwA, swA);
-        compute_tile(tile, cwB, swB);
-      } else {
-        load_rows(min(tile + 4, last), cwB, swB);
-        compute_tile(tile, cwA, swA);
-      }
-    }
-  }
+  // straight-line code (the prefetch past the wave's last tile re-reads it)
+  const int last = ntiles - 1 - ((ntiles - 1 - wave) & (AT_WAVES - 1));   // this wave's last tile
+  for (int tile = wave; any_rows && tile < ntiles; tile += AT_WAVES) compute_tile(tile, min(tile + AT_WAVES, last));
 
-  // --- merge the 4 waves: per head max, weights, then pairwise sums of O in LDS
+  // --- merge the waves: per head max, weights, then pairwise sums of O in LDS
   l_run = sum_lane_groups_a(l_run);
   if (lane < 16) { sm_m[wave][lane] = m_ref; sm_l[wave][lane] = l_run; }
   __syncthreads();
   float M = -INFINITY;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) M = fmaxf(M, sm_m[w][r]);
+  for (int w = 0; w < AT_WAVES; ++w) M = fmaxf(M, sm_m[w][r]);
   float L = 0.0f, f_own = 0.0f;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
+  for (int w = 0; w < AT_WAVES; ++w) {
     const float mw = sm_m[w][r];
     const float f = (mw == -INFINITY) ? 0.0f : __expf(mw - M);
     L += f * sm_l[w][r];
@@ -290,28 +293,24 @@ __global__ __launch_bounds__(AT_THREADS) void attention_kernel(
 #pragma unroll
   for (int t = 0; t < 32; ++t) O[t] *= f_own;
 
-  f32x4_t* bufA = (f32x4_t*)smem;                  // [32][64] x 16 B = 32 KiB
-  f32x4_t* bufB = (f32x4_t*)(smem + 32768);
-  if (wave == 1 || wave == 3) {
-    f32x4_t* buf = wave == 1 ? bufA : bufB;
+  // halving rounds: waves [h, 2h) store their O (32 KiB each), waves [0, h) add it
+  f32x4_t* obuf = (f32x4_t*)smem;
 #pragma unroll
-    for (int t = 0; t < 32; ++t) buf[t * 64 + lane] = O[t];
-  }
-  __syncthreads();
-  if (wave == 0 || wave == 2) {
-    const f32x4_t* buf = wave == 0 ? bufA : bufB;
+  for (int half = AT_WAVES / 2; half >= 1; half >>= 1) {
+    __syncthreads();
+    if (wave >= half && wave < 2 * half) {
+      f32x4_t* buf = obuf + (wave - half) * 32 * 64;
 #pragma unroll
-    for (int t = 0; t < 32; ++t) O[t] += buf[t * 64 + lane];
-  }
-  __syncthreads();
-  if (wave == 2) {
+      for (int t = 0; t < 32; ++t) buf[t * 64 + lane] = O[t];
+    }
+    __syncthreads();
+    if (wave < half) {
+      const f32x4_t* buf = obuf + wave * 32 * 64;
 #pragma unroll
-    for (int t = 0; t < 32; ++t) bufA[t * 64 + lane] = O[t];
+      for (int t = 0; t < 32; ++t) O[t] += buf[t * 64 + lane];
+    }
   }
-  __syncthreads();
   if (wave != 0) return;
-#pragma unroll
-  for (int t = 0; t < 32; ++t) O[t] += bufA[t * 64 + lane];
   if (!head_ok) return;
 
   // lane (r, kg) holds dims 16u + 4kg + i of head r in O[u][i]
@@ -364,8 +363,9 @@ __global__ __launch_bounds__(128) void attention_combine_kernel(const float* __r
 int attention_splits(int B, int H, int k) {
   const int base = B * ((H + 15) / 16);
   int S = 1;
-  // at least 128 workgroups (one per compute unit pair), each split keeping >= 64 entries
-  while (base * S < 128 && (k + 2 * S - 1) / (2 * S) >= 64) S *= 2;
+  // at least 128 workgroups (one per compute unit pair), each split keeping at
+  // least one 16-entry tile per wave
+  while (base * S < 128 && (k + 2 * S - 1) / (2 * S) >= 16 * AT_WAVES) S *= 2;
   return S;
 }
 
