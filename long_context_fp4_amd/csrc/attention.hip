@@ -48,7 +48,6 @@ constexpr int AT_WAVE_LDS = 16 * AT_PITCH;     // 16896
 constexpr int AT_LDS = AT_WAVES * AT_WAVE_LDS; // 135168 (>= 4 x 32 KiB for the merge; the queries first)
 constexpr float AT_RESCALE = 8.0f;
 constexpr int AT_QPITCH = 1040;                // bytes per head row of the fp16 queries
-constexpr int AT_QLDS_K = 2;                   // query K-slices read from LDS at every tile
 constexpr int AT_MAX_CHUNK = 2048;             // positions of one split (k <= CSA2_MAX_K)
 
 __device__ __forceinline__ f16x8_t dequant_latent8(uint32_t dw, uint32_t spair) {
@@ -85,12 +84,11 @@ __global__ __launch_bounds__(AT_THREADS) void attention_kernel(
     const int32_t* __restrict__ n_entries, const int32_t* __restrict__ idx, int k,
     const uint16_t* __restrict__ q, int B, int H, float tau, int S,
     float* __restrict__ out, float* __restrict__ lse, float* __restrict__ part) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  __shared__ float sm_m[AT_WAVES][16], sm_l[AT_WAVES][16];
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];   // tile slots; the queries first
+  __shared__ float4 pbuf[AT_WAVES][64];        // softmax weights of each slot, lane layout of the producer
+  __shared__ float mref[AT_WAVES][16];         // producer reference maximum per head
   __shared__ float sm_lscale[16];
-  __shared__ int32_t sidx[AT_MAX_CHUNK];                                   // the split's positions (-1 = skip)
-  __shared__ f16x8_t qtail[AT_QLDS_K][64];                                 // last query slices, per lane
-  uint8_t* qlds = smem;                    // fp16 queries (row = head) until the tiles start
+  __shared__ int32_t sidx[AT_MAX_CHUNK];       // the split's positions (-1 = skip)
 
   const int HG = (H + 15) / 16;
   const int wg = blockIdx.x;
@@ -102,16 +100,20 @@ __global__ __launch_bounds__(AT_THREADS) void attention_kernel(
   const int head = 16 * hg + r;
   const bool head_ok = head < H;
 
-  // --- entry range of this split, in tiles of 16; its positions go to LDS
+  // --- entry range of this split, in tiles of 16
   const int chunk = ((k + S - 1) / S + 15) & ~15;
   const int e_lo = s * chunk;
   const int e_hi = min(k, e_lo + chunk);
   const int nent = max(e_hi - e_lo, 0);
   const int ntiles = (nent + 15) / 16;
+  const int nrounds = (ntiles + AT_WAVES - 1) / AT_WAVES;
   const int64_t nb = n_entries[b];
   const int64_t row_base = entry_offset[b];
-  // --- queries: thread (qh = tid/32, c = tid%32) takes dims 16c .. 16c+15 of head 16hg + qh;
-  // their loads are issued before the split's positions are read
+  const int32_t* ib = idx + (int64_t)b * k + e_lo;
+  const bool any_rows = nb > 0;
+
+  // --- early loads: this thread's query slice, and the first rows of this wave
+  // (tile `wave`, position read straight from the index list)
   const int qh = tid >> 5, qc = tid & 31;
   const int hq = 16 * hg + qh;
   u32x4_t raw[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
@@ -120,16 +122,29 @@ __global__ __launch_bounds__(AT_THREADS) void attention_kernel(
     raw[0] = *(const u32x4_t*)src;
     raw[1] = *(const u32x4_t*)(src + 8);
   }
-  // --- entry range of this split, in tiles of 16; its positions go to LDS
-  {
-    const int32_t* ib = idx + (int64_t)b * k + e_lo;
-    for (int i = tid; i < ntiles * 16; i += AT_THREADS) {
-      int p = i < nent ? ib[i] : -1;
-      sidx[i] = (p >= 0 && p < nb) ? p : -1;
-    }
+  // A lane holds a quarter row (64 code bytes, 8 scale bytes) of one entry of
+  // the wave's current tile; each part is reloaded with the next tile's row as
+  // soon as it has been consumed. Skipped entries read row 0 of the sequence.
+  u32x4_t cw[4] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};
+  u32x2_t sw = {0, 0};
+  if (any_rows && wave < ntiles) {
+    const int e = 16 * wave + r;
+    int p = e < nent ? ib[e] : -1;
+    p = (p >= 0 && p < nb) ? p : 0;
+    const uint8_t* row = kv + (row_base + p) * 288;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) cw[c] = *(const u32x4_t*)(row + 64 * kg + 16 * c);
+    sw = *(const u32x2_t*)(row + 256 + 8 * kg);
   }
-  // Each head is scaled by a power of two that puts its largest magnitude in
-  // [2^14, 2^15) before rounding to fp16; the logit divides it out again.
+  for (int i = tid; i < nrounds * AT_WAVES * 16; i += AT_THREADS) {
+    const int p = i < nent ? ib[i] : -1;
+    sidx[i] = (p >= 0 && p < nb) ? p : -1;
+  }
+
+  // --- queries to fp16 in LDS. Each head is scaled by a power of two that puts
+  // its largest magnitude in [2^14, 2^15) before rounding; the logit divides it
+  // out again.
+  uint8_t* qlds = smem;
   {
     uint32_t qmax = 0;                       // |bf16| bit patterns order like their values
 #pragma unroll
@@ -141,8 +156,8 @@ __global__ __launch_bounds__(AT_THREADS) void attention_kernel(
       }
     qmax = row_max_u32(qmax);                // 16 lanes, then the other half of the head's 32
     {
-      const auto r = __builtin_amdgcn_permlane16_swap(qmax, qmax, false, false);
-      qmax = max((uint32_t)r[0], (uint32_t)r[1]);
+      const auto rr = __builtin_amdgcn_permlane16_swap(qmax, qmax, false, false);
+      qmax = max((uint32_t)rr[0], (uint32_t)rr[1]);
     }
     const float qmaxf = bf16_to_f32(qmax);
     int sigma = 0;
@@ -165,60 +180,43 @@ __global__ __launch_bounds__(AT_THREADS) void attention_kernel(
   }
   __syncthreads();
   // B operand of QK: column = head r, K-slice = dims 128kg + 8j .. +7
-  // (the last AT_QLDS_K slices stay in a small LDS copy, read per tile, to keep
-  // the wave within 256 registers)
-  f16x8_t qb[16 - AT_QLDS_K];
+  f16x8_t qb[16];
 #pragma unroll
-  for (int j = 0; j < 16 - AT_QLDS_K; ++j) qb[j] = *(const f16x8_t*)(qlds + r * AT_QPITCH + 256 * kg + 16 * j);
-  if (wave == 0) {
-#pragma unroll
-    for (int j = 0; j < AT_QLDS_K; ++j)
-      qtail[j][lane] = *(const f16x8_t*)(qlds + r * AT_QPITCH + 256 * kg + 16 * (16 - AT_QLDS_K + j));
-  }
+  for (int j = 0; j < 16; ++j) qb[j] = *(const f16x8_t*)(qlds + r * AT_QPITCH + 256 * kg + 16 * j);
   const float lscale = sm_lscale[r];
   uint8_t* wlds = smem + wave * AT_WAVE_LDS;
   __syncthreads();                           // the queries' LDS becomes tile space
 
-  f32x4_t O[32];
+  // Producer state (this wave's tiles): reference maximum and partial sum for
+  // head r. Consumer state (dims 64 wave .. 64 wave + 63 of every head): the
+  // common reference M_c and O^T[dims][heads] in four 16-dim M-tiles.
+  float m_w = -INFINITY, l_w = 0.0f, M_c = -INFINITY;
+  f32x4_t O[4];
 #pragma unroll
-  for (int t = 0; t < 32; ++t) O[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  float m_ref = -INFINITY, l_run = 0.0f;
+  for (int t = 0; t < 4; ++t) O[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  const int last = ntiles - 1 - ((ntiles - 1 - wave) & (AT_WAVES - 1));   // this wave's last tile
 
-  // Tiles of this wave: wave, wave + 8, ... A lane holds a quarter row (64
-  // code bytes, 8 scale bytes) of one entry; each 16-byte part is reloaded
-  // with the next tile's row as soon as the current tile has consumed it, so
-  // the next rows are in flight during the rest of the tile. Loads are
-  // unconditional (a skipped entry reads row 0 of the sequence and is masked).
-  const bool any_rows = nb > 0;
-  u32x4_t cw[4] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};
-  u32x2_t sw = {0, 0};
-  if (any_rows && wave < ntiles) {
-    const int p = sidx[16 * wave + r];
-    const uint8_t* row = kv + (row_base + (p >= 0 ? p : 0)) * 288;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) cw[c] = *(const u32x4_t*)(row + 64 * kg + 16 * c);
-    sw = *(const u32x2_t*)(row + 256 + 8 * kg);
-  }
-  auto compute_tile = [&](int tile, int next) {
-      const uint64_t vmask = __ballot(sidx[16 * tile + r] >= 0);
-      const int pn = sidx[16 * next + r];
+  for (int rd = 0; any_rows && rd < nrounds; ++rd) {
+    // ---- produce: tile t of this wave -> fp16 slot, logits, weights
+    const int t = rd * AT_WAVES + wave;
+    const bool t_ok = t < ntiles;
+    const uint64_t vmask = t_ok ? __ballot(sidx[16 * t + r] >= 0) : 0ull;
+    {
+      const int next = t_ok ? min(t + AT_WAVES, last) : last;
+      const int pn = last >= 0 ? sidx[16 * next + r] : -1;
       const uint8_t* rown = kv + (row_base + (pn >= 0 ? pn : 0)) * 288;
-
-      // dequantize 128 dims (128kg .. 128kg+127) to fp16, feed QK and copy the tile
-      // to the wave's LDS area (row = entry r); logits^T: rows = entries, columns = heads
       f32x4_t lg = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const uint32_t sbyte = (sw[j >> 3] >> (8 * ((j >> 1) & 3))) & 0xFFu;
         const f16x8_t ca = dequant_latent8(cw[j >> 2][j & 3], scale_pair(sbyte));
-        const f16x8_t qj = j < 16 - AT_QLDS_K ? qb[j < 16 - AT_QLDS_K ? j : 0] : qtail[j - (16 - AT_QLDS_K)][lane];
-        lg = __builtin_amdgcn_mfma_f32_16x16x32_f16(ca, qj, lg, 0, 0, 0);
+        lg = __builtin_amdgcn_mfma_f32_16x16x32_f16(ca, qb[j], lg, 0, 0, 0);
         *(f16x8_t*)(wlds + r * AT_PITCH + 256 * kg + 16 * j) = ca;
         if ((j & 3) == 3) cw[j >> 2] = *(const u32x4_t*)(rown + 64 * kg + 16 * (j >> 2));
       }
       sw = *(const u32x2_t*)(rown + 256 + 8 * kg);
 
-      // online softmax for head r; this lane holds entries 4kg + i of the tile
+      // this lane: entries 4kg + i of the tile, head r
       float x[4];
       float tmax = -INFINITY;
 #pragma unroll
@@ -228,111 +226,104 @@ __global__ __launch_bounds__(AT_THREADS) void attention_kernel(
         tmax = fmaxf(tmax, x[i]);
       }
       tmax = max_lane_groups(tmax);
-      const bool raise = tmax > m_ref + AT_RESCALE || (m_ref == -INFINITY && tmax > -INFINITY);
-      if (__any(raise)) {
-        const float m_new = raise ? fmaxf(m_ref, tmax) : m_ref;
-        const float alpha = (m_ref == -INFINITY) ? 0.0f : __expf(m_ref - m_new);
-        if (raise) {
-          l_run *= alpha;
+      // the reference rises only when a tile exceeds it by more than AT_RESCALE,
+      // so the weights stay below e^AT_RESCALE
+      if (tmax > m_w + AT_RESCALE || (m_w == -INFINITY && tmax > -INFINITY)) {
+        const float m_new = fmaxf(m_w, tmax);
+        l_w *= (m_w == -INFINITY) ? 0.0f : __expf(m_w - m_new);
+        m_w = m_new;
+      }
+      float4 pv;
+      pv.x = (m_w == -INFINITY) ? 0.0f : __expf(x[0] - m_w);
+      pv.y = (m_w == -INFINITY) ? 0.0f : __expf(x[1] - m_w);
+      pv.z = (m_w == -INFINITY) ? 0.0f : __expf(x[2] - m_w);
+      pv.w = (m_w == -INFINITY) ? 0.0f : __expf(x[3] - m_w);
+      l_w += (pv.x + pv.y) + (pv.z + pv.w);
+      pbuf[wave][lane] = pv;
+      if (kg == 0) mref[wave][r] = m_w;
+    }
+    __syncthreads();
+
+    // ---- consume: O^T[64 dims of this wave] += C^T P^T over the round's 8 slots
+    {
+      float mw[AT_WAVES];
+      float mr = M_c;
 #pragma unroll
-          for (int t = 0; t < 32; ++t) O[t] *= alpha;
-          m_ref = m_new;
+      for (int w = 0; w < AT_WAVES; ++w) { mw[w] = mref[w][r]; mr = fmaxf(mr, mw[w]); }
+      if (mr > M_c) {
+        const float alpha = (M_c == -INFINITY) ? 0.0f : __expf(M_c - mr);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) O[u] *= alpha;
+        M_c = mr;
+      }
+      typedef short i16x4_t __attribute__((ext_vector_type(4)));
+      typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
+      const int j = lane & 15;
+      // lane 4m + a of lane group kg points at entry 4kg + m, dims 16u + 4a .. +3;
+      // after the transposing read, lane i of the group holds dim 16u + i of entries 4kg .. 4kg+3
+      const int toff = (4 * kg + (j >> 2)) * AT_PITCH + 8 * (j & 3) + 32 * (4 * wave);
+#pragma unroll
+      for (int pr = 0; pr < AT_WAVES / 2; ++pr) {
+        const int w0 = 2 * pr, w1 = 2 * pr + 1;
+        const float f0 = (mw[w0] == -INFINITY) ? 0.0f : __expf(mw[w0] - M_c);
+        const float f1 = (mw[w1] == -INFINITY) ? 0.0f : __expf(mw[w1] - M_c);
+        const float4 p0 = pbuf[w0][lane], p1 = pbuf[w1][lane];
+        // K-slots 8kg .. 8kg+3: slot w0 entries 4kg .. 4kg+3; 8kg+4 .. 8kg+7: slot w1
+        const f16x8_t pb = {(_Float16)(p0.x * f0), (_Float16)(p0.y * f0), (_Float16)(p0.z * f0),
+                            (_Float16)(p0.w * f0), (_Float16)(p1.x * f1), (_Float16)(p1.y * f1),
+                            (_Float16)(p1.z * f1), (_Float16)(p1.w * f1)};
+        __attribute__((address_space(3))) uint8_t* t0 =
+            (__attribute__((address_space(3))) uint8_t*)smem + w0 * AT_WAVE_LDS + toff;
+        __attribute__((address_space(3))) uint8_t* t1 =
+            (__attribute__((address_space(3))) uint8_t*)smem + w1 * AT_WAVE_LDS + toff;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const i16x4_t a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(t0 + 32 * u));
+          const i16x4_t a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(t1 + 32 * u));
+          f16x8_t a;
+          __builtin_memcpy(&a, &a0, 8);
+          __builtin_memcpy((uint8_t*)&a + 8, &a1, 8);
+          O[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pb, O[u], 0, 0, 0);
         }
       }
-      float p[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[i] = (m_ref == -INFINITY) ? 0.0f : expf(x[i] - m_ref);
-        l_run += p[i];
-      }
-      const f16x4_t pb = {(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
+    }
+    __syncthreads();
+  }
 
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      // O^T[dims x heads] += C^T[dims x entries] P^T[entries x heads], one M-tile per 16 dims.
-      // A operand by transposing LDS reads: lane 4m + a of lane group kg points at entry
-      // 4kg + m, dims 16u + 4a .. +3; lane i of the group then holds dim 16u + i of
-      // entries 4kg .. 4kg+3.
-      {
-        typedef short i16x4_t __attribute__((ext_vector_type(4)));
-        typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
-        const int j = lane & 15;
-        __attribute__((address_space(3))) uint8_t* tb =
-            (__attribute__((address_space(3))) uint8_t*)wlds + (4 * kg + (j >> 2)) * AT_PITCH + 8 * (j & 3);
-#pragma unroll
-        for (int u = 0; u < 32; ++u) {
-          const i16x4_t raw = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tb + 32 * u));
-          f16x4_t a;
-          __builtin_memcpy(&a, &raw, 8);
-          O[u] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, pb, O[u], 0, 0, 0);
-        }
-      }
-      __builtin_amdgcn_wave_barrier();
-  };
-  // rounds of up to 8 tiles per wave, unrolled so the load/compute pipeline is
-  // straight-line code (the prefetch past the wave's last tile re-reads it)
-  const int last = ntiles - 1 - ((ntiles - 1 - wave) & (AT_WAVES - 1));   // this wave's last tile
-  for (int tile = wave; any_rows && tile < ntiles; tile += AT_WAVES) compute_tile(tile, min(tile + AT_WAVES, last));
-
-  // --- merge the waves: per head max, weights, then pairwise sums of O in LDS
-  l_run = sum_lane_groups_a(l_run);
-  if (lane < 16) { sm_m[wave][lane] = m_ref; sm_l[wave][lane] = l_run; }
+  // --- the sum of the weights: per wave (its own reference), then over waves
+  float* lsum = (float*)pbuf;                // [AT_WAVES][16], after the last barrier
+  float* mfin = lsum + AT_WAVES * 16;
+  l_w = sum_lane_groups_a(l_w);
+  if (lane < 16) { lsum[wave * 16 + lane] = l_w; mfin[wave * 16 + lane] = m_w; }
   __syncthreads();
-  float M = -INFINITY;
-#pragma unroll
-  for (int w = 0; w < AT_WAVES; ++w) M = fmaxf(M, sm_m[w][r]);
-  float L = 0.0f, f_own = 0.0f;
+  float L = 0.0f;
 #pragma unroll
   for (int w = 0; w < AT_WAVES; ++w) {
-    const float mw = sm_m[w][r];
-    const float f = (mw == -INFINITY) ? 0.0f : __expf(mw - M);
-    L += f * sm_l[w][r];
-    if (w == wave) f_own = f;
+    const float mw = mfin[w * 16 + r];
+    if (mw != -INFINITY) L += lsum[w * 16 + r] * __expf(mw - M_c);
   }
-#pragma unroll
-  for (int t = 0; t < 32; ++t) O[t] *= f_own;
-
-  // halving rounds: waves [h, 2h) store their O (32 KiB each), waves [0, h) add it
-  f32x4_t* obuf = (f32x4_t*)smem;
-#pragma unroll
-  for (int half = AT_WAVES / 2; half >= 1; half >>= 1) {
-    __syncthreads();
-    if (wave >= half && wave < 2 * half) {
-      f32x4_t* buf = obuf + (wave - half) * 32 * 64;
-#pragma unroll
-      for (int t = 0; t < 32; ++t) buf[t * 64 + lane] = O[t];
-    }
-    __syncthreads();
-    if (wave < half) {
-      const f32x4_t* buf = obuf + wave * 32 * 64;
-#pragma unroll
-      for (int t = 0; t < 32; ++t) O[t] += buf[t * 64 + lane];
-    }
-  }
-  if (wave != 0) return;
   if (!head_ok) return;
 
-  // lane (r, kg) holds dims 16u + 4kg + i of head r in O[u][i]
+  // lane (r, kg) holds dims 64 wave + 16u + 4kg + i of head r in O[u][i]
   if (S == 1) {
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-    float* ob = out + ((int64_t)b * H + head) * 512;
+    float* ob = out + ((int64_t)b * H + head) * 512 + 64 * wave + 4 * kg;
 #pragma unroll
-    for (int u = 0; u < 32; ++u) {
+    for (int u = 0; u < 4; ++u) {
       const f32x4_t x = O[u];
-      *(float4*)(ob + 16 * u + 4 * kg) = float4{x[0] * inv, x[1] * inv, x[2] * inv, x[3] * inv};
+      *(float4*)(ob + 16 * u) = float4{x[0] * inv, x[1] * inv, x[2] * inv, x[3] * inv};
     }
-    if (lse && kg == 0) lse[(int64_t)b * H + head] = L > 0.0f ? M + logf(L) : -INFINITY;
+    if (lse && wave == 0 && kg == 0) lse[(int64_t)b * H + head] = L > 0.0f ? M_c + logf(L) : -INFINITY;
   } else {
     // partial: [B][H][S][512 + 2] -> unnormalised O, then (M, L)
     float* pb = part + (((int64_t)b * H + head) * S + s) * 514;
 #pragma unroll
-    for (int u = 0; u < 32; ++u) {
+    for (int u = 0; u < 4; ++u) {
       const f32x4_t x = O[u];
-      float* o = pb + 16 * u + 4 * kg;
+      float* o = pb + 64 * wave + 16 * u + 4 * kg;
       o[0] = x[0]; o[1] = x[1]; o[2] = x[2]; o[3] = x[3];
     }
-    if (kg == 0) { pb[512] = M; pb[513] = L; }
+    if (wave == 0 && kg == 0) { pb[512] = M_c; pb[513] = L; }
   }
 }
 
