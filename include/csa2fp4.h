@@ -119,7 +119,7 @@ int csa2_cache_write(const uint16_t* x_lat, const uint16_t* x_idx,
  *   ik, iks        the cache's indexer rows (see csa2_cache_write)
  *   entry_offset   i64 [B]  first cache row of sequence b
  *   n_entries      i32 [B]  entries of sequence b; positions are 0..n_entries[b]-1
- *   B, max_n       host ints; 1 <= B <= CSA2_MAX_BATCH; max_n >= every n_entries[b]
+ *   B, max_n       host ints; 1 <= B <= CSA2_MAX_BATCH; 0 <= max_n <= 2^26; max_n >= every n_entries[b]
  *                  (rows at positions >= max_n are not scored)
  *   q_idx          bf16 [B][Hi][128] indexer queries; w f32 [B][Hi] head weights
  *                  (NULL = all 1; ignored by CSA2_SCORE_DOT)

@@ -86,8 +86,8 @@ int check_indexer_args(const uint8_t* ik, const uint8_t* iks, const int64_t* ent
     return fail(CSA2_ERR_NULL, "indexer: a required pointer is NULL");
   if (B < 1 || B > CSA2_MAX_BATCH)
     return fail(CSA2_ERR_SHAPE, "indexer: B must be in [1, %d] (got %d)", CSA2_MAX_BATCH, B);
-  if (max_n < 0 || max_n > ((int64_t)1 << 31) - 1)
-    return fail(CSA2_ERR_SHAPE, "indexer: max_n out of range (got %lld)", (long long)max_n);
+  if (max_n < 0 || max_n > ((int64_t)1 << 26))
+    return fail(CSA2_ERR_SHAPE, "indexer: max_n must be in [0, 2^26] (got %lld)", (long long)max_n);
   if (Hi < 1 || Hi > CSA2_MAX_INDEXER_HEADS)
     return fail(CSA2_ERR_SHAPE, "indexer: Hi must be in [1, %d] (got %d)", CSA2_MAX_INDEXER_HEADS, Hi);
   if (score_mode != CSA2_SCORE_DOT && score_mode != CSA2_SCORE_RELU_W)

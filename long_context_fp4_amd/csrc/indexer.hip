@@ -274,14 +274,16 @@ __device__ uint32_t block_or_u32(uint32_t v, uint32_t* tmp) {
 // THREADS, thread t owns bins NBINS-1-BPT*t .. NBINS-BPT-BPT*t). Returns the number of keys counted in *total,
 // the bin in ctl[0] and the count strictly above it in ctl[1] (ctl[0] = -1
 // when total < need). All threads must call it.
-template <int THREADS>
+// PACKED: two 16-bit counts per word (bin b in the half b & 1 of word b / 2).
+template <int THREADS, bool PACKED = false>
 __device__ void hist_kth_bin(const uint32_t* lhist, uint32_t need, uint32_t* scan_tmp, uint32_t* ctl,
                              uint32_t* total_out) {
   constexpr int BPT = NBINS / THREADS;
   uint32_t hv[BPT], local = 0;
 #pragma unroll
   for (int q = 0; q < BPT; ++q) {
-    hv[q] = lhist[NBINS - 1 - (BPT * threadIdx.x + q)];
+    const int bin = NBINS - 1 - (BPT * threadIdx.x + q);
+    hv[q] = PACKED ? (lhist[bin >> 1] >> ((bin & 1) * 16)) & 0xFFFFu : lhist[bin];
     local += hv[q];
   }
   if (threadIdx.x == 0) { ctl[0] = 0xFFFFFFFFu; ctl[1] = 0; }
@@ -309,37 +311,31 @@ __device__ void hist_kth_bin(const uint32_t* lhist, uint32_t need, uint32_t* sca
 //      finish_kernel turns into the threshold bin or the final top-K).
 // MODE: 0 = dot product of head 0, 1 = sum_h w_h * ReLU(q_h . k).
 template <bool CAND, int SEL, int MODE>
-__global__ __launch_bounds__(SC_THREADS) void score_kernel(
+__global__ __launch_bounds__(SC_THREADS) __attribute__((amdgpu_waves_per_eu(8))) void score_kernel(
     const uint8_t* __restrict__ ik, const uint8_t* __restrict__ iks,
     const int64_t* __restrict__ entry_offset, const int32_t* __restrict__ n_entries, int64_t max_n,
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w, int Hi,
     const int32_t* __restrict__ cand, int cand_stride,
     float* __restrict__ scores, int64_t sstride, SelBufs sb, int K) {
-  __shared__ uint32_t lbuf[NBINS + SC_CHUNK];     // histogram + staged scores
+  // histogram with 16-bit counts (two bins per word) + staged scores: 12 KiB,
+  // so that eight workgroups fit one compute unit
+  __shared__ uint32_t lbuf[NBINS / 2 + SC_CHUNK];
   __shared__ uint32_t scan_tmp[SC_THREADS / 64 + 1];
   __shared__ uint32_t ctl[8];
+  __shared__ __attribute__((aligned(16))) float lw[16];   // head weights
+  __shared__ SelBufs sbs;   // the workspace views, parked in LDS while the keys stream (frees SGPRs)
   uint32_t* lhist = lbuf;
-  float* lsc = (float*)(lbuf + NBINS);
+  float* lsc = (float*)(lbuf + NBINS / 2);
+  auto hcount = [&](uint32_t bin) -> uint32_t { return (lhist[bin >> 1] >> ((bin & 1) * 16)) & 0xFFFFu; };
 
   const int b = blockIdx.y;
-  const int64_t n_pos = min((int64_t)n_entries[b], max_n);
-  const int64_t nslots = CAND ? (int64_t)cand_stride : n_pos;
-  const int64_t start = (int64_t)blockIdx.x * SC_CHUNK;
-  if (start >= nslots) return;
-  if (CAND && n_pos <= 0) return;                  // no listed position can be valid
-  const int end = (int)min((int64_t)SC_CHUNK, nslots - start);   // slots of this workgroup
-
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, g = lane >> 4;
-  if (SEL != SEL_NONE) {
-    for (int i = tid; i < NBINS; i += SC_THREADS) lhist[i] = 0;
-  }
-  if (SEL == SEL_THRESHOLD) {
-    // select_kernel ORs into the bitmap words of this chunk: clear them here
-    uint32_t* bm = sb.bitmap + (int64_t)b * sb.bm_stride;
-    for (int64_t wd = start / 32 + tid; wd < (start + end + 31) / 32; wd += SC_THREADS) bm[wd] = 0;
-  }
-
+  // independent loads first (the sequence's length and first row, the queries,
+  // the head weights), so the keys are requested one round trip after the start
+  const int32_t ne = n_entries[b];
+  const int64_t row_base = entry_offset[b];
+  asm volatile("" ::"s"(ne), "s"(row_base));   // both loads issued here, before any branch on them
   // A operand: q[head = n][channels 32g + 8j .. +7] for MFMA j
   bf16x8_t qa[4];
 #pragma unroll
@@ -348,25 +344,86 @@ __global__ __launch_bounds__(SC_THREADS) void score_kernel(
     if (n < Hi) v = *(const u32x4_t*)(q_idx + ((int64_t)b * Hi + n) * 128 + 32 * g + 8 * j);
     __builtin_memcpy(&qa[j], &v, 16);
   }
-  // head weights of this lane's output rows (heads 4g + i)
-  float wr[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int hh = 4 * g + i;
-    wr[i] = hh < Hi ? (w ? w[(int64_t)b * Hi + hh] : 1.0f) : 0.0f;
-  }
-  const int64_t row_base = entry_offset[b];
-  const uint8_t* ikb = ik + row_base * 64 + 16 * g;     // this lane's 16-byte block of row 0
-  const uint8_t* iksb = iks + row_base * 4 + g;
+  // head weights of the output rows (lane group g takes heads 4g .. 4g+3), in
+  // LDS and read per tile, which keeps the wave within 64 registers
+  const float wv = tid < Hi ? (w ? w[(int64_t)b * Hi + tid] : 1.0f) : 0.0f;
+  const int64_t n_pos = min((int64_t)ne, max_n);
+  const int64_t nslots = CAND ? (int64_t)cand_stride : n_pos;
+  const int64_t start = (int64_t)blockIdx.x * SC_CHUNK;
+  if (start >= nslots) return;
+  if (CAND && n_pos <= 0) return;                  // no listed position can be valid
+  const int end = (int)min((int64_t)SC_CHUNK, nslots - start);   // slots of this workgroup
+  // the sequence's rows: a uniform base plus a 32-bit byte offset per lane
+  // (positions below 2^26, checked on the host), one address register per load
+  const uint8_t* ikb = ik + row_base * 64;
+  const uint8_t* iksb = iks + row_base * 4;
   const int32_t* crow = CAND ? cand + (int64_t)b * cand_stride + start : nullptr;
+  // Full pass: the first SC_UNROLL tiles of this wave are requested right away
+  u32x4_t codes[SC_UNROLL];
+  uint32_t sbyte[SC_UNROLL];
+  if (!CAND) {
+#pragma unroll
+    for (int u = 0; u < SC_UNROLL; ++u) {
+      const uint32_t p = (uint32_t)(start + min(16 * wave + 64 * u + n, end - 1));
+      codes[u] = __builtin_nontemporal_load((const u32x4_t*)(ikb + (p * 64u + 16u * g)));
+      sbyte[u] = iksb[p * 4u + (uint32_t)g];
+    }
+  }
 
-  // each wave takes tiles of 16 slots; SC_UNROLL tiles are loaded before any is used.
-  // Loads are unconditional (invalid slots read row 0 of the sequence) so that the
-  // compiler issues them all ahead of the first wait.
-  for (int t0 = 16 * wave; t0 < end; t0 += 64 * SC_UNROLL) {
-    int pos[SC_UNROLL];
-    bool ok[SC_UNROLL];
-    if (CAND) {
+  if (SEL != SEL_NONE) {
+    for (int i = tid; i < NBINS / 2; i += SC_THREADS) lhist[i] = 0;
+  }
+  if (SEL == SEL_THRESHOLD) {
+    // select_kernel ORs into the bitmap words of this chunk: clear them here
+    uint32_t* bm = sb.bitmap + (int64_t)b * sb.bm_stride;
+    for (int64_t wd = start / 32 + tid; wd < (start + end + 31) / 32; wd += SC_THREADS) bm[wd] = 0;
+  }
+  if (tid < 16) lw[tid] = wv;
+  if (SEL != SEL_NONE && tid == 0) sbs = sb;
+  __syncthreads();
+
+  // one tile = 16 slots x 16 heads: 4 MFMAs over the 128 channels; the head sum
+  // goes to the lanes of group 0, which stage the score in LDS
+  auto score_tile = [&](const u32x4_t cw, uint32_t sbyte) -> float {
+    const float scl = __uint_as_float(sbyte << 23);
+    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      bf16x8_t kb = dequant_mx_block8(cw[j], scl);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[j], kb, acc, 0, 0, 0);
+    }
+    if (MODE == 0) return acc[0];          // head 0 is row 0, held by lanes 0..15
+    const float4 wr = *(const float4*)&lw[4 * g];
+    const float sc = wr.x * fmaxf(acc[0], 0.0f) + wr.y * fmaxf(acc[1], 0.0f) +
+                     wr.z * fmaxf(acc[2], 0.0f) + wr.w * fmaxf(acc[3], 0.0f);
+    return sum_lane_groups(sc);
+  };
+  if (!CAND) {
+    // each wave takes tiles of 16 slots, SC_UNROLL of them in flight: a tile's
+    // registers are reloaded with the same tile of the next group as soon as it
+    // has been scored, so loads stay in flight all along the chunk
+    // (the reloads past the chunk's end re-read its last row, which is in
+    // cache; unconditional loads in a fully unrolled loop keep the wait counts
+    // exact, and a short last chunk scores its clamped rows without storing them)
+#pragma unroll
+    for (int it = 0; it < SC_CHUNK / (SC_THREADS * SC_UNROLL / 4); ++it) {
+      const int t0 = 16 * wave + it * 64 * SC_UNROLL;
+#pragma unroll
+      for (int u = 0; u < SC_UNROLL; ++u) {
+        const float sc = score_tile(codes[u], sbyte[u]);
+        const int ls = t0 + 64 * u + n;
+        if (g == 0 && ls < end) lsc[ls] = sc;
+        const uint32_t p = (uint32_t)(start + min(ls + 64 * SC_UNROLL, end - 1));
+        codes[u] = __builtin_nontemporal_load((const u32x4_t*)(ikb + (p * 64u + 16u * g)));
+        sbyte[u] = iksb[p * 4u + (uint32_t)g];
+      }
+    }
+  } else {
+    // listed positions: SC_UNROLL tiles are loaded before any is used (invalid
+    // slots read row 0 of the sequence and score 0)
+    for (int t0 = 16 * wave; t0 < end; t0 += 64 * SC_UNROLL) {
+      int pos[SC_UNROLL];
+      bool ok[SC_UNROLL];
       int cv[SC_UNROLL];
 #pragma unroll
       for (int u = 0; u < SC_UNROLL; ++u) cv[u] = crow[min(t0 + 64 * u + n, end - 1)];
@@ -375,40 +432,17 @@ __global__ __launch_bounds__(SC_THREADS) void score_kernel(
         ok[u] = (t0 + 64 * u + n < end) && cv[u] >= 0 && cv[u] < n_pos;
         pos[u] = ok[u] ? cv[u] : 0;
       }
-    } else {
 #pragma unroll
       for (int u = 0; u < SC_UNROLL; ++u) {
+        codes[u] = __builtin_nontemporal_load((const u32x4_t*)(ikb + ((uint32_t)pos[u] * 64u + 16u * g)));
+        sbyte[u] = iksb[(uint32_t)pos[u] * 4u + (uint32_t)g];
+      }
+#pragma unroll
+      for (int u = 0; u < SC_UNROLL; ++u) {
+        const float sc = score_tile(codes[u], sbyte[u]);
         const int ls = t0 + 64 * u + n;
-        ok[u] = ls < end;
-        pos[u] = ok[u] ? (int)(start + ls) : 0;
+        if (g == 0 && ls < end) lsc[ls] = ok[u] ? sc : 0.0f;
       }
-    }
-    u32x4_t codes[SC_UNROLL];
-    uint32_t sbyte[SC_UNROLL];
-#pragma unroll
-    for (int u = 0; u < SC_UNROLL; ++u) {
-      codes[u] = __builtin_nontemporal_load((const u32x4_t*)(ikb + (int64_t)pos[u] * 64));
-      sbyte[u] = iksb[(int64_t)pos[u] * 4];
-    }
-#pragma unroll
-    for (int u = 0; u < SC_UNROLL; ++u) {
-      const float scl = __uint_as_float(sbyte[u] << 23);
-      f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        bf16x8_t kb = dequant_mx_block8(codes[u][j], scl);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[j], kb, acc, 0, 0, 0);
-      }
-      float sc;
-      if (MODE == 0) {
-        sc = acc[0];                       // head 0 is row 0, held by lanes 0..15
-      } else {
-        sc = wr[0] * fmaxf(acc[0], 0.0f) + wr[1] * fmaxf(acc[1], 0.0f) +
-             wr[2] * fmaxf(acc[2], 0.0f) + wr[3] * fmaxf(acc[3], 0.0f);
-        sc = sum_lane_groups(sc);
-      }
-      const int ls = t0 + 64 * u + n;
-      if (g == 0 && ls < end) lsc[ls] = ok[u] ? sc : 0.0f;
     }
   }
   __syncthreads();
@@ -424,10 +458,14 @@ __global__ __launch_bounds__(SC_THREADS) void score_kernel(
   }
   if (SEL == SEL_NONE) return;
 
+  const SelBufs sbl = sbs;
   // ---- local histogram and cutoff (every slot of a Full pass is a valid position).
   // The workgroup reports into its own slot of the workspace (a header word and
   // a list), so no global atomics are needed.
-  for (int i = tid; i < end; i += SC_THREADS) atomicAdd(&lhist[score_key(lsc[i]) >> BIN_SHIFT], 1u);
+  for (int i = tid; i < end; i += SC_THREADS) {
+    const uint32_t bin = score_key(lsc[i]) >> BIN_SHIFT;
+    atomicAdd(&lhist[bin >> 1], 1u << ((bin & 1) * 16));
+  }
   __syncthreads();
   const int64_t nwg = (n_pos + SC_CHUNK - 1) / SC_CHUNK;
   // local budget: a multiple of the chunk's expected share of the top-K plus a
@@ -438,9 +476,9 @@ __global__ __launch_bounds__(SC_THREADS) void score_kernel(
   if (SEL == SEL_DIRECT) budget64 = min(budget64, max((int64_t)8, (int64_t)FIN_LDS_CANDS / nwg));
   const uint32_t budget = (uint32_t)min(budget64, (int64_t)end);
   uint32_t cnt_all;
-  hist_kth_bin<SC_THREADS>(lhist, budget, scan_tmp, ctl, &cnt_all);
+  hist_kth_bin<SC_THREADS, true>(lhist, budget, scan_tmp, ctl, &cnt_all);
   const uint32_t cbin = ctl[0], cabove = ctl[1];
-  uint64_t* hdr = sb.hdr + (int64_t)b * sb.hdr_stride + blockIdx.x;
+  uint64_t* hdr = sbl.hdr + (int64_t)b * sbl.hdr_stride + blockIdx.x;
   if (SEL == SEL_THRESHOLD) {
     // (bin, count) pairs for the non-empty bins >= cut
     const uint32_t cut = (cbin == 0xFFFFFFFFu) ? 0u : cbin;   // fewer keys than the budget: keep all
@@ -448,15 +486,15 @@ __global__ __launch_bounds__(SC_THREADS) void score_kernel(
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
       const uint32_t bin = NBINS - 1 - (16 * tid + q);
-      np += (bin >= cut && lhist[bin] != 0) ? 1u : 0u;
+      np += (bin >= cut && hcount(bin) != 0) ? 1u : 0u;
     }
     uint32_t tot;
     uint32_t off = block_exclusive_scan(np, scan_tmp, &tot);
-    uint32_t* pl = sb.summ + (int64_t)b * sb.summ_stride + (int64_t)blockIdx.x * SUM_PAIRS;
+    uint32_t* pl = sbl.summ + (int64_t)b * sbl.summ_stride + (int64_t)blockIdx.x * SUM_PAIRS;
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
       const uint32_t bin = NBINS - 1 - (16 * tid + q);
-      const uint32_t c = lhist[bin];
+      const uint32_t c = hcount(bin);
       if (bin >= cut && c != 0) {
         if (off < SUM_PAIRS) pl[off] = (bin << 16) | c;
         ++off;
@@ -468,7 +506,7 @@ __global__ __launch_bounds__(SC_THREADS) void score_kernel(
     // refine the cutoff to the top 20 key bits: 256 sub-bins of the cutoff bin
     uint32_t fine = 0;                                       // fewer keys than the budget: keep all
     if (cbin != 0xFFFFFFFFu) {
-      uint32_t* h2 = lhist;                                  // every read of the 4096 bins is done
+      uint32_t* h2 = lhist;                                  // every read of the 4096 bins is done (256 words)
       h2[tid] = 0;
       __syncthreads();
 #pragma unroll
@@ -495,7 +533,7 @@ __global__ __launch_bounds__(SC_THREADS) void score_kernel(
     }
     uint32_t tot;
     uint32_t off = block_exclusive_scan((uint32_t)__popc(m), scan_tmp, &tot);
-    uint64_t* wc = sb.wgc + (int64_t)b * sb.wgc_stride + (int64_t)blockIdx.x * CAND_CAP;
+    uint64_t* wc = sbl.wgc + (int64_t)b * sbl.wgc_stride + (int64_t)blockIdx.x * CAND_CAP;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       if ((m >> q) & 1u) {
