@@ -13,9 +13,20 @@ last-level cache, so the timed passes read HBM). The scoring kernel is timed
 by itself with HIP events that the library records around its launch on the
 step's stream; the whole step is timed with events around K steps.
 
+The same run also times the cache write on its own workload (8 sequences of
+131072 tokens merged at ratio 2, the write128k configuration) and reports it
+beside the step as "cache_write".
+
+`traffic` in the roofline object is the HBM traffic of one scoring launch from
+rocprofv3 FETCH_SIZE and WRITE_SIZE counters, each scaled by what the same
+counter reads for a plain copy of known size (`--copy-calibration` runs that
+copy). The figures are kept below with the hash of the kernel source they were
+taken on; when the source has changed since, `traffic` is null.
+
 Prints one JSON line. `--gpus N` with N > 1 exits: this path runs on one GPU.
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -26,6 +37,12 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 COPIES = 4
+SCORE_SOURCE = os.path.join(ROOT, "long_context_fp4_amd", "csrc", "indexer.hip")
+# Counter readings of one scoring launch at the decode128k size (KiB per
+# dispatch, medians over the timed launches) and the counters' scale factors
+# from the copy calibration; valid for the kernel source with this hash.
+TRAFFIC = {"source_sha": "d4dcfcb10f346419", "fetch_kib": 70252.5, "write_kib": 8771.0,
+           "fetch_scale": 2.0, "write_scale": 1.0}
 
 
 def parse():
@@ -35,7 +52,68 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle timing budget")
+    ap.add_argument("--no-cache-write", action="store_true", help="skip the cache-write leg")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device copy of 1 GiB five times (counter calibration)")
     return ap.parse_args()
+
+
+def source_hash():
+    with open(SCORE_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_bytes():
+    """HBM bytes of one scoring launch from the recorded counters, or None."""
+    if TRAFFIC is None or TRAFFIC.get("source_sha") != source_hash():
+        return None
+    return (TRAFFIC["fetch_kib"] * 1024 * TRAFFIC["fetch_scale"] +
+            TRAFFIC["write_kib"] * 1024 * TRAFFIC["write_scale"])
+
+
+def copy_calibration():
+    import torch
+    nbytes = 1 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "launches": 5}), flush=True)
+
+
+def cache_write_leg(L, synth, torch):
+    """Cache write of the write128k workload: one launch over 8 x 131072 tokens."""
+    import numpy as np
+    w = synth.workload("write128k")
+    p = synth.params(w)
+    E = w.T // w.m
+    xs = [synth.hidden_states_device(w, p, b) for b in range(w.B)]
+    x_lat = torch.stack([x[0] for x in xs])
+    x_idx = torch.stack([x[1] for x in xs])
+    del xs
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    wl, wi = d(p["w_lat"]), d(p["w_idx"])
+    kv = torch.empty((w.B * E, 288), dtype=torch.uint8, device="cuda")
+    ik = torch.empty((w.B * E, 64), dtype=torch.uint8, device="cuda")
+    iks = torch.empty((w.B * E, 4), dtype=torch.uint8, device="cuda")
+    for _ in range(2):
+        L.cache_write(x_lat, x_idx, wl, wi, w.m, kv=kv, ik=ik, iks=iks)
+    n = 10
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    torch.cuda.synchronize()
+    for e0, e1 in ev:
+        e0.record()
+        L.cache_write(x_lat, x_idx, wl, wi, w.m, kv=kv, ik=ik, iks=iks)
+        e1.record()
+    torch.cuda.synchronize()
+    us = 1e3 * float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
+    nbytes = x_lat.numel() * 2 + x_idx.numel() * 2 + kv.numel() + ik.numel() + iks.numel()
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"workload": "write128k: 8 sequences x 131072 bf16 tokens (1% outlier channels x20), ratio-2 "
+                        "merge, packed to 288 + 68 B per entry",
+            "bound": "hbm", "bytes_per_launch": nbytes, "avg_launch_us": us, "achieved": gbs,
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS}
 
 
 def log(msg):
@@ -101,6 +179,9 @@ def main():
         print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported "
               f"(the path shards by whole sequences, with no exchange between GPUs)", file=sys.stderr)
         sys.exit(2)
+    if a.copy_calibration:
+        copy_calibration()
+        return
     import numpy as np
     import torch
     import long_context_fp4_amd as L
@@ -185,12 +266,19 @@ def main():
                    "indexer_heads": w.Hi, "k": w.k, "cache_copies": COPIES},
         "roofline": {"bound": "hbm", "kernel": "score_kernel (indexer scoring pass)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_bytes(),
                      "bytes_per_launch": idx_bytes, "avg_launch_us": score_avg_us},
         "step_cache_read_gbs": step_gbs,
     }
     log(f"step {total_ms / a.steps * 1e3:.1f} us, scoring kernel {score_avg_us:.1f} us "
         f"({achieved:.0f} GB/s), {qtok_s:.0f} query-tokens/s")
+    del copies, kv, ik, iks
+    torch.cuda.empty_cache()
+    if not a.no_cache_write:
+        log("cache write leg (write128k)")
+        res["cache_write"] = cache_write_leg(L, synth, torch)
+        log(f"cache write {res['cache_write']['avg_launch_us']:.1f} us "
+            f"({res['cache_write']['achieved']:.0f} GB/s)")
     if not a.no_cpu_baseline:
         log("timing the oracle on the host")
         res["cpu_baseline"] = cpu_baseline(w, p, a.cpu_seconds)
