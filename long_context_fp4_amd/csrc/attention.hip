@@ -38,6 +38,7 @@
 #include "device.h"
 #include "kernels.h"
 #include <math.h>
+#include <atomic>
 
 namespace csa2 {
 
@@ -365,12 +366,17 @@ size_t attention_lds_bytes() { return AT_LDS; }
 hipError_t launch_attention(const uint8_t* kv, const int64_t* entry_offset, const int32_t* n_entries,
                             const int32_t* idx, int k, const uint16_t* q, int B, int H, float tau,
                             int S, float* out, float* lse, float* part, hipStream_t stream) {
-  static bool attr_set = false;
-  if (!attr_set) {
+  // the dynamic LDS limit is raised once per device (per-device flags: the
+  // attribute belongs to the current device)
+  static std::atomic<uint32_t> attr_set[64];
+  int dev = 0;
+  hipError_t e0 = hipGetDevice(&dev);
+  if (e0 != hipSuccess) return e0;
+  if (dev < 0 || dev >= 64 || !attr_set[dev].load(std::memory_order_acquire)) {
     hipError_t e = hipFuncSetAttribute((const void*)attention_kernel,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, AT_LDS);
     if (e != hipSuccess) return e;
-    attr_set = true;
+    if (dev >= 0 && dev < 64) attr_set[dev].store(1u, std::memory_order_release);
   }
   dim3 grid((unsigned)(B * ((H + 15) / 16) * S)), block(AT_THREADS);
   hipLaunchKernelGGL(attention_kernel, grid, block, AT_LDS, stream, kv, entry_offset, n_entries, idx,
