@@ -11,11 +11,11 @@
 // (64 B of codes + 4 B of scales).
 //
 // Work layout: one workgroup of 320 lanes packs 16 entries. Waves 0-3 own the
-// latent (16 lanes per entry, 32 channels = two scale blocks per lane), wave 4
-// owns the indexer key (4 lanes per entry, 32 channels = one MX block per
-// lane). Every lane therefore merges 32 channels of m rows: m x 64 B of
-// contiguous bf16 loads and one 16 B store of codes, so the reads of a row and
-// the writes of the code bytes are fully coalesced 128-bit accesses.
+// latent (16 lanes per entry), wave 4 owns the indexer key (4 lanes per
+// entry). Every lane merges 32 channels of m rows with 16-byte loads laid out
+// so that each load instruction covers whole contiguous stretches of the rows
+// (a streaming load never leaves a line half read), and writes its codes as
+// 4-byte words that are contiguous across the lanes of an entry.
 //
 // Bit-exactness: the merge is evaluated with separate float32 roundings
 // (contraction is switched off for this file), the scale division is the
@@ -77,6 +77,14 @@ __device__ __forceinline__ int floor_log2(float a) {
   return 31 - __clz(b) - 149;
 }
 
+// Lane mapping. Latent (waves 0-3): 16 lanes per entry; lane p takes the 8
+// channels 128q + 8p .. +7 for q = 0..3, so each 16-byte load instruction of
+// the 16 lanes reads 256 contiguous bytes of a row, and a 16-channel scale
+// block (channels 16b .. 16b+15, b = 8q + p/2) is split over the lane pair
+// p, p^1. Indexer (wave 4): 4 lanes per entry; lane p takes channels
+// 32q + 8p .. +7, so a 32-channel MX block q is split over the lane quad.
+// Block maxima are combined across lanes with DPP swaps (max is exact, so
+// the result does not depend on the split).
 template <int M>
 __global__ __launch_bounds__(CW_THREADS) void cache_write_kernel(
     const uint16_t* __restrict__ x_lat, const uint16_t* __restrict__ x_idx,
@@ -89,12 +97,13 @@ __global__ __launch_bounds__(CW_THREADS) void cache_write_kernel(
   const int tid = threadIdx.x;
   const bool latent = tid < 256;
   const int el = latent ? (tid >> 4) : ((tid - 256) >> 2);
-  const int part = latent ? (tid & 15) : ((tid - 256) & 3);
+  const int p = latent ? (tid & 15) : ((tid - 256) & 3);
   const int C = latent ? 512 : 128;
+  const int qstride = latent ? 128 : 32;            // channels between a lane's 8-channel groups
   const int64_t e = (int64_t)blockIdx.x * CW_ENTRIES + el;
   const bool valid = e < n_total;
 
-  float acc[32];
+  float acc[32];                                    // acc[8q + c] = channel qstride*q + 8p + c
   if (valid) {
     const int64_t b = e / E, i = e - b * E;
     const int64_t row0 = b * T + i * (int64_t)m;
@@ -102,87 +111,93 @@ __global__ __launch_bounds__(CW_THREADS) void cache_write_kernel(
     const float* wb = latent ? w_lat : w_idx;
 #pragma unroll
     for (int j = 0; j < m; ++j) {
-      const u32x4_t* src = (const u32x4_t*)(xb + (row0 + j) * C + part * 32);
-      const float4* wp = (const float4*)(wb + (int64_t)j * C + part * 32);
+      const uint16_t* src = xb + (row0 + j) * C + 8 * p;
       u32x4_t xv[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) xv[q] = __builtin_nontemporal_load(src + q);
+      for (int q = 0; q < 4; ++q) xv[q] = __builtin_nontemporal_load((const u32x4_t*)(src + qstride * q));
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        float4 wv = wp[q];
-        uint32_t d0 = xv[q >> 1][(q & 1) * 2], d1 = xv[q >> 1][(q & 1) * 2 + 1];
-        float x0 = bf16_to_f32(d0 & 0xFFFFu), x1 = bf16_to_f32(d0 >> 16);
-        float x2 = bf16_to_f32(d1 & 0xFFFFu), x3 = bf16_to_f32(d1 >> 16);
-        if (j == 0) {
-          acc[4 * q + 0] = wv.x * x0; acc[4 * q + 1] = wv.y * x1;
-          acc[4 * q + 2] = wv.z * x2; acc[4 * q + 3] = wv.w * x3;
-        } else {
-          acc[4 * q + 0] = acc[4 * q + 0] + wv.x * x0; acc[4 * q + 1] = acc[4 * q + 1] + wv.y * x1;
-          acc[4 * q + 2] = acc[4 * q + 2] + wv.z * x2; acc[4 * q + 3] = acc[4 * q + 3] + wv.w * x3;
+      for (int q = 0; q < 4; ++q) {
+        const float4* wp = (const float4*)(wb + (int64_t)j * C + qstride * q + 8 * p);
+        const float4 wa = wp[0], wc = wp[1];
+        const float wv[8] = {wa.x, wa.y, wa.z, wa.w, wc.x, wc.y, wc.z, wc.w};
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          const uint32_t d = xv[q][h];
+          const float x0 = bf16_to_f32(d & 0xFFFFu), x1 = bf16_to_f32(d >> 16);
+          if (j == 0) {
+            acc[8 * q + 2 * h] = wv[2 * h] * x0;
+            acc[8 * q + 2 * h + 1] = wv[2 * h + 1] * x1;
+          } else {
+            acc[8 * q + 2 * h] = acc[8 * q + 2 * h] + wv[2 * h] * x0;
+            acc[8 * q + 2 * h + 1] = acc[8 * q + 2 * h + 1] + wv[2 * h + 1] * x1;
+          }
         }
       }
     }
+  } else {
+#pragma unroll
+    for (int c = 0; c < 32; ++c) acc[c] = 0.0f;
+  }
+
+  // per 8-channel group: the lane's amax, combined over the lanes of its block
+  uint32_t amax_bits[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    float a = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) a = fmaxf(a, fabsf(acc[8 * q + c]));
+    uint32_t ab = __float_as_uint(a);                 // a >= 0: the bits order like the values
+    ab = max(ab, (uint32_t)__builtin_amdgcn_update_dpp((int)ab, (int)ab, 0xB1, 0xf, 0xf, false));   // lane ^ 1
+    if (!latent) ab = max(ab, (uint32_t)__builtin_amdgcn_update_dpp((int)ab, (int)ab, 0x4E, 0xf, 0xf, false));   // lane ^ 2
+    amax_bits[q] = ab;
   }
 
   if (latent) {
-    uint32_t codes[4];
-    uint32_t sbytes = 0;
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      float amax = 0.0f;
-#pragma unroll
-      for (int c = 0; c < 16; ++c) amax = fmaxf(amax, fabsf(acc[16 * blk + c]));
+    for (int q = 0; q < 4; ++q) {
+      const float amax = __uint_as_float(amax_bits[q]);
       float s;
-      uint32_t sb = e4m3fn_rne(amax / 6.0f, &s);
-      sbytes |= sb << (8 * blk);
+      const uint32_t sb = e4m3fn_rne(amax / 6.0f, &s);
       Thresholds th(s);
-#pragma unroll
-      for (int d = 0; d < 2; ++d) {
-        uint32_t word = 0;
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          float x = acc[16 * blk + 8 * d + c];
-          uint32_t code = th.mag(fabsf(x)) | ((__float_as_uint(x) >> 28) & 8u);
-          word |= code << (4 * c);
-        }
-        codes[2 * blk + d] = (s > 0.0f) ? word : 0u;
-      }
-    }
-    if (valid) {
-      u32x4_t out = {codes[0], codes[1], codes[2], codes[3]};
-      *(u32x4_t*)(kv + e * 288 + part * 16) = out;
-      ((uint16_t*)&lds_scale[el][0])[part] = (uint16_t)sbytes;
-    }
-  } else {
-    float amax = 0.0f;
-#pragma unroll
-    for (int c = 0; c < 32; ++c) amax = fmaxf(amax, fabsf(acc[c]));
-    uint32_t xbyte = 0;
-    float s = 0.0f;
-    if (amax > 0.0f) {
-      int X = floor_log2(amax) - 2;
-      int bb = X + 127;
-      bb = bb < 0 ? 0 : (bb > 254 ? 254 : bb);
-      xbyte = (uint32_t)bb;
-      s = ldexpf(1.0f, bb - 127);
-    }
-    Thresholds th(s);
-    uint32_t codes[4];
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
       uint32_t word = 0;
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
-        float x = acc[8 * d + c];
-        uint32_t code = th.mag(fabsf(x)) | ((__float_as_uint(x) >> 28) & 8u);
+        const float x = acc[8 * q + c];
+        const uint32_t code = th.mag(fabsf(x)) | ((__float_as_uint(x) >> 28) & 8u);
         word |= code << (4 * c);
       }
-      codes[d] = (amax > 0.0f) ? word : 0u;
+      if (!(s > 0.0f)) word = 0u;
+      if (valid) {
+        *(uint32_t*)(kv + e * 288 + 64 * q + 4 * p) = word;
+        if ((p & 1) == 0) ((uint8_t*)&lds_scale[el][0])[8 * q + (p >> 1)] = (uint8_t)sb;
+      }
     }
-    if (valid) {
-      u32x4_t out = {codes[0], codes[1], codes[2], codes[3]};
-      *(u32x4_t*)(ik + e * 64 + part * 16) = out;
-      iks[e * 4 + part] = (uint8_t)xbyte;
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float amax = __uint_as_float(amax_bits[q]);
+      uint32_t xbyte = 0;
+      float s = 0.0f;
+      if (amax > 0.0f) {
+        const int X = floor_log2(amax) - 2;
+        int bb = X + 127;
+        bb = bb < 0 ? 0 : (bb > 254 ? 254 : bb);
+        xbyte = (uint32_t)bb;
+        s = ldexpf(1.0f, bb - 127);
+      }
+      Thresholds th(s);
+      uint32_t word = 0;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const float x = acc[8 * q + c];
+        const uint32_t code = th.mag(fabsf(x)) | ((__float_as_uint(x) >> 28) & 8u);
+        word |= code << (4 * c);
+      }
+      if (!(amax > 0.0f)) word = 0u;
+      if (valid) {
+        *(uint32_t*)(ik + e * 64 + 16 * q + 4 * p) = word;
+        if (p == 0) iks[e * 4 + q] = (uint8_t)xbyte;
+      }
     }
   }
 
