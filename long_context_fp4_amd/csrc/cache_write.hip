@@ -93,6 +93,9 @@ __global__ __launch_bounds__(CW_THREADS) void cache_write_kernel(
     uint8_t* __restrict__ kv, uint8_t* __restrict__ ik, uint8_t* __restrict__ iks) {
   const int m = M > 0 ? M : m_rt;
   __shared__ uint32_t lds_scale[CW_ENTRIES][8];   // 32 latent scale bytes per entry
+  // the merge weights, [m][512] latent then [m][128] indexer, staged once per
+  // workgroup (every entry uses the same ones)
+  extern __shared__ __attribute__((aligned(16))) float lds_w[];
 
   const int tid = threadIdx.x;
   const bool latent = tid < 256;
@@ -103,12 +106,18 @@ __global__ __launch_bounds__(CW_THREADS) void cache_write_kernel(
   const int64_t e = (int64_t)blockIdx.x * CW_ENTRIES + el;
   const bool valid = e < n_total;
 
+  for (int k = tid; k < m * 128; k += CW_THREADS) {
+    ((float4*)lds_w)[k] = ((const float4*)w_lat)[k];
+    if (k < m * 32) ((float4*)(lds_w + m * 512))[k] = ((const float4*)w_idx)[k];
+  }
+  __syncthreads();
+
   float acc[32];                                    // acc[8q + c] = channel qstride*q + 8p + c
   if (valid) {
     const int64_t b = e / E, i = e - b * E;
     const int64_t row0 = b * T + i * (int64_t)m;
     const uint16_t* xb = latent ? x_lat : x_idx;
-    const float* wb = latent ? w_lat : w_idx;
+    const float* wb = latent ? lds_w : lds_w + m * 512;
 #pragma unroll
     for (int j = 0; j < m; ++j) {
       const uint16_t* src = xb + (row0 + j) * C + 8 * p;
@@ -222,11 +231,12 @@ hipError_t launch_cache_write(const uint16_t* x_lat, const uint16_t* x_idx, cons
   if (n_total == 0) return hipSuccess;
   const int64_t blocks = (n_total + CW_ENTRIES - 1) / CW_ENTRIES;
   dim3 grid((unsigned)blocks), block(CW_THREADS);
+  const size_t lds = (size_t)m * 640 * sizeof(float);   // the staged merge weights
   switch (m) {
-    case 1: hipLaunchKernelGGL(cache_write_kernel<1>, grid, block, 0, stream, x_lat, x_idx, w_lat, w_idx, n_total, E, T, m, kv, ik, iks); break;
-    case 2: hipLaunchKernelGGL(cache_write_kernel<2>, grid, block, 0, stream, x_lat, x_idx, w_lat, w_idx, n_total, E, T, m, kv, ik, iks); break;
-    case 4: hipLaunchKernelGGL(cache_write_kernel<4>, grid, block, 0, stream, x_lat, x_idx, w_lat, w_idx, n_total, E, T, m, kv, ik, iks); break;
-    default: hipLaunchKernelGGL(cache_write_kernel<0>, grid, block, 0, stream, x_lat, x_idx, w_lat, w_idx, n_total, E, T, m, kv, ik, iks); break;
+    case 1: hipLaunchKernelGGL(cache_write_kernel<1>, grid, block, lds, stream, x_lat, x_idx, w_lat, w_idx, n_total, E, T, m, kv, ik, iks); break;
+    case 2: hipLaunchKernelGGL(cache_write_kernel<2>, grid, block, lds, stream, x_lat, x_idx, w_lat, w_idx, n_total, E, T, m, kv, ik, iks); break;
+    case 4: hipLaunchKernelGGL(cache_write_kernel<4>, grid, block, lds, stream, x_lat, x_idx, w_lat, w_idx, n_total, E, T, m, kv, ik, iks); break;
+    default: hipLaunchKernelGGL(cache_write_kernel<0>, grid, block, lds, stream, x_lat, x_idx, w_lat, w_idx, n_total, E, T, m, kv, ik, iks); break;
   }
   return hipGetLastError();
 }
