@@ -19,7 +19,9 @@
  *   error nothing is enqueued and no HIP call is made; csa2_last_error()
  *   then returns a message for the calling thread. Device-side faults surface
  *   at the caller's next synchronisation of the stream.
- * - Alignment: every data pointer must be 16-byte aligned (CSA2_ERR_ALIGN).
+ * - Alignment: every data pointer must be 16-byte aligned (CSA2_ERR_ALIGN),
+ *   except the E8M0 key-scale array iks, which needs 4 bytes (one entry's row),
+ *   so that a cache can start at any entry of a larger buffer.
  * - Workspaces: a workspace must be zero-filled by the caller before its
  *   first use (e.g. allocated with zeros). In every call's layout its first
  *   CSA2_MAX_BATCH * 16640 bytes hold one control block per sequence index

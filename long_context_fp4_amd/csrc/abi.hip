@@ -27,6 +27,7 @@ int ok() {
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
 
 int hip_status(hipError_t e, const char* where) {
   if (e != hipSuccess) return fail(CSA2_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
@@ -102,7 +103,7 @@ int check_indexer_args(const uint8_t* ik, const uint8_t* iks, const int64_t* ent
   if (pool_k > 0 && !pool) return fail(CSA2_ERR_NULL, "indexer: pool_k > 0 needs a pool buffer");
   if (pool_k > 0 && cand) return fail(CSA2_ERR_UNSUPPORTED, "indexer: a pool is built by a Full pass only (cand must be NULL)");
   if (pool_k > 0 && pool_k < k) return fail(CSA2_ERR_SHAPE, "indexer: pool_k (%d) must be >= k (%d)", pool_k, k);
-  if (!aligned16(ik) || !aligned16(iks) || !aligned16(q_idx) || !aligned16(entry_offset) ||
+  if (!aligned16(ik) || !aligned4(iks) || !aligned16(q_idx) || !aligned16(entry_offset) ||
       !aligned16(n_entries) || !aligned16(topk) || (w && !aligned16(w)) || (cand && !aligned16(cand)) ||
       (pool && !aligned16(pool)))
     return fail(CSA2_ERR_ALIGN, "indexer: data pointers must be 16-byte aligned");
@@ -206,7 +207,7 @@ int csa2_cache_write(const uint16_t* x_lat, const uint16_t* x_idx, const float* 
   if ((int64_t)B * (T / m) > ((int64_t)1 << 35))
     return fail(CSA2_ERR_SHAPE, "cache_write: too many entries");
   if (!aligned16(x_lat) || !aligned16(x_idx) || !aligned16(w_lat) || !aligned16(w_idx) || !aligned16(kv) ||
-      !aligned16(ik) || !aligned16(iks))
+      !aligned16(ik) || !aligned4(iks))
     return fail(CSA2_ERR_ALIGN, "cache_write: data pointers must be 16-byte aligned");
   hipError_t e = csa2::launch_cache_write(x_lat, x_idx, w_lat, w_idx, B, T, m, kv, ik, iks, (hipStream_t)stream);
   return hip_status(e, "cache_write");

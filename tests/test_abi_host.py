@@ -50,6 +50,7 @@ def test_cache_write_validation(L):
     assert L.csa2_cache_write(P, P, P, P, 1, 10, 0, P, P, P, None) == -2
     assert L.csa2_cache_write(P, P, P, P, 1, 10, 17, P, P, P, None) == -2
     assert L.csa2_cache_write(P + 2, P, P, P, 1, 10, 2, P, P, P, None) == -3
+    assert L.csa2_cache_write(P, P, P, P, 1, 10, 2, P, P, P + 2, None) == -3   # iks needs 4 bytes
     assert "aligned" in err(L)
 
 

@@ -1,0 +1,145 @@
+"""GPU parity at the full sizes of the hierarchical-indexer and layer-group workloads.
+
+hsi1m: 4 sequences of 1048576 tokens (524288 ratio-2 entries), a Full layer that
+keeps a 16384-candidate pool and its top-512, then two Reindex layers over that
+pool, each with 64-head attention. group_ragged: 16 sequences of 32768 ..
+262144 tokens at ratio 1, layers Full, Reindex, Reuse, Reuse. The caches are
+written by the library from seeded device hidden states; the oracle recomputes
+the checked sequences end to end (cache bytes, scores, selections, attention).
+"""
+import numpy as np
+import pytest
+
+from oracle import attention as OA
+from oracle import cache as OC
+from oracle import indexer as OI
+from long_context_fp4_amd import synth
+from tests.gpu_util import ATTN_REL_TOL, attn_rel_err, check_topk, dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+def build_cache(L, torch, w, p, keep):
+    """Writes every sequence's cache on the GPU; returns the cache and the host
+    hidden states of the sequences in `keep`."""
+    lens = w.lengths if w.lengths is not None else [w.T] * w.B
+    ents = [t // w.m for t in lens]
+    off = np.concatenate([[0], np.cumsum(ents)[:-1]]).astype(np.int64)
+    E = int(sum(ents))
+    kv = torch.empty((E, 288), dtype=torch.uint8, device="cuda")
+    ik = torch.empty((E, 64), dtype=torch.uint8, device="cuda")
+    iks = torch.empty((E, 4), dtype=torch.uint8, device="cuda")
+    hidden = {}
+    for b in range(w.B):
+        x_lat, x_idx = synth.hidden_states_device(w, p, b)
+        rows = slice(int(off[b]), int(off[b]) + ents[b])
+        L.cache_write(x_lat[None], x_idx[None], dev(p["w_lat"]), dev(p["w_idx"]), w.m,
+                      kv=kv[rows], ik=ik[rows], iks=iks[rows])
+        if b in keep:
+            hidden[b] = (host(x_lat), host(x_idx))
+        del x_lat, x_idx
+    torch.cuda.synchronize()
+    return kv, ik, iks, off, np.asarray(ents, np.int32), hidden
+
+
+def check_attention(kv_rows, sel, q, out, lse, what):
+    ro, rl = OA.sparse_attention(kv_rows, sel, q)
+    err = attn_rel_err(out, ro)
+    assert np.all(err <= ATTN_REL_TOL), f"{what}: max rel err {err.max():.3g}"
+    assert np.all(np.abs(lse - rl) <= 2e-3), f"{what}: lse"
+
+
+def check_selection_shape(sel, n, k, what):
+    v = sel[sel >= 0]
+    assert len(v) == min(n, k), what
+    assert np.all(np.diff(v) > 0) and v[0] >= 0 and v[-1] < n, what
+    assert np.all(sel[len(v):] == -1), what
+
+
+def test_hsi1m_full_size_sampled():
+    import torch
+    import long_context_fp4_amd as L
+    w = synth.workload("hsi1m")
+    p = synth.params(w)
+    kv, ik, iks, off, ents, hidden = build_cache(L, torch, w, p, keep=(0,))
+    d = dict(kv=kv, ik=ik, iks=iks, entry_offset=dev(off), n_entries=dev(ents), max_n=int(ents.max()),
+             workspace=L.Workspace())
+    F, R1, R2 = p["layers"]
+    topF, pool, outF, lseF = L.decode_layer(L.CSA2_FULL, q=dev(F["q"]), q_idx=dev(F["q_idx"]), w=dev(F["w"]),
+                                            pool_k=w.pool_k, **d)
+    res = []
+    for R in (R1, R2):
+        top, _, out, lse = L.decode_layer(L.CSA2_REINDEX, q=dev(R["q"]), q_idx=dev(R["q_idx"]), w=dev(R["w"]),
+                                          pool=pool, **d)
+        res.append((top, out, lse))
+    torch.cuda.synchronize()
+    topF, pool, outF, lseF = host(topF), host(pool), host(outF), host(lseF)
+    res = [(host(t), host(o), host(l)) for t, o, l in res]
+    for b in range(w.B):                       # every sequence: shapes and nesting
+        check_selection_shape(pool[b], int(ents[b]), w.pool_k, f"pool{b}")
+        check_selection_shape(topF[b], int(ents[b]), w.k, f"full{b}")
+        assert np.all(np.isin(topF[b], pool[b])), f"full{b} not inside the pool"
+        for j, (t, _, _) in enumerate(res):
+            assert np.all(np.isin(t[b], pool[b])), f"reindex{j} {b} not inside the pool"
+    b = 0                                      # sequence 0 end to end against the oracle
+    okv, oik, oiks = OC.cache_write(hidden[b][0], hidden[b][1], p["w_lat"], p["w_idx"], w.m)
+    rows = slice(int(off[b]), int(off[b]) + int(ents[b]))
+    assert np.array_equal(host(kv[rows]), okv)
+    assert np.array_equal(host(ik[rows]), oik)
+    assert np.array_equal(host(iks[rows]), oiks)
+    s = OI.scores(oik, oiks, F["q_idx"][b], F["w"][b], 1)
+    check_topk(pool[b], OI.topk(s, np.arange(len(s)), w.pool_k), lambda q: s[q], w.pool_k, "pool0")
+    gp = pool[b][pool[b] >= 0]
+    check_topk(topF[b], OI.topk(s[gp], gp, w.k), lambda q: s[q], w.k, "full0")
+    check_attention(okv, topF[b], F["q"][b], outF[b], lseF[b], "full attention 0")
+    for j, (R, (t, o, l)) in enumerate(zip((R1, R2), res)):
+        s2 = np.zeros(len(s), np.float32)
+        s2[gp] = OI.scores(oik[gp], oiks[gp], R["q_idx"][b], R["w"][b], 1)
+        check_topk(t[b], OI.topk(s2[gp], gp, w.k), lambda q: s2[q], w.k, f"reindex{j} 0")
+        check_attention(okv, t[b], R["q"][b], o[b], l[b], f"reindex{j} attention 0")
+
+
+def test_group_ragged_full_size_sampled():
+    import torch
+    import long_context_fp4_amd as L
+    w = synth.workload("group_ragged")
+    p = synth.params(w)
+    lens = np.asarray(w.lengths)
+    keep = (int(lens.argmin()), int(lens.argmax()))
+    kv, ik, iks, off, ents, hidden = build_cache(L, torch, w, p, keep=keep)
+    d = dict(kv=kv, ik=ik, iks=iks, entry_offset=dev(off), n_entries=dev(ents), max_n=int(ents.max()),
+             workspace=L.Workspace())
+    F, R, U1, U2 = p["layers"]
+    topF, pool, outF, lseF = L.decode_layer(L.CSA2_FULL, q=dev(F["q"]), q_idx=dev(F["q_idx"]), w=dev(F["w"]),
+                                            pool_k=w.pool_k, **d)
+    topR, _, outR, lseR = L.decode_layer(L.CSA2_REINDEX, q=dev(R["q"]), q_idx=dev(R["q_idx"]), w=dev(R["w"]),
+                                         pool=pool, **d)
+    _, _, outU1, lseU1 = L.decode_layer(L.CSA2_REUSE, q=dev(U1["q"]), topk=topR, **d)
+    _, _, outU2, lseU2 = L.decode_layer(L.CSA2_REUSE, q=dev(U2["q"]), topk=topR, **d)
+    torch.cuda.synchronize()
+    topF, pool, topR = host(topF), host(pool), host(topR)
+    outs = [host(x) for x in (outF, lseF, outR, lseR, outU1, lseU1, outU2, lseU2)]
+    for b in range(w.B):
+        check_selection_shape(pool[b], int(ents[b]), w.pool_k, f"pool{b}")
+        check_selection_shape(topF[b], int(ents[b]), w.k, f"full{b}")
+        check_selection_shape(topR[b], int(ents[b]), w.k, f"reindex{b}")
+        assert np.all(np.isin(topR[b], pool[b])), f"reindex{b} not inside the pool"
+    for b in keep:
+        okv, oik, oiks = OC.cache_write(hidden[b][0], hidden[b][1], p["w_lat"], p["w_idx"], w.m)
+        rows = slice(int(off[b]), int(off[b]) + int(ents[b]))
+        assert np.array_equal(host(kv[rows]), okv)
+        assert np.array_equal(host(ik[rows]), oik)
+        assert np.array_equal(host(iks[rows]), oiks)
+        s = OI.scores(oik, oiks, F["q_idx"][b], F["w"][b], 1)
+        check_topk(pool[b], OI.topk(s, np.arange(len(s)), w.pool_k), lambda q: s[q], w.pool_k, f"pool{b}")
+        gp = pool[b][pool[b] >= 0]
+        check_topk(topF[b], OI.topk(s[gp], gp, w.k), lambda q: s[q], w.k, f"full{b}")
+        s2 = np.zeros(len(s), np.float32)
+        s2[gp] = OI.scores(oik[gp], oiks[gp], R["q_idx"][b], R["w"][b], 1)
+        check_topk(topR[b], OI.topk(s2[gp], gp, w.k), lambda q: s2[q], w.k, f"reindex{b}")
+        for (q, o, l, what) in ((F["q"][b], outs[0][b], outs[1][b], "full"),
+                                (R["q"][b], outs[2][b], outs[3][b], "reindex"),
+                                (U1["q"][b], outs[4][b], outs[5][b], "reuse1"),
+                                (U2["q"][b], outs[6][b], outs[7][b], "reuse2")):
+            sel = topF[b] if what == "full" else topR[b]
+            check_attention(okv, sel, q, o, l, f"{what} attention {b}")
