@@ -12,29 +12,40 @@
 // Design
 // ------
 // Workgroup = (sequence, group of 16 heads, split of the index list; a last
-// group with fewer heads runs with zero queries in the missing columns); its 4
-// waves take 16-entry tiles in turn. Per tile a lane gathers 64 code bytes and
-// 8 scale bytes of one entry (a quarter of its 288-byte row) and dequantizes
-// them to fp16: the gfx950 scaled FP4->fp16 conversion (which applies a power
-// of two exactly) gives 256 * E2M1, and one packed fp16 multiply by the E4M3
-// scale / 256 (the E4M3 bit pattern shifted into fp16 position) gives the exact
-// latent value (an E2M1 x E4M3 product has at most 6 significant bits and lies
-// in [2^-10, 2688], so fp16 holds it exactly).
-//   QK^T: v_mfma_f32_16x16x32_f16 with the dequantized tile as the A operand
-//   straight from registers and the queries as B. Queries are bf16; each head
-//   is multiplied by a power of two that puts its largest magnitude in
-//   [2^14, 2^15) before rounding to fp16, so only values below 2^-16 of the
-//   head's maximum can lose bits; the power is divided out of the logit.
-//   Softmax: online, in fp32, with the running reference maximum raised only
-//   when a tile's maximum exceeds it by more than 8 (so P <= e^8 fits fp16 and
-//   the 128 accumulators are rescaled rarely).
-//   PV: O^T += C^T P^T with v_mfma_f32_16x16x16_f16; P^T comes straight from
-//   the QK output registers, C^T is read back from the wave's LDS copy of the
-//   tile with gfx950's transposing LDS read (ds_read_b64_tr_b16), which hands
-//   every lane 4 entries of one dimension; rows are 1056 B apart so the 16 rows
-//   of a read fall on distinct banks.
-// The 4 waves' partial states are merged through LDS; with several splits the
-// workgroup writes an unnormalised partial that a small kernel combines.
+// group with fewer heads runs with zero queries in the missing columns). The
+// workgroups of one sequence are numbered so that they land on one XCD and
+// share its L2 for the gathered rows. Eight waves in two roles, which run at
+// the same time on every SIMD (one of each per SIMD), so that the VALU-heavy
+// dequantization overlaps the LDS- and MFMA-heavy PV product:
+//   Producers (waves 0-3) take 16-entry tiles in turn. Per tile a lane holds a
+//   quarter row (64 code bytes, 8 scale bytes) of one entry and dequantizes
+//   it to fp16: the gfx950 scaled FP4->fp16 conversion (which applies a power
+//   of two exactly) gives 256 * E2M1, and one packed fp16 multiply by the
+//   E4M3 scale / 256 (the E4M3 bit pattern shifted into fp16 position) gives
+//   the exact latent value (an E2M1 x E4M3 product has at most 6 significant
+//   bits and lies in [2^-10, 2688], so fp16 holds it exactly). QK^T is
+//   v_mfma_f32_16x16x32_f16 with the dequantized tile as the A operand
+//   straight from registers and the queries as B. The tile goes to an LDS
+//   slot and the softmax weights to a small LDS buffer. Rows are gathered two
+//   tiles ahead.
+//   Queries are bf16; each head is multiplied by a power of two that puts its
+//   largest magnitude in [2^14, 2^15) before rounding to fp16, so only values
+//   below 2^-16 of the head's maximum can lose bits; the power is divided out
+//   of the logit. Softmax: online, in fp32, with each producer's reference
+//   maximum raised only when a tile's maximum exceeds it by more than 11.5
+//   in log2 units (logits carry the factor log2(e); P = 2^(x - m) <= 2^11.5
+//   fits fp16 and rescaling is rare).
+//   Consumers (waves 4-7) own 128 dimensions each: O^T += C^T P^T with
+//   v_mfma_f32_16x16x32_f16 over the slots of the previous round (two slots =
+//   one K step of 32 entries); C^T comes from gfx950's transposing LDS read
+//   (ds_read_b64_tr_b16), which hands every lane 4 entries of one dimension;
+//   rows are 1056 B apart so the 16 rows of a read fall on distinct banks.
+//   P^T is rescaled from the producer's reference to the consumers' common
+//   one.
+// Two sets of four slots alternate: in round r the producers fill set r & 1
+// while the consumers drain set (r - 1) & 1; one barrier ends each round. With
+// several splits the workgroup writes an unnormalised partial that a small
+// kernel combines.
 #include "device.h"
 #include "kernels.h"
 #include <math.h>
@@ -42,14 +53,16 @@
 
 namespace csa2 {
 
-constexpr int AT_WAVES = 8;                    // two waves per SIMD
+constexpr int AT_PROD = 4;                     // producer waves, then as many consumers
+constexpr int AT_WAVES = 2 * AT_PROD;          // one producer and one consumer per SIMD
 constexpr int AT_THREADS = 64 * AT_WAVES;
 constexpr int AT_PITCH = 1056;                 // bytes per entry row of the fp16 tile (rows 8 banks apart)
-constexpr int AT_WAVE_LDS = 16 * AT_PITCH;     // 16896
-constexpr int AT_LDS = AT_WAVES * AT_WAVE_LDS; // 135168 (>= 4 x 32 KiB for the merge; the queries first)
-constexpr float AT_RESCALE = 8.0f;
+constexpr int AT_SLOT = 16 * AT_PITCH;         // 16896: one tile of 16 entries
+constexpr int AT_LDS = 2 * AT_PROD * AT_SLOT;  // 135168: two sets of AT_PROD slots (the queries in set 1 first)
+constexpr float AT_RESCALE = 11.5f;           // log2 units: weights stay below 2^11.5 (fp16)
 constexpr int AT_QPITCH = 1040;                // bytes per head row of the fp16 queries
 constexpr int AT_MAX_CHUNK = 2048;             // positions of one split (k <= CSA2_MAX_K)
+constexpr int AT_DIMS_PER_CONS = 512 / AT_PROD;  // 128 output dimensions per consumer
 
 __device__ __forceinline__ f16x8_t dequant_latent8(uint32_t dw, uint32_t spair) {
   const f16x2_t sp = bitcast_u32<f16x2_t>(spair);
@@ -80,41 +93,56 @@ __device__ __forceinline__ float sum_lane_groups_a(float v) {
   return __uint_as_float(r2[0]) + __uint_as_float(r2[1]);
 }
 
+// One entry's quarter row as a lane holds it: 64 code bytes and 8 scale bytes.
+struct QuarterRow {
+  u32x4_t cw[4];
+  u32x2_t sw;
+};
+
 __global__ __launch_bounds__(AT_THREADS) void attention_kernel(
     const uint8_t* __restrict__ kv, const int64_t* __restrict__ entry_offset,
     const int32_t* __restrict__ n_entries, const int32_t* __restrict__ idx, int k,
     const uint16_t* __restrict__ q, int B, int H, float tau, int S,
     float* __restrict__ out, float* __restrict__ lse, float* __restrict__ part) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];   // tile slots; the queries first
-  __shared__ float4 pbuf[AT_WAVES][64];        // softmax weights of each slot, lane layout of the producer
-  __shared__ float mref[AT_WAVES][16];         // producer reference maximum per head
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];   // tile slots; the queries in set 1 first
+  __shared__ float4 pbuf[2][AT_PROD][64];      // softmax weights of each slot, lane layout of the producer
+  __shared__ float mref[2][AT_PROD][16];       // producer reference maximum per head
   __shared__ float sm_lscale[16];
   __shared__ int32_t sidx[AT_MAX_CHUNK];       // the split's positions (-1 = skip)
 
   const int HG = (H + 15) / 16;
+  const int G = B * HG * S;
+  // dispatch deals workgroups to the 8 XCDs in turn; number them so that the
+  // workgroups of one sequence share an XCD (and its L2)
   const int wg = blockIdx.x;
-  const int s = wg % S;
-  const int hg = (wg / S) % HG;
-  const int b = wg / (S * HG);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lin = (G & 7) == 0 ? (wg & 7) * (G >> 3) + (wg >> 3) : wg;
+  const int s = lin % S;
+  const int hg = (lin / S) % HG;
+  const int b = lin / (S * HG);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, kg = lane >> 4;
   const int head = 16 * hg + r;
   const bool head_ok = head < H;
+  const bool producer = wave < AT_PROD;
+  const int pw = producer ? wave : wave - AT_PROD;   // index within the role
 
-  // --- entry range of this split, in tiles of 16
+  // --- entry range of this split, in tiles of 16; producer pw takes tiles
+  // pw, pw + AT_PROD, ...
   const int chunk = ((k + S - 1) / S + 15) & ~15;
   const int e_lo = s * chunk;
   const int e_hi = min(k, e_lo + chunk);
   const int nent = max(e_hi - e_lo, 0);
   const int ntiles = (nent + 15) / 16;
-  const int nrounds = (ntiles + AT_WAVES - 1) / AT_WAVES;
   const int64_t nb = n_entries[b];
   const int64_t row_base = entry_offset[b];
   const int32_t* ib = idx + (int64_t)b * k + e_lo;
-  const bool any_rows = nb > 0;
+  const bool any_rows = nb > 0 && ntiles > 0;
+  const int nrp = (ntiles + AT_PROD - 1) / AT_PROD;   // rounds with a tile to produce
+  const int R = any_rows ? nrp + 1 : 0;              // plus one round to drain
 
-  // --- early loads: this thread's query slice, and the first rows of this wave
-  // (tile `wave`, position read straight from the index list)
+  // --- early loads: this thread's query slice, its share of the index list,
+  // and (producers) the rows of their first two tiles
   const int qh = tid >> 5, qc = tid & 31;
   const int hq = 16 * hg + qh;
   u32x4_t raw[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
@@ -123,29 +151,50 @@ __global__ __launch_bounds__(AT_THREADS) void attention_kernel(
     raw[0] = *(const u32x4_t*)src;
     raw[1] = *(const u32x4_t*)(src + 8);
   }
-  // A lane holds a quarter row (64 code bytes, 8 scale bytes) of one entry of
-  // the wave's current tile; each part is reloaded with the next tile's row as
-  // soon as it has been consumed. Skipped entries read row 0 of the sequence.
-  u32x4_t cw[4] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};
-  u32x2_t sw = {0, 0};
-  if (any_rows && wave < ntiles) {
-    const int e = 16 * wave + r;
-    int p = e < nent ? ib[e] : -1;
-    p = (p >= 0 && p < nb) ? p : 0;
-    const uint8_t* row = kv + (row_base + p) * 288;
+  int32_t iv[AT_MAX_CHUNK / AT_THREADS];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) cw[c] = *(const u32x4_t*)(row + 64 * kg + 16 * c);
-    sw = *(const u32x2_t*)(row + 256 + 8 * kg);
+  for (int c = 0; c < AT_MAX_CHUNK / AT_THREADS; ++c) {
+    const int i = tid + c * AT_THREADS;
+    iv[c] = i < nent ? ib[i] : -1;
   }
-  for (int i = tid; i < nrounds * AT_WAVES * 16; i += AT_THREADS) {
-    const int p = i < nent ? ib[i] : -1;
-    sidx[i] = (p >= 0 && p < nb) ? p : -1;
+  // a producer lane's row of tile t (clamped to the last tile; skipped entries
+  // read row 0 of the sequence)
+  auto row_of = [&](int p) -> const uint8_t* {
+    p = (p >= 0 && p < nb) ? p : 0;
+    return kv + (row_base + p) * 288;
+  };
+  auto load_quarter = [&](QuarterRow& qr, const uint8_t* row) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) qr.cw[c] = *(const u32x4_t*)(row + 64 * kg + 16 * c);
+    qr.sw = *(const u32x2_t*)(row + 256 + 8 * kg);
+  };
+  QuarterRow bufA, bufB;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) { bufA.cw[c] = u32x4_t{0, 0, 0, 0}; bufB.cw[c] = u32x4_t{0, 0, 0, 0}; }
+  bufA.sw = u32x2_t{0, 0};
+  bufB.sw = u32x2_t{0, 0};
+  if (producer) {
+    // unconditional, so that the wait counts in the round loop stay exact; a
+    // split without rows reads the start of the query buffer (at least 1 KiB,
+    // never used)
+    const int t0 = max(min(pw, ntiles - 1), 0), t1 = max(min(pw + AT_PROD, ntiles - 1), 0);
+    const int e0 = 16 * t0 + r, e1 = 16 * t1 + r;
+    const int p0 = e0 < nent ? ib[e0] : -1;
+    const int p1 = e1 < nent ? ib[e1] : -1;
+    const uint8_t* const qrow = (const uint8_t*)q;
+    load_quarter(bufA, any_rows ? row_of(p0) : qrow);
+    load_quarter(bufB, any_rows ? row_of(p1) : qrow);
+  }
+#pragma unroll
+  for (int c = 0; c < AT_MAX_CHUNK / AT_THREADS; ++c) {
+    const int i = tid + c * AT_THREADS;
+    if (i < 16 * ntiles) sidx[i] = (iv[c] >= 0 && iv[c] < nb) ? iv[c] : -1;
   }
 
-  // --- queries to fp16 in LDS. Each head is scaled by a power of two that puts
-  // its largest magnitude in [2^14, 2^15) before rounding; the logit divides it
-  // out again.
-  uint8_t* qlds = smem;
+  // --- queries to fp16 in LDS (slot set 1, first written in round 1). Each
+  // head is scaled by a power of two that puts its largest magnitude in
+  // [2^14, 2^15) before rounding; the logit divides it out again.
+  uint8_t* qlds = smem + AT_PROD * AT_SLOT;
   {
     uint32_t qmax = 0;                       // |bf16| bit patterns order like their values
 #pragma unroll
@@ -180,151 +229,193 @@ __global__ __launch_bounds__(AT_THREADS) void attention_kernel(
     if (qc == 0) sm_lscale[qh] = ldexpf(tau, -sigma);
   }
   __syncthreads();
-  // B operand of QK: column = head r, K-slice = dims 128kg + 8j .. +7
+
+  // Producer state: B operand of QK (column = head r, K-slice = dims
+  // 128kg + 8j .. +7), reference maximum and partial sum for head r.
+  // Consumer state: the common reference M_c and O^T[dims][heads] for dims
+  // 128 pw .. 128 pw + 127 in eight 16-dim M-tiles.
   f16x8_t qb[16];
+  float lscale = 0.0f;
+  if (producer) {
 #pragma unroll
-  for (int j = 0; j < 16; ++j) qb[j] = *(const f16x8_t*)(qlds + r * AT_QPITCH + 256 * kg + 16 * j);
-  const float lscale = sm_lscale[r];
-  uint8_t* wlds = smem + wave * AT_WAVE_LDS;
-  __syncthreads();                           // the queries' LDS becomes tile space
-
-  // Producer state (this wave's tiles): reference maximum and partial sum for
-  // head r. Consumer state (dims 64 wave .. 64 wave + 63 of every head): the
-  // common reference M_c and O^T[dims][heads] in four 16-dim M-tiles.
+    for (int j = 0; j < 16; ++j) qb[j] = *(const f16x8_t*)(qlds + r * AT_QPITCH + 256 * kg + 16 * j);
+    lscale = sm_lscale[r] * 1.4426950408889634f;   // logits in log2 units
+  } else {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) qb[j] = f16x8_t{};
+  }
   float m_w = -INFINITY, l_w = 0.0f, M_c = -INFINITY;
-  f32x4_t O[4];
+  f32x4_t O[8];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) O[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  const int last = ntiles - 1 - ((ntiles - 1 - wave) & (AT_WAVES - 1));   // this wave's last tile
+  for (int t = 0; t < 8; ++t) O[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-  for (int rd = 0; any_rows && rd < nrounds; ++rd) {
-    // ---- produce: tile t of this wave -> fp16 slot, logits, weights
-    const int t = rd * AT_WAVES + wave;
+  // ---- produce round j: tile pw + AT_PROD j from qr into slot set `set`;
+  // qr is reloaded with the rows of the tile two rounds ahead
+  auto produce = [&](int j, QuarterRow& qr, int set) {
+    const int t = pw + AT_PROD * j;
     const bool t_ok = t < ntiles;
     const uint64_t vmask = t_ok ? __ballot(sidx[16 * t + r] >= 0) : 0ull;
-    {
-      const int next = t_ok ? min(t + AT_WAVES, last) : last;
-      const int pn = last >= 0 ? sidx[16 * next + r] : -1;
-      const uint8_t* rown = kv + (row_base + (pn >= 0 ? pn : 0)) * 288;
-      f32x4_t lg = {0.0f, 0.0f, 0.0f, 0.0f};
+    const int tn = min(t + 2 * AT_PROD, ntiles - 1);
+    const uint8_t* rown = row_of(sidx[16 * tn + r]);
+    uint8_t* wlds = smem + (set * AT_PROD + pw) * AT_SLOT;
+    // two accumulators halve the dependent MFMA chain
+    f32x4_t lg2[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const uint32_t sbyte = (sw[j >> 3] >> (8 * ((j >> 1) & 3))) & 0xFFu;
-        const f16x8_t ca = dequant_latent8(cw[j >> 2][j & 3], scale_pair(sbyte));
-        lg = __builtin_amdgcn_mfma_f32_16x16x32_f16(ca, qb[j], lg, 0, 0, 0);
-        *(f16x8_t*)(wlds + r * AT_PITCH + 256 * kg + 16 * j) = ca;
-        if ((j & 3) == 3) cw[j >> 2] = *(const u32x4_t*)(rown + 64 * kg + 16 * (j >> 2));
-      }
-      sw = *(const u32x2_t*)(rown + 256 + 8 * kg);
-
-      // this lane: entries 4kg + i of the tile, head r
-      float x[4];
-      float tmax = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bool v = (vmask >> (4 * kg + i)) & 1ull;
-        x[i] = v ? lg[i] * lscale : -INFINITY;
-        tmax = fmaxf(tmax, x[i]);
-      }
-      tmax = max_lane_groups(tmax);
-      // the reference rises only when a tile exceeds it by more than AT_RESCALE,
-      // so the weights stay below e^AT_RESCALE
-      if (tmax > m_w + AT_RESCALE || (m_w == -INFINITY && tmax > -INFINITY)) {
-        const float m_new = fmaxf(m_w, tmax);
-        l_w *= (m_w == -INFINITY) ? 0.0f : __expf(m_w - m_new);
-        m_w = m_new;
-      }
-      float4 pv;
-      pv.x = (m_w == -INFINITY) ? 0.0f : __expf(x[0] - m_w);
-      pv.y = (m_w == -INFINITY) ? 0.0f : __expf(x[1] - m_w);
-      pv.z = (m_w == -INFINITY) ? 0.0f : __expf(x[2] - m_w);
-      pv.w = (m_w == -INFINITY) ? 0.0f : __expf(x[3] - m_w);
-      l_w += (pv.x + pv.y) + (pv.z + pv.w);
-      pbuf[wave][lane] = pv;
-      if (kg == 0) mref[wave][r] = m_w;
+    for (int jj = 0; jj < 16; ++jj) {
+      const uint32_t sbyte = (qr.sw[jj >> 3] >> (8 * ((jj >> 1) & 3))) & 0xFFu;
+      const f16x8_t ca = dequant_latent8(qr.cw[jj >> 2][jj & 3], scale_pair(sbyte));
+      lg2[jj & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ca, qb[jj], lg2[jj & 1], 0, 0, 0);
+      *(f16x8_t*)(wlds + r * AT_PITCH + 256 * kg + 16 * jj) = ca;
     }
-    __syncthreads();
+    const f32x4_t lg = lg2[0] + lg2[1];
+    // the reloads go after the buffer's last use, so that they land in the
+    // same registers (no copies, hence no early waits, at the loop edge)
+    __builtin_amdgcn_sched_barrier(0);
+    load_quarter(qr, rown);
 
-    // ---- consume: O^T[64 dims of this wave] += C^T P^T over the round's 8 slots
-    {
-      float mw[AT_WAVES];
-      float mr = M_c;
+    // this lane: entries 4kg + i of the tile, head r
+    float x[4];
+    float tmax = -INFINITY;
 #pragma unroll
-      for (int w = 0; w < AT_WAVES; ++w) { mw[w] = mref[w][r]; mr = fmaxf(mr, mw[w]); }
-      if (mr > M_c) {
-        const float alpha = (M_c == -INFINITY) ? 0.0f : __expf(M_c - mr);
+    for (int i = 0; i < 4; ++i) {
+      const bool v = (vmask >> (4 * kg + i)) & 1ull;
+      x[i] = v ? lg[i] * lscale : -INFINITY;
+      tmax = fmaxf(tmax, x[i]);
+    }
+    tmax = max_lane_groups(tmax);
+    // the reference rises only when a tile exceeds it by more than AT_RESCALE,
+    // so the weights stay below 2^AT_RESCALE
+    if (tmax > m_w + AT_RESCALE || (m_w == -INFINITY && tmax > -INFINITY)) {
+      const float m_new = fmaxf(m_w, tmax);
+      l_w *= (m_w == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_w - m_new);
+      m_w = m_new;
+    }
+    float4 pv;
+    pv.x = (m_w == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(x[0] - m_w);
+    pv.y = (m_w == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(x[1] - m_w);
+    pv.z = (m_w == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(x[2] - m_w);
+    pv.w = (m_w == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(x[3] - m_w);
+    l_w += (pv.x + pv.y) + (pv.z + pv.w);
+    pbuf[set][pw][lane] = pv;
+    if (kg == 0) mref[set][pw][r] = m_w;
+  };
+
+  // ---- consume the slot set `set`: O^T[128 dims] += C^T P^T over its 4 slots
+  typedef short i16x4_t __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
+  // lane 4m + a of lane group kg points at entry 4kg + m, dims 16u + 4a .. +3;
+  // after the transposing read, lane i of the group holds dim 16u + i of entries 4kg .. 4kg+3
+  const int toff = (4 * kg + (r >> 2)) * AT_PITCH + 8 * (r & 3) + 2 * AT_DIMS_PER_CONS * pw;
+  auto consume = [&](int set) {
+    float mw[AT_PROD];
+    float mr = M_c;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) O[u] *= alpha;
-        M_c = mr;
-      }
-      typedef short i16x4_t __attribute__((ext_vector_type(4)));
-      typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
-      const int j = lane & 15;
-      // lane 4m + a of lane group kg points at entry 4kg + m, dims 16u + 4a .. +3;
-      // after the transposing read, lane i of the group holds dim 16u + i of entries 4kg .. 4kg+3
-      const int toff = (4 * kg + (j >> 2)) * AT_PITCH + 8 * (j & 3) + 32 * (4 * wave);
+    for (int w = 0; w < AT_PROD; ++w) { mw[w] = mref[set][w][r]; mr = fmaxf(mr, mw[w]); }
+    if (mr > M_c) {
+      const float alpha = (M_c == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(M_c - mr);
 #pragma unroll
-      for (int pr = 0; pr < AT_WAVES / 2; ++pr) {
-        const int w0 = 2 * pr, w1 = 2 * pr + 1;
-        const float f0 = (mw[w0] == -INFINITY) ? 0.0f : __expf(mw[w0] - M_c);
-        const float f1 = (mw[w1] == -INFINITY) ? 0.0f : __expf(mw[w1] - M_c);
-        const float4 p0 = pbuf[w0][lane], p1 = pbuf[w1][lane];
-        // K-slots 8kg .. 8kg+3: slot w0 entries 4kg .. 4kg+3; 8kg+4 .. 8kg+7: slot w1
-        const f16x8_t pb = {(_Float16)(p0.x * f0), (_Float16)(p0.y * f0), (_Float16)(p0.z * f0),
-                            (_Float16)(p0.w * f0), (_Float16)(p1.x * f1), (_Float16)(p1.y * f1),
-                            (_Float16)(p1.z * f1), (_Float16)(p1.w * f1)};
-        __attribute__((address_space(3))) uint8_t* t0 =
-            (__attribute__((address_space(3))) uint8_t*)smem + w0 * AT_WAVE_LDS + toff;
-        __attribute__((address_space(3))) uint8_t* t1 =
-            (__attribute__((address_space(3))) uint8_t*)smem + w1 * AT_WAVE_LDS + toff;
+      for (int u = 0; u < 8; ++u) O[u] *= alpha;
+      M_c = mr;
+    }
+    // all 32 transposing reads of the round are issued before the first MFMA
+    i16x4_t av[AT_PROD][8];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const i16x4_t a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(t0 + 32 * u));
-          const i16x4_t a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(t1 + 32 * u));
-          f16x8_t a;
-          __builtin_memcpy(&a, &a0, 8);
-          __builtin_memcpy((uint8_t*)&a + 8, &a1, 8);
-          O[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pb, O[u], 0, 0, 0);
-        }
+    for (int w = 0; w < AT_PROD; ++w) {
+      __attribute__((address_space(3))) uint8_t* tw =
+          (__attribute__((address_space(3))) uint8_t*)smem + (set * AT_PROD + w) * AT_SLOT + toff;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) av[w][u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tw + 32 * u));
+    }
+#pragma unroll
+    for (int pr = 0; pr < AT_PROD / 2; ++pr) {
+      const int w0 = 2 * pr, w1 = 2 * pr + 1;
+      const float f0 = (mw[w0] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mw[w0] - M_c);
+      const float f1 = (mw[w1] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mw[w1] - M_c);
+      const float4 p0 = pbuf[set][w0][lane], p1 = pbuf[set][w1][lane];
+      // K-slots 8kg .. 8kg+3: slot w0 entries 4kg .. 4kg+3; 8kg+4 .. 8kg+7: slot w1
+      const f16x8_t pb = {(_Float16)(p0.x * f0), (_Float16)(p0.y * f0), (_Float16)(p0.z * f0),
+                          (_Float16)(p0.w * f0), (_Float16)(p1.x * f1), (_Float16)(p1.y * f1),
+                          (_Float16)(p1.z * f1), (_Float16)(p1.w * f1)};
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        f16x8_t a;
+        __builtin_memcpy(&a, &av[w0][u], 8);
+        __builtin_memcpy((uint8_t*)&a + 8, &av[w1][u], 8);
+        O[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pb, O[u], 0, 0, 0);
       }
     }
-    __syncthreads();
+  };
+
+  // round rd: producers fill set rd & 1 (rounds >= nrp produce nothing
+  // visible: no valid entry, weights 0), consumers drain set (rd - 1) & 1
+  // (rounds >= 1). One barrier per round; each role runs its own loop, unrolled
+  // by two so that the set and the row buffer of each half are fixed and every
+  // load in the loop is unconditional.
+  if (R > 0) {
+    int rd = 0;
+    if (producer) {
+      for (; rd + 1 < R; rd += 2) {
+        produce(rd, bufA, 0);
+        __syncthreads();
+        produce(rd + 1, bufB, 1);
+        __syncthreads();
+      }
+      if (rd < R) {
+        produce(rd, bufA, 0);
+        __syncthreads();
+      }
+    } else {
+      for (; rd + 1 < R; rd += 2) {
+        if (rd > 0) consume(1);
+        __syncthreads();
+        consume(0);
+        __syncthreads();
+      }
+      if (rd < R) {
+        consume(1);                          // rd >= 2 here: R >= 2 whenever rows exist
+        __syncthreads();
+      }
+    }
   }
 
-  // --- the sum of the weights: per wave (its own reference), then over waves
-  float* lsum = (float*)pbuf;                // [AT_WAVES][16], after the last barrier
-  float* mfin = lsum + AT_WAVES * 16;
-  l_w = sum_lane_groups_a(l_w);
-  if (lane < 16) { lsum[wave * 16 + lane] = l_w; mfin[wave * 16 + lane] = m_w; }
+  // --- the sum of the weights: per producer (its own reference), then over producers
+  float* lsum = (float*)pbuf;                // [AT_PROD][16], after the last barrier
+  float* mfin = lsum + AT_PROD * 16;
+  if (producer) {
+    l_w = sum_lane_groups_a(l_w);
+    if (lane < 16) { lsum[pw * 16 + lane] = l_w; mfin[pw * 16 + lane] = m_w; }
+  }
   __syncthreads();
+  if (producer || !head_ok) return;
   float L = 0.0f;
 #pragma unroll
-  for (int w = 0; w < AT_WAVES; ++w) {
+  for (int w = 0; w < AT_PROD; ++w) {
     const float mw = mfin[w * 16 + r];
-    if (mw != -INFINITY) L += lsum[w * 16 + r] * __expf(mw - M_c);
+    if (mw != -INFINITY) L += lsum[w * 16 + r] * __builtin_amdgcn_exp2f(mw - M_c);
   }
-  if (!head_ok) return;
 
-  // lane (r, kg) holds dims 64 wave + 16u + 4kg + i of head r in O[u][i]
+  // lane (r, kg) holds dims 128 pw + 16u + 4kg + i of head r in O[u][i]
+  const int d0 = AT_DIMS_PER_CONS * pw + 4 * kg;
   if (S == 1) {
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-    float* ob = out + ((int64_t)b * H + head) * 512 + 64 * wave + 4 * kg;
+    float* ob = out + ((int64_t)b * H + head) * 512 + d0;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < 8; ++u) {
       const f32x4_t x = O[u];
       *(float4*)(ob + 16 * u) = float4{x[0] * inv, x[1] * inv, x[2] * inv, x[3] * inv};
     }
-    if (lse && wave == 0 && kg == 0) lse[(int64_t)b * H + head] = L > 0.0f ? M_c + logf(L) : -INFINITY;
+    if (lse && pw == 0 && kg == 0)
+      lse[(int64_t)b * H + head] = L > 0.0f ? (M_c + log2f(L)) * 0.6931471805599453f : -INFINITY;
   } else {
     // partial: [B][H][S][512 + 2] -> unnormalised O, then (M, L)
     float* pb = part + (((int64_t)b * H + head) * S + s) * 514;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < 8; ++u) {
       const f32x4_t x = O[u];
-      float* o = pb + 64 * wave + 16 * u + 4 * kg;
+      float* o = pb + d0 + 16 * u;
       o[0] = x[0]; o[1] = x[1]; o[2] = x[2]; o[3] = x[3];
     }
-    if (wave == 0 && kg == 0) { pb[512] = M_c; pb[513] = L; }
+    if (pw == 0 && kg == 0) { pb[512] = M_c * 0.6931471805599453f; pb[513] = L; }   // M in natural units
   }
 }
 
