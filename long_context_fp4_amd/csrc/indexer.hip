@@ -63,6 +63,8 @@ constexpr int FIN_THREADS = 1024;  // finish workgroup of the direct top-k
 constexpr int FIN_MAX_WG = kFinMaxWg;        // score workgroups per sequence the finish reads
 constexpr int FIN_LDS_CANDS = kFinLdsCands;  // candidates the direct finish keeps in LDS
 constexpr int FIN_SUB_CAP = 4096;   // keys of the threshold bin the direct finish keeps in LDS
+constexpr int FIN_RANK_MAX = 256;   // threshold bins up to this size are resolved by ranking
+constexpr int FIN_RUN = (kFinLdsCands + FIN_THREADS - 1) / FIN_THREADS;   // candidates per thread (direct finish)
 constexpr int SEL_THREADS = 256;
 constexpr int SEL_CHUNK = 4096;     // slots per select workgroup
 constexpr int SEL_LDS_CAP = 4096;   // candidates staged in LDS by the last select workgroup
@@ -651,8 +653,10 @@ __device__ uint32_t ordered_compact(uint32_t n, Pred pred, Emit emit, uint32_t* 
 // the lists are copied to LDS, their 20-bit prefixes (relative to that cutoff,
 // the last bin holding everything 4095 or more above it) are histogrammed; the
 // bin of the K-th best prefix follows, all keys above it are selected, and the
-// few inside it are radix-selected on the full (key, position) composite. An
-// ordered compaction then writes the K positions ascending. When a list
+// few inside it are chosen on the full (key, position) composite: by ranking
+// when the bin is small, else by radix select. Every thread owns a run of
+// consecutive candidates, so one scan of the per-thread counts places the K
+// positions in ascending order. When a list
 // overflowed, the lists exceed LDS or fewer than K keys reach the highest
 // cutoff, the same steps run on a histogram of every score of the sequence.
 __global__ __launch_bounds__(FIN_THREADS) void finish_direct_kernel(
@@ -665,13 +669,31 @@ __global__ __launch_bounds__(FIN_THREADS) void finish_direct_kernel(
   __shared__ uint64_t red[32];
   __shared__ uint32_t scan_tmp[32];
   __shared__ uint32_t ctl[8];
+  __shared__ uint64_t binl[FIN_RANK_MAX];          // keys of a small threshold bin
+  __shared__ uint32_t bin_count;
   uint32_t* hist = (uint32_t*)sub;
   const int b = blockIdx.x, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  // the first header words are read before the sequence length is known
+  constexpr int NWAVE = FIN_THREADS / 64;
+  if (tid == 0) bin_count = 0;                     // first read after several barriers
+  // the first header words, and the first 128 candidates of the four lists
+  // this wave copies first (workgroups wave, wave + NWAVE, ...), are requested
+  // before the sequence length and the list lengths are known
   const int64_t nw_max = (max_n + SC_CHUNK - 1) / SC_CHUNK;
   const uint64_t* hd = sb.hdr + (int64_t)b * sb.hdr_stride;
   const uint64_t h0 = tid < nw_max ? hd[tid] : 0ull;
+  const uint64_t* wc = sb.wgc + (int64_t)b * sb.wgc_stride;
+  const int nbk = (int)(sb.wgc_stride / CAND_CAP);   // list slots per sequence (>= 1)
+  uint64_t v0[4][2];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int w = min(wave + s * NWAVE, nbk - 1);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) v0[s][u] = wc[(int64_t)w * CAND_CAP + lane + 64 * u];
+  }
+  // keeps the compiler from sinking these loads below the early return (their
+  // latency then overlaps the sequence-length load)
+  asm volatile("" ::: "memory");
   const int64_t n_pos = min((int64_t)n_entries[b], max_n);
   int32_t* ob = out + (int64_t)b * out_stride;
   if (n_pos <= K) {                       // every position is selected (or none exists)
@@ -706,8 +728,6 @@ __global__ __launch_bounds__(FIN_THREADS) void finish_direct_kernel(
     if (ovf == 0 && total <= (uint32_t)FIN_LDS_CANDS) {
       // copy the lists in workgroup order (wave v takes workgroups v, v + 16, ...,
       // eight independent loads per lane in flight) and histogram the prefixes
-      const uint64_t* wc = sb.wgc + (int64_t)b * sb.wgc_stride;
-      constexpr int NWAVE = FIN_THREADS / 64;
       auto take = [&](uint64_t c, uint32_t at) {
         lc[at] = c;
         const uint32_t p20 = (uint32_t)(c >> 44);
@@ -722,8 +742,13 @@ __global__ __launch_bounds__(FIN_THREADS) void finish_direct_kernel(
           ws[s] = min(w0 + s * NWAVE, (int)nw - 1);
           cn[s] = (w0 + s * NWAVE < nw) ? loff[ws[s] + 1] - loff[ws[s]] : 0u;
           of[s] = loff[ws[s]];
+          if (w0 == wave) {                 // the first round: already requested
 #pragma unroll
-          for (int u = 0; u < 2; ++u) v[s][u] = wc[(int64_t)ws[s] * CAND_CAP + lane + 64 * u];
+            for (int u = 0; u < 2; ++u) v[s][u] = v0[s][u];
+          } else {
+#pragma unroll
+            for (int u = 0; u < 2; ++u) v[s][u] = wc[(int64_t)ws[s] * CAND_CAP + lane + 64 * u];
+          }
         }
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
@@ -739,28 +764,92 @@ __global__ __launch_bounds__(FIN_THREADS) void finish_direct_kernel(
       fast = ctl[0] != 0xFFFFFFFFu;       // at least K keys reach the highest cutoff
     }
   }
+  if (fast) {
+    // Keys above the threshold bin are selected; inside it (20-bit prefixes
+    // lo20 .. hi20) the `need` largest. Thread t owns the run of candidates
+    // [t R, t R + R), so one scan of the per-thread counts orders the output.
+    const uint32_t T = ctl[0], above = ctl[1], in_bin = hist[T];
+    const uint32_t need = (uint32_t)K - above;      // 1 .. in_bin
+    const uint32_t lo20 = cmax + T;
+    const uint32_t hi20 = T == NBINS - 1 ? 0xFFFFFu : cmax + T;
+    const uint32_t R = (total + FIN_THREADS - 1) / FIN_THREADS;   // <= FIN_RUN
+    const uint32_t i0 = min((uint32_t)tid * R, total), i1 = min(i0 + R, total);
+    uint64_t cv[FIN_RUN];                            // this thread's run, read once
+#pragma unroll
+    for (int q = 0; q < FIN_RUN; ++q) cv[q] = i0 + q < i1 ? lc[i0 + q] : 0ull;
+    auto in_run = [&](int q) { return i0 + (uint32_t)q < i1; };
+    auto is_above = [&](uint64_t c) { return (uint32_t)(c >> 44) > hi20; };
+    auto is_in_bin = [&](uint64_t c) {
+      const uint32_t p20 = (uint32_t)(c >> 44);
+      return p20 >= lo20 && p20 <= hi20;
+    };
+    const bool split = need < in_bin;                // else every in-bin key is selected
+    const bool small = in_bin <= (uint32_t)FIN_RANK_MAX;
+    uint64_t prefix = 0, mask = 0;                   // large bins: in-bin keys with (c & mask) >= prefix
+    uint64_t* dst = binl;
+    if (split) {
+      if (!small) {
+        __syncthreads();                             // hist reads done before sub is reused
+        dst = in_bin <= (uint32_t)FIN_SUB_CAP ? sub : sb.gscr + (int64_t)b * sb.gscr_stride;
+      }
+#pragma unroll
+      for (int q = 0; q < FIN_RUN; ++q)
+        if (in_run(q) && is_in_bin(cv[q])) {
+          const uint32_t at = atomicAdd(&bin_count, 1u);
+          if (at < in_bin) dst[at] = cv[q];
+        }
+      if (dst != sub && dst != binl) __threadfence_block();   // this workgroup reads its global copy back
+      __syncthreads();
+      if (!small) {
+        const int top = radix_top_shift(dst, in_bin, red);
+        radix_select_u64(dst, in_bin, need, top, h, ctl, &prefix, &mask);
+      }
+    }
+    // small bins: keys are distinct (they carry the position), so a key is
+    // selected when fewer than `need` keys of the bin are larger
+    auto selected = [&](uint64_t c) {
+      if (is_above(c)) return true;
+      if (!is_in_bin(c)) return false;
+      if (!split) return true;
+      if (!small) return (c & mask) >= prefix;
+      uint32_t larger = 0;
+      for (uint32_t j = 0; j < in_bin; ++j) larger += binl[j] > c ? 1u : 0u;
+      return larger < need;
+    };
+    uint32_t cnt = 0, selm = 0;
+#pragma unroll
+    for (int q = 0; q < FIN_RUN; ++q)
+      if (in_run(q) && selected(cv[q])) { ++cnt; selm |= 1u << q; }
+    uint32_t nsel;
+    uint32_t at = block_exclusive_scan(cnt, scan_tmp, &nsel);
+#pragma unroll
+    for (int q = 0; q < FIN_RUN; ++q)
+      if ((selm >> q) & 1u) {
+        if (at < (uint32_t)K) ob[at] = (int32_t)(0xFFFFFFFFu - (uint32_t)cv[q]);
+        ++at;
+      }
+    for (uint32_t j = nsel + tid; j < (uint32_t)K; j += FIN_THREADS) ob[j] = -1;
+    return;
+  }
+  // Fallback: the same steps on a histogram of every score of the sequence
+  // (12-bit key bins); the threshold bin is the range of the 256 20-bit
+  // prefixes under bin T.
   const float* sall = scores + (int64_t)b * sstride;
-  if (!fast) {
-    // histogram of every score of the sequence (12-bit key bins)
-    __syncthreads();
-    for (int i = tid; i < NBINS; i += FIN_THREADS) hist[i] = 0;
-    __syncthreads();
-    for (int64_t i = tid; i < n_pos; i += FIN_THREADS) atomicAdd(&hist[score_key(sall[i]) >> BIN_SHIFT], 1u);
-    __syncthreads();
+  __syncthreads();
+  for (int i = tid; i < NBINS; i += FIN_THREADS) hist[i] = 0;
+  __syncthreads();
+  for (int64_t i = tid; i < n_pos; i += FIN_THREADS) atomicAdd(&hist[score_key(sall[i]) >> BIN_SHIFT], 1u);
+  __syncthreads();
+  {
     uint32_t tot;
     hist_kth_bin<FIN_THREADS>(hist, (uint32_t)K, scan_tmp, ctl, &tot);   // defined: n_pos > K
   }
   const uint32_t T = ctl[0], above = ctl[1], in_bin = hist[T];
   const uint32_t need = (uint32_t)K - above;      // 1 .. in_bin
-  // The threshold bin as a range [lo20, hi20] of 20-bit key prefixes: fast
-  // path, prefix cmax + T (the last bin: everything from cmax + 4095 up);
-  // fallback, the 256 prefixes under the 12-bit bin T.
-  const uint32_t lo20 = fast ? cmax + T : T << 8;
-  const uint32_t hi20 = fast ? (T == NBINS - 1 ? 0xFFFFFu : cmax + T) : (T << 8) | 255u;
-  auto elem = [&](uint32_t i) -> uint64_t {
-    return fast ? lc[i] : composite(score_key(sall[i]), i);
-  };
-  const uint32_t n_src = fast ? total : (uint32_t)n_pos;
+  const uint32_t lo20 = T << 8;
+  const uint32_t hi20 = (T << 8) | 255u;
+  auto elem = [&](uint32_t i) -> uint64_t { return composite(score_key(sall[i]), i); };
+  const uint32_t n_src = (uint32_t)n_pos;
   uint64_t prefix = 0, mask = 0;
   if (need < in_bin) {
     // the threshold bin is split: its keys (unordered) -> radix select
@@ -791,7 +880,7 @@ __global__ __launch_bounds__(FIN_THREADS) void finish_direct_kernel(
         return p20 > hi20 || (p20 >= lo20 && p20 <= hi20 && (c & mask) >= prefix);
       },
       [&](uint32_t i, uint32_t at) {
-        if (at < (uint32_t)K) ob[at] = fast ? (int32_t)(0xFFFFFFFFu - (uint32_t)lc[i]) : (int32_t)i;
+        if (at < (uint32_t)K) ob[at] = (int32_t)i;
       },
       scan_tmp);
   for (uint32_t j = nsel + tid; j < (uint32_t)K; j += FIN_THREADS) ob[j] = -1;
