@@ -41,7 +41,7 @@ SCORE_SOURCE = os.path.join(ROOT, "long_context_fp4_amd", "csrc", "indexer.hip")
 # Counter readings of one scoring launch at the decode128k size (KiB per
 # dispatch, medians over the timed launches) and the counters' scale factors
 # from the copy calibration; valid for the kernel source with this hash.
-TRAFFIC = {"source_sha": "d4dcfcb10f346419", "fetch_kib": 70252.5, "write_kib": 8771.0,
+TRAFFIC = {"source_sha": "7a2200eea382ecb0", "fetch_kib": 70244.0, "write_kib": 8798.5,
            "fetch_scale": 2.0, "write_scale": 1.0}
 
 

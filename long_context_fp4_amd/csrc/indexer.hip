@@ -53,6 +53,8 @@ namespace csa2 {
 constexpr int SC_THREADS = 256;
 constexpr int SC_CHUNK = kScoreChunk;   // slots per score workgroup
 
+constexpr int SC_SUB = 1;           // selection chunks per score workgroup
+constexpr int SC_SPAN = SC_SUB * SC_CHUNK;   // slots a score workgroup streams
 constexpr int SC_UNROLL = 4;        // tiles in flight per wave
 constexpr int NBINS = 4096;         // histogram over the top 12 bits of the key
 constexpr int BIN_SHIFT = 20;
@@ -292,16 +294,18 @@ __device__ void hist_kth_bin(const uint32_t* lhist, uint32_t need, uint32_t* sca
   uint32_t total;
   const uint32_t prefix = block_exclusive_scan(local, scan_tmp, &total);
   if (prefix < need && prefix + local >= need) {
-    uint32_t cum = prefix;
+    // the first of this thread's bins where the running count reaches `need`
+    // (selects, not a loop with a break: no nest of saved execution masks)
+    uint32_t cum = prefix, qf = BPT, cum_at = 0;
 #pragma unroll
     for (int q = 0; q < BPT; ++q) {
-      if (cum + hv[q] >= need) {
-        ctl[0] = NBINS - 1 - (BPT * threadIdx.x + q);
-        ctl[1] = cum;
-        break;
-      }
+      const bool hit = qf == BPT && cum + hv[q] >= need;
+      qf = hit ? (uint32_t)q : qf;
+      cum_at = hit ? cum : cum_at;
       cum += hv[q];
     }
+    ctl[0] = NBINS - 1 - (BPT * threadIdx.x + qf);
+    ctl[1] = cum_at;
   }
   __syncthreads();
   *total_out = total;
@@ -312,6 +316,9 @@ __device__ void hist_kth_bin(const uint32_t* lhist, uint32_t need, uint32_t* sca
 //      local cutoff summary, and for SEL_DIRECT the candidates, that
 //      finish_kernel turns into the threshold bin or the final top-K).
 // MODE: 0 = dot product of head 0, 1 = sum_h w_h * ReLU(q_h . k).
+// A workgroup streams SC_SPAN slots (SC_SUB selection chunks of SC_CHUNK);
+// eight workgroups of four waves share a compute unit, each wave with
+// SC_UNROLL tiles in flight.
 template <bool CAND, int SEL, int MODE>
 __global__ __launch_bounds__(SC_THREADS) __attribute__((amdgpu_waves_per_eu(8))) void score_kernel(
     const uint8_t* __restrict__ ik, const uint8_t* __restrict__ iks,
@@ -321,7 +328,7 @@ __global__ __launch_bounds__(SC_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
     float* __restrict__ scores, int64_t sstride, SelBufs sb, int K) {
   // histogram with 16-bit counts (two bins per word) + staged scores: 12 KiB,
   // so that eight workgroups fit one compute unit
-  __shared__ uint32_t lbuf[NBINS / 2 + SC_CHUNK];
+  __shared__ uint32_t lbuf[NBINS / 2 + SC_SPAN];
   __shared__ uint32_t scan_tmp[SC_THREADS / 64 + 1];
   __shared__ uint32_t ctl[8];
   __shared__ __attribute__((aligned(16))) float lw[16];   // head weights
@@ -351,10 +358,10 @@ __global__ __launch_bounds__(SC_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
   const float wv = tid < Hi ? (w ? w[(int64_t)b * Hi + tid] : 1.0f) : 0.0f;
   const int64_t n_pos = min((int64_t)ne, max_n);
   const int64_t nslots = CAND ? (int64_t)cand_stride : n_pos;
-  const int64_t start = (int64_t)blockIdx.x * SC_CHUNK;
+  const int64_t start = (int64_t)blockIdx.x * SC_SPAN;
   if (start >= nslots) return;
   if (CAND && n_pos <= 0) return;                  // no listed position can be valid
-  const int end = (int)min((int64_t)SC_CHUNK, nslots - start);   // slots of this workgroup
+  const int end = (int)min((int64_t)SC_SPAN, nslots - start);   // slots of this workgroup
   // the sequence's rows: a uniform base plus a 32-bit byte offset per lane
   // (positions below 2^26, checked on the host), one address register per load
   const uint8_t* ikb = ik + row_base * 64;
@@ -372,7 +379,7 @@ __global__ __launch_bounds__(SC_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
     }
   }
 
-  if (SEL != SEL_NONE) {
+  if (SEL == SEL_THRESHOLD) {
     for (int i = tid; i < NBINS / 2; i += SC_THREADS) lhist[i] = 0;
   }
   if (SEL == SEL_THRESHOLD) {
@@ -400,6 +407,179 @@ __global__ __launch_bounds__(SC_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
                      wr.z * fmaxf(acc[2], 0.0f) + wr.w * fmaxf(acc[3], 0.0f);
     return sum_lane_groups(sc);
   };
+  // ---- per selection chunk (sub = 0 .. SC_SUB-1): store its scores, then the
+  // local cutoff (every slot of a Full pass is a valid position). Chunk cix
+  // reports into its own slot of the workspace (a header word and a list), so
+  // no global atomics are needed. With two chunks per workgroup in direct
+  // mode, the first chunk's tail runs in the middle of the stream, while the
+  // second chunk's tiles are in flight.
+  auto chunk_tail = [&](int sub) {
+  const int soff = sub * SC_CHUNK;
+  const int send = min(SC_CHUNK, end - soff);        // slots of this chunk
+  if (send <= 0) return;
+  __syncthreads();                                   // its scores are staged; the previous tail is done
+  const float* lss = lsc + soff;
+  const int64_t cix = (int64_t)blockIdx.x * SC_SUB + sub;
+  // coalesced store of the chunk's scores (slots of invalid candidates hold 0)
+  {
+    float* srow = scores + (int64_t)b * sstride + start + soff;
+    for (int i4 = 4 * tid; i4 < send; i4 += 4 * SC_THREADS) {
+      if (i4 + 3 < send && (((uintptr_t)(srow + i4)) & 15) == 0) {
+        *(float4*)(srow + i4) = *(const float4*)(lss + i4);
+      } else {
+        for (int i = i4; i < min(i4 + 4, send); ++i) srow[i] = lss[i];
+      }
+    }
+  }
+  if (SEL == SEL_NONE) return;
+  const SelBufs sbl = sbs;
+  const int64_t nwg = (n_pos + SC_CHUNK - 1) / SC_CHUNK;
+  // local budget: a multiple of the chunk's expected share of the top-K plus a
+  // margin, so that the highest cutoff over the workgroups still leaves at
+  // least K keys of the sequence above it (the finish checks this)
+  const int64_t share = ((int64_t)K * SC_CHUNK + n_pos - 1) / n_pos;
+  int64_t budget64 = SEL == SEL_DIRECT ? 2 * share + 16 : 4 * share + 32;
+  if (SEL == SEL_DIRECT) budget64 = min(budget64, max((int64_t)8, (int64_t)FIN_LDS_CANDS / nwg));
+  const uint32_t budget = (uint32_t)min(budget64, (int64_t)send);
+  uint64_t* hdr = sbl.hdr + (int64_t)b * sbl.hdr_stride + cix;
+  if (SEL == SEL_THRESHOLD) {
+    if (sub > 0) {
+      for (int i = tid; i < NBINS / 2; i += SC_THREADS) lhist[i] = 0;
+      __syncthreads();
+    }
+    for (int i = tid; i < send; i += SC_THREADS) {
+      const uint32_t bin = score_key(lss[i]) >> BIN_SHIFT;
+      atomicAdd(&lhist[bin >> 1], 1u << ((bin & 1) * 16));
+    }
+    __syncthreads();
+    uint32_t cnt_all;
+    hist_kth_bin<SC_THREADS, true>(lhist, budget, scan_tmp, ctl, &cnt_all);
+    const uint32_t cbin = ctl[0];
+    // (bin, count) pairs for the non-empty bins >= cut
+    const uint32_t cut = (cbin == 0xFFFFFFFFu) ? 0u : cbin;   // fewer keys than the budget: keep all
+    uint32_t np = 0;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const uint32_t bin = NBINS - 1 - (16 * tid + q);
+      np += (bin >= cut && hcount(bin) != 0) ? 1u : 0u;
+    }
+    uint32_t tot;
+    uint32_t off = block_exclusive_scan(np, scan_tmp, &tot);
+    uint32_t* pl = sbl.summ + (int64_t)b * sbl.summ_stride + cix * SUM_PAIRS;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const uint32_t bin = NBINS - 1 - (16 * tid + q);
+      const uint32_t c = hcount(bin);
+      if (bin >= cut && c != 0) {
+        if (off < SUM_PAIRS) pl[off] = (bin << 16) | c;
+        ++off;
+      }
+    }
+    if (tid == 0) *hdr = ((uint64_t)cut << 32) | (tot > SUM_PAIRS ? 0x80000000u : tot);
+  }
+  if (SEL == SEL_DIRECT) {
+    // The cutoff: a 20-bit key prefix `fine` with at least `budget` keys of
+    // the chunk at or above it. The keys within two octaves of the chunk's
+    // largest prefix M go to a band histogram of 256 bins, 16 prefix units
+    // each, counted down from M; spread over 256 bins the LDS atomics rarely
+    // collide, unlike the 12-bit key bins, of which a chunk fills only a
+    // handful. The bin where the running count reaches the budget gives the
+    // cutoff. A chunk with fewer than `budget` keys in the band takes the
+    // exact path instead (12-bit histogram, then the 256 20-bit sub-bins of
+    // the cutoff bin). Thread t owns slots 4t .. 4t+3.
+    constexpr uint32_t sh = 4;
+    uint32_t* hb = lhist;                            // 256 words
+    uint32_t keys[4], pmax = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int i = 4 * tid + q;
+      keys[q] = i < send ? score_key(lss[i]) : 0u;
+      if (i < send) pmax = max(pmax, keys[q] >> 12);
+    }
+    pmax = wave_max_u32(pmax);
+    if (lane == 0) scan_tmp[wave] = pmax;
+    hb[tid] = 0;
+    __syncthreads();
+    uint32_t M = 0;
+#pragma unroll
+    for (int v = 0; v < SC_THREADS / 64; ++v) M = max(M, scan_tmp[v]);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t d = (M - (keys[q] >> 12)) >> sh;
+      if (4 * tid + q < send && d < 256u) atomicAdd(&hb[d], 1u);
+    }
+    __syncthreads();
+    if (wave == 0) {
+      uint32_t hv[4], sl = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) { hv[j] = hb[4 * lane + j]; sl += hv[j]; }
+      const uint32_t incl = wave_incl_sum(sl);
+      uint32_t cum = incl - sl;
+      if (cum < budget && incl >= budget) {
+        uint32_t ds = 0xFFFFFFFFu;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bool hit = ds == 0xFFFFFFFFu && cum + hv[j] >= budget;
+          ds = hit ? 4 * lane + j : ds;
+          cum += hv[j];
+        }
+        ctl[4] = ds;
+      }
+      if (lane == 63 && incl < budget) ctl[4] = 0xFFFFFFFFu;   // too few keys within the octave
+    }
+    __syncthreads();
+    const uint32_t ds = ctl[4];
+    uint32_t fine;
+    if (ds != 0xFFFFFFFFu) {
+      // bin ds holds prefixes M - (ds << sh) - (2^sh - 1) .. M - (ds << sh)
+      const uint32_t lo = ((ds + 1u) << sh) - 1u;
+      fine = M >= lo ? M - lo : 0u;
+    } else {
+      // exact path: the 12-bit bin of the budget-th key, refined to 20 bits
+      for (int i = tid; i < NBINS / 2; i += SC_THREADS) lhist[i] = 0;
+      __syncthreads();
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (4 * tid + q < send) {
+          const uint32_t bin = keys[q] >> BIN_SHIFT;
+          atomicAdd(&lhist[bin >> 1], 1u << ((bin & 1) * 16));
+        }
+      }
+      __syncthreads();
+      uint32_t cnt_all;
+      hist_kth_bin<SC_THREADS, true>(lhist, budget, scan_tmp, ctl, &cnt_all);
+      const uint32_t cbin = ctl[0], cabove = ctl[1];
+      fine = 0;                                      // fewer keys than the budget: keep all
+      if (cbin != 0xFFFFFFFFu) {
+        uint32_t* h2 = lhist;                        // every read of the 4096 bins is done (256 words)
+        h2[tid] = 0;
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (4 * tid + q < send && (keys[q] >> BIN_SHIFT) == cbin) atomicAdd(&h2[(keys[q] >> 12) & 255u], 1u);
+        __syncthreads();
+        if (tid < 64) digit_kth(h2, budget - cabove, ctl + 4);
+        __syncthreads();
+        fine = (cbin << 8) | ctl[4];
+      }
+    }
+    // candidates: every slot whose top 20 key bits are >= fine, in slot order
+    uint32_t m = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) m |= ((4 * tid + q < send && (keys[q] >> 12) >= fine) ? 1u : 0u) << q;
+    uint32_t tot;
+    uint32_t off = block_exclusive_scan((uint32_t)__popc(m), scan_tmp, &tot);
+    uint64_t* wc = sbl.wgc + (int64_t)b * sbl.wgc_stride + cix * CAND_CAP;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if ((m >> q) & 1u) {
+        if (off < CAND_CAP) wc[off] = composite(keys[q], (uint32_t)(start + soff + 4 * tid + q));
+        ++off;
+      }
+    }
+    if (tid == 0) *hdr = ((uint64_t)fine << 32) | (tot > CAND_CAP ? 0x80000000u : tot);
+  }
+  };
   if (!CAND) {
     // each wave takes tiles of 16 slots, SC_UNROLL of them in flight: a tile's
     // registers are reloaded with the same tile of the next group as soon as it
@@ -407,8 +587,11 @@ __global__ __launch_bounds__(SC_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
     // (the reloads past the chunk's end re-read its last row, which is in
     // cache; unconditional loads in a fully unrolled loop keep the wait counts
     // exact, and a short last chunk scores its clamped rows without storing them)
+    constexpr int NIT = SC_SPAN / (SC_THREADS * SC_UNROLL / 4);
+    static_assert(SC_SUB <= 2 && NIT % SC_SUB == 0, "chunks end at stream iteration boundaries");
 #pragma unroll
-    for (int it = 0; it < SC_CHUNK / (SC_THREADS * SC_UNROLL / 4); ++it) {
+    for (int it = 0; it < NIT; ++it) {
+      if (SC_SUB == 2 && SEL == SEL_DIRECT && it == NIT / 2) chunk_tail(0);   // the next tiles are in flight
       const int t0 = 16 * wave + it * 64 * SC_UNROLL;
 #pragma unroll
       for (int u = 0; u < SC_UNROLL; ++u) {
@@ -447,104 +630,8 @@ __global__ __launch_bounds__(SC_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
       }
     }
   }
-  __syncthreads();
-  // coalesced store of the chunk's scores (slots of invalid candidates hold 0)
-  {
-    float* srow = scores + (int64_t)b * sstride + start;
-    const int i4 = 4 * tid;
-    if (i4 + 3 < end && (((uintptr_t)(srow + i4)) & 15) == 0) {
-      *(float4*)(srow + i4) = *(const float4*)(lsc + i4);
-    } else {
-      for (int i = i4; i < min(i4 + 4, end); ++i) srow[i] = lsc[i];
-    }
-  }
-  if (SEL == SEL_NONE) return;
-
-  const SelBufs sbl = sbs;
-  // ---- local histogram and cutoff (every slot of a Full pass is a valid position).
-  // The workgroup reports into its own slot of the workspace (a header word and
-  // a list), so no global atomics are needed.
-  for (int i = tid; i < end; i += SC_THREADS) {
-    const uint32_t bin = score_key(lsc[i]) >> BIN_SHIFT;
-    atomicAdd(&lhist[bin >> 1], 1u << ((bin & 1) * 16));
-  }
-  __syncthreads();
-  const int64_t nwg = (n_pos + SC_CHUNK - 1) / SC_CHUNK;
-  // local budget: a multiple of the chunk's expected share of the top-K plus a
-  // margin, so that the highest cutoff over the workgroups still leaves at
-  // least K keys of the sequence above it (the finish checks this)
-  const int64_t share = ((int64_t)K * SC_CHUNK + n_pos - 1) / n_pos;
-  int64_t budget64 = SEL == SEL_DIRECT ? 2 * share + 16 : 4 * share + 32;
-  if (SEL == SEL_DIRECT) budget64 = min(budget64, max((int64_t)8, (int64_t)FIN_LDS_CANDS / nwg));
-  const uint32_t budget = (uint32_t)min(budget64, (int64_t)end);
-  uint32_t cnt_all;
-  hist_kth_bin<SC_THREADS, true>(lhist, budget, scan_tmp, ctl, &cnt_all);
-  const uint32_t cbin = ctl[0], cabove = ctl[1];
-  uint64_t* hdr = sbl.hdr + (int64_t)b * sbl.hdr_stride + blockIdx.x;
-  if (SEL == SEL_THRESHOLD) {
-    // (bin, count) pairs for the non-empty bins >= cut
-    const uint32_t cut = (cbin == 0xFFFFFFFFu) ? 0u : cbin;   // fewer keys than the budget: keep all
-    uint32_t np = 0;
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const uint32_t bin = NBINS - 1 - (16 * tid + q);
-      np += (bin >= cut && hcount(bin) != 0) ? 1u : 0u;
-    }
-    uint32_t tot;
-    uint32_t off = block_exclusive_scan(np, scan_tmp, &tot);
-    uint32_t* pl = sbl.summ + (int64_t)b * sbl.summ_stride + (int64_t)blockIdx.x * SUM_PAIRS;
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const uint32_t bin = NBINS - 1 - (16 * tid + q);
-      const uint32_t c = hcount(bin);
-      if (bin >= cut && c != 0) {
-        if (off < SUM_PAIRS) pl[off] = (bin << 16) | c;
-        ++off;
-      }
-    }
-    if (tid == 0) *hdr = ((uint64_t)cut << 32) | (tot > SUM_PAIRS ? 0x80000000u : tot);
-  }
-  if (SEL == SEL_DIRECT) {
-    // refine the cutoff to the top 20 key bits: 256 sub-bins of the cutoff bin
-    uint32_t fine = 0;                                       // fewer keys than the budget: keep all
-    if (cbin != 0xFFFFFFFFu) {
-      uint32_t* h2 = lhist;                                  // every read of the 4096 bins is done (256 words)
-      h2[tid] = 0;
-      __syncthreads();
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int i = 4 * tid + q;
-        if (i < end) {
-          const uint32_t key = score_key(lsc[i]);
-          if ((key >> BIN_SHIFT) == cbin) atomicAdd(&h2[(key >> 12) & 255u], 1u);
-        }
-      }
-      __syncthreads();
-      if (tid < 64) digit_kth(h2, budget - cabove, ctl + 4);
-      __syncthreads();
-      fine = (cbin << 8) | ctl[4];
-    }
-    // candidates: every slot whose top 20 key bits are >= fine, in slot order
-    // (thread t owns slots 4t .. 4t+3)
-    uint32_t keys[4], m = 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int i = 4 * tid + q;
-      keys[q] = i < end ? score_key(lsc[i]) : 0u;
-      m |= ((i < end && (keys[q] >> 12) >= fine) ? 1u : 0u) << q;
-    }
-    uint32_t tot;
-    uint32_t off = block_exclusive_scan((uint32_t)__popc(m), scan_tmp, &tot);
-    uint64_t* wc = sbl.wgc + (int64_t)b * sbl.wgc_stride + (int64_t)blockIdx.x * CAND_CAP;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      if ((m >> q) & 1u) {
-        if (off < CAND_CAP) wc[off] = composite(keys[q], (uint32_t)(start + 4 * tid + q));
-        ++off;
-      }
-    }
-    if (tid == 0) *hdr = ((uint64_t)fine << 32) | (tot > CAND_CAP ? 0x80000000u : tot);
-  }
+  if (SC_SUB == 1 || CAND || SEL != SEL_DIRECT) chunk_tail(0);   // (threshold mode: its tail needs the registers)
+  if (SC_SUB == 2) chunk_tail(1);
 }
 
 // ---------------------------------------------------------------- finish (one workgroup per sequence)
@@ -1080,7 +1167,7 @@ hipError_t launch_score(const uint8_t* ik, const uint8_t* iks, const int64_t* en
                         hipStream_t stream) {
   const int64_t nslots = cand ? cand_stride : max_n;
   if (nslots <= 0) return hipSuccess;
-  const int64_t nx = (nslots + SC_CHUNK - 1) / SC_CHUNK;
+  const int64_t nx = (nslots + SC_SPAN - 1) / SC_SPAN;
   dim3 grid((unsigned)nx, (unsigned)B), block(SC_THREADS);
 #define CSA2_SCORE_LAUNCH(C, S, Mo)                                                              \
   hipLaunchKernelGGL((score_kernel<C, S, Mo>), grid, block, 0, stream, ik, iks, entry_offset,   \
