@@ -152,7 +152,7 @@ int run_indexer(const uint8_t* ik, const uint8_t* iks, const int64_t* entry_offs
     hipError_t r;
     if (!cand && ev0 && (r = hipEventRecord(ev0, stream)) != hipSuccess) return r;
     r = csa2::launch_score(ik, iks, entry_offset, n_entries, B, max_n, q_idx, w, Hi, score_mode, cand,
-                           cand_stride, scores, sstride, sb, sel, K, stream);
+                           cand_stride, scores, sstride, sb, sel, K, scores_out != nullptr, stream);
     if (r != hipSuccess) return r;
     if (!cand && ev1 && (r = hipEventRecord(ev1, stream)) != hipSuccess) return r;
     return hipSuccess;
@@ -173,14 +173,19 @@ int run_indexer(const uint8_t* ik, const uint8_t* iks, const int64_t* entry_offs
   if (pool_k == 0 && k <= csa2::kDirectMaxK) {
     e = score(csa2::SEL_DIRECT, k);
     if (e != hipSuccess) return hip_status(e, "indexer score");
-    e = csa2::launch_finish(csa2::SEL_DIRECT, n_entries, B, max_n, scores, sstride, sb, k, topk, k, stream);
+    // without scores_out the score pass keeps no scores; the finish recomputes
+    // a sequence's in its fallback
+    const csa2::ScoreSrc src{ik, iks, entry_offset, q_idx, w, Hi, score_mode};
+    e = csa2::launch_finish(csa2::SEL_DIRECT, n_entries, B, max_n, scores, sstride, sb, k, topk, k,
+                            scores_out ? nullptr : &src, stream);
     return hip_status(e, "indexer select");
   }
   const int K1 = pool_k > 0 ? pool_k : k;
   int32_t* first_out = pool_k > 0 ? pool : topk;
   e = score(csa2::SEL_THRESHOLD, K1);
   if (e != hipSuccess) return hip_status(e, "indexer score");
-  e = csa2::launch_finish(csa2::SEL_THRESHOLD, n_entries, B, max_n, scores, sstride, sb, K1, nullptr, 0, stream);
+  e = csa2::launch_finish(csa2::SEL_THRESHOLD, n_entries, B, max_n, scores, sstride, sb, K1, nullptr, 0, nullptr,
+                          stream);
   if (e != hipSuccess) return hip_status(e, "indexer threshold");
   e = csa2::launch_select(scores, sstride, n_entries, B, max_n, sb.ctrl, sb.bitmap, L.bm_words, cbuf, L.slots,
                           K1, first_out, K1, stream);

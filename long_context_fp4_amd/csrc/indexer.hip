@@ -311,6 +311,27 @@ __device__ void hist_kth_bin(const uint32_t* lhist, uint32_t need, uint32_t* sca
   *total_out = total;
 }
 
+// One tile of 16 slots x 16 heads: 4 MFMAs over the 128 channels (lane (n, g):
+// slot n, channels 32g .. 32g+31); MODE 1 applies w_h * ReLU and sums the heads
+// into the lanes of group 0. The score pass and the finish's recompute share
+// it, so both give the same float32 scores.
+template <int MODE>
+__device__ __forceinline__ float score_tile_fn(const bf16x8_t (&qa)[4], const u32x4_t cw, uint32_t sbyte,
+                                               const float* lw, int g) {
+  const float scl = __uint_as_float(sbyte << 23);
+  f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    bf16x8_t kb = dequant_mx_block8(cw[j], scl);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[j], kb, acc, 0, 0, 0);
+  }
+  if (MODE == 0) return acc[0];          // head 0 is row 0, held by lanes 0..15
+  const float4 wr = *(const float4*)&lw[4 * g];
+  const float sc = wr.x * fmaxf(acc[0], 0.0f) + wr.y * fmaxf(acc[1], 0.0f) +
+                   wr.z * fmaxf(acc[2], 0.0f) + wr.w * fmaxf(acc[3], 0.0f);
+  return sum_lane_groups(sc);
+}
+
 // CAND: score the listed positions (Reindex) instead of every entry.
 // SEL: SEL_NONE (scores only); SEL_THRESHOLD / SEL_DIRECT (also report the
 //      local cutoff summary, and for SEL_DIRECT the candidates, that
@@ -325,7 +346,7 @@ __global__ __launch_bounds__(SC_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
     const int64_t* __restrict__ entry_offset, const int32_t* __restrict__ n_entries, int64_t max_n,
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w, int Hi,
     const int32_t* __restrict__ cand, int cand_stride,
-    float* __restrict__ scores, int64_t sstride, SelBufs sb, int K) {
+    float* __restrict__ scores, int64_t sstride, SelBufs sb, int K, int store_scores) {
   // histogram with 16-bit counts (two bins per word) + staged scores: 12 KiB,
   // so that eight workgroups fit one compute unit
   __shared__ uint32_t lbuf[NBINS / 2 + SC_SPAN];
@@ -394,18 +415,7 @@ __global__ __launch_bounds__(SC_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
   // one tile = 16 slots x 16 heads: 4 MFMAs over the 128 channels; the head sum
   // goes to the lanes of group 0, which stage the score in LDS
   auto score_tile = [&](const u32x4_t cw, uint32_t sbyte) -> float {
-    const float scl = __uint_as_float(sbyte << 23);
-    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      bf16x8_t kb = dequant_mx_block8(cw[j], scl);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[j], kb, acc, 0, 0, 0);
-    }
-    if (MODE == 0) return acc[0];          // head 0 is row 0, held by lanes 0..15
-    const float4 wr = *(const float4*)&lw[4 * g];
-    const float sc = wr.x * fmaxf(acc[0], 0.0f) + wr.y * fmaxf(acc[1], 0.0f) +
-                     wr.z * fmaxf(acc[2], 0.0f) + wr.w * fmaxf(acc[3], 0.0f);
-    return sum_lane_groups(sc);
+    return score_tile_fn<MODE>(qa, cw, sbyte, lw, g);
   };
   // ---- per selection chunk (sub = 0 .. SC_SUB-1): store its scores, then the
   // local cutoff (every slot of a Full pass is a valid position). Chunk cix
@@ -421,7 +431,7 @@ __global__ __launch_bounds__(SC_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
   const float* lss = lsc + soff;
   const int64_t cix = (int64_t)blockIdx.x * SC_SUB + sub;
   // coalesced store of the chunk's scores (slots of invalid candidates hold 0)
-  {
+  if (store_scores) {
     float* srow = scores + (int64_t)b * sstride + start + soff;
     for (int i4 = 4 * tid; i4 < send; i4 += 4 * SC_THREADS) {
       if (i4 + 3 < send && (((uintptr_t)(srow + i4)) & 15) == 0) {
@@ -747,8 +757,8 @@ __device__ uint32_t ordered_compact(uint32_t n, Pred pred, Emit emit, uint32_t* 
 // overflowed, the lists exceed LDS or fewer than K keys reach the highest
 // cutoff, the same steps run on a histogram of every score of the sequence.
 __global__ __launch_bounds__(FIN_THREADS) void finish_direct_kernel(
-    const int32_t* __restrict__ n_entries, int64_t max_n, const float* __restrict__ scores, int64_t sstride,
-    SelBufs sb, int K, int32_t* __restrict__ out, int out_stride) {
+    const int32_t* __restrict__ n_entries, int64_t max_n, float* __restrict__ scores, int64_t sstride,
+    SelBufs sb, int K, int32_t* __restrict__ out, int out_stride, ScoreSrc src, int rescore) {
   __shared__ uint64_t lc[FIN_LDS_CANDS];          // the candidate lists, concatenated
   __shared__ uint64_t sub[FIN_SUB_CAP];           // histogram, then the keys inside the threshold bin
   __shared__ uint32_t loff[FIN_MAX_WG + 1];       // list offsets of the workgroups
@@ -920,8 +930,33 @@ __global__ __launch_bounds__(FIN_THREADS) void finish_direct_kernel(
   }
   // Fallback: the same steps on a histogram of every score of the sequence
   // (12-bit key bins); the threshold bin is the range of the 256 20-bit
-  // prefixes under bin T.
-  const float* sall = scores + (int64_t)b * sstride;
+  // prefixes under bin T. When the score pass did not store the scores, this
+  // workgroup recomputes the sequence's first.
+  float* sall = scores + (int64_t)b * sstride;
+  if (rescore) {
+    __shared__ __attribute__((aligned(16))) float lwf[16];
+    const int n = lane & 15, g = lane >> 4;
+    const int64_t row_base = src.entry_offset[b];
+    const uint8_t* ikb = src.ik + row_base * 64;
+    const uint8_t* iksb = src.iks + row_base * 4;
+    bf16x8_t qa[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      u32x4_t v = {0, 0, 0, 0};
+      if (n < src.Hi) v = *(const u32x4_t*)(src.q_idx + ((int64_t)b * src.Hi + n) * 128 + 32 * g + 8 * j);
+      __builtin_memcpy(&qa[j], &v, 16);
+    }
+    if (tid < 16) lwf[tid] = tid < src.Hi ? (src.w ? src.w[(int64_t)b * src.Hi + tid] : 1.0f) : 0.0f;
+    __syncthreads();
+    for (int64_t t0 = 16 * wave; t0 < n_pos; t0 += 16 * (FIN_THREADS / 64)) {
+      const uint32_t p = (uint32_t)min(t0 + n, n_pos - 1);
+      const u32x4_t cw = *(const u32x4_t*)(ikb + ((uint64_t)p * 64u + 16u * g));
+      const uint32_t sbyte = iksb[(uint64_t)p * 4u + (uint32_t)g];
+      const float sc = src.mode == 0 ? score_tile_fn<0>(qa, cw, sbyte, lwf, g) : score_tile_fn<1>(qa, cw, sbyte, lwf, g);
+      if (g == 0 && t0 + n < n_pos) sall[t0 + n] = sc;
+    }
+    __threadfence_block();                         // this workgroup reads them back
+  }
   __syncthreads();
   for (int i = tid; i < NBINS; i += FIN_THREADS) hist[i] = 0;
   __syncthreads();
@@ -1164,14 +1199,16 @@ hipError_t launch_score(const uint8_t* ik, const uint8_t* iks, const int64_t* en
                         const int32_t* n_entries, int B, int64_t max_n, const uint16_t* q_idx,
                         const float* w, int Hi, int mode, const int32_t* cand, int cand_stride,
                         float* scores, int64_t sstride, const SelBufs& sb, int sel, int K,
-                        hipStream_t stream) {
+                        bool store_scores, hipStream_t stream) {
+  const bool store = store_scores || cand || sel != SEL_DIRECT;
   const int64_t nslots = cand ? cand_stride : max_n;
   if (nslots <= 0) return hipSuccess;
   const int64_t nx = (nslots + SC_SPAN - 1) / SC_SPAN;
   dim3 grid((unsigned)nx, (unsigned)B), block(SC_THREADS);
 #define CSA2_SCORE_LAUNCH(C, S, Mo)                                                              \
   hipLaunchKernelGGL((score_kernel<C, S, Mo>), grid, block, 0, stream, ik, iks, entry_offset,   \
-                     n_entries, max_n, q_idx, w, Hi, cand, cand_stride, scores, sstride, sb, K)
+                     n_entries, max_n, q_idx, w, Hi, cand, cand_stride, scores, sstride, sb, K,  \
+                     (int)store)
   if (cand) {
     if (mode == 0) CSA2_SCORE_LAUNCH(true, SEL_NONE, 0); else CSA2_SCORE_LAUNCH(true, SEL_NONE, 1);
   } else if (sel == SEL_THRESHOLD) {
@@ -1185,12 +1222,12 @@ hipError_t launch_score(const uint8_t* ik, const uint8_t* iks, const int64_t* en
   return hipGetLastError();
 }
 
-hipError_t launch_finish(int sel, const int32_t* n_entries, int B, int64_t max_n, const float* scores,
+hipError_t launch_finish(int sel, const int32_t* n_entries, int B, int64_t max_n, float* scores,
                          int64_t sstride, const SelBufs& sb, int K, int32_t* out, int out_stride,
-                         hipStream_t stream) {
+                         const ScoreSrc* src, hipStream_t stream) {
   if (sel == SEL_DIRECT)
     hipLaunchKernelGGL(finish_direct_kernel, dim3((unsigned)B), dim3(FIN_THREADS), 0, stream, n_entries, max_n,
-                       scores, sstride, sb, K, out, out_stride);
+                       scores, sstride, sb, K, out, out_stride, src ? *src : ScoreSrc{}, src ? 1 : 0);
   else
     hipLaunchKernelGGL(finish_threshold_kernel, dim3((unsigned)B), dim3(SC_THREADS), 0, stream, n_entries,
                        max_n, scores, sstride, sb, K);

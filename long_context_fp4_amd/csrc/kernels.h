@@ -53,15 +53,29 @@ struct SelBufs {
   int64_t gscr_stride;
 };
 
+// What the score pass reads, for a finish that has to recompute scores.
+struct ScoreSrc {
+  const uint8_t* ik;
+  const uint8_t* iks;
+  const int64_t* entry_offset;
+  const uint16_t* q_idx;
+  const float* w;
+  int Hi;
+  int mode;
+};
+
+// store_scores: direct mode may skip storing the scores (the finish recomputes
+// a sequence's scores in its rare fallback); the other modes always store.
 hipError_t launch_score(const uint8_t* ik, const uint8_t* iks, const int64_t* entry_offset,
                         const int32_t* n_entries, int B, int64_t max_n, const uint16_t* q_idx,
                         const float* w, int Hi, int mode, const int32_t* cand, int cand_stride,
                         float* scores, int64_t sstride, const SelBufs& sb, int sel, int K,
-                        hipStream_t stream);
+                        bool store_scores, hipStream_t stream);
 
-hipError_t launch_finish(int sel, const int32_t* n_entries, int B, int64_t max_n, const float* scores,
+// src: non-null when the direct score pass did not store the scores.
+hipError_t launch_finish(int sel, const int32_t* n_entries, int B, int64_t max_n, float* scores,
                          int64_t sstride, const SelBufs& sb, int K, int32_t* out, int out_stride,
-                         hipStream_t stream);
+                         const ScoreSrc* src, hipStream_t stream);
 
 hipError_t launch_select(const float* scores, int64_t sstride, const int32_t* n_entries, int B,
                          int64_t max_n, uint8_t* ctrl, uint32_t* bitmap, int64_t bm_stride,

@@ -134,6 +134,50 @@ def test_exact_ties_take_the_lowest_positions(n):
     assert np.all(sc[0][:n] == 0) and np.array_equal(top[0], np.arange(512))
 
 
+def run_no_scores(ik, iks, off, n_list, max_n, q, w, k):
+    """Direct top-k without scores_out: the score pass keeps no scores."""
+    import torch
+    import long_context_fp4_amd as L
+    topk, _, _ = L.indexer_topk(dev(ik), dev(iks), dev(off), dev(np.asarray(n_list, np.int32)), max_n,
+                                dev(q), dev(w), 1, k=k, want_scores=False)
+    torch.cuda.synchronize()
+    return host(topk)
+
+
+@pytest.mark.parametrize("n", [3000, 40000])
+def test_ties_without_scores_out(n):
+    """Identical rows overflow every candidate list: the finish falls back and
+    recomputes the scores it was not given; the top-k is positions 0..k-1."""
+    rng = np.random.default_rng(n + 1)
+    ik1, iks1, _ = make_keys(rng, [1])
+    ik = np.repeat(ik1, n, axis=0)
+    iks = np.repeat(iks1, n, axis=0)
+    q = synth.indexer_query(rng, 16)[None]
+    w = synth.head_weights(rng, 16)[None]
+    top = run_no_scores(ik, iks, np.zeros(1, np.int64), [n], n, q, w, 512)
+    assert np.array_equal(top[0], np.arange(512))
+
+
+def test_fallback_recomputes_scores():
+    """The 700 largest keys sit in the first chunk (their E8M0 scales raised by
+    2^6), so too few keys reach the highest local cutoff: the finish falls back
+    to the full score set, which it recomputes (no scores_out)."""
+    rng = np.random.default_rng(11)
+    n = 40000
+    ik, iks, off = make_keys(rng, [n])
+    iks = iks.copy()
+    iks[:700] = np.minimum(iks[:700].astype(np.int32) + 6, 254).astype(np.uint8)
+    q = synth.indexer_query(rng, 16)[None]
+    w = synth.head_weights(rng, 16)[None]
+    top = run_no_scores(ik, iks, off, [n], n, q, w, 512)
+    s = OI.scores(ik, iks, q[0], w[0], 1)
+    check_topk(top[0], OI.topk(s, np.arange(n), 512), lambda p: s[p], 512, "fallback")
+    # and with scores_out (stored scores), the same selection
+    top2, _, sc = run(ik, iks, off, [n], n, q, w, 1, 512)
+    np.testing.assert_allclose(sc[0][:n], s, rtol=2e-6, atol=2e-6)
+    assert np.array_equal(top[0], top2[0])
+
+
 def test_workspace_reuse_across_batch_sizes():
     """Regression: one workspace reused by calls whose B and max_n shrink and grow again.
 
