@@ -105,6 +105,21 @@ __global__ __launch_bounds__(CW_THREADS) void cache_write_kernel(
   const int qstride = latent ? 128 : 32;            // channels between a lane's 8-channel groups
   const int64_t e = (int64_t)blockIdx.x * CW_ENTRIES + el;
   const bool valid = e < n_total;
+  const int64_t eb = valid ? e / E : 0, ei = valid ? e - eb * E : 0;
+  const int64_t row0 = eb * T + ei * (int64_t)m;
+  const uint16_t* xb = latent ? x_lat : x_idx;
+
+  // with m fixed at compile time, the rows are requested before the weights
+  // are staged, so their latency overlaps the staging
+  constexpr int MR = M > 0 ? M : 1;
+  u32x4_t xr[MR][4];
+  if (M > 0 && valid) {
+#pragma unroll
+    for (int j = 0; j < MR; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        xr[j][q] = __builtin_nontemporal_load((const u32x4_t*)(xb + (row0 + j) * C + 8 * p + qstride * q));
+  }
 
   for (int k = tid; k < m * 128; k += CW_THREADS) {
     ((float4*)lds_w)[k] = ((const float4*)w_lat)[k];
@@ -112,66 +127,54 @@ __global__ __launch_bounds__(CW_THREADS) void cache_write_kernel(
   }
   __syncthreads();
 
-  float acc[32];                                    // acc[8q + c] = channel qstride*q + 8p + c
-  if (valid) {
-    const int64_t b = e / E, i = e - b * E;
-    const int64_t row0 = b * T + i * (int64_t)m;
-    const uint16_t* xb = latent ? x_lat : x_idx;
-    const float* wb = latent ? lds_w : lds_w + m * 512;
+  // One 8-channel group q at a time (channels qstride*q + 8p .. +7): merge
+  // the m rows, take the block maximum across the lanes of the block, pack.
+  // Working group by group keeps few values live, so more waves fit a SIMD.
+  const float* wb = latent ? lds_w : lds_w + m * 512;
 #pragma unroll
-    for (int j = 0; j < m; ++j) {
-      const uint16_t* src = xb + (row0 + j) * C + 8 * p;
-      u32x4_t xv[4];
+  for (int q = 0; q < 4; ++q) {
+    float acc[8];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) xv[q] = __builtin_nontemporal_load((const u32x4_t*)(src + qstride * q));
+    for (int c = 0; c < 8; ++c) acc[c] = 0.0f;
+    if (valid) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
+      for (int j = 0; j < m; ++j) {
+        const u32x4_t xv = M > 0 ? xr[j < MR ? j : 0][q]
+                                 : __builtin_nontemporal_load((const u32x4_t*)(xb + (row0 + j) * C + 8 * p + qstride * q));
         const float4* wp = (const float4*)(wb + (int64_t)j * C + qstride * q + 8 * p);
         const float4 wa = wp[0], wc = wp[1];
         const float wv[8] = {wa.x, wa.y, wa.z, wa.w, wc.x, wc.y, wc.z, wc.w};
 #pragma unroll
         for (int h = 0; h < 4; ++h) {
-          const uint32_t d = xv[q][h];
+          const uint32_t d = xv[h];
           const float x0 = bf16_to_f32(d & 0xFFFFu), x1 = bf16_to_f32(d >> 16);
           if (j == 0) {
-            acc[8 * q + 2 * h] = wv[2 * h] * x0;
-            acc[8 * q + 2 * h + 1] = wv[2 * h + 1] * x1;
+            acc[2 * h] = wv[2 * h] * x0;
+            acc[2 * h + 1] = wv[2 * h + 1] * x1;
           } else {
-            acc[8 * q + 2 * h] = acc[8 * q + 2 * h] + wv[2 * h] * x0;
-            acc[8 * q + 2 * h + 1] = acc[8 * q + 2 * h + 1] + wv[2 * h + 1] * x1;
+            acc[2 * h] = acc[2 * h] + wv[2 * h] * x0;
+            acc[2 * h + 1] = acc[2 * h + 1] + wv[2 * h + 1] * x1;
           }
         }
       }
     }
-  } else {
-#pragma unroll
-    for (int c = 0; c < 32; ++c) acc[c] = 0.0f;
-  }
-
-  // per 8-channel group: the lane's amax, combined over the lanes of its block
-  uint32_t amax_bits[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
+    // the lane's amax, combined over the lanes of its block (max is exact, so
+    // the result does not depend on the split)
     float a = 0.0f;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) a = fmaxf(a, fabsf(acc[8 * q + c]));
+    for (int c = 0; c < 8; ++c) a = fmaxf(a, fabsf(acc[c]));
     uint32_t ab = __float_as_uint(a);                 // a >= 0: the bits order like the values
     ab = max(ab, (uint32_t)__builtin_amdgcn_update_dpp((int)ab, (int)ab, 0xB1, 0xf, 0xf, false));   // lane ^ 1
     if (!latent) ab = max(ab, (uint32_t)__builtin_amdgcn_update_dpp((int)ab, (int)ab, 0x4E, 0xf, 0xf, false));   // lane ^ 2
-    amax_bits[q] = ab;
-  }
-
-  if (latent) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float amax = __uint_as_float(amax_bits[q]);
+    const float amax = __uint_as_float(ab);
+    if (latent) {
       float s;
       const uint32_t sb = e4m3fn_rne(amax / 6.0f, &s);
       Thresholds th(s);
       uint32_t word = 0;
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
-        const float x = acc[8 * q + c];
+        const float x = acc[c];
         const uint32_t code = th.mag(fabsf(x)) | ((__float_as_uint(x) >> 28) & 8u);
         word |= code << (4 * c);
       }
@@ -180,11 +183,7 @@ __global__ __launch_bounds__(CW_THREADS) void cache_write_kernel(
         *(uint32_t*)(kv + e * 288 + 64 * q + 4 * p) = word;
         if ((p & 1) == 0) ((uint8_t*)&lds_scale[el][0])[8 * q + (p >> 1)] = (uint8_t)sb;
       }
-    }
-  } else {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float amax = __uint_as_float(amax_bits[q]);
+    } else {
       uint32_t xbyte = 0;
       float s = 0.0f;
       if (amax > 0.0f) {
@@ -198,7 +197,7 @@ __global__ __launch_bounds__(CW_THREADS) void cache_write_kernel(
       uint32_t word = 0;
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
-        const float x = acc[8 * q + c];
+        const float x = acc[c];
         const uint32_t code = th.mag(fabsf(x)) | ((__float_as_uint(x) >> 28) & 8u);
         word |= code << (4 * c);
       }
