@@ -181,7 +181,12 @@ int csa2_sparse_attention(const uint8_t* kv, const int64_t* entry_offset, const 
  *                      -> attention
  *   mode CSA2_REUSE:   topk (in) -> attention; q_idx, w, pool unused
  * Arguments mean what they mean in csa2_indexer_topk and csa2_sparse_attention.
- * workspace: csa2_decode_workspace_bytes(B, max_n, H, k, pool_k) bytes.
+ * workspace: csa2_decode_workspace_bytes(B, max_n, H, k, pool_k) bytes. In
+ * CSA2_FULL mode with pool_k == 0, k <= 512 and max_n > 16384 the top-k is
+ * finished inside the attention launch (topk is still written); the workspace
+ * then also holds scratch rows for every attention workgroup (about
+ * 12 * max_n bytes each), unless those would exceed 4 GiB, in which case the
+ * top-k finish runs as a launch of its own.
  */
 size_t csa2_decode_workspace_bytes(int B, int64_t max_n, int H, int k, int pool_k);
 int csa2_decode_layer(int mode,

@@ -124,12 +124,7 @@ int check_attention_args(const uint8_t* kv, const int64_t* entry_offset, const i
   return CSA2_OK;
 }
 
-// Runs the indexer with validated arguments on a validated workspace.
-int run_indexer(const uint8_t* ik, const uint8_t* iks, const int64_t* entry_offset,
-                const int32_t* n_entries, int B, int64_t max_n, const uint16_t* q_idx, const float* w,
-                int Hi, int score_mode, const int32_t* cand, int cand_stride, int k, int32_t* topk,
-                int pool_k, int32_t* pool, float* scores_out, uint8_t* ws, hipStream_t stream) {
-  const IndexerWs L = indexer_layout(B, max_n, cand ? cand_stride : 0);
+csa2::SelBufs make_selbufs(const IndexerWs& L, uint8_t* ws) {
   csa2::SelBufs sb;
   sb.ctrl = ws + L.ctrl;
   sb.bitmap = (uint32_t*)(ws + L.bitmap);
@@ -142,20 +137,66 @@ int run_indexer(const uint8_t* ik, const uint8_t* iks, const int64_t* entry_offs
   sb.wgc_stride = L.nblk * csa2::kCandCap;
   sb.gscr = (uint64_t*)(ws + L.gscr);
   sb.gscr_stride = L.gscr_stride;
+  return sb;
+}
+
+// A Full pass's scoring launch, bracketed by the one-shot profiling events
+// when they are set.
+hipError_t score_full(const uint8_t* ik, const uint8_t* iks, const int64_t* entry_offset, const int32_t* n_entries,
+                      int B, int64_t max_n, const uint16_t* q_idx, const float* w, int Hi, int score_mode,
+                      float* scores, int64_t sstride, const csa2::SelBufs& sb, int sel, int K, bool store,
+                      hipStream_t stream) {
+  hipEvent_t ev0 = g_ev_before, ev1 = g_ev_after;
+  g_ev_before = g_ev_after = nullptr;
+  hipError_t r;
+  if (ev0 && (r = hipEventRecord(ev0, stream)) != hipSuccess) return r;
+  r = csa2::launch_score(ik, iks, entry_offset, n_entries, B, max_n, q_idx, w, Hi, score_mode, nullptr, 0,
+                         scores, sstride, sb, sel, K, store, stream);
+  if (r != hipSuccess) return r;
+  if (ev1 && (r = hipEventRecord(ev1, stream)) != hipSuccess) return r;
+  return hipSuccess;
+}
+
+// A Full decode layer with a direct top-k (k <= kDirectMaxK, no pool, more
+// entries than the small path takes) runs the top-k finish inside the
+// attention: one scoring launch, then one attention launch. Every attention
+// workgroup gets scratch rows of its own for the finish's fallback; the plan
+// is off when they would exceed 4 GiB.
+struct FusedPlan {
+  bool on;
+  int64_t sstride, gstride;   // floats / composites per workgroup row
+  size_t bytes;
+};
+
+FusedPlan fused_plan(int B, int64_t max_n, int H, int k, int pool_k) {
+  FusedPlan f{false, 0, 0, 0};
+  if (pool_k != 0 || k > csa2::kDirectMaxK || max_n <= csa2::kSmallMax) return f;
+  const size_t G = (size_t)csa2::attention_workgroups(B, H, k);
+  f.sstride = (int64_t)round_up((size_t)max_n, 64);
+  f.gstride = (int64_t)round_up((size_t)(max_n > csa2::kFinLdsCands ? max_n : csa2::kFinLdsCands), 32);
+  f.bytes = round_up(G * (size_t)f.sstride * 4, 256) + round_up(G * (size_t)f.gstride * 8, 256);
+  f.on = f.bytes <= ((size_t)1 << 32);
+  if (!f.on) f.bytes = 0;
+  return f;
+}
+
+// Runs the indexer with validated arguments on a validated workspace.
+int run_indexer(const uint8_t* ik, const uint8_t* iks, const int64_t* entry_offset,
+                const int32_t* n_entries, int B, int64_t max_n, const uint16_t* q_idx, const float* w,
+                int Hi, int score_mode, const int32_t* cand, int cand_stride, int k, int32_t* topk,
+                int pool_k, int32_t* pool, float* scores_out, uint8_t* ws, hipStream_t stream) {
+  const IndexerWs L = indexer_layout(B, max_n, cand ? cand_stride : 0);
+  const csa2::SelBufs sb = make_selbufs(L, ws);
   uint64_t* cbuf = (uint64_t*)(ws + L.cand);
   float* scores = scores_out ? scores_out : (float*)(ws + L.scores);
   const int64_t sstride = scores_out ? (cand ? cand_stride : max_n) : L.slots;
   hipError_t e;
-  hipEvent_t ev0 = g_ev_before, ev1 = g_ev_after;
-  if (!cand) g_ev_before = g_ev_after = nullptr;
   auto score = [&](int sel, int K) -> hipError_t {
-    hipError_t r;
-    if (!cand && ev0 && (r = hipEventRecord(ev0, stream)) != hipSuccess) return r;
-    r = csa2::launch_score(ik, iks, entry_offset, n_entries, B, max_n, q_idx, w, Hi, score_mode, cand,
-                           cand_stride, scores, sstride, sb, sel, K, scores_out != nullptr, stream);
-    if (r != hipSuccess) return r;
-    if (!cand && ev1 && (r = hipEventRecord(ev1, stream)) != hipSuccess) return r;
-    return hipSuccess;
+    if (!cand)
+      return score_full(ik, iks, entry_offset, n_entries, B, max_n, q_idx, w, Hi, score_mode, scores, sstride, sb,
+                        sel, K, scores_out != nullptr, stream);
+    return csa2::launch_score(ik, iks, entry_offset, n_entries, B, max_n, q_idx, w, Hi, score_mode, cand,
+                              cand_stride, scores, sstride, sb, sel, K, scores_out != nullptr, stream);
   };
   if (cand) {
     // Reindex: score the listed positions, select k among them
@@ -257,14 +298,14 @@ int csa2_sparse_attention(const uint8_t* kv, const int64_t* entry_offset, const 
   if (!aligned16(workspace)) return fail(CSA2_ERR_ALIGN, "attention: workspace must be 16-byte aligned");
   const int S = csa2::attention_splits(B, H, k);
   hipError_t e = csa2::launch_attention(kv, entry_offset, n_entries, idx, k, q, B, H, softmax_scale, S, out, lse,
-                                        (float*)((uint8_t*)workspace + ctrl_bytes()), (hipStream_t)stream);
+                                        (float*)((uint8_t*)workspace + ctrl_bytes()), nullptr, (hipStream_t)stream);
   return hip_status(e, "attention");
 }
 
 size_t csa2_decode_workspace_bytes(int B, int64_t max_n, int H, int k, int pool_k) {
   if (B < 1 || B > CSA2_MAX_BATCH || max_n < 0 || H < 1 || H > CSA2_MAX_HEADS || k < 1 || pool_k < 0) return 0;
   const size_t a = indexer_layout(B, max_n, pool_k).total;
-  return a + attention_scratch(B, H, k);
+  return a + attention_scratch(B, H, k) + fused_plan(B, max_n, H, k, pool_k).bytes;
 }
 
 int csa2_decode_layer(int mode, const uint8_t* kv, const uint8_t* ik, const uint8_t* iks,
@@ -287,12 +328,37 @@ int csa2_decode_layer(int mode, const uint8_t* kv, const uint8_t* ik, const uint
   }
   if (rc) return rc;
   const size_t need_idx = indexer_layout(B, max_n, pool_k).total;
-  const size_t need = need_idx + attention_scratch(B, H, k);
+  const size_t need_att = attention_scratch(B, H, k);
+  const FusedPlan fp = fused_plan(B, max_n, H, k, pool_k);
+  const size_t need = need_idx + need_att + fp.bytes;
   if (!workspace || ws_bytes < need)
     return fail(CSA2_ERR_WORKSPACE, "decode_layer: workspace needs %zu bytes (got %zu)", need, workspace ? ws_bytes : 0);
   if (!aligned16(workspace)) return fail(CSA2_ERR_ALIGN, "decode_layer: workspace must be 16-byte aligned");
   uint8_t* ws = (uint8_t*)workspace;
   hipStream_t s = (hipStream_t)stream;
+  const int S = csa2::attention_splits(B, H, k);
+  if (mode == CSA2_FULL && fp.on) {
+    // scoring launch, then the attention that runs the top-k finish itself
+    const IndexerWs L = indexer_layout(B, max_n, 0);
+    const csa2::SelBufs sb = make_selbufs(L, ws);
+    hipError_t e = score_full(ik, iks, entry_offset, n_entries, B, max_n, q_idx, w, Hi, score_mode,
+                              (float*)(ws + L.scores), L.slots, sb, csa2::SEL_DIRECT, k, false, s);
+    if (e != hipSuccess) return hip_status(e, "decode_layer score");
+    uint8_t* fb = ws + need_idx + need_att;
+    const size_t G = (size_t)csa2::attention_workgroups(B, H, k);
+    csa2::FusedFinish ff;
+    ff.sb = sb;
+    ff.src = csa2::ScoreSrc{ik, iks, entry_offset, q_idx, w, Hi, score_mode};
+    ff.max_n = max_n;
+    ff.scores = (float*)fb;
+    ff.scores_stride = fp.sstride;
+    ff.gscr = (uint64_t*)(fb + round_up(G * (size_t)fp.sstride * 4, 256));
+    ff.gscr_stride = fp.gstride;
+    ff.topk = topk;
+    e = csa2::launch_attention(kv, entry_offset, n_entries, topk, k, q, B, H, softmax_scale, S, out, lse,
+                               (float*)(ws + need_idx), &ff, s);
+    return hip_status(e, "decode_layer attention");
+  }
   if (mode == CSA2_FULL) {
     rc = run_indexer(ik, iks, entry_offset, n_entries, B, max_n, q_idx, w, Hi, score_mode, nullptr, 0, k, topk,
                      pool_k, pool, nullptr, ws, s);
@@ -301,9 +367,8 @@ int csa2_decode_layer(int mode, const uint8_t* kv, const uint8_t* ik, const uint
                      nullptr, nullptr, ws, s);
   }
   if (rc) return rc;
-  const int S = csa2::attention_splits(B, H, k);
   hipError_t e = csa2::launch_attention(kv, entry_offset, n_entries, topk, k, q, B, H, softmax_scale, S, out, lse,
-                                        (float*)(ws + need_idx), s);
+                                        (float*)(ws + need_idx), nullptr, s);
   return hip_status(e, "decode_layer attention");
 }
 

@@ -48,6 +48,7 @@
 // kernel combines.
 #include "device.h"
 #include "kernels.h"
+#include "select_dev.h"
 #include <math.h>
 #include <atomic>
 
@@ -99,11 +100,16 @@ struct QuarterRow {
   u32x2_t sw;
 };
 
+// FIN: the workgroup first runs the direct top-k finish of its sequence (the
+// finish's LDS is carved from the tile slots, the weight buffer and the index
+// list, all free until the rounds start) and takes its split of the result;
+// idx is then not read.
+template <bool FIN>
 __global__ __launch_bounds__(AT_THREADS) void attention_kernel(
     const uint8_t* __restrict__ kv, const int64_t* __restrict__ entry_offset,
     const int32_t* __restrict__ n_entries, const int32_t* __restrict__ idx, int k,
     const uint16_t* __restrict__ q, int B, int H, float tau, int S,
-    float* __restrict__ out, float* __restrict__ lse, float* __restrict__ part) {
+    float* __restrict__ out, float* __restrict__ lse, float* __restrict__ part, FusedFinish ff) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];   // tile slots; the queries in set 1 first
   __shared__ float4 pbuf[2][AT_PROD][64];      // softmax weights of each slot, lane layout of the producer
   __shared__ float mref[2][AT_PROD][16];       // producer reference maximum per head
@@ -152,10 +158,32 @@ __global__ __launch_bounds__(AT_THREADS) void attention_kernel(
     raw[1] = *(const u32x4_t*)(src + 8);
   }
   int32_t iv[AT_MAX_CHUNK / AT_THREADS];
+  if (FIN) {
+    // the finish, while the queries are in flight: positions of this split go
+    // to sidx, the first workgroup of the sequence writes all k of them
+    static_assert(AT_MAX_CHUNK >= FIN_MAX_WG && AT_LDS >= 8 * (FIN_LDS_CANDS + FIN_SUB_CAP) &&
+                  sizeof(pbuf) >= 4608, "the finish's LDS fits the attention's");
+    uint8_t* pb8 = (uint8_t*)&pbuf[0][0][0];
+    const FinLds fl{(uint64_t*)smem, (uint64_t*)(smem + 8 * FIN_LDS_CANDS), (uint32_t*)sidx,
+                    (uint32_t*)(pb8 + 512), (uint64_t*)pb8, (uint32_t*)(pb8 + 256), (uint32_t*)(pb8 + 384),
+                    (uint64_t*)(pb8 + 2560), (uint32_t*)(pb8 + 416)};
+    const bool writer = hg == 0 && s == 0;
+    int32_t* tk = ff.topk + (int64_t)b * k;
+    finish_direct_body<AT_THREADS>(b, n_entries, ff.max_n, ff.scores + (int64_t)lin * ff.scores_stride,
+                                   ff.gscr + (int64_t)lin * ff.gscr_stride, ff.sb, k, ff.src, 1, fl,
+                                   [&](int j, int32_t v) {
+                                     if (writer) tk[j] = v;
+                                     const int jj = j - e_lo;
+                                     if (jj >= 0 && jj < nent) sidx[jj] = (v >= 0 && v < nb) ? v : -1;
+                                   });
+    for (int i = nent + tid; i < 16 * ntiles; i += AT_THREADS) sidx[i] = -1;
+    __syncthreads();
+  } else {
 #pragma unroll
-  for (int c = 0; c < AT_MAX_CHUNK / AT_THREADS; ++c) {
-    const int i = tid + c * AT_THREADS;
-    iv[c] = i < nent ? ib[i] : -1;
+    for (int c = 0; c < AT_MAX_CHUNK / AT_THREADS; ++c) {
+      const int i = tid + c * AT_THREADS;
+      iv[c] = i < nent ? ib[i] : -1;
+    }
   }
   // a producer lane's row of tile t (clamped to the last tile; skipped entries
   // read row 0 of the sequence)
@@ -179,16 +207,18 @@ __global__ __launch_bounds__(AT_THREADS) void attention_kernel(
     // never used)
     const int t0 = max(min(pw, ntiles - 1), 0), t1 = max(min(pw + AT_PROD, ntiles - 1), 0);
     const int e0 = 16 * t0 + r, e1 = 16 * t1 + r;
-    const int p0 = e0 < nent ? ib[e0] : -1;
-    const int p1 = e1 < nent ? ib[e1] : -1;
+    const int p0 = e0 < nent ? (FIN ? sidx[e0] : ib[e0]) : -1;
+    const int p1 = e1 < nent ? (FIN ? sidx[e1] : ib[e1]) : -1;
     const uint8_t* const qrow = (const uint8_t*)q;
     load_quarter(bufA, any_rows ? row_of(p0) : qrow);
     load_quarter(bufB, any_rows ? row_of(p1) : qrow);
   }
+  if (!FIN) {
 #pragma unroll
-  for (int c = 0; c < AT_MAX_CHUNK / AT_THREADS; ++c) {
-    const int i = tid + c * AT_THREADS;
-    if (i < 16 * ntiles) sidx[i] = (iv[c] >= 0 && iv[c] < nb) ? iv[c] : -1;
+    for (int c = 0; c < AT_MAX_CHUNK / AT_THREADS; ++c) {
+      const int i = tid + c * AT_THREADS;
+      if (i < 16 * ntiles) sidx[i] = (iv[c] >= 0 && iv[c] < nb) ? iv[c] : -1;
+    }
   }
 
   // --- queries to fp16 in LDS (slot set 1, first written in round 1). Each
@@ -452,11 +482,14 @@ int attention_splits(int B, int H, int k) {
   return S;
 }
 
+int attention_workgroups(int B, int H, int k) { return B * ((H + 15) / 16) * attention_splits(B, H, k); }
+
 size_t attention_lds_bytes() { return AT_LDS; }
 
 hipError_t launch_attention(const uint8_t* kv, const int64_t* entry_offset, const int32_t* n_entries,
                             const int32_t* idx, int k, const uint16_t* q, int B, int H, float tau,
-                            int S, float* out, float* lse, float* part, hipStream_t stream) {
+                            int S, float* out, float* lse, float* part, const FusedFinish* fin,
+                            hipStream_t stream) {
   // the dynamic LDS limit is raised once per device (per-device flags: the
   // attribute belongs to the current device)
   static std::atomic<uint32_t> attr_set[64];
@@ -464,14 +497,21 @@ hipError_t launch_attention(const uint8_t* kv, const int64_t* entry_offset, cons
   hipError_t e0 = hipGetDevice(&dev);
   if (e0 != hipSuccess) return e0;
   if (dev < 0 || dev >= 64 || !attr_set[dev].load(std::memory_order_acquire)) {
-    hipError_t e = hipFuncSetAttribute((const void*)attention_kernel,
+    hipError_t e = hipFuncSetAttribute((const void*)attention_kernel<false>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, AT_LDS);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute((const void*)attention_kernel<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              AT_LDS);
     if (e != hipSuccess) return e;
     if (dev >= 0 && dev < 64) attr_set[dev].store(1u, std::memory_order_release);
   }
   dim3 grid((unsigned)(B * ((H + 15) / 16) * S)), block(AT_THREADS);
-  hipLaunchKernelGGL(attention_kernel, grid, block, AT_LDS, stream, kv, entry_offset, n_entries, idx,
-                     k, q, B, H, tau, S, out, lse, part);
+  if (fin)
+    hipLaunchKernelGGL(attention_kernel<true>, grid, block, AT_LDS, stream, kv, entry_offset, n_entries, idx,
+                       k, q, B, H, tau, S, out, lse, part, *fin);
+  else
+    hipLaunchKernelGGL(attention_kernel<false>, grid, block, AT_LDS, stream, kv, entry_offset, n_entries, idx,
+                       k, q, B, H, tau, S, out, lse, part, FusedFinish{});
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || S == 1) return e;
   hipLaunchKernelGGL(attention_combine_kernel, dim3((unsigned)(B * H)), dim3(128), 0, stream, part, S,

@@ -86,11 +86,30 @@ hipError_t launch_select_small(const float* scores, int64_t sstride, const int32
                                int pstride, int score_by_pos, const int32_t* n_entries, int B,
                                int64_t max_n, int K, int32_t* out, int out_stride, hipStream_t stream);
 
+// A decode attention that derives its indices itself: every workgroup runs the
+// direct top-k finish of its sequence over the lists a direct score pass left
+// (scores not stored), keeps its split of the result in LDS, and the first
+// workgroup of each sequence writes the top-k to `topk`. scores / gscr give
+// every attention workgroup rows of its own for the finish's fallback.
+struct FusedFinish {
+  SelBufs sb;
+  ScoreSrc src;
+  int64_t max_n;
+  float* scores;          // [workgroups][scores_stride] (>= max_n floats per row)
+  int64_t scores_stride;
+  uint64_t* gscr;         // [workgroups][gscr_stride] (>= max(max_n, kFinLdsCands) per row)
+  int64_t gscr_stride;
+  int32_t* topk;          // [B][k]
+};
+
 // Attention: number of entry splits used for B sequences, H heads, k indices.
 int attention_splits(int B, int H, int k);
+int attention_workgroups(int B, int H, int k);
 size_t attention_lds_bytes();
+// fin: null (indices from idx) or the finish to run first (idx unused).
 hipError_t launch_attention(const uint8_t* kv, const int64_t* entry_offset, const int32_t* n_entries,
                             const int32_t* idx, int k, const uint16_t* q, int B, int H, float tau,
-                            int S, float* out, float* lse, float* part, hipStream_t stream);
+                            int S, float* out, float* lse, float* part, const FusedFinish* fin,
+                            hipStream_t stream);
 
 }  // namespace csa2

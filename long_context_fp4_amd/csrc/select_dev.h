@@ -1,0 +1,587 @@
+// Selection helpers shared by the score pass, the top-k finish and the decode
+// attention that runs the finish itself (device code, gfx950).
+//
+// Keys: a score's order-preserving 32-bit key; a composite (key << 32 |
+// ~position) orders by score descending, then position ascending, so the k
+// largest composites are the top-k of the selection order.
+#pragma once
+#include "device.h"
+#include "kernels.h"
+
+namespace csa2 {
+
+constexpr int SC_CHUNK = kScoreChunk;   // slots per score workgroup (one selection chunk)
+constexpr int CAND_CAP = kCandCap;     // candidates a chunk reports in direct top-k mode
+constexpr int FIN_MAX_WG = kFinMaxWg;        // chunks per sequence whose lists the finish reads
+constexpr int NBINS = 4096;         // histogram over the top 12 bits of the key
+constexpr int BIN_SHIFT = 20;
+constexpr int FIN_LDS_CANDS = kFinLdsCands;  // candidates the direct finish keeps in LDS
+constexpr int FIN_SUB_CAP = 4096;   // keys of the threshold bin the direct finish keeps in LDS
+constexpr int FIN_RANK_MAX = 256;   // threshold bins up to this size are resolved by ranking
+constexpr int FIN_NV = 8;           // candidates per lane the direct finish holds in registers
+
+// LDS the direct finish works in (sizes in elements).
+struct FinLds {
+  uint64_t* lc;          // FIN_LDS_CANDS: the candidate lists, concatenated
+  uint64_t* sub;         // FIN_SUB_CAP: the NBINS-bin histogram, then the keys inside the threshold bin
+  uint32_t* loff;        // FIN_MAX_WG: list offsets of the chunks
+  uint32_t* h;           // 512: radix histograms
+  uint64_t* red;         // 32
+  uint32_t* scan_tmp;    // 32
+  uint32_t* ctl;         // 8
+  uint64_t* binl;        // FIN_RANK_MAX: keys of a small threshold bin
+  uint32_t* bin_count;   // 1
+};
+
+// ---------------------------------------------------------------- block scan
+// Exclusive prefix sum over the workgroup (blockDim.x multiple of 64); returns
+// the total in *total. `tmp` holds at least blockDim.x/64 + 1 words of LDS.
+__device__ inline uint32_t block_exclusive_scan(uint32_t v, uint32_t* tmp, uint32_t* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const uint32_t x = wave_incl_sum(v);
+  if (lane == 63) tmp[wave] = x;
+  __syncthreads();
+  // the wave totals, scanned across lanes 0 .. nw-1 of every wave
+  const uint32_t t = lane < nw ? tmp[lane] : 0u;
+  const uint32_t ti = wave_incl_sum(t);
+  const uint32_t pre = readlane_u32(ti - t, wave);
+  *total = readlane_u32(ti, nw - 1);
+  __syncthreads();
+  return pre + x - v;
+}
+
+// ---------------------------------------------------------------- scoring helpers
+__device__ __forceinline__ bf16x8_t dequant_mx_block8(uint32_t dw, float scale) {
+  bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, scale, 0);
+  bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, scale, 1);
+  bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, scale, 2);
+  bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, scale, 3);
+  return bf16x8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// Sum of v over the four lanes l, l^16, l^32, l^48 (VALU lane swaps, no LDS).
+__device__ __forceinline__ float sum_lane_groups(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const float t = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  const auto r2 = __builtin_amdgcn_permlane16_swap(__float_as_uint(t), __float_as_uint(t), false, false);
+  return __uint_as_float(r2[0]) + __uint_as_float(r2[1]);
+}
+
+// ---------------------------------------------------------------- radix select
+// Run by the 64 lanes of wave 0: among the 256 digit counts h (digit 255 is the
+// best), finds the digit that holds the need-th best element (1 <= need <= the
+// sum of h): ctl[0] = digit, ctl[1] = count strictly above it, ctl[2] = count
+// with it. Lane l scans digits 255-4l .. 252-4l.
+__device__ __forceinline__ void digit_kth(const uint32_t* h, uint32_t need, uint32_t* ctl) {
+  const int l = threadIdx.x & 63;
+  uint32_t c4[4], loc = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) { c4[q] = h[255 - 4 * l - q]; loc += c4[q]; }
+  const uint32_t pre = wave_incl_sum(loc) - loc;
+  if (pre < need && pre + loc >= need) {
+    uint32_t cum = pre;
+    for (int q = 0; q < 4; ++q) {
+      if (cum + c4[q] >= need) {
+        ctl[0] = 255 - 4 * l - q;
+        ctl[1] = cum;
+        ctl[2] = c4[q];
+        break;
+      }
+      cum += c4[q];
+    }
+  }
+}
+
+// Among n distinct 64-bit composites at `v` (LDS, or global memory read after
+// an acquire fence), find the `need` largest (0 < need < n); all composites
+// agree on the bits above top_shift + 7. On return the composites c with
+// (c & *mask_out) >= *prefix_out are exactly the `need` largest. h holds 512
+// words and ctl 8 words of LDS. All threads of the workgroup must call it.
+__device__ inline void radix_select_u64(const uint64_t* v, uint32_t n, uint32_t need, int top_shift,
+                                 uint32_t* h, uint32_t* ctl, uint64_t* prefix_out, uint64_t* mask_out) {
+  // h: two 256-bin histograms and ctl: two 4-word results, alternating by pass,
+  // so each pass needs two barriers
+  uint64_t prefix = 0, pmask = 0;
+  int shift = top_shift;
+  for (int i = threadIdx.x; i < 256; i += blockDim.x) h[i] = 0;
+  __syncthreads();
+  for (int p = 0;; p ^= 1) {
+    uint32_t* hp = h + 256 * p;
+    for (uint32_t i = threadIdx.x; i < n; i += blockDim.x) {
+      const uint64_t c = v[i];
+      if ((c & pmask) == prefix) atomicAdd(&hp[(uint32_t)(c >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (threadIdx.x < 64) digit_kth(hp, need, ctl + 4 * p);
+    for (int i = threadIdx.x; i < 256; i += blockDim.x) h[256 * (p ^ 1) + i] = 0;
+    __syncthreads();
+    const uint32_t d = ctl[4 * p], above = ctl[4 * p + 1], cnt = ctl[4 * p + 2];
+    prefix |= (uint64_t)d << shift;
+    pmask |= (uint64_t)255 << shift;
+    need -= above;
+    if (cnt == need || shift == 0) break;
+    shift = shift >= 8 ? shift - 8 : 0;     // the last digit may overlap resolved bits
+  }
+  *prefix_out = prefix;
+  *mask_out = pmask;
+}
+
+// Index in an LDS list for the lanes whose `take` is set: one LDS atomic per wave.
+__device__ __forceinline__ uint32_t wave_append(bool take, uint32_t* counter) {
+  const uint64_t m = __ballot(take);
+  const int lane = threadIdx.x & 63;
+  uint32_t base = 0;
+  if (m) {
+    const int leader = __ffsll((long long)m) - 1;
+    if (lane == leader) base = atomicAdd(counter, (uint32_t)__popcll(m));
+    base = readlane_u32(base, leader);
+  }
+  return base + (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
+}
+
+// Top shift for radix_select_u64 over n composites at v: the 8-bit digit that
+// holds the highest bit in which any two composites differ (bits above it are
+// common to all of them). All threads of the workgroup must call it.
+__device__ inline int radix_top_shift(const uint64_t* v, uint32_t n, uint64_t* red) {
+  uint64_t o = 0, a = ~0ull;
+  for (uint32_t i = threadIdx.x; i < n; i += blockDim.x) { o |= v[i]; a &= v[i]; }
+  o = ((uint64_t)wave_or_u32((uint32_t)(o >> 32)) << 32) | wave_or_u32((uint32_t)o);
+  a = ((uint64_t)wave_and_u32((uint32_t)(a >> 32)) << 32) | wave_and_u32((uint32_t)a);
+  const int nw = blockDim.x >> 6, lane = threadIdx.x & 63;   // at most 16 waves; red holds 32 words
+  if (lane == 0) { red[threadIdx.x >> 6] = o; red[16 + (threadIdx.x >> 6)] = a; }
+  __syncthreads();
+  o = lane < nw ? red[lane] : 0ull;
+  a = lane < nw ? red[16 + lane] : ~0ull;
+  __syncthreads();
+  o = ((uint64_t)wave_or_u32((uint32_t)(o >> 32)) << 32) | wave_or_u32((uint32_t)o);
+  a = ((uint64_t)wave_and_u32((uint32_t)(a >> 32)) << 32) | wave_and_u32((uint32_t)a);
+  const uint64_t diff = o ^ a;
+  if (diff == 0) return 0;
+  const int hb = 63 - __clzll(diff);
+  return hb >= 7 ? hb - 7 : 0;
+}
+
+__device__ __forceinline__ uint64_t composite(uint32_t key, uint32_t pos) {
+  return ((uint64_t)key << 32) | (uint64_t)(0xFFFFFFFFu - pos);
+}
+
+// Block-wide max / or of one value per thread; tmp holds blockDim.x/64 words of LDS.
+__device__ inline uint32_t block_max_u32(uint32_t v, uint32_t* tmp) {
+  const int lane = threadIdx.x & 63;
+  v = wave_max_u32(v);
+  if (lane == 0) tmp[threadIdx.x >> 6] = v;
+  __syncthreads();
+  const uint32_t r = wave_max_u32(lane < (int)(blockDim.x >> 6) ? tmp[lane] : 0u);
+  __syncthreads();
+  return r;
+}
+// Both at once (one barrier pair); tmp holds 32 words.
+__device__ inline void block_max_or_u32(uint32_t* mx, uint32_t* ov, uint32_t* tmp) {
+  const int lane = threadIdx.x & 63, nw = blockDim.x >> 6;
+  const uint32_t m = wave_max_u32(*mx), o = wave_or_u32(*ov);
+  if (lane == 0) { tmp[threadIdx.x >> 6] = m; tmp[16 + (threadIdx.x >> 6)] = o; }
+  __syncthreads();
+  *mx = wave_max_u32(lane < nw ? tmp[lane] : 0u);
+  *ov = wave_or_u32(lane < nw ? tmp[16 + lane] : 0u);
+  __syncthreads();
+}
+__device__ inline uint32_t block_or_u32(uint32_t v, uint32_t* tmp) {
+  const int lane = threadIdx.x & 63;
+  v = wave_or_u32(v);
+  if (lane == 0) tmp[threadIdx.x >> 6] = v;
+  __syncthreads();
+  const uint32_t r = wave_or_u32(lane < (int)(blockDim.x >> 6) ? tmp[lane] : 0u);
+  __syncthreads();
+  return r;
+}
+
+// Bin holding the `need`-th best key of an LDS histogram (with BPT = NBINS /
+// THREADS, thread t owns bins NBINS-1-BPT*t .. NBINS-BPT-BPT*t). Returns the number of keys counted in *total,
+// the bin in ctl[0] and the count strictly above it in ctl[1] (ctl[0] = -1
+// when total < need). All threads must call it.
+// PACKED: two 16-bit counts per word (bin b in the half b & 1 of word b / 2).
+template <int THREADS, bool PACKED = false>
+__device__ inline void hist_kth_bin(const uint32_t* lhist, uint32_t need, uint32_t* scan_tmp, uint32_t* ctl,
+                             uint32_t* total_out) {
+  constexpr int BPT = NBINS / THREADS;
+  uint32_t hv[BPT], local = 0;
+#pragma unroll
+  for (int q = 0; q < BPT; ++q) {
+    const int bin = NBINS - 1 - (BPT * threadIdx.x + q);
+    hv[q] = PACKED ? (lhist[bin >> 1] >> ((bin & 1) * 16)) & 0xFFFFu : lhist[bin];
+    local += hv[q];
+  }
+  if (threadIdx.x == 0) { ctl[0] = 0xFFFFFFFFu; ctl[1] = 0; }
+  uint32_t total;
+  const uint32_t prefix = block_exclusive_scan(local, scan_tmp, &total);
+  if (prefix < need && prefix + local >= need) {
+    // the first of this thread's bins where the running count reaches `need`
+    // (selects, not a loop with a break: no nest of saved execution masks)
+    uint32_t cum = prefix, qf = BPT, cum_at = 0;
+#pragma unroll
+    for (int q = 0; q < BPT; ++q) {
+      const bool hit = qf == BPT && cum + hv[q] >= need;
+      qf = hit ? (uint32_t)q : qf;
+      cum_at = hit ? cum : cum_at;
+      cum += hv[q];
+    }
+    ctl[0] = NBINS - 1 - (BPT * threadIdx.x + qf);
+    ctl[1] = cum_at;
+  }
+  __syncthreads();
+  *total_out = total;
+}
+
+// One tile of 16 slots x 16 heads: 4 MFMAs over the 128 channels (lane (n, g):
+// slot n, channels 32g .. 32g+31); MODE 1 applies w_h * ReLU and sums the heads
+// into the lanes of group 0. The score pass and the finish's recompute share
+// it, so both give the same float32 scores.
+template <int MODE>
+__device__ __forceinline__ float score_tile_fn(const bf16x8_t (&qa)[4], const u32x4_t cw, uint32_t sbyte,
+                                               const float* lw, int g) {
+  const float scl = __uint_as_float(sbyte << 23);
+  f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    bf16x8_t kb = dequant_mx_block8(cw[j], scl);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[j], kb, acc, 0, 0, 0);
+  }
+  if (MODE == 0) return acc[0];          // head 0 is row 0, held by lanes 0..15
+  const float4 wr = *(const float4*)&lw[4 * g];
+  const float sc = wr.x * fmaxf(acc[0], 0.0f) + wr.y * fmaxf(acc[1], 0.0f) +
+                   wr.z * fmaxf(acc[2], 0.0f) + wr.w * fmaxf(acc[3], 0.0f);
+  return sum_lane_groups(sc);
+}
+
+// Ordered compaction over elements [0, n): pred(i) selects, emit(i, slot)
+// receives the element's place among the selected ones. Every wave owns a
+// contiguous range (a multiple of 64 elements) and ranks inside it with
+// ballots, so only one exchange of wave totals is needed. Returns the number
+// selected. All threads of the workgroup must call it.
+// Exclusive prefix over the waves of a wave-uniform count; the sum in *total.
+// tmp holds blockDim.x / 64 words of LDS. All threads must call it.
+__device__ inline uint32_t wave_count_prefix(uint32_t cnt, uint32_t* tmp, uint32_t* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  if (lane == 0) tmp[wave] = cnt;
+  __syncthreads();
+  const uint32_t t = lane < nw ? tmp[lane] : 0u;
+  const uint32_t ti = wave_incl_sum(t);
+  const uint32_t base = readlane_u32(ti - t, wave);
+  *total = readlane_u32(ti, nw - 1);
+  __syncthreads();
+  return base;
+}
+
+template <typename Pred, typename Emit>
+__device__ inline uint32_t ordered_compact(uint32_t n, Pred pred, Emit emit, uint32_t* tmp) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const uint32_t span = (n + 64 * nw - 1) / (64 * nw) * 64;
+  const uint32_t lo = min((uint32_t)wave * span, n), hi = min(lo + span, n);
+  uint32_t cnt = 0;
+  for (uint32_t i0 = lo; i0 < hi; i0 += 64) {
+    const uint32_t i = i0 + lane;
+    cnt += (uint32_t)__popcll(__ballot(i < hi && pred(i)));
+  }
+  uint32_t total;
+  uint32_t base = wave_count_prefix(cnt, tmp, &total);
+  for (uint32_t i0 = lo; i0 < hi; i0 += 64) {
+    const uint32_t i = i0 + lane;
+    const bool p = i < hi && pred(i);
+    const uint64_t m = __ballot(p);
+    if (p) emit(i, base + (uint32_t)__popcll(m & ((1ull << lane) - 1ull)));
+    base += (uint32_t)__popcll(m);
+  }
+  return total;
+}
+
+// Direct top-K (K <= kDirectMaxK). The candidate lists hold, per workgroup,
+// every key whose top 20 bits reach its refined cutoff, in position order, so
+// their concatenation in workgroup order is in position order too; the ones
+// at or above the highest cutoff are every key of the sequence there. While
+// the lists are copied to LDS, their 20-bit prefixes (relative to that cutoff,
+// the last bin holding everything 4095 or more above it) are histogrammed; the
+// bin of the K-th best prefix follows, all keys above it are selected, and the
+// few inside it are chosen on the full (key, position) composite: by ranking
+// when the bin is small, else by radix select. An ordered compaction of the
+// concatenated lists then writes the K positions in ascending order. When a
+// list overflowed, the lists exceed LDS or fewer than K keys reach the highest
+// cutoff, the same steps run on a histogram of every score of the sequence.
+//
+// Run by the NT threads of one workgroup for sequence b. The output goes
+// through emit(j, position) for every j in [0, K) exactly once (-1 past the
+// selected ones). sall: a row of at least max_n floats for the fallback's
+// scores (recomputed into it when `rescore` is set); gscr: this workgroup's
+// scratch for a threshold bin beyond FIN_SUB_CAP keys.
+template <int NT, typename Emit>
+__device__ inline void finish_direct_body(int b, const int32_t* __restrict__ n_entries, int64_t max_n,
+                                   float* __restrict__ sall, uint64_t* __restrict__ gscr, const SelBufs& sb,
+                                   int K, const ScoreSrc& src, int rescore, const FinLds& L, Emit emit) {
+  uint64_t* const lc = L.lc;
+  uint64_t* const sub = L.sub;
+  uint32_t* const loff = L.loff;
+  uint32_t* const h = L.h;
+  uint64_t* const red = L.red;
+  uint32_t* const scan_tmp = L.scan_tmp;
+  uint32_t* const ctl = L.ctl;
+  uint64_t* const binl = L.binl;
+  uint32_t& bin_count = *L.bin_count;
+  uint32_t* hist = (uint32_t*)sub;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  constexpr int NWAVE = NT / 64;
+  static_assert(NBINS % NT == 0 && NT % 64 == 0, "whole waves, whole bins per thread");
+  if (tid == 0) bin_count = 0;                     // first read after several barriers
+  // the first header words, and the first 128 candidates of the four lists
+  // this wave copies first (workgroups wave, wave + NWAVE, ...), are requested
+  // before the sequence length and the list lengths are known
+  const int64_t nw_max = (max_n + SC_CHUNK - 1) / SC_CHUNK;
+  const uint64_t* hd = sb.hdr + (int64_t)b * sb.hdr_stride;
+  const uint64_t h0 = tid < nw_max ? hd[tid] : 0ull;
+  const uint64_t* wc = sb.wgc + (int64_t)b * sb.wgc_stride;
+  const int nbk = (int)(sb.wgc_stride / CAND_CAP);   // list slots per sequence (>= 1)
+  constexpr int FS = 4096 / NT;                     // lists a wave copies per round (64 chunks in one round)
+  uint64_t v0[FS];                                  // the first 64 entries of each (the rest, when longer, later)
+#pragma unroll
+  for (int s = 0; s < FS; ++s) v0[s] = wc[(int64_t)min(wave + s * NWAVE, nbk - 1) * CAND_CAP + lane];
+  // keeps the compiler from sinking these loads below the early return (their
+  // latency then overlaps the sequence-length load)
+  asm volatile("" ::: "memory");
+  const int64_t n_pos = min((int64_t)n_entries[b], max_n);
+  if (n_pos <= K) {                       // every position is selected (or none exists)
+    for (int j = tid; j < K; j += NT) emit(j, j < n_pos ? j : -1);
+    return;
+  }
+  for (int i = tid; i < NBINS; i += NT) hist[i] = 0;
+  const int64_t nw = (n_pos + SC_CHUNK - 1) / SC_CHUNK;
+  bool fast = false;
+  uint32_t total = 0, cmax = 0;
+  if (nw <= FIN_MAX_WG) {
+    // list lengths -> offsets; thread t owns workgroups [w0, w1)
+    const int per = (int)((nw + NT - 1) / NT);
+    const int w0 = (int)min((int64_t)tid * per, nw), w1 = (int)min((int64_t)w0 + per, nw);
+    uint32_t cnt = 0, ovf = 0;
+    for (int w = w0; w < w1; ++w) {
+      const uint64_t hv = (per == 1) ? h0 : hd[w];
+      const uint32_t c = (uint32_t)hv & 0x7FFFFFFFu;
+      ovf |= (uint32_t)hv >> 31;
+      cmax = max(cmax, (uint32_t)(hv >> 32));
+      loff[w] = c;
+      cnt += c;
+    }
+    uint32_t run = block_exclusive_scan(cnt, scan_tmp, &total);
+    for (int w = w0; w < w1; ++w) {
+      const uint32_t c = loff[w];
+      loff[w] = run;
+      run += c;
+    }
+    block_max_or_u32(&cmax, &ovf, scan_tmp);
+    if (ovf == 0 && total <= (uint32_t)FIN_LDS_CANDS) {
+      // copy the lists in workgroup order (wave v takes workgroups v, v + 16, ...,
+      // eight independent loads per lane in flight) and histogram the prefixes
+      auto take = [&](uint64_t c, uint32_t at) {
+        lc[at] = c;
+        const uint32_t p20 = (uint32_t)(c >> 44);
+        if (p20 >= cmax) atomicAdd(&hist[min(p20 - cmax, (uint32_t)NBINS - 1)], 1u);
+      };
+      for (int w0 = wave; w0 < nw; w0 += FS * NWAVE) {
+        uint64_t v[FS];
+        uint32_t cn[FS], of[FS];
+        int ws[FS];
+#pragma unroll
+        for (int s = 0; s < FS; ++s) {
+          ws[s] = min(w0 + s * NWAVE, (int)nw - 1);
+          cn[s] = (w0 + s * NWAVE < nw) ? (ws[s] + 1 < nw ? loff[ws[s] + 1] : total) - loff[ws[s]] : 0u;
+          of[s] = loff[ws[s]];
+          // the first round: already requested
+          v[s] = w0 == wave ? v0[s] : wc[(int64_t)ws[s] * CAND_CAP + lane];
+        }
+#pragma unroll
+        for (int s = 0; s < FS; ++s) {
+          if ((uint32_t)lane < cn[s]) take(v[s], of[s] + lane);
+          for (uint32_t j = 64 + lane; j < cn[s]; j += 64) take(wc[(int64_t)ws[s] * CAND_CAP + j], of[s] + j);
+        }
+      }
+      __syncthreads();
+      uint32_t tot;
+      hist_kth_bin<NT>(hist, (uint32_t)K, scan_tmp, ctl, &tot);
+      fast = ctl[0] != 0xFFFFFFFFu;       // at least K keys reach the highest cutoff
+    }
+  }
+  if (fast) {
+    // Keys above the threshold bin are selected; inside it (20-bit prefixes
+    // lo20 .. hi20) the `need` largest. The candidates are read in lane order
+    // (unit stride, no LDS bank conflicts); an ordered compaction over
+    // wave-owned ranges places the selected positions in ascending order.
+    const uint32_t T = ctl[0], above = ctl[1], in_bin = hist[T];
+    const uint32_t need = (uint32_t)K - above;      // 1 .. in_bin
+    const uint32_t lo20 = cmax + T;
+    const uint32_t hi20 = T == NBINS - 1 ? 0xFFFFFu : cmax + T;
+    auto is_above = [&](uint64_t c) { return (uint32_t)(c >> 44) > hi20; };
+    auto is_in_bin = [&](uint64_t c) {
+      const uint32_t p20 = (uint32_t)(c >> 44);
+      return p20 >= lo20 && p20 <= hi20;
+    };
+    const bool split = need < in_bin;                // else every in-bin key is selected
+    const bool small = in_bin <= (uint32_t)FIN_RANK_MAX;
+    uint64_t prefix = 0, mask = 0;                   // large bins: in-bin keys with (c & mask) >= prefix
+    // Wave v owns the candidates [lo, hi) (a multiple of 64 of them); up to
+    // FIN_NV per lane they are read once, in lane order, into registers.
+    const uint32_t span = (total + NT - 1) / NT * 64;
+    const bool regs = span <= 64u * FIN_NV;
+    const uint32_t lo = min((uint32_t)wave * span, total), hi = min(lo + span, total);
+    uint64_t c[FIN_NV];
+#pragma unroll
+    for (int q = 0; q < FIN_NV; ++q) {
+      const uint32_t i = lo + 64 * q + lane;
+      c[q] = regs && i < hi ? lc[i] : 0ull;
+    }
+    if (split) {
+      uint64_t* dst = binl;
+      if (!small) {
+        __syncthreads();                             // hist reads done before sub is reused
+        dst = in_bin <= (uint32_t)FIN_SUB_CAP ? sub : gscr;
+      }
+      if (regs) {
+#pragma unroll
+        for (int q = 0; q < FIN_NV; ++q) {
+          const bool t = lo + 64 * q + lane < hi && is_in_bin(c[q]);
+          const uint32_t at = wave_append(t, &bin_count);
+          if (t && at < in_bin) dst[at] = c[q];
+        }
+      } else {
+        for (uint32_t i0 = 0; i0 < total; i0 += NT) {
+          const uint32_t i = i0 + tid;
+          const uint64_t cc = i < total ? lc[i] : 0ull;
+          const bool t = i < total && is_in_bin(cc);
+          const uint32_t at = wave_append(t, &bin_count);
+          if (t && at < in_bin) dst[at] = cc;
+        }
+      }
+      if (dst != sub && dst != binl) __threadfence_block();   // this workgroup reads its global copy back
+      __syncthreads();
+      if (!small) {
+        const int top = radix_top_shift(dst, in_bin, red);
+        radix_select_u64(dst, in_bin, need, top, h, ctl, &prefix, &mask);
+      }
+    }
+    // small bins: keys are distinct (they carry the position), so a key is
+    // selected when fewer than `need` keys of the bin are larger
+    auto selected = [&](uint64_t c) {
+      if (is_above(c)) return true;
+      if (!is_in_bin(c)) return false;
+      if (!split) return true;
+      if (!small) return (c & mask) >= prefix;
+      uint32_t larger = 0;
+      for (uint32_t j = 0; j < in_bin; ++j) larger += binl[j] > c ? 1u : 0u;
+      return larger < need;
+    };
+    uint32_t nsel;
+    if (regs) {
+      uint64_t m[FIN_NV];
+      uint32_t cnt = 0;
+#pragma unroll
+      for (int q = 0; q < FIN_NV; ++q) {
+        m[q] = __ballot(lo + 64 * q + lane < hi && selected(c[q]));
+        cnt += (uint32_t)__popcll(m[q]);
+      }
+      uint32_t base = wave_count_prefix(cnt, scan_tmp, &nsel);
+#pragma unroll
+      for (int q = 0; q < FIN_NV; ++q) {
+        if ((m[q] >> lane) & 1ull) {
+          const uint32_t at = base + (uint32_t)__popcll(m[q] & ((1ull << lane) - 1ull));
+          if (at < (uint32_t)K) emit((int)at, (int32_t)(0xFFFFFFFFu - (uint32_t)c[q]));
+        }
+        base += (uint32_t)__popcll(m[q]);
+      }
+    } else {
+      nsel = ordered_compact(
+          total, [&](uint32_t i) { return selected(lc[i]); },
+          [&](uint32_t i, uint32_t at) {
+            if (at < (uint32_t)K) emit((int)at, (int32_t)(0xFFFFFFFFu - (uint32_t)lc[i]));
+          },
+          scan_tmp);
+    }
+    for (uint32_t j = nsel + tid; j < (uint32_t)K; j += NT) emit((int)j, -1);
+    return;
+  }
+  // Fallback: the same steps on a histogram of every score of the sequence
+  // (12-bit key bins); the threshold bin is the range of the 256 20-bit
+  // prefixes under bin T. When the score pass did not store the scores, this
+  // workgroup recomputes the sequence's first.
+  if (rescore) {
+    __shared__ __attribute__((aligned(16))) float lwf[16];
+    const int n = lane & 15, g = lane >> 4;
+    const int64_t row_base = src.entry_offset[b];
+    const uint8_t* ikb = src.ik + row_base * 64;
+    const uint8_t* iksb = src.iks + row_base * 4;
+    bf16x8_t qa[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      u32x4_t v = {0, 0, 0, 0};
+      if (n < src.Hi) v = *(const u32x4_t*)(src.q_idx + ((int64_t)b * src.Hi + n) * 128 + 32 * g + 8 * j);
+      __builtin_memcpy(&qa[j], &v, 16);
+    }
+    if (tid < 16) lwf[tid] = tid < src.Hi ? (src.w ? src.w[(int64_t)b * src.Hi + tid] : 1.0f) : 0.0f;
+    __syncthreads();
+    for (int64_t t0 = 16 * wave; t0 < n_pos; t0 += 16 * NWAVE) {
+      const uint32_t p = (uint32_t)min(t0 + n, n_pos - 1);
+      const u32x4_t cw = *(const u32x4_t*)(ikb + ((uint64_t)p * 64u + 16u * g));
+      const uint32_t sbyte = iksb[(uint64_t)p * 4u + (uint32_t)g];
+      const float sc = src.mode == 0 ? score_tile_fn<0>(qa, cw, sbyte, lwf, g) : score_tile_fn<1>(qa, cw, sbyte, lwf, g);
+      if (g == 0 && t0 + n < n_pos) sall[t0 + n] = sc;
+    }
+    __threadfence_block();                         // this workgroup reads them back
+  }
+  __syncthreads();
+  for (int i = tid; i < NBINS; i += NT) hist[i] = 0;
+  __syncthreads();
+  for (int64_t i = tid; i < n_pos; i += NT) atomicAdd(&hist[score_key(sall[i]) >> BIN_SHIFT], 1u);
+  __syncthreads();
+  {
+    uint32_t tot;
+    hist_kth_bin<NT>(hist, (uint32_t)K, scan_tmp, ctl, &tot);   // defined: n_pos > K
+  }
+  const uint32_t T = ctl[0], above = ctl[1], in_bin = hist[T];
+  const uint32_t need = (uint32_t)K - above;      // 1 .. in_bin
+  const uint32_t lo20 = T << 8;
+  const uint32_t hi20 = (T << 8) | 255u;
+  auto elem = [&](uint32_t i) -> uint64_t { return composite(score_key(sall[i]), i); };
+  const uint32_t n_src = (uint32_t)n_pos;
+  uint64_t prefix = 0, mask = 0;
+  if (need < in_bin) {
+    // the threshold bin is split: its keys (unordered) -> radix select
+    __syncthreads();                               // hist reads done before sub is reused
+    uint64_t* dst = in_bin <= (uint32_t)FIN_SUB_CAP ? sub : gscr;
+    if (tid == 0) ctl[6] = 0;
+    __syncthreads();
+    for (uint32_t i0 = 0; i0 < n_src; i0 += NT) {
+      const uint32_t i = i0 + tid;
+      const uint64_t c = i < n_src ? elem(i) : 0ull;
+      const uint32_t p20 = (uint32_t)(c >> 44);
+      const bool t = i < n_src && p20 >= lo20 && p20 <= hi20;
+      const uint32_t at = wave_append(t, &ctl[6]);
+      if (t && at < in_bin) dst[at] = c;
+    }
+    if (dst != sub) __threadfence_block();         // this workgroup reads its global copy back
+    __syncthreads();
+    const int top = radix_top_shift(dst, in_bin, red);
+    radix_select_u64(dst, in_bin, need, top, h, ctl, &prefix, &mask);
+  }
+  // the K best in position order: above the threshold bin, or inside it and
+  // radix-selected
+  const uint32_t nsel = ordered_compact(
+      n_src,
+      [&](uint32_t i) {
+        const uint64_t c = elem(i);
+        const uint32_t p20 = (uint32_t)(c >> 44);
+        return p20 > hi20 || (p20 >= lo20 && p20 <= hi20 && (c & mask) >= prefix);
+      },
+      [&](uint32_t i, uint32_t at) {
+        if (at < (uint32_t)K) emit((int)at, (int32_t)i);
+      },
+      scan_tmp);
+  for (uint32_t j = nsel + tid; j < (uint32_t)K; j += NT) emit((int)j, -1);
+}
+
+
+}  // namespace csa2

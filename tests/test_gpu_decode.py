@@ -104,3 +104,63 @@ def test_decode128k_full_size_sampled():
         s = OI.scores(oik, oiks, Lr["q_idx"][b], Lr["w"][b], 1)
         check_topk(top[b], OI.topk(s, np.arange(E), w.k), lambda q: s[q], w.k, f"seq{b}")
         check_attention(okv, top[b], Lr["q"][b], out[b], lse[b], f"attention seq{b}")
+
+
+def run_full(kv, ik, iks, off, n_list, H, k, rng, ws=None):
+    import torch
+    import long_context_fp4_amd as L
+    B = len(n_list)
+    q = np.stack([synth.latent_query(rng, H) for _ in range(B)])
+    qi = np.stack([synth.indexer_query(rng, 16) for _ in range(B)])
+    w = np.stack([synth.head_weights(rng, 16) for _ in range(B)])
+    top, _, out, lse = L.decode_layer(L.CSA2_FULL, dev(kv), dev(ik), dev(iks), dev(off),
+                                      dev(np.asarray(n_list, np.int32)), max(n_list), dev(q), q_idx=dev(qi),
+                                      w=dev(w), k=k, workspace=ws)
+    torch.cuda.synchronize()
+    return q, qi, w, host(top), host(out), host(lse)
+
+
+def check_full(kv, ik, iks, off, n_list, k, q, qi, w, top, out, lse, what):
+    for b, n in enumerate(n_list):
+        rows = slice(off[b], off[b] + n)
+        if n == 0:
+            assert np.all(top[b] == -1), f"{what} seq{b}: empty sequence selects nothing"
+            assert np.all(out[b] == 0) and np.all(np.isneginf(lse[b])), f"{what} seq{b}: empty attention"
+            continue
+        s = OI.scores(ik[rows], iks[rows], qi[b], w[b], 1)
+        check_topk(top[b], OI.topk(s, np.arange(n), k), lambda p: s[p], k, f"{what} seq{b}")
+        check_attention(kv[rows], top[b], q[b], out[b], lse[b], f"{what} attention seq{b}")
+
+
+@pytest.mark.parametrize("n_list,H,k", [([40000, 300, 17000, 65536, 0], 64, 512),   # two splits
+                                        ([20000, 33000, 511], 20, 100)])               # ragged head group
+def test_full_direct_top_k_inside_attention(n_list, H, k):
+    """Full layers whose direct top-k finish runs inside the attention launch:
+    short, empty and long sequences, one and two splits, a ragged head group."""
+    rng = np.random.default_rng(len(n_list) * 1000 + H + k)
+    kv, ik, iks, off = oracle_cache(rng, n_list, 1)
+    q, qi, w, top, out, lse = run_full(kv, ik, iks, off, n_list, H, k, rng)
+    check_full(kv, ik, iks, off, n_list, k, q, qi, w, top, out, lse, "fused")
+
+
+def test_full_direct_fallback_inside_attention():
+    """The 700 largest indexer keys of sequence 1 sit in its first chunk (E8M0
+    scales raised by 2^6): too few keys reach the highest local cutoff, so each
+    attention workgroup of that sequence recomputes its scores and selects from
+    all of them; sequence 0 takes the fast path in the same launch."""
+    rng = np.random.default_rng(23)
+    n_list = [30000, 40000]
+    kv, ik, iks, off = oracle_cache(rng, n_list, 1)
+    iks = iks.copy()
+    a = off[1]
+    iks[a:a + 700] = np.minimum(iks[a:a + 700].astype(np.int32) + 6, 254).astype(np.uint8)
+    q, qi, w, top, out, lse = run_full(kv, ik, iks, off, n_list, 64, 512, rng)
+    check_full(kv, ik, iks, off, n_list, 512, q, qi, w, top, out, lse, "fallback")
+    # the same workspace again with a smaller batch: the scratch rows are rewritten
+    import long_context_fp4_amd as L
+    ws = L.Workspace()
+    for nl in (n_list, n_list[1:]):
+        offs = off if len(nl) == 2 else off[1:] - off[1]
+        sl = slice(off[0] if len(nl) == 2 else off[1], off[-1] + n_list[-1])
+        q, qi, w, top, out, lse = run_full(kv[sl], ik[sl], iks[sl], offs, nl, 64, 512, rng, ws)
+        check_full(kv[sl], ik[sl], iks[sl], offs, nl, 512, q, qi, w, top, out, lse, f"reuse B={len(nl)}")
