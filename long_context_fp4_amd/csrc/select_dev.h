@@ -441,12 +441,17 @@ __device__ inline void finish_direct_body(int b, const int32_t* __restrict__ n_e
         __syncthreads();                             // hist reads done before sub is reused
         dst = in_bin <= (uint32_t)FIN_SUB_CAP ? sub : gscr;
       }
+      // (a small bin goes to binl with LDS stores; dst may be global memory)
+      auto put = [&](uint32_t at, uint64_t v) {
+        if (small) binl[at] = v;
+        else dst[at] = v;
+      };
       if (regs) {
 #pragma unroll
         for (int q = 0; q < FIN_NV; ++q) {
           const bool t = lo + 64 * q + lane < hi && is_in_bin(c[q]);
           const uint32_t at = wave_append(t, &bin_count);
-          if (t && at < in_bin) dst[at] = c[q];
+          if (t && at < in_bin) put(at, c[q]);
         }
       } else {
         for (uint32_t i0 = 0; i0 < total; i0 += NT) {
@@ -454,26 +459,33 @@ __device__ inline void finish_direct_body(int b, const int32_t* __restrict__ n_e
           const uint64_t cc = i < total ? lc[i] : 0ull;
           const bool t = i < total && is_in_bin(cc);
           const uint32_t at = wave_append(t, &bin_count);
-          if (t && at < in_bin) dst[at] = cc;
+          if (t && at < in_bin) put(at, cc);
         }
       }
-      if (dst != sub && dst != binl) __threadfence_block();   // this workgroup reads its global copy back
+      if (dst == gscr) __threadfence_block();        // this workgroup reads its global copy back
       __syncthreads();
-      if (!small) {
+      if (small) {
+        // keys are distinct (they carry the position): the need-th largest is
+        // the one with exactly need - 1 larger keys in the bin
+        for (uint32_t j = tid; j < in_bin; j += NT) {
+          const uint64_t v = binl[j];
+          uint32_t larger = 0;
+          for (uint32_t i = 0; i < in_bin; ++i) larger += binl[i] > v ? 1u : 0u;
+          if (larger == need - 1) red[0] = v;
+        }
+        __syncthreads();
+        prefix = red[0];
+        mask = ~0ull;
+      } else {
         const int top = radix_top_shift(dst, in_bin, red);
         radix_select_u64(dst, in_bin, need, top, h, ctl, &prefix, &mask);
       }
     }
-    // small bins: keys are distinct (they carry the position), so a key is
-    // selected when fewer than `need` keys of the bin are larger
+    // selected: above the threshold bin, or inside it and among the `need` largest
     auto selected = [&](uint64_t c) {
       if (is_above(c)) return true;
       if (!is_in_bin(c)) return false;
-      if (!split) return true;
-      if (!small) return (c & mask) >= prefix;
-      uint32_t larger = 0;
-      for (uint32_t j = 0; j < in_bin; ++j) larger += binl[j] > c ? 1u : 0u;
-      return larger < need;
+      return !split || (c & mask) >= prefix;
     };
     uint32_t nsel;
     if (regs) {
