@@ -37,11 +37,12 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 COPIES = 4
-SCORE_SOURCE = os.path.join(ROOT, "long_context_fp4_amd", "csrc", "indexer.hip")
+SCORE_SOURCES = [os.path.join(ROOT, "long_context_fp4_amd", "csrc", f)
+                 for f in ("indexer.hip", "select_dev.h", "device.h", "kernels.h")]
 # Counter readings of one scoring launch at the decode128k size (KiB per
 # dispatch, medians over the timed launches) and the counters' scale factors
-# from the copy calibration; valid for the kernel source with this hash.
-TRAFFIC = {"source_sha": "7a2200eea382ecb0", "fetch_kib": 70244.0, "write_kib": 8798.5,
+# from the copy calibration; valid for the kernel sources with this hash.
+TRAFFIC = {"source_sha": "9df155f2e335f86d", "fetch_kib": 70244.0, "write_kib": 606.5,
            "fetch_scale": 2.0, "write_scale": 1.0}
 
 
@@ -59,8 +60,11 @@ def parse():
 
 
 def source_hash():
-    with open(SCORE_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in SCORE_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def traffic_bytes():
