@@ -331,18 +331,19 @@ __device__ inline void finish_direct_body(int b, const int32_t* __restrict__ n_e
   constexpr int NWAVE = NT / 64;
   static_assert(NBINS % NT == 0 && NT % 64 == 0, "whole waves, whole bins per thread");
   if (tid == 0) bin_count = 0;                     // first read after several barriers
-  // the first header words, and the first 128 candidates of the four lists
-  // this wave copies first (workgroups wave, wave + NWAVE, ...), are requested
-  // before the sequence length and the list lengths are known
+  // The first header words, and the first 64 entries of the FS lists this
+  // wave handles first (chunks FS * wave .. FS * wave + FS - 1), are requested
+  // before the sequence length and the list lengths are known.
   const int64_t nw_max = (max_n + SC_CHUNK - 1) / SC_CHUNK;
   const uint64_t* hd = sb.hdr + (int64_t)b * sb.hdr_stride;
   const uint64_t h0 = tid < nw_max ? hd[tid] : 0ull;
   const uint64_t* wc = sb.wgc + (int64_t)b * sb.wgc_stride;
   const int nbk = (int)(sb.wgc_stride / CAND_CAP);   // list slots per sequence (>= 1)
-  constexpr int FS = 4096 / NT;                     // lists a wave copies per round (64 chunks in one round)
-  uint64_t v0[FS];                                  // the first 64 entries of each (the rest, when longer, later)
+  constexpr int FS = 4096 / NT;                     // lists a wave takes per round
+  constexpr int RL = FS * NWAVE;                    // lists of one round (64)
+  uint64_t v0[FS];
 #pragma unroll
-  for (int s = 0; s < FS; ++s) v0[s] = wc[(int64_t)min(wave + s * NWAVE, nbk - 1) * CAND_CAP + lane];
+  for (int s = 0; s < FS; ++s) v0[s] = wc[(int64_t)min(FS * wave + s, nbk - 1) * CAND_CAP + lane];
   // keeps the compiler from sinking these loads below the early return (their
   // latency then overlaps the sequence-length load)
   asm volatile("" ::: "memory");
@@ -353,88 +354,28 @@ __device__ inline void finish_direct_body(int b, const int32_t* __restrict__ n_e
   }
   for (int i = tid; i < NBINS; i += NT) hist[i] = 0;
   const int64_t nw = (n_pos + SC_CHUNK - 1) / SC_CHUNK;
-  bool fast = false;
-  uint32_t total = 0, cmax = 0;
-  if (nw <= FIN_MAX_WG) {
-    // list lengths -> offsets; thread t owns workgroups [w0, w1)
-    const int per = (int)((nw + NT - 1) / NT);
-    const int w0 = (int)min((int64_t)tid * per, nw), w1 = (int)min((int64_t)w0 + per, nw);
-    uint32_t cnt = 0, ovf = 0;
-    for (int w = w0; w < w1; ++w) {
-      const uint64_t hv = (per == 1) ? h0 : hd[w];
-      const uint32_t c = (uint32_t)hv & 0x7FFFFFFFu;
-      ovf |= (uint32_t)hv >> 31;
-      cmax = max(cmax, (uint32_t)(hv >> 32));
-      loff[w] = c;
-      cnt += c;
-    }
-    uint32_t run = block_exclusive_scan(cnt, scan_tmp, &total);
-    for (int w = w0; w < w1; ++w) {
-      const uint32_t c = loff[w];
-      loff[w] = run;
-      run += c;
-    }
-    block_max_or_u32(&cmax, &ovf, scan_tmp);
-    if (ovf == 0 && total <= (uint32_t)FIN_LDS_CANDS) {
-      // copy the lists in workgroup order (wave v takes workgroups v, v + 16, ...,
-      // eight independent loads per lane in flight) and histogram the prefixes
-      auto take = [&](uint64_t c, uint32_t at) {
-        lc[at] = c;
-        const uint32_t p20 = (uint32_t)(c >> 44);
-        if (p20 >= cmax) atomicAdd(&hist[min(p20 - cmax, (uint32_t)NBINS - 1)], 1u);
-      };
-      for (int w0 = wave; w0 < nw; w0 += FS * NWAVE) {
-        uint64_t v[FS];
-        uint32_t cn[FS], of[FS];
-        int ws[FS];
-#pragma unroll
-        for (int s = 0; s < FS; ++s) {
-          ws[s] = min(w0 + s * NWAVE, (int)nw - 1);
-          cn[s] = (w0 + s * NWAVE < nw) ? (ws[s] + 1 < nw ? loff[ws[s] + 1] : total) - loff[ws[s]] : 0u;
-          of[s] = loff[ws[s]];
-          // the first round: already requested
-          v[s] = w0 == wave ? v0[s] : wc[(int64_t)ws[s] * CAND_CAP + lane];
-        }
-#pragma unroll
-        for (int s = 0; s < FS; ++s) {
-          if ((uint32_t)lane < cn[s]) take(v[s], of[s] + lane);
-          for (uint32_t j = 64 + lane; j < cn[s]; j += 64) take(wc[(int64_t)ws[s] * CAND_CAP + j], of[s] + j);
-        }
-      }
-      __syncthreads();
-      uint32_t tot;
-      hist_kth_bin<NT>(hist, (uint32_t)K, scan_tmp, ctl, &tot);
-      fast = ctl[0] != 0xFFFFFFFFu;       // at least K keys reach the highest cutoff
-    }
-  }
-  if (fast) {
-    // Keys above the threshold bin are selected; inside it (20-bit prefixes
-    // lo20 .. hi20) the `need` largest. The candidates are read in lane order
-    // (unit stride, no LDS bank conflicts); an ordered compaction over
-    // wave-owned ranges places the selected positions in ascending order.
+  uint32_t cmax = 0;
+  auto p20_of = [](uint64_t c) { return (uint32_t)(c >> 44); };
+  auto count_above_cmax = [&](uint64_t c) {
+    const uint32_t p20 = p20_of(c);
+    if (p20 >= cmax) atomicAdd(&hist[min(p20 - cmax, (uint32_t)NBINS - 1)], 1u);
+  };
+
+  // The K-th key lies in bin ctl[0] (counted from cmax) with ctl[1] keys above
+  // it: those are selected; of the bin's keys the `need` largest. When the bin
+  // holds more than needed, `collect(in_bin_pred, put)` hands over its keys
+  // and the cut key follows: the one with exactly need - 1 larger keys (the
+  // keys are distinct: they carry the position), or a radix select beyond
+  // FIN_RANK_MAX keys. Returns the predicate of the selected keys.
+  auto resolve_bin = [&](auto collect) {
     const uint32_t T = ctl[0], above = ctl[1], in_bin = hist[T];
     const uint32_t need = (uint32_t)K - above;      // 1 .. in_bin
     const uint32_t lo20 = cmax + T;
     const uint32_t hi20 = T == NBINS - 1 ? 0xFFFFFu : cmax + T;
-    auto is_above = [&](uint64_t c) { return (uint32_t)(c >> 44) > hi20; };
-    auto is_in_bin = [&](uint64_t c) {
-      const uint32_t p20 = (uint32_t)(c >> 44);
-      return p20 >= lo20 && p20 <= hi20;
-    };
+    auto is_in_bin = [=](uint64_t c) { return p20_of(c) >= lo20 && p20_of(c) <= hi20; };
     const bool split = need < in_bin;                // else every in-bin key is selected
     const bool small = in_bin <= (uint32_t)FIN_RANK_MAX;
-    uint64_t prefix = 0, mask = 0;                   // large bins: in-bin keys with (c & mask) >= prefix
-    // Wave v owns the candidates [lo, hi) (a multiple of 64 of them); up to
-    // FIN_NV per lane they are read once, in lane order, into registers.
-    const uint32_t span = (total + NT - 1) / NT * 64;
-    const bool regs = span <= 64u * FIN_NV;
-    const uint32_t lo = min((uint32_t)wave * span, total), hi = min(lo + span, total);
-    uint64_t c[FIN_NV];
-#pragma unroll
-    for (int q = 0; q < FIN_NV; ++q) {
-      const uint32_t i = lo + 64 * q + lane;
-      c[q] = regs && i < hi ? lc[i] : 0ull;
-    }
+    uint64_t prefix = 0, mask = 0;                   // in-bin keys with (c & mask) >= prefix
     if (split) {
       uint64_t* dst = binl;
       if (!small) {
@@ -442,31 +383,17 @@ __device__ inline void finish_direct_body(int b, const int32_t* __restrict__ n_e
         dst = in_bin <= (uint32_t)FIN_SUB_CAP ? sub : gscr;
       }
       // (a small bin goes to binl with LDS stores; dst may be global memory)
-      auto put = [&](uint32_t at, uint64_t v) {
-        if (small) binl[at] = v;
-        else dst[at] = v;
+      auto put = [&](bool t, uint64_t v) {
+        const uint32_t at = wave_append(t, &bin_count);
+        if (t && at < in_bin) {
+          if (small) binl[at] = v;
+          else dst[at] = v;
+        }
       };
-      if (regs) {
-#pragma unroll
-        for (int q = 0; q < FIN_NV; ++q) {
-          const bool t = lo + 64 * q + lane < hi && is_in_bin(c[q]);
-          const uint32_t at = wave_append(t, &bin_count);
-          if (t && at < in_bin) put(at, c[q]);
-        }
-      } else {
-        for (uint32_t i0 = 0; i0 < total; i0 += NT) {
-          const uint32_t i = i0 + tid;
-          const uint64_t cc = i < total ? lc[i] : 0ull;
-          const bool t = i < total && is_in_bin(cc);
-          const uint32_t at = wave_append(t, &bin_count);
-          if (t && at < in_bin) put(at, cc);
-        }
-      }
+      collect(is_in_bin, put);
       if (dst == gscr) __threadfence_block();        // this workgroup reads its global copy back
       __syncthreads();
       if (small) {
-        // keys are distinct (they carry the position): the need-th largest is
-        // the one with exactly need - 1 larger keys in the bin
         for (uint32_t j = tid; j < in_bin; j += NT) {
           const uint64_t v = binl[j];
           uint32_t larger = 0;
@@ -481,40 +408,143 @@ __device__ inline void finish_direct_body(int b, const int32_t* __restrict__ n_e
         radix_select_u64(dst, in_bin, need, top, h, ctl, &prefix, &mask);
       }
     }
-    // selected: above the threshold bin, or inside it and among the `need` largest
-    auto selected = [&](uint64_t c) {
-      if (is_above(c)) return true;
+    return [=](uint64_t c) {
+      if (p20_of(c) > hi20) return true;
       if (!is_in_bin(c)) return false;
       return !split || (c & mask) >= prefix;
     };
+  };
+  // Candidates held N per lane in cv (valid where ok(q)), in position order
+  // wave by wave, then register by register, then lane by lane: resolve the
+  // bin, then a ballot per register, one exchange of wave counts and the
+  // ballots' prefix counts place the K positions in ascending order.
+  auto finish_regs = [&](const auto& cv, auto ok) {
+    constexpr int N = sizeof(cv) / sizeof(uint64_t);
+    const auto selected = resolve_bin([&](auto in_bin_pred, auto put) {
+#pragma unroll
+      for (int q = 0; q < N; ++q) put(ok(q) && in_bin_pred(cv[q]), cv[q]);
+    });
+    uint64_t m[N];
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int q = 0; q < N; ++q) {
+      m[q] = __ballot(ok(q) && selected(cv[q]));
+      cnt += (uint32_t)__popcll(m[q]);
+    }
     uint32_t nsel;
-    if (regs) {
-      uint64_t m[FIN_NV];
-      uint32_t cnt = 0;
+    uint32_t base = wave_count_prefix(cnt, scan_tmp, &nsel);
 #pragma unroll
-      for (int q = 0; q < FIN_NV; ++q) {
-        m[q] = __ballot(lo + 64 * q + lane < hi && selected(c[q]));
-        cnt += (uint32_t)__popcll(m[q]);
+    for (int q = 0; q < N; ++q) {
+      if ((m[q] >> lane) & 1ull) {
+        const uint32_t at = base + (uint32_t)__popcll(m[q] & ((1ull << lane) - 1ull));
+        if (at < (uint32_t)K) emit((int)at, (int32_t)(0xFFFFFFFFu - (uint32_t)cv[q]));
       }
-      uint32_t base = wave_count_prefix(cnt, scan_tmp, &nsel);
-#pragma unroll
-      for (int q = 0; q < FIN_NV; ++q) {
-        if ((m[q] >> lane) & 1ull) {
-          const uint32_t at = base + (uint32_t)__popcll(m[q] & ((1ull << lane) - 1ull));
-          if (at < (uint32_t)K) emit((int)at, (int32_t)(0xFFFFFFFFu - (uint32_t)c[q]));
-        }
-        base += (uint32_t)__popcll(m[q]);
-      }
-    } else {
-      nsel = ordered_compact(
-          total, [&](uint32_t i) { return selected(lc[i]); },
-          [&](uint32_t i, uint32_t at) {
-            if (at < (uint32_t)K) emit((int)at, (int32_t)(0xFFFFFFFFu - (uint32_t)lc[i]));
-          },
-          scan_tmp);
+      base += (uint32_t)__popcll(m[q]);
     }
     for (uint32_t j = nsel + tid; j < (uint32_t)K; j += NT) emit((int)j, -1);
-    return;
+  };
+
+  if (nw <= FIN_MAX_WG) {
+    // headers: list lengths, overflow, the highest cutoff; thread t owns chunks [w0, w1)
+    const int per = (int)((nw + NT - 1) / NT);
+    const int w0 = (int)min((int64_t)tid * per, nw), w1 = (int)min((int64_t)w0 + per, nw);
+    uint32_t cnt = 0, flags = 0;
+    for (int w = w0; w < w1; ++w) {
+      const uint64_t hv = (per == 1) ? h0 : hd[w];
+      const uint32_t c = (uint32_t)hv & 0x7FFFFFFFu;
+      flags |= ((uint32_t)hv >> 31) | (c > 64u ? 2u : 0u);   // 1: a list overflowed; 2: a list beyond 64
+      cmax = max(cmax, (uint32_t)(hv >> 32));
+      loff[w] = c;
+      cnt += c;
+    }
+    block_max_or_u32(&cmax, &flags, scan_tmp);
+    if (flags == 0 && nw <= RL) {
+      // Every list is in registers already: wave v holds entry `lane` of
+      // chunks FS v .. FS v + FS - 1, which is position order.
+      uint32_t cn[FS];
+#pragma unroll
+      for (int s = 0; s < FS; ++s) {
+        const int w = FS * wave + s;
+        cn[s] = w < nw ? loff[w] : 0u;
+        if ((uint32_t)lane < cn[s]) count_above_cmax(v0[s]);
+      }
+      __syncthreads();
+      uint32_t tot;
+      hist_kth_bin<NT>(hist, (uint32_t)K, scan_tmp, ctl, &tot);
+      if (ctl[0] != 0xFFFFFFFFu) {                   // at least K keys reach the highest cutoff
+        finish_regs(v0, [&](int q) { return (uint32_t)lane < cn[q]; });
+        return;
+      }
+    } else if ((flags & 1u) == 0) {
+      // lists -> LDS at offsets from a scan of their lengths
+      uint32_t total;
+      uint32_t run = block_exclusive_scan(cnt, scan_tmp, &total);
+      for (int w = w0; w < w1; ++w) {
+        const uint32_t c = loff[w];
+        loff[w] = run;
+        run += c;
+      }
+      __syncthreads();
+      if (total <= (uint32_t)FIN_LDS_CANDS) {
+        // copy the lists in chunk order (wave v takes the FS chunks from
+        // FS v in each round of RL) and histogram the prefixes
+        auto take = [&](uint64_t c, uint32_t at) {
+          lc[at] = c;
+          count_above_cmax(c);
+        };
+        for (int r0 = 0; r0 < nw; r0 += RL) {
+          uint64_t v[FS];
+          uint32_t cn[FS], of[FS];
+          int ws[FS];
+#pragma unroll
+          for (int s = 0; s < FS; ++s) {
+            const int w = r0 + FS * wave + s;
+            ws[s] = min(w, (int)nw - 1);
+            cn[s] = w < nw ? (ws[s] + 1 < nw ? loff[ws[s] + 1] : total) - loff[ws[s]] : 0u;
+            of[s] = loff[ws[s]];
+            v[s] = r0 == 0 ? v0[s] : wc[(int64_t)ws[s] * CAND_CAP + lane];   // round 0: already requested
+          }
+#pragma unroll
+          for (int s = 0; s < FS; ++s) {
+            if ((uint32_t)lane < cn[s]) take(v[s], of[s] + lane);
+            for (uint32_t j = 64 + lane; j < cn[s]; j += 64) take(wc[(int64_t)ws[s] * CAND_CAP + j], of[s] + j);
+          }
+        }
+        __syncthreads();
+        uint32_t tot;
+        hist_kth_bin<NT>(hist, (uint32_t)K, scan_tmp, ctl, &tot);
+        if (ctl[0] != 0xFFFFFFFFu) {
+          // wave v owns the candidates [lo, hi) (a multiple of 64 of them)
+          const uint32_t span = (total + NT - 1) / NT * 64;
+          const uint32_t lo = min((uint32_t)wave * span, total), hi = min(lo + span, total);
+          if (span <= 64u * FIN_NV) {
+            uint64_t c[FIN_NV];
+#pragma unroll
+            for (int q = 0; q < FIN_NV; ++q) {
+              const uint32_t i = lo + 64 * q + lane;
+              c[q] = i < hi ? lc[i] : 0ull;
+            }
+            finish_regs(c, [&](int q) { return lo + 64 * q + lane < hi; });
+          } else {
+            const auto selected = resolve_bin([&](auto in_bin_pred, auto put) {
+              for (uint32_t i0 = 0; i0 < total; i0 += NT) {
+                const uint32_t i = i0 + tid;
+                const uint64_t cc = i < total ? lc[i] : 0ull;
+                put(i < total && in_bin_pred(cc), cc);
+              }
+            });
+            const uint32_t nsel = ordered_compact(
+                total, [&](uint32_t i) { return selected(lc[i]); },
+                [&](uint32_t i, uint32_t at) {
+                  if (at < (uint32_t)K) emit((int)at, (int32_t)(0xFFFFFFFFu - (uint32_t)lc[i]));
+                },
+                scan_tmp);
+            for (uint32_t j = nsel + tid; j < (uint32_t)K; j += NT) emit((int)j, -1);
+          }
+          return;
+        }
+      }
+    }
   }
   // Fallback: the same steps on a histogram of every score of the sequence
   // (12-bit key bins); the threshold bin is the range of the 256 20-bit

@@ -164,3 +164,21 @@ def test_full_direct_fallback_inside_attention():
         sl = slice(off[0] if len(nl) == 2 else off[1], off[-1] + n_list[-1])
         q, qi, w, top, out, lse = run_full(kv[sl], ik[sl], iks[sl], offs, nl, 64, 512, rng, ws)
         check_full(kv[sl], ik[sl], iks[sl], offs, nl, 512, q, qi, w, top, out, lse, f"reuse B={len(nl)}")
+
+
+def test_full_direct_long_lists_inside_attention():
+    """Sequence 0 carries 90 and 100 copies of its best indexer row in two
+    chunks: their lists exceed 64 candidates, so the attention workgroups copy
+    the lists to LDS before selecting; sequence 1 has more than 64 chunks."""
+    rng = np.random.default_rng(41)
+    n_list = [40000, 70000]
+    kv, ik, iks, off = oracle_cache(rng, n_list, 1)
+    qi0 = synth.indexer_query(np.random.default_rng(0), 16)
+    ik, iks = ik.copy(), iks.copy()
+    s0 = OI.scores(ik[:n_list[0]], iks[:n_list[0]], qi0, synth.head_weights(np.random.default_rng(1), 16), 1)
+    best = int(np.argmax(s0))
+    for a, cnt in ((3072, 90), (20000, 100)):
+        ik[a:a + cnt] = ik[best]
+        iks[a:a + cnt] = iks[best]
+    q, qi, w, top, out, lse = run_full(kv, ik, iks, off, n_list, 64, 512, rng)
+    check_full(kv, ik, iks, off, n_list, 512, q, qi, w, top, out, lse, "long lists")

@@ -202,3 +202,26 @@ def test_workspace_reuse_across_batch_sizes():
             check_sequence(ik, iks, off[b], n, q[b], w[b], 1, top[b], sc[b], k, what=f"B{B} seq{b}")
         # the control region is clean again after every call
         assert int(ws.buf[: 1024 * 16640].count_nonzero()) == 0
+
+
+def test_long_lists_take_the_lds_path():
+    """90 and 100 copies of the sequence's best row in two chunks: those chunks'
+    lists hold more than 64 candidates (all tied at the cutoff), so the finish
+    copies the lists to LDS instead of keeping them in registers; the tied keys
+    are taken in position order."""
+    rng = np.random.default_rng(31)
+    n = 40000
+    ik, iks, off = make_keys(rng, [n])
+    q = synth.indexer_query(rng, 16)[None]
+    w = synth.head_weights(rng, 16)[None]
+    s0 = OI.scores(ik, iks, q[0], w[0], 1)
+    best = int(np.argmax(s0))
+    ik, iks = ik.copy(), iks.copy()
+    for a, cnt in ((3072, 90), (20000, 100)):
+        ik[a:a + cnt] = ik[best]
+        iks[a:a + cnt] = iks[best]
+    s = OI.scores(ik, iks, q[0], w[0], 1)
+    want = OI.topk(s, np.arange(n), 512)
+    for top in (run_no_scores(ik, iks, off, [n], n, q, w, 512)[0], run(ik, iks, off, [n], n, q, w, 1, 512)[0][0]):
+        check_topk(top, want, lambda p: s[p], 512, "long lists")
+        assert set(range(3072, 3162)) <= set(top.tolist()) and set(range(20000, 20100)) <= set(top.tolist())
