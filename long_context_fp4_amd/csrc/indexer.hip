@@ -20,18 +20,19 @@
 //                v_mfma_f32_16x16x32_bf16; the head sum is a 4-term in-lane sum
 //                plus two VALU lane swaps. Scores are staged in LDS and written
 //                with coalesced 16-byte stores.
-//                Selection without contended atomics: each workgroup builds an
-//                LDS histogram of its 1024 score keys, picks a local cutoff bin
-//                that keeps about four times its expected share of the top-k,
-//                and writes to its own slot the (bin, count) pairs above that
-//                cutoff (and, for k <= 512, the candidates themselves). The last
-//                workgroup of a sequence merges the slots: bins at or above the
-//                highest cutoff are complete, so the bin holding the k-th best
-//                key follows exactly whenever it lies there (otherwise it falls
-//                back to a full histogram of the sequence's scores). For
-//                k <= 512 it then radix-selects the k best among the gathered
-//                candidates and writes them in ascending order; larger k (the
-//                hierarchical pool) go on to select_kernel.
+//                Selection without contended atomics: each workgroup finds a
+//                local cutoff over its 1024 score keys that keeps a multiple of
+//                its expected share of the top-k, and writes to its own slot the
+//                (bin, count) pairs above that cutoff (pool) or, for k <= 512,
+//                the candidates themselves with a header word.
+// finish_*_kernel  one workgroup per sequence merges the slots: bins at or
+//                above the highest cutoff are complete, so the bin holding the
+//                k-th best key follows exactly whenever it lies there
+//                (otherwise a full histogram of the sequence's scores is the
+//                fallback). For k <= 512 the k best among the candidates are
+//                written in ascending order (finish_direct_body, which a Full
+//                decode layer runs inside its attention launch instead); larger
+//                k (the hierarchical pool) go on to select_kernel.
 // select_kernel  (large k) marks every position whose key lies above that bin
 //                in a per-sequence bitmap and appends the ones inside it as
 //                (key, position) candidates; the last workgroup of the sequence
