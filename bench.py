@@ -15,7 +15,9 @@ step's stream; the whole step is timed with events around K steps.
 
 The same run also times the cache write on its own workload (8 sequences of
 131072 tokens merged at ratio 2, the write128k configuration) and reports it
-beside the step as "cache_write".
+beside the step as "cache_write", and the decode-time append of one token for
+each of the 32 sequences (ratio 2: every other call completes a group and
+packs 32 entries) as "append".
 
 `traffic` in the roofline object is the HBM traffic of one scoring launch from
 rocprofv3 FETCH_SIZE and WRITE_SIZE counters, each scaled by what the same
@@ -118,6 +120,45 @@ def cache_write_leg(L, synth, torch):
                         "merge, packed to 288 + 68 B per entry",
             "bound": "hbm", "bytes_per_launch": nbytes, "avg_launch_us": us, "achieved": gbs,
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS}
+
+
+def append_leg(L, synth, torch):
+    """Decode-time append: one token for each of 32 sequences per call, ratio 2."""
+    import numpy as np
+    B, m, cap, n = 32, 2, 4096, 200
+    rng = np.random.default_rng(20261210)
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    wl, wi = d(synth.merge_weights(rng, m, 512)), d(synth.merge_weights(rng, m, 128))
+    toks = [(d(synth.hidden_host(rng, (B, 512)).view(np.int16)), d(synth.hidden_host(rng, (B, 128)).view(np.int16)))
+            for _ in range(8)]
+    kv = torch.zeros((B * cap, 288), dtype=torch.uint8, device="cuda")
+    ik = torch.zeros((B * cap, 64), dtype=torch.uint8, device="cuda")
+    iks = torch.zeros((B * cap, 4), dtype=torch.uint8, device="cuda")
+    st_l = torch.zeros((B, m - 1, 512), dtype=torch.int16, device="cuda")
+    st_i = torch.zeros((B, m - 1, 128), dtype=torch.int16, device="cuda")
+    cnt = torch.zeros(B, dtype=torch.int32, device="cuda")
+    ne = torch.zeros(B, dtype=torch.int32, device="cuda")
+    off = d(np.arange(B, dtype=np.int64) * cap)
+    call = lambda i: L.cache_append(toks[i % 8][0], toks[i % 8][1], wl, wi, m, st_l, st_i, cnt, off, ne, cap,
+                                    kv, ik, iks)
+    for i in range(10):
+        call(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # a long first kernel keeps the GPU busy while the host enqueues the calls,
+    # so the events time the appends back to back, not the host's call rate
+    torch.cuda._sleep(100_000_000)
+    e0.record()
+    for i in range(n):
+        call(i)
+    e1.record()
+    torch.cuda.synchronize()
+    us = 1e3 * e0.elapsed_time(e1) / n
+    # per pair of calls: 2 tokens read per sequence, one staged (written, then read) and one entry written
+    pair_bytes = B * (2 * 1280 + 2 * 1280 + 356)
+    return {"workload": f"append: one token for each of {B} sequences per call, ratio {m} (every other call "
+                        f"packs {B} entries)", "bound": "latency", "avg_call_us": us, "calls": n,
+            "bytes_per_call": pair_bytes / 2}
 
 
 def log(msg):
@@ -283,6 +324,10 @@ def main():
         res["cache_write"] = cache_write_leg(L, synth, torch)
         log(f"cache write {res['cache_write']['avg_launch_us']:.1f} us "
             f"({res['cache_write']['achieved']:.0f} GB/s)")
+    if not a.no_cache_write:
+        log("append leg")
+        res["append"] = append_leg(L, synth, torch)
+        log(f"append {res['append']['avg_call_us']:.2f} us per call")
     if not a.no_cpu_baseline:
         log("timing the oracle on the host")
         res["cpu_baseline"] = cpu_baseline(w, p, a.cpu_seconds)

@@ -112,6 +112,40 @@ int csa2_cache_write(const uint16_t* x_lat, const uint16_t* x_idx,
                      uint8_t* kv, uint8_t* ik, uint8_t* iks, void* stream);
 
 /*
+ * Decode-time append: one new token per sequence ([FP4] section "Le compte par
+ * couche": one entry per m tokens; the tokens of a group not yet complete wait
+ * in a per-sequence stage, as in [CS] section "L'architecture : trois leviers
+ * contre le cache", where the newest tokens are covered by the window).
+ *
+ *   x_lat, x_idx   bf16 [B][512], [B][128]: this step's token of each sequence
+ *   w_lat, w_idx   the merge weights, as in csa2_cache_write
+ *   stage_lat      bf16 [B][m-1][512], stage_idx bf16 [B][m-1][128]: in/out, the
+ *                  staged tokens of each sequence's incomplete group (NULL when m == 1)
+ *   stage_count    i32 [B] in/out: staged tokens, 0 <= stage_count[b] < m
+ *   entry_offset   i64 [B]: first cache row of sequence b
+ *   n_entries      i32 [B] in/out: entries written so far
+ *   capacity       cache rows reserved per sequence
+ *   kv, ik, iks    the cache (as in csa2_cache_write)
+ *   dropped        i32 [B] out, or NULL: 1 where a completed group found the
+ *                  sequence full (n_entries[b] == capacity) and was discarded
+ * When stage_count[b] + 1 < m the token is staged at row stage_count[b] and
+ * stage_count[b] grows by one. Otherwise the m - 1 staged tokens and this one
+ * are merged and packed exactly as csa2_cache_write packs tokens m*i .. m*i+m-1
+ * into cache row entry_offset[b] + n_entries[b]; n_entries[b] grows by one and
+ * stage_count[b] returns to 0. T tokens appended one call at a time therefore
+ * leave the same floor(T/m) entries as one csa2_cache_write of the T tokens,
+ * and the last T mod m tokens in the stage. A stage count outside [0, m-1] is
+ * taken as m - 1.
+ * Errors: NULL pointer, B < 1 or B > CSA2_MAX_BATCH, m outside [1, CSA2_MAX_RATIO],
+ * capacity < 0, misalignment (16 bytes; iks 4; stage_count, n_entries, dropped 4).
+ */
+int csa2_cache_append(const uint16_t* x_lat, const uint16_t* x_idx,
+                      const float* w_lat, const float* w_idx, int B, int m,
+                      uint16_t* stage_lat, uint16_t* stage_idx, int32_t* stage_count,
+                      const int64_t* entry_offset, int32_t* n_entries, int64_t capacity,
+                      uint8_t* kv, uint8_t* ik, uint8_t* iks, int32_t* dropped, void* stream);
+
+/*
  * Indexer pass and top-k ([FP4] section "Les ingrédients": the indexer key scores
  * positions; [CS] section "L'architecture : trois leviers contre le cache": new
  * top-512 per Full layer, hierarchical pool of at most 16384 candidates; [F24]

@@ -40,6 +40,8 @@ def lib():
     vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
     L.csa2_cache_write.argtypes = [vp, vp, vp, vp, i32, i64, i32, vp, vp, vp, vp]
     L.csa2_cache_write.restype = i32
+    L.csa2_cache_append.argtypes = [vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, vp]
+    L.csa2_cache_append.restype = i32
     L.csa2_indexer_workspace_bytes.argtypes = [i32, i64, i32]
     L.csa2_indexer_workspace_bytes.restype = sz
     L.csa2_indexer_topk.argtypes = [vp, vp, vp, vp, i32, i64, vp, vp, i32, i32, vp, i32, i32, vp, i32, vp,
@@ -152,6 +154,39 @@ def cache_write(x_lat, x_idx, w_lat, w_idx, m, kv=None, ik=None, iks=None, strea
                                   B, T, m, _ptr(kv, torch.uint8, "kv"), _ptr(ik, torch.uint8, "ik"),
                                   _ptr(iks, torch.uint8, "iks"), _stream(stream)))
     return kv, ik, iks
+
+
+def cache_append(x_lat, x_idx, w_lat, w_idx, m, stage_lat, stage_idx, stage_count, entry_offset, n_entries,
+                 capacity, kv, ik, iks, dropped=None, stream=None):
+    """Append one token per sequence (x_lat [B,512], x_idx [B,128] bf16 bits) to the cache.
+
+    stage_lat [B,m-1,512] / stage_idx [B,m-1,128] (None when m == 1), stage_count [B] i32 and
+    n_entries [B] i32 are updated in place; a completed group is packed into cache row
+    entry_offset[b] + n_entries[b] of kv / ik / iks. Returns dropped [B] i32 when given.
+    """
+    torch = _torch()
+    B = x_lat.shape[0]
+    if tuple(x_lat.shape) != (B, 512) or tuple(x_idx.shape) != (B, 128):
+        raise ValueError("x_lat must be [B,512] and x_idx [B,128]")
+    if tuple(w_lat.shape) != (m, 512) or tuple(w_idx.shape) != (m, 128):
+        raise ValueError("w_lat must be [m,512] and w_idx [m,128]")
+    if m > 1 and (stage_lat is None or tuple(stage_lat.shape) != (B, m - 1, 512) or
+                  tuple(stage_idx.shape) != (B, m - 1, 128)):
+        raise ValueError("stage_lat must be [B,m-1,512] and stage_idx [B,m-1,128]")
+    if stage_count.shape[0] != B or n_entries.shape[0] != B or entry_offset.shape[0] != B:
+        raise ValueError("stage_count, n_entries and entry_offset must be [B]")
+    bt = _bf16_types()
+    st_l = _ptr(stage_lat, bt, "stage_lat") if m > 1 else None
+    st_i = _ptr(stage_idx, bt, "stage_idx") if m > 1 else None
+    _check(lib().csa2_cache_append(_ptr(x_lat, bt, "x_lat"), _ptr(x_idx, bt, "x_idx"),
+                                   _ptr(w_lat, torch.float32, "w_lat"), _ptr(w_idx, torch.float32, "w_idx"),
+                                   B, m, st_l, st_i, _ptr(stage_count, torch.int32, "stage_count"),
+                                   _ptr(entry_offset, torch.int64, "entry_offset"),
+                                   _ptr(n_entries, torch.int32, "n_entries"), int(capacity),
+                                   _ptr(kv, torch.uint8, "kv"), _ptr(ik, torch.uint8, "ik"),
+                                   _ptr(iks, torch.uint8, "iks"), _ptr(dropped, torch.int32, "dropped"),
+                                   _stream(stream)))
+    return dropped
 
 
 def indexer_topk(ik, iks, entry_offset, n_entries, max_n, q_idx, w=None, score_mode=CSA2_SCORE_RELU_W,

@@ -259,6 +259,28 @@ int csa2_cache_write(const uint16_t* x_lat, const uint16_t* x_idx, const float* 
   return hip_status(e, "cache_write");
 }
 
+int csa2_cache_append(const uint16_t* x_lat, const uint16_t* x_idx, const float* w_lat, const float* w_idx,
+                      int B, int m, uint16_t* stage_lat, uint16_t* stage_idx, int32_t* stage_count,
+                      const int64_t* entry_offset, int32_t* n_entries, int64_t capacity, uint8_t* kv,
+                      uint8_t* ik, uint8_t* iks, int32_t* dropped, void* stream) {
+  if (!x_lat || !x_idx || !w_lat || !w_idx || !stage_count || !entry_offset || !n_entries || !kv || !ik || !iks)
+    return fail(CSA2_ERR_NULL, "cache_append: a required pointer is NULL");
+  if (m > 1 && (!stage_lat || !stage_idx)) return fail(CSA2_ERR_NULL, "cache_append: m > 1 needs the stage buffers");
+  if (B < 1 || B > CSA2_MAX_BATCH)
+    return fail(CSA2_ERR_SHAPE, "cache_append: B must be in [1, %d] (got %d)", CSA2_MAX_BATCH, B);
+  if (m < 1 || m > CSA2_MAX_RATIO)
+    return fail(CSA2_ERR_SHAPE, "cache_append: m must be in [1, %d] (got %d)", CSA2_MAX_RATIO, m);
+  if (capacity < 0) return fail(CSA2_ERR_SHAPE, "cache_append: capacity must be >= 0");
+  if (!aligned16(x_lat) || !aligned16(x_idx) || !aligned16(w_lat) || !aligned16(w_idx) || !aligned16(kv) ||
+      !aligned16(ik) || !aligned4(iks) || !aligned16(entry_offset) || !aligned4(stage_count) ||
+      !aligned4(n_entries) || (dropped && !aligned4(dropped)) || (m > 1 && (!aligned16(stage_lat) || !aligned16(stage_idx))))
+    return fail(CSA2_ERR_ALIGN, "cache_append: data pointers must be aligned (16 bytes; iks and counters 4)");
+  hipError_t e = csa2::launch_cache_append(x_lat, x_idx, w_lat, w_idx, B, m, stage_lat, stage_idx, stage_count,
+                                           entry_offset, n_entries, capacity, kv, ik, iks, dropped,
+                                           (hipStream_t)stream);
+  return hip_status(e, "cache_append");
+}
+
 size_t csa2_indexer_workspace_bytes(int B, int64_t max_n, int cand_stride) {
   if (B < 1 || B > CSA2_MAX_BATCH || max_n < 0 || cand_stride < 0) return 0;
   return indexer_layout(B, max_n, cand_stride).total;

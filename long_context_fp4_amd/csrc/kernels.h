@@ -28,6 +28,11 @@ __host__ __device__ inline uint32_t* ctrl_hist(uint8_t* ctrl, int b) { return (u
 hipError_t launch_cache_write(const uint16_t* x_lat, const uint16_t* x_idx, const float* w_lat,
                               const float* w_idx, int B, int64_t T, int m, uint8_t* kv, uint8_t* ik,
                               uint8_t* iks, hipStream_t stream);
+hipError_t launch_cache_append(const uint16_t* x_lat, const uint16_t* x_idx, const float* w_lat,
+                               const float* w_idx, int B, int m, uint16_t* st_lat, uint16_t* st_idx,
+                               int32_t* st_count, const int64_t* entry_offset, int32_t* n_entries,
+                               int64_t capacity, uint8_t* kv, uint8_t* ik, uint8_t* iks, int32_t* dropped,
+                               hipStream_t stream);
 
 // Selection modes of the score pass.
 enum { SEL_NONE = 0, SEL_THRESHOLD = 1, SEL_DIRECT = 2 };

@@ -114,6 +114,30 @@ def cache_write(x_lat_bits, x_idx_bits, w_lat, w_idx, m):
     return kv, ik, iks
 
 
+def append_tokens(x_lat_bits, x_idx_bits, w_lat, w_idx, m):
+    """Decode-time append of one sequence's tokens, one at a time.
+
+    [FP4] section "Le compte par couche": one entry per m tokens. Each token
+    joins the sequence's stage; when the stage holds m tokens they are merged
+    and packed (exactly as cache_write packs one group) into the next entry
+    and the stage empties. Returns (kv, ik, iks) of the completed groups in
+    order and the staged (latent, key) rows left over.
+    """
+    kv, ik, iks = [], [], []
+    stage = []
+    for t in range(x_lat_bits.shape[0]):
+        stage.append(t)
+        if len(stage) == m:
+            a, b, c = cache_write(x_lat_bits[stage], x_idx_bits[stage], w_lat, w_idx, m)
+            kv.append(a)
+            ik.append(b)
+            iks.append(c)
+            stage = []
+    empty = lambda w: np.zeros((0, w), np.uint8)
+    return (np.concatenate(kv) if kv else empty(288), np.concatenate(ik) if ik else empty(64),
+            np.concatenate(iks) if iks else empty(4), x_lat_bits[stage], x_idx_bits[stage])
+
+
 def unpack_nibbles(packed):
     packed = np.asarray(packed, dtype=np.uint8)
     out = np.empty(packed.shape[:-1] + (packed.shape[-1] * 2,), dtype=np.uint8)

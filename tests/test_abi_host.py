@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_header_declares_the_api():
     names = declared_functions()
-    for n in ("csa2_cache_write", "csa2_indexer_topk", "csa2_sparse_attention", "csa2_decode_layer",
+    for n in ("csa2_cache_write", "csa2_cache_append", "csa2_indexer_topk", "csa2_sparse_attention", "csa2_decode_layer",
               "csa2_indexer_workspace_bytes", "csa2_attention_workspace_bytes", "csa2_decode_workspace_bytes",
               "csa2_bytes_per_token", "csa2_last_error"):
         assert n in names
@@ -51,6 +51,25 @@ def test_cache_write_validation(L):
     assert L.csa2_cache_write(P, P, P, P, 1, 10, 17, P, P, P, None) == -2
     assert L.csa2_cache_write(P + 2, P, P, P, 1, 10, 2, P, P, P, None) == -3
     assert L.csa2_cache_write(P, P, P, P, 1, 10, 2, P, P, P + 2, None) == -3   # iks needs 4 bytes
+    assert "aligned" in err(L)
+
+
+def test_cache_append_validation(L):
+    def call(**kw):
+        a = dict(xl=P, xi=P, wl=P, wi=P, B=2, m=2, sl=P, si=P, sc=P, off=P, n=P, cap=10, kv=P, ik=P, iks=P, dr=None)
+        a.update(kw)
+        return L.csa2_cache_append(a["xl"], a["xi"], a["wl"], a["wi"], a["B"], a["m"], a["sl"], a["si"], a["sc"],
+                                   a["off"], a["n"], a["cap"], a["kv"], a["ik"], a["iks"], a["dr"], None)
+    assert call(xl=None) == -1
+    assert call(n=None) == -1
+    assert call(sl=None) == -1            # m > 1 needs the stage
+    assert call(B=0) == -2 and call(B=1025) == -2
+    assert call(m=0) == -2 and call(m=17) == -2
+    assert call(cap=-1) == -2
+    assert call(xl=P + 2) == -3
+    assert call(iks=P + 2) == -3          # 4-byte alignment
+    assert call(sc=P + 2) == -3
+    assert call(dr=P + 2) == -3
     assert "aligned" in err(L)
 
 

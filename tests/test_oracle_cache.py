@@ -158,3 +158,21 @@ def test_row_layout_sizes():
     kv, ik, iks = C.cache_write(x_lat, x_idx, p["w_lat"], p["w_idx"], 2)
     assert kv.shape == (50, 288) and ik.shape == (50, 64) and iks.shape == (50, 4)
     assert kv.shape[1] + ik.shape[1] + iks.shape[1] == 356
+
+
+@pytest.mark.parametrize("m,T", [(1, 5), (2, 9), (3, 10), (4, 4), (4, 3), (16, 40)])
+def test_append_one_token_at_a_time_equals_one_write(m, T):
+    """Tokens appended one at a time leave the entries of one write of all of
+    them (floor(T/m) groups of consecutive tokens, in order) and the last
+    T mod m tokens in the stage."""
+    rng = np.random.default_rng(100 * m + T)
+    x_lat = synth.hidden_host(rng, (T, 512))
+    x_idx = synth.hidden_host(rng, (T, 128))
+    w_lat = synth.merge_weights(rng, m, 512)
+    w_idx = synth.merge_weights(rng, m, 128)
+    kv, ik, iks, st_lat, st_idx = C.append_tokens(x_lat, x_idx, w_lat, w_idx, m)
+    wkv, wik, wiks = C.cache_write(x_lat, x_idx, w_lat, w_idx, m)
+    assert kv.shape == (T // m, 288) and np.array_equal(kv, wkv)
+    assert np.array_equal(ik, wik) and np.array_equal(iks, wiks)
+    E = T // m
+    assert np.array_equal(st_lat, x_lat[E * m:]) and np.array_equal(st_idx, x_idx[E * m:])
