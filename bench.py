@@ -15,9 +15,12 @@ step's stream; the whole step is timed with events around K steps.
 
 The same run also times the cache write on its own workload (8 sequences of
 131072 tokens merged at ratio 2, the write128k configuration) and reports it
-beside the step as "cache_write", and the decode-time append of one token for
+beside the step as "cache_write", the decode-time append of one token for
 each of the 32 sequences (ratio 2: every other call completes a group and
-packs 32 entries) as "append".
+packs 32 entries) as "append", and the sliding-window branch at the step's
+shape (the window write of one token per sequence; the attention over 128
+window tokens merged into the sparse result) as "swa". Neither is part of
+the timed step, which is the one Full layer the metric is quoted on.
 
 `traffic` in the roofline object is the HBM traffic of one scoring launch from
 rocprofv3 FETCH_SIZE and WRITE_SIZE counters, each scaled by what the same
@@ -55,7 +58,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle timing budget")
-    ap.add_argument("--no-cache-write", action="store_true", help="skip the cache-write leg")
+    ap.add_argument("--no-cache-write", action="store_true",
+                    help="skip the legs beside the step (cache write, window, append)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of 1 GiB five times (counter calibration)")
     return ap.parse_args()
@@ -159,6 +163,44 @@ def append_leg(L, synth, torch):
     return {"workload": f"append: one token for each of {B} sequences per call, ratio {m} (every other call "
                         f"packs {B} entries)", "bound": "latency", "avg_call_us": us, "calls": n,
             "bytes_per_call": pair_bytes / 2}
+
+
+def swa_leg(L, synth, torch, w):
+    """Sliding window at the decode128k shape: 32 sequences, 64 heads, 128 window tokens.
+
+    Times the window write of one token per sequence and the window attention
+    merged into a sparse result, each back to back behind a long first kernel.
+    """
+    import numpy as np
+    rng = np.random.default_rng(20261211)
+    B, H = w.B, w.H
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    win = torch.zeros((B, 128, 544), dtype=torch.uint8, device="cuda")
+    L.swa_write(d(synth.hidden_host(rng, (B, 128, 512)).view(np.int16)), d(np.zeros(B, np.int64)), win)
+    toks = d(synth.hidden_host(rng, (B, 1, 512)).view(np.int16))
+    q = d(np.stack([synth.latent_query(rng, H) for _ in range(B)]).view(np.int16))
+    n_win = d(np.full(B, 128, np.int32))
+    out = torch.zeros((B, H, 512), dtype=torch.float32, device="cuda")
+    lse = torch.full((B, H), float("-inf"), dtype=torch.float32, device="cuda")
+    pos = d(np.full(B, 128, np.int64))
+
+    def timed(fn, n=100):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(100_000_000)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return 1e3 * e0.elapsed_time(e1) / n
+
+    write_us = timed(lambda: L.swa_write(toks, pos, win))
+    attn_us = timed(lambda: L.swa_attention(win, n_win, q, out, lse))
+    return {"workload": f"window of 128 FP8 tokens for each of {B} sequences, {H} heads, merged into the "
+                        f"sparse result", "bound": "latency", "write_one_token_us": write_us,
+            "attention_us": attn_us, "window_bytes_read": B * 128 * 544}
 
 
 def log(msg):
@@ -325,6 +367,9 @@ def main():
         log(f"cache write {res['cache_write']['avg_launch_us']:.1f} us "
             f"({res['cache_write']['achieved']:.0f} GB/s)")
     if not a.no_cache_write:
+        log("sliding-window leg")
+        res["swa"] = swa_leg(L, synth, torch, w)
+        log(f"window attention {res['swa']['attention_us']:.2f} us")
         log("append leg")
         res["append"] = append_leg(L, synth, torch)
         log(f"append {res['append']['avg_call_us']:.2f} us per call")

@@ -146,6 +146,40 @@ int csa2_cache_append(const uint16_t* x_lat, const uint16_t* x_idx,
                       uint8_t* kv, uint8_t* ik, uint8_t* iks, int32_t* dropped, void* stream);
 
 /*
+ * Sliding-window cache ([FP4] section "La contrepartie : la fenêtre glissante":
+ * each layer keeps a window in FP8 of 512 + 512/16 bytes per token; [CS] section
+ * "L'architecture : trois leviers contre le cache": 128 tokens).
+ *
+ *   x_lat   bf16 [B][T][512]   latent rows of tokens pos0[b] .. pos0[b] + T - 1
+ *   pos0    i64 [B]            position of each sequence's first row here
+ *   win     u8 [B][128][544]   in/out: the ring; token t lives in row t mod 128 as 512
+ *                              E4M3FN values (channel c at byte c) then 32 E8M0 scale
+ *                              bytes (block b = channels 16b..16b+15)
+ * Only the last min(T, 128) rows of each sequence are written (earlier ones would
+ * be overwritten in the ring). Block scale: the smallest power of two 2^X with
+ * amax <= 448 * 2^X (byte X + 127, clamped to [0, 254]; byte 0 and zero values
+ * for an all-zero block); values: E4M3FN nearest-even of x * 2^-X with the sign
+ * of x, so no value saturates. Values below 2^-110 in magnitude may flush to zero.
+ * Errors: NULL pointer, B < 1, T < 0, misalignment (16 bytes).
+ */
+int csa2_swa_write(const uint16_t* x_lat, int B, int64_t T, const int64_t* pos0, uint8_t* win, void* stream);
+
+/*
+ * Attention over the window, merged with the sparse branch's result already in
+ * out / lse (one softmax over the union of the selected entries and the window):
+ * o = (e^lse o + e^lse_w o_w) / (e^lse + e^lse_w), lse = log(e^lse + e^lse_w).
+ *
+ *   win     the ring (see csa2_swa_write); n_win i32 [B]: valid rows 0 .. n_win[b]-1
+ *           (min(tokens written, 128)); values outside [0, 128] are clamped
+ *   q       bf16 [B][H][512], softmax_scale tau: as in csa2_sparse_attention
+ *   out     f32 [B][H][512] in/out; lse f32 [B][H] in/out (-inf: no sparse entry)
+ * Needs no workspace. Errors: NULL pointer, B < 1 or B > CSA2_MAX_BATCH, H outside
+ * [1, CSA2_MAX_HEADS], misalignment (16 bytes).
+ */
+int csa2_swa_attention(const uint8_t* win, const int32_t* n_win, const uint16_t* q, int B, int H,
+                       float softmax_scale, float* out, float* lse, void* stream);
+
+/*
  * Indexer pass and top-k ([FP4] section "Les ingrédients": the indexer key scores
  * positions; [CS] section "L'architecture : trois leviers contre le cache": new
  * top-512 per Full layer, hierarchical pool of at most 16384 candidates; [F24]

@@ -42,6 +42,10 @@ def lib():
     L.csa2_cache_write.restype = i32
     L.csa2_cache_append.argtypes = [vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, vp]
     L.csa2_cache_append.restype = i32
+    L.csa2_swa_write.argtypes = [vp, i32, i64, vp, vp, vp]
+    L.csa2_swa_write.restype = i32
+    L.csa2_swa_attention.argtypes = [vp, vp, vp, i32, i32, f32, vp, vp, vp]
+    L.csa2_swa_attention.restype = i32
     L.csa2_indexer_workspace_bytes.argtypes = [i32, i64, i32]
     L.csa2_indexer_workspace_bytes.restype = sz
     L.csa2_indexer_topk.argtypes = [vp, vp, vp, vp, i32, i64, vp, vp, i32, i32, vp, i32, i32, vp, i32, vp,
@@ -187,6 +191,45 @@ def cache_append(x_lat, x_idx, w_lat, w_idx, m, stage_lat, stage_idx, stage_coun
                                    _ptr(iks, torch.uint8, "iks"), _ptr(dropped, torch.int32, "dropped"),
                                    _stream(stream)))
     return dropped
+
+
+SWA_WINDOW = 128
+SWA_ROW_BYTES = 544
+
+
+def swa_write(x_lat, pos0, win=None, stream=None):
+    """Write tokens pos0[b] .. pos0[b]+T-1 (x_lat [B,T,512] bf16 bits) into the window ring.
+
+    win: [B, 128, 544] u8 (created zeroed when None). Returns win.
+    """
+    torch = _torch()
+    if x_lat.dim() == 2:
+        x_lat = x_lat[:, None]
+    B, T, C = x_lat.shape
+    if C != 512 or pos0.shape[0] != B:
+        raise ValueError("x_lat must be [B,T,512] and pos0 [B]")
+    if win is None:
+        win = torch.zeros((B, SWA_WINDOW, SWA_ROW_BYTES), dtype=torch.uint8, device=x_lat.device)
+    if tuple(win.shape) != (B, SWA_WINDOW, SWA_ROW_BYTES):
+        raise ValueError("win must be [B,128,544]")
+    _check(lib().csa2_swa_write(_ptr(x_lat, _bf16_types(), "x_lat"), B, T, _ptr(pos0, torch.int64, "pos0"),
+                                _ptr(win, torch.uint8, "win"), _stream(stream)))
+    return win
+
+
+def swa_attention(win, n_win, q, out, lse, softmax_scale=1.0, stream=None):
+    """Attend over the window and merge into the sparse branch's out [B,H,512] / lse [B,H] in place."""
+    torch = _torch()
+    B, H, _ = q.shape
+    if tuple(win.shape) != (B, SWA_WINDOW, SWA_ROW_BYTES) or n_win.shape[0] != B:
+        raise ValueError("win must be [B,128,544] and n_win [B]")
+    if tuple(out.shape) != (B, H, 512) or tuple(lse.shape) != (B, H):
+        raise ValueError("out must be [B,H,512] and lse [B,H]")
+    _check(lib().csa2_swa_attention(_ptr(win, torch.uint8, "win"), _ptr(n_win, torch.int32, "n_win"),
+                                    _ptr(q, _bf16_types(), "q"), B, H, float(softmax_scale),
+                                    _ptr(out, torch.float32, "out"), _ptr(lse, torch.float32, "lse"),
+                                    _stream(stream)))
+    return out, lse
 
 
 def indexer_topk(ik, iks, entry_offset, n_entries, max_n, q_idx, w=None, score_mode=CSA2_SCORE_RELU_W,

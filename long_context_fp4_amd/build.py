@@ -7,7 +7,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libcsa2fp4.so")
-SOURCES = ["abi.hip", "cache_write.hip", "indexer.hip", "attention.hip"]
+SOURCES = ["abi.hip", "cache_write.hip", "indexer.hip", "attention.hip", "swa.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

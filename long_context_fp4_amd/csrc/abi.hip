@@ -281,6 +281,28 @@ int csa2_cache_append(const uint16_t* x_lat, const uint16_t* x_idx, const float*
   return hip_status(e, "cache_append");
 }
 
+int csa2_swa_write(const uint16_t* x_lat, int B, int64_t T, const int64_t* pos0, uint8_t* win, void* stream) {
+  if (!x_lat || !pos0 || !win) return fail(CSA2_ERR_NULL, "swa_write: a required pointer is NULL");
+  if (B < 1) return fail(CSA2_ERR_SHAPE, "swa_write: B must be >= 1 (got %d)", B);
+  if (T < 0) return fail(CSA2_ERR_SHAPE, "swa_write: T must be >= 0");
+  if (!aligned16(x_lat) || !aligned16(pos0) || !aligned16(win))
+    return fail(CSA2_ERR_ALIGN, "swa_write: data pointers must be 16-byte aligned");
+  return hip_status(csa2::launch_swa_write(x_lat, B, T, pos0, win, (hipStream_t)stream), "swa_write");
+}
+
+int csa2_swa_attention(const uint8_t* win, const int32_t* n_win, const uint16_t* q, int B, int H,
+                       float softmax_scale, float* out, float* lse, void* stream) {
+  if (!win || !n_win || !q || !out || !lse) return fail(CSA2_ERR_NULL, "swa_attention: a required pointer is NULL");
+  if (B < 1 || B > CSA2_MAX_BATCH)
+    return fail(CSA2_ERR_SHAPE, "swa_attention: B must be in [1, %d] (got %d)", CSA2_MAX_BATCH, B);
+  if (H < 1 || H > CSA2_MAX_HEADS)
+    return fail(CSA2_ERR_SHAPE, "swa_attention: H must be in [1, %d] (got %d)", CSA2_MAX_HEADS, H);
+  if (!aligned16(win) || !aligned16(n_win) || !aligned16(q) || !aligned16(out) || !aligned16(lse))
+    return fail(CSA2_ERR_ALIGN, "swa_attention: data pointers must be 16-byte aligned");
+  return hip_status(csa2::launch_swa_attention(win, n_win, q, B, H, softmax_scale, out, lse, (hipStream_t)stream),
+                    "swa_attention");
+}
+
 size_t csa2_indexer_workspace_bytes(int B, int64_t max_n, int cand_stride) {
   if (B < 1 || B > CSA2_MAX_BATCH || max_n < 0 || cand_stride < 0) return 0;
   return indexer_layout(B, max_n, cand_stride).total;

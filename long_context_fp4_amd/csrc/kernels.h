@@ -28,6 +28,13 @@ __host__ __device__ inline uint32_t* ctrl_hist(uint8_t* ctrl, int b) { return (u
 hipError_t launch_cache_write(const uint16_t* x_lat, const uint16_t* x_idx, const float* w_lat,
                               const float* w_idx, int B, int64_t T, int m, uint8_t* kv, uint8_t* ik,
                               uint8_t* iks, hipStream_t stream);
+// Sliding window: 128 tokens per sequence, 544-byte FP8 rows.
+constexpr int kSwaWindow = 128;
+constexpr int kSwaRowBytes = 544;
+hipError_t launch_swa_write(const uint16_t* x, int B, int64_t T, const int64_t* pos0, uint8_t* win,
+                            hipStream_t stream);
+hipError_t launch_swa_attention(const uint8_t* win, const int32_t* n_win, const uint16_t* q, int B, int H,
+                                float tau, float* out, float* lse, hipStream_t stream);
 hipError_t launch_cache_append(const uint16_t* x_lat, const uint16_t* x_idx, const float* w_lat,
                                const float* w_idx, int B, int m, uint16_t* st_lat, uint16_t* st_idx,
                                int32_t* st_count, const int64_t* entry_offset, int32_t* n_entries,

@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_header_declares_the_api():
     names = declared_functions()
-    for n in ("csa2_cache_write", "csa2_cache_append", "csa2_indexer_topk", "csa2_sparse_attention", "csa2_decode_layer",
+    for n in ("csa2_cache_write", "csa2_cache_append", "csa2_swa_write", "csa2_swa_attention", "csa2_indexer_topk", "csa2_sparse_attention", "csa2_decode_layer",
               "csa2_indexer_workspace_bytes", "csa2_attention_workspace_bytes", "csa2_decode_workspace_bytes",
               "csa2_bytes_per_token", "csa2_last_error"):
         assert n in names
@@ -70,6 +70,19 @@ def test_cache_append_validation(L):
     assert call(iks=P + 2) == -3          # 4-byte alignment
     assert call(sc=P + 2) == -3
     assert call(dr=P + 2) == -3
+    assert "aligned" in err(L)
+
+
+def test_swa_validation(L):
+    assert L.csa2_swa_write(None, 1, 10, P, P, None) == -1
+    assert L.csa2_swa_write(P, 0, 10, P, P, None) == -2
+    assert L.csa2_swa_write(P, 1, -1, P, P, None) == -2
+    assert L.csa2_swa_write(P, 1, 10, P, P + 8, None) == -3
+    assert L.csa2_swa_attention(P, None, P, 1, 8, 1.0, P, P, None) == -1
+    assert L.csa2_swa_attention(P, P, P, 0, 8, 1.0, P, P, None) == -2
+    assert L.csa2_swa_attention(P, P, P, 1025, 8, 1.0, P, P, None) == -2
+    assert L.csa2_swa_attention(P, P, P, 1, 129, 1.0, P, P, None) == -2
+    assert L.csa2_swa_attention(P, P, P, 1, 8, 1.0, P, P + 4, None) == -3
     assert "aligned" in err(L)
 
 
