@@ -19,8 +19,9 @@ beside the step as "cache_write", the decode-time append of one token for
 each of the 32 sequences (ratio 2: every other call completes a group and
 packs 32 entries) as "append", and the sliding-window branch at the step's
 shape (the window write of one token per sequence; the attention over 128
-window tokens merged into the sparse result) as "swa". Neither is part of
-the timed step, which is the one Full layer the metric is quoted on.
+window tokens merged into the sparse result) as "swa", and a multi-query
+prefill of 32 query tokens of one sequence as "prefill". None of these is
+part of the timed step, which is the one Full layer the metric is quoted on.
 
 `traffic` in the roofline object is the HBM traffic of one scoring launch from
 rocprofv3 FETCH_SIZE and WRITE_SIZE counters, each scaled by what the same
@@ -59,7 +60,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle timing budget")
     ap.add_argument("--no-cache-write", action="store_true",
-                    help="skip the legs beside the step (cache write, window, append)")
+                    help="skip the legs beside the step (prefill, cache write, window, append)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of 1 GiB five times (counter calibration)")
     return ap.parse_args()
@@ -201,6 +202,36 @@ def swa_leg(L, synth, torch, w):
     return {"workload": f"window of 128 FP8 tokens for each of {B} sequences, {H} heads, merged into the "
                         f"sparse result", "bound": "latency", "write_one_token_us": write_us,
             "attention_us": attn_us, "window_bytes_read": B * 128 * 544}
+
+
+def prefill_leg(L, synth, torch, w, p, kv, ik, iks):
+    """Multi-query prefill on the decode128k cache: 32 query tokens of one sequence
+    (its last 32 positions), each with its causal top-512 and attention."""
+    import numpy as np
+    E = w.T // w.m
+    Tq = 32
+    rng = np.random.default_rng(20261212)
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    pos = d(np.arange(w.T - Tq, w.T, dtype=np.int64)[None])
+    q = d(np.stack([synth.latent_query(rng, w.H) for _ in range(Tq)])[None].view(np.int16))
+    qi = d(np.stack([synth.indexer_query(rng, w.Hi) for _ in range(Tq)])[None].view(np.int16))
+    wh = d(np.stack([synth.head_weights(rng, w.Hi) for _ in range(Tq)])[None])
+    off, nb = d(np.zeros(1, np.int64)), d(np.full(1, E, np.int32))
+    ws = L.Workspace()
+    call = lambda: L.prefill_layer(kv, ik, iks, off, nb, E, w.m, pos, qi, q, w=wh, k=w.k, workspace=ws)
+    call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = 20
+    e0.record()
+    for _ in range(n):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    us = 1e3 * e0.elapsed_time(e1) / n
+    return {"workload": f"prefill: {Tq} query tokens of one 131072-token sequence (65536 entries), each with "
+                        f"its causal top-{w.k} and {w.H}-head attention", "avg_call_us": us,
+            "query_tokens_per_s": Tq / (us * 1e-6)}
 
 
 def log(msg):
@@ -359,6 +390,10 @@ def main():
     }
     log(f"step {total_ms / a.steps * 1e3:.1f} us, scoring kernel {score_avg_us:.1f} us "
         f"({achieved:.0f} GB/s), {qtok_s:.0f} query-tokens/s")
+    if not a.no_cache_write:
+        log("prefill leg")
+        res["prefill"] = prefill_leg(L, synth, torch, w, p, kv, ik, iks)
+        log(f"prefill {res['prefill']['avg_call_us']:.1f} us for 32 query tokens")
     del copies, kv, ik, iks
     torch.cuda.empty_cache()
     if not a.no_cache_write:

@@ -268,6 +268,33 @@ int csa2_decode_layer(int mode,
                       void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * Multi-query (prefill) sparse attention over the same cache: Tq query tokens
+ * per sequence, each with its own indexer query and its own causal top-k (the
+ * layer mode Full of [CS] section "L'architecture : trois leviers contre le
+ * cache", applied to every query token). Query t of sequence b, at token
+ * position pos[b][t], sees the entries its token has completed: the first
+ * min(n_entries[b], floor((pos + 1) / m)) of the sequence ([FP4] section "Le
+ * compte par couche": one entry per m tokens; the rest is in the window).
+ *
+ *   pos      i64 [B][Tq] token positions (negative: no entry visible)
+ *   q_idx    bf16 [B][Tq][Hi][128], w f32 [B][Tq][Hi] or NULL: indexer queries
+ *   q        bf16 [B][Tq][H][512]: attention queries
+ *   topk     out i32 [B][Tq][k]; out f32 [B][Tq][H][512]; lse f32 [B][Tq][H] or NULL
+ * The other arguments mean what they mean in csa2_decode_layer (CSA2_FULL, no
+ * pool). The queries run as one decode batch of B * Tq sequences sharing the
+ * cache rows, so 1 <= B * Tq <= CSA2_MAX_BATCH.
+ * workspace: csa2_prefill_workspace_bytes(B, Tq, max_n, H, k) bytes.
+ */
+size_t csa2_prefill_workspace_bytes(int B, int Tq, int64_t max_n, int H, int k);
+int csa2_prefill_layer(const uint8_t* kv, const uint8_t* ik, const uint8_t* iks,
+                       const int64_t* entry_offset, const int32_t* n_entries, int B, int64_t max_n,
+                       int m, int Tq, const int64_t* pos,
+                       const uint16_t* q_idx, const float* w, int Hi, int score_mode,
+                       const uint16_t* q, int H, float softmax_scale, int k,
+                       int32_t* topk, float* out, float* lse,
+                       void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * Host-only byte accounting ([FP4] sections "Le coût d'une entrée" and "Le
  * compte par couche"): sum over layers of (entry bytes of the latent + entry
  * bytes of the key) / ratio, where an entry of ch channels with block blk and

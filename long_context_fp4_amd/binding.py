@@ -42,6 +42,11 @@ def lib():
     L.csa2_cache_write.restype = i32
     L.csa2_cache_append.argtypes = [vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, vp]
     L.csa2_cache_append.restype = i32
+    L.csa2_prefill_workspace_bytes.argtypes = [i32, i32, i64, i32, i32]
+    L.csa2_prefill_workspace_bytes.restype = sz
+    L.csa2_prefill_layer.argtypes = [vp, vp, vp, vp, vp, i32, i64, i32, i32, vp, vp, vp, i32, i32, vp, i32, f32, i32,
+                                     vp, vp, vp, vp, sz, vp]
+    L.csa2_prefill_layer.restype = i32
     L.csa2_swa_write.argtypes = [vp, i32, i64, vp, vp, vp]
     L.csa2_swa_write.restype = i32
     L.csa2_swa_attention.argtypes = [vp, vp, vp, i32, i32, f32, vp, vp, vp]
@@ -230,6 +235,39 @@ def swa_attention(win, n_win, q, out, lse, softmax_scale=1.0, stream=None):
                                     _ptr(out, torch.float32, "out"), _ptr(lse, torch.float32, "lse"),
                                     _stream(stream)))
     return out, lse
+
+
+def prefill_layer(kv, ik, iks, entry_offset, n_entries, max_n, m, pos, q_idx, q, w=None,
+                  score_mode=CSA2_SCORE_RELU_W, softmax_scale=1.0, k=512, workspace=None, topk=None, out=None,
+                  lse=None, stream=None):
+    """Tq query tokens per sequence, each with its causal top-k and attention.
+
+    pos [B,Tq] i64, q_idx [B,Tq,Hi,128], w [B,Tq,Hi] or None, q [B,Tq,H,512] (bf16 bits).
+    Returns (topk [B,Tq,k] i32, out [B,Tq,H,512] f32, lse [B,Tq,H] f32).
+    """
+    torch = _torch()
+    B, Tq, H, D = q.shape
+    Hi = q_idx.shape[2]
+    if D != 512 or tuple(pos.shape) != (B, Tq) or tuple(q_idx.shape) != (B, Tq, Hi, 128):
+        raise ValueError("q must be [B,Tq,H,512], pos [B,Tq] and q_idx [B,Tq,Hi,128]")
+    if w is not None and tuple(w.shape) != (B, Tq, Hi):
+        raise ValueError("w must be [B,Tq,Hi]")
+    dev = q.device
+    topk = torch.empty((B, Tq, k), dtype=torch.int32, device=dev) if topk is None else topk
+    out = torch.empty((B, Tq, H, 512), dtype=torch.float32, device=dev) if out is None else out
+    lse = torch.empty((B, Tq, H), dtype=torch.float32, device=dev) if lse is None else lse
+    nbytes = lib().csa2_prefill_workspace_bytes(B, Tq, int(max_n), H, k)
+    buf = _ws(workspace, dev).get(nbytes)
+    bt = _bf16_types()
+    _check(lib().csa2_prefill_layer(_ptr(kv, torch.uint8, "kv"), _ptr(ik, torch.uint8, "ik"),
+                                    _ptr(iks, torch.uint8, "iks"), _ptr(entry_offset, torch.int64, "entry_offset"),
+                                    _ptr(n_entries, torch.int32, "n_entries"), B, int(max_n), m, Tq,
+                                    _ptr(pos, torch.int64, "pos"), _ptr(q_idx, bt, "q_idx"),
+                                    _ptr(w, torch.float32, "w"), Hi, score_mode, _ptr(q, bt, "q"), H,
+                                    float(softmax_scale), k, _ptr(topk, torch.int32, "topk"),
+                                    _ptr(out, torch.float32, "out"), _ptr(lse, torch.float32, "lse"),
+                                    _ptr(buf, torch.uint8, "workspace"), buf.numel(), _stream(stream)))
+    return topk, out, lse
 
 
 def indexer_topk(ik, iks, entry_offset, n_entries, max_n, q_idx, w=None, score_mode=CSA2_SCORE_RELU_W,

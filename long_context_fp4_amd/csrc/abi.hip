@@ -416,6 +416,43 @@ int csa2_decode_layer(int mode, const uint8_t* kv, const uint8_t* ik, const uint
   return hip_status(e, "decode_layer attention");
 }
 
+size_t csa2_prefill_workspace_bytes(int B, int Tq, int64_t max_n, int H, int k) {
+  if (B < 1 || Tq < 1 || (int64_t)B * Tq > CSA2_MAX_BATCH) return 0;
+  const int Bv = B * Tq;
+  const size_t d = csa2_decode_workspace_bytes(Bv, max_n, H, k, 0);
+  if (d == 0) return 0;
+  return d + round_up((size_t)Bv * 8, 256) + round_up((size_t)Bv * 4, 256);
+}
+
+int csa2_prefill_layer(const uint8_t* kv, const uint8_t* ik, const uint8_t* iks, const int64_t* entry_offset,
+                       const int32_t* n_entries, int B, int64_t max_n, int m, int Tq, const int64_t* pos,
+                       const uint16_t* q_idx, const float* w, int Hi, int score_mode, const uint16_t* q, int H,
+                       float softmax_scale, int k, int32_t* topk, float* out, float* lse, void* workspace,
+                       size_t ws_bytes, void* stream) {
+  if (!pos || !entry_offset || !n_entries) return fail(CSA2_ERR_NULL, "prefill_layer: a required pointer is NULL");
+  if (B < 1 || Tq < 1 || (int64_t)B * Tq > CSA2_MAX_BATCH)
+    return fail(CSA2_ERR_SHAPE, "prefill_layer: need B >= 1, Tq >= 1 and B * Tq <= %d (got %d x %d)", CSA2_MAX_BATCH,
+                B, Tq);
+  if (m < 1 || m > CSA2_MAX_RATIO)
+    return fail(CSA2_ERR_SHAPE, "prefill_layer: m must be in [1, %d] (got %d)", CSA2_MAX_RATIO, m);
+  if (!aligned16(pos) || !aligned16(entry_offset) || !aligned16(n_entries))
+    return fail(CSA2_ERR_ALIGN, "prefill_layer: data pointers must be 16-byte aligned");
+  const int Bv = B * Tq;
+  const size_t dneed = csa2_decode_workspace_bytes(Bv, max_n, H, k, 0);
+  const size_t need = csa2_prefill_workspace_bytes(B, Tq, max_n, H, k);
+  if (dneed == 0 || need == 0) return fail(CSA2_ERR_SHAPE, "prefill_layer: bad sizes (max_n, H or k)");
+  if (!workspace || ws_bytes < need)
+    return fail(CSA2_ERR_WORKSPACE, "prefill_layer: workspace needs %zu bytes (got %zu)", need, workspace ? ws_bytes : 0);
+  if (!aligned16(workspace)) return fail(CSA2_ERR_ALIGN, "prefill_layer: workspace must be 16-byte aligned");
+  uint8_t* views = (uint8_t*)workspace + dneed;
+  int64_t* eo = (int64_t*)views;
+  int32_t* ne = (int32_t*)(views + round_up((size_t)Bv * 8, 256));
+  hipError_t e = csa2::launch_prefill_views(entry_offset, n_entries, pos, m, B, Tq, eo, ne, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_status(e, "prefill_layer views");
+  return csa2_decode_layer(CSA2_FULL, kv, ik, iks, eo, ne, Bv, max_n, q_idx, w, Hi, score_mode, q, H, softmax_scale,
+                           k, 0, nullptr, topk, out, lse, workspace, dneed, stream);
+}
+
 double csa2_bytes_per_token(const int* ratios, int n_layers, int lat_ch, int lat_blk, int lat_sbytes, int idx_ch,
                             int idx_blk, int idx_sbytes) {
   if (!ratios || n_layers < 0 || lat_ch < 0 || idx_ch < 0 || lat_blk < 0 || idx_blk < 0 || lat_sbytes < 0 ||

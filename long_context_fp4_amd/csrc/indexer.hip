@@ -692,6 +692,31 @@ __global__ __launch_bounds__(SMALL_THREADS) void select_small_kernel(
   compact_bitmap(selbm, nslots, sp, K, ob, scan_tmp, keys, SMALL_MAX);
 }
 
+// ---------------------------------------------------------------- prefill views
+// Query t of sequence b becomes sequence b * Tq + t of a decode batch: the same
+// cache rows, with the entries its token has completed visible, floor((pos + 1) / m)
+// of them (at most the sequence's n_entries).
+__global__ void prefill_views_kernel(const int64_t* __restrict__ entry_offset, const int32_t* __restrict__ n_entries,
+                                     const int64_t* __restrict__ pos, int m, int B, int Tq,
+                                     int64_t* __restrict__ eo, int32_t* __restrict__ ne) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= B * Tq) return;
+  const int b = i / Tq;
+  const int64_t p = pos[i];
+  const int64_t vis = p < 0 ? 0 : (p + 1) / m;
+  const int64_t n = n_entries[b];
+  eo[i] = entry_offset[b];
+  ne[i] = (int32_t)(vis < n ? vis : (n < 0 ? 0 : n));
+}
+
+hipError_t launch_prefill_views(const int64_t* entry_offset, const int32_t* n_entries, const int64_t* pos, int m,
+                                int B, int Tq, int64_t* eo, int32_t* ne, hipStream_t stream) {
+  const int n = B * Tq;
+  hipLaunchKernelGGL(prefill_views_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, entry_offset,
+                     n_entries, pos, m, B, Tq, eo, ne);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- launchers
 hipError_t launch_score(const uint8_t* ik, const uint8_t* iks, const int64_t* entry_offset,
                         const int32_t* n_entries, int B, int64_t max_n, const uint16_t* q_idx,

@@ -28,6 +28,10 @@ __host__ __device__ inline uint32_t* ctrl_hist(uint8_t* ctrl, int b) { return (u
 hipError_t launch_cache_write(const uint16_t* x_lat, const uint16_t* x_idx, const float* w_lat,
                               const float* w_idx, int B, int64_t T, int m, uint8_t* kv, uint8_t* ik,
                               uint8_t* iks, hipStream_t stream);
+// Prefill: the decode batch of B * Tq per-query views of B sequences.
+hipError_t launch_prefill_views(const int64_t* entry_offset, const int32_t* n_entries, const int64_t* pos, int m,
+                                int B, int Tq, int64_t* eo, int32_t* ne, hipStream_t stream);
+
 // Sliding window: 128 tokens per sequence, 544-byte FP8 rows.
 constexpr int kSwaWindow = 128;
 constexpr int kSwaRowBytes = 544;

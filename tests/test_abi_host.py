@@ -25,7 +25,8 @@ def declared_functions():
 
 def test_header_declares_the_api():
     names = declared_functions()
-    for n in ("csa2_cache_write", "csa2_cache_append", "csa2_swa_write", "csa2_swa_attention", "csa2_indexer_topk", "csa2_sparse_attention", "csa2_decode_layer",
+    for n in ("csa2_cache_write", "csa2_cache_append", "csa2_swa_write", "csa2_swa_attention", "csa2_prefill_layer",
+              "csa2_prefill_workspace_bytes", "csa2_indexer_topk", "csa2_sparse_attention", "csa2_decode_layer",
               "csa2_indexer_workspace_bytes", "csa2_attention_workspace_bytes", "csa2_decode_workspace_bytes",
               "csa2_bytes_per_token", "csa2_last_error"):
         assert n in names
@@ -84,6 +85,21 @@ def test_swa_validation(L):
     assert L.csa2_swa_attention(P, P, P, 1, 129, 1.0, P, P, None) == -2
     assert L.csa2_swa_attention(P, P, P, 1, 8, 1.0, P, P + 4, None) == -3
     assert "aligned" in err(L)
+
+
+def test_prefill_validation(L):
+    def call(**kw):
+        a = dict(B=2, m=2, Tq=4, pos=P, ws=P, wsb=1 << 30)
+        a.update(kw)
+        return L.csa2_prefill_layer(P, P, P, P, P, a["B"], 1000, a["m"], a["Tq"], a["pos"], P, P, 16, 1, P, 64,
+                                    1.0, 512, P, P, P, a["ws"], a["wsb"], None)
+    assert call(pos=None) == -1
+    assert call(B=0) == -2 and call(Tq=0) == -2 and call(B=2, Tq=513) == -2
+    assert call(m=0) == -2 and call(m=17) == -2
+    assert call(pos=P + 8) == -3
+    assert call(wsb=16) == -4
+    assert L.csa2_prefill_workspace_bytes(2, 4, 1000, 64, 512) > L.csa2_decode_workspace_bytes(8, 1000, 64, 512, 0)
+    assert L.csa2_prefill_workspace_bytes(2, 513, 1000, 64, 512) == 0
 
 
 def idx_call(L, **kw):
