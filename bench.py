@@ -20,8 +20,11 @@ each of the 32 sequences (ratio 2: every other call completes a group and
 packs 32 entries) as "append", and the sliding-window branch at the step's
 shape (the window write of one token per sequence; the attention over 128
 window tokens merged into the sparse result) as "swa", and a multi-query
-prefill of 32 query tokens of one sequence as "prefill". None of these is
-part of the timed step, which is the one Full layer the metric is quoted on.
+prefill of 32 query tokens of one sequence as "prefill", and the same step
+with the quantized-query scoring variant (MXFP8 queries, block-scaled MFMA;
+its scores differ from the exact ones) as "score_qmx8". None of these is part
+of the timed step, which is the one Full layer the metric is quoted on, scored
+exactly.
 
 `traffic` in the roofline object is the HBM traffic of one scoring launch from
 rocprofv3 FETCH_SIZE and WRITE_SIZE counters, each scaled by what the same
@@ -60,7 +63,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle timing budget")
     ap.add_argument("--no-cache-write", action="store_true",
-                    help="skip the legs beside the step (prefill, cache write, window, append)")
+                    help="skip the legs beside the step (quantized-query scoring, prefill, cache write, window, append)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of 1 GiB five times (counter calibration)")
     return ap.parse_args()
@@ -323,12 +326,32 @@ def main():
     out = torch.empty((w.B, w.H, 512), dtype=torch.float32, device="cuda")
     lse = torch.empty((w.B, w.H), dtype=torch.float32, device="cuda")
 
-    def step(i, evs=None):
+    def step(i, evs=None, score_mode=L.CSA2_SCORE_RELU_W):
         c = copies[i % COPIES]
         if evs is not None:
             L.set_profile_events(*evs)
         L.decode_layer(L.CSA2_FULL, c[0], c[1], c[2], off, nb, E, q, q_idx=q_idx, w=wh, k=w.k,
-                       topk=topk, out=out, lse=lse, workspace=ws)
+                       score_mode=score_mode, topk=topk, out=out, lse=lse, workspace=ws)
+
+    def timed_steps(score_mode):
+        """(ms per step over K steps, average scoring-launch time in us)."""
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(a.steps):
+            step(i, score_mode=score_mode)
+        e1.record()
+        torch.cuda.synchronize()
+        pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for _ in range(a.steps)]
+        for x, y in pairs:
+            x.record()
+            y.record()
+        torch.cuda.synchronize()
+        for i in range(a.steps):
+            step(i, pairs[i], score_mode=score_mode)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / a.steps, 1e3 * float(np.mean([x.elapsed_time(y) for x, y in pairs]))
 
     log(f"warmup {a.warmup}")
     for i in range(a.warmup):
@@ -391,6 +414,17 @@ def main():
     log(f"step {total_ms / a.steps * 1e3:.1f} us, scoring kernel {score_avg_us:.1f} us "
         f"({achieved:.0f} GB/s), {qtok_s:.0f} query-tokens/s")
     if not a.no_cache_write:
+        log("quantized-query scoring leg")
+        qmode = L.CSA2_SCORE_RELU_W | L.CSA2_SCORE_QMX8
+        for i in range(a.warmup):
+            step(i, score_mode=qmode)
+        ms, sus = timed_steps(qmode)
+        res["score_qmx8"] = {
+            "workload": "the same decode128k step with the quantized-query variant: MXFP8 indexer queries "
+                        "and one block-scaled FP8 x FP4 MFMA per 16 entries (not the exact path)",
+            "ms_per_step": ms, "query_tokens_per_s": w.B / (ms * 1e-3), "score_avg_launch_us": sus,
+            "score_achieved_gbs": idx_bytes / (sus * 1e-6) / 1e9}
+        log(f"quantized-query step {ms * 1e3:.1f} us, scoring {sus:.1f} us")
         log("prefill leg")
         res["prefill"] = prefill_leg(L, synth, torch, w, p, kv, ik, iks)
         log(f"prefill {res['prefill']['avg_call_us']:.1f} us for 32 query tokens")

@@ -55,6 +55,20 @@ extern "C" {
 /* indexer score definitions */
 #define CSA2_SCORE_DOT     0   /* S_i = q . k_i, exactly one indexer head */
 #define CSA2_SCORE_RELU_W  1   /* S_i = sum_h w_h * max(0, q_h . k_i) */
+/*
+ * Flag OR-ed into either score mode: the quantized-query variant. Each head's
+ * query is first converted to MXFP8 (per 32 channels an E8M0 scale 2^X with
+ * X = floor(log2 amax) - 8, clamped to [-127, 127], -127 for a zero block;
+ * values nearest-even E4M3FN of x * 2^-X, saturating at 448: the OCP MX rule
+ * the keys follow as "standard MXFP4", [FP4] section "Le coût d'une entrée"),
+ * and every 16 entries x 16 heads are contracted by one block-scaled FP8 x FP4
+ * matrix instruction that reads the cached keys as they are. The scores are
+ * those of the quantized query, up to that instruction's accumulation: within
+ * each group of 8 consecutive channels, product bits more than 13 binades
+ * below the group's largest product are dropped (toward zero). A faster
+ * variant, not the exact path.
+ */
+#define CSA2_SCORE_QMX8    0x100
 
 /* CSA2 layer modes ([CS] section "L'architecture : trois leviers contre le cache") */
 #define CSA2_FULL     0   /* own indexer pass over every entry, new top-k */
@@ -193,7 +207,8 @@ int csa2_swa_attention(const uint8_t* win, const int32_t* n_win, const uint16_t*
  *                  (rows at positions >= max_n are not scored)
  *   q_idx          bf16 [B][Hi][128] indexer queries; w f32 [B][Hi] head weights
  *                  (NULL = all 1; ignored by CSA2_SCORE_DOT)
- *   Hi, score_mode 1 <= Hi <= 16; CSA2_SCORE_DOT needs Hi == 1
+ *   Hi, score_mode 1 <= Hi <= 16; CSA2_SCORE_DOT needs Hi == 1; either mode may
+ *                  carry CSA2_SCORE_QMX8
  *   cand           i32 [B][cand_stride] or NULL. NULL: score every entry (Full).
  *                  Otherwise score only the listed positions (Reindex); entries
  *                  < 0 are skipped. cand_stride <= CSA2_MAX_POOL.

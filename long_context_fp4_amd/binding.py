@@ -12,6 +12,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 
 CSA2_OK = 0
 CSA2_SCORE_DOT, CSA2_SCORE_RELU_W = 0, 1
+CSA2_SCORE_QMX8 = 0x100          # flag: quantized-query (MXFP8) variant of either score
 CSA2_FULL, CSA2_REINDEX, CSA2_REUSE = 0, 1, 2
 MAIN_ROW_BYTES, INDEXER_CODE_BYTES, INDEXER_SCALE_BYTES = 288, 64, 4
 

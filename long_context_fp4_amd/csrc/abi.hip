@@ -7,6 +7,8 @@
 #include <stdio.h>
 #include <string.h>
 
+static_assert(CSA2_SCORE_QMX8 == csa2::kScoreQmx8, "score-mode flag differs between the header and the kernels");
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -91,9 +93,10 @@ int check_indexer_args(const uint8_t* ik, const uint8_t* iks, const int64_t* ent
     return fail(CSA2_ERR_SHAPE, "indexer: max_n must be in [0, 2^26] (got %lld)", (long long)max_n);
   if (Hi < 1 || Hi > CSA2_MAX_INDEXER_HEADS)
     return fail(CSA2_ERR_SHAPE, "indexer: Hi must be in [1, %d] (got %d)", CSA2_MAX_INDEXER_HEADS, Hi);
-  if (score_mode != CSA2_SCORE_DOT && score_mode != CSA2_SCORE_RELU_W)
+  const int base_mode = score_mode & ~CSA2_SCORE_QMX8;
+  if (base_mode != CSA2_SCORE_DOT && base_mode != CSA2_SCORE_RELU_W)
     return fail(CSA2_ERR_UNSUPPORTED, "indexer: unknown score_mode %d", score_mode);
-  if (score_mode == CSA2_SCORE_DOT && Hi != 1)
+  if (base_mode == CSA2_SCORE_DOT && Hi != 1)
     return fail(CSA2_ERR_SHAPE, "indexer: the DOT score takes exactly one head (got Hi=%d)", Hi);
   if (k < 1 || k > CSA2_MAX_K) return fail(CSA2_ERR_SHAPE, "indexer: k must be in [1, %d] (got %d)", CSA2_MAX_K, k);
   if (cand && (cand_stride < 1 || cand_stride > CSA2_MAX_POOL))

@@ -52,7 +52,7 @@
 
 namespace csa2 {
 
-constexpr int SC_THREADS = 256;
+constexpr int SC_THREADS = 256;   // also the threads that stage a quantized query
 
 constexpr int SC_SUB = 1;           // selection chunks per score workgroup
 constexpr int SC_SPAN = SC_SUB * SC_CHUNK;   // slots a score workgroup streams
@@ -110,10 +110,12 @@ __device__ void compact_bitmap(const uint32_t* bm, int64_t nbits, const int32_t*
 //      local cutoff summary, and for SEL_DIRECT the candidates, that
 //      finish_kernel turns into the threshold bin or the final top-K).
 // MODE: 0 = dot product of head 0, 1 = sum_h w_h * ReLU(q_h . k).
+// QMX: the query is quantized to MXFP8 in registers and each tile is one
+//      block-scaled FP8 x FP4 MFMA (the quantized-query variant).
 // A workgroup streams SC_SPAN slots (SC_SUB selection chunks of SC_CHUNK);
 // eight workgroups of four waves share a compute unit, each wave with
 // SC_UNROLL tiles in flight.
-template <bool CAND, int SEL, int MODE>
+template <bool CAND, int SEL, int MODE, bool QMX>
 __global__ __launch_bounds__(SC_THREADS) __attribute__((amdgpu_waves_per_eu(8))) void score_kernel(
     const uint8_t* __restrict__ ik, const uint8_t* __restrict__ iks,
     const int64_t* __restrict__ entry_offset, const int32_t* __restrict__ n_entries, int64_t max_n,
@@ -127,6 +129,7 @@ __global__ __launch_bounds__(SC_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
   __shared__ uint32_t ctl[8];
   __shared__ __attribute__((aligned(16))) float lw[16];   // head weights
   __shared__ SelBufs sbs;   // the workspace views, parked in LDS while the keys stream (frees SGPRs)
+  __shared__ __attribute__((aligned(16))) uint8_t lq[QMX ? QMX_LDS_BYTES : 16];   // the quantized query
   uint32_t* lhist = lbuf;
   float* lsc = (float*)(lbuf + NBINS / 2);
   auto hcount = [&](uint32_t bin) -> uint32_t { return (lhist[bin >> 1] >> ((bin & 1) * 16)) & 0xFFFFu; };
@@ -139,13 +142,17 @@ __global__ __launch_bounds__(SC_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
   const int32_t ne = n_entries[b];
   const int64_t row_base = entry_offset[b];
   asm volatile("" ::"s"(ne), "s"(row_base));   // both loads issued here, before any branch on them
-  // A operand: q[head = n][channels 32g + 8j .. +7] for MFMA j
+  // A operand: q[head = n][channels 32g + 8j .. +7] for MFMA j (the quantized
+  // variant builds its operand once the first keys are requested)
   bf16x8_t qa[4];
+  QueryMx qm;
+  if constexpr (!QMX) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    u32x4_t v = {0, 0, 0, 0};
-    if (n < Hi) v = *(const u32x4_t*)(q_idx + ((int64_t)b * Hi + n) * 128 + 32 * g + 8 * j);
-    __builtin_memcpy(&qa[j], &v, 16);
+    for (int j = 0; j < 4; ++j) {
+      u32x4_t v = {0, 0, 0, 0};
+      if (n < Hi) v = *(const u32x4_t*)(q_idx + ((int64_t)b * Hi + n) * 128 + 32 * g + 8 * j);
+      __builtin_memcpy(&qa[j], &v, 16);
+    }
   }
   // head weights of the output rows (lane group g takes heads 4g .. 4g+3), in
   // LDS and read per tile, which keeps the wave within 64 registers
@@ -173,6 +180,8 @@ __global__ __launch_bounds__(SC_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
     }
   }
 
+  if constexpr (QMX) query_mx_stage(q_idx + (int64_t)b * Hi * 128, Hi, lq, tid);
+
   if (SEL == SEL_THRESHOLD) {
     for (int i = tid; i < NBINS / 2; i += SC_THREADS) lhist[i] = 0;
   }
@@ -184,11 +193,13 @@ __global__ __launch_bounds__(SC_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
   if (tid < 16) lw[tid] = wv;
   if (SEL != SEL_NONE && tid == 0) sbs = sb;
   __syncthreads();
+  if constexpr (QMX) qm = query_mx_operand(lq, lane);
 
   // one tile = 16 slots x 16 heads: 4 MFMAs over the 128 channels; the head sum
   // goes to the lanes of group 0, which stage the score in LDS
   auto score_tile = [&](const u32x4_t cw, uint32_t sbyte) -> float {
-    return score_tile_fn<MODE>(qa, cw, sbyte, lw, g);
+    if constexpr (QMX) return score_tile_mx<MODE>(qm, cw, sbyte, lw, g);
+    else return score_tile_fn<MODE>(qa, cw, sbyte, lw, g);
   };
   // ---- per selection chunk (sub = 0 .. SC_SUB-1): store its scores, then the
   // local cutoff (every slot of a Full pass is a valid position). Chunk cix
@@ -728,20 +739,29 @@ hipError_t launch_score(const uint8_t* ik, const uint8_t* iks, const int64_t* en
   if (nslots <= 0) return hipSuccess;
   const int64_t nx = (nslots + SC_SPAN - 1) / SC_SPAN;
   dim3 grid((unsigned)nx, (unsigned)B), block(SC_THREADS);
-#define CSA2_SCORE_LAUNCH(C, S, Mo)                                                              \
-  hipLaunchKernelGGL((score_kernel<C, S, Mo>), grid, block, 0, stream, ik, iks, entry_offset,   \
+  const bool qmx = (mode & kScoreQmx8) != 0;
+  const int base = mode & ~kScoreQmx8;
+#define CSA2_SCORE_LAUNCH1(C, S, Mo, Q)                                                          \
+  hipLaunchKernelGGL((score_kernel<C, S, Mo, Q>), grid, block, 0, stream, ik, iks, entry_offset, \
                      n_entries, max_n, q_idx, w, Hi, cand, cand_stride, scores, sstride, sb, K,  \
                      (int)store)
+#define CSA2_SCORE_LAUNCH(C, S)                                                                  \
+  if (base == 0) {                                                                               \
+    if (qmx) CSA2_SCORE_LAUNCH1(C, S, 0, true); else CSA2_SCORE_LAUNCH1(C, S, 0, false);         \
+  } else {                                                                                       \
+    if (qmx) CSA2_SCORE_LAUNCH1(C, S, 1, true); else CSA2_SCORE_LAUNCH1(C, S, 1, false);         \
+  }
   if (cand) {
-    if (mode == 0) CSA2_SCORE_LAUNCH(true, SEL_NONE, 0); else CSA2_SCORE_LAUNCH(true, SEL_NONE, 1);
+    CSA2_SCORE_LAUNCH(true, SEL_NONE)
   } else if (sel == SEL_THRESHOLD) {
-    if (mode == 0) CSA2_SCORE_LAUNCH(false, SEL_THRESHOLD, 0); else CSA2_SCORE_LAUNCH(false, SEL_THRESHOLD, 1);
+    CSA2_SCORE_LAUNCH(false, SEL_THRESHOLD)
   } else if (sel == SEL_DIRECT) {
-    if (mode == 0) CSA2_SCORE_LAUNCH(false, SEL_DIRECT, 0); else CSA2_SCORE_LAUNCH(false, SEL_DIRECT, 1);
+    CSA2_SCORE_LAUNCH(false, SEL_DIRECT)
   } else {
-    if (mode == 0) CSA2_SCORE_LAUNCH(false, SEL_NONE, 0); else CSA2_SCORE_LAUNCH(false, SEL_NONE, 1);
+    CSA2_SCORE_LAUNCH(false, SEL_NONE)
   }
 #undef CSA2_SCORE_LAUNCH
+#undef CSA2_SCORE_LAUNCH1
   return hipGetLastError();
 }
 

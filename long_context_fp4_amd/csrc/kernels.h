@@ -48,6 +48,7 @@ hipError_t launch_cache_append(const uint16_t* x_lat, const uint16_t* x_idx, con
 // Selection modes of the score pass.
 enum { SEL_NONE = 0, SEL_THRESHOLD = 1, SEL_DIRECT = 2 };
 constexpr int kScoreChunk = 1024;     // slots per score workgroup
+constexpr int kScoreQmx8 = 0x100;     // score-mode flag: MXFP8 query, block-scaled FP8 x FP4 MFMA
 constexpr int kSumWords = 32;         // (bin, count) pairs a workgroup may report
 constexpr int kCandCap = 256;         // candidates a workgroup reports in direct mode
 constexpr int kDirectMaxK = 512;      // largest k the score pass selects by itself
