@@ -51,7 +51,7 @@ SCORE_SOURCES = [os.path.join(ROOT, "long_context_fp4_amd", "csrc", f)
 # Counter readings of one scoring launch at the decode128k size (KiB per
 # dispatch, medians over the timed launches) and the counters' scale factors
 # from the copy calibration; valid for the kernel sources with this hash.
-TRAFFIC = {"source_sha": "1c340061a5daa544", "fetch_kib": 70244.0, "write_kib": 606.5,
+TRAFFIC = {"source_sha": "243497bbf2f5f343", "fetch_kib": 70245.5, "write_kib": 606.5,
            "fetch_scale": 2.0, "write_scale": 1.0}
 
 

@@ -19,7 +19,10 @@
 //                contracts 16 entries x 16 heads x 32 channels per
 //                v_mfma_f32_16x16x32_bf16; the head sum is a 4-term in-lane sum
 //                plus two VALU lane swaps. Scores are staged in LDS and written
-//                with coalesced 16-byte stores.
+//                with coalesced 16-byte stores. The quantized-query variant
+//                (score-mode flag) first converts the queries to MXFP8 in LDS
+//                and contracts each tile with one block-scaled FP8 x FP4 MFMA
+//                that reads the keys as stored.
 //                Selection without contended atomics: each workgroup finds a
 //                local cutoff over its 1024 score keys that keeps a multiple of
 //                its expected share of the top-k, and writes to its own slot the
