@@ -73,6 +73,9 @@ def test_decode128k_full_size_sampled():
     """32 sequences x 131072 tokens (65536 ratio-2 entries), one Full layer, as the benchmark runs it.
 
     Sequences 0 and 31: cache bytes bit-exact, scores, top-512 and attention against the oracle.
+    On the same cache, as the benchmark's legs run them: the quantized-query variant of the layer
+    (sequences 0 and 31, within its accumulation bound) and the prefill of 32 query tokens at the
+    last 32 positions of sequence 0 (queries 0, 17 and 31 checked).
     """
     import torch
     import long_context_fp4_amd as L
@@ -104,6 +107,38 @@ def test_decode128k_full_size_sampled():
         s = OI.scores(oik, oiks, Lr["q_idx"][b], Lr["w"][b], 1)
         check_topk(top[b], OI.topk(s, np.arange(E), w.k), lambda q: s[q], w.k, f"seq{b}")
         check_attention(okv, top[b], Lr["q"][b], out[b], lse[b], f"attention seq{b}")
+        hidden[b] = (okv, oik, oiks)
+
+    # the quantized-query variant of the same layer
+    from tests.test_gpu_qmx import qmx_bound
+    qmode = OI.SCORE_RELU_W | OI.SCORE_QMX8
+    top, _, out, lse = L.decode_layer(L.CSA2_FULL, kv, ik, iks, dev(off), dev(nb), E, dev(Lr["q"]),
+                                      q_idx=dev(Lr["q_idx"]), w=dev(Lr["w"]), score_mode=qmode, k=w.k)
+    torch.cuda.synchronize()
+    top, out, lse = host(top), host(out), host(lse)
+    for b, (okv, oik, oiks) in hidden.items():
+        s = OI.scores(oik, oiks, Lr["q_idx"][b], Lr["w"][b], qmode)
+        tol = 2 * qmx_bound(oik, oiks, Lr["q_idx"][b], Lr["w"][b], qmode).max()
+        check_topk(top[b], OI.topk(s, np.arange(E), w.k), lambda q: s[q], w.k, f"qmx seq{b}", tol=tol)
+        check_attention(okv, top[b], Lr["q"][b], out[b], lse[b], f"qmx attention seq{b}")
+
+    # prefill: 32 query tokens at the last 32 positions of sequence 0
+    okv, oik, oiks = hidden[0]
+    rng = np.random.default_rng(20261213)
+    Tq = 32
+    pos = np.arange(w.T - Tq, w.T, dtype=np.int64)[None]
+    qp = np.stack([synth.latent_query(rng, w.H) for _ in range(Tq)])[None]
+    qi = np.stack([synth.indexer_query(rng, w.Hi) for _ in range(Tq)])[None]
+    wh = np.stack([synth.head_weights(rng, w.Hi) for _ in range(Tq)])[None]
+    ptop, pout, plse = L.prefill_layer(kv, ik, iks, dev(off[:1]), dev(nb[:1]), E, w.m, dev(pos), dev(qi),
+                                       dev(qp), w=dev(wh), k=w.k)
+    torch.cuda.synchronize()
+    ptop, pout, plse = host(ptop), host(pout), host(plse)
+    for t in (0, 17, 31):
+        nv = min(E, (int(pos[0, t]) + 1) // w.m)
+        s = OI.scores(oik[:nv], oiks[:nv], qi[0, t], wh[0, t], 1)
+        check_topk(ptop[0, t], OI.topk(s, np.arange(nv), w.k), lambda q: s[q], w.k, f"prefill query {t}")
+        check_attention(okv, ptop[0, t], qp[0, t], pout[0, t], plse[0, t], f"prefill attention query {t}")
 
 
 def run_full(kv, ik, iks, off, n_list, H, k, rng, ws=None):
