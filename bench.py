@@ -45,6 +45,18 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0     # dense bf16 / fp16 matrix peak of MI355X
+
+
+def call_roofline(nbytes, flops, us):
+    """A latency-bound call against both rooflines: its algorithmic bytes and
+    matrix flops over its time, as fractions of the HBM and bf16 MFMA peaks."""
+    gbs = nbytes / (us * 1e-6) / 1e9
+    out = {"bound": "latency", "bytes": nbytes, "achieved_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS}
+    if flops:
+        tfl = flops / (us * 1e-6) / 1e12
+        out.update({"flops": flops, "achieved_tflops": tfl, "mfma_frac": tfl / MFMA_F16_PEAK_TFLOPS})
+    return out
 COPIES = 4
 SCORE_SOURCES = [os.path.join(ROOT, "long_context_fp4_amd", "csrc", f)
                  for f in ("indexer.hip", "select_dev.h", "device.h", "kernels.h")]
@@ -166,7 +178,7 @@ def append_leg(L, synth, torch):
     pair_bytes = B * (2 * 1280 + 2 * 1280 + 356)
     return {"workload": f"append: one token for each of {B} sequences per call, ratio {m} (every other call "
                         f"packs {B} entries)", "bound": "latency", "avg_call_us": us, "calls": n,
-            "bytes_per_call": pair_bytes / 2}
+            "bytes_per_call": pair_bytes / 2, "roofline": call_roofline(pair_bytes / 2, 0, us)}
 
 
 def swa_leg(L, synth, torch, w):
@@ -202,9 +214,17 @@ def swa_leg(L, synth, torch, w):
 
     write_us = timed(lambda: L.swa_write(toks, pos, win))
     attn_us = timed(lambda: L.swa_attention(win, n_win, q, out, lse))
+    # write: a bf16 token read, a 544-byte row written per sequence; attention:
+    # the window rows, the queries, the sparse (out, lse) read and written back,
+    # QK and PV over 128 tokens x 512 dims per head
+    write_bytes = B * (512 * 2 + 544)
+    attn_bytes = B * 128 * 544 + B * H * 512 * 2 + 2 * B * H * (512 + 1) * 4
+    attn_flops = 2 * (2 * B * H * 128 * 512)
     return {"workload": f"window of 128 FP8 tokens for each of {B} sequences, {H} heads, merged into the "
                         f"sparse result", "bound": "latency", "write_one_token_us": write_us,
-            "attention_us": attn_us, "window_bytes_read": B * 128 * 544}
+            "attention_us": attn_us, "window_bytes_read": B * 128 * 544,
+            "roofline_write": call_roofline(write_bytes, 0, write_us),
+            "roofline_attention": call_roofline(attn_bytes, attn_flops, attn_us)}
 
 
 def prefill_leg(L, synth, torch, w, p, kv, ik, iks):
@@ -232,9 +252,15 @@ def prefill_leg(L, synth, torch, w, p, kv, ik, iks):
     e1.record()
     torch.cuda.synchronize()
     us = 1e3 * e0.elapsed_time(e1) / n
+    # the sequence's keys once, the gathered rows, queries and outputs; scoring
+    # every visible entry for 16 heads and the 64-head attention over k rows
+    vis = [min(E, (w.T - Tq + t + 1) // w.m) for t in range(Tq)]
+    nbytes = (E * 68 + Tq * w.k * 288 + Tq * (w.H * 512 * 2 + w.Hi * (128 * 2 + 4))
+              + Tq * (w.H * (512 + 1) * 4 + w.k * 4))
+    flops = sum(vis) * w.Hi * 128 * 2 + Tq * 2 * (2 * w.H * w.k * 512)
     return {"workload": f"prefill: {Tq} query tokens of one 131072-token sequence (65536 entries), each with "
                         f"its causal top-{w.k} and {w.H}-head attention", "avg_call_us": us,
-            "query_tokens_per_s": Tq / (us * 1e-6)}
+            "query_tokens_per_s": Tq / (us * 1e-6), "roofline": call_roofline(nbytes, flops, us)}
 
 
 def log(msg):
@@ -423,7 +449,8 @@ def main():
             "workload": "the same decode128k step with the quantized-query variant: MXFP8 indexer queries "
                         "and one block-scaled FP8 x FP4 MFMA per 16 entries (not the exact path)",
             "ms_per_step": ms, "query_tokens_per_s": w.B / (ms * 1e-3), "score_avg_launch_us": sus,
-            "score_achieved_gbs": idx_bytes / (sus * 1e-6) / 1e9}
+            "score_achieved_gbs": idx_bytes / (sus * 1e-6) / 1e9,
+            "score_frac": idx_bytes / (sus * 1e-6) / 1e9 / HBM_PEAK_GBS}
         log(f"quantized-query step {ms * 1e3:.1f} us, scoring {sus:.1f} us")
         log("prefill leg")
         res["prefill"] = prefill_leg(L, synth, torch, w, p, kv, ik, iks)
