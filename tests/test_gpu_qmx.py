@@ -166,3 +166,28 @@ def test_qmx_decode_layer_fused_and_fallback():
         err = attn_rel_err(out[b], ro)
         assert np.all(err <= ATTN_REL_TOL), f"seq {b}: attention max rel err {err.max():.3g}"
         assert np.all(np.abs(lse[b] - rl) <= 2e-3), f"seq {b}: lse"
+
+
+def test_qmx_fallback_recomputes_the_variant_scores():
+    """The 700 largest keys sit in the first chunk, so the finish launch falls
+    back to the full score set, which it recomputes with the quantized query
+    (no scores stored); the selection must equal the one taken on the stored
+    scores of the same variant."""
+    import torch
+    import long_context_fp4_amd as L
+    rng = np.random.default_rng(73)
+    n = 40000
+    ik, iks, off = make_keys(rng, [n])
+    iks = iks.copy()
+    iks[:700] = np.minimum(iks[:700].astype(np.int32) + 6, 254).astype(np.uint8)
+    q = synth.indexer_query(rng, 16)[None]
+    w = synth.head_weights(rng, 16)[None]
+    mode = OI.SCORE_RELU_W | QMX
+    args = (dev(ik), dev(iks), dev(off), dev(np.asarray([n], np.int32)), n, dev(q), dev(w), mode)
+    top, _, _ = L.indexer_topk(*args, k=512)
+    top2, _, sc = L.indexer_topk(*args, k=512, want_scores=True)
+    torch.cuda.synchronize()
+    top, top2, sc = host(top), host(top2), host(sc)
+    s, bound = check_scores(sc[0][:n], ik, iks, q[0], w[0], mode, "stored")
+    check_topk(top[0], OI.topk(s, np.arange(n), 512), lambda p: s[p], 512, "fallback", tol=2 * bound.max())
+    assert np.array_equal(top[0], top2[0])
