@@ -73,7 +73,7 @@ def check_scores(gpu, ik_rows, iks_rows, q, w, mode, what):
     return s, bound
 
 
-@pytest.mark.parametrize("mode,Hi,k", [(OI.SCORE_RELU_W, 16, 512), (OI.SCORE_DOT, 1, 64)])
+@pytest.mark.parametrize("mode,Hi,k", [(OI.SCORE_RELU_W, 16, 512), (OI.SCORE_DOT, 1, 64), (OI.SCORE_RELU_W, 5, 100)])
 def test_qmx_full_scores_and_top_k(mode, Hi, k):
     import torch
     import long_context_fp4_amd as L
@@ -191,3 +191,39 @@ def test_qmx_fallback_recomputes_the_variant_scores():
     s, bound = check_scores(sc[0][:n], ik, iks, q[0], w[0], mode, "stored")
     check_topk(top[0], OI.topk(s, np.arange(n), 512), lambda p: s[p], 512, "fallback", tol=2 * bound.max())
     assert np.array_equal(top[0], top2[0])
+
+
+def test_qmx_extreme_query_magnitudes():
+    """Heads whose binary exponents are lowered by 118 (blocks whose shared
+    exponent clamps at -127) and by 60, or raised by 40, an all-zero head and a
+    head with a single non-zero value: the variant's scores stay within the
+    bound of the oracle's."""
+    import torch
+    import long_context_fp4_amd as L
+    rng = np.random.default_rng(79)
+    n = 5000
+    ik, iks, off = make_keys(rng, [n])
+    qb = synth.indexer_query(rng, 16).astype(np.uint16).copy()
+
+    def shift(bits, d):
+        """bf16 bits with the exponent field moved by d; values leaving the normal range become 0."""
+        e = (bits.astype(np.int32) >> 7) & 0xFF
+        ne = e + d
+        out = (bits & 0x807F) | (np.clip(ne, 0, 254).astype(np.uint16) << 7)
+        return np.where((e == 0) | (ne < 1), bits & 0x8000, out).astype(np.uint16)
+
+    qb[0] = shift(qb[0], -118)
+    qb[1] = shift(qb[1], -60)
+    qb[2] = shift(qb[2], 40)
+    qb[3] = 0
+    qb[4] = 0
+    qb[4, 77] = 0xC040                                   # -3.0
+    w = synth.head_weights(rng, 16)
+    mode = OI.SCORE_RELU_W | QMX
+    _, _, sc = L.indexer_topk(dev(ik), dev(iks), dev(off), dev(np.asarray([n], np.int32)), n, dev(qb[None]),
+                              dev(w[None]), mode, k=64, want_scores=True)
+    torch.cuda.synchronize()
+    check_scores(host(sc)[0][:n], ik, iks, qb, w, mode, "extreme magnitudes")
+    # the clamped block exponent really occurs in head 0
+    _, sbytes = OI.quantize_query_mx(qb)
+    assert np.any(sbytes[0] == 0)
