@@ -117,6 +117,10 @@ def test_indexer_validation(L):
     assert idx_call(L, Hi=0) == -2 and idx_call(L, Hi=17) == -2
     assert idx_call(L, mode=0, Hi=2) == -2
     assert idx_call(L, mode=7) == -5
+    # the quantized-query flag goes with either mode, nothing else
+    assert idx_call(L, mode=0x100 | 2) == -5 and idx_call(L, mode=0x200 | 1) == -5
+    assert idx_call(L, mode=0x100, Hi=2) == -2                # DOT | QMX8 still takes one head
+    assert idx_call(L, mode=0x101, ws=None) == -4             # RELU_W | QMX8 passes the mode checks
     assert idx_call(L, k=0) == -2 and idx_call(L, k=4096) == -2
     assert idx_call(L, pool_k=20000, pool=P) == -2
     assert idx_call(L, pool_k=256, pool=P) == -2          # pool smaller than k
