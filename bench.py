@@ -406,6 +406,8 @@ def main():
     torch.cuda.synchronize()
     score_ms = [e0.elapsed_time(e1) for e0, e1 in pairs]
     score_avg_us = 1e3 * float(np.mean(score_ms))
+    pct = lambda v: {"p10": float(np.percentile(v, 10)), "median": float(np.median(v)),
+                     "p90": float(np.percentile(v, 90))}
 
     steps_per_s = a.steps / (total_ms / 1e3)
     qtok_s = w.B * steps_per_s
@@ -434,7 +436,8 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "score_kernel (indexer scoring pass)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_bytes(),
-                     "bytes_per_launch": idx_bytes, "avg_launch_us": score_avg_us},
+                     "bytes_per_launch": idx_bytes, "avg_launch_us": score_avg_us,
+                     "launch_us": pct(1e3 * np.array(score_ms))},
         "step_cache_read_gbs": step_gbs,
     }
     log(f"step {total_ms / a.steps * 1e3:.1f} us, scoring kernel {score_avg_us:.1f} us "
