@@ -76,6 +76,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle timing budget")
     ap.add_argument("--no-cache-write", action="store_true",
                     help="skip the legs beside the step (quantized-query scoring, prefill, cache write, window, append)")
+    ap.add_argument("--legs", default="all",
+                    help="comma-separated legs beside the step to run (qmx8, prefill, fallback, hsi1m, "
+                         "group_ragged, cache_write, swa, append) or 'all'")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of 1 GiB five times (counter calibration)")
     return ap.parse_args()
@@ -159,7 +162,8 @@ def append_leg(L, synth, torch):
     cnt = torch.zeros(B, dtype=torch.int32, device="cuda")
     ne = torch.zeros(B, dtype=torch.int32, device="cuda")
     off = d(np.arange(B, dtype=np.int64) * cap)
-    call = lambda i: L.cache_append(toks[i % 8][0], toks[i % 8][1], wl, wi, m, st_l, st_i, cnt, off, ne, cap,
+    caps = d(np.full(B, cap, np.int64))
+    call = lambda i: L.cache_append(toks[i % 8][0], toks[i % 8][1], wl, wi, m, st_l, st_i, cnt, off, ne, caps,
                                     kv, ik, iks)
     for i in range(10):
         call(i)
@@ -263,6 +267,131 @@ def prefill_leg(L, synth, torch, w, p, kv, ik, iks):
             "query_tokens_per_s": Tq / (us * 1e-6), "roofline": call_roofline(nbytes, flops, us)}
 
 
+def group_leg(L, synth, torch, name, steps, warmup, copies=3):
+    """A layer group at full size, as the decode step of its workload runs it:
+    hsi1m (4 x 1048576 tokens at ratio 2: Full with a 16384-candidate pool and its
+    top-512, then two Reindex layers over that pool, each with 64-head attention) or
+    group_ragged (16 sequences of 32768..262144 tokens at ratio 1: Full, Reindex,
+    Reuse, Reuse). The cache is written by the library, then copied so that
+    consecutive steps read different copies (more than the 256 MB last-level
+    cache). Reports the step time from events around K steps, each layer's time
+    from events between the layers (a separate pass), and the step's algorithmic
+    cache bytes over its time against the HBM peak."""
+    import numpy as np
+    w = synth.workload(name)
+    p = synth.params(w)
+    lens = w.lengths if w.lengths is not None else [w.T] * w.B
+    ents = np.asarray([t // w.m for t in lens], np.int64)
+    off = np.concatenate([[0], np.cumsum(ents)[:-1]]).astype(np.int64)
+    E = int(ents.sum())
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    kv = torch.empty((E, 288), dtype=torch.uint8, device="cuda")
+    ik = torch.empty((E, 64), dtype=torch.uint8, device="cuda")
+    iks = torch.empty((E, 4), dtype=torch.uint8, device="cuda")
+    wl, wi = d(p["w_lat"]), d(p["w_idx"])
+    for b in range(w.B):
+        x_lat, x_idx = synth.hidden_states_device(w, p, b)
+        r = slice(int(off[b]), int(off[b] + ents[b]))
+        L.cache_write(x_lat[None], x_idx[None], wl, wi, w.m, kv=kv[r], ik=ik[r], iks=iks[r])
+        del x_lat, x_idx
+    torch.cuda.synchronize()
+    cs = [(kv, ik, iks)] + [(kv.clone(), ik.clone(), iks.clone()) for _ in range(copies - 1)]
+    offd, nbd = d(off), d(ents.astype(np.int32))
+    max_n = int(ents.max())
+    ws = L.Workspace()
+    layers = []
+    for Lr in p["layers"]:
+        layers.append({"mode": Lr["mode"], "q": d(Lr["q"].view(np.int16)),
+                       "q_idx": d(Lr["q_idx"].view(np.int16)) if "q_idx" in Lr else None,
+                       "w": d(Lr["w"]) if Lr.get("w") is not None else None,
+                       "topk": torch.empty((w.B, w.k), dtype=torch.int32, device="cuda"),
+                       "out": torch.empty((w.B, w.H, 512), dtype=torch.float32, device="cuda"),
+                       "lse": torch.empty((w.B, w.H), dtype=torch.float32, device="cuda")})
+    pool = torch.empty((w.B, w.pool_k), dtype=torch.int32, device="cuda")
+
+    def step(i, evs=None):
+        c = cs[i % copies]
+        src = None                                   # the layer whose indices a Reuse layer takes
+        for j, y in enumerate(layers):
+            if evs is not None:
+                evs[j].record()
+            if y["mode"] == 0:
+                L.decode_layer(L.CSA2_FULL, c[0], c[1], c[2], offd, nbd, max_n, y["q"], q_idx=y["q_idx"], w=y["w"],
+                               k=w.k, pool_k=w.pool_k, pool=pool, topk=y["topk"], out=y["out"], lse=y["lse"],
+                               workspace=ws)
+                src = y
+            elif y["mode"] == 1:
+                L.decode_layer(L.CSA2_REINDEX, c[0], c[1], c[2], offd, nbd, max_n, y["q"], q_idx=y["q_idx"],
+                               w=y["w"], k=w.k, pool=pool, topk=y["topk"], out=y["out"], lse=y["lse"], workspace=ws)
+                src = y
+            else:
+                L.decode_layer(L.CSA2_REUSE, c[0], c[1], c[2], offd, nbd, max_n, y["q"], topk=src["topk"],
+                               out=y["out"], lse=y["lse"], workspace=ws)
+        if evs is not None:
+            evs[len(layers)].record()
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    step_us = 1e3 * e0.elapsed_time(e1) / steps
+    per = np.zeros(len(layers))
+    for i in range(steps):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(layers) + 1)]
+        step(i, evs)
+        torch.cuda.synchronize()
+        per += [1e3 * evs[j].elapsed_time(evs[j + 1]) for j in range(len(layers))]
+    per /= steps
+    names = {0: "full", 1: "reindex", 2: "reuse"}
+    idx_bytes = int(ents.sum()) * 68
+    n_rei = sum(1 for y in layers if y["mode"] == 1)
+    rei_bytes = n_rei * int(np.minimum(ents, w.pool_k).sum()) * 68
+    gather_bytes = len(layers) * int(np.minimum(ents, w.k).sum()) * 288
+    nbytes = idx_bytes + rei_bytes + gather_bytes
+    gbs = nbytes / (step_us * 1e-6) / 1e9
+    del cs, kv, ik, iks
+    torch.cuda.empty_cache()
+    return {"workload": f"{name}: {w.B} sequences, " + (f"{w.T} tokens each" if w.lengths is None else
+                                                        f"{min(lens)}..{max(lens)} tokens") +
+                        f" at ratio {w.m}, layers " + ", ".join(names[y["mode"]] for y in layers) +
+                        f", pool {w.pool_k}, top-{w.k}, {w.H} heads",
+            "ms_per_step": step_us / 1e3, "query_tokens_per_s": w.B / (step_us * 1e-6),
+            "layer_us": {f"{j}:{names[y['mode']]}": float(per[j]) for j, y in enumerate(layers)},
+            "bytes_per_step": nbytes, "bytes": {"indexer_full": idx_bytes, "indexer_reindex": rei_bytes,
+                                                "gathered_rows": gather_bytes},
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS}}
+
+
+def fallback_leg(L, torch, w, E, copies, off, nb, q, wh, ws, steps):
+    """The decode128k step with an all-zero indexer query: every score is 0, so every
+    local candidate list overflows and the top-k finish takes its fallback (a rescore
+    and a histogram of the whole sequence); the top-512 is then positions 0..511."""
+    q_idx0 = torch.zeros((w.B, w.Hi, 128), dtype=torch.int16, device="cuda")
+    topk = torch.empty((w.B, w.k), dtype=torch.int32, device="cuda")
+    out = torch.empty((w.B, w.H, 512), dtype=torch.float32, device="cuda")
+    lse = torch.empty((w.B, w.H), dtype=torch.float32, device="cuda")
+    call = lambda i: L.decode_layer(L.CSA2_FULL, *copies[i % len(copies)], off, nb, E, q, q_idx=q_idx0, w=wh,
+                                    k=w.k, topk=topk, out=out, lse=lse, workspace=ws)
+    call(0)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        call(i)
+    e1.record()
+    torch.cuda.synchronize()
+    us = 1e3 * e0.elapsed_time(e1) / steps
+    ok = bool((topk == torch.arange(w.k, device="cuda", dtype=torch.int32)[None]).all())
+    return {"workload": "decode128k with an all-zero indexer query (every score ties at 0): the top-k "
+                        "finish's fallback path", "ms_per_step": us / 1e3, "topk_is_first_512": ok}
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -281,14 +410,56 @@ def build_cache(L, synth, torch, w, p):
     return kv, ik, iks
 
 
-def cpu_baseline(w, p, budget_s):
-    """The oracle's decode step (scores, top-512, attention) on a sample of the same workload."""
+def _oracle_steps(args):
+    """One host worker of the CPU baseline: the oracle's decode step (scores, top-k,
+    attention) on one sequence, repeated for `budget` seconds with BLAS on one thread.
+    Returns (steps done, seconds)."""
+    kv, ik, iks, q_idx, wh, q, k, budget = args
     import numpy as np
     from threadpoolctl import threadpool_limits
+    from oracle import attention as OA
+    from oracle import indexer as OI
+    done = 0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        while True:
+            n = ik.shape[0]
+            s = OI.scores(ik, iks, q_idx, wh, OI.SCORE_RELU_W)
+            top = OI.topk(s, np.arange(n), k)
+            OA.sparse_attention(kv, top, q, 1.0)
+            done += 1
+            el = time.perf_counter() - t0
+            if el >= budget:
+                return done, el
+
+
+def host_cpu():
+    """(usable cores, model name) of this host."""
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return cores, model
+
+
+def cpu_baseline(w, p, budget_s):
+    """The oracle's decode step (scores, top-512, attention) on a sample of the same
+    workload: on one core, then on all usable host cores (one oracle process per core,
+    each on one sequence of the sample, BLAS on one thread; up to 16 processes, this
+    host's share of a one-GPU machine)."""
+    import multiprocessing as mp
+    import numpy as np
     from long_context_fp4_amd import synth
     from oracle import cache as OC
-    from oracle import indexer as OI
-    from oracle import attention as OA
     import torch
 
     Lr = p["layers"][0]
@@ -301,23 +472,22 @@ def cpu_baseline(w, p, budget_s):
         caches.append(OC.cache_write(xl, xi, p["w_lat"], p["w_idx"], w.m))
     del x_lat, x_idx
     torch.cuda.empty_cache()
-    done = 0
-    t0 = time.perf_counter()
-    with threadpool_limits(limits=1):
-        while True:
-            for b, (kv, ik, iks) in zip(seqs, caches):
-                n = ik.shape[0]
-                s = OI.scores(ik, iks, Lr["q_idx"][b], Lr["w"][b], OI.SCORE_RELU_W)
-                top = OI.topk(s, np.arange(n), w.k)
-                OA.sparse_attention(kv, top, Lr["q"][b], 1.0)
-                done += 1
-            el = time.perf_counter() - t0
-            if el >= budget_s:
-                break
-    return {"value": done / el, "unit": "query-tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} decode steps (one query token each) of the decode128k workload on "
-                      f"sequences {seqs} (65536 entries, 64 heads, 16 indexer heads, top-512), "
-                      f"numpy oracle with BLAS limited to 1 thread, {el:.1f} s"}
+    job = lambda i, budget: (*caches[i % 2], Lr["q_idx"][seqs[i % 2]], Lr["w"][seqs[i % 2]],
+                             Lr["q"][seqs[i % 2]], w.k, budget)
+    one_done, one_s = _oracle_steps(job(0, budget_s / 2))
+    cores, model = host_cpu()
+    nproc = max(1, min(cores, 16))
+    with mp.get_context("spawn").Pool(nproc) as pool:
+        res = pool.map(_oracle_steps, [job(i, budget_s / 2) for i in range(nproc)])
+    all_rate = sum(d / s for d, s in res)
+    return {"value": all_rate, "unit": "query-tokens/s", "cores": nproc, "kind": "oracle",
+            "cpu_model": model, "host_cores": cores,
+            "one_core": {"value": one_done / one_s, "cores": 1, "steps": one_done, "seconds": one_s},
+            "sample": f"decode steps (one query token each) of the decode128k workload on sequences {seqs} "
+                      f"(65536 entries, 64 heads, 16 indexer heads, top-512): the numpy oracle in {nproc} "
+                      f"processes at once (BLAS on one thread each, sequences alternating), "
+                      f"{sum(d for d, _ in res)} steps in {max(s for _, s in res):.1f} s; one core alone: "
+                      f"{one_done} steps in {one_s:.1f} s"}
 
 
 def main():
@@ -426,7 +596,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp4 storage (E2M1 + E4M3/E8M0 scales); bf16 x bf16 MFMA scoring and fp16 x fp16 MFMA "
+                 "attention, f32 accumulation and softmax",
         "data": "synthetic: seeded N(0,1) bf16 hidden states packed to FP4 by the library; seeded queries",
         "config": {"workload": "decode128k: 32 sequences x 131072 tokens (65536 ratio-2 entries), one Full "
                                "layer: indexer over all entries (16 heads), top-512, attention with 64 heads "
@@ -442,7 +613,9 @@ def main():
     }
     log(f"step {total_ms / a.steps * 1e3:.1f} us, scoring kernel {score_avg_us:.1f} us "
         f"({achieved:.0f} GB/s), {qtok_s:.0f} query-tokens/s")
-    if not a.no_cache_write:
+    legs = set(("qmx8 prefill fallback hsi1m group_ragged cache_write swa append".split()
+                 if a.legs == "all" else a.legs.split(",")) if not a.no_cache_write else [])
+    if "qmx8" in legs:
         log("quantized-query scoring leg")
         qmode = L.CSA2_SCORE_RELU_W | L.CSA2_SCORE_QMX8
         for i in range(a.warmup):
@@ -455,20 +628,31 @@ def main():
             "score_achieved_gbs": idx_bytes / (sus * 1e-6) / 1e9,
             "score_frac": idx_bytes / (sus * 1e-6) / 1e9 / HBM_PEAK_GBS}
         log(f"quantized-query step {ms * 1e3:.1f} us, scoring {sus:.1f} us")
+    if "prefill" in legs:
         log("prefill leg")
         res["prefill"] = prefill_leg(L, synth, torch, w, p, kv, ik, iks)
         log(f"prefill {res['prefill']['avg_call_us']:.1f} us for 32 query tokens")
+    if "fallback" in legs:
+        log("fallback leg")
+        res["fallback"] = fallback_leg(L, torch, w, E, copies, off, nb, q, wh, ws, min(a.steps, 20))
+        log(f"fallback step {res['fallback']['ms_per_step'] * 1e3:.1f} us")
     del copies, kv, ik, iks
     torch.cuda.empty_cache()
-    if not a.no_cache_write:
+    for name in ("hsi1m", "group_ragged"):
+        if name in legs:
+            log(f"{name} leg")
+            res[name] = group_leg(L, synth, torch, name, min(a.steps, 50), min(a.warmup, 5))
+            log(f"{name} step {res[name]['ms_per_step'] * 1e3:.1f} us, layers {res[name]['layer_us']}")
+    if "cache_write" in legs:
         log("cache write leg (write128k)")
         res["cache_write"] = cache_write_leg(L, synth, torch)
         log(f"cache write {res['cache_write']['avg_launch_us']:.1f} us "
             f"({res['cache_write']['achieved']:.0f} GB/s)")
-    if not a.no_cache_write:
+    if "swa" in legs:
         log("sliding-window leg")
         res["swa"] = swa_leg(L, synth, torch, w)
         log(f"window attention {res['swa']['attention_us']:.2f} us")
+    if "append" in legs:
         log("append leg")
         res["append"] = append_leg(L, synth, torch)
         log(f"append {res['append']['avg_call_us']:.2f} us per call")

@@ -101,16 +101,22 @@ extern "C" {
  * (latent: E2M1 + one E4M3 scale per 16 channels; key: E2M1 + one E8M0 scale
  * per 32 channels).
  *
- *   x_lat  bf16 [B][T][512]   hidden latent rows of B sequences
- *   x_idx  bf16 [B][T][128]   hidden indexer-key rows
+ *   x_lat  bf16 [B][T][512]   hidden latent rows of B sequences (row b*T + t = token t of
+ *                             sequence b; T is the row stride, the longest sequence)
+ *   x_idx  bf16 [B][T][128]   hidden indexer-key rows, same layout
  *   w_lat  f32  [m][512]      merge weights, already normalised over the m positions
  *   w_idx  f32  [m][128]
- *   kv     u8   [B*E][288]    out: row b*E+i = 256 code bytes (channel 2j in the low
- *                             nibble of byte j) then 32 E4M3FN scale bytes (block b
- *                             covers channels 16b..16b+15)
- *   ik     u8   [B*E][64]     out: indexer-key codes, same nibble order
- *   iks    u8   [B*E][4]      out: E8M0 scale bytes of the 4 blocks of 32 channels
- * with E = floor(T/m); a trailing partial group of a sequence is not written.
+ *   n_tokens          i64 [B] or NULL: tokens of sequence b (clamped to [0, T]); NULL = T each
+ *   out_entry_offset  i64 [B] or NULL: cache row of sequence b's first entry;
+ *                     NULL = b * floor(T/m). With both, a ragged batch is written in one call
+ *                     into one preallocated cache (the caller keeps the rows of different
+ *                     sequences apart).
+ *   kv     u8   [rows][288]   out: entry i of sequence b goes to row out_entry_offset[b] + i:
+ *                             256 code bytes (channel 2j in the low nibble of byte j) then 32
+ *                             E4M3FN scale bytes (block b covers channels 16b..16b+15)
+ *   ik     u8   [rows][64]    out: indexer-key codes, same nibble order and rows
+ *   iks    u8   [rows][4]     out: E8M0 scale bytes of the 4 blocks of 32 channels
+ * Sequence b gets E_b = floor(n_b/m) entries; a trailing partial group is not written.
  *
  * Merge, per channel c: acc = w[0][c]*x[m*i][c], then acc = acc + w[j][c]*x[m*i+j][c]
  * for j = 1..m-1, each product and sum rounded to float32 (no fused multiply-add).
@@ -118,11 +124,14 @@ extern "C" {
  * saturating at 448); codes = E2M1 nearest-even of the float32 quotient x/s, sign bit
  * from x; s == 0 gives all codes 0. Key block: X = floor(log2 amax) - 2, byte X+127
  * clamped to [0,254]; codes = E2M1 of x*2^-X; amax == 0 gives byte 0 and codes 0.
- * Errors: NULL pointer, B < 1, T < 0, m outside [1, CSA2_MAX_RATIO], misalignment.
+ * Errors: NULL pointer, B outside [1, 65535], T < 0, m outside [1, CSA2_MAX_RATIO],
+ * misalignment (16 bytes; iks 4). The token counts and offsets are device data and are
+ * not checked on the host: rows they name must lie inside the caller's buffers.
  */
 int csa2_cache_write(const uint16_t* x_lat, const uint16_t* x_idx,
                      const float* w_lat, const float* w_idx,
                      int B, int64_t T, int m,
+                     const int64_t* n_tokens, const int64_t* out_entry_offset,
                      uint8_t* kv, uint8_t* ik, uint8_t* iks, void* stream);
 
 /*
@@ -138,10 +147,11 @@ int csa2_cache_write(const uint16_t* x_lat, const uint16_t* x_idx,
  *   stage_count    i32 [B] in/out: staged tokens, 0 <= stage_count[b] < m
  *   entry_offset   i64 [B]: first cache row of sequence b
  *   n_entries      i32 [B] in/out: entries written so far
- *   capacity       cache rows reserved per sequence
+ *   capacity       i64 [B]: cache rows reserved for sequence b (rows entry_offset[b] ..
+ *                  entry_offset[b] + capacity[b] - 1); a ragged layout gives each its own
  *   kv, ik, iks    the cache (as in csa2_cache_write)
  *   dropped        i32 [B] out, or NULL: 1 where a completed group found the
- *                  sequence full (n_entries[b] == capacity) and was discarded
+ *                  sequence full (n_entries[b] >= capacity[b]) and was discarded
  * When stage_count[b] + 1 < m the token is staged at row stage_count[b] and
  * stage_count[b] grows by one. Otherwise the m - 1 staged tokens and this one
  * are merged and packed exactly as csa2_cache_write packs tokens m*i .. m*i+m-1
@@ -151,12 +161,12 @@ int csa2_cache_write(const uint16_t* x_lat, const uint16_t* x_idx,
  * and the last T mod m tokens in the stage. A stage count outside [0, m-1] is
  * taken as m - 1.
  * Errors: NULL pointer, B < 1 or B > CSA2_MAX_BATCH, m outside [1, CSA2_MAX_RATIO],
- * capacity < 0, misalignment (16 bytes; iks 4; stage_count, n_entries, dropped 4).
+ * misalignment (16 bytes; iks 4; stage_count, n_entries, dropped 4).
  */
 int csa2_cache_append(const uint16_t* x_lat, const uint16_t* x_idx,
                       const float* w_lat, const float* w_idx, int B, int m,
                       uint16_t* stage_lat, uint16_t* stage_idx, int32_t* stage_count,
-                      const int64_t* entry_offset, int32_t* n_entries, int64_t capacity,
+                      const int64_t* entry_offset, int32_t* n_entries, const int64_t* capacity,
                       uint8_t* kv, uint8_t* ik, uint8_t* iks, int32_t* dropped, void* stream);
 
 /*
@@ -210,8 +220,12 @@ int csa2_swa_attention(const uint8_t* win, const int32_t* n_win, const uint16_t*
  *   Hi, score_mode 1 <= Hi <= 16; CSA2_SCORE_DOT needs Hi == 1; either mode may
  *                  carry CSA2_SCORE_QMX8
  *   cand           i32 [B][cand_stride] or NULL. NULL: score every entry (Full).
- *                  Otherwise score only the listed positions (Reindex); entries
- *                  < 0 are skipped. cand_stride <= CSA2_MAX_POOL.
+ *                  Otherwise score only the listed positions (Reindex). A row is
+ *                  meant to list distinct positions in ascending order, as a pool
+ *                  is written: an entry is used only when it lies in
+ *                  [0, n_entries[b]) and is greater than every in-range entry
+ *                  before it in the row; others (-1 padding, out-of-order or
+ *                  repeated positions) are skipped. cand_stride <= CSA2_MAX_POOL.
  *   k              1 <= k <= CSA2_MAX_K
  *   topk           out i32 [B][k]: the k best positions by (score descending,
  *                  position ascending), written in ascending position order,

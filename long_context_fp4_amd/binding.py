@@ -39,9 +39,9 @@ def lib():
         raise RuntimeError(f"{path} is missing: build it with `python -m long_context_fp4_amd.build`")
     L = ctypes.CDLL(path)
     vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
-    L.csa2_cache_write.argtypes = [vp, vp, vp, vp, i32, i64, i32, vp, vp, vp, vp]
+    L.csa2_cache_write.argtypes = [vp, vp, vp, vp, i32, i64, i32, vp, vp, vp, vp, vp, vp]
     L.csa2_cache_write.restype = i32
-    L.csa2_cache_append.argtypes = [vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, vp]
+    L.csa2_cache_append.argtypes = [vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     L.csa2_cache_append.restype = i32
     L.csa2_prefill_workspace_bytes.argtypes = [i32, i32, i64, i32, i32]
     L.csa2_prefill_workspace_bytes.restype = sz
@@ -138,10 +138,13 @@ def _ws(ws, device):
     return _default_ws[key]
 
 
-def cache_write(x_lat, x_idx, w_lat, w_idx, m, kv=None, ik=None, iks=None, stream=None):
+def cache_write(x_lat, x_idx, w_lat, w_idx, m, kv=None, ik=None, iks=None, n_tokens=None,
+                out_entry_offset=None, stream=None):
     """Merge + pack B sequences of hidden rows. x_lat [B,T,512], x_idx [B,T,128] bf16 bits.
 
-    Returns (kv [B*E, 288] u8, ik [B*E, 64] u8, iks [B*E, 4] u8), E = T // m.
+    n_tokens: i64 [B] tokens of each sequence (<= T; None = T each). out_entry_offset: i64 [B]
+    first cache row of each sequence (None = b * (T // m); then the outputs are created when
+    not given). Returns (kv [rows, 288] u8, ik [rows, 64] u8, iks [rows, 4] u8).
     """
     torch = _torch()
     if x_lat.dim() == 2:
@@ -151,17 +154,24 @@ def cache_write(x_lat, x_idx, w_lat, w_idx, m, kv=None, ik=None, iks=None, strea
         raise ValueError("x_lat must be [B,T,512] and x_idx [B,T,128]")
     if tuple(w_lat.shape) != (m, 512) or tuple(w_idx.shape) != (m, 128):
         raise ValueError("w_lat must be [m,512] and w_idx [m,128]")
+    for name, t in (("n_tokens", n_tokens), ("out_entry_offset", out_entry_offset)):
+        if t is not None and tuple(t.shape) != (B,):
+            raise ValueError(f"{name} must be [B]")
     E = T // m
     dev = x_lat.device
+    if out_entry_offset is not None and (kv is None or ik is None or iks is None):
+        raise ValueError("with out_entry_offset the caller provides kv, ik and iks")
     kv = torch.empty((B * E, MAIN_ROW_BYTES), dtype=torch.uint8, device=dev) if kv is None else kv
     ik = torch.empty((B * E, INDEXER_CODE_BYTES), dtype=torch.uint8, device=dev) if ik is None else ik
     iks = torch.empty((B * E, INDEXER_SCALE_BYTES), dtype=torch.uint8, device=dev) if iks is None else iks
-    if kv.shape[0] < B * E or ik.shape[0] < B * E or iks.shape[0] < B * E:
+    if out_entry_offset is None and (kv.shape[0] < B * E or ik.shape[0] < B * E or iks.shape[0] < B * E):
         raise ValueError("output buffers too small")
     bt = _bf16_types()
     _check(lib().csa2_cache_write(_ptr(x_lat, bt, "x_lat"), _ptr(x_idx, bt, "x_idx"),
                                   _ptr(w_lat, torch.float32, "w_lat"), _ptr(w_idx, torch.float32, "w_idx"),
-                                  B, T, m, _ptr(kv, torch.uint8, "kv"), _ptr(ik, torch.uint8, "ik"),
+                                  B, T, m, _ptr(n_tokens, torch.int64, "n_tokens"),
+                                  _ptr(out_entry_offset, torch.int64, "out_entry_offset"),
+                                  _ptr(kv, torch.uint8, "kv"), _ptr(ik, torch.uint8, "ik"),
                                   _ptr(iks, torch.uint8, "iks"), _stream(stream)))
     return kv, ik, iks
 
@@ -172,7 +182,8 @@ def cache_append(x_lat, x_idx, w_lat, w_idx, m, stage_lat, stage_idx, stage_coun
 
     stage_lat [B,m-1,512] / stage_idx [B,m-1,128] (None when m == 1), stage_count [B] i32 and
     n_entries [B] i32 are updated in place; a completed group is packed into cache row
-    entry_offset[b] + n_entries[b] of kv / ik / iks. Returns dropped [B] i32 when given.
+    entry_offset[b] + n_entries[b] of kv / ik / iks while n_entries[b] < capacity[b]
+    (capacity: i64 [B] device tensor). Returns dropped [B] i32 when given.
     """
     torch = _torch()
     B = x_lat.shape[0]
@@ -183,8 +194,9 @@ def cache_append(x_lat, x_idx, w_lat, w_idx, m, stage_lat, stage_idx, stage_coun
     if m > 1 and (stage_lat is None or tuple(stage_lat.shape) != (B, m - 1, 512) or
                   tuple(stage_idx.shape) != (B, m - 1, 128)):
         raise ValueError("stage_lat must be [B,m-1,512] and stage_idx [B,m-1,128]")
-    if stage_count.shape[0] != B or n_entries.shape[0] != B or entry_offset.shape[0] != B:
-        raise ValueError("stage_count, n_entries and entry_offset must be [B]")
+    if (stage_count.shape[0] != B or n_entries.shape[0] != B or entry_offset.shape[0] != B
+            or tuple(capacity.shape) != (B,)):
+        raise ValueError("stage_count, n_entries, entry_offset and capacity must be [B]")
     bt = _bf16_types()
     st_l = _ptr(stage_lat, bt, "stage_lat") if m > 1 else None
     st_i = _ptr(stage_idx, bt, "stage_idx") if m > 1 else None
@@ -192,7 +204,8 @@ def cache_append(x_lat, x_idx, w_lat, w_idx, m, stage_lat, stage_idx, stage_coun
                                    _ptr(w_lat, torch.float32, "w_lat"), _ptr(w_idx, torch.float32, "w_idx"),
                                    B, m, st_l, st_i, _ptr(stage_count, torch.int32, "stage_count"),
                                    _ptr(entry_offset, torch.int64, "entry_offset"),
-                                   _ptr(n_entries, torch.int32, "n_entries"), int(capacity),
+                                   _ptr(n_entries, torch.int32, "n_entries"),
+                                   _ptr(capacity, torch.int64, "capacity"),
                                    _ptr(kv, torch.uint8, "kv"), _ptr(ik, torch.uint8, "ik"),
                                    _ptr(iks, torch.uint8, "iks"), _ptr(dropped, torch.int32, "dropped"),
                                    _stream(stream)))

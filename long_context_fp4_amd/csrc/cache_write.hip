@@ -10,12 +10,13 @@
 // 128-channel indexer key as E2M1 codes with one E8M0 scale per 32 channels
 // (64 B of codes + 4 B of scales).
 //
-// Work layout: one workgroup of 320 lanes packs 16 entries. Waves 0-3 own the
-// latent (16 lanes per entry), wave 4 owns the indexer key (4 lanes per
-// entry). Every lane merges 32 channels of m rows with 16-byte loads laid out
-// so that each load instruction covers whole contiguous stretches of the rows
-// (a streaming load never leaves a line half read), and writes its codes as
-// 4-byte words that are contiguous across the lanes of an entry.
+// Work layout: one workgroup of 320 lanes packs 16 consecutive entries of one
+// sequence. Waves 0-3 own the latent (16 lanes per entry), wave 4 owns the
+// indexer key (4 lanes per entry). Every lane merges 32 channels of m rows with
+// 16-byte loads laid out so that each load instruction covers whole contiguous
+// stretches of the rows (a streaming load never leaves a line half read), and
+// puts its codes into the entry's row assembled in LDS; the workgroup then
+// writes its 16 rows (4608 + 1024 contiguous bytes) with 16-byte stores.
 //
 // Bit-exactness: the merge is evaluated with separate float32 roundings
 // (contraction is switched off for this file), the scale division is the
@@ -68,6 +69,19 @@ struct LaneMap {
         p(tid < 256 ? (tid & 15) : ((tid - 256) & 3)), C(tid < 256 ? 512 : 128), qstride(tid < 256 ? 128 : 32) {}
 };
 
+// The packed rows of a workgroup's 16 entries are assembled in LDS and then
+// written with 16-byte stores. Row pitches are chosen so that the 4-byte code
+// words of the lanes of one wave fall on distinct banks (latent: 80 words,
+// four entries per wave 16 banks apart; indexer: 20 words, the 64 lanes of
+// wave 4 on 64 distinct banks).
+constexpr int CW_LAT_PITCH = 320;   // bytes per staged latent row (288 used)
+constexpr int CW_IDX_PITCH = 80;    // bytes per staged indexer row (64 used)
+struct alignas(16) Staging {
+  uint8_t lat[CW_ENTRIES * CW_LAT_PITCH];
+  uint8_t idx[CW_ENTRIES * CW_IDX_PITCH];
+  uint32_t iks[CW_ENTRIES];
+};
+
 // Stages the merge weights ([m][512] latent then [m][128] indexer) in LDS;
 // every thread of the workgroup calls it (the caller's barrier follows).
 __device__ __forceinline__ void stage_weights(float* lds_w, const float* w_lat, const float* w_idx, int m) {
@@ -81,14 +95,16 @@ __device__ __forceinline__ void stage_weights(float* lds_w, const float* w_lat, 
 // qstride*q + 8p .. +7): merge the m rows (rowq(j, q): the 8 bf16 of group q
 // of row j), take the block maximum across the lanes of the block, pack.
 // Working group by group keeps few values live, so more waves fit a SIMD.
-// With `store` unset the lane still takes part in the lane exchanges. Codes go
-// to the entry's rows kv_e / ik_e / iks_e, latent scale bytes to scale_e (LDS,
-// 32 bytes per entry, stored by the caller).
+// With `store` unset the lane still takes part in the lane exchanges. The
+// codes and scale bytes go to the entry's staged rows in LDS.
 template <int M, typename RowQ>
 __device__ __forceinline__ void merge_pack(const LaneMap& L, bool store, int m, const float* lds_w, RowQ rowq,
-                                           uint8_t* kv_e, uint8_t* ik_e, uint8_t* iks_e, uint8_t* scale_e) {
+                                           Staging& st) {
   const float* wb = L.latent ? lds_w : lds_w + m * 512;
   const int p = L.p;
+  uint8_t* lat_e = st.lat + L.el * CW_LAT_PITCH;
+  uint8_t* idx_e = st.idx + L.el * CW_IDX_PITCH;
+  uint32_t xbytes = 0;                                  // indexer: the 4 E8M0 bytes of the entry
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     float acc[8];
@@ -135,9 +151,12 @@ __device__ __forceinline__ void merge_pack(const LaneMap& L, bool store, int m, 
         word |= code << (4 * c);
       }
       if (!(s > 0.0f)) word = 0u;
+      // the scale bytes of blocks 8q + 2k and 8q + 2k + 1 (lanes 4k and
+      // 4k + 2) meet in lane 4k, which stores them as one 16-bit word
+      const uint32_t sb2 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)sb, 0x4E, 0xf, 0xf, false);   // lane ^ 2
       if (store) {
-        *(uint32_t*)(kv_e + 64 * q + 4 * p) = word;
-        if ((p & 1) == 0) scale_e[8 * q + (p >> 1)] = (uint8_t)sb;
+        *(uint32_t*)(lat_e + 64 * q + 4 * p) = word;
+        if ((p & 3) == 0) *(uint16_t*)(lat_e + 256 + 8 * q + (p >> 1)) = (uint16_t)(sb | (sb2 << 8));
       }
     } else {
       uint32_t xbyte = 0;
@@ -158,46 +177,67 @@ __device__ __forceinline__ void merge_pack(const LaneMap& L, bool store, int m, 
         word |= code << (4 * c);
       }
       if (!(amax > 0.0f)) word = 0u;
-      if (store) {
-        *(uint32_t*)(ik_e + 16 * q + 4 * p) = word;
-        if (p == 0) iks_e[q] = (uint8_t)xbyte;
-      }
+      xbytes |= xbyte << (8 * q);
+      if (store) *(uint32_t*)(idx_e + 16 * q + 4 * p) = word;
     }
   }
+  if (!L.latent && store && p == 0) st.iks[L.el] = xbytes;
 }
 
-// 16 entries x 32 scale bytes from LDS = 32 stores of 16 B (threads 0..31);
-// row_of(ent) gives the cache row of entry slot ent, or -1 to skip it.
+// Writes the staged rows of the workgroup's entries with 16-byte stores (the
+// E8M0 bytes with one 4-byte store per entry). row_of(ent) gives the cache row
+// of entry slot ent, or -1 to skip it. Every thread calls it after a barrier.
 template <typename RowOf>
-__device__ __forceinline__ void store_scales(const uint32_t (*lds_scale)[8], uint8_t* kv, RowOf row_of) {
-  if (threadIdx.x < 2 * CW_ENTRIES) {
-    const int ent = threadIdx.x >> 1, half = threadIdx.x & 1;
-    const int64_t r = row_of(ent);
-    if (r >= 0) {
-      u32x4_t v = {lds_scale[ent][4 * half + 0], lds_scale[ent][4 * half + 1], lds_scale[ent][4 * half + 2],
-                   lds_scale[ent][4 * half + 3]};
-      *(u32x4_t*)(kv + r * 288 + 256 + 16 * half) = v;
+__device__ __forceinline__ void store_staged(const Staging& st, uint8_t* kv, uint8_t* ik, uint8_t* iks,
+                                             RowOf row_of) {
+  constexpr int LAT_CHUNKS = CW_ENTRIES * 18;         // 288 B = 18 x 16 B per latent row
+  constexpr int IDX_CHUNKS = CW_ENTRIES * 4;          // 64 B = 4 x 16 B per indexer row
+  constexpr int TASKS = LAT_CHUNKS + IDX_CHUNKS + CW_ENTRIES;
+  for (int t = threadIdx.x; t < TASKS; t += CW_THREADS) {
+    if (t < LAT_CHUNKS) {
+      const int ent = t / 18, c = t - 18 * (t / 18);
+      const int64_t r = row_of(ent);
+      if (r >= 0) *(u32x4_t*)(kv + r * 288 + 16 * c) = *(const u32x4_t*)(st.lat + ent * CW_LAT_PITCH + 16 * c);
+    } else if (t < LAT_CHUNKS + IDX_CHUNKS) {
+      const int u = t - LAT_CHUNKS, ent = u >> 2, c = u & 3;
+      const int64_t r = row_of(ent);
+      if (r >= 0) *(u32x4_t*)(ik + r * 64 + 16 * c) = *(const u32x4_t*)(st.idx + ent * CW_IDX_PITCH + 16 * c);
+    } else {
+      const int ent = t - LAT_CHUNKS - IDX_CHUNKS;
+      const int64_t r = row_of(ent);
+      if (r >= 0) *(uint32_t*)(iks + r * 4) = st.iks[ent];
     }
   }
 }
 
+// Grid (entry blocks of 16, sequences). Sequence b's rows are x[b*T ..
+// b*T + n_b - 1] with n_b = n_tokens[b] clamped to [0, T] (T when n_tokens is
+// NULL); it gets floor(n_b / m) entries, written at cache rows row0_b + i with
+// row0_b = out_off[b] (b * floor(T / m) when out_off is NULL).
 template <int M>
 __global__ __launch_bounds__(CW_THREADS) void cache_write_kernel(
     const uint16_t* __restrict__ x_lat, const uint16_t* __restrict__ x_idx,
-    const float* __restrict__ w_lat, const float* __restrict__ w_idx,
-    int64_t n_total, int64_t E, int64_t T, int m_rt,
+    const float* __restrict__ w_lat, const float* __restrict__ w_idx, int64_t T, int m_rt,
+    const int64_t* __restrict__ n_tokens, const int64_t* __restrict__ out_off,
     uint8_t* __restrict__ kv, uint8_t* __restrict__ ik, uint8_t* __restrict__ iks) {
   const int m = M > 0 ? M : m_rt;
-  __shared__ uint32_t lds_scale[CW_ENTRIES][8];   // 32 latent scale bytes per entry
+  __shared__ Staging st;
   // the merge weights, staged once per workgroup (every entry uses the same ones)
   extern __shared__ __attribute__((aligned(16))) float lds_w[];
 
+  const int b = blockIdx.y;
+  int64_t nb = T;
+  if (n_tokens) nb = min(max(n_tokens[b], (int64_t)0), T);
+  const int64_t Eb = nb / m;
+  const int64_t e0 = (int64_t)blockIdx.x * CW_ENTRIES;
+  if (e0 >= Eb) return;                                // uniform over the workgroup
+  const int64_t row0 = (out_off ? out_off[b] : (int64_t)b * (T / m)) + e0;
+  const int cnt = (int)min((int64_t)CW_ENTRIES, Eb - e0);
+
   const LaneMap L(threadIdx.x);
-  const int64_t e = (int64_t)blockIdx.x * CW_ENTRIES + L.el;
-  const bool valid = e < n_total;
-  const int64_t eb = valid ? e / E : 0, ei = valid ? e - eb * E : 0;
-  const int64_t row0 = eb * T + ei * (int64_t)m;
-  const uint16_t* xb = (L.latent ? x_lat : x_idx) + row0 * L.C + 8 * L.p;
+  const bool valid = L.el < cnt;
+  const int64_t ei = valid ? e0 + L.el : 0;
+  const uint16_t* xb = (L.latent ? x_lat : x_idx) + ((int64_t)b * T + ei * m) * L.C + 8 * L.p;
 
   // with m fixed at compile time, the rows are requested before the weights
   // are staged, so their latency overlaps the staging
@@ -219,21 +259,18 @@ __global__ __launch_bounds__(CW_THREADS) void cache_write_kernel(
         return M > 0 ? xr[j < MR ? j : 0][q]
                      : __builtin_nontemporal_load((const u32x4_t*)(xb + (int64_t)j * L.C + L.qstride * q));
       },
-      kv + e * 288, ik + e * 64, iks + e * 4, (uint8_t*)&lds_scale[L.el][0]);
+      st);
 
   __syncthreads();
-  store_scales(lds_scale, kv, [&](int ent) -> int64_t {
-    const int64_t e2 = (int64_t)blockIdx.x * CW_ENTRIES + ent;
-    return e2 < n_total ? e2 : -1;
-  });
+  store_staged(st, kv, ik, iks, [&](int ent) -> int64_t { return ent < cnt ? row0 + ent : -1; });
 }
 
 // Decode-time append ([FP4] section "Le compte par couche": one entry per m
 // tokens; a trailing partial group waits): one token per sequence. Workgroup =
 // 16 sequences, lanes as in cache_write_kernel. A sequence whose staged count
 // plus this token reaches m merges its m - 1 staged rows and the token into
-// the entry at row entry_offset[b] + n_entries[b] (when that is below
-// `capacity`; otherwise the group is dropped and dropped[b] is set) and
+// the entry at row entry_offset[b] + n_entries[b] (when n_entries[b] is below
+// its capacity[b]; otherwise the group is dropped and dropped[b] is set) and
 // clears its stage; any other sequence copies the token into stage row
 // stage_count[b]. The counters are updated after the workgroup's barrier, by
 // one lane per sequence, once every lane has read them. With m == 1 there is
@@ -243,10 +280,10 @@ __global__ __launch_bounds__(CW_THREADS) void cache_append_kernel(
     const uint16_t* __restrict__ x_lat, const uint16_t* __restrict__ x_idx,
     const float* __restrict__ w_lat, const float* __restrict__ w_idx, int B, int m_rt,
     uint16_t* __restrict__ st_lat, uint16_t* __restrict__ st_idx, int32_t* __restrict__ st_count,
-    const int64_t* __restrict__ entry_offset, int32_t* __restrict__ n_entries, int64_t capacity,
+    const int64_t* __restrict__ entry_offset, int32_t* __restrict__ n_entries, const int64_t* __restrict__ capacity,
     uint8_t* __restrict__ kv, uint8_t* __restrict__ ik, uint8_t* __restrict__ iks, int32_t* __restrict__ dropped) {
   const int m = M > 0 ? M : m_rt;
-  __shared__ uint32_t lds_scale[CW_ENTRIES][8];
+  __shared__ Staging st;
   __shared__ int64_t lds_row[CW_ENTRIES];        // cache row written for each sequence slot, or -1
   extern __shared__ __attribute__((aligned(16))) float lds_w[];
 
@@ -259,6 +296,7 @@ __global__ __launch_bounds__(CW_THREADS) void cache_append_kernel(
   const int32_t cnt_raw = st_count[bs];
   const int32_t ne = n_entries[bs];
   const int64_t eoff = entry_offset[bs];
+  const int64_t cap = capacity[bs];
   const uint16_t* tok = (L.latent ? x_lat : x_idx) + (int64_t)bs * L.C + 8 * L.p;
   uint16_t* stg = (L.latent ? st_lat : st_idx) + (int64_t)bs * (m - 1) * L.C + 8 * L.p;
   u32x4_t tk[4];
@@ -276,7 +314,7 @@ __global__ __launch_bounds__(CW_THREADS) void cache_append_kernel(
   // (a count outside [0, m-1] is taken as m-1, so no access leaves the stage)
   const int cnt = seq ? min(max((int)cnt_raw, 0), m - 1) : 0;
   const bool complete = seq && cnt + 1 >= m;
-  const bool write = complete && ne >= 0 && (int64_t)ne < capacity;
+  const bool write = complete && ne >= 0 && (int64_t)ne < cap;
   const int64_t row = write ? eoff + ne : -1;
   if (seq && !complete) {
 #pragma unroll
@@ -285,7 +323,6 @@ __global__ __launch_bounds__(CW_THREADS) void cache_append_kernel(
   if (L.latent && L.p == 0) lds_row[L.el] = row;
   __syncthreads();
 
-  const int64_t r = write ? row : 0;
   merge_pack<M>(
       L, write, m, lds_w,
       [&](int j, int q) -> u32x4_t {
@@ -293,10 +330,10 @@ __global__ __launch_bounds__(CW_THREADS) void cache_append_kernel(
         if (M > 1) return sr[j < MS ? j : 0][q];
         return *(const u32x4_t*)(stg + (int64_t)j * L.C + L.qstride * q);
       },
-      kv + r * 288, ik + r * 64, iks + r * 4, (uint8_t*)&lds_scale[L.el][0]);
+      st);
 
   __syncthreads();
-  store_scales(lds_scale, kv, [&](int ent) -> int64_t { return lds_row[ent]; });
+  store_staged(st, kv, ik, iks, [&](int ent) -> int64_t { return lds_row[ent]; });
   if (seq && L.latent && L.p == 0) {
     st_count[b] = complete ? 0 : cnt + 1;
     if (write) n_entries[b] = ne + 1;
@@ -305,27 +342,30 @@ __global__ __launch_bounds__(CW_THREADS) void cache_append_kernel(
 }
 
 hipError_t launch_cache_write(const uint16_t* x_lat, const uint16_t* x_idx, const float* w_lat,
-                              const float* w_idx, int B, int64_t T, int m, uint8_t* kv, uint8_t* ik,
-                              uint8_t* iks, hipStream_t stream) {
-  const int64_t E = T / m;
-  const int64_t n_total = (int64_t)B * E;
-  if (n_total == 0) return hipSuccess;
-  const int64_t blocks = (n_total + CW_ENTRIES - 1) / CW_ENTRIES;
-  dim3 grid((unsigned)blocks), block(CW_THREADS);
+                              const float* w_idx, int B, int64_t T, int m, const int64_t* n_tokens,
+                              const int64_t* out_entry_offset, uint8_t* kv, uint8_t* ik, uint8_t* iks,
+                              hipStream_t stream) {
+  const int64_t E = T / m;                             // entries of the longest possible sequence
+  if (E == 0) return hipSuccess;
+  dim3 grid((unsigned)((E + CW_ENTRIES - 1) / CW_ENTRIES), (unsigned)B), block(CW_THREADS);
   const size_t lds = (size_t)m * 640 * sizeof(float);   // the staged merge weights
+#define CSA2_WRITE(Mv)                                                                                     \
+  hipLaunchKernelGGL(cache_write_kernel<Mv>, grid, block, lds, stream, x_lat, x_idx, w_lat, w_idx, T, m, \
+                     n_tokens, out_entry_offset, kv, ik, iks)
   switch (m) {
-    case 1: hipLaunchKernelGGL(cache_write_kernel<1>, grid, block, lds, stream, x_lat, x_idx, w_lat, w_idx, n_total, E, T, m, kv, ik, iks); break;
-    case 2: hipLaunchKernelGGL(cache_write_kernel<2>, grid, block, lds, stream, x_lat, x_idx, w_lat, w_idx, n_total, E, T, m, kv, ik, iks); break;
-    case 4: hipLaunchKernelGGL(cache_write_kernel<4>, grid, block, lds, stream, x_lat, x_idx, w_lat, w_idx, n_total, E, T, m, kv, ik, iks); break;
-    default: hipLaunchKernelGGL(cache_write_kernel<0>, grid, block, lds, stream, x_lat, x_idx, w_lat, w_idx, n_total, E, T, m, kv, ik, iks); break;
+    case 1: CSA2_WRITE(1); break;
+    case 2: CSA2_WRITE(2); break;
+    case 4: CSA2_WRITE(4); break;
+    default: CSA2_WRITE(0); break;
   }
+#undef CSA2_WRITE
   return hipGetLastError();
 }
 
 hipError_t launch_cache_append(const uint16_t* x_lat, const uint16_t* x_idx, const float* w_lat,
                                const float* w_idx, int B, int m, uint16_t* st_lat, uint16_t* st_idx,
                                int32_t* st_count, const int64_t* entry_offset, int32_t* n_entries,
-                               int64_t capacity, uint8_t* kv, uint8_t* ik, uint8_t* iks, int32_t* dropped,
+                               const int64_t* capacity, uint8_t* kv, uint8_t* ik, uint8_t* iks, int32_t* dropped,
                                hipStream_t stream) {
   dim3 grid((unsigned)((B + CW_ENTRIES - 1) / CW_ENTRIES)), block(CW_THREADS);
   const size_t lds = (size_t)m * 640 * sizeof(float);

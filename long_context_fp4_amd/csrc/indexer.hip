@@ -561,8 +561,10 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
       if (lane == 0) basei = atomicAdd(&st->ncand, (uint32_t)__popcll(bc));
       basei = readlane_u32(basei, 0);
       if (cnd) {
-        const uint32_t rank = (uint32_t)__popcll(bc & ((1ull << lane) - 1ull));
-        cb[basei + rank] = composite(key, (uint32_t)i);
+        // (ncand starts at zero: the control block is left zero by every
+        // completed call; the bound keeps a dirty counter inside the row)
+        const uint64_t at = (uint64_t)basei + (uint32_t)__popcll(bc & ((1ull << lane) - 1ull));
+        if (at < (uint64_t)cb_stride) cb[at] = composite(key, (uint32_t)i);
       }
     }
   }
@@ -630,10 +632,16 @@ __global__ __launch_bounds__(SEL_THREADS) void select_finish_kernel(
 // slot_pos: [B][pstride] slot -> position (NULL: slot == position, nslots =
 // min(n_entries[b], max_n)). score_by_pos: the score of a slot is
 // scores[position] (pool of a Full layer) rather than scores[slot].
+// A listed position is used when it lies in [0, n) and is greater than every
+// in-range position listed before it, so the used slots are in ascending
+// position order and distinct (a pool is written that way; out-of-order and
+// repeated entries of a caller's list are skipped) and slot order is position
+// order for the tie rule and the output.
 __global__ __launch_bounds__(SMALL_THREADS) void select_small_kernel(
     const float* __restrict__ scores, int64_t sstride, const int32_t* __restrict__ slot_pos,
     int pstride, int score_by_pos, const int32_t* __restrict__ n_entries, int64_t max_n, int K,
     int32_t* __restrict__ out, int out_stride) {
+  constexpr int PER = SMALL_MAX / SMALL_THREADS;   // 16 consecutive slots per thread
   __shared__ uint32_t keys[SMALL_MAX];
   __shared__ uint32_t valid[SMALL_MAX / 32];
   __shared__ uint32_t selbm[SMALL_MAX / 32];
@@ -647,26 +655,48 @@ __global__ __launch_bounds__(SMALL_THREADS) void select_small_kernel(
   const int32_t* sp = slot_pos ? slot_pos + (int64_t)b * pstride : nullptr;
   const float* sb = scores + (int64_t)b * sstride;
   int32_t* ob = out + (int64_t)b * out_stride;
-  const int lane = threadIdx.x & 63;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-  for (int i = threadIdx.x; i < SMALL_MAX / 32; i += SMALL_THREADS) { valid[i] = 0; selbm[i] = 0; }
-  __syncthreads();
-  uint32_t nvalid = 0;
-  for (int base = (threadIdx.x & ~63); base < nslots; base += SMALL_THREADS) {
-    const int i = base + lane;
-    bool ok = false;
-    uint32_t key = 0;
-    if (i < nslots) {
-      int64_t pos = sp ? (int64_t)sp[i] : (int64_t)i;
-      ok = pos >= 0 && pos < n_pos;
-      if (ok) key = score_key(sb[score_by_pos ? pos : (int64_t)i]);
-      keys[i] = key;
-    }
-    const uint64_t bal = __ballot(ok);
-    if (lane == 0) valid[base >> 5] = (uint32_t)bal;
-    if (lane == 32) valid[(base >> 5) + 1] = (uint32_t)(bal >> 32);
-    nvalid += ok ? 1u : 0u;
+  for (int i = tid; i < SMALL_MAX / 32; i += SMALL_THREADS) selbm[i] = 0;
+  // this thread's slots PER*tid .. +PER-1: positions (+1; 0 = not in range)
+  uint32_t pp[PER], lmax = 0;
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    const int i = PER * tid + q;
+    int64_t pos = -1;
+    if (i < nslots) pos = sp ? (int64_t)sp[i] : (int64_t)i;
+    pp[q] = (pos >= 0 && pos < n_pos) ? (uint32_t)pos + 1u : 0u;
+    lmax = max(lmax, pp[q]);
   }
+  // exclusive max over the threads before this one (slot order)
+  uint32_t incl = lmax;
+#pragma unroll
+  for (int sh = 1; sh < 64; sh <<= 1) {
+    const uint32_t o = (uint32_t)__shfl_up((int)incl, sh, 64);
+    if (lane >= sh) incl = max(incl, o);
+  }
+  if (lane == 63) scan_tmp[wave] = incl;
+  const uint32_t up = (uint32_t)__shfl_up((int)incl, 1, 64);
+  __syncthreads();
+  uint32_t run = lane > 0 ? up : 0u;
+  for (int v = 0; v < wave; ++v) run = max(run, scan_tmp[v]);
+  uint32_t m16 = 0, nvalid = 0;
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    const bool ok = pp[q] > run;
+    run = max(run, pp[q]);
+    if (ok) {
+      const int i = PER * tid + q;
+      keys[i] = score_key(sb[score_by_pos ? (int64_t)pp[q] - 1 : (int64_t)i]);
+      m16 |= 1u << q;
+      ++nvalid;
+    }
+  }
+  {
+    const uint32_t other = (uint32_t)__shfl_xor((int)m16, 1, 64);
+    if ((tid & 1) == 0) valid[tid >> 1] = m16 | (other << 16);
+  }
+  __syncthreads();
   uint32_t total;
   block_exclusive_scan(nvalid, scan_tmp, &total);
   if (total <= (uint32_t)K) {

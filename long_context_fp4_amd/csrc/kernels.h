@@ -25,9 +25,12 @@ constexpr int64_t kCtrlStride = 256 + 4 * kNumBins;   // 16640 bytes
 __host__ __device__ inline SelState* ctrl_state(uint8_t* ctrl, int b) { return (SelState*)(ctrl + b * kCtrlStride); }
 __host__ __device__ inline uint32_t* ctrl_hist(uint8_t* ctrl, int b) { return (uint32_t*)(ctrl + b * kCtrlStride + 256); }
 
+// n_tokens, out_entry_offset: device [B] or NULL (every sequence T tokens;
+// sequence b at rows b * floor(T / m) ..).
 hipError_t launch_cache_write(const uint16_t* x_lat, const uint16_t* x_idx, const float* w_lat,
-                              const float* w_idx, int B, int64_t T, int m, uint8_t* kv, uint8_t* ik,
-                              uint8_t* iks, hipStream_t stream);
+                              const float* w_idx, int B, int64_t T, int m, const int64_t* n_tokens,
+                              const int64_t* out_entry_offset, uint8_t* kv, uint8_t* ik, uint8_t* iks,
+                              hipStream_t stream);
 // Prefill: the decode batch of B * Tq per-query views of B sequences.
 hipError_t launch_prefill_views(const int64_t* entry_offset, const int32_t* n_entries, const int64_t* pos, int m,
                                 int B, int Tq, int64_t* eo, int32_t* ne, hipStream_t stream);
@@ -42,7 +45,7 @@ hipError_t launch_swa_attention(const uint8_t* win, const int32_t* n_win, const 
 hipError_t launch_cache_append(const uint16_t* x_lat, const uint16_t* x_idx, const float* w_lat,
                                const float* w_idx, int B, int m, uint16_t* st_lat, uint16_t* st_idx,
                                int32_t* st_count, const int64_t* entry_offset, int32_t* n_entries,
-                               int64_t capacity, uint8_t* kv, uint8_t* ik, uint8_t* iks, int32_t* dropped,
+                               const int64_t* capacity, uint8_t* kv, uint8_t* ik, uint8_t* iks, int32_t* dropped,
                                hipStream_t stream);
 
 // Selection modes of the score pass.

@@ -127,12 +127,32 @@ def full_layer(ik_rows, iks_rows, q_idx_bits, w, mode, k=512, pool_k=0):
     return topk(s, pos, k), None, s
 
 
+def used_candidates(cand, n):
+    """The entries of a Reindex candidate list that a layer scores.
+
+    Reading taken (the pages only say that deeper layers look at the Full
+    layer's pool, which is a set of distinct positions and is kept in
+    ascending order here): a listed position is used when it lies in [0, n)
+    and is larger than every in-range position listed before it. A pool
+    written by a Full layer passes unchanged; for another list this keeps the
+    running record values, so the used positions are distinct and ascending.
+    """
+    out = []
+    best = -1
+    for c in np.asarray(cand).tolist():
+        if 0 <= c < n:
+            if c > best:
+                out.append(c)
+            best = max(best, c)
+    return np.asarray(out, dtype=np.int64)
+
+
 def reindex_layer(ik_rows, iks_rows, pool, q_idx_bits, w, mode, k=512):
     """Reindex layer of one sequence: rescore the pool rows of the shared key, take top-k.
 
-    Returns (topk int32 [k], pool scores float32 [len(members)]).
+    The rows rescored are used_candidates(pool, n). Returns (topk int32 [k],
+    scores float32 [len(members)] of those rows).
     """
-    members = np.asarray(pool)
-    members = members[members >= 0].astype(np.int64)
+    members = used_candidates(pool, ik_rows.shape[0])
     s = scores(ik_rows[members], iks_rows[members], q_idx_bits, w, mode)
     return topk(s, members, k), s

@@ -45,19 +45,25 @@ def err(L):
 
 
 def test_cache_write_validation(L):
-    assert L.csa2_cache_write(None, P, P, P, 1, 10, 2, P, P, P, None) == -1
-    assert L.csa2_cache_write(P, P, P, P, 0, 10, 2, P, P, P, None) == -2
-    assert L.csa2_cache_write(P, P, P, P, 1, -1, 2, P, P, P, None) == -2
-    assert L.csa2_cache_write(P, P, P, P, 1, 10, 0, P, P, P, None) == -2
-    assert L.csa2_cache_write(P, P, P, P, 1, 10, 17, P, P, P, None) == -2
-    assert L.csa2_cache_write(P + 2, P, P, P, 1, 10, 2, P, P, P, None) == -3
-    assert L.csa2_cache_write(P, P, P, P, 1, 10, 2, P, P, P + 2, None) == -3   # iks needs 4 bytes
-    assert "aligned" in err(L)
+    def call(**kw):
+        a = dict(xl=P, xi=P, wl=P, wi=P, B=1, T=10, m=2, nt=None, off=None, kv=P, ik=P, iks=P)
+        a.update(kw)
+        return L.csa2_cache_write(a["xl"], a["xi"], a["wl"], a["wi"], a["B"], a["T"], a["m"], a["nt"], a["off"],
+                                  a["kv"], a["ik"], a["iks"], None)
+    assert call(xl=None) == -1
+    assert call(iks=None) == -1
+    assert call(B=0) == -2 and call(B=65536) == -2
+    assert call(T=-1) == -2
+    assert call(m=0) == -2 and call(m=17) == -2
+    assert call(xl=P + 2) == -3
+    assert call(iks=P + 2) == -3 and "aligned" in err(L)     # iks needs 4 bytes
+    assert call(nt=P + 8) == -3                               # token counts and offsets: 16 bytes
+    assert call(off=P + 8) == -3
 
 
 def test_cache_append_validation(L):
     def call(**kw):
-        a = dict(xl=P, xi=P, wl=P, wi=P, B=2, m=2, sl=P, si=P, sc=P, off=P, n=P, cap=10, kv=P, ik=P, iks=P, dr=None)
+        a = dict(xl=P, xi=P, wl=P, wi=P, B=2, m=2, sl=P, si=P, sc=P, off=P, n=P, cap=P, kv=P, ik=P, iks=P, dr=None)
         a.update(kw)
         return L.csa2_cache_append(a["xl"], a["xi"], a["wl"], a["wi"], a["B"], a["m"], a["sl"], a["si"], a["sc"],
                                    a["off"], a["n"], a["cap"], a["kv"], a["ik"], a["iks"], a["dr"], None)
@@ -66,7 +72,8 @@ def test_cache_append_validation(L):
     assert call(sl=None) == -1            # m > 1 needs the stage
     assert call(B=0) == -2 and call(B=1025) == -2
     assert call(m=0) == -2 and call(m=17) == -2
-    assert call(cap=-1) == -2
+    assert call(cap=None) == -1           # the per-sequence capacities
+    assert call(cap=P + 8) == -3
     assert call(xl=P + 2) == -3
     assert call(iks=P + 2) == -3          # 4-byte alignment
     assert call(sc=P + 2) == -3

@@ -9,24 +9,28 @@ from tests.gpu_util import dev, host
 pytestmark = pytest.mark.gpu
 
 
-def run_append(m, B, cap, steps, seed):
+def run_append(m, B, cap, steps, seed, ragged=False):
+    """cap: rows reserved per sequence; ragged: each sequence gets its own capacity in
+    [0, cap] and the sequences' row ranges are packed back to back with one spare row
+    between neighbours (which must stay untouched)."""
     import torch
     import long_context_fp4_amd as L
     rng = np.random.default_rng(seed)
     w_lat = synth.merge_weights(rng, m, 512)
     w_idx = synth.merge_weights(rng, m, 128)
-    n0 = rng.integers(0, cap + 1, B).astype(np.int32)
-    n0[B // 2] = cap                                   # one sequence starts full: its groups are dropped
+    caps = rng.integers(0, cap + 1, B).astype(np.int64) if ragged else np.full(B, cap, np.int64)
+    n0 = np.array([rng.integers(0, c + 1) for c in caps], np.int32)
+    n0[B // 2] = caps[B // 2]                          # one sequence starts full: its groups are dropped
     c0 = rng.integers(0, m, B).astype(np.int32)
     st_lat0 = synth.hidden_host(rng, (B, max(m - 1, 1), 512))
     st_idx0 = synth.hidden_host(rng, (B, max(m - 1, 1), 128))
     tok_lat = synth.hidden_host(rng, (steps, B, 512))
     tok_idx = synth.hidden_host(rng, (steps, B, 128))
-    stride = cap + 1                                   # one spare row per sequence: must stay untouched
-    off = (np.arange(B) * stride).astype(np.int64)
-    kv0 = rng.integers(0, 256, (B * stride, 288), dtype=np.uint8)
-    ik0 = rng.integers(0, 256, (B * stride, 64), dtype=np.uint8)
-    iks0 = rng.integers(0, 256, (B * stride, 4), dtype=np.uint8)
+    off = np.concatenate([[0], np.cumsum(caps + 1)[:-1]]).astype(np.int64)   # one spare row after each
+    rows_total = int(off[-1] + caps[-1] + 1)
+    kv0 = rng.integers(0, 256, (rows_total, 288), dtype=np.uint8)
+    ik0 = rng.integers(0, 256, (rows_total, 64), dtype=np.uint8)
+    iks0 = rng.integers(0, 256, (rows_total, 4), dtype=np.uint8)
 
     kv, ik, iks = dev(kv0), dev(ik0), dev(iks0)
     st_lat = dev(st_lat0[:, : m - 1]) if m > 1 else None
@@ -36,7 +40,7 @@ def run_append(m, B, cap, steps, seed):
     drops = np.zeros(B, np.int64)
     for t in range(steps):
         L.cache_append(dev(tok_lat[t]), dev(tok_idx[t]), dev(w_lat), dev(w_idx), m, st_lat, st_idx, cnt, dev(off),
-                       n, cap, kv, ik, iks, dropped=dropped)
+                       n, dev(caps), kv, ik, iks, dropped=dropped)
         torch.cuda.synchronize()
         drops += host(dropped)
     kv, ik, iks, cnt, n = host(kv), host(ik), host(iks), host(cnt), host(n)
@@ -46,7 +50,7 @@ def run_append(m, B, cap, steps, seed):
         stream_lat = np.concatenate([st_lat0[b, : c0[b]], tok_lat[:, b]])
         stream_idx = np.concatenate([st_idx0[b, : c0[b]], tok_idx[:, b]])
         okv, oik, oiks, rest_lat, rest_idx = OC.append_tokens(stream_lat, stream_idx, w_lat, w_idx, m)
-        room = cap - int(n0[b])
+        room = int(caps[b]) - int(n0[b])
         take = min(len(okv), room)
         rows = slice(off[b] + n0[b], off[b] + n0[b] + take)
         ekv[rows], eik[rows], eiks[rows] = okv[:take], oik[:take], oiks[:take]
@@ -69,3 +73,10 @@ def test_append_one_token_at_a_time(m):
 def test_append_many_sequences():
     """More sequences than one workgroup takes (16), ratio 2."""
     run_append(2, B=41, cap=3, steps=7, seed=77)
+
+
+@pytest.mark.parametrize("m", [1, 2])
+def test_append_ragged_capacities(m):
+    """Per-sequence capacities (some 0) with the row ranges packed back to back: a
+    sequence that fills up drops its groups and never writes into its neighbour's rows."""
+    run_append(m, B=23, cap=5, steps=9, seed=900 + m, ragged=True)

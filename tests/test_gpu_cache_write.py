@@ -52,6 +52,42 @@ def test_ratios_and_ragged_tails(m, T, B):
                 f"m={m},T={T},B={B}")
 
 
+@pytest.mark.parametrize("m", [1, 2, 3])
+def test_ragged_batch_one_launch(m):
+    """Sequences of different lengths (one empty, one shorter than m) padded to the longest,
+    written in one call at per-sequence offsets into one buffer with gaps between the
+    sequences: each sequence's rows bit-exact, the gap rows untouched."""
+    import torch
+    import long_context_fp4_amd as L
+    rng = np.random.default_rng(300 + m)
+    lens = np.array([517, 0, m - 1, 2048, 35, 1000], np.int64)
+    B, T = len(lens), int(lens.max())
+    w_lat = synth.merge_weights(rng, m, 512)
+    w_idx = synth.merge_weights(rng, m, 128)
+    x_lat = synth.hidden_host(rng, (B, T, 512), outliers=np.array([7]))
+    x_idx = synth.hidden_host(rng, (B, T, 128))
+    ents = lens // m
+    off = np.zeros(B, np.int64)
+    cur = 3
+    for b in rng.permutation(B):                       # sequences placed out of order, with gaps
+        off[b] = cur
+        cur += int(ents[b]) + int(rng.integers(0, 5))
+    rows = cur + 4
+    kv0 = rng.integers(0, 256, (rows, 288), dtype=np.uint8)
+    ik0 = rng.integers(0, 256, (rows, 64), dtype=np.uint8)
+    iks0 = rng.integers(0, 256, (rows, 4), dtype=np.uint8)
+    kv, ik, iks = dev(kv0), dev(ik0), dev(iks0)
+    L.cache_write(dev(x_lat), dev(x_idx), dev(w_lat), dev(w_idx), m, kv=kv, ik=ik, iks=iks,
+                  n_tokens=dev(lens), out_entry_offset=dev(off))
+    torch.cuda.synchronize()
+    ekv, eik, eiks = kv0.copy(), ik0.copy(), iks0.copy()
+    for b in range(B):
+        okv, oik, oiks = OC.cache_write(x_lat[b, :lens[b]], x_idx[b, :lens[b]], w_lat, w_idx, m)
+        r = slice(int(off[b]), int(off[b]) + len(okv))
+        ekv[r], eik[r], eiks[r] = okv, oik, oiks
+    assert_same((host(kv), host(ik), host(iks)), (ekv, eik, eiks), f"ragged m={m}")
+
+
 def test_hand_worked_blocks():
     g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "quant_examples.json")))
     lat = [b["x"] for b in g["latent_blocks"]]

@@ -69,13 +69,15 @@ def test_layer_group_full_reindex_reuse(n_list, pool_k):
         check_attention(kv[rows], topR[b], qU[b], outU[b], lseU[b], f"reuse attention {b}")
 
 
-def test_decode128k_full_size_sampled():
+def test_decode128k_full_size():
     """32 sequences x 131072 tokens (65536 ratio-2 entries), one Full layer, as the benchmark runs it.
 
-    Sequences 0 and 31: cache bytes bit-exact, scores, top-512 and attention against the oracle.
-    On the same cache, as the benchmark's legs run them: the quantized-query variant of the layer
-    (sequences 0 and 31, within its accumulation bound) and the prefill of 32 query tokens at the
-    last 32 positions of sequence 0 (queries 0, 17 and 31 checked).
+    Every sequence: the oracle's scores, top-512 and attention over the GPU-written cache
+    bytes; sequences 0 and 31 also have those bytes checked bit-exact against the oracle's
+    cache write of their hidden states. On the same cache, as the benchmark's legs run them:
+    the quantized-query variant of the layer (sequences 0 and 31, within its accumulation
+    bound) and the prefill of 32 query tokens at the last 32 positions of sequence 0
+    (queries 0, 17 and 31 checked).
     """
     import torch
     import long_context_fp4_amd as L
@@ -99,15 +101,19 @@ def test_decode128k_full_size_sampled():
                                       q_idx=dev(Lr["q_idx"]), w=dev(Lr["w"]), k=w.k)
     torch.cuda.synchronize()
     top, out, lse = host(top), host(out), host(lse)
+    hkv, hik, hiks = host(kv), host(ik), host(iks)
     for b, (xl, xi) in hidden.items():
         okv, oik, oiks = OC.cache_write(xl, xi, p["w_lat"], p["w_idx"], w.m)
-        assert np.array_equal(host(kv[b * E:(b + 1) * E]), okv)
-        assert np.array_equal(host(ik[b * E:(b + 1) * E]), oik)
-        assert np.array_equal(host(iks[b * E:(b + 1) * E]), oiks)
-        s = OI.scores(oik, oiks, Lr["q_idx"][b], Lr["w"][b], 1)
-        check_topk(top[b], OI.topk(s, np.arange(E), w.k), lambda q: s[q], w.k, f"seq{b}")
-        check_attention(okv, top[b], Lr["q"][b], out[b], lse[b], f"attention seq{b}")
+        assert np.array_equal(hkv[b * E:(b + 1) * E], okv)
+        assert np.array_equal(hik[b * E:(b + 1) * E], oik)
+        assert np.array_equal(hiks[b * E:(b + 1) * E], oiks)
         hidden[b] = (okv, oik, oiks)
+    for b in range(w.B):
+        rows = slice(b * E, (b + 1) * E)
+        s = OI.scores(hik[rows], hiks[rows], Lr["q_idx"][b], Lr["w"][b], 1)
+        check_topk(top[b], OI.topk(s, np.arange(E), w.k), lambda q: s[q], w.k, f"seq{b}")
+        check_attention(hkv[rows], top[b], Lr["q"][b], out[b], lse[b], f"attention seq{b}")
+    del hkv, hik, hiks
 
     # the quantized-query variant of the same layer
     from tests.test_gpu_qmx import qmx_bound

@@ -118,6 +118,36 @@ def test_pool_then_topk_and_reindex():
                    f"reindex seq{b}")
 
 
+def test_reindex_unordered_candidate_list():
+    """A caller's candidate list out of order, with repeated and out-of-range positions:
+    only the records (greater than every earlier in-range entry) are scored, the
+    top-k is ascending and distinct, as the oracle's rule gives."""
+    rng = np.random.default_rng(12)
+    n_list = [30000, 5000]
+    ik, iks, off = make_keys(rng, n_list)
+    B, S = len(n_list), 9000
+    cand = np.full((B, S), -1, np.int32)
+    for b, n in enumerate(n_list):
+        nb = min(6000, n - 500)
+        base = np.sort(rng.choice(n, size=nb, replace=False)).astype(np.int32)
+        lst = np.concatenate([base, base[rng.integers(0, nb, 1500)], rng.integers(-5, n + 50, 1500)])
+        seg = rng.integers(0, len(lst) - 200)
+        lst[seg:seg + 200] = rng.permutation(lst[seg:seg + 200])     # a shuffled stretch
+        cand[b, :len(lst)] = lst
+    q = np.stack([synth.indexer_query(rng, 16) for _ in range(B)])
+    w = np.stack([synth.head_weights(rng, 16) for _ in range(B)])
+    top, _, _ = run(ik, iks, off, n_list, max(n_list), q, w, 1, 512, cand=cand)
+    for b, n in enumerate(n_list):
+        rows = slice(off[b], off[b] + n)
+        used = OI.used_candidates(cand[b], n)
+        assert len(used) > 512
+        s_used = OI.scores(ik[rows][used], iks[rows][used], q[b], w[b], 1)
+        otop, _ = OI.reindex_layer(ik[rows], iks[rows], cand[b], q[b], w[b], 1, k=512)
+        lookup = dict(zip(used.tolist(), s_used.tolist()))
+        check_topk(top[b], otop, lambda p: np.array([lookup[int(x)] for x in p], np.float32), 512,
+                   f"unordered cand seq{b}")
+
+
 @pytest.mark.parametrize("n", [3000, 40000])
 def test_exact_ties_take_the_lowest_positions(n):
     """Identical rows give identical scores: the top-k must be exactly positions 0..k-1."""

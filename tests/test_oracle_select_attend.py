@@ -85,6 +85,24 @@ def test_full_topk_is_inside_the_pool_and_reindex_with_same_query_agrees():
     assert np.array_equal(top, top2)
 
 
+def test_used_candidates_rule():
+    """A pool (distinct, ascending, -1 padded) passes unchanged; for any list the used
+    entries are the left-to-right records among the in-range ones, checked against an
+    O(n^2) brute force over every prefix."""
+    pool = np.array([2, 5, 9, 40, -1, -1])
+    assert list(I.used_candidates(pool, 50)) == [2, 5, 9, 40]
+    assert list(I.used_candidates(pool, 10)) == [2, 5, 9]          # 40 is out of range
+    rng = np.random.default_rng(8)
+    for trial in range(20):
+        n = int(rng.integers(1, 60))
+        lst = rng.integers(-3, n + 5, size=int(rng.integers(0, 80)))
+        got = list(I.used_candidates(lst, n))
+        want = [int(c) for i, c in enumerate(lst)
+                if 0 <= c < n and all(not (0 <= d < n) or d < c for d in lst[:i])]
+        assert got == want
+        assert all(a < b for a, b in zip(got, got[1:]))            # distinct, ascending
+
+
 def test_dense_attention_matches_torch_sdpa():
     rng = np.random.default_rng(5)
     kv, _, _ = random_cache(rng, 300)
