@@ -22,14 +22,11 @@
  * - Alignment: every data pointer must be 16-byte aligned (CSA2_ERR_ALIGN),
  *   except the E8M0 key-scale array iks, which needs 4 bytes (one entry's row),
  *   so that a cache can start at any entry of a larger buffer.
- * - Workspaces: a workspace must be zero-filled by the caller before its
- *   first use (e.g. allocated with zeros). In every call's layout its first
- *   CSA2_MAX_BATCH * 16640 bytes hold one control block per sequence index
- *   (selection state and a score histogram), which every successful call
- *   leaves zero again; the rest is scratch. One workspace can therefore be
- *   reused by later calls of any kind and size without clearing. Calls that
- *   share a workspace must not overlap (use one stream or separate
- *   workspaces).
+ * - Workspaces: scratch device memory of at least the size the matching
+ *   *_workspace_bytes call returns. It needs no initialisation and holds no
+ *   state between calls (every kernel writes what it reads), so one workspace
+ *   can serve later calls of any kind and size. Calls that share a workspace
+ *   must not overlap (use one stream or separate workspaces).
  * - Thread safety: the library holds no global mutable state apart from the
  *   thread-local last-error message.
  */
@@ -235,9 +232,13 @@ int csa2_swa_attention(const uint8_t* win, const int32_t* n_win, const uint16_t*
  *                  -1 padded); topk is then chosen from the pool. Full only.
  *   scores_out     NULL, or out f32 [B][max_n] (Full) / [B][cand_stride] (Reindex):
  *                  the float32 scores, for inspection
- *   workspace      csa2_indexer_workspace_bytes(B, max_n, cand_stride) bytes
+ *   workspace      csa2_indexer_workspace_bytes(B, max_n, k, pool_k, cand_stride) bytes
+ *                  (cand_stride 0 without a candidate list)
+ * Selection: with k <= 512 every score workgroup keeps the keys above a local
+ * cutoff and a finish merges them (the pool the same way from a second list);
+ * k > 512 takes a threshold-bin pass. Both are exact.
  */
-size_t csa2_indexer_workspace_bytes(int B, int64_t max_n, int cand_stride);
+size_t csa2_indexer_workspace_bytes(int B, int64_t max_n, int k, int pool_k, int cand_stride);
 int csa2_indexer_topk(const uint8_t* ik, const uint8_t* iks,
                       const int64_t* entry_offset, const int32_t* n_entries,
                       int B, int64_t max_n,
@@ -278,12 +279,14 @@ int csa2_sparse_attention(const uint8_t* kv, const int64_t* entry_offset, const 
  *                      -> attention
  *   mode CSA2_REUSE:   topk (in) -> attention; q_idx, w, pool unused
  * Arguments mean what they mean in csa2_indexer_topk and csa2_sparse_attention.
- * workspace: csa2_decode_workspace_bytes(B, max_n, H, k, pool_k) bytes. In
- * CSA2_FULL mode with pool_k == 0, k <= 512 and max_n > 16384 the top-k is
- * finished inside the attention launch (topk is still written); the workspace
- * then also holds scratch rows for every attention workgroup (about
- * 12 * max_n bytes each), unless those would exceed 4 GiB, in which case the
- * top-k finish runs as a launch of its own.
+ * workspace: csa2_decode_workspace_bytes(B, max_n, H, k, pool_k) bytes (one
+ * buffer serves all three modes). With k <= 512 (and max_n > 16384 for a Full
+ * layer) a layer is two launches: the scoring pass, then the attention, whose
+ * workgroups first finish the top-k themselves (topk is still written); a Full
+ * layer's pool is finished by B more workgroups of that launch. The workspace
+ * then also holds scratch rows for every such workgroup (about 12 * max(max_n,
+ * pool_k) bytes each), unless those would exceed 4 GiB, in which case the
+ * finishes run as launches of their own.
  */
 size_t csa2_decode_workspace_bytes(int B, int64_t max_n, int H, int k, int pool_k);
 int csa2_decode_layer(int mode,

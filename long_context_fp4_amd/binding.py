@@ -52,7 +52,7 @@ def lib():
     L.csa2_swa_write.restype = i32
     L.csa2_swa_attention.argtypes = [vp, vp, vp, i32, i32, f32, vp, vp, vp]
     L.csa2_swa_attention.restype = i32
-    L.csa2_indexer_workspace_bytes.argtypes = [i32, i64, i32]
+    L.csa2_indexer_workspace_bytes.argtypes = [i32, i64, i32, i32, i32]
     L.csa2_indexer_workspace_bytes.restype = sz
     L.csa2_indexer_topk.argtypes = [vp, vp, vp, vp, i32, i64, vp, vp, i32, i32, vp, i32, i32, vp, i32, vp,
                                     vp, vp, sz, vp]
@@ -112,7 +112,7 @@ def _bf16_types():
 
 
 class Workspace:
-    """Zero-initialised device workspace that grows on demand (one per stream of use)."""
+    """Device workspace that grows on demand (one per stream of use; needs no initialisation)."""
 
     def __init__(self, device="cuda"):
         self.device = device
@@ -122,7 +122,7 @@ class Workspace:
         torch = _torch()
         nbytes = max(int(nbytes), 256)
         if self.buf is None or self.buf.numel() < nbytes:
-            self.buf = torch.zeros(nbytes, dtype=torch.uint8, device=self.device)
+            self.buf = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
         return self.buf
 
 
@@ -310,7 +310,7 @@ def indexer_topk(ik, iks, entry_offset, n_entries, max_n, q_idx, w=None, score_m
     if want_scores:
         scores = torch.empty((B, cand_stride if cand is not None else max(int(max_n), 1)),
                              dtype=torch.float32, device=dev)
-    nbytes = lib().csa2_indexer_workspace_bytes(B, int(max_n), cand_stride)
+    nbytes = lib().csa2_indexer_workspace_bytes(B, int(max_n), k, pool_k, cand_stride)
     buf = _ws(workspace, dev).get(nbytes)
     _check(lib().csa2_indexer_topk(_ptr(ik, torch.uint8, "ik"), _ptr(iks, torch.uint8, "iks"),
                                    _ptr(entry_offset, torch.int64, "entry_offset"),

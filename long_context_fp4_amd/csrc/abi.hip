@@ -38,48 +38,40 @@ int hip_status(hipError_t e, const char* where) {
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-// Indexer workspace layout, all regions 256-byte aligned. The control region
-// comes first and always holds CSA2_MAX_BATCH blocks, so neither its place nor
-// the place of any block depends on B or max_n: the scratch regions behind it
-// can never overlap a control block of a later call with other sizes.
+// Indexer workspace layout, all regions 256-byte aligned. No region holds
+// state between calls (every kernel writes what it reads), so a workspace needs
+// no initialisation and can be reused by calls of any kind and size.
 struct IndexerWs {
-  size_t ctrl, bitmap, cand, scores, hdr, summ, wgc, gscr, total;
+  size_t ctrl, bitmap, cand, scores, hdr, summ, wgc, gscr, hdrp, wgcp, total;
   int64_t slots, bm_words, nblk, gscr_stride;
 };
 
-size_t ctrl_bytes();
-
-IndexerWs indexer_layout(int B, int64_t max_n, int cand_stride) {
+IndexerWs indexer_layout(int B, int64_t max_n, int k, int pool_k, int cand_stride) {
   IndexerWs L;
   L.slots = max_n > (int64_t)cand_stride ? max_n : (int64_t)cand_stride;
   if (L.slots < 1) L.slots = 1;
   L.bm_words = (L.slots + 31) / 32;
-  size_t off = 0;
-  L.ctrl = off;   off += ctrl_bytes();
-  L.bitmap = off; off = round_up(off + (size_t)B * L.bm_words * 4, 256);
-  L.cand = off;   off = round_up(off + (size_t)B * L.slots * 8, 256);
-  L.scores = off; off = round_up(off + (size_t)B * L.slots * 4, 256);
   L.nblk = (L.slots + csa2::kScoreChunk - 1) / csa2::kScoreChunk;
+  const bool thr = k > csa2::kDirectMaxK;          // the threshold path's regions
+  const bool pl = pool_k > 0;                      // the pool lists
+  size_t off = 0;
+  L.ctrl = off;   off = round_up(off + (size_t)B * csa2::kCtrlStride, 256);
+  L.bitmap = off; off = round_up(off + (thr ? (size_t)B * L.bm_words * 4 : 0), 256);
+  L.cand = off;   off = round_up(off + (thr ? (size_t)B * L.slots * 8 : 0), 256);
+  L.scores = off; off = round_up(off + (size_t)B * L.slots * 4, 256);
   L.hdr = off;    off = round_up(off + (size_t)B * L.nblk * 8, 256);
-  L.summ = off;   off = round_up(off + (size_t)B * L.nblk * csa2::kSumWords * 4, 256);
+  L.summ = off;   off = round_up(off + (thr ? (size_t)B * L.nblk * csa2::kSumWords * 4 : 0), 256);
   L.wgc = off;    off = round_up(off + (size_t)B * L.nblk * csa2::kCandCap * 8, 256);
   L.gscr_stride = L.slots > L.nblk * csa2::kCandCap ? L.slots : L.nblk * csa2::kCandCap;
   L.gscr = off;   off = round_up(off + (size_t)B * L.gscr_stride * 8, 256);
+  L.hdrp = off;   off = round_up(off + (pl ? (size_t)B * L.nblk * 8 : 0), 256);
+  L.wgcp = off;   off = round_up(off + (pl ? (size_t)B * L.nblk * csa2::kPoolCap * 8 : 0), 256);
   L.total = off;
   return L;
 }
 
-// Bytes of the control region that leads every workspace layout (indexer,
-// attention and decode alike), so one buffer can serve every call.
-size_t ctrl_bytes() { return round_up((size_t)CSA2_MAX_BATCH * csa2::kCtrlStride, 256); }
-
-// Scratch of the attention's split partials (placed after the control region
-// by csa2_sparse_attention, after the indexer regions by csa2_decode_layer).
-size_t attention_scratch(int B, int H, int k) {
-  const int S = csa2::attention_splits(B, H, k);
-  if (S <= 1) return 256;
-  return round_up((size_t)B * H * S * 514 * 4, 256);
-}
+// Scratch of the attention (its workgroups need none of their own).
+size_t attention_scratch(int, int, int) { return 256; }
 
 int check_indexer_args(const uint8_t* ik, const uint8_t* iks, const int64_t* entry_offset,
                        const int32_t* n_entries, int B, int64_t max_n, const uint16_t* q_idx,
@@ -140,6 +132,9 @@ csa2::SelBufs make_selbufs(const IndexerWs& L, uint8_t* ws) {
   sb.wgc_stride = L.nblk * csa2::kCandCap;
   sb.gscr = (uint64_t*)(ws + L.gscr);
   sb.gscr_stride = L.gscr_stride;
+  sb.hdrp = (uint64_t*)(ws + L.hdrp);
+  sb.wgcp = (uint64_t*)(ws + L.wgcp);
+  sb.wgcp_stride = L.nblk * csa2::kPoolCap;
   return sb;
 }
 
@@ -148,35 +143,42 @@ csa2::SelBufs make_selbufs(const IndexerWs& L, uint8_t* ws) {
 hipError_t score_full(const uint8_t* ik, const uint8_t* iks, const int64_t* entry_offset, const int32_t* n_entries,
                       int B, int64_t max_n, const uint16_t* q_idx, const float* w, int Hi, int score_mode,
                       float* scores, int64_t sstride, const csa2::SelBufs& sb, int sel, int K, bool store,
-                      hipStream_t stream) {
+                      int pool_k, hipStream_t stream) {
   hipEvent_t ev0 = g_ev_before, ev1 = g_ev_after;
   g_ev_before = g_ev_after = nullptr;
   hipError_t r;
   if (ev0 && (r = hipEventRecord(ev0, stream)) != hipSuccess) return r;
   r = csa2::launch_score(ik, iks, entry_offset, n_entries, B, max_n, q_idx, w, Hi, score_mode, nullptr, 0,
-                         scores, sstride, sb, sel, K, store, stream);
+                         scores, sstride, sb, sel, K, store, pool_k, stream);
   if (r != hipSuccess) return r;
   if (ev1 && (r = hipEventRecord(ev1, stream)) != hipSuccess) return r;
   return hipSuccess;
 }
 
-// A Full decode layer with a direct top-k (k <= kDirectMaxK, no pool, more
-// entries than the small path takes) runs the top-k finish inside the
-// attention: one scoring launch, then one attention launch. Every attention
-// workgroup gets scratch rows of its own for the finish's fallback; the plan
-// is off when they would exceed 4 GiB.
+// Which selection a call takes.
+bool direct_ok(int k) { return k <= csa2::kDirectMaxK; }
+bool small_full(int64_t max_n) { return max_n <= csa2::kSmallMax; }
+
+// A decode layer whose top-k is finished inside the attention launch (a Full
+// layer with k <= 512 and more entries than the small path takes, or a
+// Reindex layer with k <= 512): every attention workgroup, and the pool
+// workgroups of a Full layer with a pool, get scratch rows of their own for
+// the finish's fallback; the plan is off when they would exceed 4 GiB.
 struct FusedPlan {
   bool on;
   int64_t sstride, gstride;   // floats / composites per workgroup row
   size_t bytes;
 };
 
-FusedPlan fused_plan(int B, int64_t max_n, int H, int k, int pool_k) {
+FusedPlan fused_plan(int mode, int B, int64_t max_n, int H, int k, int pool_k) {
   FusedPlan f{false, 0, 0, 0};
-  if (pool_k != 0 || k > csa2::kDirectMaxK || max_n <= csa2::kSmallMax) return f;
-  const size_t G = (size_t)csa2::attention_workgroups(B, H, k);
-  f.sstride = (int64_t)round_up((size_t)max_n, 64);
-  f.gstride = (int64_t)round_up((size_t)(max_n > csa2::kFinLdsCands ? max_n : csa2::kFinLdsCands), 32);
+  if (!direct_ok(k)) return f;
+  if (mode == CSA2_FULL && small_full(max_n)) return f;
+  if (mode == CSA2_REUSE) return f;
+  const size_t G = (size_t)csa2::attention_workgroups(B, H, k) + (mode == CSA2_FULL && pool_k > 0 ? (size_t)B : 0);
+  const int64_t n = max_n > pool_k ? max_n : pool_k;
+  f.sstride = (int64_t)round_up((size_t)n, 64);
+  f.gstride = (int64_t)round_up((size_t)(n > csa2::kFinLdsCands ? n : csa2::kFinLdsCands), 32);
   f.bytes = round_up(G * (size_t)f.sstride * 4, 256) + round_up(G * (size_t)f.gstride * 8, 256);
   f.on = f.bytes <= ((size_t)1 << 32);
   if (!f.on) f.bytes = 0;
@@ -188,45 +190,72 @@ int run_indexer(const uint8_t* ik, const uint8_t* iks, const int64_t* entry_offs
                 const int32_t* n_entries, int B, int64_t max_n, const uint16_t* q_idx, const float* w,
                 int Hi, int score_mode, const int32_t* cand, int cand_stride, int k, int32_t* topk,
                 int pool_k, int32_t* pool, float* scores_out, uint8_t* ws, hipStream_t stream) {
-  const IndexerWs L = indexer_layout(B, max_n, cand ? cand_stride : 0);
+  const IndexerWs L = indexer_layout(B, max_n, k, pool_k, cand ? cand_stride : 0);
   const csa2::SelBufs sb = make_selbufs(L, ws);
   uint64_t* cbuf = (uint64_t*)(ws + L.cand);
   float* scores = scores_out ? scores_out : (float*)(ws + L.scores);
   const int64_t sstride = scores_out ? (cand ? cand_stride : max_n) : L.slots;
+  const csa2::ScoreSrc src{ik, iks, entry_offset, q_idx, w, Hi, score_mode, nullptr, 0, nullptr, 0};
   hipError_t e;
-  auto score = [&](int sel, int K) -> hipError_t {
-    if (!cand)
-      return score_full(ik, iks, entry_offset, n_entries, B, max_n, q_idx, w, Hi, score_mode, scores, sstride, sb,
-                        sel, K, scores_out != nullptr, stream);
-    return csa2::launch_score(ik, iks, entry_offset, n_entries, B, max_n, q_idx, w, Hi, score_mode, cand,
-                              cand_stride, scores, sstride, sb, sel, K, scores_out != nullptr, stream);
-  };
   if (cand) {
-    // Reindex: score the listed positions, select k among them
-    e = score(csa2::SEL_NONE, 0);
+    if (direct_ok(k)) {
+      // Reindex: score the listed positions, local cutoffs, the finish
+      e = csa2::launch_score(ik, iks, entry_offset, n_entries, B, max_n, q_idx, w, Hi, score_mode, cand, cand_stride,
+                             scores, sstride, sb, csa2::SEL_DIRECT, k, true, 0, stream);
+      if (e != hipSuccess) return hip_status(e, "indexer score");
+      csa2::ScoreSrc cs = src;
+      cs.cand = cand;
+      cs.cand_stride = cand_stride;
+      cs.cand_scores = scores;
+      cs.cand_scores_stride = sstride;
+      e = csa2::launch_finish(csa2::SEL_DIRECT, n_entries, B, max_n, scores, sstride, sb, k, topk, k, &cs, stream);
+      return hip_status(e, "indexer select");
+    }
+    e = csa2::launch_score(ik, iks, entry_offset, n_entries, B, max_n, q_idx, w, Hi, score_mode, cand, cand_stride,
+                           scores, sstride, sb, csa2::SEL_NONE, 0, true, 0, stream);
     if (e != hipSuccess) return hip_status(e, "indexer score");
     e = csa2::launch_select_small(scores, sstride, cand, cand_stride, 0, n_entries, B, max_n, k, topk, k, stream);
     return hip_status(e, "indexer select");
   }
-  if (max_n <= csa2::kSmallMax && pool_k == 0) {
-    e = score(csa2::SEL_NONE, 0);
+  if (small_full(max_n)) {
+    // every position fits one workgroup: scores, then the small select (the
+    // pool first when asked, the top-k from it)
+    e = score_full(ik, iks, entry_offset, n_entries, B, max_n, q_idx, w, Hi, score_mode, scores, sstride, sb,
+                   csa2::SEL_NONE, 0, true, 0, stream);
     if (e != hipSuccess) return hip_status(e, "indexer score");
+    if (pool_k > 0) {
+      e = csa2::launch_select_small(scores, sstride, nullptr, 0, 0, n_entries, B, max_n, pool_k, pool, pool_k, stream);
+      if (e != hipSuccess) return hip_status(e, "indexer pool select");
+      e = csa2::launch_select_small(scores, sstride, pool, pool_k, 1, n_entries, B, max_n, k, topk, k, stream);
+      return hip_status(e, "indexer select");
+    }
     e = csa2::launch_select_small(scores, sstride, nullptr, 0, 0, n_entries, B, max_n, k, topk, k, stream);
     return hip_status(e, "indexer select");
   }
-  if (pool_k == 0 && k <= csa2::kDirectMaxK) {
-    e = score(csa2::SEL_DIRECT, k);
+  if (direct_ok(k)) {
+    // local cutoffs in the score pass, then the finish (and the pool finish);
+    // the top-k of the pool is the top-k of the sequence. Without scores_out
+    // the pass keeps no scores; a finish recomputes a sequence's in its fallback
+    e = score_full(ik, iks, entry_offset, n_entries, B, max_n, q_idx, w, Hi, score_mode, scores, sstride, sb,
+                   pool_k > 0 ? csa2::SEL_POOL : csa2::SEL_DIRECT, k, scores_out != nullptr, pool_k, stream);
     if (e != hipSuccess) return hip_status(e, "indexer score");
-    // without scores_out the score pass keeps no scores; the finish recomputes
-    // a sequence's in its fallback
-    const csa2::ScoreSrc src{ik, iks, entry_offset, q_idx, w, Hi, score_mode};
     e = csa2::launch_finish(csa2::SEL_DIRECT, n_entries, B, max_n, scores, sstride, sb, k, topk, k,
                             scores_out ? nullptr : &src, stream);
-    return hip_status(e, "indexer select");
+    if (e != hipSuccess) return hip_status(e, "indexer select");
+    if (pool_k > 0) {
+      // (its fallback rows: the scores region, which this path leaves unused,
+      // and the gscr rows, free once the finish above has run)
+      e = csa2::launch_pool_finish(n_entries, B, max_n, sb, pool_k, pool, (float*)(ws + L.scores), L.slots, sb.gscr,
+                                   sb.gscr_stride, src, stream);
+      if (e != hipSuccess) return hip_status(e, "indexer pool finish");
+    }
+    return ok();
   }
+  // k > 512: threshold bin, marking pass, exact finish
   const int K1 = pool_k > 0 ? pool_k : k;
   int32_t* first_out = pool_k > 0 ? pool : topk;
-  e = score(csa2::SEL_THRESHOLD, K1);
+  e = score_full(ik, iks, entry_offset, n_entries, B, max_n, q_idx, w, Hi, score_mode, scores, sstride, sb,
+                 csa2::SEL_THRESHOLD, K1, true, 0, stream);
   if (e != hipSuccess) return hip_status(e, "indexer score");
   e = csa2::launch_finish(csa2::SEL_THRESHOLD, n_entries, B, max_n, scores, sstride, sb, K1, nullptr, 0, nullptr,
                           stream);
@@ -239,6 +268,28 @@ int run_indexer(const uint8_t* ik, const uint8_t* iks, const int64_t* entry_offs
     if (e != hipSuccess) return hip_status(e, "indexer pool select");
   }
   return ok();
+}
+
+int check_decode_args(int mode, const uint8_t* kv, const uint8_t* ik, const uint8_t* iks, const int64_t* entry_offset,
+                      const int32_t* n_entries, int B, int64_t max_n, const uint16_t* q_idx, const float* w, int Hi,
+                      int score_mode, const uint16_t* q, int H, int k, int pool_k, const int32_t* pool,
+                      const int32_t* topk, const float* out, const float* lse) {
+  if (mode != CSA2_FULL && mode != CSA2_REINDEX && mode != CSA2_REUSE)
+    return fail(CSA2_ERR_UNSUPPORTED, "decode_layer: unknown mode %d", mode);
+  int rc = check_attention_args(kv, entry_offset, n_entries, topk, k, q, B, H, out);
+  if (rc) return rc;
+  if (lse && !aligned16(lse)) return fail(CSA2_ERR_ALIGN, "decode_layer: lse must be 16-byte aligned");
+  if (mode == CSA2_FULL) {
+    rc = check_indexer_args(ik, iks, entry_offset, n_entries, B, max_n, q_idx, w, Hi, score_mode, nullptr, 0, k,
+                            topk, pool_k, pool);
+  } else if (mode == CSA2_REINDEX) {
+    if (!pool || pool_k < 1) return fail(CSA2_ERR_NULL, "decode_layer: Reindex needs the pool (pool, pool_k >= 1)");
+    rc = check_indexer_args(ik, iks, entry_offset, n_entries, B, max_n, q_idx, w, Hi, score_mode, pool, pool_k, k,
+                            topk, 0, nullptr);
+  } else if (B > CSA2_MAX_BATCH) {
+    return fail(CSA2_ERR_SHAPE, "decode_layer: B must be in [1, %d] (got %d)", CSA2_MAX_BATCH, B);
+  }
+  return rc;
 }
 
 }  // namespace
@@ -310,9 +361,9 @@ int csa2_swa_attention(const uint8_t* win, const int32_t* n_win, const uint16_t*
                     "swa_attention");
 }
 
-size_t csa2_indexer_workspace_bytes(int B, int64_t max_n, int cand_stride) {
-  if (B < 1 || B > CSA2_MAX_BATCH || max_n < 0 || cand_stride < 0) return 0;
-  return indexer_layout(B, max_n, cand_stride).total;
+size_t csa2_indexer_workspace_bytes(int B, int64_t max_n, int k, int pool_k, int cand_stride) {
+  if (B < 1 || B > CSA2_MAX_BATCH || max_n < 0 || k < 1 || pool_k < 0 || cand_stride < 0) return 0;
+  return indexer_layout(B, max_n, k, pool_k, cand_stride).total;
 }
 
 int csa2_indexer_topk(const uint8_t* ik, const uint8_t* iks, const int64_t* entry_offset,
@@ -324,7 +375,7 @@ int csa2_indexer_topk(const uint8_t* ik, const uint8_t* iks, const int64_t* entr
                               cand_stride, k, topk, pool_k, pool);
   if (rc) return rc;
   if (scores_out && !aligned16(scores_out)) return fail(CSA2_ERR_ALIGN, "indexer: scores_out must be 16-byte aligned");
-  const size_t need = indexer_layout(B, max_n, cand ? cand_stride : 0).total;
+  const size_t need = indexer_layout(B, max_n, k, pool_k, cand ? cand_stride : 0).total;
   if (!workspace || ws_bytes < need)
     return fail(CSA2_ERR_WORKSPACE, "indexer: workspace needs %zu bytes (got %zu)", need, workspace ? ws_bytes : 0);
   if (!aligned16(workspace)) return fail(CSA2_ERR_ALIGN, "indexer: workspace must be 16-byte aligned");
@@ -334,7 +385,7 @@ int csa2_indexer_topk(const uint8_t* ik, const uint8_t* iks, const int64_t* entr
 
 size_t csa2_attention_workspace_bytes(int B, int H, int k) {
   if (B < 1 || H < 1 || H > CSA2_MAX_HEADS || k < 1) return 0;
-  return ctrl_bytes() + attention_scratch(B, H, k);
+  return attention_scratch(B, H, k);
 }
 
 int csa2_sparse_attention(const uint8_t* kv, const int64_t* entry_offset, const int32_t* n_entries,
@@ -343,73 +394,77 @@ int csa2_sparse_attention(const uint8_t* kv, const int64_t* entry_offset, const 
   int rc = check_attention_args(kv, entry_offset, n_entries, idx, k, q, B, H, out);
   if (rc) return rc;
   if (lse && !aligned16(lse)) return fail(CSA2_ERR_ALIGN, "attention: lse must be 16-byte aligned");
-  const size_t need = ctrl_bytes() + attention_scratch(B, H, k);
+  const size_t need = attention_scratch(B, H, k);
   if (!workspace || ws_bytes < need)
     return fail(CSA2_ERR_WORKSPACE, "attention: workspace needs %zu bytes (got %zu)", need, workspace ? ws_bytes : 0);
   if (!aligned16(workspace)) return fail(CSA2_ERR_ALIGN, "attention: workspace must be 16-byte aligned");
-  const int S = csa2::attention_splits(B, H, k);
-  hipError_t e = csa2::launch_attention(kv, entry_offset, n_entries, idx, k, q, B, H, softmax_scale, S, out, lse,
-                                        (float*)((uint8_t*)workspace + ctrl_bytes()), nullptr, (hipStream_t)stream);
+  hipError_t e = csa2::launch_attention(kv, entry_offset, n_entries, idx, k, q, B, H, softmax_scale, 1, out, lse,
+                                        nullptr, nullptr, (hipStream_t)stream);
   return hip_status(e, "attention");
 }
 
 size_t csa2_decode_workspace_bytes(int B, int64_t max_n, int H, int k, int pool_k) {
   if (B < 1 || B > CSA2_MAX_BATCH || max_n < 0 || H < 1 || H > CSA2_MAX_HEADS || k < 1 || pool_k < 0) return 0;
-  const size_t a = indexer_layout(B, max_n, pool_k).total;
-  return a + attention_scratch(B, H, k) + fused_plan(B, max_n, H, k, pool_k).bytes;
+  // the largest of the three modes' needs (a Reindex layer scores a list of pool_k)
+  size_t need = 0;
+  for (int mode = CSA2_FULL; mode <= CSA2_REUSE; ++mode) {
+    const size_t idx = mode == CSA2_REUSE ? 0
+                       : indexer_layout(B, max_n, k, mode == CSA2_FULL ? pool_k : 0,
+                                        mode == CSA2_REINDEX ? pool_k : 0).total;
+    const size_t t = idx + attention_scratch(B, H, k) + fused_plan(mode, B, max_n, H, k, pool_k).bytes;
+    need = t > need ? t : need;
+  }
+  return need;
 }
 
-int csa2_decode_layer(int mode, const uint8_t* kv, const uint8_t* ik, const uint8_t* iks,
-                      const int64_t* entry_offset, const int32_t* n_entries, int B, int64_t max_n,
-                      const uint16_t* q_idx, const float* w, int Hi, int score_mode, const uint16_t* q, int H,
-                      float softmax_scale, int k, int pool_k, int32_t* pool, int32_t* topk, float* out,
-                      float* lse, void* workspace, size_t ws_bytes, void* stream) {
-  if (mode != CSA2_FULL && mode != CSA2_REINDEX && mode != CSA2_REUSE)
-    return fail(CSA2_ERR_UNSUPPORTED, "decode_layer: unknown mode %d", mode);
-  int rc = check_attention_args(kv, entry_offset, n_entries, topk, k, q, B, H, out);
-  if (rc) return rc;
-  if (lse && !aligned16(lse)) return fail(CSA2_ERR_ALIGN, "decode_layer: lse must be 16-byte aligned");
-  if (mode == CSA2_FULL) {
-    rc = check_indexer_args(ik, iks, entry_offset, n_entries, B, max_n, q_idx, w, Hi, score_mode, nullptr, 0, k,
-                            topk, pool_k, pool);
-  } else if (mode == CSA2_REINDEX) {
-    if (!pool || pool_k < 1) return fail(CSA2_ERR_NULL, "decode_layer: Reindex needs the pool (pool, pool_k >= 1)");
-    rc = check_indexer_args(ik, iks, entry_offset, n_entries, B, max_n, q_idx, w, Hi, score_mode, pool, pool_k, k,
-                            topk, 0, nullptr);
-  }
-  if (rc) return rc;
-  const size_t need_idx = indexer_layout(B, max_n, pool_k).total;
-  const size_t need_att = attention_scratch(B, H, k);
-  const FusedPlan fp = fused_plan(B, max_n, H, k, pool_k);
-  const size_t need = need_idx + need_att + fp.bytes;
-  if (!workspace || ws_bytes < need)
-    return fail(CSA2_ERR_WORKSPACE, "decode_layer: workspace needs %zu bytes (got %zu)", need, workspace ? ws_bytes : 0);
-  if (!aligned16(workspace)) return fail(CSA2_ERR_ALIGN, "decode_layer: workspace must be 16-byte aligned");
-  uint8_t* ws = (uint8_t*)workspace;
-  hipStream_t s = (hipStream_t)stream;
-  const int S = csa2::attention_splits(B, H, k);
-  if (mode == CSA2_FULL && fp.on) {
+namespace {
+// One decode layer with validated arguments on a validated workspace.
+int run_decode_layer(int mode, const uint8_t* kv, const uint8_t* ik, const uint8_t* iks, const int64_t* entry_offset,
+                     const int32_t* n_entries, int B, int64_t max_n, const uint16_t* q_idx, const float* w, int Hi,
+                     int score_mode, const uint16_t* q, int H, float softmax_scale, int k, int pool_k, int32_t* pool,
+                     int32_t* topk, float* out, float* lse, uint8_t* ws, hipStream_t s) {
+  const FusedPlan fp = fused_plan(mode, B, max_n, H, k, pool_k);
+  const int cand_stride = mode == CSA2_REINDEX ? pool_k : 0;
+  if (fp.on) {
     // scoring launch, then the attention that runs the top-k finish itself
-    const IndexerWs L = indexer_layout(B, max_n, 0);
+    // (and, for a Full layer with a pool, the pool finish in workgroups of its own)
+    const IndexerWs L = indexer_layout(B, max_n, k, mode == CSA2_FULL ? pool_k : 0, cand_stride);
     const csa2::SelBufs sb = make_selbufs(L, ws);
-    hipError_t e = score_full(ik, iks, entry_offset, n_entries, B, max_n, q_idx, w, Hi, score_mode,
-                              (float*)(ws + L.scores), L.slots, sb, csa2::SEL_DIRECT, k, false, s);
-    if (e != hipSuccess) return hip_status(e, "decode_layer score");
-    uint8_t* fb = ws + need_idx + need_att;
-    const size_t G = (size_t)csa2::attention_workgroups(B, H, k);
+    float* scores = (float*)(ws + L.scores);
     csa2::FusedFinish ff;
     ff.sb = sb;
-    ff.src = csa2::ScoreSrc{ik, iks, entry_offset, q_idx, w, Hi, score_mode};
+    ff.src = csa2::ScoreSrc{ik, iks, entry_offset, q_idx, w, Hi, score_mode, nullptr, 0, nullptr, 0};
+    ff.pool_k = 0;
+    ff.pool = nullptr;
+    hipError_t e;
+    if (mode == CSA2_FULL) {
+      e = score_full(ik, iks, entry_offset, n_entries, B, max_n, q_idx, w, Hi, score_mode, scores, L.slots, sb,
+                     pool_k > 0 ? csa2::SEL_POOL : csa2::SEL_DIRECT, k, false, pool_k, s);
+      ff.pool_k = pool_k;
+      ff.pool = pool;
+    } else {
+      e = csa2::launch_score(ik, iks, entry_offset, n_entries, B, max_n, q_idx, w, Hi, score_mode, pool, pool_k,
+                             scores, L.slots, sb, csa2::SEL_DIRECT, k, true, 0, s);
+      ff.src.cand = pool;
+      ff.src.cand_stride = pool_k;
+      ff.src.cand_scores = scores;
+      ff.src.cand_scores_stride = L.slots;
+    }
+    if (e != hipSuccess) return hip_status(e, "decode_layer score");
+    const size_t need_idx = L.total;
+    uint8_t* fb = ws + need_idx + attention_scratch(B, H, k);
+    const size_t G = (size_t)csa2::attention_workgroups(B, H, k) + (ff.pool_k > 0 ? (size_t)B : 0);
     ff.max_n = max_n;
     ff.scores = (float*)fb;
     ff.scores_stride = fp.sstride;
     ff.gscr = (uint64_t*)(fb + round_up(G * (size_t)fp.sstride * 4, 256));
     ff.gscr_stride = fp.gstride;
     ff.topk = topk;
-    e = csa2::launch_attention(kv, entry_offset, n_entries, topk, k, q, B, H, softmax_scale, S, out, lse,
-                               (float*)(ws + need_idx), &ff, s);
+    e = csa2::launch_attention(kv, entry_offset, n_entries, topk, k, q, B, H, softmax_scale, 1, out, lse, nullptr,
+                               &ff, s);
     return hip_status(e, "decode_layer attention");
   }
+  int rc = CSA2_OK;
   if (mode == CSA2_FULL) {
     rc = run_indexer(ik, iks, entry_offset, n_entries, B, max_n, q_idx, w, Hi, score_mode, nullptr, 0, k, topk,
                      pool_k, pool, nullptr, ws, s);
@@ -418,9 +473,26 @@ int csa2_decode_layer(int mode, const uint8_t* kv, const uint8_t* ik, const uint
                      nullptr, nullptr, ws, s);
   }
   if (rc) return rc;
-  hipError_t e = csa2::launch_attention(kv, entry_offset, n_entries, topk, k, q, B, H, softmax_scale, S, out, lse,
-                                        (float*)(ws + need_idx), nullptr, s);
+  hipError_t e = csa2::launch_attention(kv, entry_offset, n_entries, topk, k, q, B, H, softmax_scale, 1, out, lse,
+                                        nullptr, nullptr, s);
   return hip_status(e, "decode_layer attention");
+}
+}  // namespace
+
+int csa2_decode_layer(int mode, const uint8_t* kv, const uint8_t* ik, const uint8_t* iks,
+                      const int64_t* entry_offset, const int32_t* n_entries, int B, int64_t max_n,
+                      const uint16_t* q_idx, const float* w, int Hi, int score_mode, const uint16_t* q, int H,
+                      float softmax_scale, int k, int pool_k, int32_t* pool, int32_t* topk, float* out,
+                      float* lse, void* workspace, size_t ws_bytes, void* stream) {
+  int rc = check_decode_args(mode, kv, ik, iks, entry_offset, n_entries, B, max_n, q_idx, w, Hi, score_mode, q, H, k,
+                             pool_k, pool, topk, out, lse);
+  if (rc) return rc;
+  const size_t need = csa2_decode_workspace_bytes(B, max_n, H, k, pool_k);
+  if (!workspace || ws_bytes < need)
+    return fail(CSA2_ERR_WORKSPACE, "decode_layer: workspace needs %zu bytes (got %zu)", need, workspace ? ws_bytes : 0);
+  if (!aligned16(workspace)) return fail(CSA2_ERR_ALIGN, "decode_layer: workspace must be 16-byte aligned");
+  return run_decode_layer(mode, kv, ik, iks, entry_offset, n_entries, B, max_n, q_idx, w, Hi, score_mode, q, H,
+                          softmax_scale, k, pool_k, pool, topk, out, lse, (uint8_t*)workspace, (hipStream_t)stream);
 }
 
 size_t csa2_prefill_workspace_bytes(int B, int Tq, int64_t max_n, int H, int k) {

@@ -108,10 +108,16 @@ __device__ void compact_bitmap(const uint32_t* bm, int64_t nbits, const int32_t*
 // ---------------------------------------------------------------- score kernel
 
 
-// CAND: score the listed positions (Reindex) instead of every entry.
-// SEL: SEL_NONE (scores only); SEL_THRESHOLD / SEL_DIRECT (also report the
-//      local cutoff summary, and for SEL_DIRECT the candidates, that
-//      finish_kernel turns into the threshold bin or the final top-K).
+// CAND: score the listed positions (Reindex) instead of every entry. A listed
+//      position is used when it lies in [0, n) and is greater than every
+//      in-range position listed before it (so the used positions ascend with
+//      the slot); the pass stores every slot's score, with the key 0 for a
+//      slot it does not use, and selects on (score, position).
+// SEL: SEL_NONE (scores only); SEL_THRESHOLD (also the (bin, count) summary of
+//      the keys above a local cutoff, for k > 512); SEL_DIRECT (the local
+//      cutoff and its candidates, for a finish that picks the top-K); SEL_POOL
+//      (SEL_DIRECT's list plus a pool list: every key above a second, lower
+//      local cutoff for the pool_k best, with its own header).
 // MODE: 0 = dot product of head 0, 1 = sum_h w_h * ReLU(q_h . k).
 // QMX: the query is quantized to MXFP8 in registers and each tile is one
 //      block-scaled FP8 x FP4 MFMA (the quantized-query variant).
@@ -119,12 +125,12 @@ __device__ void compact_bitmap(const uint32_t* bm, int64_t nbits, const int32_t*
 // eight workgroups of four waves share a compute unit, each wave with
 // SC_UNROLL tiles in flight.
 template <bool CAND, int SEL, int MODE, bool QMX>
-__global__ __launch_bounds__(SC_THREADS) __attribute__((amdgpu_waves_per_eu(8))) void score_kernel(
+__global__ __launch_bounds__(SC_THREADS) __attribute__((amdgpu_waves_per_eu(CAND ? 6 : 8))) void score_kernel(
     const uint8_t* __restrict__ ik, const uint8_t* __restrict__ iks,
     const int64_t* __restrict__ entry_offset, const int32_t* __restrict__ n_entries, int64_t max_n,
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w, int Hi,
     const int32_t* __restrict__ cand, int cand_stride,
-    float* __restrict__ scores, int64_t sstride, SelBufs sb, int K, int store_scores) {
+    float* __restrict__ scores, int64_t sstride, SelBufs sb, int K, int store_scores, int pool_k) {
   // histogram with 16-bit counts (two bins per word) + staged scores: 12 KiB,
   // so that eight workgroups fit one compute unit
   __shared__ uint32_t lbuf[NBINS / 2 + SC_SPAN];
@@ -133,9 +139,11 @@ __global__ __launch_bounds__(SC_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
   __shared__ __attribute__((aligned(16))) float lw[16];   // head weights
   __shared__ SelBufs sbs;   // the workspace views, parked in LDS while the keys stream (frees SGPRs)
   __shared__ __attribute__((aligned(16))) uint8_t lq[QMX ? QMX_LDS_BYTES : 16];   // the quantized query
+  __shared__ uint32_t used_bm[CAND ? SC_SPAN / 32 : 1];     // candidate list: slots used
   uint32_t* lhist = lbuf;
   float* lsc = (float*)(lbuf + NBINS / 2);
   auto hcount = [&](uint32_t bin) -> uint32_t { return (lhist[bin >> 1] >> ((bin & 1) * 16)) & 0xFFFFu; };
+  constexpr bool LISTS = SEL == SEL_DIRECT || SEL == SEL_POOL;
 
   const int b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -164,13 +172,13 @@ __global__ __launch_bounds__(SC_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
   const int64_t nslots = CAND ? (int64_t)cand_stride : n_pos;
   const int64_t start = (int64_t)blockIdx.x * SC_SPAN;
   if (start >= nslots) return;
-  if (CAND && n_pos <= 0) return;                  // no listed position can be valid
+  if (CAND && n_pos <= 0 && !LISTS) return;        // no listed position can be valid (lists: still written)
   const int end = (int)min((int64_t)SC_SPAN, nslots - start);   // slots of this workgroup
   // the sequence's rows: a uniform base plus a 32-bit byte offset per lane
   // (positions below 2^26, checked on the host), one address register per load
   const uint8_t* ikb = ik + row_base * 64;
   const uint8_t* iksb = iks + row_base * 4;
-  const int32_t* crow = CAND ? cand + (int64_t)b * cand_stride + start : nullptr;
+  const int32_t* crow = CAND ? cand + (int64_t)b * cand_stride : nullptr;
   // Full pass: the first SC_UNROLL tiles of this wave are requested right away
   u32x4_t codes[SC_UNROLL];
   uint32_t sbyte[SC_UNROLL];
@@ -195,6 +203,59 @@ __global__ __launch_bounds__(SC_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
   }
   if (tid < 16) lw[tid] = wv;
   if (SEL != SEL_NONE && tid == 0) sbs = sb;
+  if constexpr (CAND) {
+    // which of this workgroup's slots the rule uses: the largest in-range
+    // position listed before the workgroup's first slot, then a scan of the
+    // workgroup's own slots (thread t: slots 4t .. 4t+3)
+    uint32_t pm = 0;                                   // position + 1, 0 = none
+    auto take = [&](int32_t c) { if (c >= 0 && c < n_pos) pm = max(pm, (uint32_t)c + 1u); };
+    if ((cand_stride & 3) == 0) {                      // 16-byte rows: four entries per load
+#pragma unroll 8
+      for (int64_t i = 4 * tid; i < start; i += 4 * SC_THREADS) {
+        const u32x4_t v = *(const u32x4_t*)(crow + i);
+        take((int32_t)v[0]); take((int32_t)v[1]); take((int32_t)v[2]); take((int32_t)v[3]);
+      }
+    } else {
+#pragma unroll 8
+      for (int64_t i = tid; i < start; i += SC_THREADS) take(crow[i]);
+    }
+    uint32_t pp[4], lmax = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int i = 4 * tid + q;
+      const int32_t c = i < end ? crow[start + i] : -1;
+      pp[q] = (c >= 0 && c < n_pos) ? (uint32_t)c + 1u : 0u;
+      lmax = max(lmax, pp[q]);
+    }
+    pm = wave_max_u32(pm);
+    uint32_t incl = lmax;                              // inclusive max over this wave's threads
+#pragma unroll
+    for (int sh = 1; sh < 64; sh <<= 1) {
+      const uint32_t o = (uint32_t)__shfl_up((int)incl, sh, 64);
+      if (lane >= sh) incl = max(incl, o);
+    }
+    const uint32_t up = (uint32_t)__shfl_up((int)incl, 1, 64);
+    if (lane == 63) scan_tmp[wave] = max(incl, pm);
+    if (lane == 0) ctl[wave] = pm;
+    __syncthreads();
+    uint32_t run = lane > 0 ? max(up, pm) : pm;
+    for (int v = 0; v < SC_THREADS / 64; ++v) {
+      run = max(run, ctl[v]);                          // every wave's share of the earlier slots
+      if (v < wave) run = max(run, scan_tmp[v]);
+    }
+    uint32_t m4 = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      m4 |= (pp[q] > run ? 1u : 0u) << q;
+      run = max(run, pp[q]);
+    }
+    // 8 threads per word: gather their 4-bit masks
+    uint32_t wd = m4 << (4 * (tid & 7));
+    wd |= (uint32_t)__shfl_xor((int)wd, 1, 64);
+    wd |= (uint32_t)__shfl_xor((int)wd, 2, 64);
+    wd |= (uint32_t)__shfl_xor((int)wd, 4, 64);
+    if ((tid & 7) == 0) used_bm[tid >> 3] = wd;
+  }
   __syncthreads();
   if constexpr (QMX) qm = query_mx_operand(lq, lane);
 
@@ -204,12 +265,48 @@ __global__ __launch_bounds__(SC_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
     if constexpr (QMX) return score_tile_mx<MODE>(qm, cw, sbyte, lw, g);
     else return score_tile_fn<MODE>(qa, cw, sbyte, lw, g);
   };
+  // The local cutoff of a chunk: a 20-bit key prefix with at least `budget`
+  // of the chunk's valid keys at or above it (0 when it has fewer). The keys
+  // within two octaves of the chunk's largest prefix M are in a band
+  // histogram of 256 bins of 16 prefix units counted down from M; spread over
+  // 256 bins the LDS atomics rarely collide. The bin where the running count
+  // reaches the budget gives the cutoff; a chunk with fewer than `budget` keys
+  // in the band takes the exact path (the 12-bit histogram, then the 256
+  // 20-bit sub-bins of the cutoff bin). Thread t owns slots 4t .. 4t+3.
+  auto exact_cutoff = [&](const uint32_t (&keys)[4], uint32_t vmask, uint32_t budget) -> uint32_t {
+    __syncthreads();                                 // the band histogram's readers are done
+    for (int i = tid; i < NBINS / 2; i += SC_THREADS) lhist[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if ((vmask >> q) & 1u) {
+        const uint32_t bin = keys[q] >> BIN_SHIFT;
+        atomicAdd(&lhist[bin >> 1], 1u << ((bin & 1) * 16));
+      }
+    }
+    __syncthreads();
+    uint32_t cnt_all;
+    hist_kth_bin<SC_THREADS, true>(lhist, budget, scan_tmp, ctl, &cnt_all);
+    const uint32_t cbin = ctl[0], cabove = ctl[1];
+    uint32_t fine = 0;                               // fewer keys than the budget: keep all
+    if (cbin != 0xFFFFFFFFu) {
+      uint32_t* h2 = lhist;                          // every read of the 4096 bins is done (256 words)
+      h2[tid] = 0;
+      __syncthreads();
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (((vmask >> q) & 1u) && (keys[q] >> BIN_SHIFT) == cbin) atomicAdd(&h2[(keys[q] >> 12) & 255u], 1u);
+      __syncthreads();
+      if (tid < 64) digit_kth(h2, budget - cabove, ctl + 4);
+      __syncthreads();
+      fine = (cbin << 8) | ctl[4];
+    }
+    return fine;
+  };
   // ---- per selection chunk (sub = 0 .. SC_SUB-1): store its scores, then the
   // local cutoff (every slot of a Full pass is a valid position). Chunk cix
   // reports into its own slot of the workspace (a header word and a list), so
-  // no global atomics are needed. With two chunks per workgroup in direct
-  // mode, the first chunk's tail runs in the middle of the stream, while the
-  // second chunk's tiles are in flight.
+  // no global atomics are needed.
   auto chunk_tail = [&](int sub) {
   const int soff = sub * SC_CHUNK;
   const int send = min(SC_CHUNK, end - soff);        // slots of this chunk
@@ -217,7 +314,7 @@ __global__ __launch_bounds__(SC_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
   __syncthreads();                                   // its scores are staged; the previous tail is done
   const float* lss = lsc + soff;
   const int64_t cix = (int64_t)blockIdx.x * SC_SUB + sub;
-  // coalesced store of the chunk's scores (slots of invalid candidates hold 0)
+  // coalesced store of the chunk's scores (slots of unused candidates hold the key 0)
   if (store_scores) {
     float* srow = scores + (int64_t)b * sstride + start + soff;
     for (int i4 = 4 * tid; i4 < send; i4 += 4 * SC_THREADS) {
@@ -230,13 +327,14 @@ __global__ __launch_bounds__(SC_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
   }
   if (SEL == SEL_NONE) return;
   const SelBufs sbl = sbs;
-  const int64_t nwg = (n_pos + SC_CHUNK - 1) / SC_CHUNK;
+  const int64_t nref = CAND ? nslots : n_pos;        // slots the shares refer to
+  const int64_t nwg = (nref + SC_CHUNK - 1) / SC_CHUNK;
   // local budget: a multiple of the chunk's expected share of the top-K plus a
   // margin, so that the highest cutoff over the workgroups still leaves at
   // least K keys of the sequence above it (the finish checks this)
-  const int64_t share = ((int64_t)K * SC_CHUNK + n_pos - 1) / n_pos;
-  int64_t budget64 = SEL == SEL_DIRECT ? 2 * share + 16 : 4 * share + 32;
-  if (SEL == SEL_DIRECT) budget64 = min(budget64, max((int64_t)8, (int64_t)FIN_LDS_CANDS / nwg));
+  const int64_t share = ((int64_t)K * SC_CHUNK + nref - 1) / nref;
+  int64_t budget64 = LISTS ? 2 * share + 16 : 4 * share + 32;
+  if (LISTS) budget64 = min(budget64, max((int64_t)8, (int64_t)FIN_LDS_CANDS / nwg));
   const uint32_t budget = (uint32_t)min(budget64, (int64_t)send);
   uint64_t* hdr = sbl.hdr + (int64_t)b * sbl.hdr_stride + cix;
   if (SEL == SEL_THRESHOLD) {
@@ -274,24 +372,17 @@ __global__ __launch_bounds__(SC_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
     }
     if (tid == 0) *hdr = ((uint64_t)cut << 32) | (tot > SUM_PAIRS ? 0x80000000u : tot);
   }
-  if (SEL == SEL_DIRECT) {
-    // The cutoff: a 20-bit key prefix `fine` with at least `budget` keys of
-    // the chunk at or above it. The keys within two octaves of the chunk's
-    // largest prefix M go to a band histogram of 256 bins, 16 prefix units
-    // each, counted down from M; spread over 256 bins the LDS atomics rarely
-    // collide, unlike the 12-bit key bins, of which a chunk fills only a
-    // handful. The bin where the running count reaches the budget gives the
-    // cutoff. A chunk with fewer than `budget` keys in the band takes the
-    // exact path instead (12-bit histogram, then the 256 20-bit sub-bins of
-    // the cutoff bin). Thread t owns slots 4t .. 4t+3.
+  if (LISTS) {
     constexpr uint32_t sh = 4;
     uint32_t* hb = lhist;                            // 256 words
-    uint32_t keys[4], pmax = 0;
+    uint32_t keys[4], pmax = 0, vmask = 0;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int i = 4 * tid + q;
       keys[q] = i < send ? score_key(lss[i]) : 0u;
-      if (i < send) pmax = max(pmax, keys[q] >> 12);
+      const bool v = i < send && (!CAND || keys[q] != 0u);
+      vmask |= (v ? 1u : 0u) << q;
+      if (v) pmax = max(pmax, keys[q] >> 12);
     }
     pmax = wave_max_u32(pmax);
     if (lane == 0) scan_tmp[wave] = pmax;
@@ -303,78 +394,82 @@ __global__ __launch_bounds__(SC_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const uint32_t d = (M - (keys[q] >> 12)) >> sh;
-      if (4 * tid + q < send && d < 256u) atomicAdd(&hb[d], 1u);
+      if (((vmask >> q) & 1u) && d < 256u) atomicAdd(&hb[d], 1u);
     }
     __syncthreads();
+    // pool budget: the same rule for the pool_k best
+    uint32_t budget_p = 0;
+    if (SEL == SEL_POOL) {
+      const int64_t share_p = ((int64_t)pool_k * SC_CHUNK + nref - 1) / nref;
+      budget_p = (uint32_t)min(2 * share_p + 16, (int64_t)send);
+    }
     if (wave == 0) {
       uint32_t hv[4], sl = 0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) { hv[j] = hb[4 * lane + j]; sl += hv[j]; }
       const uint32_t incl = wave_incl_sum(sl);
-      uint32_t cum = incl - sl;
-      if (cum < budget && incl >= budget) {
-        uint32_t ds = 0xFFFFFFFFu;
+      // the band bin where the running count reaches each budget (-1: too few in the band)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const bool hit = ds == 0xFFFFFFFFu && cum + hv[j] >= budget;
-          ds = hit ? 4 * lane + j : ds;
-          cum += hv[j];
+      for (int which = 0; which < (SEL == SEL_POOL ? 2 : 1); ++which) {
+        const uint32_t bud = which == 0 ? budget : budget_p;
+        uint32_t cum = incl - sl;
+        if (cum < bud && incl >= bud) {
+          uint32_t ds = 0xFFFFFFFFu;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const bool hit = ds == 0xFFFFFFFFu && cum + hv[j] >= bud;
+            ds = hit ? 4 * lane + j : ds;
+            cum += hv[j];
+          }
+          ctl[4 + which] = ds;
         }
-        ctl[4] = ds;
+        if (lane == 63 && incl < bud) ctl[4 + which] = 0xFFFFFFFFu;
       }
-      if (lane == 63 && incl < budget) ctl[4] = 0xFFFFFFFFu;   // too few keys within the octave
     }
     __syncthreads();
-    const uint32_t ds = ctl[4];
-    uint32_t fine;
-    if (ds != 0xFFFFFFFFu) {
-      // bin ds holds prefixes M - (ds << sh) - (2^sh - 1) .. M - (ds << sh)
-      const uint32_t lo = ((ds + 1u) << sh) - 1u;
-      fine = M >= lo ? M - lo : 0u;
-    } else {
-      // exact path: the 12-bit bin of the budget-th key, refined to 20 bits
-      for (int i = tid; i < NBINS / 2; i += SC_THREADS) lhist[i] = 0;
-      __syncthreads();
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (4 * tid + q < send) {
-          const uint32_t bin = keys[q] >> BIN_SHIFT;
-          atomicAdd(&lhist[bin >> 1], 1u << ((bin & 1) * 16));
-        }
-      }
-      __syncthreads();
-      uint32_t cnt_all;
-      hist_kth_bin<SC_THREADS, true>(lhist, budget, scan_tmp, ctl, &cnt_all);
-      const uint32_t cbin = ctl[0], cabove = ctl[1];
-      fine = 0;                                      // fewer keys than the budget: keep all
-      if (cbin != 0xFFFFFFFFu) {
-        uint32_t* h2 = lhist;                        // every read of the 4096 bins is done (256 words)
-        h2[tid] = 0;
-        __syncthreads();
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          if (4 * tid + q < send && (keys[q] >> BIN_SHIFT) == cbin) atomicAdd(&h2[(keys[q] >> 12) & 255u], 1u);
-        __syncthreads();
-        if (tid < 64) digit_kth(h2, budget - cabove, ctl + 4);
-        __syncthreads();
-        fine = (cbin << 8) | ctl[4];
-      }
-    }
-    // candidates: every slot whose top 20 key bits are >= fine, in slot order
+    const uint32_t ds_k = ctl[4], ds_p = ctl[5];
+    // bin ds holds prefixes M - (ds << sh) - (2^sh - 1) .. M - (ds << sh)
+    auto band_fine = [&](uint32_t ds) { const uint32_t lo = ((ds + 1u) << sh) - 1u; return M >= lo ? M - lo : 0u; };
+    const uint32_t fine = ds_k != 0xFFFFFFFFu ? band_fine(ds_k) : exact_cutoff(keys, vmask, budget);
+    uint32_t fine_p = 0;
+    if (SEL == SEL_POOL) fine_p = ds_p != 0xFFFFFFFFu ? band_fine(ds_p) : exact_cutoff(keys, vmask, budget_p);
+    // candidates: every valid slot whose top 20 key bits are >= fine, in slot order
+    auto position = [&](int i) -> uint32_t {
+      return CAND ? (uint32_t)crow[start + soff + i] : (uint32_t)(start + soff + i);
+    };
     uint32_t m = 0;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) m |= ((4 * tid + q < send && (keys[q] >> 12) >= fine) ? 1u : 0u) << q;
+    for (int q = 0; q < 4; ++q) m |= ((((vmask >> q) & 1u) && (keys[q] >> 12) >= fine) ? 1u : 0u) << q;
     uint32_t tot;
     uint32_t off = block_exclusive_scan((uint32_t)__popc(m), scan_tmp, &tot);
     uint64_t* wc = sbl.wgc + (int64_t)b * sbl.wgc_stride + cix * CAND_CAP;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       if ((m >> q) & 1u) {
-        if (off < CAND_CAP) wc[off] = composite(keys[q], (uint32_t)(start + soff + 4 * tid + q));
+        if (off < CAND_CAP) wc[off] = composite(keys[q], position(4 * tid + q));
         ++off;
       }
     }
     if (tid == 0) *hdr = ((uint64_t)fine << 32) | (tot > CAND_CAP ? 0x80000000u : tot);
+    if (SEL == SEL_POOL) {
+      // the pool list (never overflows: its capacity is the chunk) and its
+      // header: count | cutoff << 11 | M << 32
+      uint32_t mp = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) mp |= ((((vmask >> q) & 1u) && (keys[q] >> 12) >= fine_p) ? 1u : 0u) << q;
+      uint32_t totp;
+      uint32_t offp = block_exclusive_scan((uint32_t)__popc(mp), scan_tmp, &totp);
+      uint64_t* wcp = sbl.wgcp + (int64_t)b * sbl.wgcp_stride + cix * kPoolCap;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if ((mp >> q) & 1u) {
+          wcp[offp] = composite(keys[q], position(4 * tid + q));
+          ++offp;
+        }
+      }
+      if (tid == 0)
+        sbl.hdrp[(int64_t)b * sbl.hdr_stride + cix] = ((uint64_t)M << 32) | ((uint64_t)fine_p << 11) | totp;
+    }
   }
   };
   if (!CAND) {
@@ -385,10 +480,9 @@ __global__ __launch_bounds__(SC_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
     // cache; unconditional loads in a fully unrolled loop keep the wait counts
     // exact, and a short last chunk scores its clamped rows without storing them)
     constexpr int NIT = SC_SPAN / (SC_THREADS * SC_UNROLL / 4);
-    static_assert(SC_SUB <= 2 && NIT % SC_SUB == 0, "chunks end at stream iteration boundaries");
+    static_assert(SC_SUB == 1, "one selection chunk per workgroup");
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
-      if (SC_SUB == 2 && SEL == SEL_DIRECT && it == NIT / 2) chunk_tail(0);   // the next tiles are in flight
       const int t0 = 16 * wave + it * 64 * SC_UNROLL;
 #pragma unroll
       for (int u = 0; u < SC_UNROLL; ++u) {
@@ -400,19 +494,23 @@ __global__ __launch_bounds__(SC_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
         sbyte[u] = iksb[p * 4u + (uint32_t)g];
       }
     }
+  } else if (n_pos <= 0) {
+    // an empty sequence: no listed position is used
+    const float unused = LISTS ? __uint_as_float(0xFFFFFFFFu) : 0.0f;
+    for (int i = tid; i < end; i += SC_THREADS) lsc[i] = unused;
   } else {
-    // listed positions: SC_UNROLL tiles are loaded before any is used (invalid
-    // slots read row 0 of the sequence and score 0)
+    // listed positions: SC_UNROLL tiles are loaded before any is used (unused
+    // slots read row 0 of the sequence, and hold the key 0)
+    const float unused = __uint_as_float(0xFFFFFFFFu);     // key 0
     for (int t0 = 16 * wave; t0 < end; t0 += 64 * SC_UNROLL) {
       int pos[SC_UNROLL];
       bool ok[SC_UNROLL];
-      int cv[SC_UNROLL];
-#pragma unroll
-      for (int u = 0; u < SC_UNROLL; ++u) cv[u] = crow[min(t0 + 64 * u + n, end - 1)];
 #pragma unroll
       for (int u = 0; u < SC_UNROLL; ++u) {
-        ok[u] = (t0 + 64 * u + n < end) && cv[u] >= 0 && cv[u] < n_pos;
-        pos[u] = ok[u] ? cv[u] : 0;
+        const int i = t0 + 64 * u + n;
+        const bool inb = i < end;
+        ok[u] = inb && ((used_bm[i >> 5] >> (i & 31)) & 1u);
+        pos[u] = ok[u] ? crow[start + i] : 0;
       }
 #pragma unroll
       for (int u = 0; u < SC_UNROLL; ++u) {
@@ -423,12 +521,11 @@ __global__ __launch_bounds__(SC_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
       for (int u = 0; u < SC_UNROLL; ++u) {
         const float sc = score_tile(codes[u], sbyte[u]);
         const int ls = t0 + 64 * u + n;
-        if (g == 0 && ls < end) lsc[ls] = ok[u] ? sc : 0.0f;
+        if (g == 0 && ls < end) lsc[ls] = ok[u] ? sc : (LISTS ? unused : 0.0f);
       }
     }
   }
-  if (SC_SUB == 1 || CAND || SEL != SEL_DIRECT) chunk_tail(0);   // (threshold mode: its tail needs the registers)
-  if (SC_SUB == 2) chunk_tail(1);
+  chunk_tail(0);
 }
 
 // ---------------------------------------------------------------- finish (one workgroup per sequence)
@@ -451,6 +548,7 @@ __global__ __launch_bounds__(SC_THREADS) void finish_threshold_kernel(
   const int b = blockIdx.x, tid = threadIdx.x;
   const int64_t n_pos = min((int64_t)n_entries[b], max_n);
   SelState* st = ctrl_state(sb.ctrl, b);
+  if (tid == 0) st->ncand = 0;            // select_kernel counts its candidates from here
   if (n_pos <= K) {                       // every position is selected (or none exists)
     if (tid == 0) { st->thr_bin = -1; st->above = 0; }
     return;
@@ -520,6 +618,28 @@ __global__ __launch_bounds__(FIN_THREADS) void finish_direct_kernel(
                                   [&](int j, int32_t v) { ob[j] = v; });
 }
 
+// Pool finish, one workgroup per sequence: pool_finish_body written to
+// pool[b][0 .. pool_k). sc_rows / g_rows: the sequence's scratch rows for the
+// fallback (scores recomputed, composites of a large threshold bin).
+__global__ __launch_bounds__(FIN_THREADS) void pool_finish_kernel(
+    const int32_t* __restrict__ n_entries, int64_t max_n, SelBufs sb, int pool_k, int32_t* __restrict__ pool,
+    float* __restrict__ sc_rows, int64_t sc_stride, uint64_t* __restrict__ g_rows, int64_t g_stride, ScoreSrc src) {
+  __shared__ uint64_t lc[FIN_LDS_CANDS];
+  __shared__ uint64_t sub[FIN_SUB_CAP];
+  __shared__ uint32_t loff[FIN_MAX_WG];
+  __shared__ uint32_t h[512];
+  __shared__ uint64_t red[32];
+  __shared__ uint32_t scan_tmp[32];
+  __shared__ uint32_t ctl[8];
+  __shared__ uint64_t binl[FIN_RANK_MAX];
+  __shared__ uint32_t bin_count;
+  const int b = blockIdx.x;
+  int32_t* ob = pool + (int64_t)b * pool_k;
+  const FinLds L{lc, sub, loff, h, red, scan_tmp, ctl, binl, &bin_count};
+  pool_finish_body<FIN_THREADS>(b, n_entries, max_n, pool_k, sb, sc_rows + (int64_t)b * sc_stride,
+                                g_rows + (int64_t)b * g_stride, src, L, [&](int j, int32_t v) { ob[j] = v; });
+}
+
 // ---------------------------------------------------------------- select (long)
 // Marking pass: every key above the threshold bin sets its bit in the
 // sequence's bitmap; keys inside the bin are appended as (key, position)
@@ -561,8 +681,8 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
       if (lane == 0) basei = atomicAdd(&st->ncand, (uint32_t)__popcll(bc));
       basei = readlane_u32(basei, 0);
       if (cnd) {
-        // (ncand starts at zero: the control block is left zero by every
-        // completed call; the bound keeps a dirty counter inside the row)
+        // (ncand was set to zero by finish_threshold_kernel; the bound keeps
+        // the writes inside the row)
         const uint64_t at = (uint64_t)basei + (uint32_t)__popcll(bc & ((1ull << lane) - 1ull));
         if (at < (uint64_t)cb_stride) cb[at] = composite(key, (uint32_t)i);
       }
@@ -766,8 +886,8 @@ hipError_t launch_score(const uint8_t* ik, const uint8_t* iks, const int64_t* en
                         const int32_t* n_entries, int B, int64_t max_n, const uint16_t* q_idx,
                         const float* w, int Hi, int mode, const int32_t* cand, int cand_stride,
                         float* scores, int64_t sstride, const SelBufs& sb, int sel, int K,
-                        bool store_scores, hipStream_t stream) {
-  const bool store = store_scores || cand || sel != SEL_DIRECT;
+                        bool store_scores, int pool_k, hipStream_t stream) {
+  const bool store = store_scores || cand || (sel != SEL_DIRECT && sel != SEL_POOL);
   const int64_t nslots = cand ? cand_stride : max_n;
   if (nslots <= 0) return hipSuccess;
   const int64_t nx = (nslots + SC_SPAN - 1) / SC_SPAN;
@@ -777,7 +897,7 @@ hipError_t launch_score(const uint8_t* ik, const uint8_t* iks, const int64_t* en
 #define CSA2_SCORE_LAUNCH1(C, S, Mo, Q)                                                          \
   hipLaunchKernelGGL((score_kernel<C, S, Mo, Q>), grid, block, 0, stream, ik, iks, entry_offset, \
                      n_entries, max_n, q_idx, w, Hi, cand, cand_stride, scores, sstride, sb, K,  \
-                     (int)store)
+                     (int)store, pool_k)
 #define CSA2_SCORE_LAUNCH(C, S)                                                                  \
   if (base == 0) {                                                                               \
     if (qmx) CSA2_SCORE_LAUNCH1(C, S, 0, true); else CSA2_SCORE_LAUNCH1(C, S, 0, false);         \
@@ -785,11 +905,17 @@ hipError_t launch_score(const uint8_t* ik, const uint8_t* iks, const int64_t* en
     if (qmx) CSA2_SCORE_LAUNCH1(C, S, 1, true); else CSA2_SCORE_LAUNCH1(C, S, 1, false);         \
   }
   if (cand) {
-    CSA2_SCORE_LAUNCH(true, SEL_NONE)
+    if (sel == SEL_DIRECT) {
+      CSA2_SCORE_LAUNCH(true, SEL_DIRECT)
+    } else {
+      CSA2_SCORE_LAUNCH(true, SEL_NONE)
+    }
   } else if (sel == SEL_THRESHOLD) {
     CSA2_SCORE_LAUNCH(false, SEL_THRESHOLD)
   } else if (sel == SEL_DIRECT) {
     CSA2_SCORE_LAUNCH(false, SEL_DIRECT)
+  } else if (sel == SEL_POOL) {
+    CSA2_SCORE_LAUNCH(false, SEL_POOL)
   } else {
     CSA2_SCORE_LAUNCH(false, SEL_NONE)
   }
@@ -798,12 +924,21 @@ hipError_t launch_score(const uint8_t* ik, const uint8_t* iks, const int64_t* en
   return hipGetLastError();
 }
 
+hipError_t launch_pool_finish(const int32_t* n_entries, int B, int64_t max_n, const SelBufs& sb, int pool_k,
+                              int32_t* pool, float* sc_rows, int64_t sc_stride, uint64_t* g_rows, int64_t g_stride,
+                              const ScoreSrc& src, hipStream_t stream) {
+  hipLaunchKernelGGL(pool_finish_kernel, dim3((unsigned)B), dim3(FIN_THREADS), 0, stream, n_entries, max_n, sb,
+                     pool_k, pool, sc_rows, sc_stride, g_rows, g_stride, src);
+  return hipGetLastError();
+}
+
 hipError_t launch_finish(int sel, const int32_t* n_entries, int B, int64_t max_n, float* scores,
                          int64_t sstride, const SelBufs& sb, int K, int32_t* out, int out_stride,
                          const ScoreSrc* src, hipStream_t stream) {
   if (sel == SEL_DIRECT)
     hipLaunchKernelGGL(finish_direct_kernel, dim3((unsigned)B), dim3(FIN_THREADS), 0, stream, n_entries, max_n,
-                       scores, sstride, sb, K, out, out_stride, src ? *src : ScoreSrc{}, src ? 1 : 0);
+                       scores, sstride, sb, K, out, out_stride, src ? *src : ScoreSrc{},
+                       (src && !src->cand) ? 1 : 0);
   else
     hipLaunchKernelGGL(finish_threshold_kernel, dim3((unsigned)B), dim3(SC_THREADS), 0, stream, n_entries,
                        max_n, scores, sstride, sb, K);

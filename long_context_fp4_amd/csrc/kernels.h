@@ -5,7 +5,9 @@
 
 namespace csa2 {
 
-// Per-sequence selection state kept in the indexer workspace (zero between calls).
+// Per-sequence selection state of the threshold path (k > 512). The threshold
+// kernel sets it (including the candidate counter) before the select kernel
+// reads it, so the workspace holds no state between calls.
 struct SelState {
   uint32_t unused0;
   uint32_t unused1;
@@ -18,15 +20,9 @@ static_assert(sizeof(SelState) == 64, "control block header");
 
 constexpr int kNumBins = 4096;
 constexpr int kSmallMax = 16384;
-// Per-sequence control block of the indexer workspace: SelState, then the
-// histogram. The control region at the start of the workspace always holds
-// CSA2_MAX_BATCH blocks, so a block's place never depends on B or max_n.
-constexpr int64_t kCtrlStride = 256 + 4 * kNumBins;   // 16640 bytes
+constexpr int64_t kCtrlStride = 64;   // one SelState per sequence
 __host__ __device__ inline SelState* ctrl_state(uint8_t* ctrl, int b) { return (SelState*)(ctrl + b * kCtrlStride); }
-__host__ __device__ inline uint32_t* ctrl_hist(uint8_t* ctrl, int b) { return (uint32_t*)(ctrl + b * kCtrlStride + 256); }
 
-// n_tokens, out_entry_offset: device [B] or NULL (every sequence T tokens;
-// sequence b at rows b * floor(T / m) ..).
 hipError_t launch_cache_write(const uint16_t* x_lat, const uint16_t* x_idx, const float* w_lat,
                               const float* w_idx, int B, int64_t T, int m, const int64_t* n_tokens,
                               const int64_t* out_entry_offset, uint8_t* kv, uint8_t* ik, uint8_t* iks,
@@ -49,7 +45,7 @@ hipError_t launch_cache_append(const uint16_t* x_lat, const uint16_t* x_idx, con
                                hipStream_t stream);
 
 // Selection modes of the score pass.
-enum { SEL_NONE = 0, SEL_THRESHOLD = 1, SEL_DIRECT = 2 };
+enum { SEL_NONE = 0, SEL_THRESHOLD = 1, SEL_DIRECT = 2, SEL_POOL = 3 };
 constexpr int kScoreChunk = 1024;     // slots per score workgroup
 constexpr int kScoreQmx8 = 0x100;     // score-mode flag: MXFP8 query, block-scaled FP8 x FP4 MFMA
 constexpr int kSumWords = 32;         // (bin, count) pairs a workgroup may report
@@ -57,10 +53,11 @@ constexpr int kCandCap = 256;         // candidates a workgroup reports in direc
 constexpr int kDirectMaxK = 512;      // largest k the score pass selects by itself
 constexpr int kFinMaxWg = 2048;       // score workgroups per sequence whose slots the finish reads
 constexpr int kFinLdsCands = 12288;   // candidates the direct finish holds in LDS
+constexpr int kPoolCap = kScoreChunk;  // pool candidates a score workgroup may report (its whole chunk)
 
 // Workspace views used by the score pass's selection (per-sequence strides).
 struct SelBufs {
-  uint8_t* ctrl;        // control blocks (SelState + histogram), fixed places
+  uint8_t* ctrl;        // SelState per sequence (threshold path)
   uint32_t* bitmap;     // [B][bm_stride] words; the score pass clears its chunk's words
   int64_t bm_stride;
   uint64_t* hdr;        // [B][hdr_stride]: one header word per score workgroup
@@ -71,9 +68,14 @@ struct SelBufs {
   int64_t wgc_stride;
   uint64_t* gscr;       // [B][gscr_stride]: gathered candidates that do not fit LDS
   int64_t gscr_stride;
+  uint64_t* hdrp;       // [B][hdr_stride]: pool header per score workgroup (pool mode)
+  uint64_t* wgcp;       // [B][wgcp_stride]: kPoolCap pool candidates per workgroup (pool mode)
+  int64_t wgcp_stride;
 };
 
-// What the score pass reads, for a finish that has to recompute scores.
+// What the score pass reads, for a finish that has to recompute scores; for a
+// candidate list (Reindex), the list and the scores the pass stored per slot
+// (a slot the list does not use holds the key 0) instead.
 struct ScoreSrc {
   const uint8_t* ik;
   const uint8_t* iks;
@@ -82,17 +84,23 @@ struct ScoreSrc {
   const float* w;
   int Hi;
   int mode;
+  const int32_t* cand;          // [B][cand_stride] or NULL
+  int cand_stride;
+  const float* cand_scores;     // [B][cand_scores_stride]
+  int64_t cand_scores_stride;
 };
 
-// store_scores: direct mode may skip storing the scores (the finish recomputes
-// a sequence's scores in its rare fallback); the other modes always store.
+// store_scores: direct and pool modes may skip storing the scores (the finish
+// recomputes a sequence's scores in its rare fallback); the other modes, and
+// every candidate-list pass, always store. pool_k: the pool size (pool mode).
 hipError_t launch_score(const uint8_t* ik, const uint8_t* iks, const int64_t* entry_offset,
                         const int32_t* n_entries, int B, int64_t max_n, const uint16_t* q_idx,
                         const float* w, int Hi, int mode, const int32_t* cand, int cand_stride,
                         float* scores, int64_t sstride, const SelBufs& sb, int sel, int K,
-                        bool store_scores, hipStream_t stream);
+                        bool store_scores, int pool_k, hipStream_t stream);
 
-// src: non-null when the direct score pass did not store the scores.
+// src: non-null when the direct score pass did not store the scores, or for a
+// candidate list (src->cand set).
 hipError_t launch_finish(int sel, const int32_t* n_entries, int B, int64_t max_n, float* scores,
                          int64_t sstride, const SelBufs& sb, int K, int32_t* out, int out_stride,
                          const ScoreSrc* src, hipStream_t stream);
@@ -106,11 +114,20 @@ hipError_t launch_select_small(const float* scores, int64_t sstride, const int32
                                int pstride, int score_by_pos, const int32_t* n_entries, int B,
                                int64_t max_n, int K, int32_t* out, int out_stride, hipStream_t stream);
 
+// Pool finish of a pool-mode score pass, one workgroup per sequence: the best
+// pool_k positions, ascending, into pool [B][pool_k]. scratch rows (scores,
+// composites) per sequence serve its fallback.
+hipError_t launch_pool_finish(const int32_t* n_entries, int B, int64_t max_n, const SelBufs& sb, int pool_k,
+                              int32_t* pool, float* sc_rows, int64_t sc_stride, uint64_t* g_rows, int64_t g_stride,
+                              const ScoreSrc& src, hipStream_t stream);
+
 // A decode attention that derives its indices itself: every workgroup runs the
 // direct top-k finish of its sequence over the lists a direct score pass left
-// (scores not stored), keeps its split of the result in LDS, and the first
-// workgroup of each sequence writes the top-k to `topk`. scores / gscr give
-// every attention workgroup rows of its own for the finish's fallback.
+// (scores not stored, or a candidate list's stored scores), keeps the result in
+// LDS, and the first workgroup of each sequence writes the top-k to `topk`.
+// scores / gscr give every workgroup rows of its own for the finish's fallback.
+// With pool_k > 0 the launch has B more workgroups, one per sequence, that
+// run the pool finish of a pool-mode score pass into `pool`.
 struct FusedFinish {
   SelBufs sb;
   ScoreSrc src;
@@ -120,6 +137,8 @@ struct FusedFinish {
   uint64_t* gscr;         // [workgroups][gscr_stride] (>= max(max_n, kFinLdsCands) per row)
   int64_t gscr_stride;
   int32_t* topk;          // [B][k]
+  int pool_k;             // 0, or the pool size
+  int32_t* pool;          // [B][pool_k]
 };
 
 // Attention: number of entry splits used for B sequences, H heads, k indices.

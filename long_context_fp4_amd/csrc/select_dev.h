@@ -382,6 +382,137 @@ __device__ inline uint32_t ordered_compact(uint32_t n, Pred pred, Emit emit, uin
   return total;
 }
 
+// The selection over every score of a sequence, for a finish whose candidate
+// lists do not hold the K best (a list overflowed, the lists exceed LDS or
+// fewer than K keys reach the highest cutoff): a histogram of all the keys
+// (12-bit bins); the threshold bin is the range of the 256 20-bit prefixes
+// under bin T; its keys are radix-selected; an ordered compaction writes the
+// K best in position order through emit(j, position), -1 past the selected
+// ones. Full pass: sall is a row of at least n_pos floats, recomputed here
+// when `rescore` is set (the score pass stored none); candidate list
+// (src.cand): the scores the pass stored per slot. All threads call it.
+template <int NT, typename Emit>
+__device__ inline void fallback_select(int b, int64_t n_pos, int K, float* sall, uint64_t* gscr, const ScoreSrc& src,
+                                       int rescore, const FinLds& L, Emit emit) {
+  uint64_t* const sub = L.sub;
+  uint32_t* const h = L.h;
+  uint64_t* const red = L.red;
+  uint32_t* const scan_tmp = L.scan_tmp;
+  uint32_t* const ctl = L.ctl;
+  uint32_t* hist = (uint32_t*)sub;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int NWAVE = NT / 64;
+  const bool lst = src.cand != nullptr;
+  const int32_t* crow = lst ? src.cand + (int64_t)b * src.cand_stride : nullptr;
+  const int64_t n_slots = lst ? (int64_t)src.cand_stride : n_pos;
+  if (lst) {
+    sall = const_cast<float*>(src.cand_scores) + (int64_t)b * src.cand_scores_stride;
+  } else if (rescore) {
+    __shared__ __attribute__((aligned(16))) float lwf[16];
+    const int n = lane & 15, g = lane >> 4;
+    const int64_t row_base = src.entry_offset[b];
+    const uint8_t* ikb = src.ik + row_base * 64;
+    const uint8_t* iksb = src.iks + row_base * 4;
+    const bool qmx = (src.mode & kScoreQmx8) != 0;
+    const int base = src.mode & ~kScoreQmx8;
+    const uint16_t* qrow = n < src.Hi ? src.q_idx + ((int64_t)b * src.Hi + n) * 128 : nullptr;
+    bf16x8_t qa[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      u32x4_t v = {0, 0, 0, 0};
+      if (qrow) v = *(const u32x4_t*)(qrow + 32 * g + 8 * j);
+      __builtin_memcpy(&qa[j], &v, 16);
+    }
+    uint8_t* lq = (uint8_t*)sub;                   // free until the histogram below
+    if (qmx) query_mx_stage(src.q_idx + (int64_t)b * src.Hi * 128, src.Hi, lq, tid);
+    if (tid < 16) lwf[tid] = tid < src.Hi ? (src.w ? src.w[(int64_t)b * src.Hi + tid] : 1.0f) : 0.0f;
+    __syncthreads();
+    QueryMx qm;
+    if (qmx) qm = query_mx_operand(lq, lane);
+    for (int64_t t0 = 16 * wave; t0 < n_pos; t0 += 16 * NWAVE) {
+      const uint32_t p = (uint32_t)min(t0 + n, n_pos - 1);
+      const u32x4_t cw = *(const u32x4_t*)(ikb + ((uint64_t)p * 64u + 16u * g));
+      const uint32_t sbyte = iksb[(uint64_t)p * 4u + (uint32_t)g];
+      float sc;
+      if (qmx) sc = base == 0 ? score_tile_mx<0>(qm, cw, sbyte, lwf, g) : score_tile_mx<1>(qm, cw, sbyte, lwf, g);
+      else sc = base == 0 ? score_tile_fn<0>(qa, cw, sbyte, lwf, g) : score_tile_fn<1>(qa, cw, sbyte, lwf, g);
+      if (g == 0 && t0 + n < n_pos) sall[t0 + n] = sc;
+    }
+    __threadfence_block();                         // this workgroup reads them back
+  }
+  __syncthreads();
+  for (int i = tid; i < NBINS; i += NT) hist[i] = 0;
+  __syncthreads();
+  // (a candidate list's unused slots hold the key 0, which no score has)
+  const uint32_t n_src = (uint32_t)n_slots;
+  uint32_t nvalid = 0;
+  for (uint32_t i = tid; i < n_src; i += NT) {
+    const uint32_t key = score_key(sall[i]);
+    if (!lst || key != 0u) {
+      atomicAdd(&hist[key >> BIN_SHIFT], 1u);
+      ++nvalid;
+    }
+  }
+  __syncthreads();
+  uint32_t tot;
+  hist_kth_bin<NT>(hist, (uint32_t)K, scan_tmp, ctl, &tot);   // all valid keys are counted
+  auto pos_of = [&](uint32_t i) -> uint32_t { return lst ? (uint32_t)crow[i] : i; };
+  auto valid = [&](uint32_t i) -> bool { return !lst || score_key(sall[i]) != 0u; };
+  auto elem = [&](uint32_t i) -> uint64_t { return composite(score_key(sall[i]), pos_of(i)); };
+  if (ctl[0] == 0xFFFFFFFFu) {
+    // at most K valid slots: every one is selected, in slot (= position) order
+    const uint32_t nsel = ordered_compact(
+        n_src, [&](uint32_t i) { return valid(i); },
+        [&](uint32_t i, uint32_t at) {
+          if (at < (uint32_t)K) emit((int)at, (int32_t)pos_of(i));
+        },
+        scan_tmp);
+    for (uint32_t j = nsel + tid; j < (uint32_t)K; j += NT) emit((int)j, -1);
+    return;
+  }
+  const uint32_t T = ctl[0], above = ctl[1], in_bin = hist[T];
+  const uint32_t need = (uint32_t)K - above;      // 1 .. in_bin
+  const uint32_t lo20 = T << 8;
+  const uint32_t hi20 = (T << 8) | 255u;
+  uint64_t prefix = 0, mask = 0;
+  if (need < in_bin) {
+    // the threshold bin is split: its keys (unordered) -> radix select
+    __syncthreads();                               // hist reads done before sub is reused
+    uint64_t* dst = in_bin <= (uint32_t)FIN_SUB_CAP ? sub : gscr;
+    if (tid == 0) ctl[6] = 0;
+    __syncthreads();
+    for (uint32_t i0 = 0; i0 < n_src; i0 += NT) {
+      const uint32_t i = i0 + tid;
+      const bool ok = i < n_src && valid(i);
+      const uint64_t c = ok ? elem(i) : 0ull;
+      const uint32_t p20 = (uint32_t)(c >> 44);
+      const bool t = ok && p20 >= lo20 && p20 <= hi20;
+      const uint32_t at = wave_append(t, &ctl[6]);
+      if (t && at < in_bin) dst[at] = c;
+    }
+    if (dst != sub) __threadfence_block();         // this workgroup reads its global copy back
+    __syncthreads();
+    const int top = radix_top_shift(dst, in_bin, red);
+    radix_select_u64(dst, in_bin, need, top, h, ctl, &prefix, &mask);
+  }
+  // the K best in position order: above the threshold bin, or inside it and
+  // radix-selected
+  const uint32_t nsel = ordered_compact(
+      n_src,
+      [&](uint32_t i) {
+        if (!valid(i)) return false;
+        const uint64_t c = elem(i);
+        const uint32_t p20 = (uint32_t)(c >> 44);
+        return p20 > hi20 || (p20 >= lo20 && p20 <= hi20 && (c & mask) >= prefix);
+      },
+      [&](uint32_t i, uint32_t at) {
+        if (at < (uint32_t)K) emit((int)at, (int32_t)pos_of(i));
+      },
+      scan_tmp);
+  for (uint32_t j = nsel + tid; j < (uint32_t)K; j += NT) emit((int)j, -1);
+  (void)nvalid;
+}
+
 // Direct top-K (K <= kDirectMaxK). The candidate lists hold, per workgroup,
 // every key whose top 20 bits reach its refined cutoff, in position order, so
 // their concatenation in workgroup order is in position order too; the ones
@@ -423,7 +554,7 @@ __device__ inline void finish_direct_body(int b, const int32_t* __restrict__ n_e
   // The first header words, and the first 64 entries of the FS lists this
   // wave handles first (chunks FS * wave .. FS * wave + FS - 1), are requested
   // before the sequence length and the list lengths are known.
-  const int64_t nw_max = (max_n + SC_CHUNK - 1) / SC_CHUNK;
+  const int64_t nw_max = ((src.cand ? max(max_n, (int64_t)src.cand_stride) : max_n) + SC_CHUNK - 1) / SC_CHUNK;
   const uint64_t* hd = sb.hdr + (int64_t)b * sb.hdr_stride;
   const uint64_t h0 = tid < nw_max ? hd[tid] : 0ull;
   const uint64_t* wc = sb.wgc + (int64_t)b * sb.wgc_stride;
@@ -437,12 +568,19 @@ __device__ inline void finish_direct_body(int b, const int32_t* __restrict__ n_e
   // latency then overlaps the sequence-length load)
   asm volatile("" ::: "memory");
   const int64_t n_pos = min((int64_t)n_entries[b], max_n);
-  if (n_pos <= K) {                       // every position is selected (or none exists)
+  // a candidate list (Reindex): its slots, their stored scores (key 0: unused)
+  const bool lst = src.cand != nullptr;
+  if (!lst && n_pos <= K) {               // every position is selected (or none exists)
     for (int j = tid; j < K; j += NT) emit(j, j < n_pos ? j : -1);
     return;
   }
+  if (lst && n_pos <= 0) {                // no listed position can be used
+    for (int j = tid; j < K; j += NT) emit(j, -1);
+    return;
+  }
   for (int i = tid; i < NBINS; i += NT) hist[i] = 0;
-  const int64_t nw = (n_pos + SC_CHUNK - 1) / SC_CHUNK;
+  const int64_t n_slots = lst ? (int64_t)src.cand_stride : n_pos;
+  const int64_t nw = (n_slots + SC_CHUNK - 1) / SC_CHUNK;
   uint32_t cmax = 0;
   auto p20_of = [](uint64_t c) { return (uint32_t)(c >> 44); };
   auto count_above_cmax = [&](uint64_t c) {
@@ -635,92 +773,190 @@ __device__ inline void finish_direct_body(int b, const int32_t* __restrict__ n_e
       }
     }
   }
-  // Fallback: the same steps on a histogram of every score of the sequence
-  // (12-bit key bins); the threshold bin is the range of the 256 20-bit
-  // prefixes under bin T. When the score pass did not store the scores, this
-  // workgroup recomputes the sequence's first.
-  if (rescore) {
-    __shared__ __attribute__((aligned(16))) float lwf[16];
-    const int n = lane & 15, g = lane >> 4;
-    const int64_t row_base = src.entry_offset[b];
-    const uint8_t* ikb = src.ik + row_base * 64;
-    const uint8_t* iksb = src.iks + row_base * 4;
-    const bool qmx = (src.mode & kScoreQmx8) != 0;
-    const int base = src.mode & ~kScoreQmx8;
-    const uint16_t* qrow = n < src.Hi ? src.q_idx + ((int64_t)b * src.Hi + n) * 128 : nullptr;
-    bf16x8_t qa[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      u32x4_t v = {0, 0, 0, 0};
-      if (qrow) v = *(const u32x4_t*)(qrow + 32 * g + 8 * j);
-      __builtin_memcpy(&qa[j], &v, 16);
-    }
-    uint8_t* lq = (uint8_t*)sub;                   // free until the histogram below
-    if (qmx) query_mx_stage(src.q_idx + (int64_t)b * src.Hi * 128, src.Hi, lq, tid);
-    if (tid < 16) lwf[tid] = tid < src.Hi ? (src.w ? src.w[(int64_t)b * src.Hi + tid] : 1.0f) : 0.0f;
-    __syncthreads();
-    QueryMx qm;
-    if (qmx) qm = query_mx_operand(lq, lane);
-    for (int64_t t0 = 16 * wave; t0 < n_pos; t0 += 16 * NWAVE) {
-      const uint32_t p = (uint32_t)min(t0 + n, n_pos - 1);
-      const u32x4_t cw = *(const u32x4_t*)(ikb + ((uint64_t)p * 64u + 16u * g));
-      const uint32_t sbyte = iksb[(uint64_t)p * 4u + (uint32_t)g];
-      float sc;
-      if (qmx) sc = base == 0 ? score_tile_mx<0>(qm, cw, sbyte, lwf, g) : score_tile_mx<1>(qm, cw, sbyte, lwf, g);
-      else sc = base == 0 ? score_tile_fn<0>(qa, cw, sbyte, lwf, g) : score_tile_fn<1>(qa, cw, sbyte, lwf, g);
-      if (g == 0 && t0 + n < n_pos) sall[t0 + n] = sc;
-    }
-    __threadfence_block();                         // this workgroup reads them back
+  // Fallback: the same steps over every score of the sequence
+  fallback_select<NT>(b, n_pos, K, sall, gscr, src, rescore, L, emit);
+}
+
+// Pool finish (the K best positions, ascending) from the pool lists of a
+// pool-mode score pass. Chunk c's list holds, in position order, every key of
+// the chunk whose 20-bit prefix reaches its cutoff; its header packs count |
+// cutoff << 11 | the chunk's largest prefix << 32. At or above the highest
+// cutoff cmax every list is complete, so when at least K keys reach cmax the
+// K best are among the listed ones. Three sweeps over the lists:
+//   1. a histogram of the prefixes at or above cmax, in 4096 bins of 2^s
+//      prefix units counted down from the largest prefix (s is the smallest
+//      shift that fits the range down to cmax), and the bin T of the K-th;
+//   2. every chunk counts its keys above T, and the keys inside T are
+//      collected (LDS, or this workgroup's scratch row when more) and the
+//      `need` best of them found exactly by radix select on the composite;
+//   3. every chunk writes its selected positions at the offset the prefix
+//      sum of the counts gives.
+// A wave sweeps chunks wave, wave + 8, ... in groups of PF_G, with every
+// group's list entries requested before any is used. Fewer than K keys at or
+// above cmax: fallback_select. Output through emit(j, position) for j < K.
+template <int NT, typename Emit>
+__device__ inline void pool_finish_body(int b, const int32_t* __restrict__ n_entries, int64_t max_n, int K,
+                                        const SelBufs& sb, float* sall, uint64_t* gscr, const ScoreSrc& src,
+                                        const FinLds& L, Emit emit) {
+  constexpr int NWAVE = NT / 64;
+  constexpr int PF_G = 8;                               // chunks whose entries a wave requests at once
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t* const hist = (uint32_t*)L.sub;              // 4096 bins, then the in-bin keys
+  uint32_t* const lcount = (uint32_t*)L.lc;             // [nw] list lengths
+  uint32_t* const cnt = L.loff;                         // [nw] selected per chunk, then offsets
+  uint32_t* const ctl = L.ctl;
+  uint32_t* const scan_tmp = L.scan_tmp;
+  const int64_t n_pos = min((int64_t)n_entries[b], max_n);
+  if (n_pos <= K) {
+    for (int j = tid; j < K; j += NT) emit(j, j < n_pos ? j : -1);
+    return;
   }
-  __syncthreads();
+  const int nw = (int)((n_pos + SC_CHUNK - 1) / SC_CHUNK);
+  if (nw > FIN_MAX_WG) {                                // more chunks than the LDS counts hold
+    fallback_select<NT>(b, n_pos, K, sall, gscr, src, 1, L, emit);
+    return;
+  }
+  const uint64_t* hd = sb.hdrp + (int64_t)b * sb.hdr_stride;
+  const uint64_t* wl = sb.wgcp + (int64_t)b * sb.wgcp_stride;
+  uint32_t cmax = 0, mx = 0;
+  for (int c = tid; c < nw; c += NT) {
+    const uint64_t h = hd[c];
+    lcount[c] = (uint32_t)h & 0x7FFu;
+    cmax = max(cmax, (uint32_t)(h >> 11) & 0xFFFFFu);
+    mx = max(mx, (uint32_t)(h >> 32));
+    cnt[c] = 0;
+  }
   for (int i = tid; i < NBINS; i += NT) hist[i] = 0;
-  __syncthreads();
-  for (int64_t i = tid; i < n_pos; i += NT) atomicAdd(&hist[score_key(sall[i]) >> BIN_SHIFT], 1u);
-  __syncthreads();
   {
-    uint32_t tot;
-    hist_kth_bin<NT>(hist, (uint32_t)K, scan_tmp, ctl, &tot);   // defined: n_pos > K
+    const uint32_t a = wave_max_u32(cmax), m = wave_max_u32(mx);
+    if (lane == 0) { scan_tmp[wave] = a; scan_tmp[16 + wave] = m; }
+    __syncthreads();
+    cmax = 0; mx = 0;
+#pragma unroll
+    for (int v = 0; v < NWAVE; ++v) { cmax = max(cmax, scan_tmp[v]); mx = max(mx, scan_tmp[16 + v]); }
+    __syncthreads();
+  }
+  mx = max(mx, cmax);
+  int sh = 0;
+  while (((mx - cmax) >> sh) >= (uint32_t)NBINS) ++sh;
+  // bin of a prefix p >= cmax, NBINS - 1 for the largest (hist_kth_bin counts down from there)
+  auto bin_of = [&](uint32_t p) -> uint32_t { return (uint32_t)NBINS - 1u - min((mx - p) >> sh, (uint32_t)NBINS - 1u); };
+  // one sweep: fn(c, j0, v0, ok0, v1, ok1) per block of 128 entries (from
+  // entry j0) of chunk c's list, lane l holding entries j0 + 2l and j0 + 2l + 1
+  // (wave-uniform calls, the blocks of a chunk in order, one wave per chunk)
+  auto sweep = [&](auto fn) {
+    for (int c0 = wave; c0 < nw; c0 += NWAVE * PF_G) {
+      u32x4_t v[PF_G];
+      uint32_t n[PF_G];
+#pragma unroll
+      for (int gi = 0; gi < PF_G; ++gi) {
+        const int c = c0 + NWAVE * gi;
+        n[gi] = c < nw ? lcount[c] : 0u;
+        v[gi] = 2u * lane < n[gi] ? *(const u32x4_t*)(wl + (int64_t)c * kPoolCap + 2 * lane) : u32x4_t{0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int gi = 0; gi < PF_G; ++gi) {
+        const int c = c0 + NWAVE * gi;
+        if (c < nw) {
+          fn(c, 0u, ((uint64_t)v[gi][1] << 32) | v[gi][0], 2u * lane < n[gi],
+             ((uint64_t)v[gi][3] << 32) | v[gi][2], 2u * lane + 1 < n[gi]);
+          for (uint32_t j0 = 128; j0 < n[gi]; j0 += 128) {     // long lists
+            const uint32_t j = j0 + 2 * lane;
+            const u32x4_t x = j < n[gi] ? *(const u32x4_t*)(wl + (int64_t)c * kPoolCap + j) : u32x4_t{0, 0, 0, 0};
+            fn(c, j0, ((uint64_t)x[1] << 32) | x[0], j < n[gi], ((uint64_t)x[3] << 32) | x[2], j + 1 < n[gi]);
+          }
+        }
+      }
+    }
+  };
+  auto p20_of = [](uint64_t c) { return (uint32_t)(c >> 44); };
+  // sweep 1: histogram
+  sweep([&](int, uint32_t, uint64_t v0, bool ok0, uint64_t v1, bool ok1) {
+    const uint32_t p0 = p20_of(v0), p1 = p20_of(v1);
+    if (ok0 && p0 >= cmax) atomicAdd(&hist[bin_of(p0)], 1u);
+    if (ok1 && p1 >= cmax) atomicAdd(&hist[bin_of(p1)], 1u);
+  });
+  __syncthreads();
+  uint32_t tot;
+  hist_kth_bin<NT>(hist, (uint32_t)K, scan_tmp, ctl, &tot);
+  if (ctl[0] == 0xFFFFFFFFu) {                          // fewer than K keys reach cmax
+    fallback_select<NT>(b, n_pos, K, sall, gscr, src, 1, L, emit);
+    return;
   }
   const uint32_t T = ctl[0], above = ctl[1], in_bin = hist[T];
-  const uint32_t need = (uint32_t)K - above;      // 1 .. in_bin
-  const uint32_t lo20 = T << 8;
-  const uint32_t hi20 = (T << 8) | 255u;
-  auto elem = [&](uint32_t i) -> uint64_t { return composite(score_key(sall[i]), i); };
-  const uint32_t n_src = (uint32_t)n_pos;
-  uint64_t prefix = 0, mask = 0;
-  if (need < in_bin) {
-    // the threshold bin is split: its keys (unordered) -> radix select
-    __syncthreads();                               // hist reads done before sub is reused
-    uint64_t* dst = in_bin <= (uint32_t)FIN_SUB_CAP ? sub : gscr;
-    if (tid == 0) ctl[6] = 0;
-    __syncthreads();
-    for (uint32_t i0 = 0; i0 < n_src; i0 += NT) {
-      const uint32_t i = i0 + tid;
-      const uint64_t c = i < n_src ? elem(i) : 0ull;
-      const uint32_t p20 = (uint32_t)(c >> 44);
-      const bool t = i < n_src && p20 >= lo20 && p20 <= hi20;
-      const uint32_t at = wave_append(t, &ctl[6]);
-      if (t && at < in_bin) dst[at] = c;
+  const uint32_t need = (uint32_t)K - above;            // 1 .. in_bin
+  const bool split = need < in_bin;
+  auto in_t = [&](uint32_t p) { return p >= cmax && bin_of(p) == T; };
+  auto above_t = [&](uint32_t p) { return p >= cmax && bin_of(p) > T; };
+  __syncthreads();                                      // hist reads done before it is reused
+  uint64_t* const dst = in_bin <= (uint32_t)FIN_SUB_CAP ? L.sub : gscr;
+  if (tid == 0) ctl[6] = 0;
+  __syncthreads();
+  // sweep 2: counts above T per chunk (and inside T when all of it is taken);
+  // the keys inside T otherwise. A chunk's count is summed in a wave-uniform
+  // register over its blocks and stored after the last one (LDS written by one
+  // lane is read by the others only after a barrier).
+  uint32_t run_k = 0;
+  sweep([&](int c, uint32_t j0, uint64_t v0, bool ok0, uint64_t v1, bool ok1) {
+    const uint32_t p0 = p20_of(v0), p1 = p20_of(v1);
+    const bool a0 = ok0 && (above_t(p0) || (!split && in_t(p0)));
+    const bool a1 = ok1 && (above_t(p1) || (!split && in_t(p1)));
+    run_k = (j0 == 0 ? 0u : run_k) + (uint32_t)__popcll(__ballot(a0)) + (uint32_t)__popcll(__ballot(a1));
+    if (lane == 0 && j0 + 128u >= lcount[c]) cnt[c] = run_k;
+    if (split) {
+      const bool t0 = ok0 && in_t(p0), t1 = ok1 && in_t(p1);
+      const uint32_t at0 = wave_append(t0, &ctl[6]);
+      if (t0 && at0 < in_bin) dst[at0] = v0;
+      const uint32_t at1 = wave_append(t1, &ctl[6]);
+      if (t1 && at1 < in_bin) dst[at1] = v1;
     }
-    if (dst != sub) __threadfence_block();         // this workgroup reads its global copy back
+  });
+  uint64_t prefix = 0, mask = 0;
+  if (split) {
+    if (dst != L.sub) __threadfence_block();            // this workgroup reads its global copy back
     __syncthreads();
-    const int top = radix_top_shift(dst, in_bin, red);
-    radix_select_u64(dst, in_bin, need, top, h, ctl, &prefix, &mask);
+    const int top = radix_top_shift(dst, in_bin, L.red);
+    radix_select_u64(dst, in_bin, need, top, L.h, ctl, &prefix, &mask);
+    for (uint32_t i = tid; i < in_bin; i += NT) {
+      const uint64_t v = dst[i];
+      if ((v & mask) >= prefix) atomicAdd(&cnt[(0xFFFFFFFFu - (uint32_t)v) / (uint32_t)SC_CHUNK], 1u);
+    }
   }
-  // the K best in position order: above the threshold bin, or inside it and
-  // radix-selected
-  const uint32_t nsel = ordered_compact(
-      n_src,
-      [&](uint32_t i) {
-        const uint64_t c = elem(i);
-        const uint32_t p20 = (uint32_t)(c >> 44);
-        return p20 > hi20 || (p20 >= lo20 && p20 <= hi20 && (c & mask) >= prefix);
-      },
-      [&](uint32_t i, uint32_t at) {
-        if (at < (uint32_t)K) emit((int)at, (int32_t)i);
-      },
-      scan_tmp);
-  for (uint32_t j = nsel + tid; j < (uint32_t)K; j += NT) emit((int)j, -1);
+  __syncthreads();
+  // offsets: an exclusive scan of the counts (thread t: chunks t * per ..)
+  {
+    const int per = (nw + NT - 1) / NT;
+    const int w0 = min(tid * per, nw), w1 = min(w0 + per, nw);
+    uint32_t sum = 0;
+    for (int c = w0; c < w1; ++c) sum += cnt[c];
+    uint32_t total;
+    uint32_t run = block_exclusive_scan(sum, scan_tmp, &total);
+    for (int c = w0; c < w1; ++c) {
+      const uint32_t x = cnt[c];
+      cnt[c] = run;
+      run += x;
+    }
+  }
+  __syncthreads();
+  // sweep 3: the selected positions of each chunk at its offset, in list order
+  // (entry 2l before 2l + 1, lane by lane)
+  // (the running offset of a chunk is a wave-uniform register: the chunk's
+  // offset at its first block, then advanced by each block's selections)
+  uint32_t run_o = 0;
+  sweep([&](int c, uint32_t j0, uint64_t v0, bool ok0, uint64_t v1, bool ok1) {
+    auto sel = [&](uint64_t v, bool ok) {
+      const uint32_t p = p20_of(v);
+      return ok && (above_t(p) || (in_t(p) && (!split || (v & mask) >= prefix)));
+    };
+    const bool s0 = sel(v0, ok0), s1 = sel(v1, ok1);
+    const uint64_t m0 = __ballot(s0), m1 = __ballot(s1);
+    const uint64_t below = (1ull << lane) - 1ull;
+    if (j0 == 0) run_o = cnt[c];
+    const uint32_t r0 = run_o + (uint32_t)__popcll(m0 & below) + (uint32_t)__popcll(m1 & below);
+    if (s0) emit((int)r0, (int32_t)(0xFFFFFFFFu - (uint32_t)v0));
+    if (s1) emit((int)(r0 + (s0 ? 1u : 0u)), (int32_t)(0xFFFFFFFFu - (uint32_t)v1));
+    run_o += (uint32_t)__popcll(m0) + (uint32_t)__popcll(m1);
+  });
 }
 
 

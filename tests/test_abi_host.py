@@ -135,9 +135,15 @@ def test_indexer_validation(L):
     assert idx_call(L, cand=P, cs=20000) == -2
     assert idx_call(L, q=P + 8) == -3
     assert idx_call(L, ws=None) == -4
-    need = L.csa2_indexer_workspace_bytes(2, 1000, 0)
-    assert need >= 1024 * 16640                     # fixed-capacity control region
-    assert L.csa2_indexer_workspace_bytes(1025, 1000, 0) == 0
+    need = L.csa2_indexer_workspace_bytes(2, 1000, 512, 0, 0)
+    assert need > 0
+    # the pool lists and a Reindex list longer than max_n take more room
+    assert L.csa2_indexer_workspace_bytes(2, 1000, 512, 1024, 0) > need
+    assert L.csa2_indexer_workspace_bytes(2, 1000, 512, 0, 4096) > need
+    # the threshold path (k above the direct finish's limit) takes its bitmap and lists
+    assert L.csa2_indexer_workspace_bytes(2, 1000, 2048, 0, 0) > need
+    assert L.csa2_indexer_workspace_bytes(1025, 1000, 512, 0, 0) == 0
+    assert L.csa2_indexer_workspace_bytes(2, 1000, 0, 0, 0) == 0
     assert idx_call(L, B=1025) == -2
     assert idx_call(L, ws_bytes=need - 1) == -4
     assert "workspace" in err(L)

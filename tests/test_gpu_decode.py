@@ -48,11 +48,6 @@ def test_layer_group_full_reindex_reuse(n_list, pool_k):
     topR, _, outR, lseR = L.decode_layer(L.CSA2_REINDEX, q=dev(qR), q_idx=dev(qiR), w=dev(wR), pool=pool, **d)
     _, _, outU, lseU = L.decode_layer(L.CSA2_REUSE, q=dev(qU), topk=topR, **d)
     torch.cuda.synchronize()
-    assert int(ws.buf[: 1024 * 16640].count_nonzero()) == 0      # control region clean after the calls
-    # a standalone attention call on the same workspace leaves it clean too
-    L.sparse_attention(d["kv"], d["entry_offset"], d["n_entries"], topR, dev(qU), workspace=ws)
-    torch.cuda.synchronize()
-    assert int(ws.buf[: 1024 * 16640].count_nonzero()) == 0
     topF, pool, topR = host(topF), host(pool), host(topR)
     outF, outR, outU, lseF, lseR, lseU = map(host, (outF, outR, outU, lseF, lseR, lseU))
     for b, n in enumerate(n_list):

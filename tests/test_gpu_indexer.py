@@ -209,10 +209,10 @@ def test_fallback_recomputes_scores():
 
 
 def test_workspace_reuse_across_batch_sizes():
-    """Regression: one workspace reused by calls whose B and max_n shrink and grow again.
+    """One workspace reused by calls whose B and max_n shrink and grow again.
 
-    The control blocks must stay at fixed places; scratch regions of one call
-    must never land on a control block that a later, larger call uses.
+    The workspace holds no state between calls: each call lays its regions out
+    afresh and sets every counter it reads, whatever an earlier call left there.
     """
     import long_context_fp4_amd as L
     ws = L.Workspace()
@@ -230,8 +230,6 @@ def test_workspace_reuse_across_batch_sizes():
         top, sc = host(top), host(sc)
         for b, n in enumerate(n_list):
             check_sequence(ik, iks, off[b], n, q[b], w[b], 1, top[b], sc[b], k, what=f"B{B} seq{b}")
-        # the control region is clean again after every call
-        assert int(ws.buf[: 1024 * 16640].count_nonzero()) == 0
 
 
 def test_long_lists_take_the_lds_path():
