@@ -300,6 +300,31 @@ int csa2_decode_layer(int mode,
                       void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * csa2_decode_layer without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops and
+ * harnesses that forbid hipMalloc). It allocates nothing: its scratch is a
+ * static device array of CSA2_NOALLOC_SCRATCH_BYTES that each device the
+ * library runs on holds until the process ends. Arguments, outputs and errors
+ * are those of csa2_decode_layer (minus workspace and ws_bytes), with the same
+ * results. The fused two-launch plan is taken when its scratch fits the array,
+ * else the plan of separate indexer and attention launches; a call whose
+ * indexer scratch alone exceeds the array returns CSA2_ERR_WORKSPACE before
+ * any launch. The scratch needs no initialisation (every kernel writes what it
+ * reads), but all calls on one device share it: calls that overlap on a device
+ * (on different streams, or from different threads without ordering) race and
+ * must not be made.
+ */
+#define CSA2_NOALLOC_SCRATCH_BYTES (64u << 20)
+int csa2_decode_layer_noalloc(int mode,
+                              const uint8_t* kv, const uint8_t* ik, const uint8_t* iks,
+                              const int64_t* entry_offset, const int32_t* n_entries,
+                              int B, int64_t max_n,
+                              const uint16_t* q_idx, const float* w, int Hi, int score_mode,
+                              const uint16_t* q, int H, float softmax_scale,
+                              int k, int pool_k, int32_t* pool, int32_t* topk,
+                              float* out, float* lse, void* stream);
+
+/*
  * Multi-query (prefill) sparse attention over the same cache: Tq query tokens
  * per sequence, each with its own indexer query and its own causal top-k (the
  * layer mode Full of [CS] section "L'architecture : trois leviers contre le

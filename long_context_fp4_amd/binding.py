@@ -14,6 +14,7 @@ CSA2_OK = 0
 CSA2_SCORE_DOT, CSA2_SCORE_RELU_W = 0, 1
 CSA2_SCORE_QMX8 = 0x100          # flag: quantized-query (MXFP8) variant of either score
 CSA2_FULL, CSA2_REINDEX, CSA2_REUSE = 0, 1, 2
+CSA2_NOALLOC_SCRATCH_BYTES = 64 << 20   # static scratch of csa2_decode_layer_noalloc
 MAIN_ROW_BYTES, INDEXER_CODE_BYTES, INDEXER_SCALE_BYTES = 288, 64, 4
 
 _lib = None
@@ -66,6 +67,9 @@ def lib():
     L.csa2_decode_layer.argtypes = [i32, vp, vp, vp, vp, vp, i32, i64, vp, vp, i32, i32, vp, i32, f32, i32, i32,
                                     vp, vp, vp, vp, vp, sz, vp]
     L.csa2_decode_layer.restype = i32
+    L.csa2_decode_layer_noalloc.argtypes = [i32, vp, vp, vp, vp, vp, i32, i64, vp, vp, i32, i32, vp, i32, f32, i32,
+                                            i32, vp, vp, vp, vp, vp]
+    L.csa2_decode_layer_noalloc.restype = i32
     L.csa2_bytes_per_token.argtypes = [ctypes.POINTER(ctypes.c_int), i32, i32, i32, i32, i32, i32, i32]
     L.csa2_bytes_per_token.restype = ctypes.c_double
     L.csa2_set_profile_events.argtypes = [vp, vp]
@@ -344,10 +348,8 @@ def sparse_attention(kv, entry_offset, n_entries, idx, q, softmax_scale=1.0, wor
     return out, lse
 
 
-def decode_layer(mode, kv, ik, iks, entry_offset, n_entries, max_n, q, q_idx=None, w=None,
-                 score_mode=CSA2_SCORE_RELU_W, softmax_scale=1.0, k=512, pool_k=0, pool=None, topk=None,
-                 workspace=None, out=None, lse=None, stream=None):
-    """One CSA2 layer (Full / Reindex / Reuse). Returns (topk, pool, out, lse)."""
+def _layer_outputs(mode, q, q_idx, k, pool_k, pool, topk, out, lse):
+    """Output tensors of a layer call (allocated when not given) and its k, pool_k, Hi."""
     torch = _torch()
     B, H, _ = q.shape
     dev = q.device
@@ -367,16 +369,44 @@ def decode_layer(mode, kv, ik, iks, entry_offset, n_entries, max_n, q, q_idx=Non
         k = topk.shape[1]
     out = torch.empty((B, H, 512), dtype=torch.float32, device=dev) if out is None else out
     lse = torch.empty((B, H), dtype=torch.float32, device=dev) if lse is None else lse
+    return topk, pool, out, lse, k, pool_k, Hi
+
+
+def _layer_args(mode, kv, ik, iks, entry_offset, n_entries, max_n, q, q_idx, w, Hi, score_mode, softmax_scale, k,
+                pool_k, pool, topk, out, lse):
+    torch = _torch()
+    B, H, _ = q.shape
+    return (mode, _ptr(kv, torch.uint8, "kv"), _ptr(ik, torch.uint8, "ik"), _ptr(iks, torch.uint8, "iks"),
+            _ptr(entry_offset, torch.int64, "entry_offset"), _ptr(n_entries, torch.int32, "n_entries"), B,
+            int(max_n), _ptr(q_idx, _bf16_types(), "q_idx"), _ptr(w, torch.float32, "w"), Hi, score_mode,
+            _ptr(q, _bf16_types(), "q"), H, float(softmax_scale), k, pool_k, _ptr(pool, torch.int32, "pool"),
+            _ptr(topk, torch.int32, "topk"), _ptr(out, torch.float32, "out"), _ptr(lse, torch.float32, "lse"))
+
+
+def decode_layer(mode, kv, ik, iks, entry_offset, n_entries, max_n, q, q_idx=None, w=None,
+                 score_mode=CSA2_SCORE_RELU_W, softmax_scale=1.0, k=512, pool_k=0, pool=None, topk=None,
+                 workspace=None, out=None, lse=None, stream=None):
+    """One CSA2 layer (Full / Reindex / Reuse). Returns (topk, pool, out, lse)."""
+    topk, pool, out, lse, k, pool_k, Hi = _layer_outputs(mode, q, q_idx, k, pool_k, pool, topk, out, lse)
+    B, H, _ = q.shape
     nbytes = lib().csa2_decode_workspace_bytes(B, int(max_n), H, k, pool_k)
-    buf = _ws(workspace, dev).get(nbytes)
-    _check(lib().csa2_decode_layer(mode, _ptr(kv, torch.uint8, "kv"), _ptr(ik, torch.uint8, "ik"),
-                                   _ptr(iks, torch.uint8, "iks"), _ptr(entry_offset, torch.int64, "entry_offset"),
-                                   _ptr(n_entries, torch.int32, "n_entries"), B, int(max_n),
-                                   _ptr(q_idx, _bf16_types(), "q_idx"), _ptr(w, torch.float32, "w"), Hi,
-                                   score_mode, _ptr(q, _bf16_types(), "q"), H, float(softmax_scale), k, pool_k,
-                                   _ptr(pool, torch.int32, "pool"), _ptr(topk, torch.int32, "topk"),
-                                   _ptr(out, torch.float32, "out"), _ptr(lse, torch.float32, "lse"), _ptr(buf),
-                                   buf.numel(), _stream(stream)))
+    buf = _ws(workspace, q.device).get(nbytes)
+    args = _layer_args(mode, kv, ik, iks, entry_offset, n_entries, max_n, q, q_idx, w, Hi, score_mode,
+                       softmax_scale, k, pool_k, pool, topk, out, lse)
+    _check(lib().csa2_decode_layer(*args, _ptr(buf), buf.numel(), _stream(stream)))
+    return topk, pool, out, lse
+
+
+def decode_layer_noalloc(mode, kv, ik, iks, entry_offset, n_entries, max_n, q, topk, out, lse, q_idx=None, w=None,
+                         score_mode=CSA2_SCORE_RELU_W, softmax_scale=1.0, k=512, pool_k=0, pool=None, stream=None):
+    """decode_layer on the library's static scratch: the caller passes every output
+    (topk, out, lse, and pool for a Full layer with pool_k > 0). Returns (topk, pool, out, lse)."""
+    if mode == CSA2_FULL and pool_k and pool is None:
+        raise ValueError("a Full layer with pool_k > 0 needs the pool output")
+    topk, pool, out, lse, k, pool_k, Hi = _layer_outputs(mode, q, q_idx, k, pool_k, pool, topk, out, lse)
+    args = _layer_args(mode, kv, ik, iks, entry_offset, n_entries, max_n, q, q_idx, w, Hi, score_mode,
+                       softmax_scale, k, pool_k, pool, topk, out, lse)
+    _check(lib().csa2_decode_layer_noalloc(*args, _stream(stream)))
     return topk, pool, out, lse
 
 

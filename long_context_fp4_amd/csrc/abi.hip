@@ -6,6 +6,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
+#include <mutex>
 
 static_assert(CSA2_SCORE_QMX8 == csa2::kScoreQmx8, "score-mode flag differs between the header and the kernels");
 
@@ -422,10 +423,10 @@ namespace {
 int run_decode_layer(int mode, const uint8_t* kv, const uint8_t* ik, const uint8_t* iks, const int64_t* entry_offset,
                      const int32_t* n_entries, int B, int64_t max_n, const uint16_t* q_idx, const float* w, int Hi,
                      int score_mode, const uint16_t* q, int H, float softmax_scale, int k, int pool_k, int32_t* pool,
-                     int32_t* topk, float* out, float* lse, uint8_t* ws, hipStream_t s) {
+                     int32_t* topk, float* out, float* lse, uint8_t* ws, hipStream_t s, bool allow_fused = true) {
   const FusedPlan fp = fused_plan(mode, B, max_n, H, k, pool_k);
   const int cand_stride = mode == CSA2_REINDEX ? pool_k : 0;
-  if (fp.on) {
+  if (fp.on && allow_fused) {
     // scoring launch, then the attention that runs the top-k finish itself
     // (and, for a Full layer with a pool, the pool finish in workgroups of its own)
     const IndexerWs L = indexer_layout(B, max_n, k, mode == CSA2_FULL ? pool_k : 0, cand_stride);
@@ -478,6 +479,66 @@ int run_decode_layer(int mode, const uint8_t* kv, const uint8_t* ik, const uint8
   return hip_status(e, "decode_layer attention");
 }
 }  // namespace
+
+// Scratch of csa2_decode_layer_noalloc: one copy per device, held until the
+// process ends. Host code never passes `scratch` itself to a kernel (on the
+// host it names a stand-in, not device memory): the device address comes from
+// hipGetSymbolAddress, once per device.
+static __device__ __align__(256) uint8_t scratch[CSA2_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+uint8_t* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch in *out (looked up on the
+// first call on that device, with the device current); a status code.
+int device_scratch(uint8_t** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "decode_layer_noalloc: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(CSA2_ERR_UNSUPPORTED, "decode_layer_noalloc: device %d beyond the %d this library tracks", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "decode_layer_noalloc: hipGetSymbolAddress(scratch)");
+    if (!ptr) return fail(CSA2_ERR_HIP, "decode_layer_noalloc: hipGetSymbolAddress(scratch) gave NULL");
+    g_scratch_ptr[dev] = (uint8_t*)ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return CSA2_OK;
+}
+}  // namespace
+
+int csa2_decode_layer_noalloc(int mode, const uint8_t* kv, const uint8_t* ik, const uint8_t* iks,
+                              const int64_t* entry_offset, const int32_t* n_entries, int B, int64_t max_n,
+                              const uint16_t* q_idx, const float* w, int Hi, int score_mode, const uint16_t* q, int H,
+                              float softmax_scale, int k, int pool_k, int32_t* pool, int32_t* topk, float* out,
+                              float* lse, void* stream) {
+  int rc = check_decode_args(mode, kv, ik, iks, entry_offset, n_entries, B, max_n, q_idx, w, Hi, score_mode, q, H, k,
+                             pool_k, pool, topk, out, lse);
+  if (rc) return rc;
+  // this mode's scratch: the fused plan (scoring, then the attention that
+  // finishes the top-k itself) when it fits, else the plan of separate launches
+  const size_t cap = (size_t)CSA2_NOALLOC_SCRATCH_BYTES;
+  const size_t idx = mode == CSA2_REUSE ? 0
+                     : indexer_layout(B, max_n, k, mode == CSA2_FULL ? pool_k : 0,
+                                      mode == CSA2_REINDEX ? pool_k : 0).total;
+  const FusedPlan fp = fused_plan(mode, B, max_n, H, k, pool_k);
+  const size_t need_fused = fp.on ? idx + attention_scratch(B, H, k) + fp.bytes : 0;
+  const bool fused = fp.on && need_fused <= cap;
+  if (!fused && idx > cap)
+    return fail(CSA2_ERR_WORKSPACE, "decode_layer_noalloc: needs %zu bytes of scratch, the static scratch holds %zu",
+                idx, cap);
+  uint8_t* ws = nullptr;
+  rc = device_scratch(&ws);
+  if (rc) return rc;
+  return run_decode_layer(mode, kv, ik, iks, entry_offset, n_entries, B, max_n, q_idx, w, Hi, score_mode, q, H,
+                          softmax_scale, k, pool_k, pool, topk, out, lse, ws, (hipStream_t)stream, fused);
+}
 
 int csa2_decode_layer(int mode, const uint8_t* kv, const uint8_t* ik, const uint8_t* iks,
                       const int64_t* entry_offset, const int32_t* n_entries, int B, int64_t max_n,

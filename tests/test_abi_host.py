@@ -28,7 +28,7 @@ def test_header_declares_the_api():
     for n in ("csa2_cache_write", "csa2_cache_append", "csa2_swa_write", "csa2_swa_attention", "csa2_prefill_layer",
               "csa2_prefill_workspace_bytes", "csa2_indexer_topk", "csa2_sparse_attention", "csa2_decode_layer",
               "csa2_indexer_workspace_bytes", "csa2_attention_workspace_bytes", "csa2_decode_workspace_bytes",
-              "csa2_bytes_per_token", "csa2_last_error"):
+              "csa2_bytes_per_token", "csa2_last_error", "csa2_decode_layer_noalloc"):
         assert n in names
 
 
@@ -192,3 +192,25 @@ def test_product_path_refuses_cpu_tensors(L):
     x = torch.zeros((1, 4, 512), dtype=torch.int16)
     with pytest.raises(TypeError):
         Lp.cache_write(x, torch.zeros((1, 4, 128), dtype=torch.int16), torch.ones(2, 512), torch.ones(2, 128), 2)
+
+
+def test_decode_noalloc_validation(L):
+    """The allocation-free layer: the argument checks of the workspace one, and a
+    call whose indexer scratch exceeds the static array refused before any HIP call."""
+    from long_context_fp4_amd import binding
+
+    def call(**kw):
+        a = dict(mode=0, kv=P, B=2, max_n=1000, H=64, k=512, pool_k=0, pool=None, topk=P)
+        a.update(kw)
+        return L.csa2_decode_layer_noalloc(a["mode"], a["kv"], P, P, P, P, a["B"], a["max_n"], P, P, 16, 1, P,
+                                           a["H"], 1.0, a["k"], a["pool_k"], a["pool"], a["topk"], P, P, None)
+    assert call(kv=None) == -1
+    assert call(mode=5) == -5
+    assert call(B=0) == -2 and call(H=0) == -2 and call(k=0) == -2
+    assert call(mode=1, pool=None, pool_k=0) == -1               # Reindex needs the pool
+    assert call(topk=P + 4) == -3
+    assert call(B=4, max_n=1 << 22) == -4 and "static scratch" in err(L)
+    assert call(B=1024, max_n=1 << 20) == -4
+    assert binding.CSA2_NOALLOC_SCRATCH_BYTES == 64 << 20
+    hdr = open(HEADER).read()
+    assert "#define CSA2_NOALLOC_SCRATCH_BYTES (64u << 20)" in hdr
