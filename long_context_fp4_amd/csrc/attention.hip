@@ -160,30 +160,79 @@ __global__ __launch_bounds__(AT_THREADS) void attention_kernel(
   }
   constexpr int NIV = AT_MAX_K / AT_THREADS;
   int32_t iv[NIV];
+  // the finish's first loads (headers, list entries) go out with the queries'
+  FinPrefetch<AT_THREADS> pf;
   if (FIN) {
-    // the finish, while the queries are in flight
-    static_assert(AT_MAX_K >= FIN_MAX_WG && AT_LDS >= 8 * (FIN_LDS_CANDS + FIN_SUB_CAP) &&
-                  sizeof(pbuf) >= 4608, "the finish's LDS fits the attention's");
-    uint8_t* pb8 = (uint8_t*)&pbuf[0][0];
-    const FinLds fl{(uint64_t*)smem, (uint64_t*)(smem + 8 * FIN_LDS_CANDS), (uint32_t*)sidx,
-                    (uint32_t*)(pb8 + 512), (uint64_t*)pb8, (uint32_t*)(pb8 + 256), (uint32_t*)(pb8 + 384),
-                    (uint64_t*)(pb8 + 2560), (uint32_t*)(pb8 + 416)};
-    const bool writer = hg == 0;
-    int32_t* tk = ff.topk + (int64_t)b * k;
-    finish_direct_body<AT_THREADS>(b, n_entries, ff.max_n, ff.scores + (int64_t)lin * ff.scores_stride,
-                                   ff.gscr + (int64_t)lin * ff.gscr_stride, ff.sb, k, ff.src, 1, fl,
-                                   [&](int j, int32_t v) {
-                                     if (writer) tk[j] = v;
-                                     sidx[j] = (v >= 0 && v < nb) ? v : -1;
-                                   });
-    for (int i = k + tid; i < npad; i += AT_THREADS) sidx[i] = -1;
-    __syncthreads();
+    finish_prefetch<AT_THREADS>(pf, b, ff.max_n, ff.sb, ff.src);
   } else {
 #pragma unroll
     for (int c = 0; c < NIV; ++c) {
       const int i = tid + c * AT_THREADS;
       iv[c] = i < k ? ib[i] : -1;
     }
+  }
+
+  // --- queries to fp16 in LDS (the first 16 KiB of the slot area, which the
+  // finish's register path leaves alone). Each head is scaled by a power of
+  // two that puts its largest magnitude in [2^14, 2^15) before rounding; the
+  // logit divides it out again.
+  uint8_t* qlds = smem;
+  auto stage_queries = [&]() {
+    uint32_t qmax = 0;                       // |bf16| bit patterns order like their values
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        qmax = max(qmax, raw[j][t] & 0x7FFFu);
+        qmax = max(qmax, (raw[j][t] >> 16) & 0x7FFFu);
+      }
+    qmax = row_max_u32(qmax);                // 16 lanes, then the other half of the head's 32
+    {
+      const auto rr = __builtin_amdgcn_permlane16_swap(qmax, qmax, false, false);
+      qmax = max((uint32_t)rr[0], (uint32_t)rr[1]);
+    }
+    const float qmaxf = bf16_to_f32(qmax);
+    int sigma = 0;
+    if (qmaxf > 0.0f) {
+      int e;
+      frexpf(qmaxf, &e);         // qmax in [2^(e-1), 2^e)
+      sigma = 15 - e;            // qmax * 2^sigma in [2^14, 2^15)
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      f16x8_t v;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        v[2 * t] = (_Float16)ldexpf(bf16_to_f32(raw[j][t] & 0xFFFFu), sigma);
+        v[2 * t + 1] = (_Float16)ldexpf(bf16_to_f32(raw[j][t] >> 16), sigma);
+      }
+      *(f16x8_t*)(qlds + qh * AT_QPITCH + 32 * qc + 16 * j) = v;
+    }
+    if (qc == 0) sm_lscale[qh] = ldexpf(tau, -sigma);
+  };
+
+  if (FIN) {
+    // the queries while the finish's loads are in flight, then the finish
+    static_assert(AT_MAX_K >= FIN_MAX_WG && AT_LDS >= 8 * (FIN_LDS_CANDS + FIN_SUB_CAP) &&
+                  sizeof(pbuf) >= 4608 && 16 * AT_QPITCH <= 8 * FIN_LDS_CANDS,
+                  "the finish's LDS fits the attention's; the queries lie in its list area only");
+    stage_queries();
+    uint8_t* pb8 = (uint8_t*)&pbuf[0][0];
+    const FinLds fl{(uint64_t*)smem, (uint64_t*)(smem + 8 * FIN_LDS_CANDS), (uint32_t*)sidx,
+                    (uint32_t*)(pb8 + 512), (uint64_t*)pb8, (uint32_t*)(pb8 + 256), (uint32_t*)(pb8 + 384),
+                    (uint64_t*)(pb8 + 2560), (uint32_t*)(pb8 + 416)};
+    // (the positions go to sidx only; the first workgroup of the sequence
+    // copies them to ff.topk at the end: every position is below n_entries)
+    const bool lists_in_lds =
+        finish_direct_body<AT_THREADS>(b, n_entries, ff.max_n, ff.scores + (int64_t)lin * ff.scores_stride,
+                                       ff.gscr + (int64_t)lin * ff.gscr_stride, ff.sb, k, ff.src, 1, fl, pf,
+                                       [&](int j, int32_t v) { sidx[j] = (v >= 0 && v < nb) ? v : -1; });
+    if (lists_in_lds) {                      // the list copy overwrote the queries
+      __syncthreads();
+      stage_queries();
+    }
+    for (int i = k + tid; i < npad; i += AT_THREADS) sidx[i] = -1;
+    __syncthreads();
   }
   // a lane's row for list entry e (skipped entries read row 0 of the sequence);
   // before the list is in LDS (no finish) it is read from idx
@@ -216,45 +265,10 @@ __global__ __launch_bounds__(AT_THREADS) void attention_kernel(
   }
 #pragma unroll
   for (int j = 0; j < AT_NPF; ++j) load_quarter(buf[j], row_at(pe[j]));
-
-  // --- queries to fp16 in LDS (the slot area). Each head is scaled by a power
-  // of two that puts its largest magnitude in [2^14, 2^15) before rounding;
-  // the logit divides it out again.
-  uint8_t* qlds = smem;
-  {
-    uint32_t qmax = 0;                       // |bf16| bit patterns order like their values
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        qmax = max(qmax, raw[j][t] & 0x7FFFu);
-        qmax = max(qmax, (raw[j][t] >> 16) & 0x7FFFu);
-      }
-    qmax = row_max_u32(qmax);                // 16 lanes, then the other half of the head's 32
-    {
-      const auto rr = __builtin_amdgcn_permlane16_swap(qmax, qmax, false, false);
-      qmax = max((uint32_t)rr[0], (uint32_t)rr[1]);
-    }
-    const float qmaxf = bf16_to_f32(qmax);
-    int sigma = 0;
-    if (qmaxf > 0.0f) {
-      int e;
-      frexpf(qmaxf, &e);         // qmax in [2^(e-1), 2^e)
-      sigma = 15 - e;            // qmax * 2^sigma in [2^14, 2^15)
-    }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      f16x8_t v;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        v[2 * t] = (_Float16)ldexpf(bf16_to_f32(raw[j][t] & 0xFFFFu), sigma);
-        v[2 * t + 1] = (_Float16)ldexpf(bf16_to_f32(raw[j][t] >> 16), sigma);
-      }
-      *(f16x8_t*)(qlds + qh * AT_QPITCH + 32 * qc + 16 * j) = v;
-    }
-    if (qc == 0) sm_lscale[qh] = ldexpf(tau, -sigma);
+  if (!FIN) {
+    stage_queries();
+    __syncthreads();
   }
-  __syncthreads();
 
   // B operand of QK (column = head r, K-slice = dims 128kg + 8j .. +7); the
   // slots are overwritten once every wave has read it
@@ -391,6 +405,10 @@ __global__ __launch_bounds__(AT_THREADS) void attention_kernel(
   float* mfin = lsum + AT_WAVES * 16;
   l_w = sum_lane_groups_a(l_w);
   if (lane < 16) { lsum[wave * 16 + lane] = l_w; mfin[wave * 16 + lane] = m_w; }
+  if (FIN && hg == 0) {
+    int32_t* tk = ff.topk + (int64_t)b * k;
+    for (int j = tid; j < k; j += AT_THREADS) tk[j] = sidx[j];
+  }
   __syncthreads();
   if (!head_ok) return;
   float L = 0.0f;

@@ -613,8 +613,10 @@ __global__ __launch_bounds__(FIN_THREADS) void finish_direct_kernel(
   const int b = blockIdx.x;
   int32_t* ob = out + (int64_t)b * out_stride;
   const FinLds L{lc, sub, loff, h, red, scan_tmp, ctl, binl, &bin_count};
+  FinPrefetch<FIN_THREADS> pf;
+  finish_prefetch<FIN_THREADS>(pf, b, max_n, sb, src);
   finish_direct_body<FIN_THREADS>(b, n_entries, max_n, scores + (int64_t)b * sstride,
-                                  sb.gscr + (int64_t)b * sb.gscr_stride, sb, K, src, rescore, L,
+                                  sb.gscr + (int64_t)b * sb.gscr_stride, sb, K, src, rescore, L, pf,
                                   [&](int j, int32_t v) { ob[j] = v; });
 }
 

@@ -513,6 +513,174 @@ __device__ inline void fallback_select(int b, int64_t n_pos, int K, float* sall,
   (void)nvalid;
 }
 
+// The loads a direct finish requests first, before the sequence length and the
+// list lengths are known: the header of chunk `lane` (every wave), the header
+// of chunk tid, and entry `lane` of the FS lists this wave handles first
+// (chunks FS * wave .. FS * wave + FS - 1).
+template <int NT>
+struct FinPrefetch {
+  static constexpr int FS = 4096 / NT;
+  uint64_t hw, h0;
+  uint64_t v0[FS];
+};
+
+template <int NT>
+__device__ inline void finish_prefetch(FinPrefetch<NT>& pf, int b, int64_t max_n, const SelBufs& sb,
+                                       const ScoreSrc& src) {
+  constexpr int FS = FinPrefetch<NT>::FS;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t nw_max = ((src.cand ? max(max_n, (int64_t)src.cand_stride) : max_n) + SC_CHUNK - 1) / SC_CHUNK;
+  const uint64_t* hd = sb.hdr + (int64_t)b * sb.hdr_stride;
+  pf.h0 = tid < nw_max ? hd[tid] : 0ull;
+  pf.hw = lane < nw_max ? hd[lane] : 0ull;
+  const uint64_t* wc = sb.wgc + (int64_t)b * sb.wgc_stride;
+  const int nbk = (int)(sb.wgc_stride / CAND_CAP);   // list slots per sequence (>= 1)
+#pragma unroll
+  for (int s = 0; s < FS; ++s) pf.v0[s] = wc[(int64_t)min(FS * wave + s, nbk - 1) * CAND_CAP + lane];
+  // keeps the compiler from sinking these loads below later waits
+  asm volatile("" ::: "memory");
+}
+
+// Register finish for at most 64 chunks whose lists hold at most 64 entries
+// each (none overflowed): wave v holds entry `lane` of chunks FS v ..
+// FS v + FS - 1 in v0, which is position order. Every wave reads all 64
+// headers itself (no barrier for the highest cutoff cmax); the prefixes at or
+// above cmax go into a 4096-bin histogram and a 64-bin coarse one (64 fine
+// bins each), from which every wave finds the bin T of the K-th best key on
+// its own; when T holds more keys than are needed, its keys are collected
+// (one LDS atomic per wave) and ranked on the full composite. A count per wave
+// then places every selected position in ascending order. Four barriers.
+// Returns 1 when the K positions were emitted, 0 when the lists do not fit
+// this path (no LDS touched), -1 when fewer than K keys reach cmax or T is
+// too large to rank (after a barrier; the caller runs the fallback).
+template <int NT, typename Emit>
+__device__ inline int finish_fast64(int nw, int K, uint64_t hw, const uint64_t (&v0)[4096 / NT], const FinLds& L,
+                                    Emit emit) {
+  constexpr int FS = 4096 / NT, NWAVE = NT / 64;
+  static_assert(FS * NWAVE == 64, "64 lists in registers");
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool in = lane < nw;
+  const uint32_t cnt = in ? (uint32_t)hw & 0x7FFFFFFFu : 0u;
+  if (__ballot(in && (((uint32_t)hw >> 31) != 0u || cnt > 64u)) != 0ull) return 0;
+  const uint32_t cmax = wave_max_u32(in ? (uint32_t)(hw >> 32) : 0u);
+  uint32_t cn[FS];
+#pragma unroll
+  for (int s = 0; s < FS; ++s) cn[s] = (uint32_t)__builtin_amdgcn_readlane((int)cnt, FS * wave + s);
+  uint32_t* const hist = (uint32_t*)L.sub;              // fine bins: prefix - cmax (the last: 4095 or more)
+  uint32_t* const coarse = L.h;                         // coarse bins: fine bin >> 6
+  for (int i = tid; i < NBINS; i += NT) hist[i] = 0;
+  if (tid < 64) coarse[tid] = 0;
+  if (tid == 0) L.ctl[7] = 0;
+  __syncthreads();
+  auto p20_of = [](uint64_t c) { return (uint32_t)(c >> 44); };
+  auto fbin = [&](uint32_t p) { return min(p - cmax, (uint32_t)NBINS - 1u); };   // for p >= cmax
+#pragma unroll
+  for (int s = 0; s < FS; ++s) {
+    const uint32_t p = p20_of(v0[s]);
+    if ((uint32_t)lane < cn[s] && p >= cmax) {
+      const uint32_t f = fbin(p);
+      atomicAdd(&hist[f], 1u);
+      atomicAdd(&coarse[f >> 6], 1u);
+    }
+  }
+  __syncthreads();
+  // the K-th from the top: coarse bins (lane l holds bin 63 - l), then the 64
+  // fine bins of the coarse bin that reaches K
+  const uint32_t cv = coarse[63 - lane];
+  const uint32_t ci = wave_incl_sum(cv);
+  if (readlane_u32(ci, 63) < (uint32_t)K) {
+    __syncthreads();
+    return -1;
+  }
+  const int lc = __ffsll((long long)__ballot(ci >= (uint32_t)K)) - 1;
+  const uint32_t cb = 63u - (uint32_t)lc;
+  const uint32_t above_c = readlane_u32(ci - cv, lc);
+  const uint32_t fv = hist[64u * cb + 63u - (uint32_t)lane];
+  const uint32_t fi = wave_incl_sum(fv);
+  const int lf = __ffsll((long long)__ballot(above_c + fi >= (uint32_t)K)) - 1;
+  const uint32_t T = 64u * cb + 63u - (uint32_t)lf;
+  const uint32_t above = above_c + readlane_u32(fi - fv, lf);
+  const uint32_t in_bin = readlane_u32(fv, lf);
+  const uint32_t need = (uint32_t)K - above;            // 1 .. in_bin
+  const bool split = need < in_bin;
+  auto in_t = [&](uint64_t c) { const uint32_t p = p20_of(c); return p >= cmax && fbin(p) == T; };
+  uint64_t cut = 0;                                     // the in-bin keys c >= cut are selected
+  if (split) {
+    if (in_bin > (uint32_t)FIN_RANK_MAX) {
+      __syncthreads();
+      return -1;
+    }
+    uint64_t m[FS];
+    uint32_t tw = 0;
+#pragma unroll
+    for (int s = 0; s < FS; ++s) {
+      m[s] = __ballot((uint32_t)lane < cn[s] && in_t(v0[s]));
+      tw += (uint32_t)__popcll(m[s]);
+    }
+    uint32_t base = 0;
+    if (tw) {
+      if (lane == 0) base = atomicAdd(&L.ctl[7], tw);
+      base = readlane_u32(base, 0);
+    }
+    const uint64_t below = (1ull << lane) - 1ull;
+#pragma unroll
+    for (int s = 0; s < FS; ++s) {
+      if ((m[s] >> lane) & 1ull) L.binl[base + (uint32_t)__popcll(m[s] & below)] = v0[s];
+      base += (uint32_t)__popcll(m[s]);
+    }
+    __syncthreads();
+    // every wave: the key with exactly need - 1 larger ones (keys are distinct);
+    // up to 64 keys one per lane, compared through lane reads
+    bool found = false;
+    uint64_t best = 0;
+    if (in_bin <= 64u) {
+      const uint64_t v = (uint32_t)lane < in_bin ? L.binl[lane] : 0ull;
+      const uint32_t vh = (uint32_t)(v >> 32), vl = (uint32_t)v;
+      uint32_t larger = 0;
+      for (uint32_t i = 0; i < in_bin; ++i) {
+        const uint64_t o = ((uint64_t)readlane_u32(vh, (int)i) << 32) | readlane_u32(vl, (int)i);
+        larger += o > v ? 1u : 0u;
+      }
+      if ((uint32_t)lane < in_bin && larger == need - 1) { found = true; best = v; }
+    } else {
+      for (uint32_t j = lane; j < in_bin; j += 64) {
+        const uint64_t v = L.binl[j];
+        uint32_t larger = 0;
+        for (uint32_t i = 0; i < in_bin; ++i) larger += L.binl[i] > v ? 1u : 0u;
+        if (larger == need - 1) { found = true; best = v; }
+      }
+    }
+    const int src = __ffsll((long long)__ballot(found)) - 1;
+    cut = ((uint64_t)readlane_u32((uint32_t)(best >> 32), src) << 32) | readlane_u32((uint32_t)best, src);
+  }
+  auto sel = [&](uint64_t c) {
+    const uint32_t p = p20_of(c);
+    if (p < cmax) return false;
+    const uint32_t f = fbin(p);
+    return f > T || (f == T && (!split || c >= cut));
+  };
+  uint64_t ms[FS];
+  uint32_t cw = 0;
+#pragma unroll
+  for (int s = 0; s < FS; ++s) {
+    ms[s] = __ballot((uint32_t)lane < cn[s] && sel(v0[s]));
+    cw += (uint32_t)__popcll(ms[s]);
+  }
+  if (lane == 0) L.scan_tmp[wave] = cw;
+  __syncthreads();
+  const uint32_t wcnt = lane < NWAVE ? L.scan_tmp[lane] : 0u;
+  uint32_t base = readlane_u32(wave_incl_sum(wcnt) - wcnt, wave);   // selected in the earlier waves' chunks
+  const uint64_t below = (1ull << lane) - 1ull;
+#pragma unroll
+  for (int s = 0; s < FS; ++s) {
+    if ((ms[s] >> lane) & 1ull)
+      emit((int)(base + (uint32_t)__popcll(ms[s] & below)), (int32_t)(0xFFFFFFFFu - (uint32_t)v0[s]));
+    base += (uint32_t)__popcll(ms[s]);
+  }
+  return 1;
+}
+
 // Direct top-K (K <= kDirectMaxK). The candidate lists hold, per workgroup,
 // every key whose top 20 bits reach its refined cutoff, in position order, so
 // their concatenation in workgroup order is in position order too; the ones
@@ -530,11 +698,13 @@ __device__ inline void fallback_select(int b, int64_t n_pos, int K, float* sall,
 // through emit(j, position) for every j in [0, K) exactly once (-1 past the
 // selected ones). sall: a row of at least max_n floats for the fallback's
 // scores (recomputed into it when `rescore` is set); gscr: this workgroup's
-// scratch for a threshold bin beyond FIN_SUB_CAP keys.
+// scratch for a threshold bin beyond FIN_SUB_CAP keys. pf: the loads of
+// finish_prefetch. Returns true when L.lc was written (the lists copied to LDS).
 template <int NT, typename Emit>
-__device__ inline void finish_direct_body(int b, const int32_t* __restrict__ n_entries, int64_t max_n,
+__device__ inline bool finish_direct_body(int b, const int32_t* __restrict__ n_entries, int64_t max_n,
                                    float* __restrict__ sall, uint64_t* __restrict__ gscr, const SelBufs& sb,
-                                   int K, const ScoreSrc& src, int rescore, const FinLds& L, Emit emit) {
+                                   int K, const ScoreSrc& src, int rescore, const FinLds& L,
+                                   const FinPrefetch<NT>& pf, Emit emit) {
   uint64_t* const lc = L.lc;
   uint64_t* const sub = L.sub;
   uint32_t* const loff = L.loff;
@@ -551,36 +721,36 @@ __device__ inline void finish_direct_body(int b, const int32_t* __restrict__ n_e
   static_assert(NBINS % NT == 0 && NT % 64 == 0, "whole waves, whole bins per thread");
   static_assert(NT >= 256 && FIN_SUB_CAP * 8 >= QMX_LDS_BYTES, "the quantized query is staged by 256 threads in sub");
   if (tid == 0) bin_count = 0;                     // first read after several barriers
-  // The first header words, and the first 64 entries of the FS lists this
-  // wave handles first (chunks FS * wave .. FS * wave + FS - 1), are requested
-  // before the sequence length and the list lengths are known.
-  const int64_t nw_max = ((src.cand ? max(max_n, (int64_t)src.cand_stride) : max_n) + SC_CHUNK - 1) / SC_CHUNK;
+  // (the first header words and list entries were requested by finish_prefetch)
   const uint64_t* hd = sb.hdr + (int64_t)b * sb.hdr_stride;
-  const uint64_t h0 = tid < nw_max ? hd[tid] : 0ull;
+  const uint64_t h0 = pf.h0;
   const uint64_t* wc = sb.wgc + (int64_t)b * sb.wgc_stride;
-  const int nbk = (int)(sb.wgc_stride / CAND_CAP);   // list slots per sequence (>= 1)
-  constexpr int FS = 4096 / NT;                     // lists a wave takes per round
+  constexpr int FS = FinPrefetch<NT>::FS;           // lists a wave takes per round
   constexpr int RL = FS * NWAVE;                    // lists of one round (64)
-  uint64_t v0[FS];
-#pragma unroll
-  for (int s = 0; s < FS; ++s) v0[s] = wc[(int64_t)min(FS * wave + s, nbk - 1) * CAND_CAP + lane];
-  // keeps the compiler from sinking these loads below the early return (their
-  // latency then overlaps the sequence-length load)
-  asm volatile("" ::: "memory");
+  const uint64_t (&v0)[FS] = pf.v0;
   const int64_t n_pos = min((int64_t)n_entries[b], max_n);
   // a candidate list (Reindex): its slots, their stored scores (key 0: unused)
   const bool lst = src.cand != nullptr;
   if (!lst && n_pos <= K) {               // every position is selected (or none exists)
     for (int j = tid; j < K; j += NT) emit(j, j < n_pos ? j : -1);
-    return;
+    return false;
   }
   if (lst && n_pos <= 0) {                // no listed position can be used
     for (int j = tid; j < K; j += NT) emit(j, -1);
-    return;
+    return false;
   }
-  for (int i = tid; i < NBINS; i += NT) hist[i] = 0;
   const int64_t n_slots = lst ? (int64_t)src.cand_stride : n_pos;
   const int64_t nw = (n_slots + SC_CHUNK - 1) / SC_CHUNK;
+  if (!lst && nw <= RL) {
+    const int r = finish_fast64<NT>((int)nw, K, pf.hw, v0, L, emit);
+    if (r > 0) return false;
+    if (r < 0) {
+      fallback_select<NT>(b, n_pos, K, sall, gscr, src, rescore, L, emit);
+      return false;
+    }
+  }
+  for (int i = tid; i < NBINS; i += NT) hist[i] = 0;
+  bool lc_used = false;                  // the LDS list copy overwrote L.lc
   uint32_t cmax = 0;
   auto p20_of = [](uint64_t c) { return (uint32_t)(c >> 44); };
   auto count_above_cmax = [&](uint64_t c) {
@@ -700,7 +870,7 @@ __device__ inline void finish_direct_body(int b, const int32_t* __restrict__ n_e
       hist_kth_bin<NT>(hist, (uint32_t)K, scan_tmp, ctl, &tot);
       if (ctl[0] != 0xFFFFFFFFu) {                   // at least K keys reach the highest cutoff
         finish_regs(v0, [&](int q) { return (uint32_t)lane < cn[q]; });
-        return;
+        return false;
       }
     } else if ((flags & 1u) == 0) {
       // lists -> LDS at offsets from a scan of their lengths
@@ -713,6 +883,7 @@ __device__ inline void finish_direct_body(int b, const int32_t* __restrict__ n_e
       }
       __syncthreads();
       if (total <= (uint32_t)FIN_LDS_CANDS) {
+        lc_used = true;
         // copy the lists in chunk order (wave v takes the FS chunks from
         // FS v in each round of RL) and histogram the prefixes
         auto take = [&](uint64_t c, uint32_t at) {
@@ -768,13 +939,14 @@ __device__ inline void finish_direct_body(int b, const int32_t* __restrict__ n_e
                 scan_tmp);
             for (uint32_t j = nsel + tid; j < (uint32_t)K; j += NT) emit((int)j, -1);
           }
-          return;
+          return true;
         }
       }
     }
   }
   // Fallback: the same steps over every score of the sequence
   fallback_select<NT>(b, n_pos, K, sall, gscr, src, rescore, L, emit);
+  return lc_used;
 }
 
 // Pool finish (the K best positions, ascending) from the pool lists of a
