@@ -125,7 +125,7 @@ __device__ void compact_bitmap(const uint32_t* bm, int64_t nbits, const int32_t*
 // eight workgroups of four waves share a compute unit, each wave with
 // SC_UNROLL tiles in flight.
 template <bool CAND, int SEL, int MODE, bool QMX>
-__global__ __launch_bounds__(SC_THREADS) __attribute__((amdgpu_waves_per_eu(CAND ? 6 : 8))) void score_kernel(
+__global__ __launch_bounds__(SC_THREADS) __attribute__((amdgpu_waves_per_eu(CAND ? 4 : 8))) void score_kernel(
     const uint8_t* __restrict__ ik, const uint8_t* __restrict__ iks,
     const int64_t* __restrict__ entry_offset, const int32_t* __restrict__ n_entries, int64_t max_n,
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w, int Hi,
@@ -140,6 +140,7 @@ __global__ __launch_bounds__(SC_THREADS) __attribute__((amdgpu_waves_per_eu(CAND
   __shared__ SelBufs sbs;   // the workspace views, parked in LDS while the keys stream (frees SGPRs)
   __shared__ __attribute__((aligned(16))) uint8_t lq[QMX ? QMX_LDS_BYTES : 16];   // the quantized query
   __shared__ uint32_t used_bm[CAND ? SC_SPAN / 32 : 1];     // candidate list: slots used
+  __shared__ int32_t lpos[CAND ? SC_SPAN : 1];               // candidate list: the row of each slot
   uint32_t* lhist = lbuf;
   float* lsc = (float*)(lbuf + NBINS / 2);
   auto hcount = [&](uint32_t bin) -> uint32_t { return (lhist[bin >> 1] >> ((bin & 1) * 16)) & 0xFFFFu; };
@@ -249,6 +250,9 @@ __global__ __launch_bounds__(SC_THREADS) __attribute__((amdgpu_waves_per_eu(CAND
       m4 |= (pp[q] > run ? 1u : 0u) << q;
       run = max(run, pp[q]);
     }
+    // the row each slot reads (row 0 of the sequence for an unused slot)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) lpos[4 * tid + q] = ((m4 >> q) & 1u) ? (int32_t)pp[q] - 1 : 0;
     // 8 threads per word: gather their 4-bit masks
     uint32_t wd = m4 << (4 * (tid & 7));
     wd |= (uint32_t)__shfl_xor((int)wd, 1, 64);
@@ -499,30 +503,27 @@ __global__ __launch_bounds__(SC_THREADS) __attribute__((amdgpu_waves_per_eu(CAND
     const float unused = LISTS ? __uint_as_float(0xFFFFFFFFu) : 0.0f;
     for (int i = tid; i < end; i += SC_THREADS) lsc[i] = unused;
   } else {
-    // listed positions: SC_UNROLL tiles are loaded before any is used (unused
-    // slots read row 0 of the sequence, and hold the key 0)
+    // listed positions: every tile of the wave is requested at once (the
+    // rows come from lpos, written by the scan above), so the gathers cost
+    // one memory round trip; unused slots read row 0 of the sequence and hold
+    // the key 0
     const float unused = __uint_as_float(0xFFFFFFFFu);     // key 0
-    for (int t0 = 16 * wave; t0 < end; t0 += 64 * SC_UNROLL) {
-      int pos[SC_UNROLL];
-      bool ok[SC_UNROLL];
+    constexpr int CT = SC_SPAN / (16 * (SC_THREADS / 64)); // tiles per wave
+    u32x4_t cwl[CT];
+    uint32_t sbl[CT];
 #pragma unroll
-      for (int u = 0; u < SC_UNROLL; ++u) {
-        const int i = t0 + 64 * u + n;
-        const bool inb = i < end;
-        ok[u] = inb && ((used_bm[i >> 5] >> (i & 31)) & 1u);
-        pos[u] = ok[u] ? crow[start + i] : 0;
-      }
+    for (int u = 0; u < CT; ++u) {
+      const int i = 16 * wave + 64 * u + n;                 // < SC_SPAN
+      const uint32_t p = (uint32_t)lpos[i];
+      cwl[u] = __builtin_nontemporal_load((const u32x4_t*)(ikb + (p * 64u + 16u * g)));
+      sbl[u] = iksb[p * 4u + (uint32_t)g];
+    }
 #pragma unroll
-      for (int u = 0; u < SC_UNROLL; ++u) {
-        codes[u] = __builtin_nontemporal_load((const u32x4_t*)(ikb + ((uint32_t)pos[u] * 64u + 16u * g)));
-        sbyte[u] = iksb[(uint32_t)pos[u] * 4u + (uint32_t)g];
-      }
-#pragma unroll
-      for (int u = 0; u < SC_UNROLL; ++u) {
-        const float sc = score_tile(codes[u], sbyte[u]);
-        const int ls = t0 + 64 * u + n;
-        if (g == 0 && ls < end) lsc[ls] = ok[u] ? sc : (LISTS ? unused : 0.0f);
-      }
+    for (int u = 0; u < CT; ++u) {
+      const float sc = score_tile(cwl[u], sbl[u]);
+      const int ls = 16 * wave + 64 * u + n;
+      const bool ok = ls < end && ((used_bm[ls >> 5] >> (ls & 31)) & 1u);
+      if (g == 0 && ls < end) lsc[ls] = ok ? sc : (LISTS ? unused : 0.0f);
     }
   }
   chunk_tail(0);
