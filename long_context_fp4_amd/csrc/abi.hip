@@ -423,7 +423,8 @@ namespace {
 int run_decode_layer(int mode, const uint8_t* kv, const uint8_t* ik, const uint8_t* iks, const int64_t* entry_offset,
                      const int32_t* n_entries, int B, int64_t max_n, const uint16_t* q_idx, const float* w, int Hi,
                      int score_mode, const uint16_t* q, int H, float softmax_scale, int k, int pool_k, int32_t* pool,
-                     int32_t* topk, float* out, float* lse, uint8_t* ws, hipStream_t s, bool allow_fused = true) {
+                     int32_t* topk, float* out, float* lse, uint8_t* ws, hipStream_t s, bool allow_fused = true,
+                     int pre_B = 0, int pre_Tq = 0) {
   const FusedPlan fp = fused_plan(mode, B, max_n, H, k, pool_k);
   const int cand_stride = mode == CSA2_REINDEX ? pool_k : 0;
   if (fp.on && allow_fused) {
@@ -438,7 +439,12 @@ int run_decode_layer(int mode, const uint8_t* kv, const uint8_t* ik, const uint8
     ff.pool_k = 0;
     ff.pool = nullptr;
     hipError_t e;
-    if (mode == CSA2_FULL) {
+    if (mode == CSA2_FULL && pre_Tq > 0 && pool_k == 0 && (score_mode & CSA2_SCORE_QMX8) == 0) {
+      // a prefill's virtual batch: the multi-query pass reads each key tile
+      // once for several of a sequence's queries
+      e = csa2::launch_score_prefill(ik, iks, entry_offset, n_entries, pre_B, pre_Tq, max_n, q_idx, w, Hi,
+                                     score_mode, sb, k, s);
+    } else if (mode == CSA2_FULL) {
       e = score_full(ik, iks, entry_offset, n_entries, B, max_n, q_idx, w, Hi, score_mode, scores, L.slots, sb,
                      pool_k > 0 ? csa2::SEL_POOL : csa2::SEL_DIRECT, k, false, pool_k, s);
       ff.pool_k = pool_k;
@@ -540,11 +546,16 @@ int csa2_decode_layer_noalloc(int mode, const uint8_t* kv, const uint8_t* ik, co
                           softmax_scale, k, pool_k, pool, topk, out, lse, ws, (hipStream_t)stream, fused);
 }
 
-int csa2_decode_layer(int mode, const uint8_t* kv, const uint8_t* ik, const uint8_t* iks,
-                      const int64_t* entry_offset, const int32_t* n_entries, int B, int64_t max_n,
-                      const uint16_t* q_idx, const float* w, int Hi, int score_mode, const uint16_t* q, int H,
-                      float softmax_scale, int k, int pool_k, int32_t* pool, int32_t* topk, float* out,
-                      float* lse, void* workspace, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+// csa2_decode_layer, and (pre_Tq > 0) the virtual decode batch of a prefill:
+// B = pre_B * pre_Tq queries of pre_B sequences.
+int decode_layer_ws(int mode, const uint8_t* kv, const uint8_t* ik, const uint8_t* iks, const int64_t* entry_offset,
+                    const int32_t* n_entries, int B, int64_t max_n, const uint16_t* q_idx, const float* w, int Hi,
+                    int score_mode, const uint16_t* q, int H, float softmax_scale, int k, int pool_k, int32_t* pool,
+                    int32_t* topk, float* out, float* lse, void* workspace, size_t ws_bytes, void* stream, int pre_B,
+                    int pre_Tq) {
   int rc = check_decode_args(mode, kv, ik, iks, entry_offset, n_entries, B, max_n, q_idx, w, Hi, score_mode, q, H, k,
                              pool_k, pool, topk, out, lse);
   if (rc) return rc;
@@ -553,7 +564,20 @@ int csa2_decode_layer(int mode, const uint8_t* kv, const uint8_t* ik, const uint
     return fail(CSA2_ERR_WORKSPACE, "decode_layer: workspace needs %zu bytes (got %zu)", need, workspace ? ws_bytes : 0);
   if (!aligned16(workspace)) return fail(CSA2_ERR_ALIGN, "decode_layer: workspace must be 16-byte aligned");
   return run_decode_layer(mode, kv, ik, iks, entry_offset, n_entries, B, max_n, q_idx, w, Hi, score_mode, q, H,
-                          softmax_scale, k, pool_k, pool, topk, out, lse, (uint8_t*)workspace, (hipStream_t)stream);
+                          softmax_scale, k, pool_k, pool, topk, out, lse, (uint8_t*)workspace, (hipStream_t)stream,
+                          true, pre_B, pre_Tq);
+}
+}  // namespace
+
+extern "C" {
+
+int csa2_decode_layer(int mode, const uint8_t* kv, const uint8_t* ik, const uint8_t* iks,
+                      const int64_t* entry_offset, const int32_t* n_entries, int B, int64_t max_n,
+                      const uint16_t* q_idx, const float* w, int Hi, int score_mode, const uint16_t* q, int H,
+                      float softmax_scale, int k, int pool_k, int32_t* pool, int32_t* topk, float* out,
+                      float* lse, void* workspace, size_t ws_bytes, void* stream) {
+  return decode_layer_ws(mode, kv, ik, iks, entry_offset, n_entries, B, max_n, q_idx, w, Hi, score_mode, q, H,
+                         softmax_scale, k, pool_k, pool, topk, out, lse, workspace, ws_bytes, stream, 0, 0);
 }
 
 size_t csa2_prefill_workspace_bytes(int B, int Tq, int64_t max_n, int H, int k) {
@@ -589,8 +613,8 @@ int csa2_prefill_layer(const uint8_t* kv, const uint8_t* ik, const uint8_t* iks,
   int32_t* ne = (int32_t*)(views + round_up((size_t)Bv * 8, 256));
   hipError_t e = csa2::launch_prefill_views(entry_offset, n_entries, pos, m, B, Tq, eo, ne, (hipStream_t)stream);
   if (e != hipSuccess) return hip_status(e, "prefill_layer views");
-  return csa2_decode_layer(CSA2_FULL, kv, ik, iks, eo, ne, Bv, max_n, q_idx, w, Hi, score_mode, q, H, softmax_scale,
-                           k, 0, nullptr, topk, out, lse, workspace, dneed, stream);
+  return decode_layer_ws(CSA2_FULL, kv, ik, iks, eo, ne, Bv, max_n, q_idx, w, Hi, score_mode, q, H, softmax_scale, k,
+                         0, nullptr, topk, out, lse, workspace, dneed, stream, B, Tq);
 }
 
 double csa2_bytes_per_token(const int* ratios, int n_layers, int lat_ch, int lat_blk, int lat_sbytes, int idx_ch,

@@ -121,22 +121,31 @@ __device__ void compact_bitmap(const uint32_t* bm, int64_t nbits, const int32_t*
 // MODE: 0 = dot product of head 0, 1 = sum_h w_h * ReLU(q_h . k).
 // QMX: the query is quantized to MXFP8 in registers and each tile is one
 //      block-scaled FP8 x FP4 MFMA (the quantized-query variant).
+// MQ: queries per workgroup (the multi-query pass of a prefill; Full pass,
+//      direct top-k, exact scores only). Sequence index y of the grid is then
+//      (sequence bs, query group): queries t0 .. t0+MQ-1 of the Tq queries of
+//      sequence bs, which are the virtual sequences bs*Tq + t of the
+//      per-query arrays (entry_offset, n_entries = the query's visible
+//      entries, q_idx, w, and the selection's headers and lists). Each key
+//      tile is read and dequantized once and contracted with every query.
 // A workgroup streams SC_SPAN slots (SC_SUB selection chunks of SC_CHUNK);
 // eight workgroups of four waves share a compute unit, each wave with
 // SC_UNROLL tiles in flight.
-template <bool CAND, int SEL, int MODE, bool QMX>
-__global__ __launch_bounds__(SC_THREADS) __attribute__((amdgpu_waves_per_eu(CAND ? 4 : 8))) void score_kernel(
+template <bool CAND, int SEL, int MODE, bool QMX, int MQ = 1>
+__global__ __launch_bounds__(SC_THREADS) __attribute__((amdgpu_waves_per_eu(CAND ? 4 : (MQ > 1 ? 2 : 8)))) void score_kernel(
     const uint8_t* __restrict__ ik, const uint8_t* __restrict__ iks,
     const int64_t* __restrict__ entry_offset, const int32_t* __restrict__ n_entries, int64_t max_n,
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w, int Hi,
     const int32_t* __restrict__ cand, int cand_stride,
-    float* __restrict__ scores, int64_t sstride, SelBufs sb, int K, int store_scores, int pool_k) {
+    float* __restrict__ scores, int64_t sstride, SelBufs sb, int K, int store_scores, int pool_k, int Tq) {
+  static_assert(MQ == 1 || (!CAND && SEL == SEL_DIRECT && !QMX), "the multi-query pass is a direct Full pass");
+  static_assert(MQ <= SC_THREADS / 64, "one wave per query in the multi-query tail");
   // histogram with 16-bit counts (two bins per word) + staged scores: 12 KiB,
   // so that eight workgroups fit one compute unit
-  __shared__ uint32_t lbuf[NBINS / 2 + SC_SPAN];
+  __shared__ __attribute__((aligned(16))) uint32_t lbuf[NBINS / 2 + MQ * SC_SPAN];
   __shared__ uint32_t scan_tmp[SC_THREADS / 64 + 1];
   __shared__ uint32_t ctl[8];
-  __shared__ __attribute__((aligned(16))) float lw[16];   // head weights
+  __shared__ __attribute__((aligned(16))) float lw[16 * MQ];   // head weights (per query)
   __shared__ SelBufs sbs;   // the workspace views, parked in LDS while the keys stream (frees SGPRs)
   __shared__ __attribute__((aligned(16))) uint8_t lq[QMX ? QMX_LDS_BYTES : 16];   // the quantized query
   __shared__ uint32_t used_bm[CAND ? SC_SPAN / 32 : 1];     // candidate list: slots used
@@ -146,30 +155,58 @@ __global__ __launch_bounds__(SC_THREADS) __attribute__((amdgpu_waves_per_eu(CAND
   auto hcount = [&](uint32_t bin) -> uint32_t { return (lhist[bin >> 1] >> ((bin & 1) * 16)) & 0xFFFFu; };
   constexpr bool LISTS = SEL == SEL_DIRECT || SEL == SEL_POOL;
 
-  const int b = blockIdx.y;
+  // the sequence (or, MQ > 1, query) index of each query's selection
+  int vq[MQ];
+  bool qok[MQ];
+  if constexpr (MQ == 1) {
+    vq[0] = blockIdx.y;
+    qok[0] = true;
+  } else {
+    const int QG = (Tq + MQ - 1) / MQ;
+    const int bs = blockIdx.y / QG, t0 = (blockIdx.y % QG) * MQ;
+#pragma unroll
+    for (int m = 0; m < MQ; ++m) {
+      qok[m] = t0 + m < Tq;
+      vq[m] = bs * Tq + min(t0 + m, Tq - 1);
+    }
+  }
+  const int b = vq[0];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, g = lane >> 4;
   // independent loads first (the sequence's length and first row, the queries,
   // the head weights), so the keys are requested one round trip after the start
-  const int32_t ne = n_entries[b];
+  int32_t neq[MQ];
+#pragma unroll
+  for (int m = 0; m < MQ; ++m) neq[m] = n_entries[vq[m]];
+  const int32_t ne = neq[0];
   const int64_t row_base = entry_offset[b];
   asm volatile("" ::"s"(ne), "s"(row_base));   // both loads issued here, before any branch on them
   // A operand: q[head = n][channels 32g + 8j .. +7] for MFMA j (the quantized
   // variant builds its operand once the first keys are requested)
-  bf16x8_t qa[4];
+  bf16x8_t qa[MQ][4];
   QueryMx qm;
   if constexpr (!QMX) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      u32x4_t v = {0, 0, 0, 0};
-      if (n < Hi) v = *(const u32x4_t*)(q_idx + ((int64_t)b * Hi + n) * 128 + 32 * g + 8 * j);
-      __builtin_memcpy(&qa[j], &v, 16);
-    }
+    for (int m = 0; m < MQ; ++m)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        u32x4_t v = {0, 0, 0, 0};
+        if (n < Hi) v = *(const u32x4_t*)(q_idx + ((int64_t)vq[m] * Hi + n) * 128 + 32 * g + 8 * j);
+        __builtin_memcpy(&qa[m][j], &v, 16);
+      }
   }
   // head weights of the output rows (lane group g takes heads 4g .. 4g+3), in
   // LDS and read per tile, which keeps the wave within 64 registers
-  const float wv = tid < Hi ? (w ? w[(int64_t)b * Hi + tid] : 1.0f) : 0.0f;
-  const int64_t n_pos = min((int64_t)ne, max_n);
+  const int wq = tid >> 4, wh = tid & 15;
+  const float wv = (tid < 16 * MQ && wh < Hi) ? (w ? w[(int64_t)vq[wq < MQ ? wq : 0] * Hi + wh] : 1.0f) : 0.0f;
+  // positions each query's selection covers (MQ > 1: its visible entries)
+  int64_t npq[MQ];
+  int64_t n_pos = 0;
+#pragma unroll
+  for (int m = 0; m < MQ; ++m) {
+    npq[m] = qok[m] ? min((int64_t)neq[m], max_n) : 0;
+    n_pos = max(n_pos, npq[m]);
+  }
   const int64_t nslots = CAND ? (int64_t)cand_stride : n_pos;
   const int64_t start = (int64_t)blockIdx.x * SC_SPAN;
   if (start >= nslots) return;
@@ -202,7 +239,7 @@ __global__ __launch_bounds__(SC_THREADS) __attribute__((amdgpu_waves_per_eu(CAND
     uint32_t* bm = sb.bitmap + (int64_t)b * sb.bm_stride;
     for (int64_t wd = start / 32 + tid; wd < (start + end + 31) / 32; wd += SC_THREADS) bm[wd] = 0;
   }
-  if (tid < 16) lw[tid] = wv;
+  if (tid < 16 * MQ) lw[tid] = wv;
   if (SEL != SEL_NONE && tid == 0) sbs = sb;
   if constexpr (CAND) {
     // which of this workgroup's slots the rule uses: the largest in-range
@@ -267,7 +304,7 @@ __global__ __launch_bounds__(SC_THREADS) __attribute__((amdgpu_waves_per_eu(CAND
   // goes to the lanes of group 0, which stage the score in LDS
   auto score_tile = [&](const u32x4_t cw, uint32_t sbyte) -> float {
     if constexpr (QMX) return score_tile_mx<MODE>(qm, cw, sbyte, lw, g);
-    else return score_tile_fn<MODE>(qa, cw, sbyte, lw, g);
+    else return score_tile_fn<MODE>(qa[0], cw, sbyte, lw, g);
   };
   // The local cutoff of a chunk: a 20-bit key prefix with at least `budget`
   // of the chunk's valid keys at or above it (0 when it has fewer). The keys
@@ -311,16 +348,19 @@ __global__ __launch_bounds__(SC_THREADS) __attribute__((amdgpu_waves_per_eu(CAND
   // local cutoff (every slot of a Full pass is a valid position). Chunk cix
   // reports into its own slot of the workspace (a header word and a list), so
   // no global atomics are needed.
-  auto chunk_tail = [&](int sub) {
+  auto chunk_tail = [&](int sub, int mq) {
+  const int bq = vq[mq];                             // the selection's sequence (or query) index
+  const int64_t npos_q = npq[mq];
+  const int end_q = MQ == 1 ? end : (int)max((int64_t)0, min((int64_t)SC_SPAN, npos_q - start));
   const int soff = sub * SC_CHUNK;
-  const int send = min(SC_CHUNK, end - soff);        // slots of this chunk
+  const int send = min(SC_CHUNK, end_q - soff);      // slots of this chunk
   if (send <= 0) return;
   __syncthreads();                                   // its scores are staged; the previous tail is done
-  const float* lss = lsc + soff;
+  const float* lss = lsc + mq * SC_SPAN + soff;
   const int64_t cix = (int64_t)blockIdx.x * SC_SUB + sub;
   // coalesced store of the chunk's scores (slots of unused candidates hold the key 0)
   if (store_scores) {
-    float* srow = scores + (int64_t)b * sstride + start + soff;
+    float* srow = scores + (int64_t)bq * sstride + start + soff;
     for (int i4 = 4 * tid; i4 < send; i4 += 4 * SC_THREADS) {
       if (i4 + 3 < send && (((uintptr_t)(srow + i4)) & 15) == 0) {
         *(float4*)(srow + i4) = *(const float4*)(lss + i4);
@@ -331,7 +371,7 @@ __global__ __launch_bounds__(SC_THREADS) __attribute__((amdgpu_waves_per_eu(CAND
   }
   if (SEL == SEL_NONE) return;
   const SelBufs sbl = sbs;
-  const int64_t nref = CAND ? nslots : n_pos;        // slots the shares refer to
+  const int64_t nref = CAND ? nslots : npos_q;       // slots the shares refer to
   const int64_t nwg = (nref + SC_CHUNK - 1) / SC_CHUNK;
   // local budget: a multiple of the chunk's expected share of the top-K plus a
   // margin, so that the highest cutoff over the workgroups still leaves at
@@ -340,7 +380,7 @@ __global__ __launch_bounds__(SC_THREADS) __attribute__((amdgpu_waves_per_eu(CAND
   int64_t budget64 = LISTS ? 2 * share + 16 : 4 * share + 32;
   if (LISTS) budget64 = min(budget64, max((int64_t)8, (int64_t)FIN_LDS_CANDS / nwg));
   const uint32_t budget = (uint32_t)min(budget64, (int64_t)send);
-  uint64_t* hdr = sbl.hdr + (int64_t)b * sbl.hdr_stride + cix;
+  uint64_t* hdr = sbl.hdr + (int64_t)bq * sbl.hdr_stride + cix;
   if (SEL == SEL_THRESHOLD) {
     if (sub > 0) {
       for (int i = tid; i < NBINS / 2; i += SC_THREADS) lhist[i] = 0;
@@ -364,7 +404,7 @@ __global__ __launch_bounds__(SC_THREADS) __attribute__((amdgpu_waves_per_eu(CAND
     }
     uint32_t tot;
     uint32_t off = block_exclusive_scan(np, scan_tmp, &tot);
-    uint32_t* pl = sbl.summ + (int64_t)b * sbl.summ_stride + cix * SUM_PAIRS;
+    uint32_t* pl = sbl.summ + (int64_t)bq * sbl.summ_stride + cix * SUM_PAIRS;
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
       const uint32_t bin = NBINS - 1 - (16 * tid + q);
@@ -446,7 +486,7 @@ __global__ __launch_bounds__(SC_THREADS) __attribute__((amdgpu_waves_per_eu(CAND
     for (int q = 0; q < 4; ++q) m |= ((((vmask >> q) & 1u) && (keys[q] >> 12) >= fine) ? 1u : 0u) << q;
     uint32_t tot;
     uint32_t off = block_exclusive_scan((uint32_t)__popc(m), scan_tmp, &tot);
-    uint64_t* wc = sbl.wgc + (int64_t)b * sbl.wgc_stride + cix * CAND_CAP;
+    uint64_t* wc = sbl.wgc + (int64_t)bq * sbl.wgc_stride + cix * CAND_CAP;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       if ((m >> q) & 1u) {
@@ -463,7 +503,7 @@ __global__ __launch_bounds__(SC_THREADS) __attribute__((amdgpu_waves_per_eu(CAND
       for (int q = 0; q < 4; ++q) mp |= ((((vmask >> q) & 1u) && (keys[q] >> 12) >= fine_p) ? 1u : 0u) << q;
       uint32_t totp;
       uint32_t offp = block_exclusive_scan((uint32_t)__popc(mp), scan_tmp, &totp);
-      uint64_t* wcp = sbl.wgcp + (int64_t)b * sbl.wgcp_stride + cix * kPoolCap;
+      uint64_t* wcp = sbl.wgcp + (int64_t)bq * sbl.wgcp_stride + cix * kPoolCap;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         if ((mp >> q) & 1u) {
@@ -472,7 +512,7 @@ __global__ __launch_bounds__(SC_THREADS) __attribute__((amdgpu_waves_per_eu(CAND
         }
       }
       if (tid == 0)
-        sbl.hdrp[(int64_t)b * sbl.hdr_stride + cix] = ((uint64_t)M << 32) | ((uint64_t)fine_p << 11) | totp;
+        sbl.hdrp[(int64_t)bq * sbl.hdr_stride + cix] = ((uint64_t)M << 32) | ((uint64_t)fine_p << 11) | totp;
     }
   }
   };
@@ -490,9 +530,17 @@ __global__ __launch_bounds__(SC_THREADS) __attribute__((amdgpu_waves_per_eu(CAND
       const int t0 = 16 * wave + it * 64 * SC_UNROLL;
 #pragma unroll
       for (int u = 0; u < SC_UNROLL; ++u) {
-        const float sc = score_tile(codes[u], sbyte[u]);
         const int ls = t0 + 64 * u + n;
-        if (g == 0 && ls < end) lsc[ls] = sc;
+        if constexpr (MQ == 1) {
+          const float sc = score_tile(codes[u], sbyte[u]);
+          if (g == 0 && ls < end) lsc[ls] = sc;
+        } else {
+          float sc[MQ];
+          score_tile_multi<MODE, MQ>(qa, codes[u], sbyte[u], lw, g, sc);
+#pragma unroll
+          for (int m = 0; m < MQ; ++m)
+            if (g == 0 && ls < end) lsc[m * SC_SPAN + ls] = sc[m];
+        }
         const uint32_t p = (uint32_t)(start + min(ls + 64 * SC_UNROLL, end - 1));
         codes[u] = __builtin_nontemporal_load((const u32x4_t*)(ikb + (p * 64u + 16u * g)));
         sbyte[u] = iksb[p * 4u + (uint32_t)g];
@@ -526,7 +574,29 @@ __global__ __launch_bounds__(SC_THREADS) __attribute__((amdgpu_waves_per_eu(CAND
       if (g == 0 && ls < end) lsc[ls] = ok ? sc : (LISTS ? unused : 0.0f);
     }
   }
-  chunk_tail(0);
+  // (the multi-query pass: one wave per query computes that query's local
+  // cutoff and list, so the queries' tails run side by side; a single query's
+  // tail is faster on the whole workgroup)
+  if constexpr (MQ == 1) {
+    chunk_tail(0, 0);
+  } else {
+    __syncthreads();                                 // every query's scores are staged
+    if (wave < MQ) {
+      const int64_t nref = npq[wave];
+      const int send = (int)max((int64_t)0, min((int64_t)SC_SPAN, nref - start));
+      if (send > 0) {
+        const SelBufs sbl = sbs;
+        const int64_t nwg = (nref + SC_CHUNK - 1) / SC_CHUNK;
+        const int64_t share = ((int64_t)K * SC_CHUNK + nref - 1) / nref;
+        const int64_t budget64 = min(2 * share + 16, max((int64_t)8, (int64_t)FIN_LDS_CANDS / nwg));
+        const int64_t cix = blockIdx.x;
+        wave_direct_tail(lsc + wave * SC_SPAN, send, (uint32_t)min(budget64, (int64_t)send), lhist + 256 * wave,
+                         sbl.hdr + (int64_t)vq[wave] * sbl.hdr_stride + cix,
+                         sbl.wgc + (int64_t)vq[wave] * sbl.wgc_stride + cix * CAND_CAP, CAND_CAP,
+                         [&](int i) { return (uint32_t)(start + i); });
+      }
+    }
+  }
 }
 
 // ---------------------------------------------------------------- finish (one workgroup per sequence)
@@ -900,7 +970,7 @@ hipError_t launch_score(const uint8_t* ik, const uint8_t* iks, const int64_t* en
 #define CSA2_SCORE_LAUNCH1(C, S, Mo, Q)                                                          \
   hipLaunchKernelGGL((score_kernel<C, S, Mo, Q>), grid, block, 0, stream, ik, iks, entry_offset, \
                      n_entries, max_n, q_idx, w, Hi, cand, cand_stride, scores, sstride, sb, K,  \
-                     (int)store, pool_k)
+                     (int)store, pool_k, 0)
 #define CSA2_SCORE_LAUNCH(C, S)                                                                  \
   if (base == 0) {                                                                               \
     if (qmx) CSA2_SCORE_LAUNCH1(C, S, 0, true); else CSA2_SCORE_LAUNCH1(C, S, 0, false);         \
@@ -924,6 +994,27 @@ hipError_t launch_score(const uint8_t* ik, const uint8_t* iks, const int64_t* en
   }
 #undef CSA2_SCORE_LAUNCH
 #undef CSA2_SCORE_LAUNCH1
+  return hipGetLastError();
+}
+
+// The multi-query pass of a prefill: B sequences of Tq queries each, scored
+// PREFILL_MQ queries per workgroup, selections per query (the virtual
+// sequences b * Tq + t of eo, ne, q_idx, w and sb); direct mode, exact scores.
+constexpr int PREFILL_MQ = 4;
+
+hipError_t launch_score_prefill(const uint8_t* ik, const uint8_t* iks, const int64_t* eo, const int32_t* ne, int B,
+                                int Tq, int64_t max_n, const uint16_t* q_idx, const float* w, int Hi, int mode,
+                                const SelBufs& sb, int K, hipStream_t stream) {
+  if (max_n <= 0) return hipSuccess;
+  if ((mode & kScoreQmx8) != 0) return hipErrorInvalidValue;
+  const int QG = (Tq + PREFILL_MQ - 1) / PREFILL_MQ;
+  dim3 grid((unsigned)((max_n + SC_SPAN - 1) / SC_SPAN), (unsigned)(B * QG)), block(SC_THREADS);
+  if (mode == 0)
+    hipLaunchKernelGGL((score_kernel<false, SEL_DIRECT, 0, false, PREFILL_MQ>), grid, block, 0, stream, ik, iks, eo, ne,
+                       max_n, q_idx, w, Hi, nullptr, 0, nullptr, 0, sb, K, 0, 0, Tq);
+  else
+    hipLaunchKernelGGL((score_kernel<false, SEL_DIRECT, 1, false, PREFILL_MQ>), grid, block, 0, stream, ik, iks, eo, ne,
+                       max_n, q_idx, w, Hi, nullptr, 0, nullptr, 0, sb, K, 0, 0, Tq);
   return hipGetLastError();
 }
 

@@ -99,6 +99,14 @@ hipError_t launch_score(const uint8_t* ik, const uint8_t* iks, const int64_t* en
                         float* scores, int64_t sstride, const SelBufs& sb, int sel, int K,
                         bool store_scores, int pool_k, hipStream_t stream);
 
+// The multi-query scoring pass of a prefill (direct top-k, exact scores): B
+// sequences of Tq queries; eo / ne / q_idx / w / sb are per query (virtual
+// sequence b * Tq + t, ne = its visible entries). The finish and attention of
+// the virtual decode batch follow unchanged.
+hipError_t launch_score_prefill(const uint8_t* ik, const uint8_t* iks, const int64_t* eo, const int32_t* ne, int B,
+                                int Tq, int64_t max_n, const uint16_t* q_idx, const float* w, int Hi, int mode,
+                                const SelBufs& sb, int K, hipStream_t stream);
+
 // src: non-null when the direct score pass did not store the scores, or for a
 // candidate list (src->cand set).
 hipError_t launch_finish(int sel, const int32_t* n_entries, int B, int64_t max_n, float* scores,

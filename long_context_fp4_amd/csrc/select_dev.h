@@ -262,6 +262,142 @@ __device__ __forceinline__ float score_tile_fn(const bf16x8_t (&qa)[4], const u3
   return head_sum<MODE>(acc, lw, g);
 }
 
+// ---------------------------------------------------------------- wave-level chunk tail
+// Bin of the need-th largest in 256 LDS counts h (bin 255 = largest), run by
+// one wave (every lane gets the result): *digit, and *above = the count in
+// higher bins. Returns false when the bins hold fewer than need.
+__device__ __forceinline__ bool wave_kth_digit(const uint32_t* h, uint32_t need, uint32_t* digit, uint32_t* above) {
+  const int lane = threadIdx.x & 63;
+  uint32_t c4[4], loc = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) { c4[q] = h[255 - 4 * lane - q]; loc += c4[q]; }
+  const uint32_t incl = wave_incl_sum(loc), pre = incl - loc;
+  if (readlane_u32(incl, 63) < need) return false;
+  const uint64_t hit = __ballot(pre < need && incl >= need);
+  const int hl = __ffsll((long long)hit) - 1;
+  uint32_t dq = 0, ab = 0, cum = pre;
+  bool found = false;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const bool h_ = !found && cum + c4[q] >= need;
+    dq = h_ ? 255u - 4u * lane - q : dq;
+    ab = h_ ? cum : ab;
+    found = found || h_;
+    cum += c4[q];
+  }
+  *digit = readlane_u32(dq, hl);
+  *above = readlane_u32(ab, hl);
+  return true;
+}
+
+// The local cutoff and candidate list of one chunk, computed by a single wave
+// (no workgroup barriers): the chunk's n <= 1024 scores sit in LDS at lss in
+// slot order; lane l takes slots 16l .. 16l+15. The cutoff is a 20-bit key
+// prefix with at least `budget` of the chunk's keys at or above it (0 when
+// there are fewer): from a band histogram of 256 bins of 16 prefix units
+// counted down from the chunk's largest prefix, or, when the band holds
+// fewer than `budget` keys, by a radix select of the prefix (8 + 8 + 4 bits).
+// Every key at or above it is written to wc as a composite, in position order
+// (at most cap of them), and the header word as (cutoff << 32 | count, bit 31
+// set when the list overflowed). hb: 256 words of LDS owned by this wave.
+// position(i): the position of slot i.
+template <typename Position>
+__device__ inline void wave_direct_tail(const float* lss, int n, uint32_t budget, uint32_t* hb, uint64_t* hdr,
+                                        uint64_t* wc, int cap, Position position) {
+  const int lane = threadIdx.x & 63;
+  uint32_t key[16];
+  uint32_t vm = 0, pmax = 0;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const float4 v = *(const float4*)(lss + 16 * lane + 4 * c);
+    const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int q = 4 * c + j;
+      key[q] = score_key(vv[j]);
+      const bool ok = 16 * lane + q < n;
+      vm |= (ok ? 1u : 0u) << q;
+      if (ok) pmax = max(pmax, key[q] >> 12);
+    }
+  }
+  const uint32_t M = wave_max_u32(pmax);
+  uint32_t fine = 0;                                  // keep all: fewer keys than the budget
+  // (an LDS wave's accesses are performed in order: each histogram is cleared,
+  // filled and read by this wave alone)
+  auto clear = [&]() {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) hb[4 * lane + j] = 0u;
+  };
+  clear();
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const uint32_t d = (M - (key[q] >> 12)) >> 4;
+    if (((vm >> q) & 1u) && d < 256u) atomicAdd(&hb[255u - d], 1u);   // bin 255 = the top 16 prefix units
+  }
+  uint32_t digit, above;
+  if (wave_kth_digit(hb, budget, &digit, &above)) {
+    const uint32_t lo = ((256u - digit) << 4) - 1u;  // the bin holds prefixes M - lo .. M - lo + 15
+    fine = M >= lo ? M - lo : 0u;
+  } else {
+    // radix select of the budget-th largest prefix: bits 19..12, 11..4, 3..0
+    uint32_t pre = 0, pmask = 0, need = budget;
+    bool enough = true;
+#pragma unroll
+    for (int pass = 0; pass < 3 && enough; ++pass) {
+      const int sh = pass == 0 ? 12 : (pass == 1 ? 4 : 0);
+      const uint32_t dmask = pass == 2 ? 15u : 255u;
+      clear();
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const uint32_t p = key[q] >> 12;
+        if (((vm >> q) & 1u) && (p & pmask) == pre) atomicAdd(&hb[(p >> sh) & dmask], 1u);
+      }
+      enough = wave_kth_digit(hb, need, &digit, &above);
+      if (enough) {
+        pre |= digit << sh;
+        pmask |= dmask << sh;
+        need -= above;
+      }
+    }
+    if (enough) fine = pre;
+  }
+  // the keys at or above the cutoff, in slot order
+  uint32_t sel = 0;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) sel |= ((((vm >> q) & 1u) && (key[q] >> 12) >= fine) ? 1u : 0u) << q;
+  const uint32_t cnt = (uint32_t)__popc(sel);
+  const uint32_t incl = wave_incl_sum(cnt);
+  const uint32_t tot = readlane_u32(incl, 63);
+  uint32_t at = incl - cnt;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    if ((sel >> q) & 1u) {
+      if (at < (uint32_t)cap) wc[at] = composite(key[q], position(16 * lane + q));
+      ++at;
+    }
+  }
+  if (lane == 0) *hdr = ((uint64_t)fine << 32) | (tot > (uint32_t)cap ? 0x80000000u : tot);
+}
+
+// MQ queries against one tile: the keys are dequantized once, then each query
+// takes the 4 MFMAs and head sum of score_tile_fn (the same float32 scores as
+// one query at a time). lw holds 16 head weights per query.
+template <int MODE, int MQ>
+__device__ __forceinline__ void score_tile_multi(const bf16x8_t (&qa)[MQ][4], const u32x4_t cw, uint32_t sbyte,
+                                                 const float* lw, int g, float (&out)[MQ]) {
+  const float scl = __uint_as_float(sbyte << 23);
+  bf16x8_t kb[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) kb[j] = dequant_mx_block8(cw[j], scl);
+#pragma unroll
+  for (int m = 0; m < MQ; ++m) {
+    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[m][j], kb[j], acc, 0, 0, 0);
+    out[m] = head_sum<MODE>(acc, lw + 16 * m, g);
+  }
+}
+
 // ---- quantized-query variant: gfx950's block-scaled FP8 x FP4 MFMA
 // v_mfma_scale_f32_16x16x128_f8f6f4 contracts 16 rows x 16 columns x 128 K in
 // one instruction, applying one E8M0 scale per row (column) and 32-K block.

@@ -46,3 +46,44 @@ def test_prefill_queries_see_only_completed_entries(m, T_list, k):
             fin = np.isfinite(rl)
             assert np.array_equal(fin, np.isfinite(lse[b, t]))
             assert np.all(np.abs(lse[b, t][fin] - rl[fin]) <= 2e-3), f"seq {b} query {t}: lse"
+
+
+def test_prefill_multi_query_pass_matches_oracle():
+    """The multi-query scoring pass (a long sequence, so the fused plan runs):
+    Tq = 11 is not a multiple of the queries a workgroup scores together, the
+    queries' visible ranges end in different 1024-entry chunks (one inside the
+    first chunk, one exactly at a chunk boundary), and two sequences of
+    different lengths share the launch."""
+    import torch
+    import long_context_fp4_amd as L
+    rng = np.random.default_rng(777)
+    m, k, H = 2, 512, 16
+    T_list = [70000, 41000]
+    w_lat = synth.merge_weights(rng, m, 512)
+    w_idx = synth.merge_weights(rng, m, 128)
+    parts = [OC.cache_write(synth.hidden_host(rng, (T, 512)), synth.hidden_host(rng, (T, 128)), w_lat, w_idx, m)
+             for T in T_list]
+    E = [p[0].shape[0] for p in parts]
+    kv, ik, iks = (np.concatenate([p[i] for p in parts]) for i in range(3))
+    off = np.concatenate([[0], np.cumsum(E)[:-1]]).astype(np.int64)
+    B, Tq = len(T_list), 11
+    pos = np.stack([np.array([1500, 2047, 2048 * 3 - 1, 2048 * 5, T // 2, T // 2 + 1, T - 700, T - 40, T - 3,
+                              T - 2, T - 1], np.int64) for T in T_list])
+    q = np.stack([[synth.latent_query(rng, H) for _ in range(Tq)] for _ in range(B)])
+    qi = np.stack([[synth.indexer_query(rng, 16) for _ in range(Tq)] for _ in range(B)])
+    w = np.stack([[synth.head_weights(rng, 16) for _ in range(Tq)] for _ in range(B)])
+    top, out, lse = L.prefill_layer(dev(kv), dev(ik), dev(iks), dev(off), dev(np.asarray(E, np.int32)), max(E), m,
+                                    dev(pos), dev(qi), dev(q), w=dev(w), k=k)
+    torch.cuda.synchronize()
+    top, out, lse = host(top), host(out), host(lse)
+    for b in range(B):
+        for t in range(Tq):
+            nv = min(E[b], (int(pos[b, t]) + 1) // m)
+            rows = slice(off[b], off[b] + nv)
+            s = OI.scores(ik[rows], iks[rows], qi[b, t], w[b, t], 1)
+            want = OI.topk(s, np.arange(nv), k)
+            check_topk(top[b, t], want, lambda p: s[p], k, f"seq {b} query {t}")
+            ro, rl = OA.sparse_attention(kv[off[b]:off[b] + E[b]], top[b, t], q[b, t])
+            err = attn_rel_err(out[b, t], ro)
+            assert np.all(err <= ATTN_REL_TOL), f"seq {b} query {t}: max rel err {err.max():.3g}"
+            assert np.all(np.abs(lse[b, t] - rl) <= 2e-3), f"seq {b} query {t}: lse"
