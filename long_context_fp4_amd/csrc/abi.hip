@@ -6,6 +6,8 @@
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
+#include <algorithm>
+#include <atomic>
 #include <mutex>
 
 static_assert(CSA2_SCORE_QMX8 == csa2::kScoreQmx8, "score-mode flag differs between the header and the kernels");
@@ -43,9 +45,16 @@ size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // state between calls (every kernel writes what it reads), so a workspace needs
 // no initialisation and can be reused by calls of any kind and size.
 struct IndexerWs {
-  size_t ctrl, bitmap, cand, scores, hdr, summ, wgc, gscr, hdrp, wgcp, total;
+  size_t ctrl, bitmap, cand, scores, hdr, summ, wgc, gscr, hdrp, wgcp, psync, pxh, pxk, pxn, pxc, total;
   int64_t slots, bm_words, nblk, gscr_stride;
+  int pool_parts_max;   // workgroups per sequence the pool exchange is sized for
 };
+
+// Most workgroups per sequence a split pool finish may use for B sequences.
+int pool_parts_max(int B) {
+  const int p = csa2::kPoolPartBudget / (B > 0 ? B : 1);
+  return p < 1 ? 1 : (p > csa2::kPoolMaxParts ? csa2::kPoolMaxParts : p);
+}
 
 IndexerWs indexer_layout(int B, int64_t max_n, int k, int pool_k, int cand_stride) {
   IndexerWs L;
@@ -67,8 +76,34 @@ IndexerWs indexer_layout(int B, int64_t max_n, int k, int pool_k, int cand_strid
   L.gscr = off;   off = round_up(off + (size_t)B * L.gscr_stride * 8, 256);
   L.hdrp = off;   off = round_up(off + (pl ? (size_t)B * L.nblk * 8 : 0), 256);
   L.wgcp = off;   off = round_up(off + (pl ? (size_t)B * L.nblk * csa2::kPoolCap * 8 : 0), 256);
+  // a pool finish split over several workgroups per sequence: arrival
+  // counters, per-part histograms and threshold-bin keys, per-chunk counts
+  L.pool_parts_max = pl ? pool_parts_max(B) : 1;
+  const size_t xp = L.pool_parts_max > 1 ? (size_t)B * L.pool_parts_max : 0;
+  L.psync = off;  off = round_up(off + (pl ? (size_t)B * 16 : 0), 256);
+  L.pxh = off;    off = round_up(off + xp * csa2::kPoolXBins * 4, 256);
+  L.pxk = off;    off = round_up(off + xp * csa2::kPoolXKeys * 8, 256);
+  L.pxn = off;    off = round_up(off + xp * 4, 256);
+  L.pxc = off;    off = round_up(off + (xp ? (size_t)B * L.nblk * 4 : 0), 256);
   L.total = off;
   return L;
+}
+
+// Compute units of the current device in *out (queried once per device); a
+// status code.
+int device_cus(int* out) {
+  static std::atomic<int> cus[64];
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  int v = (dev >= 0 && dev < 64) ? cus[dev].load(std::memory_order_relaxed) : 0;
+  if (v <= 0) {
+    e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_status(e, "hipDeviceGetAttribute(multiprocessors)");
+    if (dev >= 0 && dev < 64) cus[dev].store(v, std::memory_order_relaxed);
+  }
+  *out = v;
+  return CSA2_OK;
 }
 
 // Scratch of the attention (its workgroups need none of their own).
@@ -136,6 +171,7 @@ csa2::SelBufs make_selbufs(const IndexerWs& L, uint8_t* ws) {
   sb.hdrp = (uint64_t*)(ws + L.hdrp);
   sb.wgcp = (uint64_t*)(ws + L.wgcp);
   sb.wgcp_stride = L.nblk * csa2::kPoolCap;
+  sb.psync = L.psync != L.pxh ? (uint32_t*)(ws + L.psync) : nullptr;
   return sb;
 }
 
@@ -427,6 +463,7 @@ int run_decode_layer(int mode, const uint8_t* kv, const uint8_t* ik, const uint8
                      int pre_B = 0, int pre_Tq = 0) {
   const FusedPlan fp = fused_plan(mode, B, max_n, H, k, pool_k);
   const int cand_stride = mode == CSA2_REINDEX ? pool_k : 0;
+  int rc0 = CSA2_OK;
   if (fp.on && allow_fused) {
     // scoring launch, then the attention that runs the top-k finish itself
     // (and, for a Full layer with a pool, the pool finish in workgroups of its own)
@@ -438,6 +475,7 @@ int run_decode_layer(int mode, const uint8_t* kv, const uint8_t* ik, const uint8
     ff.src = csa2::ScoreSrc{ik, iks, entry_offset, q_idx, w, Hi, score_mode, nullptr, 0, nullptr, 0};
     ff.pool_k = 0;
     ff.pool = nullptr;
+    ff.px = csa2::PoolExchange{nullptr, nullptr, nullptr, nullptr, L.nblk, 1};
     hipError_t e;
     if (mode == CSA2_FULL && pre_Tq > 0 && pool_k == 0 && (score_mode & CSA2_SCORE_QMX8) == 0) {
       // a prefill's virtual batch: the multi-query pass reads each key tile
@@ -449,6 +487,20 @@ int run_decode_layer(int mode, const uint8_t* kv, const uint8_t* ik, const uint8
                      pool_k > 0 ? csa2::SEL_POOL : csa2::SEL_DIRECT, k, false, pool_k, s);
       ff.pool_k = pool_k;
       ff.pool = pool;
+      if (pool_k > 0) {
+        // the pool finish split over as many workgroups per sequence as stay
+        // resident beside the attention's (one workgroup per compute unit;
+        // a launch that asks for every unit waits for some of them, so three
+        // quarters), each with at least 8 chunk lists
+        const int G = csa2::attention_workgroups(B, H, k);
+        int cus = 0;
+        if ((rc0 = device_cus(&cus)) != CSA2_OK) return rc0;
+        int parts = L.pool_parts_max;
+        parts = std::min(parts, std::max(1, (cus * 3 / 4 - G) / B));
+        parts = std::min(parts, std::max(1, (int)(L.nblk / 8)));
+        ff.px = csa2::PoolExchange{(uint32_t*)(ws + L.pxh), (uint64_t*)(ws + L.pxk), (uint32_t*)(ws + L.pxn),
+                                   (uint32_t*)(ws + L.pxc), L.nblk, parts};
+      }
     } else {
       e = csa2::launch_score(ik, iks, entry_offset, n_entries, B, max_n, q_idx, w, Hi, score_mode, pool, pool_k,
                              scores, L.slots, sb, csa2::SEL_DIRECT, k, true, 0, s);

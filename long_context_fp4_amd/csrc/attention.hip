@@ -118,16 +118,24 @@ __global__ __launch_bounds__(AT_THREADS) void attention_kernel(
   const int G = B * HG;
   const int wg = blockIdx.x;
   if (FIN && wg >= G) {
-    // one of the launch's last B workgroups: the pool finish of sequence wg - G
+    // one of the launch's last B * P workgroups: part wg - G mod P of the pool
+    // finish of sequence (wg - G) / P; part 0 has the sequence's scratch rows
     uint8_t* pb8 = (uint8_t*)&pbuf[0][0];
     const FinLds fl{(uint64_t*)smem, (uint64_t*)(smem + 8 * FIN_LDS_CANDS), (uint32_t*)sidx,
                     (uint32_t*)(pb8 + 512), (uint64_t*)pb8, (uint32_t*)(pb8 + 256), (uint32_t*)(pb8 + 384),
                     (uint64_t*)(pb8 + 2560), (uint32_t*)(pb8 + 416)};
-    const int bp = wg - G;
+    const int P = ff.px.parts;
+    const int bp = (wg - G) / P, part = (wg - G) % P;
+    float* sall = part == 0 ? ff.scores + (int64_t)(G + bp) * ff.scores_stride : nullptr;
+    uint64_t* gs = part == 0 ? ff.gscr + (int64_t)(G + bp) * ff.gscr_stride : nullptr;
     int32_t* po = ff.pool + (int64_t)bp * ff.pool_k;
-    pool_finish_body<AT_THREADS>(bp, n_entries, ff.max_n, ff.pool_k, ff.sb,
-                                 ff.scores + (int64_t)wg * ff.scores_stride, ff.gscr + (int64_t)wg * ff.gscr_stride,
-                                 ff.src, fl, [&](int j, int32_t v) { po[j] = v; });
+    auto emit = [&](int j, int32_t v) { po[j] = v; };
+    if (pool_finish_body<AT_THREADS>(bp, n_entries, ff.max_n, ff.pool_k, ff.sb, sall, gs, ff.src, fl, emit, &ff.px,
+                                     part)) {
+      __syncthreads();
+      // a wait ran out of time: the whole finish, unsplit
+      pool_finish_body<AT_THREADS>(bp, n_entries, ff.max_n, ff.pool_k, ff.sb, sall, gs, ff.src, fl, emit);
+    }
     return;
   }
   // dispatch deals workgroups to the 8 XCDs in turn; number them so that the
@@ -458,7 +466,8 @@ hipError_t launch_attention(const uint8_t* kv, const int64_t* entry_offset, cons
     if (dev >= 0 && dev < 64) attr_set[dev].store(1u, std::memory_order_release);
   }
   const int G = B * ((H + 15) / 16);
-  dim3 grid((unsigned)(G + (fin && fin->pool_k > 0 ? B : 0))), block(AT_THREADS);
+  if (fin && fin->pool_k > 0 && (fin->px.parts < 1 || fin->px.parts > kPoolMaxParts)) return hipErrorInvalidValue;
+  dim3 grid((unsigned)(G + (fin && fin->pool_k > 0 ? B * fin->px.parts : 0))), block(AT_THREADS);
   if (fin)
     hipLaunchKernelGGL(attention_kernel<true>, grid, block, AT_LDS, stream, kv, entry_offset, n_entries, idx,
                        k, q, B, H, tau, out, lse, *fin);

@@ -173,6 +173,8 @@ __global__ __launch_bounds__(SC_THREADS) __attribute__((amdgpu_waves_per_eu(CAND
   const int b = vq[0];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, g = lane >> 4;
+  // the counters of the split pool finish that follows this pass start at zero
+  if (SEL == SEL_POOL && blockIdx.x == 0 && tid < 4 && sb.psync) sb.psync[(int64_t)b * 4 + tid] = 0u;
   // independent loads first (the sequence's length and first row, the queries,
   // the head weights), so the keys are requested one round trip after the start
   int32_t neq[MQ];

@@ -71,6 +71,27 @@ struct SelBufs {
   uint64_t* hdrp;       // [B][hdr_stride]: pool header per score workgroup (pool mode)
   uint64_t* wgcp;       // [B][wgcp_stride]: kPoolCap pool candidates per workgroup (pool mode)
   int64_t wgcp_stride;
+  uint32_t* psync;      // [B][4]: arrival counters of a split pool finish; the pool-mode
+                        // score pass sets them to zero (NULL: nothing to clear)
+};
+
+// A pool finish split over `parts` workgroups per sequence, each sweeping a
+// contiguous range of the chunk lists; they exchange per-part histograms,
+// per-chunk counts and the keys inside the threshold bin through these
+// buffers (device-scope loads and stores) and wait for one another at two
+// counters of SelBufs::psync. Workgroup bytes per sequence and part:
+// kPoolXBins * 4 + kPoolXKeys * 8 + 4, plus 4 per chunk.
+constexpr int kPoolXBins = 4096;       // histogram bins of the pool finish
+constexpr int kPoolXKeys = 4096;       // threshold-bin keys a split finish exchanges (in total)
+constexpr int kPoolMaxParts = 16;      // workgroups per sequence
+constexpr int kPoolPartBudget = 256;   // pool workgroups of one launch, at most (all resident at once)
+struct PoolExchange {
+  uint32_t* hist;       // [B][parts][kPoolXBins]
+  uint64_t* keys;       // [B][parts][kPoolXKeys]
+  uint32_t* nkeys;      // [B][parts]
+  uint32_t* counts;     // [B][nblk]
+  int64_t nblk;
+  int parts;            // 1: one workgroup per sequence, nothing exchanged
 };
 
 // What the score pass reads, for a finish that has to recompute scores; for a
@@ -134,8 +155,9 @@ hipError_t launch_pool_finish(const int32_t* n_entries, int B, int64_t max_n, co
 // (scores not stored, or a candidate list's stored scores), keeps the result in
 // LDS, and the first workgroup of each sequence writes the top-k to `topk`.
 // scores / gscr give every workgroup rows of its own for the finish's fallback.
-// With pool_k > 0 the launch has B more workgroups, one per sequence, that
-// run the pool finish of a pool-mode score pass into `pool`.
+// With pool_k > 0 the launch has B * px.parts more workgroups, px.parts per
+// sequence, that run the pool finish of a pool-mode score pass into `pool`
+// (part 0 of each sequence uses the sequence's scratch rows G + b).
 struct FusedFinish {
   SelBufs sb;
   ScoreSrc src;
@@ -147,6 +169,7 @@ struct FusedFinish {
   int32_t* topk;          // [B][k]
   int pool_k;             // 0, or the pool size
   int32_t* pool;          // [B][pool_k]
+  PoolExchange px;        // the split of the pool finish (px.parts >= 1)
 };
 
 // Attention: number of entry splits used for B sequences, H heads, k indices.

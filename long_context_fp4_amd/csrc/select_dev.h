@@ -1021,13 +1021,19 @@ __device__ inline bool finish_direct_body(int b, const int32_t* __restrict__ n_e
       if (total <= (uint32_t)FIN_LDS_CANDS) {
         lc_used = true;
         // copy the lists in chunk order (wave v takes the FS chunks from
-        // FS v in each round of RL) and histogram the prefixes
+        // FS v in each round of RL) and histogram the prefixes. A round's
+        // entries 64 .. 127 are requested with its first 64 (entry `lane` of
+        // round 0 is in v0 already), and the next round's first entries
+        // before this round's are stored, so a round waits for one round trip.
         auto take = [&](uint64_t c, uint32_t at) {
           lc[at] = c;
           count_above_cmax(c);
         };
+        uint64_t vn[FS];
+#pragma unroll
+        for (int s = 0; s < FS; ++s) vn[s] = v0[s];
         for (int r0 = 0; r0 < nw; r0 += RL) {
-          uint64_t v[FS];
+          uint64_t v[FS], v2[FS];
           uint32_t cn[FS], of[FS];
           int ws[FS];
 #pragma unroll
@@ -1036,12 +1042,19 @@ __device__ inline bool finish_direct_body(int b, const int32_t* __restrict__ n_e
             ws[s] = min(w, (int)nw - 1);
             cn[s] = w < nw ? (ws[s] + 1 < nw ? loff[ws[s] + 1] : total) - loff[ws[s]] : 0u;
             of[s] = loff[ws[s]];
-            v[s] = r0 == 0 ? v0[s] : wc[(int64_t)ws[s] * CAND_CAP + lane];   // round 0: already requested
+            v[s] = vn[s];
+            v2[s] = 64u + lane < cn[s] ? wc[(int64_t)ws[s] * CAND_CAP + 64 + lane] : 0ull;
+          }
+          if (r0 + RL < nw) {
+#pragma unroll
+            for (int s = 0; s < FS; ++s)
+              vn[s] = wc[(int64_t)min(r0 + RL + FS * wave + s, (int)nw - 1) * CAND_CAP + lane];
           }
 #pragma unroll
           for (int s = 0; s < FS; ++s) {
             if ((uint32_t)lane < cn[s]) take(v[s], of[s] + lane);
-            for (uint32_t j = 64 + lane; j < cn[s]; j += 64) take(wc[(int64_t)ws[s] * CAND_CAP + j], of[s] + j);
+            if (64u + lane < cn[s]) take(v2[s], of[s] + 64 + lane);
+            for (uint32_t j = 128 + lane; j < cn[s]; j += 64) take(wc[(int64_t)ws[s] * CAND_CAP + j], of[s] + j);
           }
         }
         __syncthreads();
@@ -1085,6 +1098,56 @@ __device__ inline bool finish_direct_body(int b, const int32_t* __restrict__ n_e
   return lc_used;
 }
 
+// ---------------------------------------------------------------- device-scope exchange
+// Loads and stores with the sc1 cache policy reach the device's coherence
+// point, so workgroups on different XCDs (each with an L2 of its own) see one
+// another's values without any cache flush.
+constexpr int kRsrcWord3 = 0x00020000;   // buffer resource word 3: raw 32-bit data
+constexpr int kSc1 = 16;                 // buffer cache policy: sc1 (device scope)
+typedef uint32_t buf_u32x4_t __attribute__((vector_size(16)));
+typedef uint32_t buf_u32x2_t __attribute__((vector_size(8)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t dev_rsrc(const void* p, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, bytes, kRsrcWord3);
+}
+__device__ __forceinline__ u32x4_t dev_load16(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kSc1));
+}
+__device__ __forceinline__ void dev_store16(__amdgpu_buffer_rsrc_t r, int off, u32x4_t v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(buf_u32x4_t, v), r, off, 0, kSc1);
+}
+__device__ __forceinline__ uint32_t dev_load4(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kSc1);
+}
+__device__ __forceinline__ void dev_store4(__amdgpu_buffer_rsrc_t r, int off, uint32_t v) {
+  __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, kSc1);
+}
+
+// Arrival of this workgroup at counter c, then a wait (bounded: until the
+// real-time counter passes `deadline`) for `parts` arrivals. Every thread's
+// device-scope stores are complete before the arrival: they write through to
+// the coherence point, so waiting for their completion (vmcnt 0) is all the
+// release needs (no L2 write-back). Returns true when all arrived (the same
+// value in every thread); `flag` is one word of LDS.
+__device__ inline bool arrive_and_wait(uint32_t* c, uint32_t parts, uint64_t deadline, uint32_t* flag) {
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's loads and stores are complete
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t ok = 0;
+    for (;;) {
+      if (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= parts) { ok = 1; break; }
+      if (__builtin_amdgcn_s_memrealtime() > deadline) break;
+      __builtin_amdgcn_s_sleep(1);
+    }
+    *flag = ok;
+  }
+  __syncthreads();
+  const bool ok = *flag != 0;
+  __syncthreads();
+  return ok;
+}
+
 // Pool finish (the K best positions, ascending) from the pool lists of a
 // pool-mode score pass. Chunk c's list holds, in position order, every key of
 // the chunk whose 20-bit prefix reaches its cutoff; its header packs count |
@@ -1102,13 +1165,29 @@ __device__ inline bool finish_direct_body(int b, const int32_t* __restrict__ n_e
 // A wave sweeps chunks wave, wave + 8, ... in groups of PF_G, with every
 // group's list entries requested before any is used. Fewer than K keys at or
 // above cmax: fallback_select. Output through emit(j, position) for j < K.
+//
+// Split (px->parts = P > 1): part p of the sequence sweeps chunks
+// [nw p / P, nw (p + 1) / P); the parts add up their histograms after the
+// first sweep and, after the second, share their per-chunk counts and the
+// keys inside T, so each finds T, the cut inside it and its chunks' output
+// offsets by itself. The fallback and a threshold bin beyond kPoolXKeys keys
+// are left to part 0 (the others return). sall / gscr: the scratch rows (NULL
+// for a workgroup without rows, which then returns instead of using them).
+// Returns true when a wait for the other parts ran out of time (nothing was
+// emitted by this call): the caller then runs the whole finish unsplit, as
+// part 0 with rows or as a part without them; every way of finishing emits
+// the same positions, so overlapping writers write equal values.
 template <int NT, typename Emit>
-__device__ inline void pool_finish_body(int b, const int32_t* __restrict__ n_entries, int64_t max_n, int K,
+__device__ inline bool pool_finish_body(int b, const int32_t* __restrict__ n_entries, int64_t max_n, int K,
                                         const SelBufs& sb, float* sall, uint64_t* gscr, const ScoreSrc& src,
-                                        const FinLds& L, Emit emit) {
+                                        const FinLds& L, Emit emit, const PoolExchange* px = nullptr, int part = 0) {
   constexpr int NWAVE = NT / 64;
   constexpr int PF_G = 8;                               // chunks whose entries a wave requests at once
+  static_assert(NBINS == kPoolXBins && NBINS % (4 * NT) == 0 && FIN_SUB_CAP == kPoolXKeys, "exchange sizes");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int P = px ? px->parts : 1;
+  const bool split_wgs = P > 1;
+  const bool rows = sall != nullptr;
   uint32_t* const hist = (uint32_t*)L.sub;              // 4096 bins, then the in-bin keys
   uint32_t* const lcount = (uint32_t*)L.lc;             // [nw] list lengths
   uint32_t* const cnt = L.loff;                         // [nw] selected per chunk, then offsets
@@ -1116,14 +1195,18 @@ __device__ inline void pool_finish_body(int b, const int32_t* __restrict__ n_ent
   uint32_t* const scan_tmp = L.scan_tmp;
   const int64_t n_pos = min((int64_t)n_entries[b], max_n);
   if (n_pos <= K) {
-    for (int j = tid; j < K; j += NT) emit(j, j < n_pos ? j : -1);
-    return;
+    if (part == 0)
+      for (int j = tid; j < K; j += NT) emit(j, j < n_pos ? j : -1);
+    return false;
   }
   const int nw = (int)((n_pos + SC_CHUNK - 1) / SC_CHUNK);
   if (nw > FIN_MAX_WG) {                                // more chunks than the LDS counts hold
-    fallback_select<NT>(b, n_pos, K, sall, gscr, src, 1, L, emit);
-    return;
+    if (rows) fallback_select<NT>(b, n_pos, K, sall, gscr, src, 1, L, emit);
+    return false;
   }
+  const int c_lo = (int)((int64_t)nw * part / P), c_hi = (int)((int64_t)nw * (part + 1) / P);
+  // (a wait longer than ~4 ms means the parts are not all resident)
+  const uint64_t deadline = split_wgs ? __builtin_amdgcn_s_memrealtime() + 400000u : 0u;
   const uint64_t* hd = sb.hdrp + (int64_t)b * sb.hdr_stride;
   const uint64_t* wl = sb.wgcp + (int64_t)b * sb.wgcp_stride;
   uint32_t cmax = 0, mx = 0;
@@ -1149,23 +1232,36 @@ __device__ inline void pool_finish_body(int b, const int32_t* __restrict__ n_ent
   while (((mx - cmax) >> sh) >= (uint32_t)NBINS) ++sh;
   // bin of a prefix p >= cmax, NBINS - 1 for the largest (hist_kth_bin counts down from there)
   auto bin_of = [&](uint32_t p) -> uint32_t { return (uint32_t)NBINS - 1u - min((mx - p) >> sh, (uint32_t)NBINS - 1u); };
-  // one sweep: fn(c, j0, v0, ok0, v1, ok1) per block of 128 entries (from
-  // entry j0) of chunk c's list, lane l holding entries j0 + 2l and j0 + 2l + 1
-  // (wave-uniform calls, the blocks of a chunk in order, one wave per chunk)
+  // one sweep over this part's chunks: fn(c, j0, v0, ok0, v1, ok1) per block
+  // of 128 entries (from entry j0) of chunk c's list, lane l holding entries
+  // j0 + 2l and j0 + 2l + 1 (wave-uniform calls, the blocks of a chunk in
+  // order, one wave per chunk). The next group's first blocks are requested
+  // before this group's are used.
+  auto fetch = [&](int c0, u32x4_t (&v)[PF_G], uint32_t (&n)[PF_G]) {
+#pragma unroll
+    for (int gi = 0; gi < PF_G; ++gi) {
+      const int c = c0 + NWAVE * gi;
+      n[gi] = c < c_hi ? lcount[c] : 0u;
+      v[gi] = 2u * lane < n[gi] ? *(const u32x4_t*)(wl + (int64_t)c * kPoolCap + 2 * lane) : u32x4_t{0, 0, 0, 0};
+    }
+  };
   auto sweep = [&](auto fn) {
-    for (int c0 = wave; c0 < nw; c0 += NWAVE * PF_G) {
+    u32x4_t vn[PF_G];
+    uint32_t nn[PF_G];
+    fetch(c_lo + wave, vn, nn);
+    for (int c0 = c_lo + wave; c0 < c_hi; c0 += NWAVE * PF_G) {
       u32x4_t v[PF_G];
       uint32_t n[PF_G];
 #pragma unroll
       for (int gi = 0; gi < PF_G; ++gi) {
-        const int c = c0 + NWAVE * gi;
-        n[gi] = c < nw ? lcount[c] : 0u;
-        v[gi] = 2u * lane < n[gi] ? *(const u32x4_t*)(wl + (int64_t)c * kPoolCap + 2 * lane) : u32x4_t{0, 0, 0, 0};
+        v[gi] = vn[gi];
+        n[gi] = nn[gi];
       }
+      if (c0 + NWAVE * PF_G < c_hi) fetch(c0 + NWAVE * PF_G, vn, nn);
 #pragma unroll
       for (int gi = 0; gi < PF_G; ++gi) {
         const int c = c0 + NWAVE * gi;
-        if (c < nw) {
+        if (c < c_hi) {
           fn(c, 0u, ((uint64_t)v[gi][1] << 32) | v[gi][0], 2u * lane < n[gi],
              ((uint64_t)v[gi][3] << 32) | v[gi][2], 2u * lane + 1 < n[gi]);
           for (uint32_t j0 = 128; j0 < n[gi]; j0 += 128) {     // long lists
@@ -1178,6 +1274,10 @@ __device__ inline void pool_finish_body(int b, const int32_t* __restrict__ n_ent
     }
   };
   auto p20_of = [](uint64_t c) { return (uint32_t)(c >> 44); };
+  // the sequence's exchange views (split only)
+  uint32_t* const sync = split_wgs ? sb.psync + (int64_t)b * 4 : nullptr;
+  const __amdgpu_buffer_rsrc_t xh =
+      dev_rsrc(split_wgs ? px->hist + (int64_t)b * P * NBINS : nullptr, split_wgs ? P * NBINS * 4 : 0);
   // sweep 1: histogram
   sweep([&](int, uint32_t, uint64_t v0, bool ok0, uint64_t v1, bool ok1) {
     const uint32_t p0 = p20_of(v0), p1 = p20_of(v1);
@@ -1185,19 +1285,46 @@ __device__ inline void pool_finish_body(int b, const int32_t* __restrict__ n_ent
     if (ok1 && p1 >= cmax) atomicAdd(&hist[bin_of(p1)], 1u);
   });
   __syncthreads();
+  if (split_wgs) {
+    // publish this part's histogram, wait for the others', add them up
+    // (thread t: bins 4t .. 4t + 3 of each 4 * NT)
+#pragma unroll
+    for (int i = 4 * tid; i < NBINS; i += 4 * NT)
+      dev_store16(xh, (part * NBINS + i) * 4, *(const u32x4_t*)&hist[i]);
+    if (!arrive_and_wait(sync, (uint32_t)P, deadline, &ctl[7])) return true;
+#pragma unroll
+    for (int i = 4 * tid; i < NBINS; i += 4 * NT) {
+      u32x4_t v[kPoolMaxParts];
+#pragma unroll
+      for (int q = 0; q < kPoolMaxParts; ++q)
+        v[q] = q < P ? dev_load16(xh, (q * NBINS + i) * 4) : u32x4_t{0, 0, 0, 0};
+      u32x4_t t = v[0];
+#pragma unroll
+      for (int q = 1; q < kPoolMaxParts; ++q) t += v[q];
+      *(u32x4_t*)&hist[i] = t;
+    }
+    __syncthreads();
+  }
   uint32_t tot;
   hist_kth_bin<NT>(hist, (uint32_t)K, scan_tmp, ctl, &tot);
   if (ctl[0] == 0xFFFFFFFFu) {                          // fewer than K keys reach cmax
-    fallback_select<NT>(b, n_pos, K, sall, gscr, src, 1, L, emit);
-    return;
+    if (rows && (part == 0 || !split_wgs)) fallback_select<NT>(b, n_pos, K, sall, gscr, src, 1, L, emit);
+    return false;
   }
   const uint32_t T = ctl[0], above = ctl[1], in_bin = hist[T];
   const uint32_t need = (uint32_t)K - above;            // 1 .. in_bin
   const bool split = need < in_bin;
   auto in_t = [&](uint32_t p) { return p >= cmax && bin_of(p) == T; };
   auto above_t = [&](uint32_t p) { return p >= cmax && bin_of(p) > T; };
+  const bool big_bin = in_bin > (uint32_t)FIN_SUB_CAP;
+  if (split && big_bin && (split_wgs || !rows)) {
+    // the bin's keys do not fit the exchange (or this workgroup has no row
+    // for them): an unsplit finish with rows handles the sequence
+    if (split_wgs && part == 0 && rows) return true;
+    return false;
+  }
   __syncthreads();                                      // hist reads done before it is reused
-  uint64_t* const dst = in_bin <= (uint32_t)FIN_SUB_CAP ? L.sub : gscr;
+  uint64_t* const dst = big_bin ? gscr : L.sub;
   if (tid == 0) ctl[6] = 0;
   __syncthreads();
   // sweep 2: counts above T per chunk (and inside T when all of it is taken);
@@ -1219,6 +1346,70 @@ __device__ inline void pool_finish_body(int b, const int32_t* __restrict__ n_ent
       if (t1 && at1 < in_bin) dst[at1] = v1;
     }
   });
+  if (split_wgs) {
+    // publish this part's chunk counts and threshold-bin keys, wait for the
+    // others', then take every chunk's count and every key of the bin
+    __syncthreads();
+    const int64_t xb = (int64_t)b * P;
+    const __amdgpu_buffer_rsrc_t xc = dev_rsrc(px->counts + (int64_t)b * px->nblk, nw * 4);
+    const __amdgpu_buffer_rsrc_t xk = dev_rsrc(px->keys + xb * kPoolXKeys, P * kPoolXKeys * 8);
+    const __amdgpu_buffer_rsrc_t xn = dev_rsrc(px->nkeys + xb, P * 4);
+    for (int c = c_lo + tid; c < c_hi; c += NT) dev_store4(xc, 4 * c, cnt[c]);
+    const uint32_t mine = split ? min(ctl[6], in_bin) : 0u;
+    for (uint32_t j = tid; j < mine; j += NT) {
+      const uint64_t v = dst[j];
+      const u32x2_t w2 = {(uint32_t)v, (uint32_t)(v >> 32)};
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(buf_u32x2_t, w2), xk,
+                                            (int)(((int64_t)part * kPoolXKeys + j) * 8), 0, kSc1);
+    }
+    if (tid == 0) dev_store4(xn, 4 * part, mine);
+    if (!arrive_and_wait(sync + 1, (uint32_t)P, deadline, &ctl[7])) return true;
+    // counts of every chunk (thread t: chunks t, t + NT, ...)
+    {
+      constexpr int NC = FIN_MAX_WG / NT;
+      uint32_t cv[NC];
+#pragma unroll
+      for (int q = 0; q < NC; ++q) {
+        const int c = tid + q * NT;
+        cv[q] = c < nw ? dev_load4(xc, 4 * c) : 0u;
+      }
+#pragma unroll
+      for (int q = 0; q < NC; ++q)
+        if (tid + q * NT < nw) cnt[tid + q * NT] = cv[q];
+    }
+    if (split) {
+      // the parts' key counts and where each part's keys go
+      uint32_t nk[kPoolMaxParts], off[kPoolMaxParts];
+#pragma unroll
+      for (int q = 0; q < kPoolMaxParts; ++q) nk[q] = q < P ? dev_load4(xn, 4 * q) : 0u;
+      uint32_t run = 0;
+#pragma unroll
+      for (int q = 0; q < kPoolMaxParts; ++q) { off[q] = run; run += nk[q]; }
+      constexpr int NK = FIN_SUB_CAP / NT;
+      uint64_t kv[NK];
+      uint32_t at[NK];
+      bool okk[NK];
+#pragma unroll
+      for (int u = 0; u < NK; ++u) {
+        const uint32_t j = tid + u * NT;             // index in the bin's keys
+        int q = 0;
+#pragma unroll
+        for (int q2 = 1; q2 < kPoolMaxParts; ++q2) q = (q2 < P && j >= off[q2]) ? q2 : q;
+        at[u] = j;
+        const bool ok = j < run && j < in_bin;
+        okk[u] = ok;
+        const u32x2_t w2 = ok ? __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(
+                                                                 xk, (int)(((int64_t)q * kPoolXKeys + (j - off[q])) * 8),
+                                                                 0, kSc1))
+                              : u32x2_t{0u, 0u};
+        kv[u] = (uint64_t)w2[1] << 32 | w2[0];
+      }
+      __syncthreads();                                  // this part's own keys in dst are read
+#pragma unroll
+      for (int u = 0; u < NK; ++u)
+        if (okk[u]) dst[at[u]] = kv[u];
+    }
+  }
   uint64_t prefix = 0, mask = 0;
   if (split) {
     if (dst != L.sub) __threadfence_block();            // this workgroup reads its global copy back
@@ -1265,6 +1456,7 @@ __device__ inline void pool_finish_body(int b, const int32_t* __restrict__ n_ent
     if (s1) emit((int)(r0 + (s0 ? 1u : 0u)), (int32_t)(0xFFFFFFFFu - (uint32_t)v1));
     run_o += (uint32_t)__popcll(m0) + (uint32_t)__popcll(m1);
   });
+  return false;
 }
 
 

@@ -64,6 +64,51 @@ def test_layer_group_full_reindex_reuse(n_list, pool_k):
         check_attention(kv[rows], topR[b], qU[b], outU[b], lseU[b], f"reuse attention {b}")
 
 
+def test_full_layer_pool_edge_cases():
+    """A Full layer with a 4096 pool whose finish is split over several
+    workgroups per sequence: sequence 0 has its 700 largest keys in its first
+    chunk (too few keys reach the highest pool cutoff: the fallback), sequence
+    1 is shorter than the pool, sequence 2 holds one indexer row 30000 times
+    (every key in the threshold bin, more than the parts exchange: one
+    workgroup finishes it with its scratch rows), sequence 3 is empty and
+    sequence 4 takes the split path; then the same workspace with the batch
+    reversed."""
+    import torch
+    import long_context_fp4_amd as L
+    rng = np.random.default_rng(77)
+    n_list = [40000, 3000, 30000, 0, 50000]
+    pool_k, H = 4096, 64
+    kv, ik, iks, off = oracle_cache(rng, n_list, 1)
+    ik, iks = ik.copy(), iks.copy()
+    iks[:700] = np.minimum(iks[:700].astype(np.int32) + 6, 254).astype(np.uint8)
+    a = int(off[2])
+    ik[a:a + 30000] = ik[a]
+    iks[a:a + 30000] = iks[a]
+    ws = L.Workspace()
+    for order in (list(range(5)), list(range(4, -1, -1))):
+        nl = [n_list[i] for i in order]
+        offs = np.asarray([off[i] for i in order], np.int64)
+        B = len(nl)
+        qF, qiF, wF = (np.stack([f(rng, h) for _ in range(B)]) for f, h in
+                       ((synth.latent_query, H), (synth.indexer_query, 16), (synth.head_weights, 16)))
+        topF, pool, outF, lseF = L.decode_layer(L.CSA2_FULL, dev(kv), dev(ik), dev(iks), dev(offs),
+                                                dev(np.asarray(nl, np.int32)), max(nl), dev(qF), q_idx=dev(qiF),
+                                                w=dev(wF), pool_k=pool_k, workspace=ws)
+        torch.cuda.synchronize()
+        topF, pool, outF, lseF = host(topF), host(pool), host(outF), host(lseF)
+        for b, n in enumerate(nl):
+            what = f"seq{order[b]} (n={n})"
+            if n == 0:
+                assert np.all(pool[b] == -1) and np.all(topF[b] == -1), what
+                continue
+            rows = slice(offs[b], offs[b] + n)
+            s = OI.scores(ik[rows], iks[rows], qiF[b], wF[b], 1)
+            check_topk(pool[b], OI.topk(s, np.arange(n), pool_k), lambda p: s[p], pool_k, f"pool {what}")
+            gp = pool[b][pool[b] >= 0]
+            check_topk(topF[b], OI.topk(s[gp], gp, 512), lambda p: s[p], 512, f"full {what}")
+            check_attention(kv[rows], topF[b], qF[b], outF[b], lseF[b], f"attention {what}")
+
+
 def test_decode128k_full_size():
     """32 sequences x 131072 tokens (65536 ratio-2 entries), one Full layer, as the benchmark runs it.
 
