@@ -5,6 +5,7 @@
 // ~position) orders by score descending, then position ascending, so the k
 // largest composites are the top-k of the selection order.
 #pragma once
+#include <type_traits>
 #include "codec_dev.h"
 #include "device.h"
 #include "kernels.h"
@@ -1021,41 +1022,88 @@ __device__ inline bool finish_direct_body(int b, const int32_t* __restrict__ n_e
       if (total <= (uint32_t)FIN_LDS_CANDS) {
         lc_used = true;
         // copy the lists in chunk order (wave v takes the FS chunks from
-        // FS v in each round of RL) and histogram the prefixes. A round's
-        // entries 64 .. 127 are requested with its first 64 (entry `lane` of
-        // round 0 is in v0 already), and the next round's first entries
-        // before this round's are stored, so a round waits for one round trip.
+        // FS v in each round of RL) and histogram the prefixes. The entries
+        // of RG rounds are requested at once, every load unconditional and
+        // inside its list's slot (round 0's first entries are in v0): with
+        // lists of at most 64 entries four rounds, else two rounds with their
+        // entries 64 .. 127; entries from 128 on are copied after the rounds.
         auto take = [&](uint64_t c, uint32_t at) {
           lc[at] = c;
           count_above_cmax(c);
         };
-        uint64_t vn[FS];
+        auto list_span = [&](int w, uint32_t* cnt_out) {
+          const int wc_ = min(w, (int)nw - 1);
+          const uint32_t a = loff[wc_];
+          *cnt_out = w < nw ? (wc_ + 1 < nw ? loff[wc_ + 1] : total) - a : 0u;
+          return a;
+        };
+        // RR: one round whose lists are dealt to the waves in turn (list
+        // wave + NWAVE s), all loads fresh; else wave v takes lists FS v ..
+        // FS v + FS - 1 of each round, round 0's first entries from v0
+        auto copy_rounds = [&](auto rg_tag, auto v2_tag, auto rr_tag) {
+          constexpr int RG = decltype(rg_tag)::value;
+          constexpr bool V2 = decltype(v2_tag)::value;
+          constexpr bool RR = decltype(rr_tag)::value;
+          auto list_of = [&](int r0, int g, int s) { return r0 + g * RL + (RR ? wave + NWAVE * s : FS * wave + s); };
+          for (int r0 = 0; r0 < nw; r0 += RG * RL) {
+            uint64_t v[RG][FS], v2[RG][FS];
+            // (requested in the order they are stored: the wait before each
+            // store then covers the loads ahead of it only)
 #pragma unroll
-        for (int s = 0; s < FS; ++s) vn[s] = v0[s];
-        for (int r0 = 0; r0 < nw; r0 += RL) {
-          uint64_t v[FS], v2[FS];
-          uint32_t cn[FS], of[FS];
-          int ws[FS];
+            for (int g = 0; g < RG; ++g)
 #pragma unroll
-          for (int s = 0; s < FS; ++s) {
-            const int w = r0 + FS * wave + s;
-            ws[s] = min(w, (int)nw - 1);
-            cn[s] = w < nw ? (ws[s] + 1 < nw ? loff[ws[s] + 1] : total) - loff[ws[s]] : 0u;
-            of[s] = loff[ws[s]];
-            v[s] = vn[s];
-            v2[s] = 64u + lane < cn[s] ? wc[(int64_t)ws[s] * CAND_CAP + 64 + lane] : 0ull;
+              for (int s = 0; s < FS; ++s) {
+                const int64_t row = (int64_t)min(list_of(r0, g, s), (int)nw - 1) * CAND_CAP;
+                const uint64_t x = wc[row + lane];
+                v[g][s] = (!RR && g == 0 && r0 == 0) ? v0[s] : x;
+              }
+            asm volatile("" ::: "memory");
+            if constexpr (V2) {
+#pragma unroll
+              for (int g = 0; g < RG; ++g)
+#pragma unroll
+                for (int s = 0; s < FS; ++s)
+                  v2[g][s] = wc[(int64_t)min(list_of(r0, g, s), (int)nw - 1) * CAND_CAP + 64 + lane];
+              asm volatile("" ::: "memory");
+            }
+            uint32_t cn[RG][FS], of[RG][FS];
+#pragma unroll
+            for (int g = 0; g < RG; ++g)
+#pragma unroll
+              for (int s = 0; s < FS; ++s) of[g][s] = list_span(list_of(r0, g, s), &cn[g][s]);
+#pragma unroll
+            for (int g = 0; g < RG; ++g)
+#pragma unroll
+              for (int s = 0; s < FS; ++s)
+                if ((uint32_t)lane < cn[g][s]) take(v[g][s], of[g][s] + lane);
+            if constexpr (V2) {
+#pragma unroll
+              for (int g = 0; g < RG; ++g)
+#pragma unroll
+                for (int s = 0; s < FS; ++s)
+                  if (64u + lane < cn[g][s]) take(v2[g][s], of[g][s] + 64 + lane);
+            }
           }
-          if (r0 + RL < nw) {
+        };
+        // (v0 is needed here: waiting for it before the rounds' loads keeps
+        // their wait counts exact)
 #pragma unroll
-            for (int s = 0; s < FS; ++s)
-              vn[s] = wc[(int64_t)min(r0 + RL + FS * wave + s, (int)nw - 1) * CAND_CAP + lane];
-          }
-#pragma unroll
-          for (int s = 0; s < FS; ++s) {
-            if ((uint32_t)lane < cn[s]) take(v[s], of[s] + lane);
-            if (64u + lane < cn[s]) take(v2[s], of[s] + 64 + lane);
-            for (uint32_t j = 128 + lane; j < cn[s]; j += 64) take(wc[(int64_t)ws[s] * CAND_CAP + j], of[s] + j);
-          }
+        for (int s = 0; s < FS; ++s) asm volatile("" ::"v"(v0[s]));
+        if (nw <= RL) {
+          copy_rounds(std::integral_constant<int, 1>{}, std::true_type{}, std::true_type{});
+        } else if ((flags & 2u) == 0) {
+          copy_rounds(std::integral_constant<int, 4>{}, std::false_type{}, std::false_type{});
+        } else {
+          copy_rounds(std::integral_constant<int, 2>{}, std::true_type{}, std::false_type{});
+        }
+        if (flags & 2u) {
+          for (int r0 = 0; r0 < nw; r0 += RL)
+            for (int s = 0; s < FS; ++s) {
+              const int w = r0 + FS * wave + s;
+              uint32_t c;
+              const uint32_t a = list_span(w, &c);
+              for (uint32_t j = 128 + lane; j < c; j += 64) take(wc[(int64_t)w * CAND_CAP + j], a + j);
+            }
         }
         __syncthreads();
         uint32_t tot;
