@@ -62,6 +62,9 @@ IndexerWs indexer_layout(int B, int64_t max_n, int k, int pool_k, int cand_strid
   if (L.slots < 1) L.slots = 1;
   L.bm_words = (L.slots + 31) / 32;
   L.nblk = (L.slots + csa2::kScoreChunk - 1) / csa2::kScoreChunk;
+  // (a candidate list's direct pass reports per chunk of kCandChunk slots)
+  const int64_t cblk = ((int64_t)cand_stride + csa2::kCandChunk - 1) / csa2::kCandChunk;
+  if (cblk > L.nblk) L.nblk = cblk;
   const bool thr = k > csa2::kDirectMaxK;          // the threshold path's regions
   const bool pl = pool_k > 0;                      // the pool lists
   size_t off = 0;

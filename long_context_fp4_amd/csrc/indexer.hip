@@ -140,6 +140,12 @@ __global__ __launch_bounds__(SC_THREADS) __attribute__((amdgpu_waves_per_eu(CAND
     float* __restrict__ scores, int64_t sstride, SelBufs sb, int K, int store_scores, int pool_k, int Tq) {
   static_assert(MQ == 1 || (!CAND && SEL == SEL_DIRECT && !QMX), "the multi-query pass is a direct Full pass");
   static_assert(MQ <= SC_THREADS / 64, "one wave per query in the multi-query tail");
+  // a candidate-list direct pass takes chunks of kCandChunk slots: more
+  // workgroups gather the listed rows, and the finish gets short lists
+  constexpr bool SMALL = CAND && SEL == SEL_DIRECT;
+  constexpr int SPAN = SMALL ? kCandChunk : SC_SPAN;      // slots of this workgroup
+  constexpr int CHUNK = SMALL ? kCandChunk : SC_CHUNK;    // slots of one selection chunk
+  static_assert(SPAN % (16 * (SC_THREADS / 64)) == 0 && SPAN <= 4 * SC_THREADS, "whole tiles per wave");
   // histogram with 16-bit counts (two bins per word) + staged scores: 12 KiB,
   // so that eight workgroups fit one compute unit
   __shared__ __attribute__((aligned(16))) uint32_t lbuf[NBINS / 2 + MQ * SC_SPAN];
@@ -210,10 +216,10 @@ __global__ __launch_bounds__(SC_THREADS) __attribute__((amdgpu_waves_per_eu(CAND
     n_pos = max(n_pos, npq[m]);
   }
   const int64_t nslots = CAND ? (int64_t)cand_stride : n_pos;
-  const int64_t start = (int64_t)blockIdx.x * SC_SPAN;
+  const int64_t start = (int64_t)blockIdx.x * SPAN;
   if (start >= nslots) return;
   if (CAND && n_pos <= 0 && !LISTS) return;        // no listed position can be valid (lists: still written)
-  const int end = (int)min((int64_t)SC_SPAN, nslots - start);   // slots of this workgroup
+  const int end = (int)min((int64_t)SPAN, nslots - start);   // slots of this workgroup
   // the sequence's rows: a uniform base plus a 32-bit byte offset per lane
   // (positions below 2^26, checked on the host), one address register per load
   const uint8_t* ikb = ik + row_base * 64;
@@ -243,22 +249,16 @@ __global__ __launch_bounds__(SC_THREADS) __attribute__((amdgpu_waves_per_eu(CAND
   }
   if (tid < 16 * MQ) lw[tid] = wv;
   if (SEL != SEL_NONE && tid == 0) sbs = sb;
+  // CAND: each wave's tiles of listed rows, requested before the rule that
+  // decides which slots are used is known
+  constexpr int CT = SPAN / (16 * (SC_THREADS / 64));      // tiles per wave
+  u32x4_t ccw[CAND ? CT : 1];
+  uint32_t csb[CAND ? CT : 1];
   if constexpr (CAND) {
-    // which of this workgroup's slots the rule uses: the largest in-range
-    // position listed before the workgroup's first slot, then a scan of the
-    // workgroup's own slots (thread t: slots 4t .. 4t+3)
-    uint32_t pm = 0;                                   // position + 1, 0 = none
-    auto take = [&](int32_t c) { if (c >= 0 && c < n_pos) pm = max(pm, (uint32_t)c + 1u); };
-    if ((cand_stride & 3) == 0) {                      // 16-byte rows: four entries per load
-#pragma unroll 8
-      for (int64_t i = 4 * tid; i < start; i += 4 * SC_THREADS) {
-        const u32x4_t v = *(const u32x4_t*)(crow + i);
-        take((int32_t)v[0]); take((int32_t)v[1]); take((int32_t)v[2]); take((int32_t)v[3]);
-      }
-    } else {
-#pragma unroll 8
-      for (int64_t i = tid; i < start; i += SC_THREADS) take(crow[i]);
-    }
+    // this workgroup's listed positions (thread t: slots 4t .. 4t+3); a slot
+    // reads the row of its position when that lies in [0, n), else row 0 of
+    // the sequence, and every tile of the wave is requested at once (one
+    // memory round trip for the gathers, overlapping the rule's scan)
     uint32_t pp[4], lmax = 0;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -267,6 +267,32 @@ __global__ __launch_bounds__(SC_THREADS) __attribute__((amdgpu_waves_per_eu(CAND
       pp[q] = (c >= 0 && c < n_pos) ? (uint32_t)c + 1u : 0u;
       lmax = max(lmax, pp[q]);
     }
+    // (with them, the rule's input: the largest in-range position listed
+    // before the workgroup's first slot)
+    uint32_t pm = 0;                                   // position + 1, 0 = none
+    auto take = [&](int32_t c) { if (c >= 0 && c < n_pos) pm = max(pm, (uint32_t)c + 1u); };
+    if ((cand_stride & 3) == 0) {                      // 16-byte rows: four entries per load
+#pragma unroll 16
+      for (int64_t i = 4 * tid; i < start; i += 4 * SC_THREADS) {
+        const u32x4_t v = *(const u32x4_t*)(crow + i);
+        take((int32_t)v[0]); take((int32_t)v[1]); take((int32_t)v[2]); take((int32_t)v[3]);
+      }
+    } else {
+#pragma unroll 8
+      for (int64_t i = tid; i < start; i += SC_THREADS) take(crow[i]);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) lpos[4 * tid + q] = pp[q] > 0u ? (int32_t)pp[q] - 1 : 0;
+    __syncthreads();
+    if (n_pos > 0) {
+#pragma unroll
+      for (int u = 0; u < CT; ++u) {
+        const uint32_t p = (uint32_t)lpos[16 * wave + 64 * u + n];
+        ccw[u] = __builtin_nontemporal_load((const u32x4_t*)(ikb + (p * 64u + 16u * g)));
+        csb[u] = iksb[p * 4u + (uint32_t)g];
+      }
+    }
+    // which slots the rule uses: a scan of the workgroup's own slots
     pm = wave_max_u32(pm);
     uint32_t incl = lmax;                              // inclusive max over this wave's threads
 #pragma unroll
@@ -289,9 +315,6 @@ __global__ __launch_bounds__(SC_THREADS) __attribute__((amdgpu_waves_per_eu(CAND
       m4 |= (pp[q] > run ? 1u : 0u) << q;
       run = max(run, pp[q]);
     }
-    // the row each slot reads (row 0 of the sequence for an unused slot)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) lpos[4 * tid + q] = ((m4 >> q) & 1u) ? (int32_t)pp[q] - 1 : 0;
     // 8 threads per word: gather their 4-bit masks
     uint32_t wd = m4 << (4 * (tid & 7));
     wd |= (uint32_t)__shfl_xor((int)wd, 1, 64);
@@ -354,8 +377,8 @@ __global__ __launch_bounds__(SC_THREADS) __attribute__((amdgpu_waves_per_eu(CAND
   const int bq = vq[mq];                             // the selection's sequence (or query) index
   const int64_t npos_q = npq[mq];
   const int end_q = MQ == 1 ? end : (int)max((int64_t)0, min((int64_t)SC_SPAN, npos_q - start));
-  const int soff = sub * SC_CHUNK;
-  const int send = min(SC_CHUNK, end_q - soff);      // slots of this chunk
+  const int soff = sub * CHUNK;
+  const int send = min(CHUNK, end_q - soff);         // slots of this chunk
   if (send <= 0) return;
   __syncthreads();                                   // its scores are staged; the previous tail is done
   const float* lss = lsc + mq * SC_SPAN + soff;
@@ -374,11 +397,11 @@ __global__ __launch_bounds__(SC_THREADS) __attribute__((amdgpu_waves_per_eu(CAND
   if (SEL == SEL_NONE) return;
   const SelBufs sbl = sbs;
   const int64_t nref = CAND ? nslots : npos_q;       // slots the shares refer to
-  const int64_t nwg = (nref + SC_CHUNK - 1) / SC_CHUNK;
+  const int64_t nwg = (nref + CHUNK - 1) / CHUNK;
   // local budget: a multiple of the chunk's expected share of the top-K plus a
   // margin, so that the highest cutoff over the workgroups still leaves at
   // least K keys of the sequence above it (the finish checks this)
-  const int64_t share = ((int64_t)K * SC_CHUNK + nref - 1) / nref;
+  const int64_t share = ((int64_t)K * CHUNK + nref - 1) / nref;
   int64_t budget64 = LISTS ? 2 * share + 16 : 4 * share + 32;
   if (LISTS) budget64 = min(budget64, max((int64_t)8, (int64_t)FIN_LDS_CANDS / nwg));
   const uint32_t budget = (uint32_t)min(budget64, (int64_t)send);
@@ -446,7 +469,7 @@ __global__ __launch_bounds__(SC_THREADS) __attribute__((amdgpu_waves_per_eu(CAND
     // pool budget: the same rule for the pool_k best
     uint32_t budget_p = 0;
     if (SEL == SEL_POOL) {
-      const int64_t share_p = ((int64_t)pool_k * SC_CHUNK + nref - 1) / nref;
+      const int64_t share_p = ((int64_t)pool_k * CHUNK + nref - 1) / nref;
       budget_p = (uint32_t)min(2 * share_p + 16, (int64_t)send);
     }
     if (wave == 0) {
@@ -553,24 +576,11 @@ __global__ __launch_bounds__(SC_THREADS) __attribute__((amdgpu_waves_per_eu(CAND
     const float unused = LISTS ? __uint_as_float(0xFFFFFFFFu) : 0.0f;
     for (int i = tid; i < end; i += SC_THREADS) lsc[i] = unused;
   } else {
-    // listed positions: every tile of the wave is requested at once (the
-    // rows come from lpos, written by the scan above), so the gathers cost
-    // one memory round trip; unused slots read row 0 of the sequence and hold
-    // the key 0
+    // listed positions: the tiles requested above; unused slots hold the key 0
     const float unused = __uint_as_float(0xFFFFFFFFu);     // key 0
-    constexpr int CT = SC_SPAN / (16 * (SC_THREADS / 64)); // tiles per wave
-    u32x4_t cwl[CT];
-    uint32_t sbl[CT];
 #pragma unroll
     for (int u = 0; u < CT; ++u) {
-      const int i = 16 * wave + 64 * u + n;                 // < SC_SPAN
-      const uint32_t p = (uint32_t)lpos[i];
-      cwl[u] = __builtin_nontemporal_load((const u32x4_t*)(ikb + (p * 64u + 16u * g)));
-      sbl[u] = iksb[p * 4u + (uint32_t)g];
-    }
-#pragma unroll
-    for (int u = 0; u < CT; ++u) {
-      const float sc = score_tile(cwl[u], sbl[u]);
+      const float sc = score_tile(ccw[u], csb[u]);
       const int ls = 16 * wave + 64 * u + n;
       const bool ok = ls < end && ((used_bm[ls >> 5] >> (ls & 31)) & 1u);
       if (g == 0 && ls < end) lsc[ls] = ok ? sc : (LISTS ? unused : 0.0f);
@@ -965,7 +975,8 @@ hipError_t launch_score(const uint8_t* ik, const uint8_t* iks, const int64_t* en
   const bool store = store_scores || cand || (sel != SEL_DIRECT && sel != SEL_POOL);
   const int64_t nslots = cand ? cand_stride : max_n;
   if (nslots <= 0) return hipSuccess;
-  const int64_t nx = (nslots + SC_SPAN - 1) / SC_SPAN;
+  const int span = (cand && sel == SEL_DIRECT) ? kCandChunk : SC_SPAN;   // the kernel's SPAN
+  const int64_t nx = (nslots + span - 1) / span;
   dim3 grid((unsigned)nx, (unsigned)B), block(SC_THREADS);
   const bool qmx = (mode & kScoreQmx8) != 0;
   const int base = mode & ~kScoreQmx8;

@@ -54,6 +54,7 @@ constexpr int kDirectMaxK = 512;      // largest k the score pass selects by its
 constexpr int kFinMaxWg = 2048;       // score workgroups per sequence whose slots the finish reads
 constexpr int kFinLdsCands = 12288;   // candidates the direct finish holds in LDS
 constexpr int kPoolCap = kScoreChunk;  // pool candidates a score workgroup may report (its whole chunk)
+constexpr int kCandChunk = 256;      // slots per workgroup (and selection chunk) of a candidate-list direct pass
 
 // Workspace views used by the score pass's selection (per-sequence strides).
 struct SelBufs {

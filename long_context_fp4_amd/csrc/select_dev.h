@@ -666,7 +666,9 @@ __device__ inline void finish_prefetch(FinPrefetch<NT>& pf, int b, int64_t max_n
                                        const ScoreSrc& src) {
   constexpr int FS = FinPrefetch<NT>::FS;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t nw_max = ((src.cand ? max(max_n, (int64_t)src.cand_stride) : max_n) + SC_CHUNK - 1) / SC_CHUNK;
+  // (a candidate list's direct pass has chunks of kCandChunk slots)
+  const int64_t nw_max = src.cand ? ((int64_t)src.cand_stride + kCandChunk - 1) / kCandChunk
+                                  : (max_n + SC_CHUNK - 1) / SC_CHUNK;
   const uint64_t* hd = sb.hdr + (int64_t)b * sb.hdr_stride;
   pf.h0 = tid < nw_max ? hd[tid] : 0ull;
   pf.hw = lane < nw_max ? hd[lane] : 0ull;
@@ -877,8 +879,9 @@ __device__ inline bool finish_direct_body(int b, const int32_t* __restrict__ n_e
     return false;
   }
   const int64_t n_slots = lst ? (int64_t)src.cand_stride : n_pos;
-  const int64_t nw = (n_slots + SC_CHUNK - 1) / SC_CHUNK;
-  if (!lst && nw <= RL) {
+  const int chunk = lst ? kCandChunk : SC_CHUNK;     // slots per chunk list
+  const int64_t nw = (n_slots + chunk - 1) / chunk;
+  if (nw <= RL) {
     const int r = finish_fast64<NT>((int)nw, K, pf.hw, v0, L, emit);
     if (r > 0) return false;
     if (r < 0) {
