@@ -1029,7 +1029,8 @@ __device__ inline bool finish_direct_body(int b, const int32_t* __restrict__ n_e
         // of RG rounds are requested at once, every load unconditional and
         // inside its list's slot (round 0's first entries are in v0): with
         // lists of at most 64 entries four rounds, else two rounds with their
-        // entries 64 .. 127; entries from 128 on are copied after the rounds.
+        // entries 64 .. 127 (half that with 1024 threads); entries from 128
+        // on are copied after the rounds.
         auto take = [&](uint64_t c, uint32_t at) {
           lc[at] = c;
           count_above_cmax(c);
@@ -1094,10 +1095,10 @@ __device__ inline bool finish_direct_body(int b, const int32_t* __restrict__ n_e
         for (int s = 0; s < FS; ++s) asm volatile("" ::"v"(v0[s]));
         if (nw <= RL) {
           copy_rounds(std::integral_constant<int, 1>{}, std::true_type{}, std::true_type{});
-        } else if ((flags & 2u) == 0) {
-          copy_rounds(std::integral_constant<int, 4>{}, std::false_type{}, std::false_type{});
+        } else if ((flags & 2u) == 0) {   // (half the rounds at once in the 1024-thread finish: registers)
+          copy_rounds(std::integral_constant<int, NT <= 512 ? 4 : 2>{}, std::false_type{}, std::false_type{});
         } else {
-          copy_rounds(std::integral_constant<int, 2>{}, std::true_type{}, std::false_type{});
+          copy_rounds(std::integral_constant<int, NT <= 512 ? 2 : 1>{}, std::true_type{}, std::false_type{});
         }
         if (flags & 2u) {
           for (int r0 = 0; r0 < nw; r0 += RL)
@@ -1109,6 +1110,30 @@ __device__ inline bool finish_direct_body(int b, const int32_t* __restrict__ n_e
             }
         }
         __syncthreads();
+        if (total > (uint32_t)(64 * FIN_NV * NWAVE)) {
+          // more than the register selection holds: keep only the keys at or
+          // above cmax (no other key can be among the K best when this path
+          // applies), in place and in order (thread t: entries PER t ..)
+          constexpr int PER = FIN_LDS_CANDS / NT;
+          const uint32_t a = (uint32_t)tid * PER;
+          uint64_t kv[PER];
+          uint32_t km = 0, cnt = 0;
+#pragma unroll
+          for (int j = 0; j < PER; ++j) {
+            const uint32_t i = a + j;
+            kv[j] = i < total ? lc[i] : 0ull;
+            const bool keep = i < total && p20_of(kv[j]) >= cmax;
+            km |= (keep ? 1u : 0u) << j;
+            cnt += keep ? 1u : 0u;
+          }
+          uint32_t kept;
+          uint32_t d = block_exclusive_scan(cnt, scan_tmp, &kept);   // (its barriers follow every read)
+#pragma unroll
+          for (int j = 0; j < PER; ++j)
+            if ((km >> j) & 1u) lc[d++] = kv[j];
+          total = kept;
+          __syncthreads();
+        }
         uint32_t tot;
         hist_kth_bin<NT>(hist, (uint32_t)K, scan_tmp, ctl, &tot);
         if (ctl[0] != 0xFFFFFFFFu) {
