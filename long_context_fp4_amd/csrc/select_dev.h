@@ -1035,10 +1035,12 @@ __device__ inline bool finish_direct_body(int b, const int32_t* __restrict__ n_e
           lc[at] = c;
           count_above_cmax(c);
         };
+        // (both offsets read unconditionally, so a round's reads go out together)
         auto list_span = [&](int w, uint32_t* cnt_out) {
-          const int wc_ = min(w, (int)nw - 1);
-          const uint32_t a = loff[wc_];
-          *cnt_out = w < nw ? (wc_ + 1 < nw ? loff[wc_ + 1] : total) - a : 0u;
+          const uint32_t a = loff[min(w, (int)nw - 1)];
+          const uint32_t e1 = loff[min(w + 1, (int)nw - 1)];
+          const uint32_t e = w + 1 < nw ? e1 : total;
+          *cnt_out = w < nw ? e - a : 0u;
           return a;
         };
         // RR: one round whose lists are dealt to the waves in turn (list
