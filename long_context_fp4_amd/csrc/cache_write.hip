@@ -19,16 +19,14 @@
 // writes its 16 rows (4608 + 1024 contiguous bytes) with 16-byte stores.
 //
 // Bit-exactness: the merge is evaluated with separate float32 roundings
-// (contraction is switched off for this file), the scale division is the
-// correctly rounded float32 division, and the E2M1 code of x/s is decided by
-// exact comparisons of |x| against t*s for the seven rounding thresholds t of
-// the E2M1 grid. t*s is exact in float32 (t has at most 3 significant bits,
-// an E4M3 scale at most 4), and for |x| and s in float32 no quotient |x|/s can
-// lie strictly between a threshold and the float32 rounding boundary next to
-// it (the smallest gap |x|/s - t is ulp(|x|)/s, which exceeds half an ulp of t
-// because the scale's significand is below 2), so these comparisons give the
-// same code as rounding the float32 quotient. Thresholds where the tie goes
-// down use '>', those where it goes up use '>='.
+// (contraction is switched off for this file). The E2M1 code of a latent
+// value x is the nearest-even E2M1 value (saturating at 6) of the correctly
+// rounded float32 quotient x / s: the quotient comes from one multiply by the
+// correctly rounded reciprocal of s and Markstein's correction step (two fused
+// multiply-adds), and gfx950's f32 -> FP4 conversion (nearest even, ties to
+// even, saturating, sign kept also for zero; checked against the rounding
+// thresholds of every E4M3 scale) turns two quotients into one code byte. An
+// indexer value is scaled by 2^-X exactly (ldexp) and converted the same way.
 #include "device.h"
 #include "codec_dev.h"
 #include <math.h>
@@ -40,18 +38,19 @@ namespace csa2 {
 constexpr int CW_ENTRIES = 16;
 constexpr int CW_THREADS = 320;
 
-// E2M1 magnitude code of |x| for block scale s (s > 0), via the thresholds
-// 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5 times s.
-struct Thresholds {
-  float t0, t1, t2, t3, t4, t5, t6;
-  __device__ __forceinline__ explicit Thresholds(float s)
-      : t0(0.25f * s), t1(0.75f * s), t2(1.25f * s), t3(1.75f * s),
-        t4(2.5f * s), t5(3.5f * s), t6(5.0f * s) {}
-  __device__ __forceinline__ uint32_t mag(float a) const {
-    return (uint32_t)(a > t0) + (uint32_t)(a >= t1) + (uint32_t)(a > t2) + (uint32_t)(a >= t3) +
-           (uint32_t)(a > t4) + (uint32_t)(a >= t5) + (uint32_t)(a > t6);
-  }
-};
+// The correctly rounded quotient x / s for an E4M3 scale s > 0, given
+// y = 1 / s correctly rounded: q = x y; t = q s - x (exact, one fused
+// multiply-add); q - t y is then the correctly rounded quotient (Markstein's
+// correction step; it holds whenever no intermediate underflows, and an
+// underflow only touches quotients far below the first rounding threshold).
+// The order of the two fused operations keeps the sign of a zero quotient.
+// No overflow: |x| is at most the block maximum, so |x| y stays below 2^128
+// for every scale the block maximum can round to.
+__device__ __forceinline__ float quotient(float x, float s, float y) {
+  const float q = x * y;
+  const float t = fmaf(q, s, -x);
+  return fmaf(-t, y, q);
+}
 
 // Lane mapping. Latent (waves 0-3): 16 lanes per entry; lane p takes the 8
 // channels 128q + 8p .. +7 for q = 0..3, so each 16-byte load instruction of
@@ -142,14 +141,13 @@ __device__ __forceinline__ void merge_pack(const LaneMap& L, bool store, int m, 
     if (L.latent) {
       float s;
       const uint32_t sb = e4m3fn_rne(amax / 6.0f, &s);
-      Thresholds th(s);
+      // codes of the correctly rounded quotients x / s (two channels per conversion)
+      const float y = 1.0f / s;
       uint32_t word = 0;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const float x = acc[c];
-        const uint32_t code = th.mag(fabsf(x)) | ((__float_as_uint(x) >> 28) & 8u);
-        word |= code << (4 * c);
-      }
+      word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, quotient(acc[0], s, y), quotient(acc[1], s, y), 1.0f, 0);
+      word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, quotient(acc[2], s, y), quotient(acc[3], s, y), 1.0f, 1);
+      word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, quotient(acc[4], s, y), quotient(acc[5], s, y), 1.0f, 2);
+      word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, quotient(acc[6], s, y), quotient(acc[7], s, y), 1.0f, 3);
       if (!(s > 0.0f)) word = 0u;
       // the scale bytes of blocks 8q + 2k and 8q + 2k + 1 (lanes 4k and
       // 4k + 2) meet in lane 4k, which stores them as one 16-bit word
@@ -160,22 +158,20 @@ __device__ __forceinline__ void merge_pack(const LaneMap& L, bool store, int m, 
       }
     } else {
       uint32_t xbyte = 0;
-      float s = 0.0f;
       if (amax > 0.0f) {
         const int X = floor_log2(amax) - 2;
         int bb = X + 127;
         bb = bb < 0 ? 0 : (bb > 254 ? 254 : bb);
         xbyte = (uint32_t)bb;
-        s = ldexpf(1.0f, bb - 127);
       }
-      Thresholds th(s);
+      // x * 2^-X is exact (the values lie below 8: no overflow; an underflow
+      // only touches values far below the first rounding threshold)
+      const int nx = 127 - (int)xbyte;
       uint32_t word = 0;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const float x = acc[c];
-        const uint32_t code = th.mag(fabsf(x)) | ((__float_as_uint(x) >> 28) & 8u);
-        word |= code << (4 * c);
-      }
+      word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, ldexpf(acc[0], nx), ldexpf(acc[1], nx), 1.0f, 0);
+      word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, ldexpf(acc[2], nx), ldexpf(acc[3], nx), 1.0f, 1);
+      word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, ldexpf(acc[4], nx), ldexpf(acc[5], nx), 1.0f, 2);
+      word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, ldexpf(acc[6], nx), ldexpf(acc[7], nx), 1.0f, 3);
       if (!(amax > 0.0f)) word = 0u;
       xbytes |= xbyte << (8 * q);
       if (store) *(uint32_t*)(idx_e + 16 * q + 4 * p) = word;
