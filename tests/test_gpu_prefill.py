@@ -87,3 +87,36 @@ def test_prefill_multi_query_pass_matches_oracle():
             err = attn_rel_err(out[b, t], ro)
             assert np.all(err <= ATTN_REL_TOL), f"seq {b} query {t}: max rel err {err.max():.3g}"
             assert np.all(np.abs(lse[b, t] - rl) <= 2e-3), f"seq {b} query {t}: lse"
+
+
+def test_prefill_128_queries():
+    """128 query tokens of one sequence in one call (32 query groups of the
+    multi-query pass), every 37th token position of the sequence's last ~4.7K,
+    so consecutive queries see different numbers of entries and the visible
+    ranges end inside chunks and at chunk boundaries alike."""
+    import torch
+    import long_context_fp4_amd as L
+    rng = np.random.default_rng(128)
+    m, k, H, T = 2, 512, 16, 70001
+    w_lat = synth.merge_weights(rng, m, 512)
+    w_idx = synth.merge_weights(rng, m, 128)
+    kv, ik, iks = OC.cache_write(synth.hidden_host(rng, (T, 512)), synth.hidden_host(rng, (T, 128)), w_lat, w_idx, m)
+    E = kv.shape[0]
+    Tq = 128
+    pos = (T - 1 - 37 * np.arange(Tq)[::-1]).astype(np.int64)[None]
+    q = np.stack([synth.latent_query(rng, H) for _ in range(Tq)])[None]
+    qi = np.stack([synth.indexer_query(rng, 16) for _ in range(Tq)])[None]
+    w = np.stack([synth.head_weights(rng, 16) for _ in range(Tq)])[None]
+    top, out, lse = L.prefill_layer(dev(kv), dev(ik), dev(iks), dev(np.zeros(1, np.int64)),
+                                    dev(np.array([E], np.int32)), E, m, dev(pos), dev(qi), dev(q), w=dev(w), k=k)
+    torch.cuda.synchronize()
+    top, out, lse = host(top), host(out), host(lse)
+    for t in range(Tq):
+        nv = min(E, (int(pos[0, t]) + 1) // m)
+        s = OI.scores(ik[:nv], iks[:nv], qi[0, t], w[0, t], 1)
+        want = OI.topk(s, np.arange(nv), k)
+        check_topk(top[0, t], want, lambda p: s[p], k, f"query {t}")
+        ro, rl = OA.sparse_attention(kv, top[0, t], q[0, t])
+        err = attn_rel_err(out[0, t], ro)
+        assert np.all(err <= ATTN_REL_TOL), f"query {t}: max rel err {err.max():.3g}"
+        assert np.all(np.abs(lse[0, t] - rl) <= 2e-3), f"query {t}: lse"
