@@ -99,6 +99,7 @@ __device__ __forceinline__ void digit_kth(const uint32_t* h, uint32_t need, uint
 // agree on the bits above top_shift + 7. On return the composites c with
 // (c & *mask_out) >= *prefix_out are exactly the `need` largest. h holds 512
 // words and ctl 8 words of LDS. All threads of the workgroup must call it.
+template <int RU = 1>
 __device__ inline void radix_select_u64(const uint64_t* v, uint32_t n, uint32_t need, int top_shift,
                                  uint32_t* h, uint32_t* ctl, uint64_t* prefix_out, uint64_t* mask_out) {
   // h: two 256-bin histograms and ctl: two 4-word results, alternating by pass,
@@ -109,9 +110,13 @@ __device__ inline void radix_select_u64(const uint64_t* v, uint32_t n, uint32_t 
   __syncthreads();
   for (int p = 0;; p ^= 1) {
     uint32_t* hp = h + 256 * p;
-    for (uint32_t i = threadIdx.x; i < n; i += blockDim.x) {
-      const uint64_t c = v[i];
-      if ((c & pmask) == prefix) atomicAdd(&hp[(uint32_t)(c >> shift) & 255u], 1u);
+    for (uint32_t i0 = threadIdx.x; i0 < n; i0 += RU * blockDim.x) {   // RU requested at once
+      uint64_t x[RU];
+#pragma unroll
+      for (int u = 0; u < RU; ++u) x[u] = v[min(i0 + u * blockDim.x, n - 1)];
+#pragma unroll
+      for (int u = 0; u < RU; ++u)
+        if (i0 + u * blockDim.x < n && (x[u] & pmask) == prefix) atomicAdd(&hp[(uint32_t)(x[u] >> shift) & 255u], 1u);
     }
     __syncthreads();
     if (threadIdx.x < 64) digit_kth(hp, need, ctl + 4 * p);
@@ -144,9 +149,18 @@ __device__ __forceinline__ uint32_t wave_append(bool take, uint32_t* counter) {
 // Top shift for radix_select_u64 over n composites at v: the 8-bit digit that
 // holds the highest bit in which any two composites differ (bits above it are
 // common to all of them). All threads of the workgroup must call it.
+// RU values per thread requested at once (a clamped repeat changes neither
+// the OR nor the AND).
+template <int RU = 1>
 __device__ inline int radix_top_shift(const uint64_t* v, uint32_t n, uint64_t* red) {
   uint64_t o = 0, a = ~0ull;
-  for (uint32_t i = threadIdx.x; i < n; i += blockDim.x) { o |= v[i]; a &= v[i]; }
+  for (uint32_t i0 = threadIdx.x; i0 < n; i0 += RU * blockDim.x) {
+    uint64_t x[RU];
+#pragma unroll
+    for (int u = 0; u < RU; ++u) x[u] = v[min(i0 + u * blockDim.x, n - 1)];
+#pragma unroll
+    for (int u = 0; u < RU; ++u) { o |= x[u]; a &= x[u]; }
+  }
   o = ((uint64_t)wave_or_u32((uint32_t)(o >> 32)) << 32) | wave_or_u32((uint32_t)o);
   a = ((uint64_t)wave_and_u32((uint32_t)(a >> 32)) << 32) | wave_and_u32((uint32_t)a);
   const int nw = blockDim.x >> 6, lane = threadIdx.x & 63;   // at most 16 waves; red holds 32 words
@@ -497,24 +511,40 @@ __device__ inline uint32_t wave_count_prefix(uint32_t cnt, uint32_t* tmp, uint32
   return base;
 }
 
-template <typename Pred, typename Emit>
+// OC_U > 1: the predicate is evaluated for OC_U steps of 64 slots at once (at
+// clamped, in-range slots, so whatever it reads from memory is requested
+// together); it must have no side effects.
+template <int OC_U = 1, typename Pred, typename Emit>
 __device__ inline uint32_t ordered_compact(uint32_t n, Pred pred, Emit emit, uint32_t* tmp) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const uint32_t span = (n + 64 * nw - 1) / (64 * nw) * 64;
   const uint32_t lo = min((uint32_t)wave * span, n), hi = min(lo + span, n);
+  auto preds = [&](uint32_t i0, bool (&p)[OC_U]) {
+#pragma unroll
+    for (int u = 0; u < OC_U; ++u) {
+      const uint32_t i = i0 + 64 * u + lane;
+      const bool v = pred(min(i, hi - 1));
+      p[u] = i < hi && v;
+    }
+  };
   uint32_t cnt = 0;
-  for (uint32_t i0 = lo; i0 < hi; i0 += 64) {
-    const uint32_t i = i0 + lane;
-    cnt += (uint32_t)__popcll(__ballot(i < hi && pred(i)));
+  for (uint32_t i0 = lo; i0 < hi; i0 += 64 * OC_U) {
+    bool p[OC_U];
+    preds(i0, p);
+#pragma unroll
+    for (int u = 0; u < OC_U; ++u) cnt += (uint32_t)__popcll(__ballot(p[u]));
   }
   uint32_t total;
   uint32_t base = wave_count_prefix(cnt, tmp, &total);
-  for (uint32_t i0 = lo; i0 < hi; i0 += 64) {
-    const uint32_t i = i0 + lane;
-    const bool p = i < hi && pred(i);
-    const uint64_t m = __ballot(p);
-    if (p) emit(i, base + (uint32_t)__popcll(m & ((1ull << lane) - 1ull)));
-    base += (uint32_t)__popcll(m);
+  for (uint32_t i0 = lo; i0 < hi; i0 += 64 * OC_U) {
+    bool p[OC_U];
+    preds(i0, p);
+#pragma unroll
+    for (int u = 0; u < OC_U; ++u) {
+      const uint64_t m = __ballot(p[u]);
+      if (p[u]) emit(i0 + 64 * u + lane, base + (uint32_t)__popcll(m & ((1ull << lane) - 1ull)));
+      base += (uint32_t)__popcll(m);
+    }
   }
   return total;
 }
@@ -566,28 +596,64 @@ __device__ inline void fallback_select(int b, int64_t n_pos, int K, float* sall,
     __syncthreads();
     QueryMx qm;
     if (qmx) qm = query_mx_operand(lq, lane);
-    for (int64_t t0 = 16 * wave; t0 < n_pos; t0 += 16 * NWAVE) {
-      const uint32_t p = (uint32_t)min(t0 + n, n_pos - 1);
-      const u32x4_t cw = *(const u32x4_t*)(ikb + ((uint64_t)p * 64u + 16u * g));
-      const uint32_t sbyte = iksb[(uint64_t)p * 4u + (uint32_t)g];
-      float sc;
-      if (qmx) sc = base == 0 ? score_tile_mx<0>(qm, cw, sbyte, lwf, g) : score_tile_mx<1>(qm, cw, sbyte, lwf, g);
-      else sc = base == 0 ? score_tile_fn<0>(qa, cw, sbyte, lwf, g) : score_tile_fn<1>(qa, cw, sbyte, lwf, g);
-      if (g == 0 && t0 + n < n_pos) sall[t0 + n] = sc;
+    // (u tiles of a wave requested at once, at clamped in-range rows; the
+    // exact variants FB_U deep, the quantized-query ones one tile at a time)
+    auto rescore = [&](auto u_tag, auto tile) {
+      constexpr int U = decltype(u_tag)::value;
+      for (int64_t t0 = 16 * wave; t0 < n_pos; t0 += 16 * NWAVE * U) {
+        u32x4_t cw[U];
+        uint32_t sbyte[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const uint32_t p = (uint32_t)min(t0 + 16 * NWAVE * u + n, n_pos - 1);
+          cw[u] = *(const u32x4_t*)(ikb + ((uint64_t)p * 64u + 16u * g));
+          sbyte[u] = iksb[(uint64_t)p * 4u + (uint32_t)g];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const float sc = tile(cw[u], sbyte[u]);
+          const int64_t at = t0 + 16 * NWAVE * u + n;
+          if (g == 0 && at < n_pos) sall[at] = sc;
+        }
+      }
+    };
+    constexpr int FB_U = NT <= 512 ? 8 : 4;
+    using Deep = std::integral_constant<int, FB_U>;
+    using One = std::integral_constant<int, 1>;
+    if (qmx) {
+      if (base == 0) rescore(One{}, [&](const u32x4_t c, uint32_t sb) { return score_tile_mx<0>(qm, c, sb, lwf, g); });
+      else rescore(One{}, [&](const u32x4_t c, uint32_t sb) { return score_tile_mx<1>(qm, c, sb, lwf, g); });
+    } else {
+      if (base == 0) rescore(Deep{}, [&](const u32x4_t c, uint32_t sb) { return score_tile_fn<0>(qa, c, sb, lwf, g); });
+      else rescore(Deep{}, [&](const u32x4_t c, uint32_t sb) { return score_tile_fn<1>(qa, c, sb, lwf, g); });
     }
     __threadfence_block();                         // this workgroup reads them back
   }
   __syncthreads();
   for (int i = tid; i < NBINS; i += NT) hist[i] = 0;
   __syncthreads();
-  // (a candidate list's unused slots hold the key 0, which no score has)
+  // (a candidate list's unused slots hold the key 0, which no score has).
+  // FB_H scores per thread are requested at once; the lanes of a wave whose
+  // key falls in the bin of its first counted lane add with one atomic (ties)
+  constexpr int FB_H = 4;
   const uint32_t n_src = (uint32_t)n_slots;
-  uint32_t nvalid = 0;
-  for (uint32_t i = tid; i < n_src; i += NT) {
-    const uint32_t key = score_key(sall[i]);
-    if (!lst || key != 0u) {
-      atomicAdd(&hist[key >> BIN_SHIFT], 1u);
-      ++nvalid;
+  for (uint32_t i0 = 0; i0 < n_src; i0 += NT * FB_H) {
+    float sv[FB_H];
+#pragma unroll
+    for (int u = 0; u < FB_H; ++u) sv[u] = sall[min(i0 + NT * u + tid, n_src - 1)];
+#pragma unroll
+    for (int u = 0; u < FB_H; ++u) {
+      const uint32_t key = score_key(sv[u]);
+      const bool ok = i0 + NT * u + tid < n_src && (!lst || key != 0u);
+      const uint32_t bin = key >> BIN_SHIFT;
+      const uint64_t okm = __ballot(ok);
+      if (okm) {
+        const int leader = __ffsll((long long)okm) - 1;
+        const uint32_t b0 = readlane_u32(bin, leader);
+        const uint64_t same = __ballot(ok && bin == b0);
+        if (lane == leader) atomicAdd(&hist[b0], (uint32_t)__popcll(same));
+        if (ok && bin != b0) atomicAdd(&hist[bin], 1u);
+      }
     }
   }
   __syncthreads();
@@ -598,7 +664,7 @@ __device__ inline void fallback_select(int b, int64_t n_pos, int K, float* sall,
   auto elem = [&](uint32_t i) -> uint64_t { return composite(score_key(sall[i]), pos_of(i)); };
   if (ctl[0] == 0xFFFFFFFFu) {
     // at most K valid slots: every one is selected, in slot (= position) order
-    const uint32_t nsel = ordered_compact(
+    const uint32_t nsel = ordered_compact<4>(
         n_src, [&](uint32_t i) { return valid(i); },
         [&](uint32_t i, uint32_t at) {
           if (at < (uint32_t)K) emit((int)at, (int32_t)pos_of(i));
@@ -618,23 +684,33 @@ __device__ inline void fallback_select(int b, int64_t n_pos, int K, float* sall,
     uint64_t* dst = in_bin <= (uint32_t)FIN_SUB_CAP ? sub : gscr;
     if (tid == 0) ctl[6] = 0;
     __syncthreads();
-    for (uint32_t i0 = 0; i0 < n_src; i0 += NT) {
-      const uint32_t i = i0 + tid;
-      const bool ok = i < n_src && valid(i);
-      const uint64_t c = ok ? elem(i) : 0ull;
-      const uint32_t p20 = (uint32_t)(c >> 44);
-      const bool t = ok && p20 >= lo20 && p20 <= hi20;
-      const uint32_t at = wave_append(t, &ctl[6]);
-      if (t && at < in_bin) dst[at] = c;
+    constexpr int FB_C = 4;                        // slots per thread requested at once
+    for (uint32_t i0 = 0; i0 < n_src; i0 += NT * FB_C) {
+      uint64_t cv[FB_C];
+      bool okv[FB_C];
+#pragma unroll
+      for (int u = 0; u < FB_C; ++u) {
+        const uint32_t i = i0 + NT * u + tid, ic = min(i, n_src - 1);
+        const bool v = valid(ic);
+        cv[u] = elem(ic);
+        okv[u] = i < n_src && v;
+      }
+#pragma unroll
+      for (int u = 0; u < FB_C; ++u) {
+        const uint32_t p20 = (uint32_t)(cv[u] >> 44);
+        const bool t = okv[u] && p20 >= lo20 && p20 <= hi20;
+        const uint32_t at = wave_append(t, &ctl[6]);
+        if (t && at < in_bin) dst[at] = cv[u];
+      }
     }
     if (dst != sub) __threadfence_block();         // this workgroup reads its global copy back
     __syncthreads();
-    const int top = radix_top_shift(dst, in_bin, red);
-    radix_select_u64(dst, in_bin, need, top, h, ctl, &prefix, &mask);
+    const int top = radix_top_shift<4>(dst, in_bin, red);
+    radix_select_u64<4>(dst, in_bin, need, top, h, ctl, &prefix, &mask);
   }
   // the K best in position order: above the threshold bin, or inside it and
   // radix-selected
-  const uint32_t nsel = ordered_compact(
+  const uint32_t nsel = ordered_compact<4>(
       n_src,
       [&](uint32_t i) {
         if (!valid(i)) return false;
@@ -647,7 +723,6 @@ __device__ inline void fallback_select(int b, int64_t n_pos, int K, float* sall,
       },
       scan_tmp);
   for (uint32_t j = nsel + tid; j < (uint32_t)K; j += NT) emit((int)j, -1);
-  (void)nvalid;
 }
 
 // The loads a direct finish requests first, before the sequence length and the
@@ -881,13 +956,12 @@ __device__ inline bool finish_direct_body(int b, const int32_t* __restrict__ n_e
   const int64_t n_slots = lst ? (int64_t)src.cand_stride : n_pos;
   const int chunk = lst ? kCandChunk : SC_CHUNK;     // slots per chunk list
   const int64_t nw = (n_slots + chunk - 1) / chunk;
+  // (one place calls the fallback, so the kernel holds one copy of it)
+  bool fast_failed = false;
   if (nw <= RL) {
     const int r = finish_fast64<NT>((int)nw, K, pf.hw, v0, L, emit);
     if (r > 0) return false;
-    if (r < 0) {
-      fallback_select<NT>(b, n_pos, K, sall, gscr, src, rescore, L, emit);
-      return false;
-    }
+    fast_failed = r < 0;
   }
   for (int i = tid; i < NBINS; i += NT) hist[i] = 0;
   bool lc_used = false;                  // the LDS list copy overwrote L.lc
@@ -981,7 +1055,7 @@ __device__ inline bool finish_direct_body(int b, const int32_t* __restrict__ n_e
     for (uint32_t j = nsel + tid; j < (uint32_t)K; j += NT) emit((int)j, -1);
   };
 
-  if (nw <= FIN_MAX_WG) {
+  if (!fast_failed && nw <= FIN_MAX_WG) {
     // headers: list lengths, overflow, the highest cutoff; thread t owns chunks [w0, w1)
     const int per = (int)((nw + NT - 1) / NT);
     const int w0 = (int)min((int64_t)tid * per, nw), w1 = (int)min((int64_t)w0 + per, nw);
