@@ -77,7 +77,7 @@ def parse():
     ap.add_argument("--no-cache-write", action="store_true",
                     help="skip the legs beside the step (quantized-query scoring, prefill, cache write, window, append)")
     ap.add_argument("--legs", default="all",
-                    help="comma-separated legs beside the step to run (qmx8, prefill, fallback, hsi1m, "
+                    help="comma-separated legs beside the step to run (qmx8, prefill, fallback, clustered, hsi1m, "
                          "group_ragged, cache_write, swa, append) or 'all'")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of 1 GiB five times (counter calibration)")
@@ -392,6 +392,42 @@ def fallback_leg(L, torch, w, E, copies, off, nb, q, wh, ws, steps):
                         "finish's fallback path", "ms_per_step": us / 1e3, "topk_is_first_512": ok}
 
 
+def clustered_leg(L, torch, w, E, copies, off, nb, q, q_idx, wh, ws, steps):
+    """The decode128k step with the top keys of every sequence clustered in one
+    chunk: the E8M0 scales of 700 rows at the start of each sequence's last chunk
+    of 1024 entries are raised by 2^6, so those rows hold the sequence's top-512
+    and that chunk's local cutoff lies far above every other chunk's. Too few
+    keys reach the highest cutoff; the finish rescores that chunk alone and
+    takes every other chunk's listed keys. Checks that the top-512 lies in the
+    cluster."""
+    lo = E - 1024
+    cl = []
+    for kv, ik, iks in copies:
+        x = iks.clone().view(w.B, E, 4)
+        x[:, lo:lo + 700] = torch.clamp(x[:, lo:lo + 700].to(torch.int32) + 6, max=254).to(torch.uint8)
+        cl.append((kv, ik, x.view(-1, 4)))
+    topk = torch.empty((w.B, w.k), dtype=torch.int32, device="cuda")
+    out = torch.empty((w.B, w.H, 512), dtype=torch.float32, device="cuda")
+    lse = torch.empty((w.B, w.H), dtype=torch.float32, device="cuda")
+    call = lambda i: L.decode_layer(L.CSA2_FULL, *cl[i % len(cl)], off, nb, E, q, q_idx=q_idx, w=wh,
+                                    k=w.k, topk=topk, out=out, lse=lse, workspace=ws)
+    for i in range(3):
+        call(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        call(i)
+    e1.record()
+    torch.cuda.synchronize()
+    us = 1e3 * e0.elapsed_time(e1) / steps
+    inside = bool(((topk >= lo) & (topk < lo + 700)).all())
+    del cl
+    return {"workload": "decode128k with each sequence's top keys clustered in its last chunk (700 rows with "
+                        "E8M0 scales raised by 2^6): the finish rescores that chunk only",
+            "ms_per_step": us / 1e3, "query_tokens_per_s": w.B / (us * 1e-6), "topk_in_cluster": inside}
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -613,7 +649,7 @@ def main():
     }
     log(f"step {total_ms / a.steps * 1e3:.1f} us, scoring kernel {score_avg_us:.1f} us "
         f"({achieved:.0f} GB/s), {qtok_s:.0f} query-tokens/s")
-    legs = set(("qmx8 prefill fallback hsi1m group_ragged cache_write swa append".split()
+    legs = set(("qmx8 prefill fallback clustered hsi1m group_ragged cache_write swa append".split()
                  if a.legs == "all" else a.legs.split(",")) if not a.no_cache_write else [])
     if "qmx8" in legs:
         log("quantized-query scoring leg")
@@ -636,6 +672,10 @@ def main():
         log("fallback leg")
         res["fallback"] = fallback_leg(L, torch, w, E, copies, off, nb, q, wh, ws, min(a.steps, 20))
         log(f"fallback step {res['fallback']['ms_per_step'] * 1e3:.1f} us")
+    if "clustered" in legs:
+        log("clustered leg")
+        res["clustered"] = clustered_leg(L, torch, w, E, copies, off, nb, q, q_idx, wh, ws, min(a.steps, 50))
+        log(f"clustered step {res['clustered']['ms_per_step'] * 1e3:.1f} us")
     del copies, kv, ik, iks
     torch.cuda.empty_cache()
     for name in ("hsi1m", "group_ragged"):

@@ -560,7 +560,7 @@ __device__ inline uint32_t ordered_compact(uint32_t n, Pred pred, Emit emit, uin
 // (src.cand): the scores the pass stored per slot. All threads call it.
 template <int NT, typename Emit>
 __device__ inline void fallback_select(int b, int64_t n_pos, int K, float* sall, uint64_t* gscr, const ScoreSrc& src,
-                                       int rescore, const FinLds& L, Emit emit) {
+                                       int rescore, const FinLds& L, Emit emit, const SelBufs* klists = nullptr) {
   uint64_t* const sub = L.sub;
   uint32_t* const h = L.h;
   uint64_t* const red = L.red;
@@ -569,9 +569,11 @@ __device__ inline void fallback_select(int b, int64_t n_pos, int K, float* sall,
   uint32_t* hist = (uint32_t*)sub;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   constexpr int NWAVE = NT / 64;
-  const bool lst = src.cand != nullptr;
+  // (a partial rescore below turns the selection into one over a compact
+  // candidate list: these three then describe it)
+  bool lst = src.cand != nullptr;
   const int32_t* crow = lst ? src.cand + (int64_t)b * src.cand_stride : nullptr;
-  const int64_t n_slots = lst ? (int64_t)src.cand_stride : n_pos;
+  int64_t n_slots = lst ? (int64_t)src.cand_stride : n_pos;
   if (lst) {
     sall = const_cast<float*>(src.cand_scores) + (int64_t)b * src.cand_scores_stride;
   } else if (rescore) {
@@ -598,14 +600,16 @@ __device__ inline void fallback_select(int b, int64_t n_pos, int K, float* sall,
     if (qmx) qm = query_mx_operand(lq, lane);
     // (u tiles of a wave requested at once, at clamped in-range rows; the
     // exact variants FB_U deep, the quantized-query ones one tile at a time)
-    auto rescore = [&](auto u_tag, auto tile) {
+    // over the slots [s0, s1), slot s to dsc[s - s0] (and its position to
+    // dpos[s - s0] when given)
+    auto rescore = [&](auto u_tag, auto tile, int64_t s0, int64_t s1, float* dsc, int32_t* dpos) {
       constexpr int U = decltype(u_tag)::value;
-      for (int64_t t0 = 16 * wave; t0 < n_pos; t0 += 16 * NWAVE * U) {
+      for (int64_t t0 = s0 + 16 * wave; t0 < s1; t0 += 16 * NWAVE * U) {
         u32x4_t cw[U];
         uint32_t sbyte[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-          const uint32_t p = (uint32_t)min(t0 + 16 * NWAVE * u + n, n_pos - 1);
+          const uint32_t p = (uint32_t)min(t0 + 16 * NWAVE * u + n, s1 - 1);
           cw[u] = *(const u32x4_t*)(ikb + ((uint64_t)p * 64u + 16u * g));
           sbyte[u] = iksb[(uint64_t)p * 4u + (uint32_t)g];
         }
@@ -613,20 +617,155 @@ __device__ inline void fallback_select(int b, int64_t n_pos, int K, float* sall,
         for (int u = 0; u < U; ++u) {
           const float sc = tile(cw[u], sbyte[u]);
           const int64_t at = t0 + 16 * NWAVE * u + n;
-          if (g == 0 && at < n_pos) sall[at] = sc;
+          if (g == 0 && at < s1) {
+            dsc[at - s0] = sc;
+            if (dpos) dpos[at - s0] = (int32_t)at;
+          }
         }
       }
     };
     constexpr int FB_U = NT <= 512 ? 8 : 4;
     using Deep = std::integral_constant<int, FB_U>;
     using One = std::integral_constant<int, 1>;
-    if (qmx) {
-      if (base == 0) rescore(One{}, [&](const u32x4_t c, uint32_t sb) { return score_tile_mx<0>(qm, c, sb, lwf, g); });
-      else rescore(One{}, [&](const u32x4_t c, uint32_t sb) { return score_tile_mx<1>(qm, c, sb, lwf, g); });
-    } else {
-      if (base == 0) rescore(Deep{}, [&](const u32x4_t c, uint32_t sb) { return score_tile_fn<0>(qa, c, sb, lwf, g); });
-      else rescore(Deep{}, [&](const u32x4_t c, uint32_t sb) { return score_tile_fn<1>(qa, c, sb, lwf, g); });
+    auto rescore_range = [&](int64_t s0, int64_t s1, float* dsc, int32_t* dpos) {
+      if (qmx) {
+        if (base == 0)
+          rescore(One{}, [&](const u32x4_t c, uint32_t sb) { return score_tile_mx<0>(qm, c, sb, lwf, g); }, s0, s1, dsc, dpos);
+        else
+          rescore(One{}, [&](const u32x4_t c, uint32_t sb) { return score_tile_mx<1>(qm, c, sb, lwf, g); }, s0, s1, dsc, dpos);
+      } else {
+        if (base == 0)
+          rescore(Deep{}, [&](const u32x4_t c, uint32_t sb) { return score_tile_fn<0>(qa, c, sb, lwf, g); }, s0, s1, dsc, dpos);
+        else
+          rescore(Deep{}, [&](const u32x4_t c, uint32_t sb) { return score_tile_fn<1>(qa, c, sb, lwf, g); }, s0, s1, dsc, dpos);
+      }
+    };
+    // Partial rescore (the direct finish's chunk lists given): every list
+    // holds all of its chunk's keys whose 20-bit prefix reaches the chunk's
+    // cutoff (all of them up to its capacity; an overflowed list only part).
+    // For a level lam with at least K listed keys at or above it, every key of
+    // the K best reaches lam, so it is in the list of every chunk whose cutoff
+    // is at most lam. Only the chunks above lam (and the overflowed ones) are
+    // rescored: chunk by chunk in position order, the listed keys of the other
+    // chunks and every slot of the rescored ones form a compact candidate list
+    // that holds every key of the K best exactly, and the selection runs over
+    // it (scores in sall, positions in gscr after room for the threshold
+    // bin's keys). lam runs over the distinct cutoffs from the highest down;
+    // no suitable lam within PR_MAXR chunks, or a list longer than PR_CAP (or
+    // than the scratch rows hold): the whole sequence is rescored.
+    constexpr int PR_LV = 8, PR_MAXR = 8, PR_CAP = 8192;
+    const int nwc = (int)((n_pos + SC_CHUNK - 1) / SC_CHUNK);
+    bool partial = false;
+    if (klists != nullptr && nwc <= NT) {
+      uint32_t* const lv = h;                        // [1 + PR_LV] levels
+      uint32_t* const cR = h + 16;                   // [PR_LV] chunks to rescore per level
+      uint32_t* const cL = h + 32;                   // [PR_LV] listed keys at or above each level
+      uint32_t* const rch = h + 64;                  // [PR_MAXR] the chunks rescored
+      const uint64_t* hd = klists->hdr + (int64_t)b * klists->hdr_stride;
+      const uint64_t* wcl = klists->wgc + (int64_t)b * klists->wgc_stride;
+      const bool mine = tid < nwc;
+      const uint64_t hv = mine ? hd[tid] : 0ull;
+      const uint32_t cut = (uint32_t)(hv >> 32);
+      const bool ovf = mine && ((uint32_t)hv >> 31) != 0u;
+      if (tid < 2 * 16 + 16) h[16 + tid] = 0u;       // cR, cL and the rescore count
+      uint32_t prev = block_max_u32(mine ? cut + 1u : 0u, scan_tmp);   // (cutoff + 1; 0: none)
+      if (tid == 0) lv[0] = prev;
+      for (int i = 1; i <= PR_LV; ++i) {
+        prev = block_max_u32(mine && cut + 1u < prev ? cut + 1u : 0u, scan_tmp);
+        if (tid == 0) lv[i] = prev;
+      }
+      __syncthreads();
+      uint32_t lvr[PR_LV];
+#pragma unroll
+      for (int i = 0; i < PR_LV; ++i) lvr[i] = lv[1 + i];
+      // chunks above each level (or overflowed)
+      uint32_t nr[PR_LV];
+#pragma unroll
+      for (int i = 0; i < PR_LV; ++i) {
+        const bool above = mine && (ovf || cut + 1u > lvr[i]);
+        nr[i] = (uint32_t)__popcll(__ballot(above));
+      }
+      if (lane == 0) {
+#pragma unroll
+        for (int i = 0; i < PR_LV; ++i) atomicAdd(&cR[i], nr[i]);
+      }
+      // listed keys at or above each level: wave v reads the lists of chunks
+      // v, v + NWAVE, ..., four chunks (of up to CAND_CAP entries) at a time
+      uint32_t nl[PR_LV];
+#pragma unroll
+      for (int i = 0; i < PR_LV; ++i) nl[i] = 0u;
+      for (int c0 = wave; c0 < nwc; c0 += 4 * NWAVE) {
+        uint64_t e[4][CAND_CAP / 64];
+        uint32_t ce[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int c = min(c0 + q * NWAVE, nwc - 1);
+          ce[q] = c0 + q * NWAVE < nwc ? min((uint32_t)hd[c] & 0x7FFFFFFFu, (uint32_t)CAND_CAP) : 0u;
+#pragma unroll
+          for (int j = 0; j < CAND_CAP / 64; ++j) e[q][j] = wcl[(int64_t)c * CAND_CAP + 64 * j + lane];
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int j = 0; j < CAND_CAP / 64; ++j) {
+            const bool ok = (uint32_t)(64 * j + lane) < ce[q];
+            const uint32_t p1 = (uint32_t)(e[q][j] >> 44) + 1u;
+#pragma unroll
+            for (int i = 0; i < PR_LV; ++i) nl[i] += (ok && lvr[i] != 0u && p1 >= lvr[i]) ? 1u : 0u;
+          }
+      }
+#pragma unroll
+      for (int i = 0; i < PR_LV; ++i) {
+        const uint32_t t = wave_incl_sum(nl[i]);
+        if (lane == 63) atomicAdd(&cL[i], t);
+      }
+      __syncthreads();
+      int pick = -1;
+      for (int i = 0; i < PR_LV && pick < 0; ++i)
+        if (lvr[i] != 0u && cR[i] <= (uint32_t)PR_MAXR && cL[i] >= (uint32_t)K) pick = i;
+      if (pick >= 0) {
+        const uint32_t lam1 = lvr[pick];               // the level + 1
+        const bool re = mine && (ovf || cut + 1u > lam1);
+        const uint32_t nlist = mine ? min((uint32_t)hv & 0x7FFFFFFFu, (uint32_t)CAND_CAP) : 0u;
+        const uint32_t myn =
+            !mine ? 0u : re ? (uint32_t)(min((int64_t)(tid + 1) * SC_CHUNK, n_pos) - (int64_t)tid * SC_CHUNK) : nlist;
+        uint32_t tot;
+        const uint32_t myoff = block_exclusive_scan(myn, scan_tmp, &tot);
+        if (tot > 0u && tot <= (uint32_t)PR_CAP && 3 * (int64_t)tot <= 2 * n_pos) {
+          partial = true;
+          uint32_t* const coff = L.loff;               // each chunk's offset in the candidate list
+          if (mine) coff[tid] = myoff;
+          if (re) rch[atomicAdd(&h[48], 1u)] = (uint32_t)tid;
+          __syncthreads();
+          int32_t* const cpos = (int32_t*)(gscr + tot);
+          // the listed keys of the chunks not rescored
+          for (int c = wave; c < nwc; c += NWAVE) {
+            const uint64_t hc = hd[c];
+            const uint32_t cc = (uint32_t)(hc >> 32);
+            if (((uint32_t)hc >> 31) != 0u || cc + 1u > lam1) continue;
+            const uint32_t ncl = min((uint32_t)hc & 0x7FFFFFFFu, (uint32_t)CAND_CAP);
+            const uint32_t o = coff[c];
+            for (uint32_t j = lane; j < ncl; j += 64) {
+              const uint64_t ev = wcl[(int64_t)c * CAND_CAP + j];
+              const uint32_t key = (uint32_t)(ev >> 32);
+              sall[o + j] = __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+              cpos[o + j] = (int32_t)(0xFFFFFFFFu - (uint32_t)ev);
+            }
+          }
+          // every slot of the rescored chunks
+          const uint32_t nre = h[48];
+          for (uint32_t r = 0; r < nre; ++r) {
+            const int64_t c = rch[r];
+            const uint32_t o = coff[c];
+            rescore_range(c * SC_CHUNK, min((c + 1) * (int64_t)SC_CHUNK, n_pos), sall + o, cpos + o);
+          }
+          lst = true;
+          crow = cpos;
+          n_slots = tot;
+        }
+      }
     }
+    if (!partial) rescore_range(0, n_pos, sall, nullptr);
     __threadfence_block();                         // this workgroup reads them back
   }
   __syncthreads();
@@ -1245,8 +1384,9 @@ __device__ inline bool finish_direct_body(int b, const int32_t* __restrict__ n_e
       }
     }
   }
-  // Fallback: the same steps over every score of the sequence
-  fallback_select<NT>(b, n_pos, K, sall, gscr, src, rescore, L, emit);
+  // Fallback: the same steps over every score of the sequence (rescored where
+  // the chunk lists do not hold them)
+  fallback_select<NT>(b, n_pos, K, sall, gscr, src, rescore, L, emit, &sb);
   return lc_used;
 }
 

@@ -247,6 +247,25 @@ def test_full_direct_fallback_inside_attention():
         check_full(kv[sl], ik[sl], iks[sl], offs, nl, 512, q, qi, w, top, out, lse, f"reuse B={len(nl)}")
 
 
+@pytest.mark.parametrize("chunks", [[63], [0, 5, 17], [1, 4, 9, 12, 20, 26, 31, 37, 44, 50, 55, 61]])
+def test_full_direct_clustered_top_keys(chunks):
+    """The top keys of sequence 1 sit in a few chunks (300 rows at the start of
+    each listed chunk with E8M0 scales raised by 2^6): those chunks' local
+    cutoffs lie far above the others', so too few keys reach the highest one.
+    With one or three such chunks the finish rescores only them and takes every
+    other chunk's listed keys; with twelve (more than it rescores alone) it
+    rescores the whole sequence. Sequence 0 takes the fast path."""
+    rng = np.random.default_rng(97 + len(chunks))
+    n_list = [30000, 65000]
+    kv, ik, iks, off = oracle_cache(rng, n_list, 1)
+    iks = iks.copy()
+    for c in chunks:
+        a = off[1] + 1024 * c
+        iks[a:a + 300] = np.minimum(iks[a:a + 300].astype(np.int32) + 6, 254).astype(np.uint8)
+    q, qi, w, top, out, lse = run_full(kv, ik, iks, off, n_list, 64, 512, rng)
+    check_full(kv, ik, iks, off, n_list, 512, q, qi, w, top, out, lse, f"clustered {len(chunks)}")
+
+
 def test_full_direct_long_lists_inside_attention():
     """Sequence 0 carries 90 and 100 copies of its best indexer row in two
     chunks: their lists exceed 64 candidates, so the attention workgroups copy
