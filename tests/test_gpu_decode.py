@@ -266,6 +266,48 @@ def test_full_direct_clustered_top_keys(chunks):
     check_full(kv, ik, iks, off, n_list, 512, q, qi, w, top, out, lse, f"clustered {len(chunks)}")
 
 
+def test_full_direct_overflowed_tied_chunk():
+    """Sequence 1: copies of its best indexer row with E8M0 scales raised by a
+    power of two (scores scale exactly): 800 tied copies (x4) fill chunk 7's
+    list past its capacity, and 30 copies (x64) after them are the best keys
+    of the sequence; 20 chunks hold 30 copies (x8) each and three chunks 300
+    copies (x16). The finish must rescore chunk 7 although its list holds
+    only ties, and break the ties by position."""
+    rng = np.random.default_rng(131)
+    n_list = [20000, 60000]
+    kv, ik, iks, off = oracle_cache(rng, n_list, 1)
+    ik, iks = ik.copy(), iks.copy()
+    qi1 = synth.indexer_query(np.random.default_rng(7), 16)
+    w1 = synth.head_weights(np.random.default_rng(8), 16)
+    a = off[1]
+    s1 = OI.scores(ik[a:a + n_list[1]], iks[a:a + n_list[1]], qi1, w1, 1)
+    best = a + int(np.argmax(s1))
+
+    def put(row, cnt, boost):
+        ik[row:row + cnt] = ik[best]
+        iks[row:row + cnt] = np.minimum(iks[best].astype(np.int32) + boost, 254).astype(np.uint8)
+
+    put(a + 7 * 1024, 800, 2)
+    put(a + 7 * 1024 + 900, 30, 6)
+    for c in range(20, 40):
+        put(a + c * 1024, 30, 3)
+    for c in (50, 52, 54):
+        put(a + c * 1024, 300, 4)
+    import torch
+    import long_context_fp4_amd as L
+    B = 2
+    q = np.stack([synth.latent_query(rng, 64) for _ in range(B)])
+    qi = np.stack([synth.indexer_query(rng, 16), qi1])
+    w = np.stack([synth.head_weights(rng, 16), w1])
+    top, _, out, lse = L.decode_layer(L.CSA2_FULL, dev(kv), dev(ik), dev(iks), dev(off),
+                                      dev(np.asarray(n_list, np.int32)), max(n_list), dev(q), q_idx=dev(qi),
+                                      w=dev(w), k=512)
+    torch.cuda.synchronize()
+    top, out, lse = host(top), host(out), host(lse)
+    check_full(kv, ik, iks, off, n_list, 512, q, qi, w, top, out, lse, "overflowed tied chunk")
+    assert np.all(np.isin(np.arange(7 * 1024 + 900, 7 * 1024 + 930), top[1]))
+
+
 def test_full_direct_long_lists_inside_attention():
     """Sequence 0 carries 90 and 100 copies of its best indexer row in two
     chunks: their lists exceed 64 candidates, so the attention workgroups copy
