@@ -259,8 +259,10 @@ template <int MODE>
 __device__ __forceinline__ float head_sum(const f32x4_t acc, const float* lw, int g) {
   if (MODE == 0) return acc[0];          // head 0 is row 0, held by lanes 0..15
   const float4 wr = *(const float4*)&lw[4 * g];
-  const float sc = wr.x * fmaxf(acc[0], 0.0f) + wr.y * fmaxf(acc[1], 0.0f) +
-                   wr.z * fmaxf(acc[2], 0.0f) + wr.w * fmaxf(acc[3], 0.0f);
+  // ReLU as a signed integer max of the bit pattern with 0: one instruction
+  // (a float max would first quiet a possible signalling NaN); -0 gives +0
+  auto relu = [](float x) { return __int_as_float(max(__float_as_int(x), 0)); };
+  const float sc = wr.x * relu(acc[0]) + wr.y * relu(acc[1]) + wr.z * relu(acc[2]) + wr.w * relu(acc[3]);
   return sum_lane_groups(sc);
 }
 
