@@ -324,6 +324,14 @@ __global__ __launch_bounds__(SC_THREADS) __attribute__((amdgpu_waves_per_eu(CAND
   }
   __syncthreads();
   if constexpr (QMX) qm = query_mx_operand(lq, lane);
+  // four queries with head weights: each query's weights of this lane
+  // group's heads, kept in registers
+  constexpr bool QUAD = MQ == 4 && MODE == 1;
+  float4 wr4[QUAD ? 4 : 1];
+  if constexpr (QUAD) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) wr4[m] = *(const float4*)&lw[16 * m + 4 * g];
+  }
 
   // one tile = 16 slots x 16 heads: 4 MFMAs over the 128 channels; the head sum
   // goes to the lanes of group 0, which stage the score in LDS
@@ -559,6 +567,9 @@ __global__ __launch_bounds__(SC_THREADS) __attribute__((amdgpu_waves_per_eu(CAND
         if constexpr (MQ == 1) {
           const float sc = score_tile(codes[u], sbyte[u]);
           if (g == 0 && ls < end) lsc[ls] = sc;
+        } else if constexpr (QUAD) {
+          const float sc = score_tile_quad(qa, codes[u], sbyte[u], wr4);   // lane group g: query g
+          if (ls < end) lsc[g * SC_SPAN + ls] = sc;
         } else {
           float sc[MQ];
           score_tile_multi<MODE, MQ>(qa, codes[u], sbyte[u], lw, g, sc);

@@ -255,15 +255,18 @@ __device__ inline void hist_kth_bin(const uint32_t* lhist, uint32_t need, uint32
 // Score of entry (lane & 15) from the 16 x 16 head x entry tile acc (lane
 // holds heads 4g .. 4g+3): head 0 for the dot score, else sum_h w_h ReLU(.)
 // gathered onto every lane group.
-template <int MODE>
-__device__ __forceinline__ float head_sum(const f32x4_t acc, const float* lw, int g) {
-  if (MODE == 0) return acc[0];          // head 0 is row 0, held by lanes 0..15
-  const float4 wr = *(const float4*)&lw[4 * g];
+// This lane's part of sum_h w_h ReLU(.): its four heads.
+__device__ __forceinline__ float weighted_relu4(const f32x4_t acc, const float4 wr) {
   // ReLU as a signed integer max of the bit pattern with 0: one instruction
   // (a float max would first quiet a possible signalling NaN); -0 gives +0
   auto relu = [](float x) { return __int_as_float(max(__float_as_int(x), 0)); };
-  const float sc = wr.x * relu(acc[0]) + wr.y * relu(acc[1]) + wr.z * relu(acc[2]) + wr.w * relu(acc[3]);
-  return sum_lane_groups(sc);
+  return wr.x * relu(acc[0]) + wr.y * relu(acc[1]) + wr.z * relu(acc[2]) + wr.w * relu(acc[3]);
+}
+
+template <int MODE>
+__device__ __forceinline__ float head_sum(const f32x4_t acc, const float* lw, int g) {
+  if (MODE == 0) return acc[0];          // head 0 is row 0, held by lanes 0..15
+  return sum_lane_groups(weighted_relu4(acc, *(const float4*)&lw[4 * g]));
 }
 
 template <int MODE>
@@ -413,6 +416,36 @@ __device__ __forceinline__ void score_tile_multi(const bf16x8_t (&qa)[MQ][4], co
     for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[m][j], kb[j], acc, 0, 0, 0);
     out[m] = head_sum<MODE>(acc, lw + 16 * m, g);
   }
+}
+
+// Four queries against one tile, sum_h w_h ReLU(.) (MODE 1), with the four
+// head sums done as one reduce-scatter over the lane groups: lane group m
+// ends with query m's score. The lane-half swap pairs queries 0 with 2 and 1
+// with 3 (the low half keeps queries 0 and 1, the high half 2 and 3), the
+// row swap then pairs the two partial sums: three swaps instead of eight.
+// Each total is (groups 0 + 2) + (groups 1 + 3) with the operands in the
+// order of sum_lane_groups, so the scores equal score_tile_fn's bit for bit.
+// wr[m]: query m's weights of this lane group's heads 4g .. 4g+3.
+__device__ __forceinline__ float score_tile_quad(const bf16x8_t (&qa)[4][4], const u32x4_t cw, uint32_t sbyte,
+                                                 const float4 (&wr)[4]) {
+  const float scl = __uint_as_float(sbyte << 23);
+  bf16x8_t kb[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) kb[j] = dequant_mx_block8(cw[j], scl);
+  float s[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[m][j], kb[j], acc, 0, 0, 0);
+    s[m] = weighted_relu4(acc, wr[m]);
+  }
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(s[0]), __float_as_uint(s[2]), false, false);
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(s[1]), __float_as_uint(s[3]), false, false);
+  const float x02 = __uint_as_float(a[0]) + __uint_as_float(a[1]);   // low half: query 0, high half: query 2
+  const float x13 = __uint_as_float(c[0]) + __uint_as_float(c[1]);   // low half: query 1, high half: query 3
+  const auto d = __builtin_amdgcn_permlane16_swap(__float_as_uint(x02), __float_as_uint(x13), false, false);
+  return __uint_as_float(d[0]) + __uint_as_float(d[1]);
 }
 
 // ---- quantized-query variant: gfx950's block-scaled FP8 x FP4 MFMA

@@ -120,3 +120,36 @@ def test_prefill_128_queries():
         err = attn_rel_err(out[0, t], ro)
         assert np.all(err <= ATTN_REL_TOL), f"query {t}: max rel err {err.max():.3g}"
         assert np.all(np.abs(lse[0, t] - rl) <= 2e-3), f"query {t}: lse"
+
+
+@pytest.mark.parametrize("Tq", [8, 6])
+def test_prefill_selects_what_decode_selects(Tq):
+    """The multi-query pass scores four queries per key tile with one combined
+    head-sum reduction; its scores must equal the one-query pass's bit for bit.
+    Each query of the prefill is also run as a decode sequence over the entries
+    it sees: the selections must be the same positions (near-ties included)
+    and the attention outputs the same bits. Tq = 6 leaves the second group
+    of four queries half empty."""
+    import torch
+    import long_context_fp4_amd as L
+    rng = np.random.default_rng(4000 + Tq)
+    m, k, H, T = 2, 512, 16, 90001
+    w_lat = synth.merge_weights(rng, m, 512)
+    w_idx = synth.merge_weights(rng, m, 128)
+    kv, ik, iks = OC.cache_write(synth.hidden_host(rng, (T, 512)), synth.hidden_host(rng, (T, 128)), w_lat, w_idx, m)
+    E = kv.shape[0]
+    pos = np.sort(rng.choice(np.arange(3000, T), size=Tq, replace=False)).astype(np.int64)
+    pos[-1] = T - 1
+    q = np.stack([synth.latent_query(rng, H) for _ in range(Tq)])
+    qi = np.stack([synth.indexer_query(rng, 16) for _ in range(Tq)])
+    w = np.stack([synth.head_weights(rng, 16) for _ in range(Tq)])
+    dkv, dik, diks = dev(kv), dev(ik), dev(iks)
+    top, out, lse = L.prefill_layer(dkv, dik, diks, dev(np.zeros(1, np.int64)), dev(np.array([E], np.int32)), E, m,
+                                    dev(pos[None]), dev(qi[None]), dev(q[None]), w=dev(w[None]), k=k)
+    vis = np.minimum(E, (pos + 1) // m).astype(np.int32)
+    dtop, _, dout, dlse = L.decode_layer(L.CSA2_FULL, dkv, dik, diks, dev(np.zeros(Tq, np.int64)), dev(vis), E,
+                                         dev(q), q_idx=dev(qi), w=dev(w), k=k)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(top)[0], host(dtop))
+    assert np.array_equal(host(out)[0].view(np.uint32), host(dout).view(np.uint32))
+    assert np.array_equal(host(lse)[0].view(np.uint32), host(dlse).view(np.uint32))
