@@ -463,10 +463,21 @@ int run_decode_layer(int mode, const uint8_t* kv, const uint8_t* ik, const uint8
                      const int32_t* n_entries, int B, int64_t max_n, const uint16_t* q_idx, const float* w, int Hi,
                      int score_mode, const uint16_t* q, int H, float softmax_scale, int k, int pool_k, int32_t* pool,
                      int32_t* topk, float* out, float* lse, uint8_t* ws, hipStream_t s, bool allow_fused = true,
-                     int pre_B = 0, int pre_Tq = 0) {
+                     int pre_B = 0, int pre_Tq = 0, const csa2::PrefillViews* pv = nullptr) {
   const FusedPlan fp = fused_plan(mode, B, max_n, H, k, pool_k);
   const int cand_stride = mode == CSA2_REINDEX ? pool_k : 0;
   int rc0 = CSA2_OK;
+  // a prefill's virtual batch (pre_Tq > 0; pv: the sequences, positions and
+  // the views' arrays entry_offset and n_entries): the multi-query pass
+  // computes and writes the views itself; every other plan takes them from a
+  // launch of their own first
+  const bool multi_query = pre_Tq > 0 && fp.on && allow_fused && mode == CSA2_FULL && pool_k == 0 &&
+                           (score_mode & CSA2_SCORE_QMX8) == 0;
+  if (pre_Tq > 0 && !multi_query) {
+    const hipError_t e = csa2::launch_prefill_views(pv->entry_offset, pv->n_entries, pv->pos, pv->m, pre_B, pre_Tq,
+                                                    pv->eo, pv->ne, s);
+    if (e != hipSuccess) return hip_status(e, "prefill_layer views");
+  }
   if (fp.on && allow_fused) {
     // scoring launch, then the attention that runs the top-k finish itself
     // (and, for a Full layer with a pool, the pool finish in workgroups of its own)
@@ -480,11 +491,10 @@ int run_decode_layer(int mode, const uint8_t* kv, const uint8_t* ik, const uint8
     ff.pool = nullptr;
     ff.px = csa2::PoolExchange{nullptr, nullptr, nullptr, nullptr, L.nblk, 1};
     hipError_t e;
-    if (mode == CSA2_FULL && pre_Tq > 0 && pool_k == 0 && (score_mode & CSA2_SCORE_QMX8) == 0) {
-      // a prefill's virtual batch: the multi-query pass reads each key tile
-      // once for several of a sequence's queries
-      e = csa2::launch_score_prefill(ik, iks, entry_offset, n_entries, pre_B, pre_Tq, max_n, q_idx, w, Hi,
-                                     score_mode, sb, k, s);
+    if (multi_query) {
+      // the multi-query pass reads each key tile once for several of a
+      // sequence's queries
+      e = csa2::launch_score_prefill(ik, iks, pre_B, pre_Tq, max_n, q_idx, w, Hi, score_mode, sb, k, *pv, s);
     } else if (mode == CSA2_FULL) {
       e = score_full(ik, iks, entry_offset, n_entries, B, max_n, q_idx, w, Hi, score_mode, scores, L.slots, sb,
                      pool_k > 0 ? csa2::SEL_POOL : csa2::SEL_DIRECT, k, false, pool_k, s);
@@ -605,12 +615,13 @@ int csa2_decode_layer_noalloc(int mode, const uint8_t* kv, const uint8_t* ik, co
 
 namespace {
 // csa2_decode_layer, and (pre_Tq > 0) the virtual decode batch of a prefill:
-// B = pre_B * pre_Tq queries of pre_B sequences.
+// B = pre_B * pre_Tq queries of pre_B sequences, whose views (written to
+// entry_offset and n_entries before they are read) pv describes.
 int decode_layer_ws(int mode, const uint8_t* kv, const uint8_t* ik, const uint8_t* iks, const int64_t* entry_offset,
                     const int32_t* n_entries, int B, int64_t max_n, const uint16_t* q_idx, const float* w, int Hi,
                     int score_mode, const uint16_t* q, int H, float softmax_scale, int k, int pool_k, int32_t* pool,
                     int32_t* topk, float* out, float* lse, void* workspace, size_t ws_bytes, void* stream, int pre_B,
-                    int pre_Tq) {
+                    int pre_Tq, const csa2::PrefillViews* pv) {
   int rc = check_decode_args(mode, kv, ik, iks, entry_offset, n_entries, B, max_n, q_idx, w, Hi, score_mode, q, H, k,
                              pool_k, pool, topk, out, lse);
   if (rc) return rc;
@@ -620,7 +631,7 @@ int decode_layer_ws(int mode, const uint8_t* kv, const uint8_t* ik, const uint8_
   if (!aligned16(workspace)) return fail(CSA2_ERR_ALIGN, "decode_layer: workspace must be 16-byte aligned");
   return run_decode_layer(mode, kv, ik, iks, entry_offset, n_entries, B, max_n, q_idx, w, Hi, score_mode, q, H,
                           softmax_scale, k, pool_k, pool, topk, out, lse, (uint8_t*)workspace, (hipStream_t)stream,
-                          true, pre_B, pre_Tq);
+                          true, pre_B, pre_Tq, pv);
 }
 }  // namespace
 
@@ -632,7 +643,7 @@ int csa2_decode_layer(int mode, const uint8_t* kv, const uint8_t* ik, const uint
                       float softmax_scale, int k, int pool_k, int32_t* pool, int32_t* topk, float* out,
                       float* lse, void* workspace, size_t ws_bytes, void* stream) {
   return decode_layer_ws(mode, kv, ik, iks, entry_offset, n_entries, B, max_n, q_idx, w, Hi, score_mode, q, H,
-                         softmax_scale, k, pool_k, pool, topk, out, lse, workspace, ws_bytes, stream, 0, 0);
+                         softmax_scale, k, pool_k, pool, topk, out, lse, workspace, ws_bytes, stream, 0, 0, nullptr);
 }
 
 size_t csa2_prefill_workspace_bytes(int B, int Tq, int64_t max_n, int H, int k) {
@@ -666,10 +677,9 @@ int csa2_prefill_layer(const uint8_t* kv, const uint8_t* ik, const uint8_t* iks,
   uint8_t* views = (uint8_t*)workspace + dneed;
   int64_t* eo = (int64_t*)views;
   int32_t* ne = (int32_t*)(views + round_up((size_t)Bv * 8, 256));
-  hipError_t e = csa2::launch_prefill_views(entry_offset, n_entries, pos, m, B, Tq, eo, ne, (hipStream_t)stream);
-  if (e != hipSuccess) return hip_status(e, "prefill_layer views");
+  const csa2::PrefillViews pv{entry_offset, n_entries, pos, m, eo, ne};
   return decode_layer_ws(CSA2_FULL, kv, ik, iks, eo, ne, Bv, max_n, q_idx, w, Hi, score_mode, q, H, softmax_scale, k,
-                         0, nullptr, topk, out, lse, workspace, dneed, stream, B, Tq);
+                         0, nullptr, topk, out, lse, workspace, dneed, stream, B, Tq, &pv);
 }
 
 double csa2_bytes_per_token(const int* ratios, int n_layers, int lat_ch, int lat_blk, int lat_sbytes, int idx_ch,

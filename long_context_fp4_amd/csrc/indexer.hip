@@ -137,7 +137,8 @@ __global__ __launch_bounds__(SC_THREADS) __attribute__((amdgpu_waves_per_eu(CAND
     const int64_t* __restrict__ entry_offset, const int32_t* __restrict__ n_entries, int64_t max_n,
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w, int Hi,
     const int32_t* __restrict__ cand, int cand_stride,
-    float* __restrict__ scores, int64_t sstride, SelBufs sb, int K, int store_scores, int pool_k, int Tq) {
+    float* __restrict__ scores, int64_t sstride, SelBufs sb, int K, int store_scores, int pool_k, int Tq,
+    PrefillViews pv) {
   static_assert(MQ == 1 || (!CAND && SEL == SEL_DIRECT && !QMX), "the multi-query pass is a direct Full pass");
   static_assert(MQ <= SC_THREADS / 64, "one wave per query in the multi-query tail");
   // a candidate-list direct pass takes chunks of kCandChunk slots: more
@@ -184,11 +185,23 @@ __global__ __launch_bounds__(SC_THREADS) __attribute__((amdgpu_waves_per_eu(CAND
   // independent loads first (the sequence's length and first row, the queries,
   // the head weights), so the keys are requested one round trip after the start
   int32_t neq[MQ];
+  int64_t row_base;
+  // (MQ > 1: the sequence's arrays and the queries' token positions)
+  int64_t nseq = 0, pq[MQ];
+  if constexpr (MQ == 1) {
+    neq[0] = n_entries[b];
+    row_base = entry_offset[b];
+    asm volatile("" ::"s"(neq[0]), "s"(row_base));   // both loads issued here, before any branch on them
+  } else {
+    const int bs = vq[0] / Tq;
+    nseq = pv.n_entries[bs];
+    row_base = pv.entry_offset[bs];
 #pragma unroll
-  for (int m = 0; m < MQ; ++m) neq[m] = n_entries[vq[m]];
-  const int32_t ne = neq[0];
-  const int64_t row_base = entry_offset[b];
-  asm volatile("" ::"s"(ne), "s"(row_base));   // both loads issued here, before any branch on them
+    for (int m = 0; m < MQ; ++m) pq[m] = pv.pos[vq[m]];
+#pragma unroll
+    for (int m = 0; m < MQ; ++m) asm volatile("" ::"s"(pq[m]));
+    asm volatile("" ::"s"(nseq), "s"(row_base));       // every load issued here, the queries' next
+  }
   // A operand: q[head = n][channels 32g + 8j .. +7] for MFMA j (the quantized
   // variant builds its operand once the first keys are requested)
   bf16x8_t qa[MQ][4];
@@ -207,6 +220,28 @@ __global__ __launch_bounds__(SC_THREADS) __attribute__((amdgpu_waves_per_eu(CAND
   // LDS and read per tile, which keeps the wave within 64 registers
   const int wq = tid >> 4, wh = tid & 15;
   const float wv = (tid < 16 * MQ && wh < Hi) ? (w ? w[(int64_t)vq[wq < MQ ? wq : 0] * Hi + wh] : 1.0f) : 0.0f;
+  if constexpr (MQ > 1) {
+    // the queries' views: the sequence's rows, floor((pos + 1) / m) of them
+    // visible (at most its n_entries); the first workgroup of each query
+    // group writes them out for the finish and the attention
+#pragma unroll
+    for (int m = 0; m < MQ; ++m) {
+      // (a 32-bit division whenever the position allows it)
+      const int64_t p1 = pq[m] + 1;
+      const int64_t vis = pq[m] < 0 ? 0
+                          : (p1 >> 31) == 0 ? (int64_t)((uint32_t)p1 / (uint32_t)pv.m) : p1 / pv.m;
+      neq[m] = (int32_t)(vis < nseq ? vis : (nseq < 0 ? 0 : nseq));
+    }
+    if (blockIdx.x == 0) {
+#pragma unroll
+      for (int m = 0; m < MQ; ++m) {
+        if (tid == m && qok[m]) {
+          pv.eo[vq[m]] = row_base;
+          pv.ne[vq[m]] = neq[m];
+        }
+      }
+    }
+  }
   // positions each query's selection covers (MQ > 1: its visible entries)
   int64_t npq[MQ];
   int64_t n_pos = 0;
@@ -994,7 +1029,7 @@ hipError_t launch_score(const uint8_t* ik, const uint8_t* iks, const int64_t* en
 #define CSA2_SCORE_LAUNCH1(C, S, Mo, Q)                                                          \
   hipLaunchKernelGGL((score_kernel<C, S, Mo, Q>), grid, block, 0, stream, ik, iks, entry_offset, \
                      n_entries, max_n, q_idx, w, Hi, cand, cand_stride, scores, sstride, sb, K,  \
-                     (int)store, pool_k, 0)
+                     (int)store, pool_k, 0, PrefillViews{})
 #define CSA2_SCORE_LAUNCH(C, S)                                                                  \
   if (base == 0) {                                                                               \
     if (qmx) CSA2_SCORE_LAUNCH1(C, S, 0, true); else CSA2_SCORE_LAUNCH1(C, S, 0, false);         \
@@ -1023,22 +1058,24 @@ hipError_t launch_score(const uint8_t* ik, const uint8_t* iks, const int64_t* en
 
 // The multi-query pass of a prefill: B sequences of Tq queries each, scored
 // PREFILL_MQ queries per workgroup, selections per query (the virtual
-// sequences b * Tq + t of eo, ne, q_idx, w and sb); direct mode, exact scores.
+// sequences b * Tq + t of q_idx, w, sb and the views it writes to pv.eo and
+// pv.ne); direct mode, exact scores.
 constexpr int PREFILL_MQ = 4;
 
-hipError_t launch_score_prefill(const uint8_t* ik, const uint8_t* iks, const int64_t* eo, const int32_t* ne, int B,
-                                int Tq, int64_t max_n, const uint16_t* q_idx, const float* w, int Hi, int mode,
-                                const SelBufs& sb, int K, hipStream_t stream) {
-  if (max_n <= 0) return hipSuccess;
+hipError_t launch_score_prefill(const uint8_t* ik, const uint8_t* iks, int B, int Tq, int64_t max_n,
+                                const uint16_t* q_idx, const float* w, int Hi, int mode, const SelBufs& sb, int K,
+                                const PrefillViews& pv, hipStream_t stream) {
+  if (max_n <= 0)   // nothing to score: the views alone
+    return launch_prefill_views(pv.entry_offset, pv.n_entries, pv.pos, pv.m, B, Tq, pv.eo, pv.ne, stream);
   if ((mode & kScoreQmx8) != 0) return hipErrorInvalidValue;
   const int QG = (Tq + PREFILL_MQ - 1) / PREFILL_MQ;
   dim3 grid((unsigned)((max_n + SC_SPAN - 1) / SC_SPAN), (unsigned)(B * QG)), block(SC_THREADS);
   if (mode == 0)
-    hipLaunchKernelGGL((score_kernel<false, SEL_DIRECT, 0, false, PREFILL_MQ>), grid, block, 0, stream, ik, iks, eo, ne,
-                       max_n, q_idx, w, Hi, nullptr, 0, nullptr, 0, sb, K, 0, 0, Tq);
+    hipLaunchKernelGGL((score_kernel<false, SEL_DIRECT, 0, false, PREFILL_MQ>), grid, block, 0, stream, ik, iks, nullptr,
+                       nullptr, max_n, q_idx, w, Hi, nullptr, 0, nullptr, 0, sb, K, 0, 0, Tq, pv);
   else
-    hipLaunchKernelGGL((score_kernel<false, SEL_DIRECT, 1, false, PREFILL_MQ>), grid, block, 0, stream, ik, iks, eo, ne,
-                       max_n, q_idx, w, Hi, nullptr, 0, nullptr, 0, sb, K, 0, 0, Tq);
+    hipLaunchKernelGGL((score_kernel<false, SEL_DIRECT, 1, false, PREFILL_MQ>), grid, block, 0, stream, ik, iks, nullptr,
+                       nullptr, max_n, q_idx, w, Hi, nullptr, 0, nullptr, 0, sb, K, 0, 0, Tq, pv);
   return hipGetLastError();
 }
 

@@ -125,9 +125,20 @@ hipError_t launch_score(const uint8_t* ik, const uint8_t* iks, const int64_t* en
 // sequences of Tq queries; eo / ne / q_idx / w / sb are per query (virtual
 // sequence b * Tq + t, ne = its visible entries). The finish and attention of
 // the virtual decode batch follow unchanged.
-hipError_t launch_score_prefill(const uint8_t* ik, const uint8_t* iks, const int64_t* eo, const int32_t* ne, int B,
-                                int Tq, int64_t max_n, const uint16_t* q_idx, const float* w, int Hi, int mode,
-                                const SelBufs& sb, int K, hipStream_t stream);
+// The multi-query pass computes the views itself from the sequences' arrays
+// and the token positions, uses them, and its first workgroup of each query
+// group writes them to eo and ne for the launches that follow.
+struct PrefillViews {
+  const int64_t* entry_offset;   // [B] the sequences' first cache rows
+  const int32_t* n_entries;      // [B] the sequences' entries
+  const int64_t* pos;            // [B][Tq] token position of every query
+  int m;                         // merge ratio
+  int64_t* eo;                   // [B * Tq] out: every query's first cache row
+  int32_t* ne;                   // [B * Tq] out: every query's visible entries
+};
+hipError_t launch_score_prefill(const uint8_t* ik, const uint8_t* iks, int B, int Tq, int64_t max_n,
+                                const uint16_t* q_idx, const float* w, int Hi, int mode, const SelBufs& sb, int K,
+                                const PrefillViews& pv, hipStream_t stream);
 
 // src: non-null when the direct score pass did not store the scores, or for a
 // candidate list (src->cand set).

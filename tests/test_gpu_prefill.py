@@ -122,16 +122,21 @@ def test_prefill_128_queries():
         assert np.all(np.abs(lse[0, t] - rl) <= 2e-3), f"query {t}: lse"
 
 
-@pytest.mark.parametrize("Tq", [8, 6])
-def test_prefill_selects_what_decode_selects(Tq):
+@pytest.mark.parametrize("Tq,mode", [(8, "relu_w"), (6, "relu_w"), (5, "dot"), (4, "qmx8")])
+def test_prefill_selects_what_decode_selects(Tq, mode):
     """The multi-query pass scores four queries per key tile with one combined
-    head-sum reduction; its scores must equal the one-query pass's bit for bit.
-    Each query of the prefill is also run as a decode sequence over the entries
-    it sees: the selections must be the same positions (near-ties included)
-    and the attention outputs the same bits. Tq = 6 leaves the second group
-    of four queries half empty."""
+    head-sum reduction and computes the queries' visible entries itself; its
+    scores must equal the one-query pass's bit for bit. Each query of the
+    prefill is also run as a decode sequence over the entries it sees: the
+    selections must be the same positions (near-ties included) and the
+    attention outputs the same bits. Tq = 6 leaves the second group of four
+    queries half empty; the dot-product mode takes the multi-query pass's
+    per-query head sums; the quantized-query mode has no multi-query pass (a
+    launch of its own computes the views, then the decode path runs)."""
     import torch
     import long_context_fp4_amd as L
+    sm = {"relu_w": L.CSA2_SCORE_RELU_W, "dot": L.CSA2_SCORE_DOT,
+          "qmx8": L.CSA2_SCORE_RELU_W | L.CSA2_SCORE_QMX8}[mode]
     rng = np.random.default_rng(4000 + Tq)
     m, k, H, T = 2, 512, 16, 90001
     w_lat = synth.merge_weights(rng, m, 512)
@@ -141,14 +146,15 @@ def test_prefill_selects_what_decode_selects(Tq):
     pos = np.sort(rng.choice(np.arange(3000, T), size=Tq, replace=False)).astype(np.int64)
     pos[-1] = T - 1
     q = np.stack([synth.latent_query(rng, H) for _ in range(Tq)])
-    qi = np.stack([synth.indexer_query(rng, 16) for _ in range(Tq)])
-    w = np.stack([synth.head_weights(rng, 16) for _ in range(Tq)])
+    Hi = 1 if mode == "dot" else 16                   # the dot-product score takes one indexer head
+    qi = np.stack([synth.indexer_query(rng, Hi) for _ in range(Tq)])
+    w = np.stack([synth.head_weights(rng, Hi) for _ in range(Tq)])
     dkv, dik, diks = dev(kv), dev(ik), dev(iks)
     top, out, lse = L.prefill_layer(dkv, dik, diks, dev(np.zeros(1, np.int64)), dev(np.array([E], np.int32)), E, m,
-                                    dev(pos[None]), dev(qi[None]), dev(q[None]), w=dev(w[None]), k=k)
+                                    dev(pos[None]), dev(qi[None]), dev(q[None]), w=dev(w[None]), score_mode=sm, k=k)
     vis = np.minimum(E, (pos + 1) // m).astype(np.int32)
     dtop, _, dout, dlse = L.decode_layer(L.CSA2_FULL, dkv, dik, diks, dev(np.zeros(Tq, np.int64)), dev(vis), E,
-                                         dev(q), q_idx=dev(qi), w=dev(w), k=k)
+                                         dev(q), q_idx=dev(qi), w=dev(w), score_mode=sm, k=k)
     torch.cuda.synchronize()
     assert np.array_equal(host(top)[0], host(dtop))
     assert np.array_equal(host(out)[0].view(np.uint32), host(dout).view(np.uint32))
