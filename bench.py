@@ -63,7 +63,7 @@ SCORE_SOURCES = [os.path.join(ROOT, "long_context_fp4_amd", "csrc", f)
 # Counter readings of one scoring launch at the decode128k size (KiB per
 # dispatch, medians over the timed launches) and the counters' scale factors
 # from the copy calibration; valid for the kernel sources with this hash.
-TRAFFIC = {"source_sha": "a248f18cd9b54cc9", "fetch_kib": 70246.0, "write_kib": 606.7,
+TRAFFIC = {"source_sha": "a248f18cd9b54cc9", "fetch_kib": 70245.0, "write_kib": 606.7,
            "fetch_scale": 2.0, "write_scale": 1.0}
 
 
