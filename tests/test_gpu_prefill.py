@@ -24,8 +24,9 @@ def test_prefill_queries_see_only_completed_entries(m, T_list, k):
     E = [p[0].shape[0] for p in parts]
     kv, ik, iks = (np.concatenate([p[i] for p in parts]) for i in range(3))
     off = np.concatenate([[0], np.cumsum(E)[:-1]]).astype(np.int64)
-    B, Tq, H = len(T_list), 5, 32
-    pos = np.stack([np.array([0, 2 * k - 1, T // 3, T - 2, T - 1], np.int64) for T in T_list])
+    # (a negative position and one past the sequence's tokens clamp to none and all)
+    B, Tq, H = len(T_list), 7, 32
+    pos = np.stack([np.array([-1, 0, 2 * k - 1, T // 3, T - 2, T - 1, T + 300], np.int64) for T in T_list])
     q = np.stack([[synth.latent_query(rng, H) for _ in range(Tq)] for _ in range(B)])
     qi = np.stack([[synth.indexer_query(rng, 16) for _ in range(Tq)] for _ in range(B)])
     w = np.stack([[synth.head_weights(rng, 16) for _ in range(Tq)] for _ in range(B)])
@@ -35,7 +36,7 @@ def test_prefill_queries_see_only_completed_entries(m, T_list, k):
     top, out, lse = host(top), host(out), host(lse)
     for b in range(B):
         for t in range(Tq):
-            nv = min(E[b], (int(pos[b, t]) + 1) // m)
+            nv = max(0, min(E[b], (int(pos[b, t]) + 1) // m))
             rows = slice(off[b], off[b] + nv)
             s = OI.scores(ik[rows], iks[rows], qi[b, t], w[b, t], 1) if nv else np.zeros(0, np.float32)
             want = OI.topk(s, np.arange(nv), k)
@@ -129,10 +130,12 @@ def test_prefill_selects_what_decode_selects(Tq, mode):
     scores must equal the one-query pass's bit for bit. Each query of the
     prefill is also run as a decode sequence over the entries it sees: the
     selections must be the same positions (near-ties included) and the
-    attention outputs the same bits. Tq = 6 leaves the second group of four
-    queries half empty; the dot-product mode takes the multi-query pass's
-    per-query head sums; the quantized-query mode has no multi-query pass (a
-    launch of its own computes the views, then the decode path runs)."""
+    attention outputs the same bits. The first query sees no entry (even Tq)
+    or fewer than k, the last sits past the cached entries and sees them all.
+    Tq = 6 leaves the second group of four queries half empty; the
+    dot-product mode takes the multi-query pass's per-query head sums; the
+    quantized-query mode has no multi-query pass (a launch of its own
+    computes the views, then the decode path runs)."""
     import torch
     import long_context_fp4_amd as L
     sm = {"relu_w": L.CSA2_SCORE_RELU_W, "dot": L.CSA2_SCORE_DOT,
@@ -144,7 +147,8 @@ def test_prefill_selects_what_decode_selects(Tq, mode):
     kv, ik, iks = OC.cache_write(synth.hidden_host(rng, (T, 512)), synth.hidden_host(rng, (T, 128)), w_lat, w_idx, m)
     E = kv.shape[0]
     pos = np.sort(rng.choice(np.arange(3000, T), size=Tq, replace=False)).astype(np.int64)
-    pos[-1] = T - 1
+    pos[-1] = T + 500                                  # past the cached entries: all of them visible
+    pos[0] = -1 if Tq % 2 == 0 else 700                # no entry visible / fewer than k
     q = np.stack([synth.latent_query(rng, H) for _ in range(Tq)])
     Hi = 1 if mode == "dot" else 16                   # the dot-product score takes one indexer head
     qi = np.stack([synth.indexer_query(rng, Hi) for _ in range(Tq)])
@@ -152,7 +156,7 @@ def test_prefill_selects_what_decode_selects(Tq, mode):
     dkv, dik, diks = dev(kv), dev(ik), dev(iks)
     top, out, lse = L.prefill_layer(dkv, dik, diks, dev(np.zeros(1, np.int64)), dev(np.array([E], np.int32)), E, m,
                                     dev(pos[None]), dev(qi[None]), dev(q[None]), w=dev(w[None]), score_mode=sm, k=k)
-    vis = np.minimum(E, (pos + 1) // m).astype(np.int32)
+    vis = np.where(pos < 0, 0, np.minimum(E, (pos + 1) // m)).astype(np.int32)
     dtop, _, dout, dlse = L.decode_layer(L.CSA2_FULL, dkv, dik, diks, dev(np.zeros(Tq, np.int64)), dev(vis), E,
                                          dev(q), q_idx=dev(qi), w=dev(w), score_mode=sm, k=k)
     torch.cuda.synchronize()
