@@ -180,8 +180,10 @@ __device__ __forceinline__ void merge_pack(const LaneMap& L, bool store, int m, 
   if (!L.latent && store && p == 0) st.iks[L.el] = xbytes;
 }
 
-// Writes the staged rows of the workgroup's entries with 16-byte stores (the
-// E8M0 bytes with one 4-byte store per entry). row_of(ent) gives the cache row
+// Writes the staged rows of the workgroup's entries with 16-byte non-temporal
+// stores (the written cache is not read back by this launch; plain stores
+// made the write128k launch ~4 % slower), the E8M0 bytes with one 4-byte store
+// per entry. row_of(ent) gives the cache row
 // of entry slot ent, or -1 to skip it. Every thread calls it after a barrier.
 template <typename RowOf>
 __device__ __forceinline__ void store_staged(const Staging& st, uint8_t* kv, uint8_t* ik, uint8_t* iks,
@@ -193,11 +195,13 @@ __device__ __forceinline__ void store_staged(const Staging& st, uint8_t* kv, uin
     if (t < LAT_CHUNKS) {
       const int ent = t / 18, c = t - 18 * (t / 18);
       const int64_t r = row_of(ent);
-      if (r >= 0) *(u32x4_t*)(kv + r * 288 + 16 * c) = *(const u32x4_t*)(st.lat + ent * CW_LAT_PITCH + 16 * c);
+      if (r >= 0)
+        __builtin_nontemporal_store(*(const u32x4_t*)(st.lat + ent * CW_LAT_PITCH + 16 * c), (u32x4_t*)(kv + r * 288 + 16 * c));
     } else if (t < LAT_CHUNKS + IDX_CHUNKS) {
       const int u = t - LAT_CHUNKS, ent = u >> 2, c = u & 3;
       const int64_t r = row_of(ent);
-      if (r >= 0) *(u32x4_t*)(ik + r * 64 + 16 * c) = *(const u32x4_t*)(st.idx + ent * CW_IDX_PITCH + 16 * c);
+      if (r >= 0)
+        __builtin_nontemporal_store(*(const u32x4_t*)(st.idx + ent * CW_IDX_PITCH + 16 * c), (u32x4_t*)(ik + r * 64 + 16 * c));
     } else {
       const int ent = t - LAT_CHUNKS - IDX_CHUNKS;
       const int64_t r = row_of(ent);
